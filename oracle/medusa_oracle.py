@@ -1,0 +1,450 @@
+"""CPU oracle for the Medusa decode step.  TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this module.  The library under
+``speculative_decoding_02_amd/`` never imports it, and it imports nothing from
+the library: the two share only the seeded input generators in ``synth``.
+
+What it computes is the decode step that the page "Medusa Heads" (Ultralytics
+glossary) describes in its sections "Come le teste prevedono i token
+successivi" (how the heads predict the next tokens) and "Attenzione sull'albero
+e accettazione" (tree attention and acceptance), with the one-pass tree
+verification of "Têtes de décodage Medusa" (section "Plongée profonde") and of
+the arXiv abstract page "Medusa: Simple LLM Inference Acceleration Framework
+with Multiple Decoding Heads".
+
+Form
+----
+* Plain numpy in float64.  Inputs given as float32 or bfloat16 values are
+  upcast exactly.  A matmul (``@``), ``exp``/``log`` and a stable sort are the
+  only library primitives used; there is no blocking, fusion or reordering.
+* Integer decisions that floating point takes (top-k order, argmax, typical
+  acceptance) are taken on logits rounded to float32, the precision the
+  library produces logits in: ties in float32 go to the lower token id.
+* Loops are plain Python where the sizes are tiny (per node, per head).
+
+Pins (tests/test_oracle_*.py, all ``-m "not gpu"``)
+-------------------------------------------------
+heads:        zero-initialised heads reproduce lm_head logits exactly (the
+              page's printed ``[True, True, True]``); nn.Linear semantics
+              via torch; closed form for W1 = 0, b1 = c, W2 = I.
+topk:         brute-force repeated max with planted ties.
+build_tree:   hand-derived 9-node template of the top-2 x top-3 example
+              (tests/golden/c1_tree.json); 6 candidates = itertools.product.
+tree_attention: chain tree = causal attention (torch SDPA, fp64); root-only
+              = decode attention; Q = 0 gives the mean of visible V; ancestor
+              walk + SDPA with an explicit boolean mask on random trees.
+decoder:      logits equal Hugging Face ``LlamaForCausalLM`` (fp64) on the
+              same weights; sequential greedy equals its greedy ``generate``.
+accept_greedy / medusa_generate: Medusa greedy output equals sequential
+              greedy decoding on the tiny random model (the lossless claim);
+              cheating heads accept the full depth; never-matching heads
+              accept nothing.
+accept_typical: special cases only (threshold 0 accepts everything; a
+              near-one-hot distribution reproduces greedy; monotone in
+              epsilon and delta).  The threshold FORMULA ``min(eps,
+              delta*exp(-H))`` is not printed on the pages, which only tie
+              the threshold to the entropy: parity unpinned for it.
+kv_compact:   compacted cache equals the cache of sequential decoding of the
+              same tokens; hand example path (0, 2, 7).
+"""
+from __future__ import annotations
+
+import itertools
+
+import numpy as np
+
+F64 = np.float64
+
+
+# ----------------------------------------------------------------------------
+# heads ("Medusa Heads", section on how the heads predict the next tokens)
+# ----------------------------------------------------------------------------
+def silu(z):
+    """SiLU(z) = z * sigmoid(z) = z / (1 + e^-z)  (torch's F.silu)."""
+    z = np.asarray(z, dtype=F64)
+    with np.errstate(over="ignore"):
+        return z / (1.0 + np.exp(-z))
+
+
+def linear(x, w, b=None):
+    """nn.Linear: y = x W^T (+ b), W stored [out_features, in_features]."""
+    y = np.asarray(x, dtype=F64) @ np.asarray(w, dtype=F64).T
+    if b is not None:
+        y = y + np.asarray(b, dtype=F64)
+    return y
+
+
+def head_hidden(x, w1_k, b1_k):
+    """Residual SiLU feed-forward layer of one head: U = x + SiLU(x W1^T + b1)."""
+    x = np.asarray(x, dtype=F64)
+    return x + silu(linear(x, w1_k, b1_k))
+
+
+def head_logits(x, w1, b1, w2):
+    """Logits of every Medusa head for every row of ``x``.
+
+    Head k reads the same final hidden state as lm_head, applies one residual
+    SiLU feed-forward layer, then a vocabulary projection without bias:
+    ``logits_k = (x + SiLU(x W1_k^T + b1_k)) W2_k^T``.  Returns [K, M, V].
+    """
+    return np.stack([linear(head_hidden(x, w1[k], b1[k]), w2[k]) for k in range(len(w1))])
+
+
+# ----------------------------------------------------------------------------
+# top-k and argmax (decisions in float32)
+# ----------------------------------------------------------------------------
+def f32(x):
+    return np.asarray(x, dtype=np.float32)
+
+
+def topk(values, k):
+    """Top-k of a float32 vector: value descending, equal values -> lower index.
+
+    "Le ipotesi migliori delle teste" ("Medusa Heads", tree attention section):
+    the heads' best guesses.  Implemented as a full stable sort.
+    Returns (ids int32[k], vals float32[k]).
+    """
+    v = f32(values)
+    order = np.argsort(-v, kind="stable")[:k]
+    return order.astype(np.int32), v[order]
+
+
+def argmax(values):
+    """Index of the largest float32 value, lowest index on ties."""
+    v = f32(values)
+    return int(np.flatnonzero(v == v.max())[0])
+
+
+# ----------------------------------------------------------------------------
+# candidate tree ("Medusa Heads", tree attention and acceptance section)
+# ----------------------------------------------------------------------------
+def cartesian_candidates(topk_lists):
+    """All continuations formed by the Cartesian product of per-head top-k lists."""
+    return list(itertools.product(*[list(t) for t in topk_lists]))
+
+
+def build_tree(parent, rank, root_tok, topk_ids, ctx):
+    """Fill a tree template with tokens; derive depths, positions and masks.
+
+    Node 0 holds ``root_tok``.  A node at depth d >= 1 with rank r holds
+    ``topk_ids[d-1][r]`` (head d proposes the token at t+d+1; every branch of
+    head d-1 gets the same proposals of head d).  A node sees itself and its
+    ancestors: ``mask[i]`` has bit j set iff tree node j is i or an ancestor.
+    Position of a node = ctx + depth.
+    Returns dict(tokens int32[N], depth int32[N], pos int32[N], mask uint64[N]).
+    """
+    n = len(parent)
+    tokens = np.zeros(n, np.int32)
+    depth = np.zeros(n, np.int32)
+    mask = np.zeros(n, np.uint64)
+    for i in range(n):
+        if i == 0:
+            tokens[0], depth[0], mask[0] = root_tok, 0, np.uint64(1)
+            continue
+        p = int(parent[i])
+        depth[i] = depth[p] + 1
+        tokens[i] = int(topk_ids[depth[i] - 1][int(rank[i])])
+        mask[i] = mask[p] | (np.uint64(1) << np.uint64(i))
+    return dict(tokens=tokens, depth=depth, pos=(ctx + depth).astype(np.int32), mask=mask)
+
+
+def visible(mask_i, n):
+    """Tree node indices whose bit is set in ``mask_i``."""
+    m = int(mask_i)
+    return [j for j in range(n) if (m >> j) & 1]
+
+
+# ----------------------------------------------------------------------------
+# tree-masked attention ("Medusa Heads", tree attention section; arXiv
+# abstract: tree-based attention verifies all candidates in one step)
+# ----------------------------------------------------------------------------
+def tree_attention(q, k_cache, v_cache, k_tree, v_tree, mask, scale):
+    """Softmax attention of every tree node over the cache plus its ancestors.
+
+    q [N, Hq, D]; k_cache/v_cache [ctx, Hkv, D] (logical order); k_tree/v_tree
+    [N, Hkv, D]; mask uint64[N].  Node i attends to all ``ctx`` cached keys and
+    to tree node j iff bit j of mask[i] is set; masked keys take no part.
+    Query head h reads key/value head h // (Hq / Hkv).  Returns [N, Hq, D].
+    """
+    q = np.asarray(q, F64)
+    kc, vc = np.asarray(k_cache, F64), np.asarray(v_cache, F64)
+    kt, vt = np.asarray(k_tree, F64), np.asarray(v_tree, F64)
+    n, hq, d = q.shape
+    group = hq // kt.shape[1]
+    out = np.zeros((n, hq, d), F64)
+    for i in range(n):
+        vis = visible(mask[i], n)
+        for h in range(hq):
+            g = h // group
+            keys = np.concatenate([kc[:, g, :], kt[vis, g, :]], axis=0)
+            vals = np.concatenate([vc[:, g, :], vt[vis, g, :]], axis=0)
+            s = (keys @ q[i, h]) * float(scale)
+            p = np.exp(s - s.max())
+            out[i, h] = (p / p.sum()) @ vals
+    return out
+
+
+def cache_rows(pool, page_table_row, n, page_size):
+    """Logical rows 0..n-1 of a paged cache pool [pages, Hkv, P, D] -> [n, Hkv, D]."""
+    pool = np.asarray(pool)
+    slots = np.arange(n)
+    pages = np.asarray(page_table_row)[slots // page_size]
+    return pool[pages, :, slots % page_size, :]
+
+
+# ----------------------------------------------------------------------------
+# acceptance ("Medusa Heads", tree attention and acceptance section)
+# ----------------------------------------------------------------------------
+def _accept_sweep(tokens, parent, ok, n_heads):
+    """Longest accepted branch given a per-node criterion ``ok(i)``.
+
+    acc[0] = True (the root is the model's own choice); acc[i] = acc[parent] and
+    ok(i).  The kept branch ends at the deepest accepted node, lowest index on
+    ties.  Returns (accept_len, path int32[n_heads+1] padded with -1, best).
+    """
+    n = len(parent)
+    depth = np.zeros(n, np.int32)
+    acc = np.zeros(n, bool)
+    acc[0] = True
+    for i in range(1, n):
+        p = int(parent[i])
+        depth[i] = depth[p] + 1
+        acc[i] = acc[p] and ok(i)
+    best = 0
+    for i in range(1, n):
+        if acc[i] and depth[i] > depth[best]:
+            best = i
+    a = int(depth[best])
+    path = -np.ones(n_heads + 1, np.int32)
+    j = best
+    for d in range(a, -1, -1):
+        path[d] = j
+        j = int(parent[j])
+    return a, path, best
+
+
+def accept_greedy(logits, tokens, parent, n_heads):
+    """Greedy acceptance: a candidate is kept when it equals the model's top choice.
+
+    ``logits`` [N, V] are the verification logits of the tree nodes: row p
+    scores the token after node p.  Returns dict(accept_len, path, next_token,
+    best); next_token = argmax of the kept branch's last row.
+    """
+    top = [argmax(row) for row in logits]
+    a, path, best = _accept_sweep(tokens, parent,
+                                  lambda i: int(tokens[i]) == top[int(parent[i])], n_heads)
+    return dict(accept_len=a, path=path, next_token=top[best], best=best)
+
+
+def typical_stats(logits_row, temperature):
+    """(log-probabilities, entropy) of softmax(logits / T), in float64."""
+    z = f32(logits_row).astype(F64) / float(temperature)
+    z = z - z.max()
+    logp = z - np.log(np.exp(z).sum())
+    p = np.exp(logp)
+    ent = -float(np.sum(np.where(p > 0, p * logp, 0.0)))
+    return logp, ent
+
+
+def accept_typical(logits, tokens, parent, n_heads, temperature, epsilon, delta,
+                   return_margins=False):
+    """Typical acceptance: keep a candidate whose base-model probability is above
+    an entropy-linked threshold.
+
+    Reading (the formula itself is not on the pages): with p = softmax(z / T)
+    of the parent's row and H its natural-log entropy, accept iff
+    ``p(token) > min(epsilon, delta * exp(-H))``.  The next root token is the
+    argmax of the kept branch's last row.  With ``return_margins`` also
+    returns, per node, ln p(token) - ln(threshold).
+    """
+    n = len(parent)
+    stats = {}
+    margins = np.full(n, np.inf)
+
+    def ok(i):
+        p = int(parent[i])
+        if p not in stats:
+            stats[p] = typical_stats(logits[p], temperature)
+        logp, ent = stats[p]
+        thr = min(float(epsilon), float(delta) * np.exp(-ent))
+        lp = logp[int(tokens[i])]
+        margins[i] = lp - (np.log(thr) if thr > 0 else -np.inf)
+        return bool(np.exp(lp) > thr)
+
+    a, path, best = _accept_sweep(tokens, parent, ok, n_heads)
+    out = dict(accept_len=a, path=path, next_token=argmax(logits[best]), best=best)
+    if return_margins:
+        out["margins"] = margins
+    return out
+
+
+# ----------------------------------------------------------------------------
+# KV compaction (only the kept branch stays in the cache: "Medusa Heads",
+# tree attention section, the longest accepted branch is kept)
+# ----------------------------------------------------------------------------
+def kv_compact(cache, ctx, path, accept_len):
+    """Move the kept branch's rows to slots ctx..ctx+a (logical [S, ...] cache).
+
+    Row ctx+d receives old row ctx+path[d] for d = 0..a (all reads happen
+    before any write).  Returns (new_cache, src_slots, dst_slots, new_ctx);
+    src/dst are padded with -1 to len(path).
+    """
+    new = np.array(cache, copy=True)
+    a = int(accept_len)
+    src = -np.ones(len(path), np.int32)
+    dst = -np.ones(len(path), np.int32)
+    rows = [np.array(cache[ctx + int(path[d])], copy=True) for d in range(a + 1)]
+    for d in range(a + 1):
+        new[ctx + d] = rows[d]
+        src[d], dst[d] = ctx + int(path[d]), ctx + d
+    return new, src, dst, ctx + a + 1
+
+
+# ----------------------------------------------------------------------------
+# Llama-style backbone (the model being verified; the pages fix only that the
+# tree is checked in one forward pass of the base model)
+# ----------------------------------------------------------------------------
+def rmsnorm(x, g, eps):
+    x = np.asarray(x, F64)
+    return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps) * np.asarray(g, F64)
+
+
+def rope(x, pos, base):
+    """Rotary embedding, rotate-half convention, over the full head dim.
+
+    x [n, heads, D]; angle(p, j) = p * base^(-2j/D) for j < D/2; the pair
+    (x_j, x_{j+D/2}) is rotated by that angle.
+    """
+    x = np.asarray(x, F64)
+    d = x.shape[-1]
+    half = d // 2
+    inv = base ** (-np.arange(half, dtype=F64) * 2.0 / d)
+    ang = np.asarray(pos, F64)[:, None] * inv[None, :]
+    c, s = np.cos(ang)[:, None, :], np.sin(ang)[:, None, :]
+    x1, x2 = x[..., :half], x[..., half:]
+    return np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=-1)
+
+
+class KVCache:
+    """Per-layer logical K/V caches [capacity, Hkv, D] in float64."""
+
+    def __init__(self, model, capacity):
+        shape = (capacity, model.n_kv_heads, model.head_dim)
+        self.k = [np.zeros(shape, F64) for _ in range(model.n_layers)]
+        self.v = [np.zeros(shape, F64) for _ in range(model.n_layers)]
+
+    def copy(self):
+        c = KVCache.__new__(KVCache)
+        c.k = [a.copy() for a in self.k]
+        c.v = [a.copy() for a in self.v]
+        return c
+
+
+def forward_rows(model, tokens, pos, mask, cache, ctx, layer_hook=None):
+    """One forward pass of ``n`` new rows that see the cache and, among
+    themselves, what ``mask`` allows (a chain mask = ordinary causal decoding).
+
+    Writes the rows' K/V into cache slots ctx..ctx+n-1.  Returns
+    (logits [n, V] float64, final hidden state after the last RMSNorm [n, H]).
+    """
+    n = len(tokens)
+    x = np.asarray(model.embed, F64)[np.asarray(tokens)]
+    nh, nkv, hd = model.n_heads, model.n_kv_heads, model.head_dim
+    scale = 1.0 / np.sqrt(hd)
+    for li, L in enumerate(model.layers):
+        h = rmsnorm(x, L["g_attn"], model.eps)
+        q = rope(linear(h, L["wq"]).reshape(n, nh, hd), pos, model.rope_base)
+        k = rope(linear(h, L["wk"]).reshape(n, nkv, hd), pos, model.rope_base)
+        v = linear(h, L["wv"]).reshape(n, nkv, hd)
+        o = tree_attention(q, cache.k[li][:ctx], cache.v[li][:ctx], k, v, mask, scale)
+        cache.k[li][ctx:ctx + n] = k
+        cache.v[li][ctx:ctx + n] = v
+        x = x + linear(o.reshape(n, nh * hd), L["wo"])
+        h = rmsnorm(x, L["g_mlp"], model.eps)
+        x = x + linear(silu(linear(h, L["wg"])) * linear(h, L["wu"]), L["wd"])
+        if layer_hook is not None:
+            layer_hook(li, x)
+    hf = rmsnorm(x, model.g_final, model.eps)
+    return linear(hf, model.lm_head), hf
+
+
+def chain_mask(n):
+    """Mask of a single path of n nodes: node i sees nodes 0..i."""
+    return np.array([(1 << (i + 1)) - 1 for i in range(n)], dtype=np.uint64)
+
+
+def prefill(model, prompt, cache):
+    """Causal forward over the prompt (positions 0..P-1)."""
+    p = len(prompt)
+    return forward_rows(model, prompt, np.arange(p), chain_mask(p), cache, 0)
+
+
+def sequential_greedy(model, prompt, n_new, capacity=None):
+    """Plain greedy decoding: one token per forward pass, x_{t+1} = argmax."""
+    capacity = capacity or len(prompt) + n_new + 1
+    cache = KVCache(model, capacity)
+    logits, _ = prefill(model, prompt, cache)
+    out = [argmax(logits[-1])]
+    ctx = len(prompt)
+    while len(out) < n_new:
+        logits, _ = forward_rows(model, [out[-1]], [ctx], np.array([1], np.uint64), cache, ctx)
+        ctx += 1
+        out.append(argmax(logits[-1]))
+    return np.array(out, np.int32), cache, ctx
+
+
+def medusa_generate(model, prompt, n_new, parent, rank, mode="greedy", temperature=1.0,
+                    epsilon=0.3, delta=0.09, heads=None, capacity=None, record=None):
+    """Medusa decoding loop, steps in the order the pages give them.
+
+    1. Prefill; root = argmax of the last row; heads on the last hidden state
+       give per-head top-k (k = max rank + 1 of the template).
+    2. Build the tree from the template; verify all nodes in one forward pass
+       with the ancestor mask.
+    3. Accept the longest branch (greedy or typical); emit its a+1 tokens.
+    4. Keep only that branch in the cache; feed its last hidden state to the
+       heads for the next round; next root = argmax of its last row.
+    ``heads`` (optional) replaces the learned heads by a function
+    hidden_row -> [K, V] logits (used by pins).  ``record`` collects per-step
+    dicts.  Returns (tokens int32[n_new], cache, ctx).
+    """
+    parent = np.asarray(parent)
+    rank = np.asarray(rank)
+    depth_of = np.zeros(len(parent), np.int32)
+    for i in range(1, len(parent)):
+        depth_of[i] = depth_of[parent[i]] + 1
+    n_heads = int(depth_of.max())
+    width = int(rank.max()) + 1
+    n = len(parent)
+    capacity = capacity or len(prompt) + n_new + n + 1
+    cache = KVCache(model, capacity)
+    logits, hf = prefill(model, prompt, cache)
+    ctx = len(prompt)
+
+    def head_topk(hrow):
+        lg = heads(hrow) if heads is not None else head_logits(hrow[None], model.w1, model.b1, model.w2)[:, 0]
+        return [topk(lg[k], width)[0] for k in range(n_heads)]
+
+    root = argmax(logits[-1])
+    ids = head_topk(hf[-1])
+    out = []
+    while len(out) < n_new:
+        tree = build_tree(parent, rank, root, ids, ctx)
+        logits, hf = forward_rows(model, tree["tokens"], tree["pos"], tree["mask"], cache, ctx)
+        lf = f32(logits)
+        if mode == "greedy":
+            res = accept_greedy(lf, tree["tokens"], parent, n_heads)
+        else:
+            res = accept_typical(lf, tree["tokens"], parent, n_heads, temperature, epsilon, delta)
+        a, path = res["accept_len"], res["path"]
+        out.extend(int(tree["tokens"][path[d]]) for d in range(a + 1))
+        for li in range(model.n_layers):
+            cache.k[li], _, _, _ = kv_compact(cache.k[li], ctx, path, a)
+            cache.v[li], src, dst, new_ctx = kv_compact(cache.v[li], ctx, path, a)
+        if record is not None:
+            record.append(dict(ctx=ctx, tree=tree, accept=res, src=src, dst=dst))
+        ctx = new_ctx
+        root = res["next_token"]
+        ids = head_topk(hf[res["best"]])
+    return np.array(out[:n_new], np.int32), cache, ctx
