@@ -1,0 +1,264 @@
+/*
+ * libmedusa: the Medusa decode step on one AMD Instinct MI355X (gfx950).
+ *
+ * The step (page "Medusa Heads", Ultralytics glossary; page "Têtes de
+ * décodage Medusa", section "Plongée profonde"; arXiv abstract page "Medusa:
+ * Simple LLM Inference Acceleration Framework with Multiple Decoding Heads"):
+ *   1. K extra heads read the final hidden state; head k scores the token at
+ *      t+k+1 (medusa_heads, medusa_topk).
+ *   2. The per-head top-k lists are combined as a Cartesian product into a
+ *      candidate tree whose nodes share prefixes (medusa_build_tree).
+ *   3. One forward pass verifies every tree node at once; an attention mask
+ *      lets each node see only its ancestors (medusa_tree_attention, plus
+ *      the backbone calls medusa_embed ... medusa_linear).
+ *   4. The longest branch the model agrees with is kept, greedy or typical
+ *      (medusa_accept), and only that branch stays in the KV cache
+ *      (kv_compact); its last hidden state feeds the heads next round
+ *      (medusa_gather_rows).
+ *
+ * Conventions for every call
+ * --------------------------
+ * - Pointers are DEVICE pointers unless a parameter says "host".  Tensors are
+ *   dense row-major in the layout given in brackets, innermost last.
+ * - dtype: MEDUSA_F32 tensors hold float; MEDUSA_BF16 tensors hold bfloat16
+ *   bit patterns (uint16).  Logits, top-k values, softmax statistics and the
+ *   residual stream are always float.  Arithmetic is fp32 in both modes.
+ * - Ownership: the caller allocates and frees every buffer, workspaces
+ *   included; the library never allocates and keeps no state between calls.
+ * - Streams: `stream` is a hipStream_t passed as void* (NULL = default
+ *   stream).  Every call only enqueues work and returns; nothing blocks the
+ *   host.  Buffers must stay alive until the stream has passed the call.
+ * - Errors: every call returns a medusa_status.  Arguments are validated on
+ *   the host before any launch; on failure nothing is enqueued and
+ *   medusa_last_error() (thread-local) describes the problem.  Values read
+ *   on the device (token ids, ctx, page tables, templates, paths) are not
+ *   checked: out-of-range device data is undefined behaviour.
+ * - Limits: tree nodes N <= 64 (one uint64 mask per node), heads K <= 8,
+ *   top-k <= 64, head dim D in {64, 128}, Hq a multiple of Hkv.
+ */
+#ifndef MEDUSA_H_
+#define MEDUSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { MEDUSA_F32 = 0, MEDUSA_BF16 = 1 } medusa_dtype;
+
+typedef enum {
+  MEDUSA_OK = 0,
+  MEDUSA_ERR_INVALID_ARG = 1,   /* NULL pointer, negative size, bad template ... */
+  MEDUSA_ERR_UNSUPPORTED = 2,   /* dtype, head dim or size outside the limits     */
+  MEDUSA_ERR_WORKSPACE = 3,     /* workspace smaller than the *_ws query          */
+  MEDUSA_ERR_HIP = 4            /* a HIP launch failed                            */
+} medusa_status;
+
+#define MEDUSA_MAX_NODES 64
+#define MEDUSA_MAX_HEADS 8
+#define MEDUSA_MAX_TOPK 64
+#define MEDUSA_MAX_LAYERS 128
+
+const char* medusa_status_string(int32_t status);
+const char* medusa_last_error(void);
+int32_t medusa_abi_version(void);
+
+/* ------------------------------------------------------------------------
+ * Tree template check (host only).
+ * The tree is the Cartesian product of per-head top-k ("Medusa Heads",
+ * section "Attenzione sull'albero e accettazione").  A template fixes its
+ * shape: node 0 is the root (parent -1); node i > 0 has parent[i] < i and
+ * uses rank[i] of the top-k list of head depth(i).
+ * parent, rank: HOST arrays [N].  Checks N in [1, 64], parent[0] == -1,
+ * 0 <= parent[i] < i, depth(i) <= K, 0 <= rank[i] < topk, and distinct ranks
+ * among siblings.  Returns MEDUSA_OK or MEDUSA_ERR_INVALID_ARG.
+ * ---------------------------------------------------------------------- */
+int32_t medusa_tree_validate(const int32_t* parent, const int32_t* rank, int32_t N,
+                             int32_t K, int32_t topk);
+
+/* ------------------------------------------------------------------------
+ * Generic projection  Y = epilogue(X W^T)   (nn.Linear orientation).
+ * The backbone's projections and the heads' two layers ("Medusa Heads",
+ * section "Come le teste prevedono i token successivi": a feed-forward layer
+ * with SiLU and a residual connection, then a vocabulary projection).
+ *   X [batch][M, Kd] (dtype dt, row stride Kd, batch stride x_bstride
+ *     elements, 0 = shared), W [batch][N, Kd] (dt), Y [batch][M, N].
+ *   epilogue:
+ *     MEDUSA_EPI_NONE        Y = acc                          (Y dtype: y_f32 ? float : dt)
+ *     MEDUSA_EPI_BIAS_SILU_RES  Y = R + SiLU(acc + bias)      (R = aux [batch][M, N] dt,
+ *                                bias [batch][N] dt; needs N == Kd when R is X)
+ *     MEDUSA_EPI_RES_ADD_F32 Y = aux + acc, Y and aux float [M, N] (may alias)
+ *     MEDUSA_EPI_SWIGLU      W holds gate and up rows interleaved in blocks of
+ *                            16 (block j: gate rows 16j..16j+15 then up rows);
+ *                            Y [M, N/2] = SiLU(gate) * up   (dt)
+ *   Reduction order per output element depends only on Kd, never on M or
+ *   batch: equal inputs give bitwise equal outputs.
+ * Kd must be a multiple of 8 (bf16) or 4 (f32).  ws may be NULL (none needed).
+ * ---------------------------------------------------------------------- */
+typedef enum {
+  MEDUSA_EPI_NONE = 0,
+  MEDUSA_EPI_BIAS_SILU_RES = 1,
+  MEDUSA_EPI_RES_ADD_F32 = 2,
+  MEDUSA_EPI_SWIGLU = 3
+} medusa_epilogue;
+
+int32_t medusa_linear(const void* X, int64_t x_bstride, int64_t M, int64_t Kd, const void* W,
+                      int64_t N, int32_t batch, int32_t dt, int32_t epilogue, const void* bias,
+                      const void* aux, void* Y, int32_t y_f32, void* stream);
+
+/* ------------------------------------------------------------------------
+ * medusa_heads: K Medusa heads on M hidden rows, plus per-head top-k.
+ * ("Medusa Heads", section "Come le teste prevedono i token successivi":
+ *  head k reads the final hidden state h that lm_head reads and scores the
+ *  token at t+k+1 as  logits_k = W2_k (h + SiLU(W1_k h + b1_k)).)
+ *   X [M, H] (dt), W1 [K, H, H] (row = output feature), b1 [K, H] (dt),
+ *   W2 [K, V, H] (dt, no bias).
+ *   logits: [K, M, V] float, or NULL to keep them internal.
+ *   topk (0..64): if > 0, topk_ids [K, M, topk] int32 and topk_vals
+ *   [K, M, topk] float receive each row's largest logits, value descending,
+ *   equal values ordered by lower token id.
+ *   ws: device workspace of at least medusa_heads_ws(...) bytes.
+ * With W1 = 0, b1 = 0 and W2_k = lm_head the logits equal
+ * medusa_linear(X, lm_head) bit for bit.
+ * ---------------------------------------------------------------------- */
+size_t medusa_heads_ws(int64_t M, int64_t H, int32_t K, int64_t V, int32_t topk, int32_t dt);
+int32_t medusa_heads(const void* X, int64_t M, int64_t H, int32_t K, const void* W1,
+                     const void* b1, const void* W2, int64_t V, int32_t dt, float* logits,
+                     int32_t topk, int32_t* topk_ids, float* topk_vals, void* ws,
+                     size_t ws_bytes, void* stream);
+
+/* medusa_topk: top-k of each float row ("Medusa Heads", tree section: the
+ * heads' best guesses).  logits [R, V] float -> ids [R, k] int32, vals [R, k]
+ * float; order value descending, ties by lower index; 1 <= k <= 64, k <= V. */
+int32_t medusa_topk(const float* logits, int64_t R, int64_t V, int32_t k, int32_t* ids,
+                    float* vals, void* stream);
+
+/* ------------------------------------------------------------------------
+ * medusa_build_tree: fill B tree templates with tokens ("Medusa Heads",
+ * section "Attenzione sull'albero e accettazione": the Cartesian product of
+ * the heads' top-k forms a prefix-sharing tree; each token sees only its
+ * ancestors).
+ *   parent, rank [B, N] int32 (templates, validated beforehand on the host)
+ *   root_tok [B] int32: the model's own next token (node 0)
+ *   topk_ids [K, B, topk] int32: node i at depth d >= 1 gets
+ *     topk_ids[d-1, b, rank[b, i]]
+ *   ctx [B] int32: committed tokens in the cache
+ * Outputs tokens [B, N] int32, pos [B, N] int32 = ctx + depth, mask [B, N]
+ * uint64 with bit j set iff node j is node i or one of its ancestors.
+ * ---------------------------------------------------------------------- */
+int32_t medusa_build_tree(int32_t B, int32_t N, const int32_t* parent, const int32_t* rank,
+                          const int32_t* root_tok, const int32_t* topk_ids, int32_t K,
+                          int32_t topk, const int32_t* ctx, int32_t* tokens, int32_t* pos,
+                          uint64_t* mask, void* stream);
+
+/* ------------------------------------------------------------------------
+ * medusa_tree_attention: one tree-masked attention pass ("Medusa Heads",
+ * tree section: all candidate tokens are appended at once and a mask lets
+ * each see only its ancestors, so every branch is checked in parallel; arXiv
+ * abstract page: tree-based attention).
+ *   Q  [B, N, Hq, D] (dt)   queries of the N tree nodes (RoPE applied)
+ *   Kt, Vt [B, N, Hkv, D]   keys / values of the tree nodes
+ *   Kc, Vc [pages, Hkv, P, D]  paged cache pools; logical slot s of sequence
+ *          b lives in page page_table[b, s / P] at row s % P
+ *   page_table [B, max_pages] int32; ctx [B] int32 committed tokens
+ *   max_ctx: host-side upper bound of every ctx[b] (sizes the grid)
+ *   mask [B, N] uint64 (from medusa_build_tree)
+ *   O  [B, N, Hq, D] (dt)
+ * Node i of sequence b attends, with scores q.k * scale and an fp32 softmax,
+ * to cache slots 0..ctx[b]-1 and to tree node j iff bit j of mask[b, i].
+ * Query head h uses kv head h / (Hq / Hkv).  The call also stores Kt, Vt into
+ * cache slots ctx[b] .. ctx[b]+N-1 (those pages must exist in page_table).
+ * ws: medusa_tree_attention_ws(...) bytes, ZERO-FILLED before its first use;
+ * each call leaves its counter area zero again.  Calls sharing one ws must
+ * not overlap in time.
+ * ---------------------------------------------------------------------- */
+size_t medusa_tree_attention_ws(int32_t B, int32_t N, int32_t Hq, int32_t Hkv, int32_t D,
+                                int32_t max_ctx);
+int32_t medusa_tree_attention(const void* Q, const void* Kt, const void* Vt, void* Kc, void* Vc,
+                              const int32_t* page_table, int32_t max_pages, int32_t P,
+                              const int32_t* ctx, int32_t max_ctx, const uint64_t* mask,
+                              int32_t B, int32_t N, int32_t Hq, int32_t Hkv, int32_t D,
+                              float scale, int32_t dt, void* O, void* ws, size_t ws_bytes,
+                              void* stream);
+
+/* ------------------------------------------------------------------------
+ * medusa_accept: longest accepted branch per sequence ("Medusa Heads", tree
+ * section: the longest branch the model accepts is kept; greedy keeps a
+ * candidate equal to the model's top choice; typical acceptance keeps a
+ * candidate whose base-model probability exceeds an entropy-linked
+ * threshold).
+ *   logits [B, N, V] float: verification logits, row p scores the token that
+ *     follows node p
+ *   tokens, parent [B, N] int32
+ *   K: number of heads = longest possible branch minus one; path has K+1 slots
+ *   mode 0 greedy: node i accepted iff its parent is and tokens[i] ==
+ *     argmax(logits[parent]) (lowest id on ties)
+ *   mode 1 typical: iff its parent is and p(tokens[i]) > min(epsilon,
+ *     delta * exp(-H(p))), p = softmax(logits[parent] / temperature),
+ *     H natural-log entropy
+ * Outputs: accept_len [B] = depth of the deepest accepted node (lowest index
+ * on ties); path [B, K+1] node indices root..best, padded with -1;
+ * next_token [B] = argmax of logits[best].
+ * ws: medusa_accept_ws(B, N) bytes.
+ * ---------------------------------------------------------------------- */
+size_t medusa_accept_ws(int32_t B, int32_t N);
+int32_t medusa_accept(const float* logits, int64_t V, const int32_t* tokens,
+                      const int32_t* parent, int32_t B, int32_t N, int32_t K, int32_t mode,
+                      float temperature, float epsilon, float delta, int32_t* accept_len,
+                      int32_t* path, int32_t* next_token, void* ws, size_t ws_bytes,
+                      void* stream);
+
+/* ------------------------------------------------------------------------
+ * kv_compact: keep only the accepted branch in every layer's cache (the
+ * branch the model accepted is kept: "Medusa Heads", tree section).
+ * For d = 0..accept_len[b]: slot ctx[b]+d <- slot ctx[b]+path[b, d], K and V,
+ * all layers, all kv heads; every read happens before any write.
+ *   Kc, Vc: HOST arrays of L device pointers, one [pages, Hkv, P, D] pool per
+ *   layer (L <= 128); page_table [B, max_pages]; ctx [B]; path [B, K+1];
+ *   accept_len [B].
+ * Outputs: src_slots, dst_slots [B, K+1] int32 (logical slots, -1 padded;
+ * either may be NULL), new_ctx [B] = ctx + accept_len + 1 (must not alias ctx).
+ * ---------------------------------------------------------------------- */
+int32_t kv_compact(void* const* Kc, void* const* Vc, int32_t L, const int32_t* page_table,
+                   int32_t max_pages, int32_t P, const int32_t* ctx, const int32_t* path,
+                   const int32_t* accept_len, int32_t B, int32_t K, int32_t Hkv, int32_t D,
+                   int32_t dt, int32_t* src_slots, int32_t* dst_slots, int32_t* new_ctx,
+                   void* stream);
+
+/* ------------------------------------------------------------------------
+ * Backbone pieces of the verification forward pass (the base model checks
+ * the whole tree in one pass: "Têtes de décodage Medusa", section "Plongée
+ * profonde").  Llama-style: RMSNorm, rotary positions, SwiGLU.
+ * ---------------------------------------------------------------------- */
+
+/* out [M, H] float = table[tokens[m], :]; table [V, H] (dt). */
+int32_t medusa_embed(const int32_t* tokens, int64_t M, const void* table, int64_t V, int64_t H,
+                     int32_t dt, float* out, void* stream);
+
+/* out [M, H] (dt) = x / sqrt(mean(x^2) + eps) * gain; x float [M, H];
+ * gain [H] (dt) or NULL for 1. */
+int32_t medusa_rmsnorm(const float* x, int64_t M, int64_t H, const void* gain, float eps,
+                       int32_t dt, void* out, void* stream);
+
+/* Split qkv [M, (Hq + 2 Hkv) * D] (dt) into q [M, Hq, D], k [M, Hkv, D],
+ * v [M, Hkv, D] and rotate q and k by position pos[m] (rotate-half pairs
+ * (j, j + D/2), angle pos * base^(-2j/D)). */
+int32_t medusa_qkv_rope(const void* qkv, int64_t M, int32_t Hq, int32_t Hkv, int32_t D,
+                        const int32_t* pos, float base, int32_t dt, void* q, void* k, void* v,
+                        void* stream);
+
+/* out [M, F] (dt) = SiLU(gu[:, :F]) * gu[:, F:], gu [M, 2F] (dt). */
+int32_t medusa_swiglu(const void* gu, int64_t M, int64_t F, int32_t dt, void* out, void* stream);
+
+/* out [B, H] (dt) = h[b, path[b, accept_len[b]], :] with h [B, N, H] (dt),
+ * path [B, K+1]: the kept branch's last hidden state, fed to the heads. */
+int32_t medusa_gather_rows(const void* h, int32_t B, int32_t N, int64_t H, const int32_t* path,
+                           const int32_t* accept_len, int32_t K, int32_t dt, void* out,
+                           void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MEDUSA_H_ */

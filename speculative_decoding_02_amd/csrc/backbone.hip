@@ -1,0 +1,179 @@
+// Element-wise and row-wise pieces of the Llama-style verification forward
+// pass (the base model checks every tree node in one pass: "Têtes de décodage
+// Medusa", section "Plongée profonde").  The projections themselves run in
+// gemm.hip.  The residual stream is fp32; GEMM inputs are in the model dtype.
+#include "common.h"
+
+namespace medusa {
+
+template <typename T>
+__global__ __launch_bounds__(256) void embed_kernel(const int* __restrict__ tokens,
+                                                    const T* __restrict__ table, int64_t H,
+                                                    float* __restrict__ out) {
+  const int64_t m = blockIdx.x;
+  const T* row = table + (int64_t)tokens[m] * H;
+  for (int64_t e = threadIdx.x; e < H; e += 256) out[m * H + e] = ld<T>(row, e);
+}
+
+// One workgroup per row; fixed-order reduction (per-thread strided sums, then
+// a butterfly inside each wave, then waves in order).
+template <typename T>
+__global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ x, int64_t H,
+                                                      const T* __restrict__ gain, float eps,
+                                                      T* __restrict__ out) {
+  const int64_t m = blockIdx.x;
+  const float* xr = x + m * H;
+  float ss = 0.f;
+  for (int64_t e = threadIdx.x; e < H; e += 256) ss += xr[e] * xr[e];
+  ss = wave_sum(ss);
+  __shared__ float part[4];
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  const float tot = (part[0] + part[1]) + (part[2] + part[3]);
+  const float rs = 1.0f / sqrtf(tot / (float)H + eps);
+  for (int64_t e = threadIdx.x; e < H; e += 256) {
+    const float g = gain ? ld<T>(gain, e) : 1.f;
+    st<T>(out, m * H + e, xr[e] * rs * g);
+  }
+}
+
+// Rotary positions, rotate-half pairs (j, j + D/2), angle pos * base^(-2j/D);
+// the angles and their cosines / sines are evaluated in fp64 once per row.
+template <typename T>
+__global__ __launch_bounds__(256) void qkv_rope_kernel(const T* __restrict__ qkv, int Hq, int Hkv,
+                                                       int D, const int* __restrict__ pos,
+                                                       double log2_base, T* __restrict__ q,
+                                                       T* __restrict__ k, T* __restrict__ v) {
+  const int64_t m = blockIdx.x;
+  __shared__ float cs[64], sn[64];
+  const int half = D / 2;
+  if (threadIdx.x < half) {
+    const double inv = exp2(-(2.0 * threadIdx.x / D) * log2_base);
+    const double ang = (double)pos[m] * inv;
+    cs[threadIdx.x] = (float)cos(ang);
+    sn[threadIdx.x] = (float)sin(ang);
+  }
+  __syncthreads();
+  const int W = (Hq + 2 * Hkv) * D;
+  const T* in = qkv + m * W;
+  // rotated part: q and k heads, one pair per thread step
+  const int pairs = (Hq + Hkv) * half;
+  for (int e = threadIdx.x; e < pairs; e += 256) {
+    const int hh = e / half, j = e % half;
+    const float x1 = ld<T>(in, (int64_t)hh * D + j), x2 = ld<T>(in, (int64_t)hh * D + j + half);
+    const float o1 = x1 * cs[j] - x2 * sn[j];
+    const float o2 = x2 * cs[j] + x1 * sn[j];
+    T* dst = hh < Hq ? q + (m * Hq + hh) * D : k + (m * Hkv + (hh - Hq)) * D;
+    st<T>(dst, j, o1);
+    st<T>(dst, j + half, o2);
+  }
+  for (int e = threadIdx.x; e < Hkv * D; e += 256) v[m * Hkv * D + e] = in[(int64_t)(Hq + Hkv) * D + e];
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void swiglu_kernel(const T* __restrict__ gu, int64_t F,
+                                                     T* __restrict__ out) {
+  const int64_t m = blockIdx.x;
+  for (int64_t e = threadIdx.x; e < F; e += 256) {
+    const float g = ld<T>(gu, m * 2 * F + e), u = ld<T>(gu, m * 2 * F + F + e);
+    st<T>(out, m * F + e, silu_f(g) * u);
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void gather_rows_kernel(const T* __restrict__ h, int N, int64_t H,
+                                                          const int* __restrict__ path,
+                                                          const int* __restrict__ accept_len,
+                                                          int K, T* __restrict__ out) {
+  const int b = blockIdx.x;
+  const int a = min(accept_len[b], K);
+  const int node = path[(int64_t)b * (K + 1) + a];
+  const T* src = h + ((int64_t)b * N + node) * H;
+  for (int64_t e = threadIdx.x; e < H; e += 256) out[(int64_t)b * H + e] = src[e];
+}
+
+}  // namespace medusa
+
+#define MEDUSA_DT_DISPATCH(dt, ...)                 \
+  do {                                              \
+    if ((dt) == MEDUSA_BF16) {                      \
+      using T = medusa::bf16_t;                     \
+      __VA_ARGS__;                                  \
+    } else {                                        \
+      using T = float;                              \
+      __VA_ARGS__;                                  \
+    }                                               \
+  } while (0)
+
+extern "C" int32_t medusa_embed(const int32_t* tokens, int64_t M, const void* table, int64_t V,
+                                int64_t H, int32_t dt, float* out, void* stream) {
+  using namespace medusa_host;
+  MEDUSA_REQUIRE(dt == MEDUSA_F32 || dt == MEDUSA_BF16, MEDUSA_ERR_UNSUPPORTED, "medusa_embed: dtype");
+  MEDUSA_REQUIRE(M >= 0 && V >= 1 && H >= 1 && M <= INT32_MAX, MEDUSA_ERR_INVALID_ARG,
+                 "medusa_embed: bad sizes");
+  if (M == 0) return MEDUSA_OK;
+  MEDUSA_REQUIRE(tokens && table && out, MEDUSA_ERR_INVALID_ARG, "medusa_embed: NULL pointer");
+  MEDUSA_DT_DISPATCH(dt, hipLaunchKernelGGL(medusa::embed_kernel<T>, dim3((unsigned)M), dim3(256), 0,
+                                            (hipStream_t)stream, tokens, (const T*)table, H, out));
+  return check_launch("medusa_embed");
+}
+
+extern "C" int32_t medusa_rmsnorm(const float* x, int64_t M, int64_t H, const void* gain, float eps,
+                                  int32_t dt, void* out, void* stream) {
+  using namespace medusa_host;
+  MEDUSA_REQUIRE(dt == MEDUSA_F32 || dt == MEDUSA_BF16, MEDUSA_ERR_UNSUPPORTED, "medusa_rmsnorm: dtype");
+  MEDUSA_REQUIRE(M >= 0 && H >= 1 && M <= INT32_MAX && eps >= 0.f, MEDUSA_ERR_INVALID_ARG,
+                 "medusa_rmsnorm: bad sizes");
+  if (M == 0) return MEDUSA_OK;
+  MEDUSA_REQUIRE(x && out, MEDUSA_ERR_INVALID_ARG, "medusa_rmsnorm: NULL pointer");
+  MEDUSA_DT_DISPATCH(dt, hipLaunchKernelGGL(medusa::rmsnorm_kernel<T>, dim3((unsigned)M), dim3(256), 0,
+                                            (hipStream_t)stream, x, H, (const T*)gain, eps, (T*)out));
+  return check_launch("medusa_rmsnorm");
+}
+
+extern "C" int32_t medusa_qkv_rope(const void* qkv, int64_t M, int32_t Hq, int32_t Hkv, int32_t D,
+                                   const int32_t* pos, float base, int32_t dt, void* q, void* k,
+                                   void* v, void* stream) {
+  using namespace medusa_host;
+  MEDUSA_REQUIRE(dt == MEDUSA_F32 || dt == MEDUSA_BF16, MEDUSA_ERR_UNSUPPORTED, "medusa_qkv_rope: dtype");
+  MEDUSA_REQUIRE(D >= 2 && D <= 128 && D % 2 == 0, MEDUSA_ERR_UNSUPPORTED,
+                 "medusa_qkv_rope: head dim %d", D);
+  MEDUSA_REQUIRE(M >= 0 && M <= INT32_MAX && Hq >= 1 && Hkv >= 1 && base > 1.f,
+                 MEDUSA_ERR_INVALID_ARG, "medusa_qkv_rope: bad sizes or base");
+  if (M == 0) return MEDUSA_OK;
+  MEDUSA_REQUIRE(qkv && pos && q && k && v, MEDUSA_ERR_INVALID_ARG, "medusa_qkv_rope: NULL pointer");
+  const double lb = log2((double)base);
+  MEDUSA_DT_DISPATCH(dt, hipLaunchKernelGGL(medusa::qkv_rope_kernel<T>, dim3((unsigned)M), dim3(256), 0,
+                                            (hipStream_t)stream, (const T*)qkv, Hq, Hkv, D, pos, lb,
+                                            (T*)q, (T*)k, (T*)v));
+  return check_launch("medusa_qkv_rope");
+}
+
+extern "C" int32_t medusa_swiglu(const void* gu, int64_t M, int64_t F, int32_t dt, void* out,
+                                 void* stream) {
+  using namespace medusa_host;
+  MEDUSA_REQUIRE(dt == MEDUSA_F32 || dt == MEDUSA_BF16, MEDUSA_ERR_UNSUPPORTED, "medusa_swiglu: dtype");
+  MEDUSA_REQUIRE(M >= 0 && M <= INT32_MAX && F >= 1, MEDUSA_ERR_INVALID_ARG, "medusa_swiglu: bad sizes");
+  if (M == 0) return MEDUSA_OK;
+  MEDUSA_REQUIRE(gu && out, MEDUSA_ERR_INVALID_ARG, "medusa_swiglu: NULL pointer");
+  MEDUSA_DT_DISPATCH(dt, hipLaunchKernelGGL(medusa::swiglu_kernel<T>, dim3((unsigned)M), dim3(256), 0,
+                                            (hipStream_t)stream, (const T*)gu, F, (T*)out));
+  return check_launch("medusa_swiglu");
+}
+
+extern "C" int32_t medusa_gather_rows(const void* h, int32_t B, int32_t N, int64_t H,
+                                      const int32_t* path, const int32_t* accept_len, int32_t K,
+                                      int32_t dt, void* out, void* stream) {
+  using namespace medusa_host;
+  MEDUSA_REQUIRE(dt == MEDUSA_F32 || dt == MEDUSA_BF16, MEDUSA_ERR_UNSUPPORTED, "medusa_gather_rows: dtype");
+  MEDUSA_REQUIRE(B >= 0 && N >= 1 && N <= MEDUSA_MAX_NODES && H >= 1 && K >= 0 &&
+                     K <= MEDUSA_MAX_NODES - 1,
+                 MEDUSA_ERR_INVALID_ARG, "medusa_gather_rows: bad sizes");
+  if (B == 0) return MEDUSA_OK;
+  MEDUSA_REQUIRE(h && path && accept_len && out, MEDUSA_ERR_INVALID_ARG,
+                 "medusa_gather_rows: NULL pointer");
+  MEDUSA_DT_DISPATCH(dt, hipLaunchKernelGGL(medusa::gather_rows_kernel<T>, dim3(B), dim3(256), 0,
+                                            (hipStream_t)stream, (const T*)h, N, H, path, accept_len,
+                                            K, (T*)out));
+  return check_launch("medusa_gather_rows");
+}

@@ -1,0 +1,105 @@
+// Internal helpers shared by the HIP kernels of libmedusa (CDNA4 / gfx950).
+//
+// Storage types: MEDUSA_F32 tensors are `float`, MEDUSA_BF16 tensors are raw
+// bfloat16 bit patterns (`uint16_t`).  All arithmetic is fp32; bf16 values are
+// widened exactly and narrowed round-to-nearest-even.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#include "../../include/medusa.h"
+
+namespace medusa {
+
+typedef uint16_t bf16_t;
+
+// Native clang vectors for register data: selects and element access stay in
+// VGPRs (HIP's uint4/float4 are structs, and a select on them goes through
+// scratch memory).
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf2f(bf16_t h) { return __uint_as_float(((uint32_t)h) << 16); }
+
+__device__ __forceinline__ bf16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (bf16_t)(u >> 16);
+}
+
+// Pack two fp32 values into one dword of two bf16 (lo = a, hi = b), RNE.
+__device__ __forceinline__ uint32_t pack_bf2(float a, float b) {
+  return (uint32_t)f2bf(a) | ((uint32_t)f2bf(b) << 16);
+}
+
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  static __device__ __forceinline__ float load(const float* p, size_t i) { return p[i]; }
+  static __device__ __forceinline__ void store(float* p, size_t i, float v) { p[i] = v; }
+  static constexpr int per16 = 4;  // elements per 16-byte vector
+};
+template <> struct Elem<bf16_t> {
+  static __device__ __forceinline__ float load(const bf16_t* p, size_t i) { return bf2f(p[i]); }
+  static __device__ __forceinline__ void store(bf16_t* p, size_t i, float v) { p[i] = f2bf(v); }
+  static constexpr int per16 = 8;
+};
+
+template <typename T> __device__ __forceinline__ float ld(const T* p, size_t i) { return Elem<T>::load(p, i); }
+template <typename T> __device__ __forceinline__ void st(T* p, size_t i, float v) { Elem<T>::store(p, i, v); }
+
+// ---------------------------------------------------------------------------
+// MFMA wrappers.  Layout of a 16x16 fp32 result (both wrappers): lane l holds
+// column (l % 16) and rows 4*(l/16) + r in element r.  For the operands, lane
+// l supplies row (l % 16) of A and column (l % 16) of B; the lanes with the
+// same l/16 supply the same contraction indices for A and B.
+// ---------------------------------------------------------------------------
+
+// bf16: one 16-byte vector per lane = 8 contraction elements (16x16x32).
+__device__ __forceinline__ f32x4 mfma_bf16_16x16x32(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+// bf16: 4 contraction elements per lane (16x16x16); lane l's elements are
+// contraction indices 4*(l/16)+r.
+__device__ __forceinline__ f32x4 mfma_bf16_16x16x16(u32x2 a, u32x2 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, a),
+                                                   __builtin_bit_cast(i16x4, b), c, 0, 0, 0);
+}
+// fp32: one contraction element per lane (16x16x4), index l/16.
+__device__ __forceinline__ f32x4 mfma_f32_16x16x4(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float silu_f(float z) { return z / (1.0f + expf(-z)); }
+
+// Wavefront-wide reductions (64 lanes).
+__device__ __forceinline__ float wave_max(float v) {
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+}  // namespace medusa
+
+// ---------------------------------------------------------------------------
+// Host side: status handling shared by the entry points.
+// ---------------------------------------------------------------------------
+namespace medusa_host {
+void set_error(const char* fmt, ...);
+int32_t fail(int32_t status, const char* fmt, ...);
+int32_t check_launch(const char* what);
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+}  // namespace medusa_host
+
+#define MEDUSA_REQUIRE(cond, status, ...)                                    \
+  do {                                                                       \
+    if (!(cond)) return medusa_host::fail((status), __VA_ARGS__);            \
+  } while (0)

@@ -1,0 +1,254 @@
+// Skinny projection GEMM  Y = epilogue(X W^T)  on MFMA (gfx950).
+//
+// Serves the heads' two layers ("Medusa Heads", section "Come le teste
+// prevedono i token successivi": a residual SiLU feed-forward layer, then a
+// vocabulary projection) and every projection of the verification forward
+// pass.  At decode shapes (M <= 64 rows) the work is bound by streaming W
+// from HBM, so the design goal is many independent 16-byte weight loads in
+// flight, not MFMA throughput:
+//   * one workgroup = 4 waves computes a [16*MB x 32] output tile over the
+//     full contraction; the contraction steps are split evenly over the
+//     waves, each wave streaming its slice of 32 weight rows straight from
+//     HBM into registers (no LDS for W: no wave shares W data);
+//   * the 4 partial tiles are added in LDS in wave order, so an output's
+//     reduction order depends on Kd only (never on M or the batch);
+//   * the epilogue (bias + SiLU + residual, residual add, SwiGLU) is fused.
+#include "common.h"
+
+namespace medusa {
+
+template <typename T> struct GemmTraits;
+template <> struct GemmTraits<bf16_t> {
+  static constexpr int per16 = 8;   // contraction elements per 16-byte vector
+  static __device__ __forceinline__ f32x4 mma(u32x4 a, u32x4 b, f32x4 c) {
+    return mfma_bf16_16x16x32(a, b, c);
+  }
+};
+template <> struct GemmTraits<float> {
+  static constexpr int per16 = 4;
+  static __device__ __forceinline__ f32x4 mma(u32x4 a, u32x4 b, f32x4 c) {
+    c = mfma_f32_16x16x4(__uint_as_float(a.x), __uint_as_float(b.x), c);
+    c = mfma_f32_16x16x4(__uint_as_float(a.y), __uint_as_float(b.y), c);
+    c = mfma_f32_16x16x4(__uint_as_float(a.z), __uint_as_float(b.z), c);
+    c = mfma_f32_16x16x4(__uint_as_float(a.w), __uint_as_float(b.w), c);
+    return c;
+  }
+};
+
+constexpr int GEMM_WAVES = 4;
+constexpr int GEMM_NB = 2;          // 16-column blocks per tile (32 W rows)
+constexpr int GEMM_U = 2;           // contraction steps per pipeline stage
+
+template <typename T, int MB, int EPI>
+__global__ __launch_bounds__(256) void gemm_kernel(const T* __restrict__ X, int64_t xbs,
+                                                   int M, int Kd, const T* __restrict__ W,
+                                                   int Nw, const T* __restrict__ bias,
+                                                   const void* aux, void* Y, int y_f32) {
+  using TR = GemmTraits<T>;
+  constexpr int P16 = TR::per16;
+  constexpr int KSTEP = 4 * P16;
+  constexpr int TM = 16 * MB, TN = 16 * GEMM_NB;
+  constexpr int LDR = TN + 1;  // padded LDS row (floats)
+  __shared__ float red[GEMM_WAVES][TM * LDR];
+
+  const int g = blockIdx.z;
+  const int n0 = blockIdx.x * TN;
+  const int m0 = blockIdx.y * TM;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int lr = lane & 15, lg = lane >> 4;
+
+  const T* Xg = X + (int64_t)g * xbs;
+  const T* Wg = W + (int64_t)g * Nw * Kd;
+  const T* xrow[MB];
+  const T* wrow[GEMM_NB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    int r = min(m0 + mb * 16 + lr, M - 1);
+    xrow[mb] = Xg + (int64_t)r * Kd + lg * P16;
+  }
+#pragma unroll
+  for (int nb = 0; nb < GEMM_NB; ++nb) {
+    int r = min(n0 + nb * 16 + lr, Nw - 1);
+    wrow[nb] = Wg + (int64_t)r * Kd + lg * P16;
+  }
+
+  const int nsteps = (Kd + KSTEP - 1) / KSTEP;
+  const int s_beg = (int)((int64_t)nsteps * wave / GEMM_WAVES);
+  const int s_end = (int)((int64_t)nsteps * (wave + 1) / GEMM_WAVES);
+  const int kmax = Kd - lg * P16;  // this lane's vector at step s is valid iff s*KSTEP < kmax
+
+  f32x4 acc[MB][GEMM_NB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < GEMM_NB; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  u32x4 fa[2][GEMM_U][MB], fb[2][GEMM_U][GEMM_NB];
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+  auto load = [&](int buf, int s) {
+#pragma unroll
+    for (int u = 0; u < GEMM_U; ++u) {
+      const int st = s + u;
+      const int k = st * KSTEP;
+      const bool ok = (st < s_end) && (k < kmax);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+        fa[buf][u][mb] = ok ? *reinterpret_cast<const u32x4*>(xrow[mb] + k) : zero;
+#pragma unroll
+      for (int nb = 0; nb < GEMM_NB; ++nb)
+        fb[buf][u][nb] = ok ? *reinterpret_cast<const u32x4*>(wrow[nb] + k) : zero;
+    }
+  };
+  auto compute = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < GEMM_U; ++u)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < GEMM_NB; ++nb)
+          acc[mb][nb] = TR::mma(fa[buf][u][mb], fb[buf][u][nb], acc[mb][nb]);
+  };
+
+  if (s_beg < s_end) {
+    // two register stages, ping-pong unrolled so every index is static
+    load(0, s_beg);
+    int s = s_beg;
+    while (true) {
+      if (s + GEMM_U < s_end) load(1, s + GEMM_U);
+      compute(0);
+      s += GEMM_U;
+      if (s >= s_end) break;
+      if (s + GEMM_U < s_end) load(0, s + GEMM_U);
+      compute(1);
+      s += GEMM_U;
+      if (s >= s_end) break;
+    }
+  }
+
+  // partial tiles -> LDS
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < GEMM_NB; ++nb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        red[wave][(mb * 16 + lg * 4 + r) * LDR + nb * 16 + lr] = acc[mb][nb][r];
+  __syncthreads();
+
+  if (EPI == MEDUSA_EPI_SWIGLU) {
+    // tile columns [0,16) are gate rows, [16,32) the matching up rows
+    const int F = Nw / 2;
+    T* Yg = reinterpret_cast<T*>(Y) + (int64_t)g * M * F;
+    for (int e = threadIdx.x; e < TM * 16; e += 256) {
+      const int row = e >> 4, c = e & 15;
+      const int m = m0 + row, f = (n0 >> 1) + c;
+      if (m >= M || f >= F) continue;
+      float gte = 0.f, up = 0.f;
+#pragma unroll
+      for (int w = 0; w < GEMM_WAVES; ++w) {
+        gte += red[w][row * LDR + c];
+        up += red[w][row * LDR + 16 + c];
+      }
+      st<T>(Yg, (int64_t)m * F + f, silu_f(gte) * up);
+    }
+    return;
+  }
+
+  for (int e = threadIdx.x; e < TM * TN; e += 256) {
+    const int row = e / TN, col = e % TN;
+    const int m = m0 + row, n = n0 + col;
+    if (m >= M || n >= Nw) continue;
+    float v = red[0][row * LDR + col];
+#pragma unroll
+    for (int w = 1; w < GEMM_WAVES; ++w) v += red[w][row * LDR + col];
+    const int64_t o = (int64_t)g * M * Nw + (int64_t)m * Nw + n;
+    if (EPI == MEDUSA_EPI_NONE) {
+      if (y_f32) reinterpret_cast<float*>(Y)[o] = v;
+      else st<T>(reinterpret_cast<T*>(Y), o, v);
+    } else if (EPI == MEDUSA_EPI_BIAS_SILU_RES) {
+      const T* R = reinterpret_cast<const T*>(aux) + (int64_t)g * xbs;
+      const float res = ld<T>(R, (int64_t)m * Nw + n);
+      const float b = bias ? ld<T>(bias, (int64_t)g * Nw + n) : 0.f;
+      st<T>(reinterpret_cast<T*>(Y), o, res + silu_f(v + b));
+    } else {  // MEDUSA_EPI_RES_ADD_F32
+      const float res = reinterpret_cast<const float*>(aux)[(int64_t)m * Nw + n];
+      reinterpret_cast<float*>(Y)[(int64_t)m * Nw + n] = res + v;
+    }
+  }
+}
+
+template <typename T, int EPI>
+static void launch_gemm_t(const void* X, int64_t xbs, int64_t M, int64_t Kd, const void* W,
+                          int64_t Nw, int batch, const void* bias, const void* aux, void* Y,
+                          int y_f32, hipStream_t st) {
+  const int TN = 16 * GEMM_NB;
+  auto go = [&](auto mbc) {
+    constexpr int MB = decltype(mbc)::value;
+    dim3 grid((unsigned)((Nw + TN - 1) / TN), (unsigned)((M + 16 * MB - 1) / (16 * MB)),
+              (unsigned)batch);
+    hipLaunchKernelGGL((gemm_kernel<T, MB, EPI>), grid, dim3(256), 0, st,
+                       reinterpret_cast<const T*>(X), xbs, (int)M, (int)Kd,
+                       reinterpret_cast<const T*>(W), (int)Nw, reinterpret_cast<const T*>(bias),
+                       aux, Y, y_f32);
+  };
+  if (M <= 16) go(std::integral_constant<int, 1>());
+  else if (M <= 32) go(std::integral_constant<int, 2>());
+  else go(std::integral_constant<int, 4>());
+}
+
+}  // namespace medusa
+
+namespace medusa_host {
+// Internal launcher shared with medusa_heads (arguments already validated).
+void launch_gemm(const void* X, int64_t xbs, int64_t M, int64_t Kd, const void* W, int64_t Nw,
+                 int batch, int dt, int epi, const void* bias, const void* aux, void* Y,
+                 int y_f32, hipStream_t st) {
+  using namespace medusa;
+#define MEDUSA_GEMM_CASE(T, E)                                                              \
+  launch_gemm_t<T, E>(X, xbs, M, Kd, W, Nw, batch, bias, aux, Y, y_f32, st)
+#define MEDUSA_GEMM_EPI(T)                                                                  \
+  switch (epi) {                                                                            \
+    case MEDUSA_EPI_NONE: MEDUSA_GEMM_CASE(T, MEDUSA_EPI_NONE); break;                      \
+    case MEDUSA_EPI_BIAS_SILU_RES: MEDUSA_GEMM_CASE(T, MEDUSA_EPI_BIAS_SILU_RES); break;    \
+    case MEDUSA_EPI_RES_ADD_F32: MEDUSA_GEMM_CASE(T, MEDUSA_EPI_RES_ADD_F32); break;        \
+    default: MEDUSA_GEMM_CASE(T, MEDUSA_EPI_SWIGLU); break;                                 \
+  }
+  if (dt == MEDUSA_BF16) { MEDUSA_GEMM_EPI(bf16_t) } else { MEDUSA_GEMM_EPI(float) }
+#undef MEDUSA_GEMM_EPI
+#undef MEDUSA_GEMM_CASE
+}
+}  // namespace medusa_host
+
+extern "C" int32_t medusa_linear(const void* X, int64_t x_bstride, int64_t M, int64_t Kd,
+                                 const void* W, int64_t N, int32_t batch, int32_t dt,
+                                 int32_t epilogue, const void* bias, const void* aux, void* Y,
+                                 int32_t y_f32, void* stream) {
+  using namespace medusa_host;
+  MEDUSA_REQUIRE(dt == MEDUSA_F32 || dt == MEDUSA_BF16, MEDUSA_ERR_UNSUPPORTED,
+                 "medusa_linear: unknown dtype %d", dt);
+  MEDUSA_REQUIRE(epilogue >= MEDUSA_EPI_NONE && epilogue <= MEDUSA_EPI_SWIGLU,
+                 MEDUSA_ERR_INVALID_ARG, "medusa_linear: unknown epilogue %d", epilogue);
+  MEDUSA_REQUIRE(M >= 0 && Kd > 0 && N > 0 && batch >= 1 && x_bstride >= 0,
+                 MEDUSA_ERR_INVALID_ARG, "medusa_linear: bad sizes M=%lld Kd=%lld N=%lld batch=%d",
+                 (long long)M, (long long)Kd, (long long)N, batch);
+  MEDUSA_REQUIRE(M <= INT32_MAX && Kd <= INT32_MAX && N <= INT32_MAX, MEDUSA_ERR_UNSUPPORTED,
+                 "medusa_linear: sizes above 2^31");
+  const int p16 = dt == MEDUSA_BF16 ? 8 : 4;
+  MEDUSA_REQUIRE(Kd % p16 == 0 && x_bstride % p16 == 0, MEDUSA_ERR_UNSUPPORTED,
+                 "medusa_linear: Kd and x_bstride must be multiples of %d", p16);
+  if (M == 0) return MEDUSA_OK;
+  MEDUSA_REQUIRE(X && W && Y, MEDUSA_ERR_INVALID_ARG, "medusa_linear: NULL X, W or Y");
+  MEDUSA_REQUIRE(((uintptr_t)X | (uintptr_t)W) % 16 == 0, MEDUSA_ERR_INVALID_ARG,
+                 "medusa_linear: X and W must be 16-byte aligned");
+  if (epilogue == MEDUSA_EPI_BIAS_SILU_RES)
+    MEDUSA_REQUIRE(aux != NULL, MEDUSA_ERR_INVALID_ARG, "medusa_linear: residual (aux) is NULL");
+  if (epilogue == MEDUSA_EPI_RES_ADD_F32)
+    MEDUSA_REQUIRE(aux != NULL && batch == 1, MEDUSA_ERR_INVALID_ARG,
+                   "medusa_linear: residual add needs aux and batch == 1");
+  if (epilogue == MEDUSA_EPI_SWIGLU)
+    MEDUSA_REQUIRE(N % 32 == 0, MEDUSA_ERR_INVALID_ARG,
+                   "medusa_linear: SwiGLU needs N (gate+up rows) to be a multiple of 32");
+  launch_gemm(X, x_bstride, M, Kd, W, N, batch, dt, epilogue, bias, aux, Y, y_f32,
+              (hipStream_t)stream);
+  return check_launch("medusa_linear");
+}

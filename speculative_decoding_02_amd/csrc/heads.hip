@@ -1,0 +1,66 @@
+// medusa_heads: K Medusa heads on M hidden rows, then per-head top-k.
+// ("Medusa Heads", section "Come le teste prevedono i token successivi":
+// head k = one feed-forward layer with SiLU and a residual connection, then a
+// vocabulary projection, all reading the hidden state lm_head reads.)
+//
+// Two batched GEMM launches (batch = heads):
+//   U_k      = X + SiLU(X W1_k^T + b1_k)     fused epilogue, U kept in ws
+//   logits_k = U_k W2_k^T                     fp32
+// then one top-k launch over the K*M logits rows.  Stage 2 and a plain
+// lm_head projection run the same kernel with the same contraction length,
+// so zero-initialised heads reproduce lm_head's logits bit for bit.
+#include "common.h"
+
+namespace medusa_host {
+void launch_gemm(const void* X, int64_t xbs, int64_t M, int64_t Kd, const void* W, int64_t Nw,
+                 int batch, int dt, int epi, const void* bias, const void* aux, void* Y,
+                 int y_f32, hipStream_t st);
+void launch_topk(const float* logits, int64_t R, int64_t V, int k, int* ids, float* vals,
+                 hipStream_t st);
+}  // namespace medusa_host
+
+extern "C" size_t medusa_heads_ws(int64_t M, int64_t H, int32_t K, int64_t V, int32_t topk,
+                                  int32_t dt) {
+  (void)topk;
+  if (M < 0 || H < 0 || K < 0 || V < 0) return 0;
+  const size_t es = dt == MEDUSA_BF16 ? 2 : 4;
+  return medusa_host::align_up((size_t)K * M * H * es, 256) +
+         medusa_host::align_up((size_t)K * M * V * 4, 256);
+}
+
+extern "C" int32_t medusa_heads(const void* X, int64_t M, int64_t H, int32_t K, const void* W1,
+                                const void* b1, const void* W2, int64_t V, int32_t dt,
+                                float* logits, int32_t topk, int32_t* topk_ids,
+                                float* topk_vals, void* ws, size_t ws_bytes, void* stream) {
+  using namespace medusa_host;
+  MEDUSA_REQUIRE(dt == MEDUSA_F32 || dt == MEDUSA_BF16, MEDUSA_ERR_UNSUPPORTED,
+                 "medusa_heads: unknown dtype %d", dt);
+  MEDUSA_REQUIRE(M >= 0 && H > 0 && V > 0 && M <= INT32_MAX && H <= INT32_MAX && V <= INT32_MAX,
+                 MEDUSA_ERR_INVALID_ARG, "medusa_heads: bad sizes M=%lld H=%lld V=%lld",
+                 (long long)M, (long long)H, (long long)V);
+  MEDUSA_REQUIRE(K >= 1 && K <= MEDUSA_MAX_HEADS, MEDUSA_ERR_UNSUPPORTED,
+                 "medusa_heads: K=%d outside [1, %d]", K, MEDUSA_MAX_HEADS);
+  MEDUSA_REQUIRE(topk >= 0 && topk <= MEDUSA_MAX_TOPK && topk <= V, MEDUSA_ERR_UNSUPPORTED,
+                 "medusa_heads: topk=%d outside [0, min(64, V)]", topk);
+  const int p16 = dt == MEDUSA_BF16 ? 8 : 4;
+  MEDUSA_REQUIRE(H % p16 == 0, MEDUSA_ERR_UNSUPPORTED, "medusa_heads: H must be a multiple of %d", p16);
+  if (M == 0) return MEDUSA_OK;
+  MEDUSA_REQUIRE(X && W1 && W2, MEDUSA_ERR_INVALID_ARG, "medusa_heads: NULL X, W1 or W2");
+  MEDUSA_REQUIRE(((uintptr_t)X | (uintptr_t)W1 | (uintptr_t)W2) % 16 == 0, MEDUSA_ERR_INVALID_ARG,
+                 "medusa_heads: X, W1, W2 must be 16-byte aligned");
+  MEDUSA_REQUIRE(topk == 0 || (topk_ids && topk_vals), MEDUSA_ERR_INVALID_ARG,
+                 "medusa_heads: NULL top-k outputs");
+  const size_t need = medusa_heads_ws(M, H, K, V, topk, dt);
+  MEDUSA_REQUIRE(ws != NULL && ws_bytes >= need, MEDUSA_ERR_WORKSPACE,
+                 "medusa_heads: workspace %zu < %zu bytes", ws_bytes, need);
+  MEDUSA_REQUIRE((uintptr_t)ws % 256 == 0, MEDUSA_ERR_INVALID_ARG,
+                 "medusa_heads: ws must be 256-byte aligned");
+  const size_t es = dt == MEDUSA_BF16 ? 2 : 4;
+  char* U = (char*)ws;
+  float* lg = logits ? logits : (float*)(U + align_up((size_t)K * M * H * es, 256));
+  hipStream_t st = (hipStream_t)stream;
+  launch_gemm(X, 0, M, H, W1, H, K, dt, MEDUSA_EPI_BIAS_SILU_RES, b1, X, U, 0, st);
+  launch_gemm(U, M * H, M, H, W2, V, K, dt, MEDUSA_EPI_NONE, nullptr, nullptr, lg, 1, st);
+  if (topk > 0) launch_topk(lg, (int64_t)K * M, V, topk, topk_ids, topk_vals, st);
+  return check_launch("medusa_heads");
+}

@@ -1,0 +1,456 @@
+// medusa_tree_attention: one tree-masked attention pass over a paged KV cache
+// plus the tree's own keys ("Medusa Heads", section "Attenzione sull'albero e
+// accettazione": every candidate token is appended at once and the mask lets
+// each token see only its ancestors, so all branches are verified in one pass;
+// arXiv abstract page: tree-based attention).
+//
+// Work decomposition (gfx950, 64-wide waves):
+//   grid = (splits, Hq, B); a workgroup owns one contiguous key range of one
+//   (sequence, query head): cached keys 0..ctx-1 followed by the N tree keys.
+//   Its 4 waves each own 16 tree nodes (query rows) and sweep the range in
+//   tiles of 64 keys.
+//   * K tile [64 x D] and the TRANSPOSED V tile [D x 64] are staged in LDS
+//     (16-byte global loads; the next tile is prefetched into registers while
+//     the current one is computed).
+//   * S^T = K Q^T on MFMA: the result lands with lane l holding node l%16 and
+//     keys 4*(l/16)+r, which is exactly the operand layout of P^T in
+//     O^T += V^T P^T, so probabilities never leave registers.
+//   * online softmax in fp32 (base-2 exponent), per node; tree keys are
+//     kept iff their bit is set in the node's uint64 ancestor mask.
+//   * the tree keys' K/V are stored into cache slots ctx..ctx+N-1 by the
+//     workgroup that reads them (first query head of each kv group).
+//   * splits write (max, sum, unnormalised O) partials; the last split of a
+//     (sequence, head) to finish - found with one atomic counter - merges
+//     them in fixed split order and writes O.  Deterministic.
+#include "common.h"
+
+namespace medusa {
+
+constexpr int ATT_TILE = 64;
+constexpr int ATT_THREADS = 256;
+
+template <typename T, int D>
+struct AttnCfg {
+  static constexpr int P16 = 16 / (int)sizeof(T);       // elements per 16-byte vector
+  static constexpr int LDK = D + P16;                    // K row, padded by 16 B
+  static constexpr int LDV = ATT_TILE + 4;               // V^T row, padded
+  static constexpr int QSTEPS = D / (4 * P16);           // MFMA steps over the head dim
+  static constexpr int KCHUNKS = ATT_TILE * D / P16;     // 16-byte chunks per K tile
+  static constexpr int KPT = KCHUNKS / ATT_THREADS;      // chunks per thread
+  static constexpr int VGROUPS = (ATT_TILE / 4) * (D / P16);  // (4 keys x P16 dims) groups
+  static constexpr int VPT = (VGROUPS + ATT_THREADS - 1) / ATT_THREADS;
+  static_assert(KCHUNKS % ATT_THREADS == 0, "K tile chunks");
+};
+
+// component i (compile-time after unrolling) of a 16-byte register vector
+__device__ __forceinline__ uint32_t u4c(u32x4 v, int i) { return v[i]; }
+
+template <typename T> struct AttnMma;
+template <> struct AttnMma<bf16_t> {
+  // scores: K rows (A) x Q rows (B), 8 dims per lane
+  static __device__ __forceinline__ f32x4 qk(u32x4 a, u32x4 b, f32x4 c) { return mfma_bf16_16x16x32(a, b, c); }
+};
+template <> struct AttnMma<float> {
+  static __device__ __forceinline__ f32x4 qk(u32x4 a, u32x4 b, f32x4 c) {
+    c = mfma_f32_16x16x4(__uint_as_float(a.x), __uint_as_float(b.x), c);
+    c = mfma_f32_16x16x4(__uint_as_float(a.y), __uint_as_float(b.y), c);
+    c = mfma_f32_16x16x4(__uint_as_float(a.z), __uint_as_float(b.z), c);
+    c = mfma_f32_16x16x4(__uint_as_float(a.w), __uint_as_float(b.w), c);
+    return c;
+  }
+};
+
+struct AttnArgs {
+  const void* Q;
+  const void* Kt;
+  const void* Vt;
+  void* Kc;
+  void* Vc;
+  const int* page_table;
+  const int* ctx;
+  const uint64_t* mask;
+  void* O;
+  int* counters;     // [B*Hq]
+  float2* ml;        // [B*Hq*S*N]  (running max in log2 units, sum)
+  float* opart;      // [B*Hq*S*N*D]
+  int max_pages, P, B, N, Hq, Hkv, chunk;  // chunk = keys per split (multiple of 64)
+  float scale_log2;
+};
+
+template <typename T, int D>
+__global__ __launch_bounds__(ATT_THREADS) void tree_attention_kernel(AttnArgs a) {
+  using C = AttnCfg<T, D>;
+  constexpr int P16 = C::P16;
+  __shared__ __attribute__((aligned(16))) T Ks[ATT_TILE * C::LDK];
+  __shared__ __attribute__((aligned(16))) T Vs[D * C::LDV];
+  __shared__ int s_last;
+
+  const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int S = gridDim.x;
+  const int N = a.N;
+  const int ctxb = a.ctx[b];
+  const int total = ctxb + N;
+  const int k_beg = s * a.chunk;
+  if (k_beg >= total) return;
+  const int k_end = min(k_beg + a.chunk, total);
+  const int nsplit = (total + a.chunk - 1) / a.chunk;
+  const int group = a.Hq / a.Hkv;
+  const int kvh = h / group;
+  const bool appender = (h % group) == 0;
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+  const int node = wave * 16 + lr;
+  const bool wave_active = wave * 16 < N;
+  const int nodec = min(node, N - 1);
+
+  const T* Qp = reinterpret_cast<const T*>(a.Q);
+  const T* Ktp = reinterpret_cast<const T*>(a.Kt);
+  const T* Vtp = reinterpret_cast<const T*>(a.Vt);
+  T* Kcp = reinterpret_cast<T*>(a.Kc);
+  T* Vcp = reinterpret_cast<T*>(a.Vc);
+  const int* pt = a.page_table + (int64_t)b * a.max_pages;
+
+  // element offset of key j's row for kv head kvh (cache slot or tree node)
+  auto cache_off = [&](int j) -> int64_t {
+    const int page = pt[j / a.P];
+    return (((int64_t)page * a.Hkv + kvh) * a.P + (j % a.P)) * D;
+  };
+  auto tree_off = [&](int j) -> int64_t {
+    return (((int64_t)b * N + (j - ctxb)) * a.Hkv + kvh) * D;
+  };
+
+  // ---- this wave's queries, B operand of S^T = K Q^T ----
+  u32x4 qf[C::QSTEPS];
+  {
+    const T* qrow = Qp + (((int64_t)b * N + nodec) * a.Hq + h) * D;
+#pragma unroll
+    for (int st = 0; st < C::QSTEPS; ++st)
+      qf[st] = *reinterpret_cast<const u32x4*>(qrow + st * 4 * P16 + lg * P16);
+  }
+  const uint64_t mrow = a.mask[(int64_t)b * N + nodec];
+
+  // ---- tile loaders ----
+  u32x4 kreg[C::KPT];
+  u32x4 vreg[C::VPT][4];
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+
+  // Branch-free loads: out-of-range keys read a valid row (clamped index) and
+  // are replaced by zeros, so the unrolled loops keep their registers.
+  auto gload = [&](int tile0) {
+#pragma unroll
+    for (int i = 0; i < C::KPT; ++i) {
+      const int c = tid + i * ATT_THREADS;
+      const int key = c / (D / P16), part = c % (D / P16);
+      const int j = tile0 + key, jj = min(j, k_end - 1);
+      const T* src = (jj < ctxb ? Kcp + cache_off(jj) : Ktp + tree_off(jj)) + part * P16;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(src);
+      kreg[i] = j < k_end ? v : zero;
+    }
+#pragma unroll
+    for (int i = 0; i < C::VPT; ++i) {
+      const int g = min(tid + i * ATT_THREADS, C::VGROUPS - 1);
+      const int kg = g / (D / P16), dg = g % (D / P16);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int j = tile0 + kg * 4 + r, jj = min(j, k_end - 1);
+        const T* src = (jj < ctxb ? Vcp + cache_off(jj) : Vtp + tree_off(jj)) + dg * P16;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(src);
+        vreg[i][r] = j < k_end ? v : zero;
+      }
+    }
+  };
+
+  auto lds_store = [&](int tile0) {
+#pragma unroll
+    for (int i = 0; i < C::KPT; ++i) {
+      const int c = tid + i * ATT_THREADS;
+      const int key = c / (D / P16), part = c % (D / P16);
+      *reinterpret_cast<u32x4*>(&Ks[key * C::LDK + part * P16]) = kreg[i];
+      const int j = tile0 + key;
+      if (appender && j >= ctxb && j < k_end)
+        *reinterpret_cast<u32x4*>(Kcp + cache_off(j) + part * P16) = kreg[i];
+    }
+#pragma unroll
+    for (int i = 0; i < C::VPT; ++i) {
+      const int g = tid + i * ATT_THREADS;
+      if (g < C::VGROUPS) {
+        const int kg = g / (D / P16), dg = g % (D / P16);
+        const int key0 = kg * 4, d0 = dg * P16;
+        if constexpr (sizeof(T) == 2) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int sh = (e & 1) * 16, wi = e >> 1;
+            u32x2 v;
+            v.x = ((u4c(vreg[i][0], wi) >> sh) & 0xffffu) | (((u4c(vreg[i][1], wi) >> sh) & 0xffffu) << 16);
+            v.y = ((u4c(vreg[i][2], wi) >> sh) & 0xffffu) | (((u4c(vreg[i][3], wi) >> sh) & 0xffffu) << 16);
+            *reinterpret_cast<u32x2*>(&Vs[(d0 + e) * C::LDV + key0]) = v;
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            u32x4 v = {u4c(vreg[i][0], e), u4c(vreg[i][1], e), u4c(vreg[i][2], e), u4c(vreg[i][3], e)};
+            *reinterpret_cast<u32x4*>(&Vs[(d0 + e) * C::LDV + key0]) = v;
+          }
+        }
+        if (appender) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int j = tile0 + key0 + r;
+            if (j >= ctxb && j < k_end)
+              *reinterpret_cast<u32x4*>(Vcp + cache_off(j) + d0) = vreg[i][r];
+          }
+        }
+      }
+    }
+  };
+
+  // ---- running softmax state: lane holds node lr; O^T rows d = db*16+4*lg+r ----
+  constexpr int DB = D / 16;
+  f32x4 oacc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float mrun = -INFINITY, lrun = 0.f;
+
+  const int ntiles = (k_end - k_beg + ATT_TILE - 1) / ATT_TILE;
+  gload(k_beg);
+  for (int t = 0; t < ntiles; ++t) {
+    const int tile0 = k_beg + t * ATT_TILE;
+    lds_store(tile0);
+    __syncthreads();
+    if (t + 1 < ntiles) gload(tile0 + ATT_TILE);
+
+    if (wave_active) {
+      f32x4 sacc[4];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        sacc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int st = 0; st < C::QSTEPS; ++st) {
+          const u32x4 kf = *reinterpret_cast<const u32x4*>(
+              &Ks[(kb * 16 + lr) * C::LDK + st * 4 * P16 + lg * P16]);
+          sacc[kb] = AttnMma<T>::qk(kf, qf[st], sacc[kb]);
+        }
+      }
+      float x[4][4];
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int j = tile0 + kb * 16 + lg * 4 + r;
+          bool ok = j < k_end;
+          if (j >= ctxb) ok = ok && ((mrow >> (uint32_t)(min(j - ctxb, 63))) & 1ull);
+          x[kb][r] = ok ? sacc[kb][r] * a.scale_log2 : -INFINITY;
+          tmax = fmaxf(tmax, x[kb][r]);
+        }
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+      const float mnew = fmaxf(mrun, tmax);
+      const float alpha = (mnew == -INFINITY) ? 1.f : exp2f(mrun - mnew);
+      float psum = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float p = (x[kb][r] == -INFINITY) ? 0.f : exp2f(x[kb][r] - mnew);
+          x[kb][r] = p;
+          psum += p;
+        }
+      lrun = lrun * alpha + psum;
+      mrun = mnew;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        if constexpr (sizeof(T) == 2) {
+          u32x2 pb;
+          pb.x = pack_bf2(x[kb][0], x[kb][1]);
+          pb.y = pack_bf2(x[kb][2], x[kb][3]);
+#pragma unroll
+          for (int db = 0; db < DB; ++db) {
+            const u32x2 vf = *reinterpret_cast<const u32x2*>(
+                &Vs[(db * 16 + lr) * C::LDV + kb * 16 + lg * 4]);
+            oacc[db] = mfma_bf16_16x16x16(vf, pb, oacc[db]);
+          }
+        } else {
+#pragma unroll
+          for (int db = 0; db < DB; ++db) {
+            const f32x4 vf = *reinterpret_cast<const f32x4*>(
+                &Vs[(db * 16 + lr) * C::LDV + kb * 16 + lg * 4]);
+            oacc[db] = mfma_f32_16x16x4(vf.x, x[kb][0], oacc[db]);
+            oacc[db] = mfma_f32_16x16x4(vf.y, x[kb][1], oacc[db]);
+            oacc[db] = mfma_f32_16x16x4(vf.z, x[kb][2], oacc[db]);
+            oacc[db] = mfma_f32_16x16x4(vf.w, x[kb][3], oacc[db]);
+          }
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  float ltot = lrun + __shfl_xor(lrun, 16, 64);
+  ltot = ltot + __shfl_xor(ltot, 32, 64);
+  T* Op = reinterpret_cast<T*>(a.O);
+  const bool node_ok = wave_active && node < N;
+
+  if (nsplit == 1) {
+    if (node_ok) {
+      const float inv = 1.f / ltot;
+      T* orow = Op + (((int64_t)b * N + node) * a.Hq + h) * D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) st<T>(orow, db * 16 + lg * 4 + r, oacc[db][r] * inv);
+    }
+    return;
+  }
+
+  // ---- multi-split: partials, then the last split merges ----
+  const int64_t bh = (int64_t)b * a.Hq + h;
+  if (node_ok) {
+    float* op = a.opart + ((bh * S + s) * N + node) * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+      *reinterpret_cast<float4*>(op + db * 16 + lg * 4) =
+          make_float4(oacc[db][0], oacc[db][1], oacc[db][2], oacc[db][3]);
+    if (lg == 0) a.ml[(bh * S + s) * N + node] = make_float2(mrun, ltot);
+  }
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) {
+    const int prev = atomicAdd(&a.counters[bh], 1);
+    s_last = (prev == nsplit - 1);
+  }
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+
+  constexpr int D4 = D / 4;
+  for (int it = tid; it < N * D4; it += ATT_THREADS) {
+    const int n = it / D4, d0 = (it % D4) * 4;
+    float M = -INFINITY;
+    for (int q = 0; q < nsplit; ++q) M = fmaxf(M, a.ml[(bh * S + q) * N + n].x);
+    float L = 0.f;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int q = 0; q < nsplit; ++q) {
+      const float2 mlq = a.ml[(bh * S + q) * N + n];
+      const float w = (mlq.x == -INFINITY) ? 0.f : exp2f(mlq.x - M);
+      L += w * mlq.y;
+      const float4 o = *reinterpret_cast<const float4*>(a.opart + ((bh * S + q) * N + n) * D + d0);
+      acc.x += w * o.x;
+      acc.y += w * o.y;
+      acc.z += w * o.z;
+      acc.w += w * o.w;
+    }
+    const float inv = 1.f / L;
+    T* orow = Op + (((int64_t)b * N + n) * a.Hq + h) * D;
+    st<T>(orow, d0 + 0, acc.x * inv);
+    st<T>(orow, d0 + 1, acc.y * inv);
+    st<T>(orow, d0 + 2, acc.z * inv);
+    st<T>(orow, d0 + 3, acc.w * inv);
+  }
+  if (tid == 0) a.counters[bh] = 0;
+}
+
+}  // namespace medusa
+
+namespace {
+
+// Keys per split and number of splits.  A split is a whole number of 64-key
+// tiles; the count aims at ~4 workgroups per compute unit.
+struct SplitPlan {
+  int chunk, splits;
+};
+SplitPlan plan_splits(int B, int Hq, int N, int max_ctx) {
+  const int total = max_ctx + N;
+  const int tiles = (total + medusa::ATT_TILE - 1) / medusa::ATT_TILE;
+  const int target_wgs = 1024;
+  const int bh = B * Hq;
+  const int want = (target_wgs + bh - 1) / bh;
+  int tps = (tiles + want - 1) / want;
+  if (tps < 1) tps = 1;
+  const int chunk = tps * medusa::ATT_TILE;
+  return {chunk, (total + chunk - 1) / chunk};
+}
+
+struct WsLayout {
+  size_t counters, ml, opart, total;
+};
+WsLayout ws_layout(int B, int Hq, int N, int D, int S) {
+  using medusa_host::align_up;
+  WsLayout w;
+  w.counters = 0;
+  w.ml = align_up((size_t)B * Hq * sizeof(int), 256);
+  w.opart = w.ml + align_up((size_t)B * Hq * S * N * sizeof(float2), 256);
+  w.total = w.opart + align_up((size_t)B * Hq * S * N * D * sizeof(float), 256);
+  return w;
+}
+
+}  // namespace
+
+extern "C" size_t medusa_tree_attention_ws(int32_t B, int32_t N, int32_t Hq, int32_t Hkv,
+                                           int32_t D, int32_t max_ctx) {
+  (void)Hkv;
+  if (B <= 0 || N <= 0 || Hq <= 0 || D <= 0 || max_ctx < 0) return 0;
+  const SplitPlan p = plan_splits(B, Hq, N, max_ctx);
+  return ws_layout(B, Hq, N, D, p.splits).total;
+}
+
+extern "C" int32_t medusa_tree_attention(const void* Q, const void* Kt, const void* Vt, void* Kc,
+                                         void* Vc, const int32_t* page_table, int32_t max_pages,
+                                         int32_t P, const int32_t* ctx, int32_t max_ctx,
+                                         const uint64_t* mask, int32_t B, int32_t N, int32_t Hq,
+                                         int32_t Hkv, int32_t D, float scale, int32_t dt,
+                                         void* O, void* ws, size_t ws_bytes, void* stream) {
+  using namespace medusa_host;
+  MEDUSA_REQUIRE(dt == MEDUSA_F32 || dt == MEDUSA_BF16, MEDUSA_ERR_UNSUPPORTED,
+                 "medusa_tree_attention: unknown dtype %d", dt);
+  MEDUSA_REQUIRE(D == 64 || D == 128, MEDUSA_ERR_UNSUPPORTED,
+                 "medusa_tree_attention: head dim %d not in {64, 128}", D);
+  MEDUSA_REQUIRE(N >= 1 && N <= MEDUSA_MAX_NODES, MEDUSA_ERR_UNSUPPORTED,
+                 "medusa_tree_attention: N=%d outside [1, 64]", N);
+  MEDUSA_REQUIRE(B >= 0 && Hq >= 1 && Hkv >= 1 && Hq % Hkv == 0, MEDUSA_ERR_INVALID_ARG,
+                 "medusa_tree_attention: B=%d Hq=%d Hkv=%d (Hq must be a multiple of Hkv)", B, Hq,
+                 Hkv);
+  MEDUSA_REQUIRE(P >= 1 && max_pages >= 1 && max_ctx >= 0, MEDUSA_ERR_INVALID_ARG,
+                 "medusa_tree_attention: P=%d max_pages=%d max_ctx=%d", P, max_pages, max_ctx);
+  MEDUSA_REQUIRE((int64_t)max_ctx + N <= (int64_t)max_pages * P, MEDUSA_ERR_INVALID_ARG,
+                 "medusa_tree_attention: max_ctx + N = %d exceeds max_pages * P = %lld",
+                 max_ctx + N, (long long)max_pages * P);
+  MEDUSA_REQUIRE(scale > 0.f && scale < 1e30f, MEDUSA_ERR_INVALID_ARG,
+                 "medusa_tree_attention: scale must be positive and finite");
+  if (B == 0) return MEDUSA_OK;
+  MEDUSA_REQUIRE(Q && Kt && Vt && Kc && Vc && page_table && ctx && mask && O,
+                 MEDUSA_ERR_INVALID_ARG, "medusa_tree_attention: NULL pointer");
+  MEDUSA_REQUIRE(((uintptr_t)Q | (uintptr_t)Kt | (uintptr_t)Vt | (uintptr_t)Kc | (uintptr_t)Vc) %
+                         16 == 0,
+                 MEDUSA_ERR_INVALID_ARG, "medusa_tree_attention: tensors must be 16-byte aligned");
+  const SplitPlan p = plan_splits(B, Hq, N, max_ctx);
+  const WsLayout L = ws_layout(B, Hq, N, D, p.splits);
+  MEDUSA_REQUIRE(ws != NULL && ws_bytes >= L.total, MEDUSA_ERR_WORKSPACE,
+                 "medusa_tree_attention: workspace %zu < %zu bytes", ws_bytes, L.total);
+  MEDUSA_REQUIRE((uintptr_t)ws % 256 == 0, MEDUSA_ERR_INVALID_ARG,
+                 "medusa_tree_attention: ws must be 256-byte aligned");
+
+  medusa::AttnArgs a;
+  a.Q = Q; a.Kt = Kt; a.Vt = Vt; a.Kc = Kc; a.Vc = Vc;
+  a.page_table = page_table; a.ctx = ctx; a.mask = mask; a.O = O;
+  a.counters = (int*)((char*)ws + L.counters);
+  a.ml = (float2*)((char*)ws + L.ml);
+  a.opart = (float*)((char*)ws + L.opart);
+  a.max_pages = max_pages; a.P = P; a.B = B; a.N = N; a.Hq = Hq; a.Hkv = Hkv;
+  a.chunk = p.chunk;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  dim3 grid((unsigned)p.splits, (unsigned)Hq, (unsigned)B);
+  hipStream_t st = (hipStream_t)stream;
+  if (dt == MEDUSA_BF16) {
+    if (D == 128) hipLaunchKernelGGL((medusa::tree_attention_kernel<medusa::bf16_t, 128>), grid, dim3(medusa::ATT_THREADS), 0, st, a);
+    else hipLaunchKernelGGL((medusa::tree_attention_kernel<medusa::bf16_t, 64>), grid, dim3(medusa::ATT_THREADS), 0, st, a);
+  } else {
+    if (D == 128) hipLaunchKernelGGL((medusa::tree_attention_kernel<float, 128>), grid, dim3(medusa::ATT_THREADS), 0, st, a);
+    else hipLaunchKernelGGL((medusa::tree_attention_kernel<float, 64>), grid, dim3(medusa::ATT_THREADS), 0, st, a);
+  }
+  return check_launch("medusa_tree_attention");
+}

@@ -1,0 +1,204 @@
+"""Medusa decode loop on one GPU, driven entirely through libmedusa.
+
+One decode step ("Medusa Heads", sections "Come le teste prevedono i token
+successivi" and "Attenzione sull'albero e accettazione"):
+
+  build_tree  (root token + per-head top-k -> N tree tokens, positions, masks)
+  verification forward of the N tree rows in ONE pass (Llama-style layers;
+      tree-masked attention over the paged KV cache + the tree's own keys)
+  accept      (greedy or typical; longest accepted branch, next root token)
+  kv_compact  (keep only the accepted branch in every layer's cache)
+  gather_rows + heads (the kept branch's last hidden state -> next top-k)
+
+Python only allocates device buffers, uploads static inputs (weights, tree
+template, prompt) and reads back the accepted tokens; every computation is a
+library kernel.  Weight layout chosen for the GPU: Wq|Wk|Wv stacked into one
+[(Hq+2Hkv)*D, H] matrix, and gate/up interleaved in 16-row blocks so the
+down-projection input comes straight out of the SwiGLU epilogue.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import medusa as M
+
+
+def interleave_gate_up(wg: np.ndarray, wu: np.ndarray) -> np.ndarray:
+    """[F,H] gate and up -> [2F,H] with block j = gate rows 16j.. then up rows 16j.."""
+    F, H = wg.shape
+    assert F % 16 == 0
+    return np.stack([wg.reshape(F // 16, 16, H), wu.reshape(F // 16, 16, H)], axis=1).reshape(2 * F, H)
+
+
+class DeviceModel:
+    """Device copy of a Llama-style decoder with Medusa heads.
+
+    ``src`` is any object with the fields of ``synth.TinyDecoder`` (numpy
+    arrays), or None together with ``tensors`` (a dict of ready device tensors,
+    used for large random models generated on the GPU).
+    """
+
+    def __init__(self, src=None, dtype=torch.float32, device="cuda", tensors=None, meta=None):
+        self.dtype, self.device = dtype, torch.device(device)
+        if src is not None:
+            meta = dict(vocab=src.vocab, hidden=src.hidden, n_layers=src.n_layers,
+                        n_heads=src.n_heads, n_kv_heads=src.n_kv_heads, head_dim=src.head_dim,
+                        ffn=src.ffn, rope_base=src.rope_base, eps=src.eps)
+            up = lambda a: torch.tensor(np.ascontiguousarray(a, dtype=np.float32)).to(
+                device=self.device, dtype=dtype)
+            t = dict(embed=up(src.embed), g_final=up(src.g_final), lm_head=up(src.lm_head),
+                     w1=up(src.w1), b1=up(src.b1), w2=up(src.w2), layers=[])
+            for L in src.layers:
+                t["layers"].append(dict(
+                    wqkv=up(np.concatenate([L["wq"], L["wk"], L["wv"]], axis=0)), wo=up(L["wo"]),
+                    wgu=up(interleave_gate_up(L["wg"], L["wu"])), wd=up(L["wd"]),
+                    g_attn=up(L["g_attn"]), g_mlp=up(L["g_mlp"])))
+            tensors = t
+        self.meta = meta
+        self.t = tensors
+        for k, v in meta.items():
+            setattr(self, k, v)
+        self.n_medusa = tensors["w1"].shape[0]
+
+
+class MedusaDecoder:
+    """Paged-KV Medusa decoding for one sequence (B = 1).
+
+    ``parent``, ``rank``: the tree template (node 0 = root); a single-node
+    template turns the loop into plain greedy decoding (no heads).
+    """
+
+    def __init__(self, model: DeviceModel, parent, rank, capacity, page_size=16, mode="greedy",
+                 temperature=1.0, epsilon=0.3, delta=0.09):
+        self.m = model
+        dev = model.device
+        parent = np.asarray(parent, np.int32)
+        rank = np.asarray(rank, np.int32)
+        self.N = len(parent)
+        depth = np.zeros(self.N, np.int32)
+        for i in range(1, self.N):
+            depth[i] = depth[parent[i]] + 1
+        self.K = int(depth.max())
+        self.width = int(rank.max()) + 1
+        if self.K > 0:
+            M.medusa_tree_validate(parent, rank, self.K, self.width)
+        self.mode = 0 if mode == "greedy" else 1
+        self.T, self.eps, self.delta = temperature, epsilon, delta
+        self.P = page_size
+        self.max_pages = (capacity + self.N + 64 + page_size - 1) // page_size
+        self.capacity = self.max_pages * page_size
+        i32 = dict(dtype=torch.int32, device=dev)
+        self.parent = torch.tensor(parent[None], **i32)
+        self.rank = torch.tensor(rank[None], **i32)
+        self.page_table = torch.arange(self.max_pages, **i32)[None].contiguous()
+        shape = (self.max_pages, model.n_kv_heads, page_size, model.head_dim)
+        self.Kc = [torch.zeros(shape, dtype=model.dtype, device=dev) for _ in range(model.n_layers)]
+        self.Vc = [torch.zeros(shape, dtype=model.dtype, device=dev) for _ in range(model.n_layers)]
+        self.ctx = torch.zeros(1, **i32)
+        self.ctx_host = 0
+        self.root = torch.zeros(1, **i32)
+        Kh = max(self.K, 1)
+        self.topk_ids = torch.zeros((Kh, 1, self.width), **i32)
+        self.topk_vals = torch.zeros((Kh, 1, self.width), dtype=torch.float32, device=dev)
+        self.max_ctx = self.capacity - 64          # every call has ctx + n <= capacity
+        self.attn_ws = M._ws(max(M.tree_attention_ws_bytes(1, n, model.n_heads, model.n_kv_heads,
+                                                           model.head_dim, self.max_ctx)
+                                 for n in range(1, 65)), dev, zero=True)
+        self.acc_ws = M._ws(M._lib.medusa_accept_ws(1, 64), dev)
+        dt = M._dt(model.t["embed"])
+        self.heads_ws = M._ws(M._lib.medusa_heads_ws(1, model.hidden, model.n_medusa, model.vocab,
+                                                     self.width, dt), dev)
+        self.out = (torch.zeros(1, **i32), torch.zeros((1, self.K + 1), **i32), torch.zeros(1, **i32))
+        self.new_ctx = torch.zeros(1, **i32)
+        self.src = torch.zeros((1, self.K + 1), **i32)
+        self.dst = torch.zeros((1, self.K + 1), **i32)
+
+    # ------------------------------------------------------------------
+    def forward(self, tokens, pos, mask):
+        """Verification forward of n rows (tokens/pos [1,n] int32, mask [1,n] int64).
+
+        Stores the rows' K/V at cache slots ctx..ctx+n-1.  Returns (logits
+        [n,V] float32, final hidden [n,H] model dtype)."""
+        m, t = self.m, self.m.t
+        n = tokens.shape[-1]
+        x = M.medusa_embed(tokens.reshape(-1), t["embed"])
+        scale = 1.0 / float(np.sqrt(m.head_dim))
+        for li, L in enumerate(t["layers"]):
+            h = M.medusa_rmsnorm(x, L["g_attn"], m.eps, m.dtype)
+            qkv = M.medusa_linear(h, L["wqkv"])
+            q, k, v = M.medusa_qkv_rope(qkv, m.n_heads, m.n_kv_heads, m.head_dim, pos.reshape(-1),
+                                        m.rope_base)
+            o = M.medusa_tree_attention(q[None], k[None], v[None], self.Kc[li], self.Vc[li],
+                                        self.page_table, self.ctx, self.max_ctx,
+                                        mask, scale, ws=self.attn_ws)
+            M.medusa_linear(o.reshape(n, -1), L["wo"], M.EPI_RES_ADD_F32, aux=x, out=x)
+            h = M.medusa_rmsnorm(x, L["g_mlp"], m.eps, m.dtype)
+            f = M.medusa_linear(h, L["wgu"], M.EPI_SWIGLU)
+            M.medusa_linear(f, L["wd"], M.EPI_RES_ADD_F32, aux=x, out=x)
+        hN = M.medusa_rmsnorm(x, t["g_final"], m.eps, m.dtype)
+        logits = M.medusa_linear(hN, t["lm_head"], y_f32=True)
+        return logits, hN
+
+    def _heads(self, h_row):
+        if self.K == 0:
+            return
+        t = self.m.t
+        M.medusa_heads(h_row, t["w1"], t["b1"], t["w2"], self.width, logits=None,
+                       ids=self.topk_ids, vals=self.topk_vals, ws=self.heads_ws,
+                       want_logits=False)
+
+    def _set_ctx(self, c):
+        self.ctx.copy_(torch.tensor([c], dtype=torch.int32))
+        self.ctx_host = c
+
+    def prefill(self, prompt):
+        """Causal forward over the prompt in chunks of <= 64 chain-masked rows."""
+        prompt = np.asarray(prompt, np.int32)
+        dev = self.m.device
+        self._set_ctx(0)
+        c = 0
+        while c < len(prompt):
+            n = min(64, len(prompt) - c)
+            tok = torch.tensor(prompt[None, c:c + n], dtype=torch.int32, device=dev)
+            pos = torch.arange(c, c + n, dtype=torch.int32, device=dev)[None].contiguous()
+            mask = torch.tensor([[(1 << (i + 1)) - 1 if i < 63 else -1 for i in range(n)]],
+                                dtype=torch.int64, device=dev)
+            logits, hN = self.forward(tok, pos, mask)
+            c += n
+            self._set_ctx(c)
+        ids, _ = M.medusa_topk(logits[n - 1:n].contiguous(), 1)
+        self.root.copy_(ids.reshape(1))
+        self._heads(hN[n - 1:n].contiguous())
+
+    def step(self):
+        """One Medusa decode step (all on the GPU); returns (accept_len, path, tokens) tensors."""
+        tokens, pos, mask = M.medusa_build_tree(self.parent, self.rank, self.root, self.topk_ids,
+                                                self.ctx)
+        logits, hN = self.forward(tokens, pos, mask)
+        acc, path, nxt = M.medusa_accept(logits[None], tokens, self.parent, self.K, self.mode,
+                                         self.T, self.eps, self.delta, out=self.out, ws=self.acc_ws)
+        M.kv_compact(self.Kc, self.Vc, self.page_table, self.ctx, path, acc, new_ctx=self.new_ctx,
+                     src=self.src, dst=self.dst)
+        if self.K > 0:
+            hbest = M.medusa_gather_rows(hN[None], path, acc)
+            self._heads(hbest)
+        self.root.copy_(nxt)
+        self.ctx.copy_(self.new_ctx)
+        self.last = dict(tokens=tokens, logits=logits, hN=hN, pos=pos, mask=mask)
+        return acc, path, tokens
+
+    def generate(self, prompt, n_new, record=None):
+        """Prefill, then Medusa steps until n_new tokens are emitted.  Returns int32[n_new]."""
+        self.prefill(prompt)
+        out = []
+        while len(out) < n_new:
+            acc, path, tokens = self.step()
+            a = int(acc.item())
+            p = path[0, :a + 1].cpu().numpy()
+            tk = tokens[0].cpu().numpy()
+            out.extend(int(tk[j]) for j in p)
+            self.ctx_host += a + 1
+            if record is not None:
+                record.append(a)
+        return np.array(out[:n_new], np.int32)
