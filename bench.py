@@ -1,0 +1,277 @@
+#!/usr/bin/env python3
+"""Benchmark of the Medusa decode step on one MI355X.
+
+Workload (synthetic, seeded, random-init): a Llama-7B-shaped decoder in bf16
+(32 layers, hidden 4096, 32 heads x 128, FFN 11008, vocab 32000) with 5 Medusa
+heads (W1 ~ N(0, 0.01), b1 = 0, W2 = lm_head), a 512-token random prompt and
+a 64-node verification tree (Cartesian product of top-(4,3,2,2,1), pruned to
+64 nodes by seeded leaf removal).  One step = one pass of the whole hot path:
+tree build, the 64-row verification forward with tree-masked attention over
+the paged KV cache, acceptance, KV compaction, and the heads + top-k on the
+kept branch's hidden state.  ``value`` = accepted (emitted) tokens per second
+over the K timed steps, inputs resident in HBM.
+
+Also reported on the same line:
+  roofline       the dominant kernel of the step (the gate/up projection, a
+                 weight-streaming GEMM, HBM-bound) from HIP events on its
+                 launching stream over the timed steps;
+  tree_attention the tree-attention kernel alone at the 7B layer shape
+                 (32 heads x 128, 2048 cached tokens + 64 tree nodes), KV
+                 buffers rotated over > 256 MB so the MALL cannot serve them;
+  cpu_baseline   the CPU oracle on a bounded sample of the same step.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "accepted tokens/s + tree-attn HBM GB/s (% peak), 7B-shape, 64-node tree"
+HBM_PEAK_GBS = 8000.0
+
+
+def graph_time_us(torch, launches, reps=10, inner=2):
+    """Mean duration (us) of one call of ``launches`` (a list of zero-argument
+    callables, each one kernel launch), from HIP events around replays of a
+    graph that holds ``inner`` passes over the list, on the replay stream."""
+    for f in launches:
+        f()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        with torch.cuda.graph(g, stream=st):
+            for _ in range(inner):
+                for f in launches:
+                    f()
+    torch.cuda.current_stream().wait_stream(st)
+    g.replay()
+    torch.cuda.synchronize()
+    per = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        per.append(1000.0 * a.elapsed_time(b) / (inner * len(launches)))
+    per.sort()
+    return sum(per) / len(per), per[len(per) // 2]
+
+
+def tree_attention_c2(torch, M, synth, reps=10, copies=17):
+    """Tree attention alone at the 7B layer shape; returns a dict of figures."""
+    import numpy as np
+    B, N, H, D, ctx, P = 1, 64, 32, 128, 2048, 16
+    dev = "cuda"
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(2)
+    bf = torch.bfloat16
+    pages = (ctx + N + P - 1) // P
+    Q = torch.randn((B, N, H, D), generator=gen, device=dev).to(bf)
+    Kt = torch.randn((B, N, H, D), generator=gen, device=dev).to(bf)
+    Vt = torch.randn((B, N, H, D), generator=gen, device=dev).to(bf)
+    Kc = [torch.randn((pages, H, P, D), generator=gen, device=dev).to(bf) for _ in range(copies)]
+    Vc = [torch.randn((pages, H, P, D), generator=gen, device=dev).to(bf) for _ in range(copies)]
+    parent, rank = synth.tree_template((4, 3, 2, 2, 1))
+    parent, rank = synth.prune_template(parent, rank, N, 2)
+    i32 = dict(dtype=torch.int32, device=dev)
+    pt = torch.arange(pages, **i32)[None].contiguous()
+    ctx_t = torch.tensor([ctx], **i32)
+    topk = torch.zeros((5, 1, 4), **i32)
+    _, _, mask = M.medusa_build_tree(torch.tensor(parent[None], **i32), torch.tensor(rank[None], **i32),
+                                     torch.zeros(1, **i32), topk, ctx_t)
+    out = torch.empty_like(Q)
+    ws = M._ws(M.tree_attention_ws_bytes(B, N, H, H, D, ctx), dev, zero=True)
+    scale = 1.0 / np.sqrt(D)
+    launches = [lambda i=i: M.medusa_tree_attention(Q, Kt, Vt, Kc[i], Vc[i], pt, ctx_t, ctx, mask,
+                                                     scale, out=out, ws=ws)
+                for i in range(copies)]
+    us, us_med = graph_time_us(torch, launches, reps=reps)
+    kv = (ctx + N) * H * D * 2 * 2          # cached + tree K and V read
+    nbytes = kv + 2 * B * N * H * D * 2 + N * 8 + N * H * D * 2 * 2  # + Q, O, masks, appended tree K/V
+    flops = 4.0 * N * H * D * (ctx + N)     # QK^T and PV, upper bound (all keys)
+    gbs = nbytes / (us * 1e-6) / 1e9
+    return dict(workload="7B layer: 32 heads x 128, ctx 2048 + 64-node tree, bf16, 16-token pages",
+                us=round(us, 3), us_median=round(us_med, 3),
+                bytes=nbytes, gbs=round(gbs, 1), frac=round(gbs / HBM_PEAK_GBS, 4),
+                tflops=round(flops / (us * 1e-6) / 1e12, 2),
+                verified_tree_tokens_per_s=round(N / (us * 1e-6), 1),
+                timing="HIP events around graph replays of back-to-back launches",
+                kv_copies_rotated=copies, rotated_mb=round(copies * 2 * Kc[0].numel() * 2 / 1e6, 1))
+
+
+def cpu_baseline(torch, dec, model_src, emitted_per_step, sample_layers):
+    """The oracle, as is, on a bounded sample of one decode step (host cores)."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+    import synth
+    from oracle import medusa_oracle as orc
+
+    meta = model_src["meta"]
+    H, V = meta["hidden"], meta["vocab"]
+    host = lambda t: t.float().cpu().numpy().astype(np.float64)
+    layers = []
+    for L in model_src["layers"][:sample_layers]:
+        layers.append({k: host(v) for k, v in L.items()})
+    tiny = synth.TinyDecoder(V, H, sample_layers, meta["n_heads"], meta["n_kv_heads"],
+                             meta["head_dim"], meta["ffn"], meta["rope_base"], meta["eps"],
+                             host(model_src["embed"]), layers, host(model_src["g_final"]),
+                             host(model_src["lm_head"]), host(model_src["w1"]), host(model_src["b1"]),
+                             host(model_src["w2"]))
+    last = dec.last
+    ctx = dec.ctx_sample
+    tokens = last["tokens"][0].cpu().numpy()
+    pos = last["pos"][0].cpu().numpy()
+    mask = last["mask"][0].cpu().numpy().view(np.uint64)
+    cache = orc.KVCache(tiny, ctx + 64)
+    for li in range(sample_layers):
+        for pool, dst in ((dec.Kc[li], cache.k[li]), (dec.Vc[li], cache.v[li])):
+            rows = pool.float().cpu().numpy().transpose(0, 2, 1, 3).reshape(-1, meta["n_kv_heads"],
+                                                                             meta["head_dim"])
+            dst[:ctx] = rows[:ctx]
+    parent = dec.parent[0].cpu().numpy()
+    stamps = []
+    t0 = time.perf_counter()
+    logits, hf = orc.forward_rows(tiny, tokens, pos, mask, cache, ctx,
+                                  layer_hook=lambda li, x: stamps.append(time.perf_counter()))
+    t1 = time.perf_counter()
+    t_layers = stamps[-1] - t0          # embedding + the sampled layers
+    t_head = t1 - stamps[-1]            # final norm + lm_head
+    res = orc.accept_greedy(orc.f32(logits), tokens, parent, dec.K)
+    hl = orc.head_logits(hf[res["best"]][None], tiny.w1, tiny.b1, tiny.w2)
+    ids = [orc.topk(hl[k, 0], dec.width)[0] for k in range(dec.K)]
+    t2 = time.perf_counter()
+    # lm_head, accept and heads ran in full; the layers are scaled to all of them
+    step_s = t_layers * meta["n_layers"] / sample_layers + t_head + (t2 - t1)
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return dict(value=round(emitted_per_step / step_s, 4), unit="tokens/s", cores=int(threads),
+                kind="oracle",
+                sample=(f"one 64-node verification step at ctx={ctx}: {sample_layers} of "
+                        f"{meta['n_layers']} layers timed ({t_layers:.2f} s, scaled x"
+                        f"{meta['n_layers'] / sample_layers:g}) plus lm_head, greedy accept and the "
+                        f"5 heads + top-k in full ({t_head + t2 - t1:.2f} s); tokens/step from the GPU "
+                        f"run ({emitted_per_step:.3f})"),
+                step_seconds_extrapolated=round(step_s, 3), _ids=len(ids))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--mode", default="greedy", choices=["greedy", "typical"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-layers", type=int, default=4)
+    ap.add_argument("--skip-c2", action="store_true")
+    ap.add_argument("--skip-plain", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures the one-GPU Medusa step; runs on more than one GPU are not "
+              "part of this build (see DESIGN.md for how the path would shard).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import synth
+    from speculative_decoding_02_amd import medusa as M
+    from speculative_decoding_02_amd.decoder import DeviceModel, MedusaDecoder
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    log = lambda *a: print(*a, file=sys.stderr, flush=True)
+    log("[bench] drawing the random 7B-shaped decoder on the GPU")
+    src = synth.device_llama(seed=4)
+    model = DeviceModel.from_llama(src)
+    parent, rank = synth.prune_template(*synth.tree_template((4, 3, 2, 2, 1)), 64, 2)
+    prompt = synth.prompt_tokens(4, 512, 32000)
+    capacity = 512 + 6 * (args.warmup + args.steps) + 128
+    dec = MedusaDecoder(model, parent, rank, capacity=capacity, mode=args.mode)
+    log("[bench] prefill 512 + record the step graph + warmup")
+    dec.prefill(prompt)
+    dec.capture()
+    for _ in range(args.warmup):
+        acc, _, _ = dec.step_graph()
+        int(acc.item())
+    dec.prefill(prompt)  # timed steps start from the 512-token prompt again
+    torch.cuda.synchronize()
+    log(f"[bench] timing {args.steps} steps (graph replay, one host read of accept_len per step)")
+    emitted, accepts = 0, []
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        acc, _, _ = dec.step_graph()
+        a = int(acc.item())
+        accepts.append(a)
+        emitted += a + 1
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    dec.ctx_sample = 512 + emitted - (accepts[-1] + 1)  # ctx of the last timed step
+    step_ms = 1000.0 * (t1 - t0) / args.steps
+    tok_s = emitted / (t1 - t0)
+
+    # dominant kernel: the gate/up projection (SwiGLU epilogue), weight
+    # streaming; one step's 32 launches over the model's own weights
+    H, F = 4096, 11008
+    hin = torch.randn((64, H), device="cuda").to(torch.bfloat16)
+    gout = torch.empty((64, F), device="cuda", dtype=torch.bfloat16)
+    gu_launches = [lambda L=L: M.medusa_linear(hin, L["wgu"], M.EPI_SWIGLU, out=gout)
+                   for L in model.t["layers"]]
+    gu_us, gu_med = graph_time_us(torch, gu_launches, reps=10, inner=2)
+    gu_bytes = 2 * F * H * 2 + 64 * H * 2 + 64 * F * 2
+    gu_gbs = gu_bytes / (gu_us * 1e-6) / 1e9
+
+    plain = None
+    if not args.skip_plain:
+        log("[bench] plain one-token greedy decoding on the same path")
+        pdec = MedusaDecoder(model, np.array([-1]), np.array([0]), capacity=capacity)
+        pdec.prefill(prompt)
+        pdec.capture()
+        for _ in range(3):
+            int(pdec.step_graph()[0].item())
+        torch.cuda.synchronize()
+        p0 = time.perf_counter()
+        for _ in range(args.steps):
+            int(pdec.step_graph()[0].item())
+        torch.cuda.synchronize()
+        plain = round(args.steps / (time.perf_counter() - p0), 2)
+        del pdec
+
+    c2 = None if args.skip_c2 else tree_attention_c2(torch, M, synth)
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] CPU oracle baseline (bounded sample)")
+        cpu = cpu_baseline(torch, dec, src, emitted / args.steps, args.cpu_sample_layers)
+        cpu.pop("_ids", None)
+
+    line = {
+        "metric": METRIC, "value": round(tok_s, 2), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step_ms, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded random-init weights and prompt)",
+        "config": {"workload": "Medusa decode step, random Llama-7B-shaped bf16 decoder "
+                               "(32 layers, hidden 4096, 32x128 heads, FFN 11008, vocab 32000) + "
+                               "5 Medusa heads, prompt 512, 64-node tree (4,3,2,2,1) pruned",
+                   "mode": args.mode, "tree_nodes": 64, "prompt": 512, "batch": 1},
+        "mean_accept_len": round(float(np.mean(accepts)), 3),
+        "tokens_per_step": round(emitted / args.steps, 3),
+        "verified_tree_tokens_per_s": round(64 * args.steps / (t1 - t0), 1),
+        "plain_decode_tokens_per_s": plain,
+        "roofline": {"bound": "hbm", "kernel": "gemm_kernel (gate/up projection, SwiGLU epilogue)",
+                     "achieved": round(gu_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gu_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "bytes_per_launch": gu_bytes, "us_per_launch": round(gu_us, 2),
+                     "us_median": round(gu_med, 2),
+                     "timing": "HIP events around graph replays of the 32 per-step launches"},
+        "tree_attention": c2,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -161,7 +161,7 @@ int32_t medusa_build_tree(int32_t B, int32_t N, const int32_t* parent, const int
  *   Q  [B, N, Hq, D] (dt)   queries of the N tree nodes (RoPE applied)
  *   Kt, Vt [B, N, Hkv, D]   keys / values of the tree nodes
  *   Kc, Vc [pages, Hkv, P, D]  paged cache pools; logical slot s of sequence
- *          b lives in page page_table[b, s / P] at row s % P
+ *          b lives in page page_table[b, s / P] at row s % P (4 <= P <= 4096)
  *   page_table [B, max_pages] int32; ctx [B] int32 committed tokens
  *   max_ctx: host-side upper bound of every ctx[b] (sizes the grid)
  *   mask [B, N] uint64 (from medusa_build_tree)
@@ -170,12 +170,11 @@ int32_t medusa_build_tree(int32_t B, int32_t N, const int32_t* parent, const int
  * to cache slots 0..ctx[b]-1 and to tree node j iff bit j of mask[b, i].
  * Query head h uses kv head h / (Hq / Hkv).  The call also stores Kt, Vt into
  * cache slots ctx[b] .. ctx[b]+N-1 (those pages must exist in page_table).
- * ws: medusa_tree_attention_ws(...) bytes, ZERO-FILLED before its first use;
- * each call leaves its counter area zero again.  Calls sharing one ws must
- * not overlap in time.
+ * ws: medusa_tree_attention_ws(...) bytes of scratch (split partials); no
+ * initialisation needed.  Calls sharing one ws must not overlap in time.
  * ---------------------------------------------------------------------- */
 size_t medusa_tree_attention_ws(int32_t B, int32_t N, int32_t Hq, int32_t Hkv, int32_t D,
-                                int32_t max_ctx);
+                                int32_t max_ctx, int32_t P);
 int32_t medusa_tree_attention(const void* Q, const void* Kt, const void* Vt, void* Kc, void* Vc,
                               const int32_t* page_table, int32_t max_pages, int32_t P,
                               const int32_t* ctx, int32_t max_ctx, const uint64_t* mask,

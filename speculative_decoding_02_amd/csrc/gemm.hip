@@ -35,21 +35,27 @@ template <> struct GemmTraits<float> {
   }
 };
 
-constexpr int GEMM_WAVES = 4;
-constexpr int GEMM_NB = 2;          // 16-column blocks per tile (32 W rows)
-constexpr int GEMM_U = 2;           // contraction steps per pipeline stage
+// Register-ring depth (contraction steps in flight per wave) for a given
+// number of 16-row blocks of X: the ring holds MB + NB 16-byte vectors per
+// step, kept near 150 VGPRs so two waves fit on each SIMD.
+template <int MB, int NB> struct GemmRing {
+  static constexpr int per_step = MB + NB;
+  static constexpr int PF = per_step >= 8 ? 4 : per_step >= 6 ? 6 : per_step >= 4 ? 8 : 12;
+};
 
-template <typename T, int MB, int EPI>
-__global__ __launch_bounds__(256) void gemm_kernel(const T* __restrict__ X, int64_t xbs,
-                                                   int M, int Kd, const T* __restrict__ W,
-                                                   int Nw, const T* __restrict__ bias,
-                                                   const void* aux, void* Y, int y_f32) {
+template <typename T, int MB, int NB, int KS, int EPI>
+__global__ __launch_bounds__(64 * KS) void gemm_kernel(const T* __restrict__ X, int64_t xbs,
+                                                       int M, int Kd, const T* __restrict__ W,
+                                                       int Nw, const T* __restrict__ bias,
+                                                       const void* aux, void* Y, int y_f32) {
   using TR = GemmTraits<T>;
   constexpr int P16 = TR::per16;
   constexpr int KSTEP = 4 * P16;
-  constexpr int TM = 16 * MB, TN = 16 * GEMM_NB;
+  constexpr int TM = 16 * MB, TN = 16 * NB;
   constexpr int LDR = TN + 1;  // padded LDS row (floats)
-  __shared__ float red[GEMM_WAVES][TM * LDR];
+  constexpr int PF = GemmRing<MB, NB>::PF;
+  constexpr int NT = 64 * KS;
+  __shared__ float red[KS][TM * LDR];
 
   const int g = blockIdx.z;
   const int n0 = blockIdx.x * TN;
@@ -60,107 +66,116 @@ __global__ __launch_bounds__(256) void gemm_kernel(const T* __restrict__ X, int6
   const T* Xg = X + (int64_t)g * xbs;
   const T* Wg = W + (int64_t)g * Nw * Kd;
   const T* xrow[MB];
-  const T* wrow[GEMM_NB];
+  const T* wrow[NB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
     int r = min(m0 + mb * 16 + lr, M - 1);
     xrow[mb] = Xg + (int64_t)r * Kd + lg * P16;
   }
 #pragma unroll
-  for (int nb = 0; nb < GEMM_NB; ++nb) {
+  for (int nb = 0; nb < NB; ++nb) {
     int r = min(n0 + nb * 16 + lr, Nw - 1);
     wrow[nb] = Wg + (int64_t)r * Kd + lg * P16;
   }
 
-  const int nsteps = (Kd + KSTEP - 1) / KSTEP;
-  const int s_beg = (int)((int64_t)nsteps * wave / GEMM_WAVES);
-  const int s_end = (int)((int64_t)nsteps * (wave + 1) / GEMM_WAVES);
-  const int kmax = Kd - lg * P16;  // this lane's vector at step s is valid iff s*KSTEP < kmax
+  // Contraction steps: nfull full steps (every lane's 16-byte vector in
+  // range) split evenly over the KS waves, plus at most one ragged tail step
+  // done by the last wave.  Loads in the main loop are unconditional (clamped
+  // to a valid step) and never feed a select, so the ring really keeps PF
+  // steps of loads in flight; out-of-range steps are skipped at compute.
+  const int nfull = Kd / KSTEP;
+  const int s_beg = (int)((int64_t)nfull * wave / KS);
+  const int s_end = (int)((int64_t)nfull * (wave + 1) / KS);
+  const int s_last = max(s_end - 1, 0);
 
-  f32x4 acc[MB][GEMM_NB];
+  f32x4 acc[MB][NB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-    for (int nb = 0; nb < GEMM_NB; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  u32x4 fa[2][GEMM_U][MB], fb[2][GEMM_U][GEMM_NB];
-  const u32x4 zero = {0u, 0u, 0u, 0u};
-  auto load = [&](int buf, int s) {
+  u32x4 fa[PF][MB], fb[PF][NB];
+  auto load = [&](int u, int st) {
+    const int k = st * KSTEP;
 #pragma unroll
-    for (int u = 0; u < GEMM_U; ++u) {
-      const int st = s + u;
-      const int k = st * KSTEP;
-      const bool ok = (st < s_end) && (k < kmax);
+    for (int mb = 0; mb < MB; ++mb) fa[u][mb] = *reinterpret_cast<const u32x4*>(xrow[mb] + k);
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-        fa[buf][u][mb] = ok ? *reinterpret_cast<const u32x4*>(xrow[mb] + k) : zero;
-#pragma unroll
-      for (int nb = 0; nb < GEMM_NB; ++nb)
-        fb[buf][u][nb] = ok ? *reinterpret_cast<const u32x4*>(wrow[nb] + k) : zero;
-    }
+    for (int nb = 0; nb < NB; ++nb) fb[u][nb] = *reinterpret_cast<const u32x4*>(wrow[nb] + k);
   };
-  auto compute = [&](int buf) {
+  auto compute = [&](int u) {
 #pragma unroll
-    for (int u = 0; u < GEMM_U; ++u)
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < GEMM_NB; ++nb)
-          acc[mb][nb] = TR::mma(fa[buf][u][mb], fb[buf][u][nb], acc[mb][nb]);
+      for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = TR::mma(fa[u][mb], fb[u][nb], acc[mb][nb]);
   };
 
   if (s_beg < s_end) {
-    // two register stages, ping-pong unrolled so every index is static
-    load(0, s_beg);
+    // ring of PF steps in flight; slot u holds step s + u.  The loop body has
+    // no branches, so the compiler's wait before each slot's compute counts
+    // exactly the later slots' loads.
+#pragma unroll
+    for (int u = 0; u < PF; ++u) load(u, min(s_beg + u, s_last));
     int s = s_beg;
-    while (true) {
-      if (s + GEMM_U < s_end) load(1, s + GEMM_U);
-      compute(0);
-      s += GEMM_U;
-      if (s >= s_end) break;
-      if (s + GEMM_U < s_end) load(0, s + GEMM_U);
-      compute(1);
-      s += GEMM_U;
-      if (s >= s_end) break;
+    for (; s + PF <= s_end; s += PF) {
+#pragma unroll
+      for (int u = 0; u < PF; ++u) {
+        compute(u);
+        load(u, min(s + u + PF, s_last));
+      }
     }
+#pragma unroll
+    for (int u = 0; u < PF; ++u)
+      if (u < s_end - s) compute(u);  // remainder: already in slots 0..r-1
+  }
+  if (Kd % KSTEP != 0 && wave == KS - 1) {
+    // ragged tail step: lanes whose vector starts past Kd contribute zeros
+    const int k = nfull * KSTEP;
+    const bool ok = k + lg * P16 < Kd;
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) fa[0][mb] = ok ? *reinterpret_cast<const u32x4*>(xrow[mb] + k) : zero;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) fb[0][nb] = ok ? *reinterpret_cast<const u32x4*>(wrow[nb] + k) : zero;
+    compute(0);
   }
 
-  // partial tiles -> LDS
+  // partial tiles -> LDS, summed in wave order
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-    for (int nb = 0; nb < GEMM_NB; ++nb)
+    for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
         red[wave][(mb * 16 + lg * 4 + r) * LDR + nb * 16 + lr] = acc[mb][nb][r];
   __syncthreads();
 
   if (EPI == MEDUSA_EPI_SWIGLU) {
-    // tile columns [0,16) are gate rows, [16,32) the matching up rows
+    // each 32-column pair of blocks: [0,16) gate rows, [16,32) the matching up rows
     const int F = Nw / 2;
     T* Yg = reinterpret_cast<T*>(Y) + (int64_t)g * M * F;
-    for (int e = threadIdx.x; e < TM * 16; e += 256) {
-      const int row = e >> 4, c = e & 15;
-      const int m = m0 + row, f = (n0 >> 1) + c;
+    for (int e = threadIdx.x; e < TM * (TN / 2); e += NT) {
+      const int row = e / (TN / 2), cc = e % (TN / 2);
+      const int pair = cc >> 4, c = cc & 15;
+      const int m = m0 + row, f = (n0 >> 1) + pair * 16 + c;
       if (m >= M || f >= F) continue;
       float gte = 0.f, up = 0.f;
 #pragma unroll
-      for (int w = 0; w < GEMM_WAVES; ++w) {
-        gte += red[w][row * LDR + c];
-        up += red[w][row * LDR + 16 + c];
+      for (int w = 0; w < KS; ++w) {
+        gte += red[w][row * LDR + pair * 32 + c];
+        up += red[w][row * LDR + pair * 32 + 16 + c];
       }
       st<T>(Yg, (int64_t)m * F + f, silu_f(gte) * up);
     }
     return;
   }
 
-  for (int e = threadIdx.x; e < TM * TN; e += 256) {
+  for (int e = threadIdx.x; e < TM * TN; e += NT) {
     const int row = e / TN, col = e % TN;
     const int m = m0 + row, n = n0 + col;
     if (m >= M || n >= Nw) continue;
     float v = red[0][row * LDR + col];
 #pragma unroll
-    for (int w = 1; w < GEMM_WAVES; ++w) v += red[w][row * LDR + col];
+    for (int w = 1; w < KS; ++w) v += red[w][row * LDR + col];
     const int64_t o = (int64_t)g * M * Nw + (int64_t)m * Nw + n;
     if (EPI == MEDUSA_EPI_NONE) {
       if (y_f32) reinterpret_cast<float*>(Y)[o] = v;
@@ -177,16 +192,24 @@ __global__ __launch_bounds__(256) void gemm_kernel(const T* __restrict__ X, int6
   }
 }
 
+#ifndef MEDUSA_GEMM_NB
+#define MEDUSA_GEMM_NB 2
+#endif
+#ifndef MEDUSA_GEMM_KS
+#define MEDUSA_GEMM_KS 4
+#endif
+
 template <typename T, int EPI>
 static void launch_gemm_t(const void* X, int64_t xbs, int64_t M, int64_t Kd, const void* W,
                           int64_t Nw, int batch, const void* bias, const void* aux, void* Y,
                           int y_f32, hipStream_t st) {
-  const int TN = 16 * GEMM_NB;
+  constexpr int NB = MEDUSA_GEMM_NB, KS = MEDUSA_GEMM_KS;
+  constexpr int TN = 16 * NB;
   auto go = [&](auto mbc) {
     constexpr int MB = decltype(mbc)::value;
     dim3 grid((unsigned)((Nw + TN - 1) / TN), (unsigned)((M + 16 * MB - 1) / (16 * MB)),
               (unsigned)batch);
-    hipLaunchKernelGGL((gemm_kernel<T, MB, EPI>), grid, dim3(256), 0, st,
+    hipLaunchKernelGGL((gemm_kernel<T, MB, NB, KS, EPI>), grid, dim3(64 * KS), 0, st,
                        reinterpret_cast<const T*>(X), xbs, (int)M, (int)Kd,
                        reinterpret_cast<const T*>(W), (int)Nw, reinterpret_cast<const T*>(bias),
                        aux, Y, y_f32);

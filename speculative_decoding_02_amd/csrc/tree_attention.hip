@@ -18,16 +18,22 @@
 //   * online softmax in fp32 (base-2 exponent), per node; tree keys are
 //     kept iff their bit is set in the node's uint64 ancestor mask.
 //   * the tree keys' K/V are stored into cache slots ctx..ctx+N-1 by the
-//     workgroup that reads them (first query head of each kv group).
-//   * splits write (max, sum, unnormalised O) partials; the last split of a
-//     (sequence, head) to finish - found with one atomic counter - merges
-//     them in fixed split order and writes O.  Deterministic.
+//     workgroup whose split covers them (first query head of each kv group),
+//     after its tile loop.
+//   * a (sequence, head) whose key range needs one split writes O directly;
+//     otherwise every split writes (max, sum, unnormalised O) partials and a
+//     second, small launch merges them in fixed split order.  Deterministic;
+//     no cross-workgroup synchronisation inside a launch.
+//   * the tile loads run PF tiles ahead through a ring of register stages
+//     (unrolled, so every stage index is static), keeping a workgroup's whole
+//     key range in flight for the short ranges of decode-time splits.
 #include "common.h"
 
 namespace medusa {
 
 constexpr int ATT_TILE = 64;
 constexpr int ATT_THREADS = 256;
+constexpr int ATT_MAX_SPLIT_PAGES = 256;  // page-table window of one split (LDS)
 
 template <typename T, int D>
 struct AttnCfg {
@@ -70,20 +76,19 @@ struct AttnArgs {
   const int* ctx;
   const uint64_t* mask;
   void* O;
-  int* counters;     // [B*Hq]
   float2* ml;        // [B*Hq*S*N]  (running max in log2 units, sum)
   float* opart;      // [B*Hq*S*N*D]
   int max_pages, P, B, N, Hq, Hkv, chunk;  // chunk = keys per split (multiple of 64)
   float scale_log2;
 };
 
-template <typename T, int D>
+template <typename T, int D, int PF>
 __global__ __launch_bounds__(ATT_THREADS) void tree_attention_kernel(AttnArgs a) {
   using C = AttnCfg<T, D>;
   constexpr int P16 = C::P16;
   __shared__ __attribute__((aligned(16))) T Ks[ATT_TILE * C::LDK];
   __shared__ __attribute__((aligned(16))) T Vs[D * C::LDV];
-  __shared__ int s_last;
+  __shared__ int spages[ATT_MAX_SPLIT_PAGES];
 
   const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int S = gridDim.x;
@@ -111,13 +116,22 @@ __global__ __launch_bounds__(ATT_THREADS) void tree_attention_kernel(AttnArgs a)
   T* Vcp = reinterpret_cast<T*>(a.Vc);
   const int* pt = a.page_table + (int64_t)b * a.max_pages;
 
+  // The split's slice of the page table goes to LDS once, so that address
+  // computation never waits on a global load (a wait there would also wait
+  // for every tile load in flight).  Tree slots ctx..ctx+N-1 are in the
+  // slice too (the append needs them).
+  const int page0 = k_beg / a.P;
+  const int npages = (k_end - 1) / a.P - page0 + 1;
+  for (int i = threadIdx.x; i < npages; i += ATT_THREADS) spages[i] = pt[page0 + i];
+  __syncthreads();
+
   // element offset of key j's row for kv head kvh (cache slot or tree node)
   auto cache_off = [&](int j) -> int64_t {
-    const int page = pt[j / a.P];
+    const int page = spages[j / a.P - page0];
     return (((int64_t)page * a.Hkv + kvh) * a.P + (j % a.P)) * D;
   };
   auto tree_off = [&](int j) -> int64_t {
-    return (((int64_t)b * N + (j - ctxb)) * a.Hkv + kvh) * D;
+    return (((int64_t)b * N + max(j - ctxb, 0)) * a.Hkv + kvh) * D;
   };
 
   // ---- this wave's queries, B operand of S^T = K Q^T ----
@@ -129,23 +143,27 @@ __global__ __launch_bounds__(ATT_THREADS) void tree_attention_kernel(AttnArgs a)
       qf[st] = *reinterpret_cast<const u32x4*>(qrow + st * 4 * P16 + lg * P16);
   }
   const uint64_t mrow = a.mask[(int64_t)b * N + nodec];
+  // Queries and mask are in registers before any tile load is issued, so the
+  // loop never waits on them (a wait there would also drain the tile loads).
+  __builtin_amdgcn_s_waitcnt(0);
 
   // ---- tile loaders ----
-  u32x4 kreg[C::KPT];
-  u32x4 vreg[C::VPT][4];
-  const u32x4 zero = {0u, 0u, 0u, 0u};
+  u32x4 kreg[PF][C::KPT];
+  u32x4 vreg[PF][C::VPT][4];
 
-  // Branch-free loads: out-of-range keys read a valid row (clamped index) and
-  // are replaced by zeros, so the unrolled loops keep their registers.
-  auto gload = [&](int tile0) {
+  // Loads never feed a select (that would wait for them at once): keys past
+  // the split's end read a valid row (clamped index) whose score is masked
+  // to -inf later, so its probability is exactly 0 and its finite V adds 0.
+  auto gload = [&](int u, int tile0) {
 #pragma unroll
     for (int i = 0; i < C::KPT; ++i) {
       const int c = tid + i * ATT_THREADS;
       const int key = c / (D / P16), part = c % (D / P16);
-      const int j = tile0 + key, jj = min(j, k_end - 1);
-      const T* src = (jj < ctxb ? Kcp + cache_off(jj) : Ktp + tree_off(jj)) + part * P16;
-      const u32x4 v = *reinterpret_cast<const u32x4*>(src);
-      kreg[i] = j < k_end ? v : zero;
+      const int jj = min(tile0 + key, k_end - 1);
+      const T* kc = Kcp + cache_off(jj);
+      const T* kt = Ktp + tree_off(jj);
+      const T* src = (jj < ctxb ? kc : kt) + part * P16;
+      kreg[u][i] = *reinterpret_cast<const u32x4*>(src);
     }
 #pragma unroll
     for (int i = 0; i < C::VPT; ++i) {
@@ -153,23 +171,21 @@ __global__ __launch_bounds__(ATT_THREADS) void tree_attention_kernel(AttnArgs a)
       const int kg = g / (D / P16), dg = g % (D / P16);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int j = tile0 + kg * 4 + r, jj = min(j, k_end - 1);
-        const T* src = (jj < ctxb ? Vcp + cache_off(jj) : Vtp + tree_off(jj)) + dg * P16;
-        const u32x4 v = *reinterpret_cast<const u32x4*>(src);
-        vreg[i][r] = j < k_end ? v : zero;
+        const int jj = min(tile0 + kg * 4 + r, k_end - 1);
+        const T* vc = Vcp + cache_off(jj);
+        const T* vt = Vtp + tree_off(jj);
+        const T* src = (jj < ctxb ? vc : vt) + dg * P16;
+        vreg[u][i][r] = *reinterpret_cast<const u32x4*>(src);
       }
     }
   };
 
-  auto lds_store = [&](int tile0) {
+  auto lds_store = [&](int u, int tile0) {
 #pragma unroll
     for (int i = 0; i < C::KPT; ++i) {
       const int c = tid + i * ATT_THREADS;
       const int key = c / (D / P16), part = c % (D / P16);
-      *reinterpret_cast<u32x4*>(&Ks[key * C::LDK + part * P16]) = kreg[i];
-      const int j = tile0 + key;
-      if (appender && j >= ctxb && j < k_end)
-        *reinterpret_cast<u32x4*>(Kcp + cache_off(j) + part * P16) = kreg[i];
+      *reinterpret_cast<u32x4*>(&Ks[key * C::LDK + part * P16]) = kreg[u][i];
     }
 #pragma unroll
     for (int i = 0; i < C::VPT; ++i) {
@@ -182,23 +198,15 @@ __global__ __launch_bounds__(ATT_THREADS) void tree_attention_kernel(AttnArgs a)
           for (int e = 0; e < 8; ++e) {
             const int sh = (e & 1) * 16, wi = e >> 1;
             u32x2 v;
-            v.x = ((u4c(vreg[i][0], wi) >> sh) & 0xffffu) | (((u4c(vreg[i][1], wi) >> sh) & 0xffffu) << 16);
-            v.y = ((u4c(vreg[i][2], wi) >> sh) & 0xffffu) | (((u4c(vreg[i][3], wi) >> sh) & 0xffffu) << 16);
+            v.x = ((u4c(vreg[u][i][0], wi) >> sh) & 0xffffu) | (((u4c(vreg[u][i][1], wi) >> sh) & 0xffffu) << 16);
+            v.y = ((u4c(vreg[u][i][2], wi) >> sh) & 0xffffu) | (((u4c(vreg[u][i][3], wi) >> sh) & 0xffffu) << 16);
             *reinterpret_cast<u32x2*>(&Vs[(d0 + e) * C::LDV + key0]) = v;
           }
         } else {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            u32x4 v = {u4c(vreg[i][0], e), u4c(vreg[i][1], e), u4c(vreg[i][2], e), u4c(vreg[i][3], e)};
+            u32x4 v = {u4c(vreg[u][i][0], e), u4c(vreg[u][i][1], e), u4c(vreg[u][i][2], e), u4c(vreg[u][i][3], e)};
             *reinterpret_cast<u32x4*>(&Vs[(d0 + e) * C::LDV + key0]) = v;
-          }
-        }
-        if (appender) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int j = tile0 + key0 + r;
-            if (j >= ctxb && j < k_end)
-              *reinterpret_cast<u32x4*>(Vcp + cache_off(j) + d0) = vreg[i][r];
           }
         }
       }
@@ -212,13 +220,21 @@ __global__ __launch_bounds__(ATT_THREADS) void tree_attention_kernel(AttnArgs a)
   for (int db = 0; db < DB; ++db) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
   float mrun = -INFINITY, lrun = 0.f;
 
+  // Prologue and refills load unconditionally (tile index clamped to the
+  // split's last tile), so the waits before each tile count only later loads.
   const int ntiles = (k_end - k_beg + ATT_TILE - 1) / ATT_TILE;
-  gload(k_beg);
-  for (int t = 0; t < ntiles; ++t) {
+  const int last_tile0 = k_beg + (ntiles - 1) * ATT_TILE;
+#pragma unroll
+  for (int u = 0; u < PF; ++u) gload(u, min(k_beg + u * ATT_TILE, last_tile0));
+  for (int t0 = 0; t0 < ntiles; t0 += PF) {
+#pragma unroll
+  for (int u = 0; u < PF; ++u) {
+    const int t = t0 + u;
+    if (t >= ntiles) break;
     const int tile0 = k_beg + t * ATT_TILE;
-    lds_store(tile0);
+    lds_store(u, tile0);
     __syncthreads();
-    if (t + 1 < ntiles) gload(tile0 + ATT_TILE);
+    gload(u, min(tile0 + PF * ATT_TILE, last_tile0));
 
     if (wave_active) {
       f32x4 sacc[4];
@@ -239,8 +255,8 @@ __global__ __launch_bounds__(ATT_THREADS) void tree_attention_kernel(AttnArgs a)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int j = tile0 + kb * 16 + lg * 4 + r;
-          bool ok = j < k_end;
-          if (j >= ctxb) ok = ok && ((mrow >> (uint32_t)(min(j - ctxb, 63))) & 1ull);
+          const uint32_t bit = (uint32_t)(mrow >> (uint32_t)min(max(j - ctxb, 0), 63)) & 1u;
+          const bool ok = (j < k_end) & ((j < ctxb) | (bit != 0u));
           x[kb][r] = ok ? sacc[kb][r] * a.scale_log2 : -INFINITY;
           tmax = fmaxf(tmax, x[kb][r]);
         }
@@ -289,6 +305,22 @@ __global__ __launch_bounds__(ATT_THREADS) void tree_attention_kernel(AttnArgs a)
     }
     __syncthreads();
   }
+  }
+
+  // Store the tree keys' K/V of this split into cache slots ctx..ctx+N-1
+  // (after the tile loop, so these stores never sit between tile loads).
+  if (appender && k_end > ctxb) {
+    constexpr int CPR = D / P16;  // 16-byte chunks per row
+    const int j0 = max(k_beg, ctxb);
+    const int items = (k_end - j0) * CPR * 2;
+    for (int e = tid; e < items; e += ATT_THREADS) {
+      const int which = e / ((k_end - j0) * CPR), rem = e % ((k_end - j0) * CPR);
+      const int j = j0 + rem / CPR, part = rem % CPR;
+      const T* src = (which ? Vtp : Ktp) + tree_off(j) + part * P16;
+      T* dst = (which ? Vcp : Kcp) + cache_off(j) + part * P16;
+      *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src);
+    }
+  }
 
   float ltot = lrun + __shfl_xor(lrun, 16, 64);
   ltot = ltot + __shfl_xor(ltot, 32, 64);
@@ -307,82 +339,83 @@ __global__ __launch_bounds__(ATT_THREADS) void tree_attention_kernel(AttnArgs a)
     return;
   }
 
-  // ---- multi-split: partials, then the last split merges ----
+  // ---- multi-split: partials; tree_attention_combine merges them ----
   const int64_t bh = (int64_t)b * a.Hq + h;
   if (node_ok) {
     float* op = a.opart + ((bh * S + s) * N + node) * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
-      *reinterpret_cast<float4*>(op + db * 16 + lg * 4) =
-          make_float4(oacc[db][0], oacc[db][1], oacc[db][2], oacc[db][3]);
+      *reinterpret_cast<f32x4*>(op + db * 16 + lg * 4) = oacc[db];
     if (lg == 0) a.ml[(bh * S + s) * N + node] = make_float2(mrun, ltot);
   }
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    const int prev = atomicAdd(&a.counters[bh], 1);
-    s_last = (prev == nsplit - 1);
-  }
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
+}
 
+// Merge of the split partials of one (sequence, head): O = sum_s w_s O_s /
+// sum_s w_s l_s with w_s = 2^(m_s - max m), splits in index order.
+template <typename T, int D>
+__global__ __launch_bounds__(ATT_THREADS) void tree_attention_combine_kernel(AttnArgs a, int S) {
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int N = a.N;
+  const int total = a.ctx[b] + N;
+  const int nsplit = (total + a.chunk - 1) / a.chunk;
+  if (nsplit <= 1) return;
+  const int64_t bh = (int64_t)b * a.Hq + h;
+  T* Op = reinterpret_cast<T*>(a.O);
   constexpr int D4 = D / 4;
-  for (int it = tid; it < N * D4; it += ATT_THREADS) {
+  for (int it = threadIdx.x; it < N * D4; it += ATT_THREADS) {
     const int n = it / D4, d0 = (it % D4) * 4;
     float M = -INFINITY;
     for (int q = 0; q < nsplit; ++q) M = fmaxf(M, a.ml[(bh * S + q) * N + n].x);
     float L = 0.f;
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     for (int q = 0; q < nsplit; ++q) {
       const float2 mlq = a.ml[(bh * S + q) * N + n];
       const float w = (mlq.x == -INFINITY) ? 0.f : exp2f(mlq.x - M);
       L += w * mlq.y;
-      const float4 o = *reinterpret_cast<const float4*>(a.opart + ((bh * S + q) * N + n) * D + d0);
-      acc.x += w * o.x;
-      acc.y += w * o.y;
-      acc.z += w * o.z;
-      acc.w += w * o.w;
+      acc += w * *reinterpret_cast<const f32x4*>(a.opart + ((bh * S + q) * N + n) * D + d0);
     }
     const float inv = 1.f / L;
     T* orow = Op + (((int64_t)b * N + n) * a.Hq + h) * D;
-    st<T>(orow, d0 + 0, acc.x * inv);
-    st<T>(orow, d0 + 1, acc.y * inv);
-    st<T>(orow, d0 + 2, acc.z * inv);
-    st<T>(orow, d0 + 3, acc.w * inv);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) st<T>(orow, d0 + r, acc[r] * inv);
   }
-  if (tid == 0) a.counters[bh] = 0;
 }
 
 }  // namespace medusa
 
 namespace {
 
-// Keys per split and number of splits.  A split is a whole number of 64-key
-// tiles; the count aims at ~4 workgroups per compute unit.
+// Keys per split and number of splits: a split is a whole number of 64-key
+// tiles, sized so that B * Hq * splits is near MEDUSA_ATTN_TARGET_WGS
+// workgroups (about one to two per compute unit).
+#ifndef MEDUSA_ATTN_TARGET_WGS
+#define MEDUSA_ATTN_TARGET_WGS 384
+#endif
+#ifndef MEDUSA_ATTN_PF
+#define MEDUSA_ATTN_PF 2
+#endif
 struct SplitPlan {
   int chunk, splits;
 };
-SplitPlan plan_splits(int B, int Hq, int N, int max_ctx) {
+SplitPlan plan_splits(int B, int Hq, int N, int max_ctx, int P) {
   const int total = max_ctx + N;
-  const int tiles = (total + medusa::ATT_TILE - 1) / medusa::ATT_TILE;
-  const int target_wgs = 1024;
   const int bh = B * Hq;
-  const int want = (target_wgs + bh - 1) / bh;
-  int tps = (tiles + want - 1) / want;
-  if (tps < 1) tps = 1;
-  const int chunk = tps * medusa::ATT_TILE;
+  const int want = (MEDUSA_ATTN_TARGET_WGS + bh - 1) / bh;
+  int chunk = (total + want - 1) / want;
+  chunk = (chunk + medusa::ATT_TILE - 1) / medusa::ATT_TILE * medusa::ATT_TILE;
+  // a split's keys must span at most ATT_MAX_SPLIT_PAGES pages
+  const int cap = ((medusa::ATT_MAX_SPLIT_PAGES - 1) * P) / medusa::ATT_TILE * medusa::ATT_TILE;
+  if (cap >= medusa::ATT_TILE && chunk > cap) chunk = cap;
   return {chunk, (total + chunk - 1) / chunk};
 }
 
 struct WsLayout {
-  size_t counters, ml, opart, total;
+  size_t ml, opart, total;
 };
 WsLayout ws_layout(int B, int Hq, int N, int D, int S) {
   using medusa_host::align_up;
   WsLayout w;
-  w.counters = 0;
-  w.ml = align_up((size_t)B * Hq * sizeof(int), 256);
+  w.ml = 0;
   w.opart = w.ml + align_up((size_t)B * Hq * S * N * sizeof(float2), 256);
   w.total = w.opart + align_up((size_t)B * Hq * S * N * D * sizeof(float), 256);
   return w;
@@ -391,10 +424,10 @@ WsLayout ws_layout(int B, int Hq, int N, int D, int S) {
 }  // namespace
 
 extern "C" size_t medusa_tree_attention_ws(int32_t B, int32_t N, int32_t Hq, int32_t Hkv,
-                                           int32_t D, int32_t max_ctx) {
+                                           int32_t D, int32_t max_ctx, int32_t P) {
   (void)Hkv;
-  if (B <= 0 || N <= 0 || Hq <= 0 || D <= 0 || max_ctx < 0) return 0;
-  const SplitPlan p = plan_splits(B, Hq, N, max_ctx);
+  if (B <= 0 || N <= 0 || Hq <= 0 || D <= 0 || max_ctx < 0 || P < 1) return 0;
+  const SplitPlan p = plan_splits(B, Hq, N, max_ctx, P);
   return ws_layout(B, Hq, N, D, p.splits).total;
 }
 
@@ -416,6 +449,8 @@ extern "C" int32_t medusa_tree_attention(const void* Q, const void* Kt, const vo
                  Hkv);
   MEDUSA_REQUIRE(P >= 1 && max_pages >= 1 && max_ctx >= 0, MEDUSA_ERR_INVALID_ARG,
                  "medusa_tree_attention: P=%d max_pages=%d max_ctx=%d", P, max_pages, max_ctx);
+  MEDUSA_REQUIRE(P >= 4 && P <= 4096, MEDUSA_ERR_UNSUPPORTED,
+                 "medusa_tree_attention: page size %d outside [4, 4096]", P);
   MEDUSA_REQUIRE((int64_t)max_ctx + N <= (int64_t)max_pages * P, MEDUSA_ERR_INVALID_ARG,
                  "medusa_tree_attention: max_ctx + N = %d exceeds max_pages * P = %lld",
                  max_ctx + N, (long long)max_pages * P);
@@ -427,7 +462,7 @@ extern "C" int32_t medusa_tree_attention(const void* Q, const void* Kt, const vo
   MEDUSA_REQUIRE(((uintptr_t)Q | (uintptr_t)Kt | (uintptr_t)Vt | (uintptr_t)Kc | (uintptr_t)Vc) %
                          16 == 0,
                  MEDUSA_ERR_INVALID_ARG, "medusa_tree_attention: tensors must be 16-byte aligned");
-  const SplitPlan p = plan_splits(B, Hq, N, max_ctx);
+  const SplitPlan p = plan_splits(B, Hq, N, max_ctx, P);
   const WsLayout L = ws_layout(B, Hq, N, D, p.splits);
   MEDUSA_REQUIRE(ws != NULL && ws_bytes >= L.total, MEDUSA_ERR_WORKSPACE,
                  "medusa_tree_attention: workspace %zu < %zu bytes", ws_bytes, L.total);
@@ -437,20 +472,28 @@ extern "C" int32_t medusa_tree_attention(const void* Q, const void* Kt, const vo
   medusa::AttnArgs a;
   a.Q = Q; a.Kt = Kt; a.Vt = Vt; a.Kc = Kc; a.Vc = Vc;
   a.page_table = page_table; a.ctx = ctx; a.mask = mask; a.O = O;
-  a.counters = (int*)((char*)ws + L.counters);
   a.ml = (float2*)((char*)ws + L.ml);
   a.opart = (float*)((char*)ws + L.opart);
   a.max_pages = max_pages; a.P = P; a.B = B; a.N = N; a.Hq = Hq; a.Hkv = Hkv;
   a.chunk = p.chunk;
   a.scale_log2 = scale * 1.4426950408889634f;
   dim3 grid((unsigned)p.splits, (unsigned)Hq, (unsigned)B);
+  dim3 cgrid((unsigned)Hq, (unsigned)B);
   hipStream_t st = (hipStream_t)stream;
+  const dim3 blk(medusa::ATT_THREADS);
+  constexpr int PF = MEDUSA_ATTN_PF;
+#define MEDUSA_ATT_LAUNCH(T, DD)                                                             \
+  do {                                                                                       \
+    hipLaunchKernelGGL((medusa::tree_attention_kernel<T, DD, PF>), grid, blk, 0, st, a);     \
+    if (p.splits > 1)                                                                        \
+      hipLaunchKernelGGL((medusa::tree_attention_combine_kernel<T, DD>), cgrid, blk, 0, st,  \
+                         a, p.splits);                                                       \
+  } while (0)
   if (dt == MEDUSA_BF16) {
-    if (D == 128) hipLaunchKernelGGL((medusa::tree_attention_kernel<medusa::bf16_t, 128>), grid, dim3(medusa::ATT_THREADS), 0, st, a);
-    else hipLaunchKernelGGL((medusa::tree_attention_kernel<medusa::bf16_t, 64>), grid, dim3(medusa::ATT_THREADS), 0, st, a);
+    if (D == 128) MEDUSA_ATT_LAUNCH(medusa::bf16_t, 128); else MEDUSA_ATT_LAUNCH(medusa::bf16_t, 64);
   } else {
-    if (D == 128) hipLaunchKernelGGL((medusa::tree_attention_kernel<float, 128>), grid, dim3(medusa::ATT_THREADS), 0, st, a);
-    else hipLaunchKernelGGL((medusa::tree_attention_kernel<float, 64>), grid, dim3(medusa::ATT_THREADS), 0, st, a);
+    if (D == 128) MEDUSA_ATT_LAUNCH(float, 128); else MEDUSA_ATT_LAUNCH(float, 64);
   }
+#undef MEDUSA_ATT_LAUNCH
   return check_launch("medusa_tree_attention");
 }

@@ -57,9 +57,30 @@ class DeviceModel:
             tensors = t
         self.meta = meta
         self.t = tensors
+        if "wqkv" not in tensors["layers"][0]:  # Llama layout -> GPU layout (one-time copy)
+            self.t = dict(tensors)
+            self.t["layers"] = [self._gpu_layout(L) for L in tensors["layers"]]
         for k, v in meta.items():
-            setattr(self, k, v)
+            if k != "seed":
+                setattr(self, k, v)
         self.n_medusa = tensors["w1"].shape[0]
+
+
+    @staticmethod
+    def _gpu_layout(L):
+        wg, wu = L["wg"], L["wu"]
+        F, H = wg.shape
+        wgu = torch.stack([wg.reshape(F // 16, 16, H), wu.reshape(F // 16, 16, H)], 1)
+        return dict(wqkv=torch.cat([L["wq"], L["wk"], L["wv"]], 0).contiguous(), wo=L["wo"],
+                    wgu=wgu.reshape(2 * F, H).contiguous(), wd=L["wd"], g_attn=L["g_attn"],
+                    g_mlp=L["g_mlp"])
+
+    @classmethod
+    def from_llama(cls, d):
+        """Build from ``synth.device_llama`` output (tensors already on the GPU)."""
+        t = {k: v for k, v in d.items() if k != "meta"}
+        return cls(None, dtype=d["embed"].dtype, device=d["embed"].device, tensors=t,
+                   meta=dict(d["meta"]))
 
 
 class MedusaDecoder:
@@ -103,7 +124,7 @@ class MedusaDecoder:
         self.topk_vals = torch.zeros((Kh, 1, self.width), dtype=torch.float32, device=dev)
         self.max_ctx = self.capacity - 64          # every call has ctx + n <= capacity
         self.attn_ws = M._ws(max(M.tree_attention_ws_bytes(1, n, model.n_heads, model.n_kv_heads,
-                                                           model.head_dim, self.max_ctx)
+                                                           model.head_dim, self.max_ctx, page_size)
                                  for n in range(1, 65)), dev, zero=True)
         self.acc_ws = M._ws(M._lib.medusa_accept_ws(1, 64), dev)
         dt = M._dt(model.t["embed"])
@@ -188,12 +209,38 @@ class MedusaDecoder:
         self.last = dict(tokens=tokens, logits=logits, hN=hN, pos=pos, mask=mask)
         return acc, path, tokens
 
-    def generate(self, prompt, n_new, record=None):
+    # ------------------------------------------------------------------
+    def capture(self):
+        """Record one decode step as a HIP graph (replayed by ``step_graph``).
+
+        Every call of the step reads its changing state (ctx, root token,
+        top-k ids) from device memory and has static shapes, so one recording
+        serves every later step; recording runs nothing.  Workspaces are all
+        preallocated, so the graph holds no allocation and no memset."""
+        self.graph = torch.cuda.CUDAGraph()
+        stream = torch.cuda.Stream()
+        stream.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(stream):
+            with torch.cuda.graph(self.graph, stream=stream):
+                self.g_out = self.step()
+                self.g_last = self.last
+        torch.cuda.current_stream().wait_stream(stream)
+        return self.graph
+
+    def step_graph(self):
+        """Replay the recorded step; same outputs as ``step``."""
+        self.graph.replay()
+        self.last = self.g_last
+        return self.g_out
+
+    def generate(self, prompt, n_new, record=None, graph=False):
         """Prefill, then Medusa steps until n_new tokens are emitted.  Returns int32[n_new]."""
         self.prefill(prompt)
+        if graph and getattr(self, "graph", None) is None:
+            self.capture()
         out = []
         while len(out) < n_new:
-            acc, path, tokens = self.step()
+            acc, path, tokens = self.step_graph() if graph else self.step()
             a = int(acc.item())
             p = path[0, :a + 1].cpu().numpy()
             tk = tokens[0].cpu().numpy()

@@ -32,7 +32,7 @@ _SIGS = {
     "medusa_heads": (i32, [vp, i64, i64, i32, vp, vp, vp, i64, i32, vp, i32, vp, vp, vp, sz, vp]),
     "medusa_topk": (i32, [vp, i64, i64, i32, vp, vp, vp]),
     "medusa_build_tree": (i32, [i32, i32, vp, vp, vp, vp, i32, i32, vp, vp, vp, vp, vp]),
-    "medusa_tree_attention_ws": (sz, [i32, i32, i32, i32, i32, i32]),
+    "medusa_tree_attention_ws": (sz, [i32, i32, i32, i32, i32, i32, i32]),
     "medusa_tree_attention": (i32, [vp, vp, vp, vp, vp, vp, i32, i32, vp, i32, vp, i32, i32, i32,
                                     i32, i32, f32, i32, vp, vp, sz, vp]),
     "medusa_accept_ws": (sz, [i32, i32]),
@@ -102,6 +102,8 @@ def _p(t):
 
 
 def _ws(nbytes, device, zero=False):
+    if torch.cuda.is_current_stream_capturing():
+        raise RuntimeError("workspace allocation during graph capture: preallocate it")
     nbytes = max(int(nbytes), 256)
     f = torch.zeros if zero else torch.empty
     return f(nbytes, dtype=torch.uint8, device=device)
@@ -186,8 +188,8 @@ def medusa_build_tree(parent, rank, root_tok, topk_ids, ctx, tokens=None, pos=No
     return tokens, pos, mask
 
 
-def tree_attention_ws_bytes(B, N, Hq, Hkv, D, max_ctx):
-    return _lib.medusa_tree_attention_ws(B, N, Hq, Hkv, D, max_ctx)
+def tree_attention_ws_bytes(B, N, Hq, Hkv, D, max_ctx, P=16):
+    return _lib.medusa_tree_attention_ws(B, N, Hq, Hkv, D, max_ctx, P)
 
 
 def medusa_tree_attention(Q, Kt, Vt, Kc, Vc, page_table, ctx, max_ctx, mask, scale, out=None,
@@ -198,7 +200,7 @@ def medusa_tree_attention(Q, Kt, Vt, Kc, Vc, page_table, ctx, max_ctx, mask, sca
     B, N, Hq, D = Q.shape
     Hkv, P = Kc.shape[1], Kc.shape[2]
     out = out if out is not None else torch.empty_like(Q)
-    need = _lib.medusa_tree_attention_ws(B, N, Hq, Hkv, D, int(max_ctx))
+    need = _lib.medusa_tree_attention_ws(B, N, Hq, Hkv, D, int(max_ctx), P)
     if ws is None or ws.numel() < need:
         ws = _ws(need, Q.device, zero=True)
     _check("medusa_tree_attention", _lib.medusa_tree_attention(

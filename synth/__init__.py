@@ -262,3 +262,49 @@ def heads_inputs(seed, M, H, V, K, w1_std=0.01, w2_std=0.02, x_std=1.0, bf16=Tru
     b1 = rnd(gb.standard_normal((K, H), dtype=np.float32) * np.float32(w1_std))
     W2 = rnd(g2.standard_normal((K, V, H), dtype=np.float32) * np.float32(w2_std))
     return dict(X=X, W1=W1, b1=b1, W2=W2)
+
+
+# ----------------------------------------------------------------------------
+# large random decoders, drawn on the GPU (seeded torch generator)
+# ----------------------------------------------------------------------------
+def device_llama(seed, n_layers=32, hidden=4096, n_heads=32, n_kv_heads=None, head_dim=128,
+                 ffn=11008, vocab=32000, n_medusa=5, std=0.02, head_std=0.01, dtype=None,
+                 device="cuda"):
+    """Random-init Llama-style decoder + Medusa heads as device tensors.
+
+    Same recipe as ``tiny_decoder`` (weights ~ N(0, std), gains 1, W1 ~
+    N(0, head_std), b1 = 0, W2_k = lm_head) but drawn by a seeded torch
+    generator on ``device`` in float32 and cast to ``dtype`` (default bf16).
+    Draw order: embedding, per layer wq wk wv wo wg wu wd, lm_head, W1.
+    Returns a dict with ``meta``, ``embed``, ``layers`` (list of dicts with
+    the Llama layout), ``g_final``, ``lm_head``, ``w1``, ``b1``, ``w2``.
+    """
+    import torch
+
+    dtype = dtype or torch.bfloat16
+    n_kv_heads = n_heads if n_kv_heads is None else n_kv_heads
+    gen = torch.Generator(device=device)
+    gen.manual_seed(int(seed))
+
+    def draw(shape, s):
+        t = torch.randn(shape, generator=gen, device=device, dtype=torch.float32)
+        return t.mul_(s).to(dtype)
+
+    ones = lambda n: torch.ones(n, device=device, dtype=dtype)
+    qd, kd = n_heads * head_dim, n_kv_heads * head_dim
+    out = dict(meta=dict(vocab=vocab, hidden=hidden, n_layers=n_layers, n_heads=n_heads,
+                         n_kv_heads=n_kv_heads, head_dim=head_dim, ffn=ffn, rope_base=10000.0,
+                         eps=1e-5, seed=seed))
+    out["embed"] = draw((vocab, hidden), std)
+    out["layers"] = []
+    for _ in range(n_layers):
+        out["layers"].append(dict(
+            wq=draw((qd, hidden), std), wk=draw((kd, hidden), std), wv=draw((kd, hidden), std),
+            wo=draw((hidden, qd), std), wg=draw((ffn, hidden), std), wu=draw((ffn, hidden), std),
+            wd=draw((hidden, ffn), std), g_attn=ones(hidden), g_mlp=ones(hidden)))
+    out["lm_head"] = draw((vocab, hidden), std)
+    out["g_final"] = ones(hidden)
+    out["w1"] = draw((n_medusa, hidden, hidden), head_std)
+    out["b1"] = torch.zeros((n_medusa, hidden), device=device, dtype=dtype)
+    out["w2"] = out["lm_head"].unsqueeze(0).repeat(n_medusa, 1, 1).contiguous()
+    return out

@@ -191,8 +191,8 @@ def test_tree_attention(lib, B, N, Hq, Hkv, D, ctx, P, perm, dt):
 
 
 def test_tree_attention_chain_is_causal_and_repeatable(lib):
-    """Chain tree = causal attention; a second call on the same workspace (its
-    counters left zero by the first) gives bitwise equal output."""
+    """Chain tree = causal attention; a second call on the same workspace gives
+    bitwise equal output (fixed merge order, no atomics)."""
     case("tree_attention chain + repeat")
     B, N, H, D, c = 1, 64, 4, 128, 1500
     d = synth.attention_inputs(9, B, N, H, H, D, c, bf16=True)
@@ -200,7 +200,7 @@ def test_tree_attention_chain_is_causal_and_repeatable(lib):
     args = [dev(d["Q"], torch.bfloat16), dev(d["Kt"], torch.bfloat16), dev(d["Vt"], torch.bfloat16),
             dev(d["Kc"], torch.bfloat16), dev(d["Vc"], torch.bfloat16), dev(d["page_table"]),
             dev(d["ctx"]), c, dev(mask), float(d["scale"])]
-    ws = lib._ws(lib.tree_attention_ws_bytes(B, N, H, H, D, c), "cuda", zero=True)
+    ws = lib._ws(lib.tree_attention_ws_bytes(B, N, H, H, D, c), "cuda")
     o1 = lib.medusa_tree_attention(*args, ws=ws).clone()
     o2 = lib.medusa_tree_attention(*args, ws=ws)
     assert torch.equal(o1, o2)
@@ -208,7 +208,6 @@ def test_tree_attention_chain_is_causal_and_repeatable(lib):
     vc = orc.cache_rows(d["Vc"], d["page_table"][0], c, 16)
     ref = orc.tree_attention(d["Q"][0], kc, vc, d["Kt"][0], d["Vt"][0], mask[0], d["scale"])
     assert_close(host(o1[0]), ref, 2e-2, "chain")
-    assert int(ws[:4 * B * H].view(torch.int32).abs().sum().item()) == 0
 
 
 # ------------------------------------------------------------------ accept ---
