@@ -131,9 +131,11 @@ int32_t medusa_heads(const void* X, int64_t M, int64_t H, int32_t K, const void*
 
 /* medusa_topk: top-k of each float row ("Medusa Heads", tree section: the
  * heads' best guesses).  logits [R, V] float -> ids [R, k] int32, vals [R, k]
- * float; order value descending, ties by lower index; 1 <= k <= 64, k <= V. */
+ * float; order value descending, ties by lower index; 1 <= k <= 64, k <= V.
+ * ws: medusa_topk_ws(R, V, k) bytes (0 when V <= 4096; then ws may be NULL). */
+size_t medusa_topk_ws(int64_t R, int64_t V, int32_t k);
 int32_t medusa_topk(const float* logits, int64_t R, int64_t V, int32_t k, int32_t* ids,
-                    float* vals, void* stream);
+                    float* vals, void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
  * medusa_build_tree: fill B tree templates with tokens ("Medusa Heads",

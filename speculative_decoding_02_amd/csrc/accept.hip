@@ -38,7 +38,23 @@ __global__ __launch_bounds__(256) void accept_stats_kernel(const float* __restri
 
   float bv = -INFINITY;
   int bi = 0x7fffffff;
-  for (int64_t e = tid; e < V; e += 256) arg_better(bv, bi, z[e], (int)e);
+  // 16-byte loads, four in flight per thread before any comparison
+  const bool vec = (V % 4 == 0) && (((uintptr_t)z) % 16 == 0);
+  const int64_t V4 = vec ? V / 4 : 0;
+  for (int64_t e0 = tid; e0 < V4; e0 += 4 * 256) {
+    f32x4 q[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t e = min(e0 + u * 256, V4 - 1);
+      q[u] = reinterpret_cast<const f32x4*>(z)[e];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (e0 + u * 256 < V4)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) arg_better(bv, bi, q[u][r], (int)((e0 + u * 256) * 4 + r));
+  }
+  for (int64_t e = V4 * 4 + tid; e < V; e += 256) arg_better(bv, bi, z[e], (int)e);
   for (int o = 32; o > 0; o >>= 1) {
     const float ov = __shfl_xor(bv, o, 64);
     const int oi = __shfl_xor(bi, o, 64);
@@ -59,7 +75,22 @@ __global__ __launch_bounds__(256) void accept_stats_kernel(const float* __restri
     // m = max(z/T) = max(z)/T for T > 0
     const float m = rs.m;
     float s = 0.f, e1 = 0.f;
-    for (int64_t e = tid; e < V; e += 256) {
+    for (int64_t e0 = tid; e0 < V4; e0 += 4 * 256) {
+      f32x4 q[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) q[u] = reinterpret_cast<const f32x4*>(z)[min(e0 + u * 256, V4 - 1)];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (e0 + u * 256 < V4)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float y = q[u][r] * inv_t - m;
+            const float p = expf(y);
+            s += p;
+            e1 += p * y;
+          }
+    }
+    for (int64_t e = V4 * 4 + tid; e < V; e += 256) {
       const float y = z[e] * inv_t - m;
       const float p = expf(y);
       s += p;

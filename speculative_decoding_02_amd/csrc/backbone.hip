@@ -15,30 +15,44 @@ __global__ __launch_bounds__(256) void embed_kernel(const int* __restrict__ toke
   for (int64_t e = threadIdx.x; e < H; e += 256) out[m * H + e] = ld<T>(row, e);
 }
 
-// One workgroup per row; fixed-order reduction (per-thread strided sums, then
-// a butterfly inside each wave, then waves in order).
+// One wave per row (4 rows per workgroup, no block barrier): 16-byte loads,
+// per-lane partial sums in a fixed order, then a butterfly over the wave;
+// the second pass re-reads the row (L2 hit) to normalise.
 template <typename T>
-__global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ x, int64_t H,
-                                                      const T* __restrict__ gain, float eps,
-                                                      T* __restrict__ out) {
-  const int64_t m = blockIdx.x;
+__global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ x, int64_t M,
+                                                      int64_t H, const T* __restrict__ gain,
+                                                      float eps, T* __restrict__ out) {
+  const int64_t m = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (m >= M) return;
+  const int lane = threadIdx.x & 63;
   const float* xr = x + m * H;
+  const int64_t H4 = (H % 4 == 0) ? H / 4 : 0;
   float ss = 0.f;
-  for (int64_t e = threadIdx.x; e < H; e += 256) ss += xr[e] * xr[e];
+  for (int64_t e = lane; e < H4; e += 64) {
+    const f32x4 v = reinterpret_cast<const f32x4*>(xr)[e];
+    ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+  }
+  for (int64_t e = H4 * 4 + lane; e < H; e += 64) ss += xr[e] * xr[e];
   ss = wave_sum(ss);
-  __shared__ float part[4];
-  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
-  __syncthreads();
-  const float tot = (part[0] + part[1]) + (part[2] + part[3]);
-  const float rs = 1.0f / sqrtf(tot / (float)H + eps);
-  for (int64_t e = threadIdx.x; e < H; e += 256) {
+  const float rs = 1.0f / sqrtf(ss / (float)H + eps);
+  T* orow = out + m * H;
+  for (int64_t e = lane; e < H4; e += 64) {
+    const f32x4 v = reinterpret_cast<const f32x4*>(xr)[e];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float g = gain ? ld<T>(gain, e * 4 + r) : 1.f;
+      st<T>(orow, e * 4 + r, v[r] * rs * g);
+    }
+  }
+  for (int64_t e = H4 * 4 + lane; e < H; e += 64) {
     const float g = gain ? ld<T>(gain, e) : 1.f;
-    st<T>(out, m * H + e, xr[e] * rs * g);
+    st<T>(orow, e, xr[e] * rs * g);
   }
 }
 
-// Rotary positions, rotate-half pairs (j, j + D/2), angle pos * base^(-2j/D);
-// the angles and their cosines / sines are evaluated in fp64 once per row.
+// Rotary positions, rotate-half pairs (j, j + D/2), angle pos * base^(-2j/D).
+// The angle is formed and reduced to [-pi, pi] in fp64, then its cosine and
+// sine are taken in fp32; one pass per row over 4 consecutive j per thread.
 template <typename T>
 __global__ __launch_bounds__(256) void qkv_rope_kernel(const T* __restrict__ qkv, int Hq, int Hkv,
                                                        int D, const int* __restrict__ pos,
@@ -49,25 +63,34 @@ __global__ __launch_bounds__(256) void qkv_rope_kernel(const T* __restrict__ qkv
   const int half = D / 2;
   if (threadIdx.x < half) {
     const double inv = exp2(-(2.0 * threadIdx.x / D) * log2_base);
-    const double ang = (double)pos[m] * inv;
-    cs[threadIdx.x] = (float)cos(ang);
-    sn[threadIdx.x] = (float)sin(ang);
+    double ang = (double)pos[m] * inv;
+    const double two_pi = 6.283185307179586476925286766559;
+    ang -= two_pi * rint(ang / two_pi);
+    float c, sv;
+    sincosf((float)ang, &sv, &c);
+    cs[threadIdx.x] = c;
+    sn[threadIdx.x] = sv;
   }
   __syncthreads();
   const int W = (Hq + 2 * Hkv) * D;
   const T* in = qkv + m * W;
-  // rotated part: q and k heads, one pair per thread step
-  const int pairs = (Hq + Hkv) * half;
-  for (int e = threadIdx.x; e < pairs; e += 256) {
-    const int hh = e / half, j = e % half;
-    const float x1 = ld<T>(in, (int64_t)hh * D + j), x2 = ld<T>(in, (int64_t)hh * D + j + half);
-    const float o1 = x1 * cs[j] - x2 * sn[j];
-    const float o2 = x2 * cs[j] + x1 * sn[j];
+  const int quads = (Hq + Hkv) * (half / 4);   // 4 consecutive j per item
+  for (int e = threadIdx.x; e < quads; e += 256) {
+    const int hh = e / (half / 4), j0 = (e % (half / 4)) * 4;
     T* dst = hh < Hq ? q + (m * Hq + hh) * D : k + (m * Hkv + (hh - Hq)) * D;
-    st<T>(dst, j, o1);
-    st<T>(dst, j + half, o2);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int j = j0 + r;
+      const float x1 = ld<T>(in, (int64_t)hh * D + j), x2 = ld<T>(in, (int64_t)hh * D + j + half);
+      st<T>(dst, j, x1 * cs[j] - x2 * sn[j]);
+      st<T>(dst, j + half, x2 * cs[j] + x1 * sn[j]);
+    }
   }
-  for (int e = threadIdx.x; e < Hkv * D; e += 256) v[m * Hkv * D + e] = in[(int64_t)(Hq + Hkv) * D + e];
+  // v: straight copy in 16-byte pieces
+  const int vb = Hkv * D * (int)sizeof(T) / 16;
+  const u32x4* vin = reinterpret_cast<const u32x4*>(in + (int64_t)(Hq + Hkv) * D);
+  u32x4* vout = reinterpret_cast<u32x4*>(v + m * Hkv * D);
+  for (int e = threadIdx.x; e < vb; e += 256) vout[e] = vin[e];
 }
 
 template <typename T>
@@ -126,8 +149,10 @@ extern "C" int32_t medusa_rmsnorm(const float* x, int64_t M, int64_t H, const vo
                  "medusa_rmsnorm: bad sizes");
   if (M == 0) return MEDUSA_OK;
   MEDUSA_REQUIRE(x && out, MEDUSA_ERR_INVALID_ARG, "medusa_rmsnorm: NULL pointer");
-  MEDUSA_DT_DISPATCH(dt, hipLaunchKernelGGL(medusa::rmsnorm_kernel<T>, dim3((unsigned)M), dim3(256), 0,
-                                            (hipStream_t)stream, x, H, (const T*)gain, eps, (T*)out));
+  MEDUSA_REQUIRE(((uintptr_t)x) % 16 == 0, MEDUSA_ERR_INVALID_ARG, "medusa_rmsnorm: x must be 16-byte aligned");
+  MEDUSA_DT_DISPATCH(dt, hipLaunchKernelGGL(medusa::rmsnorm_kernel<T>, dim3((unsigned)((M + 3) / 4)),
+                                            dim3(256), 0, (hipStream_t)stream, x, M, H,
+                                            (const T*)gain, eps, (T*)out));
   return check_launch("medusa_rmsnorm");
 }
 
@@ -136,8 +161,10 @@ extern "C" int32_t medusa_qkv_rope(const void* qkv, int64_t M, int32_t Hq, int32
                                    void* v, void* stream) {
   using namespace medusa_host;
   MEDUSA_REQUIRE(dt == MEDUSA_F32 || dt == MEDUSA_BF16, MEDUSA_ERR_UNSUPPORTED, "medusa_qkv_rope: dtype");
-  MEDUSA_REQUIRE(D >= 2 && D <= 128 && D % 2 == 0, MEDUSA_ERR_UNSUPPORTED,
-                 "medusa_qkv_rope: head dim %d", D);
+  MEDUSA_REQUIRE(D >= 8 && D <= 128 && D % 8 == 0, MEDUSA_ERR_UNSUPPORTED,
+                 "medusa_qkv_rope: head dim %d (multiple of 8 up to 128)", D);
+  MEDUSA_REQUIRE(((uintptr_t)qkv | (uintptr_t)v) % 16 == 0, MEDUSA_ERR_INVALID_ARG,
+                 "medusa_qkv_rope: qkv and v must be 16-byte aligned");
   MEDUSA_REQUIRE(M >= 0 && M <= INT32_MAX && Hq >= 1 && Hkv >= 1 && base > 1.f,
                  MEDUSA_ERR_INVALID_ARG, "medusa_qkv_rope: bad sizes or base");
   if (M == 0) return MEDUSA_OK;

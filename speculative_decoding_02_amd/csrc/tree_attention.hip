@@ -351,34 +351,36 @@ __global__ __launch_bounds__(ATT_THREADS) void tree_attention_kernel(AttnArgs a)
 }
 
 // Merge of the split partials of one (sequence, head): O = sum_s w_s O_s /
-// sum_s w_s l_s with w_s = 2^(m_s - max m), splits in index order.
+// sum_s w_s l_s with w_s = 2^(m_s - max m), splits in index order.  One
+// workgroup per (group of 8 nodes, head, sequence); 32 lanes per node (4
+// head dims each), so the grid covers the chip even at batch 1.
+constexpr int CMB_NODES = 8;
 template <typename T, int D>
 __global__ __launch_bounds__(ATT_THREADS) void tree_attention_combine_kernel(AttnArgs a, int S) {
-  const int h = blockIdx.x, b = blockIdx.y;
+  const int h = blockIdx.y, b = blockIdx.z;
   const int N = a.N;
   const int total = a.ctx[b] + N;
   const int nsplit = (total + a.chunk - 1) / a.chunk;
   if (nsplit <= 1) return;
+  constexpr int D4 = D / 4;                       // lanes per node
+  const int n = blockIdx.x * CMB_NODES + threadIdx.x / D4;
+  if (threadIdx.x / D4 >= CMB_NODES || n >= N) return;
+  const int d0 = (threadIdx.x % D4) * 4;
   const int64_t bh = (int64_t)b * a.Hq + h;
-  T* Op = reinterpret_cast<T*>(a.O);
-  constexpr int D4 = D / 4;
-  for (int it = threadIdx.x; it < N * D4; it += ATT_THREADS) {
-    const int n = it / D4, d0 = (it % D4) * 4;
-    float M = -INFINITY;
-    for (int q = 0; q < nsplit; ++q) M = fmaxf(M, a.ml[(bh * S + q) * N + n].x);
-    float L = 0.f;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int q = 0; q < nsplit; ++q) {
-      const float2 mlq = a.ml[(bh * S + q) * N + n];
-      const float w = (mlq.x == -INFINITY) ? 0.f : exp2f(mlq.x - M);
-      L += w * mlq.y;
-      acc += w * *reinterpret_cast<const f32x4*>(a.opart + ((bh * S + q) * N + n) * D + d0);
-    }
-    const float inv = 1.f / L;
-    T* orow = Op + (((int64_t)b * N + n) * a.Hq + h) * D;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) st<T>(orow, d0 + r, acc[r] * inv);
+  float M = -INFINITY;
+  for (int q = 0; q < nsplit; ++q) M = fmaxf(M, a.ml[(bh * S + q) * N + n].x);
+  float L = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int q = 0; q < nsplit; ++q) {
+    const float2 mlq = a.ml[(bh * S + q) * N + n];
+    const float w = (mlq.x == -INFINITY) ? 0.f : exp2f(mlq.x - M);
+    L += w * mlq.y;
+    acc += w * *reinterpret_cast<const f32x4*>(a.opart + ((bh * S + q) * N + n) * D + d0);
   }
+  const float inv = 1.f / L;
+  T* orow = reinterpret_cast<T*>(a.O) + (((int64_t)b * N + n) * a.Hq + h) * D;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) st<T>(orow, d0 + r, acc[r] * inv);
 }
 
 }  // namespace medusa
@@ -478,7 +480,7 @@ extern "C" int32_t medusa_tree_attention(const void* Q, const void* Kt, const vo
   a.chunk = p.chunk;
   a.scale_log2 = scale * 1.4426950408889634f;
   dim3 grid((unsigned)p.splits, (unsigned)Hq, (unsigned)B);
-  dim3 cgrid((unsigned)Hq, (unsigned)B);
+  dim3 cgrid((unsigned)((N + medusa::CMB_NODES - 1) / medusa::CMB_NODES), (unsigned)Hq, (unsigned)B);
   hipStream_t st = (hipStream_t)stream;
   const dim3 blk(medusa::ATT_THREADS);
   constexpr int PF = MEDUSA_ATTN_PF;

@@ -30,7 +30,8 @@ _SIGS = {
     "medusa_linear": (i32, [vp, i64, i64, i64, vp, i64, i32, i32, i32, vp, vp, vp, i32, vp]),
     "medusa_heads_ws": (sz, [i64, i64, i32, i64, i32, i32]),
     "medusa_heads": (i32, [vp, i64, i64, i32, vp, vp, vp, i64, i32, vp, i32, vp, vp, vp, sz, vp]),
-    "medusa_topk": (i32, [vp, i64, i64, i32, vp, vp, vp]),
+    "medusa_topk_ws": (sz, [i64, i64, i32]),
+    "medusa_topk": (i32, [vp, i64, i64, i32, vp, vp, vp, sz, vp]),
     "medusa_build_tree": (i32, [i32, i32, vp, vp, vp, vp, i32, i32, vp, vp, vp, vp, vp]),
     "medusa_tree_attention_ws": (sz, [i32, i32, i32, i32, i32, i32, i32]),
     "medusa_tree_attention": (i32, [vp, vp, vp, vp, vp, vp, i32, i32, vp, i32, vp, i32, i32, i32,
@@ -165,12 +166,17 @@ def medusa_heads(X, W1, b1, W2, topk=0, logits=None, ids=None, vals=None, ws=Non
     return logits, ids[..., :topk], vals[..., :topk]
 
 
-def medusa_topk(logits, k, ids=None, vals=None):
-    R, V = logits.shape[0] if logits.dim() == 2 else logits[..., 0].numel(), logits.shape[-1]
+def medusa_topk(logits, k, ids=None, vals=None, ws=None):
+    R, V = logits[..., 0].numel(), logits.shape[-1]
     dev = logits.device
     ids = ids if ids is not None else torch.empty(logits.shape[:-1] + (k,), dtype=torch.int32, device=dev)
     vals = vals if vals is not None else torch.empty(logits.shape[:-1] + (k,), dtype=torch.float32, device=dev)
-    _check("medusa_topk", _lib.medusa_topk(_p(logits), R, V, k, _p(ids), _p(vals), _stream()))
+    need = _lib.medusa_topk_ws(R, V, k)
+    if need and (ws is None or ws.numel() < need):
+        ws = _ws(need, dev)
+    _check("medusa_topk", _lib.medusa_topk(_p(logits), R, V, k, _p(ids), _p(vals),
+                                           _p(ws) if need else None, ws.numel() if need else 0,
+                                           _stream()))
     return ids, vals
 
 
