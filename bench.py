@@ -219,7 +219,8 @@ def main():
     H, F = 4096, 11008
     hin = torch.randn((64, H), device="cuda").to(torch.bfloat16)
     gout = torch.empty((64, F), device="cuda", dtype=torch.bfloat16)
-    gu_launches = [lambda L=L: M.medusa_linear(hin, L["wgu"], M.EPI_SWIGLU, out=gout)
+    gws = M._ws(M.linear_ws_bytes(64, H, 2 * F, 1, M.BF16), "cuda")
+    gu_launches = [lambda L=L: M.medusa_linear(hin, L["wgu"], M.EPI_SWIGLU, out=gout, ws=gws)
                    for L in model.t["layers"]]
     gu_us, gu_med = graph_time_us(torch, gu_launches, reps=10, inner=2)
     gu_bytes = 2 * F * H * 2 + 64 * H * 2 + 64 * F * 2

@@ -93,9 +93,12 @@ int32_t medusa_tree_validate(const int32_t* parent, const int32_t* rank, int32_t
  *     MEDUSA_EPI_SWIGLU      W holds gate and up rows interleaved in blocks of
  *                            16 (block j: gate rows 16j..16j+15 then up rows);
  *                            Y [M, N/2] = SiLU(gate) * up   (dt)
- *   Reduction order per output element depends only on Kd, never on M or
- *   batch: equal inputs give bitwise equal outputs.
- * Kd must be a multiple of 8 (bf16) or 4 (f32).  ws may be NULL (none needed).
+ *   The launch plan (tiling, contraction split) is a function of (M, Kd, N,
+ *   dt) only, never of the batch, and every reduction runs in a fixed order:
+ *   equal inputs and shapes give bitwise equal outputs.
+ * Kd must be a multiple of 8 (bf16) or 4 (f32).
+ * ws: medusa_linear_ws(M, Kd, N, batch, dt) bytes of scratch for contraction
+ * split partials (0 for shapes that do not split; then ws may be NULL).
  * ---------------------------------------------------------------------- */
 typedef enum {
   MEDUSA_EPI_NONE = 0,
@@ -104,9 +107,11 @@ typedef enum {
   MEDUSA_EPI_SWIGLU = 3
 } medusa_epilogue;
 
+size_t medusa_linear_ws(int64_t M, int64_t Kd, int64_t N, int32_t batch, int32_t dt);
 int32_t medusa_linear(const void* X, int64_t x_bstride, int64_t M, int64_t Kd, const void* W,
                       int64_t N, int32_t batch, int32_t dt, int32_t epilogue, const void* bias,
-                      const void* aux, void* Y, int32_t y_f32, void* stream);
+                      const void* aux, void* Y, int32_t y_f32, void* ws, size_t ws_bytes,
+                      void* stream);
 
 /* ------------------------------------------------------------------------
  * medusa_heads: K Medusa heads on M hidden rows, plus per-head top-k.
@@ -238,8 +243,8 @@ int32_t kv_compact(void* const* Kc, void* const* Vc, int32_t L, const int32_t* p
 int32_t medusa_embed(const int32_t* tokens, int64_t M, const void* table, int64_t V, int64_t H,
                      int32_t dt, float* out, void* stream);
 
-/* out [M, H] (dt) = x / sqrt(mean(x^2) + eps) * gain; x float [M, H];
- * gain [H] (dt) or NULL for 1. */
+/* out [M, H] (dt) = x / sqrt(mean(x^2) + eps) * gain; x float [M, H] (16-byte
+ * aligned, H a multiple of 4, H <= 8192); gain [H] (dt) or NULL for 1. */
 int32_t medusa_rmsnorm(const float* x, int64_t M, int64_t H, const void* gain, float eps,
                        int32_t dt, void* out, void* stream);
 

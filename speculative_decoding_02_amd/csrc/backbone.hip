@@ -15,38 +15,46 @@ __global__ __launch_bounds__(256) void embed_kernel(const int* __restrict__ toke
   for (int64_t e = threadIdx.x; e < H; e += 256) out[m * H + e] = ld<T>(row, e);
 }
 
-// One wave per row (4 rows per workgroup, no block barrier): 16-byte loads,
-// per-lane partial sums in a fixed order, then a butterfly over the wave;
-// the second pass re-reads the row (L2 hit) to normalise.
+// One workgroup per row.  Every thread issues all of its 16-byte loads before
+// using any (up to RMS_V4 per thread, enough for H = 8192 in fp32), so a row
+// costs one memory round trip; the sum of squares is reduced in a fixed order
+// (per-thread, then a butterfly per wave, then the 4 waves in order) and the
+// normalised values are written from registers.
+constexpr int RMS_V4 = 8;
 template <typename T>
 __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ x, int64_t M,
                                                       int64_t H, const T* __restrict__ gain,
                                                       float eps, T* __restrict__ out) {
-  const int64_t m = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (m >= M) return;
-  const int lane = threadIdx.x & 63;
+  const int64_t m = blockIdx.x;
   const float* xr = x + m * H;
-  const int64_t H4 = (H % 4 == 0) ? H / 4 : 0;
-  float ss = 0.f;
-  for (int64_t e = lane; e < H4; e += 64) {
-    const f32x4 v = reinterpret_cast<const f32x4*>(xr)[e];
-    ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
-  }
-  for (int64_t e = H4 * 4 + lane; e < H; e += 64) ss += xr[e] * xr[e];
-  ss = wave_sum(ss);
-  const float rs = 1.0f / sqrtf(ss / (float)H + eps);
-  T* orow = out + m * H;
-  for (int64_t e = lane; e < H4; e += 64) {
-    const f32x4 v = reinterpret_cast<const f32x4*>(xr)[e];
+  const int64_t H4 = H / 4;
+  f32x4 v[RMS_V4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float g = gain ? ld<T>(gain, e * 4 + r) : 1.f;
-      st<T>(orow, e * 4 + r, v[r] * rs * g);
-    }
+  for (int i = 0; i < RMS_V4; ++i) {
+    const int64_t e = threadIdx.x + (int64_t)i * 256;
+    v[i] = reinterpret_cast<const f32x4*>(xr)[e < H4 ? e : 0];
   }
-  for (int64_t e = H4 * 4 + lane; e < H; e += 64) {
-    const float g = gain ? ld<T>(gain, e) : 1.f;
-    st<T>(orow, e, xr[e] * rs * g);
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < RMS_V4; ++i)
+    if (threadIdx.x + (int64_t)i * 256 < H4)
+      ss += v[i].x * v[i].x + v[i].y * v[i].y + v[i].z * v[i].z + v[i].w * v[i].w;
+  ss = wave_sum(ss);
+  __shared__ float part[4];
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  const float tot = (part[0] + part[1]) + (part[2] + part[3]);
+  const float rs = 1.0f / sqrtf(tot / (float)H + eps);
+  T* orow = out + m * H;
+#pragma unroll
+  for (int i = 0; i < RMS_V4; ++i) {
+    const int64_t e = threadIdx.x + (int64_t)i * 256;
+    if (e < H4)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float g = gain ? ld<T>(gain, e * 4 + r) : 1.f;
+        st<T>(orow, e * 4 + r, v[i][r] * rs * g);
+      }
   }
 }
 
@@ -149,10 +157,13 @@ extern "C" int32_t medusa_rmsnorm(const float* x, int64_t M, int64_t H, const vo
                  "medusa_rmsnorm: bad sizes");
   if (M == 0) return MEDUSA_OK;
   MEDUSA_REQUIRE(x && out, MEDUSA_ERR_INVALID_ARG, "medusa_rmsnorm: NULL pointer");
-  MEDUSA_REQUIRE(((uintptr_t)x) % 16 == 0, MEDUSA_ERR_INVALID_ARG, "medusa_rmsnorm: x must be 16-byte aligned");
-  MEDUSA_DT_DISPATCH(dt, hipLaunchKernelGGL(medusa::rmsnorm_kernel<T>, dim3((unsigned)((M + 3) / 4)),
-                                            dim3(256), 0, (hipStream_t)stream, x, M, H,
-                                            (const T*)gain, eps, (T*)out));
+  MEDUSA_REQUIRE(((uintptr_t)x) % 16 == 0 && H % 4 == 0 && H <= 4 * 256 * medusa::RMS_V4,
+                 MEDUSA_ERR_UNSUPPORTED,
+                 "medusa_rmsnorm: needs 16-byte aligned x, H a multiple of 4 and H <= %d",
+                 4 * 256 * medusa::RMS_V4);
+  MEDUSA_DT_DISPATCH(dt, hipLaunchKernelGGL(medusa::rmsnorm_kernel<T>, dim3((unsigned)M), dim3(256),
+                                            0, (hipStream_t)stream, x, M, H, (const T*)gain, eps,
+                                            (T*)out));
   return check_launch("medusa_rmsnorm");
 }
 

@@ -13,6 +13,8 @@
 //   * the 4 partial tiles are added in LDS in wave order, so an output's
 //     reduction order depends on Kd only (never on M or the batch);
 //   * the epilogue (bias + SiLU + residual, residual add, SwiGLU) is fused.
+#include <algorithm>
+
 #include "common.h"
 
 namespace medusa {
@@ -38,9 +40,13 @@ template <> struct GemmTraits<float> {
 // Register-ring depth (contraction steps in flight per wave) for a given
 // number of 16-row blocks of X: the ring holds MB + NB 16-byte vectors per
 // step, kept near 150 VGPRs so two waves fit on each SIMD.
+#ifndef MEDUSA_GEMM_PF
+#define MEDUSA_GEMM_PF 0
+#endif
 template <int MB, int NB> struct GemmRing {
   static constexpr int per_step = MB + NB;
-  static constexpr int PF = per_step >= 8 ? 4 : per_step >= 6 ? 6 : per_step >= 4 ? 8 : 12;
+  static constexpr int PF = MEDUSA_GEMM_PF > 0 ? MEDUSA_GEMM_PF
+                          : per_step >= 8 ? 4 : per_step >= 6 ? 6 : per_step >= 4 ? 8 : 12;
 };
 
 template <typename T, int MB, int NB, int KS, int EPI>
@@ -192,6 +198,170 @@ __global__ __launch_bounds__(64 * KS) void gemm_kernel(const T* __restrict__ X, 
   }
 }
 
+// Variant for M > 16 rows: the 4 waves split the OUTPUT rows (16*NB weight
+// rows each, full contraction per wave) and share the activation rows
+// through LDS, loaded cooperatively one 256-wide contraction chunk at a time
+// (the next chunk is staged in registers while the current one is used).
+// Each activation byte then costs one load instruction per workgroup instead
+// of one per wave, which keeps the weight stream's loads in flight.  Each
+// output is one wave's single accumulation chain in step order, so results
+// do not depend on M or the batch.
+constexpr int XL_KC = 256;  // contraction chunk (elements) held in LDS
+template <typename T, int MB, int NB, int EPI>
+__global__ __launch_bounds__(256) void gemm_xlds_kernel(const T* __restrict__ X, int64_t xbs,
+                                                        int M, int Kd, const T* __restrict__ W,
+                                                        int Nw, const T* __restrict__ bias,
+                                                        const void* aux, void* Y, int y_f32,
+                                                        int ksplit, float* __restrict__ part) {
+  using TR = GemmTraits<T>;
+  constexpr int P16 = TR::per16;
+  constexpr int KSTEP = 4 * P16;
+  constexpr int SC = XL_KC / KSTEP;          // steps per chunk
+  constexpr int TM = 16 * MB;
+  constexpr int LDX = XL_KC + P16;           // padded LDS row (elements)
+  constexpr int XV = TM * XL_KC / P16 / 256; // 16-byte vectors per thread per chunk
+  constexpr int PF = MEDUSA_GEMM_PF > 0 ? MEDUSA_GEMM_PF : (NB >= 4 ? 4 : 8);
+  static_assert(SC % PF == 0, "ring slots must align with chunk boundaries");
+  static_assert(NB % 2 == 0 || EPI != MEDUSA_EPI_SWIGLU, "SwiGLU pairs blocks within a wave");
+  __shared__ __attribute__((aligned(16))) T xs[TM * LDX];
+
+  const int g = blockIdx.z / ksplit, ks = blockIdx.z % ksplit;
+  const int m0 = blockIdx.y * TM;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int lr = lane & 15, lg = lane >> 4;
+  const int n0 = blockIdx.x * (64 * NB) + wave * 16 * NB;
+  const T* Xg = X + (int64_t)g * xbs;
+  const T* Wg = W + (int64_t)g * Nw * Kd;
+  const T* wrow[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int r = min(n0 + nb * 16 + lr, Nw - 1);
+    wrow[nb] = Wg + (int64_t)r * Kd + lg * P16;
+  }
+  // this workgroup's share of the contraction: chunks [c_beg, c_end)
+  const int total_chunks = Kd / XL_KC;   // Kd is a multiple of XL_KC here
+  const int c_beg = (int)((int64_t)total_chunks * ks / ksplit);
+  const int c_end = (int)((int64_t)total_chunks * (ks + 1) / ksplit);
+  const int nchunks = c_end - c_beg;
+  const int step0 = c_beg * SC;
+  const int nsteps = nchunks * SC;
+
+  // cooperative activation chunk: vector v of thread t covers row idx/(KC/P16)
+  u32x4 xr[XV];
+  auto xload = [&](int c) {
+#pragma unroll
+    for (int i = 0; i < XV; ++i) {
+      const int idx = threadIdx.x + i * 256;
+      const int row = idx / (XL_KC / P16), col = idx % (XL_KC / P16);
+      const int rr = min(m0 + row, M - 1);
+      xr[i] = *reinterpret_cast<const u32x4*>(Xg + (int64_t)rr * Kd + (c_beg + c) * XL_KC + col * P16);
+    }
+  };
+  auto xstore = [&]() {
+#pragma unroll
+    for (int i = 0; i < XV; ++i) {
+      const int idx = threadIdx.x + i * 256;
+      const int row = idx / (XL_KC / P16), col = idx % (XL_KC / P16);
+      *reinterpret_cast<u32x4*>(&xs[row * LDX + col * P16]) = xr[i];
+    }
+  };
+
+  f32x4 acc[MB][NB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  u32x4 fb[PF][NB];
+  auto wload = [&](int u, int st) {
+    const int k = (step0 + min(st, nsteps - 1)) * KSTEP;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) fb[u][nb] = *reinterpret_cast<const u32x4*>(wrow[nb] + k);
+  };
+
+#pragma unroll
+  for (int u = 0; u < PF; ++u) wload(u, u);
+  xload(0);
+  int s = 0;
+  for (int c = 0; c < nchunks; ++c) {
+    __syncthreads();  // everyone is done reading the previous chunk
+    xstore();
+    __syncthreads();
+    if (c + 1 < nchunks) xload(c + 1);
+    // SC steps of this chunk; the weight ring runs across chunk boundaries
+    for (int s0 = 0; s0 < SC; s0 += PF) {
+#pragma unroll
+      for (int u = 0; u < PF; ++u) {
+        const int sl = s0 + u;  // step within the chunk (SC is a multiple of PF)
+        u32x4 xa[MB];
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+          xa[mb] = *reinterpret_cast<const u32x4*>(&xs[(mb * 16 + lr) * LDX + sl * KSTEP + lg * P16]);
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = TR::mma(xa[mb], fb[u][nb], acc[mb][nb]);
+        wload(u, s + sl + PF);
+      }
+    }
+    s += SC;
+  }
+
+  // epilogue straight from the accumulators: lane holds weight row
+  // n0 + nb*16 + lr and activation rows m0 + mb*16 + 4*lg + r
+  if (ksplit > 1) {  // fp32 partial of this contraction share; gemm_split_reduce finishes
+    float* pg = part + ((int64_t)g * ksplit + ks) * M * Nw;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int m = m0 + mb * 16 + lg * 4 + r, n = n0 + nb * 16 + lr;
+          if (m < M && n < Nw) pg[(int64_t)m * Nw + n] = acc[mb][nb][r];
+        }
+    return;
+  }
+  if (EPI == MEDUSA_EPI_SWIGLU) {
+    // NB is even: block 2j is gate, 2j+1 the matching up rows
+    const int F = Nw / 2;
+    T* Yg = reinterpret_cast<T*>(Y) + (int64_t)g * M * F;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int j = 0; j < NB / 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int m = m0 + mb * 16 + lg * 4 + r;
+          const int f = (n0 >> 1) + j * 16 + lr;
+          if (m < M && f < F) st<T>(Yg, (int64_t)m * F + f, silu_f(acc[mb][2 * j][r]) * acc[mb][2 * j + 1][r]);
+        }
+    return;
+  }
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = m0 + mb * 16 + lg * 4 + r, n = n0 + nb * 16 + lr;
+        if (m >= M || n >= Nw) continue;
+        const float v = acc[mb][nb][r];
+        const int64_t o = (int64_t)g * M * Nw + (int64_t)m * Nw + n;
+        if (EPI == MEDUSA_EPI_NONE) {
+          if (y_f32) reinterpret_cast<float*>(Y)[o] = v;
+          else st<T>(reinterpret_cast<T*>(Y), o, v);
+        } else if (EPI == MEDUSA_EPI_BIAS_SILU_RES) {
+          const T* R = reinterpret_cast<const T*>(aux) + (int64_t)g * xbs;
+          const float res = ld<T>(R, (int64_t)m * Nw + n);
+          const float b = bias ? ld<T>(bias, (int64_t)g * Nw + n) : 0.f;
+          st<T>(reinterpret_cast<T*>(Y), o, res + silu_f(v + b));
+        } else {
+          const float res = reinterpret_cast<const float*>(aux)[(int64_t)m * Nw + n];
+          reinterpret_cast<float*>(Y)[(int64_t)m * Nw + n] = res + v;
+        }
+      }
+}
+
 #ifndef MEDUSA_GEMM_NB
 #define MEDUSA_GEMM_NB 2
 #endif
@@ -199,16 +369,119 @@ __global__ __launch_bounds__(64 * KS) void gemm_kernel(const T* __restrict__ X, 
 #define MEDUSA_GEMM_KS 4
 #endif
 
+// Sum of the split-contraction partials in split order, then the epilogue.
+// One thread per output element.
+template <typename T, int EPI>
+__global__ __launch_bounds__(256) void gemm_split_reduce_kernel(const float* __restrict__ part,
+                                                                int ksplit, int M, int Nw,
+                                                                int64_t xbs, const T* __restrict__ bias,
+                                                                const void* aux, void* Y, int y_f32) {
+  const int g = blockIdx.y;
+  const int cols = EPI == MEDUSA_EPI_SWIGLU ? Nw / 2 : Nw;
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= (int64_t)M * cols) return;
+  const int m = (int)(e / cols), c = (int)(e % cols);
+  const float* pg = part + (int64_t)g * ksplit * M * Nw;
+  auto sum = [&](int n) {
+    float v = pg[(int64_t)m * Nw + n];
+    for (int q = 1; q < ksplit; ++q) v += pg[((int64_t)q * M + m) * Nw + n];
+    return v;
+  };
+  if (EPI == MEDUSA_EPI_SWIGLU) {
+    const int ncol = (c >> 4) * 32 + (c & 15);  // gate column; up is 16 further
+    T* Yg = reinterpret_cast<T*>(Y) + (int64_t)g * M * cols;
+    st<T>(Yg, (int64_t)m * cols + c, silu_f(sum(ncol)) * sum(ncol + 16));
+    return;
+  }
+  const float v = sum(c);
+  const int64_t o = (int64_t)g * M * Nw + (int64_t)m * Nw + c;
+  if (EPI == MEDUSA_EPI_NONE) {
+    if (y_f32) reinterpret_cast<float*>(Y)[o] = v;
+    else st<T>(reinterpret_cast<T*>(Y), o, v);
+  } else if (EPI == MEDUSA_EPI_BIAS_SILU_RES) {
+    const T* R = reinterpret_cast<const T*>(aux) + (int64_t)g * xbs;
+    const float res = ld<T>(R, (int64_t)m * Nw + c);
+    const float b = bias ? ld<T>(bias, (int64_t)g * Nw + c) : 0.f;
+    st<T>(reinterpret_cast<T*>(Y), o, res + silu_f(v + b));
+  } else {
+    const float res = reinterpret_cast<const float*>(aux)[(int64_t)m * Nw + c];
+    reinterpret_cast<float*>(Y)[(int64_t)m * Nw + c] = res + v;
+  }
+}
+
+#ifndef MEDUSA_GEMM_XL_NB
+#define MEDUSA_GEMM_XL_NB 2
+#endif
+#ifndef MEDUSA_GEMM_XL_TARGET_WGS
+#define MEDUSA_GEMM_XL_TARGET_WGS 384
+#endif
+#ifndef MEDUSA_GEMM_XL_MIN_N
+#define MEDUSA_GEMM_XL_MIN_N 0
+#endif
+
+}  // namespace medusa
+
+namespace medusa_host {
+// Launch plan for one projection; a function of (M, Kd, N, dtype) only, never
+// of the batch, so that equal shapes always take the same arithmetic path.
+struct GemmPlan {
+  bool xl;
+  int ksplit;
+};
+GemmPlan gemm_plan(int64_t M, int64_t Kd, int64_t Nw, int dt) {
+  using namespace medusa;
+  constexpr int XNB = MEDUSA_GEMM_XL_NB;
+  GemmPlan p{false, 1};
+  p.xl = dt == MEDUSA_BF16 && M > 16 && Kd % XL_KC == 0 && Nw >= MEDUSA_GEMM_XL_MIN_N &&
+         Nw % (64 * XNB) == 0;
+  if (!p.xl) return p;
+  // Split the contraction only when the output tiles alone leave the chip
+  // under-filled: each workgroup streams about 16-19 GB/s (latency bound), so
+  // ~384 of them are needed, while a split costs M*N*4 bytes of partials per
+  // share (measured: splitting 172+ tiles is a loss, 32-96 tiles a large win).
+  const int64_t tiles = (Nw / (64 * XNB)) * ((M + 63) / 64);
+  int64_t ks = 1;
+  if (tiles < 160) ks = (MEDUSA_GEMM_XL_TARGET_WGS + tiles - 1) / tiles;
+  ks = std::min<int64_t>(ks, Kd / XL_KC);
+  ks = std::min<int64_t>(ks, 8);
+  p.ksplit = (int)std::max<int64_t>(ks, 1);
+  return p;
+}
+size_t gemm_ws_bytes(int64_t M, int64_t Kd, int64_t Nw, int batch, int dt) {
+  const GemmPlan p = gemm_plan(M, Kd, Nw, dt);
+  if (!p.xl || p.ksplit <= 1) return 0;
+  return align_up((size_t)batch * p.ksplit * M * Nw * sizeof(float), 256);
+}
+}  // namespace medusa_host
+
+namespace medusa {
 template <typename T, int EPI>
 static void launch_gemm_t(const void* X, int64_t xbs, int64_t M, int64_t Kd, const void* W,
                           int64_t Nw, int batch, const void* bias, const void* aux, void* Y,
-                          int y_f32, hipStream_t st) {
+                          int y_f32, void* ws, hipStream_t st) {
   constexpr int NB = MEDUSA_GEMM_NB, KS = MEDUSA_GEMM_KS;
   constexpr int TN = 16 * NB;
+  constexpr int XNB = MEDUSA_GEMM_XL_NB;
+  const medusa_host::GemmPlan plan = medusa_host::gemm_plan(M, Kd, Nw, sizeof(T) == 2 ? MEDUSA_BF16 : MEDUSA_F32);
   auto go = [&](auto mbc) {
     constexpr int MB = decltype(mbc)::value;
-    dim3 grid((unsigned)((Nw + TN - 1) / TN), (unsigned)((M + 16 * MB - 1) / (16 * MB)),
-              (unsigned)batch);
+    const unsigned gy = (unsigned)((M + 16 * MB - 1) / (16 * MB));
+    if (plan.xl) {
+      dim3 grid((unsigned)(Nw / (64 * XNB)), gy, (unsigned)(batch * plan.ksplit));
+      hipLaunchKernelGGL((gemm_xlds_kernel<T, MB, XNB, EPI>), grid, dim3(256), 0, st,
+                         reinterpret_cast<const T*>(X), xbs, (int)M, (int)Kd,
+                         reinterpret_cast<const T*>(W), (int)Nw, reinterpret_cast<const T*>(bias),
+                         aux, Y, y_f32, plan.ksplit, reinterpret_cast<float*>(ws));
+      if (plan.ksplit > 1) {
+        const int64_t cols = EPI == MEDUSA_EPI_SWIGLU ? Nw / 2 : Nw;
+        dim3 rgrid((unsigned)((M * cols + 255) / 256), (unsigned)batch);
+        hipLaunchKernelGGL((gemm_split_reduce_kernel<T, EPI>), rgrid, dim3(256), 0, st,
+                           reinterpret_cast<const float*>(ws), plan.ksplit, (int)M, (int)Nw, xbs,
+                           reinterpret_cast<const T*>(bias), aux, Y, y_f32);
+      }
+      return;
+    }
+    dim3 grid((unsigned)((Nw + TN - 1) / TN), gy, (unsigned)batch);
     hipLaunchKernelGGL((gemm_kernel<T, MB, NB, KS, EPI>), grid, dim3(64 * KS), 0, st,
                        reinterpret_cast<const T*>(X), xbs, (int)M, (int)Kd,
                        reinterpret_cast<const T*>(W), (int)Nw, reinterpret_cast<const T*>(bias),
@@ -225,10 +498,10 @@ namespace medusa_host {
 // Internal launcher shared with medusa_heads (arguments already validated).
 void launch_gemm(const void* X, int64_t xbs, int64_t M, int64_t Kd, const void* W, int64_t Nw,
                  int batch, int dt, int epi, const void* bias, const void* aux, void* Y,
-                 int y_f32, hipStream_t st) {
+                 int y_f32, void* ws, hipStream_t st) {
   using namespace medusa;
 #define MEDUSA_GEMM_CASE(T, E)                                                              \
-  launch_gemm_t<T, E>(X, xbs, M, Kd, W, Nw, batch, bias, aux, Y, y_f32, st)
+  launch_gemm_t<T, E>(X, xbs, M, Kd, W, Nw, batch, bias, aux, Y, y_f32, ws, st)
 #define MEDUSA_GEMM_EPI(T)                                                                  \
   switch (epi) {                                                                            \
     case MEDUSA_EPI_NONE: MEDUSA_GEMM_CASE(T, MEDUSA_EPI_NONE); break;                      \
@@ -242,10 +515,15 @@ void launch_gemm(const void* X, int64_t xbs, int64_t M, int64_t Kd, const void* 
 }
 }  // namespace medusa_host
 
+extern "C" size_t medusa_linear_ws(int64_t M, int64_t Kd, int64_t N, int32_t batch, int32_t dt) {
+  if (M <= 0 || Kd <= 0 || N <= 0 || batch <= 0) return 0;
+  return medusa_host::gemm_ws_bytes(M, Kd, N, batch, dt);
+}
+
 extern "C" int32_t medusa_linear(const void* X, int64_t x_bstride, int64_t M, int64_t Kd,
                                  const void* W, int64_t N, int32_t batch, int32_t dt,
                                  int32_t epilogue, const void* bias, const void* aux, void* Y,
-                                 int32_t y_f32, void* stream) {
+                                 int32_t y_f32, void* ws, size_t ws_bytes, void* stream) {
   using namespace medusa_host;
   MEDUSA_REQUIRE(dt == MEDUSA_F32 || dt == MEDUSA_BF16, MEDUSA_ERR_UNSUPPORTED,
                  "medusa_linear: unknown dtype %d", dt);
@@ -271,7 +549,10 @@ extern "C" int32_t medusa_linear(const void* X, int64_t x_bstride, int64_t M, in
   if (epilogue == MEDUSA_EPI_SWIGLU)
     MEDUSA_REQUIRE(N % 32 == 0, MEDUSA_ERR_INVALID_ARG,
                    "medusa_linear: SwiGLU needs N (gate+up rows) to be a multiple of 32");
-  launch_gemm(X, x_bstride, M, Kd, W, N, batch, dt, epilogue, bias, aux, Y, y_f32,
+  const size_t need = gemm_ws_bytes(M, Kd, N, batch, dt);
+  MEDUSA_REQUIRE(need == 0 || (ws != NULL && ws_bytes >= need), MEDUSA_ERR_WORKSPACE,
+                 "medusa_linear: workspace %zu < %zu bytes", ws_bytes, need);
+  launch_gemm(X, x_bstride, M, Kd, W, N, batch, dt, epilogue, bias, aux, Y, y_f32, ws,
               (hipStream_t)stream);
   return check_launch("medusa_linear");
 }

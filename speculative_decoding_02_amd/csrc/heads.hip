@@ -9,12 +9,15 @@
 // then one top-k launch over the K*M logits rows.  Stage 2 and a plain
 // lm_head projection run the same kernel with the same contraction length,
 // so zero-initialised heads reproduce lm_head's logits bit for bit.
+#include <algorithm>
+
 #include "common.h"
 
 namespace medusa_host {
 void launch_gemm(const void* X, int64_t xbs, int64_t M, int64_t Kd, const void* W, int64_t Nw,
                  int batch, int dt, int epi, const void* bias, const void* aux, void* Y,
-                 int y_f32, hipStream_t st);
+                 int y_f32, void* ws, hipStream_t st);
+size_t gemm_ws_bytes(int64_t M, int64_t Kd, int64_t Nw, int batch, int dt);
 void launch_topk(const float* logits, int64_t R, int64_t V, int k, int* ids, float* vals, void* ws,
                  hipStream_t st);
 size_t topk_ws_bytes(int64_t R, int64_t V, int k);
@@ -24,9 +27,10 @@ extern "C" size_t medusa_heads_ws(int64_t M, int64_t H, int32_t K, int64_t V, in
                                   int32_t dt) {
   if (M < 0 || H < 0 || K < 0 || V < 0) return 0;
   const size_t es = dt == MEDUSA_BF16 ? 2 : 4;
-  return medusa_host::align_up((size_t)K * M * H * es, 256) +
-         medusa_host::align_up((size_t)K * M * V * 4, 256) +
-         medusa_host::topk_ws_bytes((int64_t)K * M, V, topk);
+  using namespace medusa_host;
+  const size_t gws = std::max(gemm_ws_bytes(M, H, H, K, dt), gemm_ws_bytes(M, H, V, K, dt));
+  return align_up((size_t)K * M * H * es, 256) + align_up((size_t)K * M * V * 4, 256) +
+         std::max(topk_ws_bytes((int64_t)K * M, V, topk), gws);
 }
 
 extern "C" int32_t medusa_heads(const void* X, int64_t M, int64_t H, int32_t K, const void* W1,
@@ -60,10 +64,10 @@ extern "C" int32_t medusa_heads(const void* X, int64_t M, int64_t H, int32_t K, 
   char* U = (char*)ws;
   char* lg_ws = U + align_up((size_t)K * M * H * es, 256);
   float* lg = logits ? logits : (float*)lg_ws;
-  void* tk_ws = lg_ws + align_up((size_t)K * M * V * 4, 256);
+  void* tk_ws = lg_ws + align_up((size_t)K * M * V * 4, 256);  // also the projections' split space
   hipStream_t st = (hipStream_t)stream;
-  launch_gemm(X, 0, M, H, W1, H, K, dt, MEDUSA_EPI_BIAS_SILU_RES, b1, X, U, 0, st);
-  launch_gemm(U, M * H, M, H, W2, V, K, dt, MEDUSA_EPI_NONE, nullptr, nullptr, lg, 1, st);
+  launch_gemm(X, 0, M, H, W1, H, K, dt, MEDUSA_EPI_BIAS_SILU_RES, b1, X, U, 0, tk_ws, st);
+  launch_gemm(U, M * H, M, H, W2, V, K, dt, MEDUSA_EPI_NONE, nullptr, nullptr, lg, 1, tk_ws, st);
   if (topk > 0) launch_topk(lg, (int64_t)K * M, V, topk, topk_ids, topk_vals, tk_ws, st);
   return check_launch("medusa_heads");
 }

@@ -130,6 +130,12 @@ class MedusaDecoder:
         dt = M._dt(model.t["embed"])
         self.heads_ws = M._ws(M._lib.medusa_heads_ws(1, model.hidden, model.n_medusa, model.vocab,
                                                      self.width, dt), dev)
+        # split-contraction scratch of the verification projections (rows <= 64)
+        H, F, V = model.hidden, model.ffn, model.vocab
+        qkv_n = (model.n_heads + 2 * model.n_kv_heads) * model.head_dim
+        shapes = [(H, qkv_n), (model.n_heads * model.head_dim, H), (H, 2 * F), (F, H), (H, V)]
+        self.lin_ws = M._ws(max([M.linear_ws_bytes(n, kd, nn, 1, dt) for n in range(1, 65)
+                                 for kd, nn in shapes] + [256]), dev)
         self.out = (torch.zeros(1, **i32), torch.zeros((1, self.K + 1), **i32), torch.zeros(1, **i32))
         self.new_ctx = torch.zeros(1, **i32)
         self.src = torch.zeros((1, self.K + 1), **i32)
@@ -147,18 +153,19 @@ class MedusaDecoder:
         scale = 1.0 / float(np.sqrt(m.head_dim))
         for li, L in enumerate(t["layers"]):
             h = M.medusa_rmsnorm(x, L["g_attn"], m.eps, m.dtype)
-            qkv = M.medusa_linear(h, L["wqkv"])
+            qkv = M.medusa_linear(h, L["wqkv"], ws=self.lin_ws)
             q, k, v = M.medusa_qkv_rope(qkv, m.n_heads, m.n_kv_heads, m.head_dim, pos.reshape(-1),
                                         m.rope_base)
             o = M.medusa_tree_attention(q[None], k[None], v[None], self.Kc[li], self.Vc[li],
                                         self.page_table, self.ctx, self.max_ctx,
                                         mask, scale, ws=self.attn_ws)
-            M.medusa_linear(o.reshape(n, -1), L["wo"], M.EPI_RES_ADD_F32, aux=x, out=x)
+            M.medusa_linear(o.reshape(n, -1), L["wo"], M.EPI_RES_ADD_F32, aux=x, out=x,
+                            ws=self.lin_ws)
             h = M.medusa_rmsnorm(x, L["g_mlp"], m.eps, m.dtype)
-            f = M.medusa_linear(h, L["wgu"], M.EPI_SWIGLU)
-            M.medusa_linear(f, L["wd"], M.EPI_RES_ADD_F32, aux=x, out=x)
+            f = M.medusa_linear(h, L["wgu"], M.EPI_SWIGLU, ws=self.lin_ws)
+            M.medusa_linear(f, L["wd"], M.EPI_RES_ADD_F32, aux=x, out=x, ws=self.lin_ws)
         hN = M.medusa_rmsnorm(x, t["g_final"], m.eps, m.dtype)
-        logits = M.medusa_linear(hN, t["lm_head"], y_f32=True)
+        logits = M.medusa_linear(hN, t["lm_head"], y_f32=True, ws=self.lin_ws)
         return logits, hN
 
     def _heads(self, h_row):

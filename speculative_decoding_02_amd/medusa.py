@@ -27,7 +27,9 @@ _SIGS = {
     "medusa_last_error": (C.c_char_p, []),
     "medusa_abi_version": (i32, []),
     "medusa_tree_validate": (i32, [vp, vp, i32, i32, i32]),
-    "medusa_linear": (i32, [vp, i64, i64, i64, vp, i64, i32, i32, i32, vp, vp, vp, i32, vp]),
+    "medusa_linear_ws": (sz, [i64, i64, i64, i32, i32]),
+    "medusa_linear": (i32, [vp, i64, i64, i64, vp, i64, i32, i32, i32, vp, vp, vp, i32, vp, sz,
+                            vp]),
     "medusa_heads_ws": (sz, [i64, i64, i32, i64, i32, i32]),
     "medusa_heads": (i32, [vp, i64, i64, i32, vp, vp, vp, i64, i32, vp, i32, vp, vp, vp, sz, vp]),
     "medusa_topk_ws": (sz, [i64, i64, i32]),
@@ -120,8 +122,12 @@ def medusa_tree_validate(parent, rank, K, topk):
         p.ctypes.data, r.ctypes.data, len(p), int(K), int(topk)))
 
 
+def linear_ws_bytes(M, Kd, N, batch, dt):
+    return _lib.medusa_linear_ws(M, Kd, N, batch, dt)
+
+
 def medusa_linear(X, W, epilogue=EPI_NONE, bias=None, aux=None, out=None, y_f32=False,
-                  x_bstride=0):
+                  x_bstride=0, ws=None):
     """Y = epilogue(X W^T).  W [batch, N, Kd] or [N, Kd]; X [M, Kd] or [batch, M, Kd]."""
     dt = _dt(W)
     batch = W.shape[0] if W.dim() == 3 else 1
@@ -134,9 +140,12 @@ def medusa_linear(X, W, epilogue=EPI_NONE, bias=None, aux=None, out=None, y_f32=
         ydt = torch.float32 if (y_f32 or epilogue == EPI_RES_ADD_F32) else W.dtype
         shape = (batch, M, cols) if batch > 1 or W.dim() == 3 else (M, cols)
         out = torch.empty(shape, dtype=ydt, device=W.device)
+    need = _lib.medusa_linear_ws(M, Kd, N, batch, dt)
+    if need and (ws is None or ws.numel() < need):
+        ws = _ws(need, W.device)
     _check("medusa_linear", _lib.medusa_linear(
         _p(X), x_bstride, M, Kd, _p(W), N, batch, dt, epilogue, _p(bias), _p(aux), _p(out),
-        int(bool(y_f32)), _stream()))
+        int(bool(y_f32)), _p(ws) if need else None, ws.numel() if need else 0, _stream()))
     return out
 
 

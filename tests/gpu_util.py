@@ -40,3 +40,12 @@ def assert_close(got, ref, tol, what=""):
     assert np.all(np.isfinite(got)), f"{what}: non-finite output"
     assert err <= tol, f"{what}: max abs err {err:.3e} > {tol:.1e}"
     return err
+
+
+def assert_close_stored(got, ref, tol, what=""):
+    """For outputs stored in the model dtype: the bound is ``tol`` absolute
+    up to |ref| = 1 and relative beyond (bf16 storage alone rounds by up to
+    2^-8 |y|, well inside 2e-2 |y|)."""
+    ref = np.asarray(ref, np.float64)
+    scale = np.maximum(1.0, np.abs(ref))
+    return assert_close(np.asarray(got, np.float64) / scale, ref / scale, tol, what)
