@@ -33,6 +33,24 @@ sys.path.insert(0, ROOT)
 
 METRIC = "accepted tokens/s + tree-attn HBM GB/s (% peak), 7B-shape, 64-node tree"
 HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_7b_counters.md")
+
+
+def measured_traffic(label, source):
+    """Calibrated HBM bytes per launch of ``label`` from the committed counter
+    summary, or None when absent or taken on a different version of
+    ``source`` (the kernel changed since the counters were read)."""
+    import hashlib
+    try:
+        line = [l for l in open(TRAFFIC_FILE) if l.startswith("traffic_json: ")][0]
+        d = json.loads(line[len("traffic_json: "):])
+        cur = hashlib.sha256(open(os.path.join(ROOT, "speculative_decoding_02_amd", "csrc", source),
+                                  "rb").read()).hexdigest()[:16]
+        if d["sources"].get(source) != cur:
+            return None
+        return d[label]["traffic_bytes"]
+    except (OSError, IndexError, KeyError, ValueError):
+        return None
 
 
 def graph_time_us(torch, launches, reps=10, inner=2):
@@ -65,8 +83,8 @@ def graph_time_us(torch, launches, reps=10, inner=2):
     return sum(per) / len(per), per[len(per) // 2]
 
 
-def tree_attention_c2(torch, M, synth, reps=10, copies=17):
-    """Tree attention alone at the 7B layer shape; returns a dict of figures."""
+def c2_inputs(torch, M, synth, copies=17):
+    """Tree-attention inputs at the 7B layer shape (KV copies rotated > MALL)."""
     import numpy as np
     B, N, H, D, ctx, P = 1, 64, 32, 128, 2048, 16
     dev = "cuda"
@@ -88,11 +106,18 @@ def tree_attention_c2(torch, M, synth, reps=10, copies=17):
     _, _, mask = M.medusa_build_tree(torch.tensor(parent[None], **i32), torch.tensor(rank[None], **i32),
                                      torch.zeros(1, **i32), topk, ctx_t)
     out = torch.empty_like(Q)
-    ws = M._ws(M.tree_attention_ws_bytes(B, N, H, H, D, ctx), dev, zero=True)
+    ws = M._ws(M.tree_attention_ws_bytes(B, N, H, H, D, ctx), dev)
     scale = 1.0 / np.sqrt(D)
-    launches = [lambda i=i: M.medusa_tree_attention(Q, Kt, Vt, Kc[i], Vc[i], pt, ctx_t, ctx, mask,
-                                                     scale, out=out, ws=ws)
-                for i in range(copies)]
+    call = lambda i: M.medusa_tree_attention(Q, Kt, Vt, Kc[i], Vc[i], pt, ctx_t, ctx, mask, scale,
+                                             out=out, ws=ws)
+    return call, dict(B=B, N=N, H=H, D=D, ctx=ctx, P=P, kc_bytes=Kc[0].numel() * 2)
+
+
+def tree_attention_c2(torch, M, synth, reps=10, copies=17):
+    """Tree attention alone at the 7B layer shape; returns a dict of figures."""
+    call, c = c2_inputs(torch, M, synth, copies)
+    B, N, H, D, ctx = c["B"], c["N"], c["H"], c["D"], c["ctx"]
+    launches = [lambda i=i: call(i) for i in range(copies)]
     us, us_med = graph_time_us(torch, launches, reps=reps)
     kv = (ctx + N) * H * D * 2 * 2          # cached + tree K and V read
     nbytes = kv + 2 * B * N * H * D * 2 + N * 8 + N * H * D * 2 * 2  # + Q, O, masks, appended tree K/V
@@ -104,7 +129,8 @@ def tree_attention_c2(torch, M, synth, reps=10, copies=17):
                 tflops=round(flops / (us * 1e-6) / 1e12, 2),
                 verified_tree_tokens_per_s=round(N / (us * 1e-6), 1),
                 timing="HIP events around graph replays of back-to-back launches",
-                kv_copies_rotated=copies, rotated_mb=round(copies * 2 * Kc[0].numel() * 2 / 1e6, 1))
+                traffic=measured_traffic("tree_attention", "tree_attention.hip"),
+                kv_copies_rotated=copies, rotated_mb=round(copies * 2 * c["kc_bytes"] / 1e6, 1))
 
 
 def cpu_baseline(torch, dec, model_src, emitted_per_step, sample_layers):
@@ -161,6 +187,38 @@ def cpu_baseline(torch, dec, model_src, emitted_per_step, sample_layers):
                 step_seconds_extrapolated=round(step_s, 3), _ids=len(ids))
 
 
+def kernels_only(torch, M, synth, log):
+    """Counter-pass workload: 32 gate/up projection launches (64 rows, 7B
+    shapes, one weight copy per layer as in the step), 17 tree-attention
+    launches at the 7B layer shape, and a 1 GiB device copy whose byte count
+    calibrates FETCH_SIZE / WRITE_SIZE."""
+    H, F = 4096, 11008
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(7)
+    hin = torch.randn((64, H), generator=gen, device="cuda").to(torch.bfloat16)
+    gout = torch.empty((64, F), device="cuda", dtype=torch.bfloat16)
+    gws = M._ws(M.linear_ws_bytes(64, H, 2 * F, 1, M.BF16), "cuda")
+    log("[bench] kernels-only: gate/up launches")
+    for _ in range(32):
+        w = torch.randn((2 * F, H), generator=gen, device="cuda").mul_(0.02).to(torch.bfloat16)
+        torch.cuda.synchronize()
+        M.medusa_linear(hin, w, M.EPI_SWIGLU, out=gout, ws=gws)
+        torch.cuda.synchronize()
+        del w
+    log("[bench] kernels-only: tree attention")
+    call, _ = c2_inputs(torch, M, synth, 17)
+    for i in range(17):
+        call(i)
+    torch.cuda.synchronize()
+    log("[bench] kernels-only: 1 GiB calibration copy")
+    src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"kernels_only": True, "copy_bytes": 1 << 30,
+                      "gate_up_bytes_per_launch": 2 * F * H * 2 + 64 * H * 2 + 64 * F * 2}))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -171,6 +229,10 @@ def main():
     ap.add_argument("--cpu-sample-layers", type=int, default=4)
     ap.add_argument("--skip-c2", action="store_true")
     ap.add_argument("--skip-plain", action="store_true")
+    ap.add_argument("--kernels-only", action="store_true",
+                    help="run only the dominant projection kernel (32 launches over 7B-shaped "
+                         "gate/up weights), the tree-attention launches and a 1 GiB copy, "
+                         "for hardware-counter passes")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures the one-GPU Medusa step; runs on more than one GPU are not "
@@ -185,6 +247,9 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     log = lambda *a: print(*a, file=sys.stderr, flush=True)
+    if args.kernels_only:
+        kernels_only(torch, M, synth, log)
+        return
     log("[bench] drawing the random 7B-shaped decoder on the GPU")
     src = synth.device_llama(seed=4)
     model = DeviceModel.from_llama(src)
@@ -242,6 +307,29 @@ def main():
         plain = round(args.steps / (time.perf_counter() - p0), 2)
         del pdec
 
+    typical = None
+    if args.mode == "greedy" and not args.skip_plain:
+        log("[bench] typical acceptance (epsilon 0.3, delta 0.09) on the same model")
+        tdec = MedusaDecoder(model, parent, rank, capacity=capacity, mode="typical",
+                             epsilon=0.3, delta=0.09)
+        tdec.prefill(prompt)
+        tdec.capture()
+        for _ in range(args.warmup):
+            int(tdec.step_graph()[0].item())
+        tdec.prefill(prompt)
+        torch.cuda.synchronize()
+        t_emit, t_acc = 0, []
+        q0 = time.perf_counter()
+        for _ in range(args.steps):
+            a = int(tdec.step_graph()[0].item())
+            t_acc.append(a)
+            t_emit += a + 1
+        torch.cuda.synchronize()
+        dt_ = time.perf_counter() - q0
+        typical = dict(tokens_per_s=round(t_emit / dt_, 2), mean_accept_len=round(float(np.mean(t_acc)), 3),
+                       ms_per_step=round(1000 * dt_ / args.steps, 3), epsilon=0.3, delta=0.09)
+        del tdec
+
     c2 = None if args.skip_c2 else tree_attention_c2(torch, M, synth)
     cpu = None
     if not args.no_cpu_baseline:
@@ -262,9 +350,11 @@ def main():
         "tokens_per_step": round(emitted / args.steps, 3),
         "verified_tree_tokens_per_s": round(64 * args.steps / (t1 - t0), 1),
         "plain_decode_tokens_per_s": plain,
+        "typical": typical,
         "roofline": {"bound": "hbm", "kernel": "gemm_kernel (gate/up projection, SwiGLU epilogue)",
                      "achieved": round(gu_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gu_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(gu_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic("gate_up_projection", "gemm.hip"),
                      "bytes_per_launch": gu_bytes, "us_per_launch": round(gu_us, 2),
                      "us_median": round(gu_med, 2),
                      "timing": "HIP events around graph replays of the 32 per-step launches"},
