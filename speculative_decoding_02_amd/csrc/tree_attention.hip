@@ -48,6 +48,12 @@ struct AttnCfg {
   static_assert(KCHUNKS % ATT_THREADS == 0, "K tile chunks");
 };
 
+// Element type of the split partials: fp16 for bf16 attention (the partial
+// is the split's normalised output, |O_s| <= max |v|, so fp16's 2^-11
+// relative rounding sits far inside bf16's 2^-8), fp32 for fp32 attention.
+template <typename T> struct PartT { using type = float; };
+template <> struct PartT<bf16_t> { using type = _Float16; };
+
 // component i (compile-time after unrolling) of a 16-byte register vector
 __device__ __forceinline__ uint32_t u4c(u32x4 v, int i) { return v[i]; }
 
@@ -77,8 +83,9 @@ struct AttnArgs {
   const uint64_t* mask;
   void* O;
   float2* ml;        // [B*Hq*S*N]  (running max in log2 units, sum)
-  float* opart;      // [B*Hq*S*N*D]
+  void* opart;       // [B*Hq*S*N*D] of PartT<T>: a split's output divided by its own sum
   int max_pages, P, B, N, Hq, Hkv, chunk;  // chunk = keys per split (multiple of 64)
+  int max_ctx;
   float scale_log2;
 };
 
@@ -93,12 +100,7 @@ __global__ __launch_bounds__(ATT_THREADS) void tree_attention_kernel(AttnArgs a)
   const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int S = gridDim.x;
   const int N = a.N;
-  const int ctxb = a.ctx[b];
-  const int total = ctxb + N;
   const int k_beg = s * a.chunk;
-  if (k_beg >= total) return;
-  const int k_end = min(k_beg + a.chunk, total);
-  const int nsplit = (total + a.chunk - 1) / a.chunk;
   const int group = a.Hq / a.Hkv;
   const int kvh = h / group;
   const bool appender = (h % group) == 0;
@@ -116,14 +118,23 @@ __global__ __launch_bounds__(ATT_THREADS) void tree_attention_kernel(AttnArgs a)
   T* Vcp = reinterpret_cast<T*>(a.Vc);
   const int* pt = a.page_table + (int64_t)b * a.max_pages;
 
-  // The split's slice of the page table goes to LDS once, so that address
+  // One round trip before the tile loads: the sequence length, the split's
+  // slice of the page table (sized from max_ctx + N, so it does not wait for
+  // the length; it covers the cache slots and the tree slots the split may
+  // touch), this wave's queries and its nodes' ancestor masks are all
+  // loaded together.  The page slice goes to LDS, so that address
   // computation never waits on a global load (a wait there would also wait
-  // for every tile load in flight).  Tree slots ctx..ctx+N-1 are in the
-  // slice too (the append needs them).
+  // for every tile load in flight).
   const int page0 = k_beg / a.P;
-  const int npages = (k_end - 1) / a.P - page0 + 1;
-  for (int i = threadIdx.x; i < npages; i += ATT_THREADS) spages[i] = pt[page0 + i];
-  __syncthreads();
+  const int slice_end = min(k_beg + a.chunk, a.max_ctx + N);
+  const int npages = slice_end > k_beg ? (slice_end - 1) / a.P - page0 + 1 : 0;
+  // (a length outside [0, max_ctx] breaks the caller's contract; it is
+  // clamped so that every access stays inside the page slice)
+  const int ctxb = min(max(a.ctx[b], 0), a.max_ctx);
+  // npages <= ATT_MAX_SPLIT_PAGES == ATT_THREADS: one page per thread, held
+  // in a register until the queries' loads are issued too
+  static_assert(ATT_MAX_SPLIT_PAGES <= ATT_THREADS, "one page-table entry per thread");
+  const int my_page = threadIdx.x < npages ? pt[page0 + threadIdx.x] : 0;
 
   // element offset of key j's row for kv head kvh (cache slot or tree node)
   auto cache_off = [&](int j) -> int64_t {
@@ -143,9 +154,15 @@ __global__ __launch_bounds__(ATT_THREADS) void tree_attention_kernel(AttnArgs a)
       qf[st] = *reinterpret_cast<const u32x4*>(qrow + st * 4 * P16 + lg * P16);
   }
   const uint64_t mrow = a.mask[(int64_t)b * N + nodec];
-  // Queries and mask are in registers before any tile load is issued, so the
-  // loop never waits on them (a wait there would also drain the tile loads).
+  // Everything above is in registers or LDS before any tile load is issued,
+  // so the loop never waits on it (a wait there would also drain the tile
+  // loads).
   __builtin_amdgcn_s_waitcnt(0);
+  if (threadIdx.x < npages) spages[threadIdx.x] = my_page;
+  __syncthreads();
+  const int total = ctxb + N;
+  if (k_beg >= total) return;  // uniform over the workgroup
+  const int k_end = min(k_beg + a.chunk, total);
 
   // ---- tile loaders ----
   u32x4 kreg[PF][C::KPT];
@@ -327,7 +344,9 @@ __global__ __launch_bounds__(ATT_THREADS) void tree_attention_kernel(AttnArgs a)
   T* Op = reinterpret_cast<T*>(a.O);
   const bool node_ok = wave_active && node < N;
 
-  if (nsplit == 1) {
+  // A one-split grid writes O directly; otherwise every split writes its
+  // partials (a sequence whose range fits in one split included).
+  if (S == 1) {
     if (node_ok) {
       const float inv = 1.f / ltot;
       T* orow = Op + (((int64_t)b * N + node) * a.Hq + h) * D;
@@ -342,40 +361,81 @@ __global__ __launch_bounds__(ATT_THREADS) void tree_attention_kernel(AttnArgs a)
   // ---- multi-split: partials; tree_attention_combine merges them ----
   const int64_t bh = (int64_t)b * a.Hq + h;
   if (node_ok) {
-    float* op = a.opart + ((bh * S + s) * N + node) * D;
+    using PT = typename PartT<T>::type;
+    PT* op = reinterpret_cast<PT*>(a.opart) + ((bh * S + s) * N + node) * D;
+    const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
-      *reinterpret_cast<f32x4*>(op + db * 16 + lg * 4) = oacc[db];
+    for (int db = 0; db < DB; ++db) {
+      if constexpr (sizeof(PT) == 2) {
+        typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+        h4 v = {(_Float16)(oacc[db][0] * inv), (_Float16)(oacc[db][1] * inv), (_Float16)(oacc[db][2] * inv),
+                (_Float16)(oacc[db][3] * inv)};
+        *reinterpret_cast<h4*>(op + db * 16 + lg * 4) = v;
+      } else {
+        *reinterpret_cast<f32x4*>(op + db * 16 + lg * 4) = oacc[db] * inv;
+      }
+    }
     if (lg == 0) a.ml[(bh * S + s) * N + node] = make_float2(mrun, ltot);
   }
 }
 
-// Merge of the split partials of one (sequence, head): O = sum_s w_s O_s /
-// sum_s w_s l_s with w_s = 2^(m_s - max m), splits in index order.  One
+// Merge of the split partials of one (sequence, head): O = sum_s w_s l_s o_s
+// / sum_s w_s l_s with w_s = 2^(m_s - max m) and o_s the split's normalised
+// output, splits in index order.  One
 // workgroup per (group of 8 nodes, head, sequence); 32 lanes per node (4
-// head dims each), so the grid covers the chip even at batch 1.
+// head dims each), so the grid covers the chip even at batch 1.  Up to
+// CMB_BATCH splits are loaded in one go together with the sequence length
+// (splits past the sequence's last one are read but weighted out), so a
+// decode-time merge costs one round trip.
 constexpr int CMB_NODES = 8;
+constexpr int CMB_BATCH = 16;
 template <typename T, int D>
 __global__ __launch_bounds__(ATT_THREADS) void tree_attention_combine_kernel(AttnArgs a, int S) {
   const int h = blockIdx.y, b = blockIdx.z;
   const int N = a.N;
-  const int total = a.ctx[b] + N;
-  const int nsplit = (total + a.chunk - 1) / a.chunk;
-  if (nsplit <= 1) return;
   constexpr int D4 = D / 4;                       // lanes per node
   const int n = blockIdx.x * CMB_NODES + threadIdx.x / D4;
   if (threadIdx.x / D4 >= CMB_NODES || n >= N) return;
   const int d0 = (threadIdx.x % D4) * 4;
   const int64_t bh = (int64_t)b * a.Hq + h;
-  float M = -INFINITY;
-  for (int q = 0; q < nsplit; ++q) M = fmaxf(M, a.ml[(bh * S + q) * N + n].x);
-  float L = 0.f;
+  const int ctxb = min(max(a.ctx[b], 0), a.max_ctx);
+  float M = -INFINITY, L = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int q = 0; q < nsplit; ++q) {
-    const float2 mlq = a.ml[(bh * S + q) * N + n];
-    const float w = (mlq.x == -INFINITY) ? 0.f : exp2f(mlq.x - M);
-    L += w * mlq.y;
-    acc += w * *reinterpret_cast<const f32x4*>(a.opart + ((bh * S + q) * N + n) * D + d0);
+  for (int q0 = 0; q0 < S; q0 += CMB_BATCH) {
+    float2 ml[CMB_BATCH];
+    f32x4 op[CMB_BATCH];
+#pragma unroll
+    for (int j = 0; j < CMB_BATCH; ++j) {
+      const int q = min(q0 + j, S - 1);
+      ml[j] = a.ml[(bh * S + q) * N + n];
+      using PT = typename PartT<T>::type;
+      const PT* src = reinterpret_cast<const PT*>(a.opart) + ((bh * S + q) * N + n) * D + d0;
+      if constexpr (sizeof(PT) == 2) {
+        typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+        const h4 v = *reinterpret_cast<const h4*>(src);
+        op[j] = f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+      } else {
+        op[j] = *reinterpret_cast<const f32x4*>(src);
+      }
+    }
+    const int nsplit = (ctxb + N + a.chunk - 1) / a.chunk;
+    // this batch's maximum, then the running state rescaled to it
+    float Mb = M;
+#pragma unroll
+    for (int j = 0; j < CMB_BATCH; ++j)
+      if (q0 + j < nsplit) Mb = fmaxf(Mb, ml[j].x);
+    const float r = (M == -INFINITY) ? 0.f : exp2f(M - Mb);
+    L *= r;
+    acc *= r;
+#pragma unroll
+    for (int j = 0; j < CMB_BATCH; ++j) {
+      if (q0 + j < nsplit && ml[j].x != -INFINITY) {
+        const float wl = exp2f(ml[j].x - Mb) * ml[j].y;
+        L += wl;
+        acc += wl * op[j];
+      }
+    }
+    M = Mb;
   }
   const float inv = 1.f / L;
   T* orow = reinterpret_cast<T*>(a.O) + (((int64_t)b * N + n) * a.Hq + h) * D;
@@ -414,12 +474,12 @@ SplitPlan plan_splits(int B, int Hq, int N, int max_ctx, int P) {
 struct WsLayout {
   size_t ml, opart, total;
 };
-WsLayout ws_layout(int B, int Hq, int N, int D, int S) {
+WsLayout ws_layout(int B, int Hq, int N, int D, int S, size_t part_elem) {
   using medusa_host::align_up;
   WsLayout w;
   w.ml = 0;
   w.opart = w.ml + align_up((size_t)B * Hq * S * N * sizeof(float2), 256);
-  w.total = w.opart + align_up((size_t)B * Hq * S * N * D * sizeof(float), 256);
+  w.total = w.opart + align_up((size_t)B * Hq * S * N * D * part_elem, 256);
   return w;
 }
 
@@ -430,7 +490,7 @@ extern "C" size_t medusa_tree_attention_ws(int32_t B, int32_t N, int32_t Hq, int
   (void)Hkv;
   if (B <= 0 || N <= 0 || Hq <= 0 || D <= 0 || max_ctx < 0 || P < 1) return 0;
   const SplitPlan p = plan_splits(B, Hq, N, max_ctx, P);
-  return ws_layout(B, Hq, N, D, p.splits).total;
+  return ws_layout(B, Hq, N, D, p.splits, sizeof(float)).total;  // fits either dtype
 }
 
 extern "C" int32_t medusa_tree_attention(const void* Q, const void* Kt, const void* Vt, void* Kc,
@@ -465,7 +525,7 @@ extern "C" int32_t medusa_tree_attention(const void* Q, const void* Kt, const vo
                          16 == 0,
                  MEDUSA_ERR_INVALID_ARG, "medusa_tree_attention: tensors must be 16-byte aligned");
   const SplitPlan p = plan_splits(B, Hq, N, max_ctx, P);
-  const WsLayout L = ws_layout(B, Hq, N, D, p.splits);
+  const WsLayout L = ws_layout(B, Hq, N, D, p.splits, sizeof(float));
   MEDUSA_REQUIRE(ws != NULL && ws_bytes >= L.total, MEDUSA_ERR_WORKSPACE,
                  "medusa_tree_attention: workspace %zu < %zu bytes", ws_bytes, L.total);
   MEDUSA_REQUIRE((uintptr_t)ws % 256 == 0, MEDUSA_ERR_INVALID_ARG,
@@ -475,9 +535,10 @@ extern "C" int32_t medusa_tree_attention(const void* Q, const void* Kt, const vo
   a.Q = Q; a.Kt = Kt; a.Vt = Vt; a.Kc = Kc; a.Vc = Vc;
   a.page_table = page_table; a.ctx = ctx; a.mask = mask; a.O = O;
   a.ml = (float2*)((char*)ws + L.ml);
-  a.opart = (float*)((char*)ws + L.opart);
+  a.opart = (char*)ws + L.opart;
   a.max_pages = max_pages; a.P = P; a.B = B; a.N = N; a.Hq = Hq; a.Hkv = Hkv;
   a.chunk = p.chunk;
+  a.max_ctx = max_ctx;
   a.scale_log2 = scale * 1.4426950408889634f;
   dim3 grid((unsigned)p.splits, (unsigned)Hq, (unsigned)B);
   dim3 cgrid((unsigned)((N + medusa::CMB_NODES - 1) / medusa::CMB_NODES), (unsigned)Hq, (unsigned)B);

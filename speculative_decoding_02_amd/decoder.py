@@ -125,7 +125,7 @@ class MedusaDecoder:
         self.max_ctx = self.capacity - 64          # every call has ctx + n <= capacity
         self.attn_ws = M._ws(max(M.tree_attention_ws_bytes(1, n, model.n_heads, model.n_kv_heads,
                                                            model.head_dim, self.max_ctx, page_size)
-                                 for n in range(1, 65)), dev, zero=True)
+                                 for n in range(1, 65)), dev)
         self.acc_ws = M._ws(M._lib.medusa_accept_ws(1, 64), dev)
         dt = M._dt(model.t["embed"])
         self.heads_ws = M._ws(M._lib.medusa_heads_ws(1, model.hidden, model.n_medusa, model.vocab,

@@ -104,12 +104,13 @@ def _p(t):
     return t.data_ptr()
 
 
-def _ws(nbytes, device, zero=False):
+def _ws(nbytes, device):
+    """A zero-filled workspace (the projection's arrival counters must start
+    at zero; the library leaves them zero)."""
     if torch.cuda.is_current_stream_capturing():
         raise RuntimeError("workspace allocation during graph capture: preallocate it")
     nbytes = max(int(nbytes), 256)
-    f = torch.zeros if zero else torch.empty
-    return f(nbytes, dtype=torch.uint8, device=device)
+    return torch.zeros(nbytes, dtype=torch.uint8, device=device)
 
 
 # ---------------------------------------------------------------------------
@@ -217,7 +218,7 @@ def medusa_tree_attention(Q, Kt, Vt, Kc, Vc, page_table, ctx, max_ctx, mask, sca
     out = out if out is not None else torch.empty_like(Q)
     need = _lib.medusa_tree_attention_ws(B, N, Hq, Hkv, D, int(max_ctx), P)
     if ws is None or ws.numel() < need:
-        ws = _ws(need, Q.device, zero=True)
+        ws = _ws(need, Q.device)
     _check("medusa_tree_attention", _lib.medusa_tree_attention(
         _p(Q), _p(Kt), _p(Vt), _p(Kc), _p(Vc), _p(page_table), page_table.shape[1], P, _p(ctx),
         int(max_ctx), _p(mask), B, N, Hq, Hkv, D, float(scale), dt, _p(out), _p(ws), ws.numel(),
