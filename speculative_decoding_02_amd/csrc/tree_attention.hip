@@ -27,6 +27,8 @@
 //   * the tile loads run PF tiles ahead through a ring of register stages
 //     (unrolled, so every stage index is static), keeping a workgroup's whole
 //     key range in flight for the short ranges of decode-time splits.
+#include <algorithm>
+
 #include "common.h"
 
 namespace medusa {
@@ -379,6 +381,253 @@ __global__ __launch_bounds__(ATT_THREADS) void tree_attention_kernel(AttnArgs a)
   }
 }
 
+// bf16 variant with the key/value tiles streamed straight into LDS.
+//   * Each wave issues LDS-DMA loads (16 bytes per lane, written at m0 +
+//     16*lane) for its quarter of a tile's K and V rows; tiles go to a ring of
+//     R LDS slots, so R tiles are in flight without holding registers, and
+//     the loop body is not unrolled (the slot is a runtime index).
+//   * Row r of a tile keeps its 16-byte chunk c at position c ^ (r & SW):
+//     the lane that fills position p fetches chunk p ^ (r & SW).  The score
+//     MFMA's operand reads (16 rows, one chunk column) then hit 16 distinct
+//     bank groups.
+//   * V stays row-major; the P.V MFMA's V^T operand comes from the gfx950
+//     transposing LDS read: within a 16-lane block, lane i returns element
+//     i%4 of the 4 values at source lane (i/4)+4r's address, so pointing lane
+//     j of block g at V[key 4g + j/4][dim 4(j%4)] yields V[key 4g + r][dim i].
+//   * Waits are explicit: s_barrier without a fence (a fenced barrier would
+//     wait for every DMA in flight) after waiting until only the later
+//     tiles' (R-1) x OPS DMA loads are outstanding.
+// One LDS-DMA instruction: every lane's 16 bytes at gptr land at LDS byte
+// address lds_addr + 16 * lane (lds_addr is wave-uniform, set in m0).  It is
+// issued from inline asm so that the compiler does not treat it as an LDS
+// store it must wait for before every LDS read (it would wait for all DMA in
+// flight); the kernel's own vmcnt waits and barriers order the accesses.
+// The instruction writes no register.  m0 cannot be declared as clobbered
+// (it is reserved); the kernels that use this helper contain no other m0
+// use (no indexed register moves, no m0-based LDS or message instructions),
+// which the compiled code of this file shows.
+__device__ __forceinline__ void lds_dma16(const void* gptr, uint32_t lds_addr) {
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_addr);
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+               :
+               : "s"(m0v), "v"(gptr)
+               : "memory");
+}
+
+template <int D, int R>
+__global__ __launch_bounds__(ATT_THREADS) void tree_attention_dma_kernel(AttnArgs a) {
+  using T = bf16_t;
+  constexpr int P16 = 8;                       // bf16 per 16 bytes
+  constexpr int ROWB = D * 2;                  // bytes per key row
+  constexpr int CPR = ROWB / 16;               // 16-byte chunks per row
+  constexpr int SW = CPR - 1;                  // swizzle mask
+  constexpr int TILEB = ATT_TILE * ROWB;       // bytes of one K (or V) tile
+  constexpr int SLOTB = 2 * TILEB;
+  constexpr int RPD = 1024 / ROWB;             // rows per DMA instruction (64 lanes x 16 B)
+  constexpr int DPW = TILEB / 1024 / 4;        // DMA instructions per wave per tensor
+  constexpr int OPS = 2 * DPW;                 // vector-memory ops per wave per tile
+  constexpr int QSTEPS = D / 32;
+  constexpr int DB = D / 16;
+  constexpr int WAITN = (R - 1) * OPS;         // DMA ops allowed in flight at a tile start
+  static_assert(WAITN < 64, "vmcnt range");
+  constexpr int WAIT_IMM = (WAITN & 15) | ((WAITN >> 4) << 14) | (7 << 4) | (15 << 8);
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[R * SLOTB];
+  __shared__ int spages[ATT_MAX_SPLIT_PAGES];
+
+  const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int S = gridDim.x;
+  const int N = a.N;
+  const int k_beg = s * a.chunk;
+  const int group = a.Hq / a.Hkv;
+  const int kvh = h / group;
+  const bool appender = (h % group) == 0;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+  const int node = wave * 16 + lr;
+  const bool wave_active = wave * 16 < N;
+  const int nodec = min(node, N - 1);
+
+  const T* Qp = reinterpret_cast<const T*>(a.Q);
+  const T* Ktp = reinterpret_cast<const T*>(a.Kt);
+  const T* Vtp = reinterpret_cast<const T*>(a.Vt);
+  T* Kcp = reinterpret_cast<T*>(a.Kc);
+  T* Vcp = reinterpret_cast<T*>(a.Vc);
+  const int* pt = a.page_table + (int64_t)b * a.max_pages;
+
+  // One round trip before the tile stream (as in tree_attention_kernel).
+  const int page0 = k_beg / a.P;
+  const int slice_end = min(k_beg + a.chunk, a.max_ctx + N);
+  const int npages = slice_end > k_beg ? (slice_end - 1) / a.P - page0 + 1 : 0;
+  const int ctxb = min(max(a.ctx[b], 0), a.max_ctx);
+  static_assert(ATT_MAX_SPLIT_PAGES <= ATT_THREADS, "one page-table entry per thread");
+  const int my_page = threadIdx.x < npages ? pt[page0 + threadIdx.x] : 0;
+  u32x4 qf[QSTEPS];
+  {
+    const T* qrow = Qp + (((int64_t)b * N + nodec) * a.Hq + h) * D;
+#pragma unroll
+    for (int st = 0; st < QSTEPS; ++st)
+      qf[st] = *reinterpret_cast<const u32x4*>(qrow + st * 4 * P16 + lg * P16);
+  }
+  const uint64_t mrow = a.mask[(int64_t)b * N + nodec];
+  __builtin_amdgcn_s_waitcnt(0);
+  if (threadIdx.x < npages) spages[threadIdx.x] = my_page;
+  __syncthreads();
+  const int total = ctxb + N;
+  if (k_beg >= total) return;  // uniform over the workgroup
+  const int k_end = min(k_beg + a.chunk, total);
+  const int ntiles = (k_end - k_beg + ATT_TILE - 1) / ATT_TILE;
+
+  auto cache_off = [&](int j) -> int64_t {
+    const int page = spages[j / a.P - page0];
+    return (((int64_t)page * a.Hkv + kvh) * a.P + (j % a.P)) * D;
+  };
+  auto tree_off = [&](int j) -> int64_t {
+    return (((int64_t)b * N + max(j - ctxb, 0)) * a.Hkv + kvh) * D;
+  };
+
+  const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)lds;
+  // DMA of tile t (clamped to the split's last tile) into ring slot `slot`
+  auto issue = [&](int t, int slot) {
+    const int tile0 = k_beg + min(t, ntiles - 1) * ATT_TILE;
+#pragma unroll
+    for (int i = 0; i < DPW; ++i) {
+      const int q = wave * DPW + i;          // 1 KB block of the tile
+      const int r = q * RPD + lane / CPR;    // tile row this lane fills
+      const int c = (lane % CPR) ^ (r & SW); // chunk fetched for that position
+      const int jj = min(tile0 + r, k_end - 1);
+      const bool cached = jj < ctxb;
+      const int64_t off = cached ? cache_off(jj) : tree_off(jj);
+      const T* ksrc = (cached ? Kcp : Ktp) + off + c * P16;
+      const T* vsrc = (cached ? Vcp : Vtp) + off + c * P16;
+      const uint32_t kd = lds_base + slot * SLOTB + q * 1024;
+      lds_dma16(ksrc, kd);
+      lds_dma16(vsrc, kd + TILEB);
+    }
+  };
+
+  f32x4 oacc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float mrun = -INFINITY, lrun = 0.f;
+
+  for (int t = 0; t < R; ++t) issue(t, t);
+  for (int t = 0; t < ntiles; ++t) {
+    const int slot = t % R;
+    const int tile0 = k_beg + t * ATT_TILE;
+    __builtin_amdgcn_s_waitcnt(WAIT_IMM);  // this wave's DMA of tile t is done
+    __builtin_amdgcn_s_barrier();          // ... and every other wave's
+    asm volatile("" ::: "memory");         // no LDS access moves across the barrier
+    const unsigned char* ks = lds + slot * SLOTB;
+    const unsigned char* vs = ks + TILEB;
+    if (wave_active) {
+      f32x4 sacc[4];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        sacc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const int r = kb * 16 + lr;
+#pragma unroll
+        for (int st = 0; st < QSTEPS; ++st) {
+          const int c = (st * 4 + lg) ^ (r & SW);
+          const u32x4 kf = *reinterpret_cast<const u32x4*>(ks + r * ROWB + c * 16);
+          sacc[kb] = mfma_bf16_16x16x32(kf, qf[st], sacc[kb]);
+        }
+      }
+      float x[4][4];
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int j = tile0 + kb * 16 + lg * 4 + r;
+          const uint32_t bit = (uint32_t)(mrow >> (uint32_t)min(max(j - ctxb, 0), 63)) & 1u;
+          const bool ok = (j < k_end) & ((j < ctxb) | (bit != 0u));
+          x[kb][r] = ok ? sacc[kb][r] * a.scale_log2 : -INFINITY;
+          tmax = fmaxf(tmax, x[kb][r]);
+        }
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+      const float mnew = fmaxf(mrun, tmax);
+      const float alpha = (mnew == -INFINITY) ? 1.f : exp2f(mrun - mnew);
+      float psum = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float p = (x[kb][r] == -INFINITY) ? 0.f : exp2f(x[kb][r] - mnew);
+          x[kb][r] = p;
+          psum += p;
+        }
+      lrun = lrun * alpha + psum;
+      mrun = mnew;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        u32x2 pb;
+        pb.x = pack_bf2(x[kb][0], x[kb][1]);
+        pb.y = pack_bf2(x[kb][2], x[kb][3]);
+        const int rr = kb * 16 + 4 * lg + (lr >> 2);  // source row of this lane's address
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const int c = db * 2 + ((lr & 3) >> 1);
+          const unsigned char* src = vs + rr * ROWB + ((c ^ (rr & SW)) * 16) + (lr & 1) * 8;
+          typedef short s4 __attribute__((ext_vector_type(4)));
+          const s4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4*)src);
+          oacc[db] = mfma_bf16_16x16x16(__builtin_bit_cast(u32x2, v), pb, oacc[db]);
+        }
+      }
+    }
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);    // lgkmcnt(0): this wave's LDS reads are done
+    __builtin_amdgcn_s_barrier();          // ... so the slot can be refilled
+    asm volatile("" ::: "memory");
+    issue(t + R, slot);
+  }
+  __builtin_amdgcn_s_waitcnt(0);           // drain the clamped refills before leaving
+
+  // Store the tree keys' K/V of this split into cache slots ctx..ctx+N-1.
+  if (appender && k_end > ctxb) {
+    constexpr int CPRT = D / P16;
+    const int j0 = max(k_beg, ctxb);
+    const int items = (k_end - j0) * CPRT * 2;
+    for (int e = tid; e < items; e += ATT_THREADS) {
+      const int which = e / ((k_end - j0) * CPRT), rem = e % ((k_end - j0) * CPRT);
+      const int j = j0 + rem / CPRT, part = rem % CPRT;
+      const T* src = (which ? Vtp : Ktp) + tree_off(j) + part * P16;
+      T* dst = (which ? Vcp : Kcp) + cache_off(j) + part * P16;
+      *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src);
+    }
+  }
+
+  float ltot = lrun + __shfl_xor(lrun, 16, 64);
+  ltot = ltot + __shfl_xor(ltot, 32, 64);
+  const bool node_ok = wave_active && node < N;
+  if (S == 1) {
+    if (node_ok) {
+      const float inv = 1.f / ltot;
+      T* orow = reinterpret_cast<T*>(a.O) + (((int64_t)b * N + node) * a.Hq + h) * D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) st<T>(orow, db * 16 + lg * 4 + r, oacc[db][r] * inv);
+    }
+    return;
+  }
+  const int64_t bh = (int64_t)b * a.Hq + h;
+  if (node_ok) {
+    _Float16* op = reinterpret_cast<_Float16*>(a.opart) + ((bh * S + s) * N + node) * D;
+    const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+    typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      h4 v = {(_Float16)(oacc[db][0] * inv), (_Float16)(oacc[db][1] * inv), (_Float16)(oacc[db][2] * inv),
+              (_Float16)(oacc[db][3] * inv)};
+      *reinterpret_cast<h4*>(op + db * 16 + lg * 4) = v;
+    }
+    if (lg == 0) a.ml[(bh * S + s) * N + node] = make_float2(mrun, ltot);
+  }
+}
+
 // Merge of the split partials of one (sequence, head): O = sum_s w_s l_s o_s
 // / sum_s w_s l_s with w_s = 2^(m_s - max m) and o_s the split's normalised
 // output, splits in index order.  One
@@ -459,10 +708,16 @@ namespace {
 struct SplitPlan {
   int chunk, splits;
 };
-SplitPlan plan_splits(int B, int Hq, int N, int max_ctx, int P) {
+#ifndef MEDUSA_ATTN_DMA_WGS
+#define MEDUSA_ATTN_DMA_WGS 256
+#endif
+#ifndef MEDUSA_ATTN_DMA_R
+#define MEDUSA_ATTN_DMA_R 2
+#endif
+SplitPlan plan_splits(int B, int Hq, int N, int max_ctx, int P, int target) {
   const int total = max_ctx + N;
   const int bh = B * Hq;
-  const int want = (MEDUSA_ATTN_TARGET_WGS + bh - 1) / bh;
+  const int want = (target + bh - 1) / bh;
   int chunk = (total + want - 1) / want;
   chunk = (chunk + medusa::ATT_TILE - 1) / medusa::ATT_TILE * medusa::ATT_TILE;
   // a split's keys must span at most ATT_MAX_SPLIT_PAGES pages
@@ -489,8 +744,10 @@ extern "C" size_t medusa_tree_attention_ws(int32_t B, int32_t N, int32_t Hq, int
                                            int32_t D, int32_t max_ctx, int32_t P) {
   (void)Hkv;
   if (B <= 0 || N <= 0 || Hq <= 0 || D <= 0 || max_ctx < 0 || P < 1) return 0;
-  const SplitPlan p = plan_splits(B, Hq, N, max_ctx, P);
-  return ws_layout(B, Hq, N, D, p.splits, sizeof(float)).total;  // fits either dtype
+  // either dtype's plan (fp32 partials are the larger element)
+  const SplitPlan p1 = plan_splits(B, Hq, N, max_ctx, P, MEDUSA_ATTN_TARGET_WGS);
+  const SplitPlan p2 = plan_splits(B, Hq, N, max_ctx, P, MEDUSA_ATTN_DMA_WGS);
+  return ws_layout(B, Hq, N, D, std::max(p1.splits, p2.splits), sizeof(float)).total;
 }
 
 extern "C" int32_t medusa_tree_attention(const void* Q, const void* Kt, const void* Vt, void* Kc,
@@ -524,7 +781,8 @@ extern "C" int32_t medusa_tree_attention(const void* Q, const void* Kt, const vo
   MEDUSA_REQUIRE(((uintptr_t)Q | (uintptr_t)Kt | (uintptr_t)Vt | (uintptr_t)Kc | (uintptr_t)Vc) %
                          16 == 0,
                  MEDUSA_ERR_INVALID_ARG, "medusa_tree_attention: tensors must be 16-byte aligned");
-  const SplitPlan p = plan_splits(B, Hq, N, max_ctx, P);
+  const SplitPlan p = plan_splits(B, Hq, N, max_ctx, P,
+                                  dt == MEDUSA_BF16 ? MEDUSA_ATTN_DMA_WGS : MEDUSA_ATTN_TARGET_WGS);
   const WsLayout L = ws_layout(B, Hq, N, D, p.splits, sizeof(float));
   MEDUSA_REQUIRE(ws != NULL && ws_bytes >= L.total, MEDUSA_ERR_WORKSPACE,
                  "medusa_tree_attention: workspace %zu < %zu bytes", ws_bytes, L.total);
@@ -545,17 +803,20 @@ extern "C" int32_t medusa_tree_attention(const void* Q, const void* Kt, const vo
   hipStream_t st = (hipStream_t)stream;
   const dim3 blk(medusa::ATT_THREADS);
   constexpr int PF = MEDUSA_ATTN_PF;
-#define MEDUSA_ATT_LAUNCH(T, DD)                                                             \
+#define MEDUSA_ATT_LAUNCH(KERNEL, T, DD)                                                     \
   do {                                                                                       \
-    hipLaunchKernelGGL((medusa::tree_attention_kernel<T, DD, PF>), grid, blk, 0, st, a);     \
+    hipLaunchKernelGGL((KERNEL), grid, blk, 0, st, a);                                       \
     if (p.splits > 1)                                                                        \
       hipLaunchKernelGGL((medusa::tree_attention_combine_kernel<T, DD>), cgrid, blk, 0, st,  \
                          a, p.splits);                                                       \
   } while (0)
+  constexpr int RD = MEDUSA_ATTN_DMA_R;
   if (dt == MEDUSA_BF16) {
-    if (D == 128) MEDUSA_ATT_LAUNCH(medusa::bf16_t, 128); else MEDUSA_ATT_LAUNCH(medusa::bf16_t, 64);
+    if (D == 128) MEDUSA_ATT_LAUNCH((medusa::tree_attention_dma_kernel<128, RD>), medusa::bf16_t, 128);
+    else MEDUSA_ATT_LAUNCH((medusa::tree_attention_dma_kernel<64, 2 * RD>), medusa::bf16_t, 64);
   } else {
-    if (D == 128) MEDUSA_ATT_LAUNCH(float, 128); else MEDUSA_ATT_LAUNCH(float, 64);
+    if (D == 128) MEDUSA_ATT_LAUNCH((medusa::tree_attention_kernel<float, 128, PF>), float, 128);
+    else MEDUSA_ATT_LAUNCH((medusa::tree_attention_kernel<float, 64, PF>), float, 64);
   }
 #undef MEDUSA_ATT_LAUNCH
   return check_launch("medusa_tree_attention");
