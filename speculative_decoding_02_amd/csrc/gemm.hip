@@ -362,6 +362,193 @@ __global__ __launch_bounds__(256) void gemm_xlds_kernel(const T* __restrict__ X,
       }
 }
 
+// ---------------------------------------------------------------------------
+// Variant for wide outputs (M > 16 rows, N/16 >= MEDUSA_GEMM_XB_MIN_BLOCKS):
+// G workgroups per (batch element, activation-row tile), about one per
+// compute unit, each owning a contiguous range of whole 16-row weight blocks
+// over the full contraction (pairs of blocks for SwiGLU, whose gate and up
+// rows interleave in 16-row blocks).  Every compute unit then streams nearly
+// the same number of weight bytes with no split-contraction partials.
+// Within a workgroup, wave w takes the range's blocks w and w+4 (0, 1 or 2
+// blocks: one code path per count, all with the same sequence of barriers);
+// the activation rows are shared through LDS one 256-wide chunk at a time
+// (two register sets give a two-chunk lead).  Weight loads run PF steps
+// ahead in registers, every load is unconditional (clamped) and scheduling
+// barriers fix the issue order, so the compiler's wait counts stay exact.
+// The epilogue goes through LDS, so a gate block and its up block may sit in
+// different waves and the output stores are coalesced.  Each output is one
+// wave's accumulation chain in step order: results depend on (Kd, N) only.
+constexpr int XB_KC = 256;
+constexpr int XB_XSETS = 2;
+constexpr int XB_MAXB = 8;  // blocks per workgroup: 2 per wave
+constexpr int xb_gcd(int a, int b) { return b == 0 ? a : xb_gcd(b, a % b); }
+constexpr int xb_lcm(int a, int b) { return a / xb_gcd(a, b) * b; }
+
+template <typename T, int EPI>
+__device__ __forceinline__ void xb_store(int gi, int M, int Nw, int64_t xbs, const T* bias,
+                                         const void* aux, void* Y, int y_f32, int m, int n, float v) {
+  const int64_t o = (int64_t)gi * M * Nw + (int64_t)m * Nw + n;
+  if (EPI == MEDUSA_EPI_NONE) {
+    if (y_f32) reinterpret_cast<float*>(Y)[o] = v;
+    else st<T>(reinterpret_cast<T*>(Y), o, v);
+  } else if (EPI == MEDUSA_EPI_BIAS_SILU_RES) {
+    const T* R = reinterpret_cast<const T*>(aux) + (int64_t)gi * xbs;
+    const float res = ld<T>(R, (int64_t)m * Nw + n);
+    const float b = bias ? ld<T>(bias, (int64_t)gi * Nw + n) : 0.f;
+    st<T>(reinterpret_cast<T*>(Y), o, res + silu_f(v + b));
+  } else {  // MEDUSA_EPI_RES_ADD_F32
+    const float res = reinterpret_cast<const float*>(aux)[(int64_t)m * Nw + n];
+    reinterpret_cast<float*>(Y)[(int64_t)m * Nw + n] = res + v;
+  }
+}
+
+template <typename T, int MB, int PF, int EPI>
+__global__ __launch_bounds__(256) void gemm_xlb_kernel(const T* __restrict__ X, int64_t xbs, int M,
+                                                       int Kd, const T* __restrict__ W, int Nw,
+                                                       const T* __restrict__ bias, const void* aux,
+                                                       void* Y, int y_f32, int G, int MT, int unit) {
+  using TR = GemmTraits<T>;
+  constexpr int P16 = TR::per16;
+  constexpr int KSTEP = 4 * P16;
+  constexpr int SC = XB_KC / KSTEP;            // steps per chunk
+  constexpr int TM = 16 * MB;
+  constexpr int LDX = XB_KC + P16;             // padded LDS row (elements)
+  constexpr int XV = TM * XB_KC / P16 / 256;   // 16-byte vectors per thread per chunk
+  constexpr int GS = xb_lcm(PF, XB_XSETS * SC);  // unrolled group: whole ring and set turns
+  constexpr int LDE = TM + 1;
+  __shared__ __attribute__((aligned(16))) T xs[TM * LDX];
+  __shared__ float ep[XB_MAXB * 16 * LDE];
+
+  const int g = blockIdx.x, slice = blockIdx.y;
+  const int gi = slice / MT, m0 = (slice % MT) * TM;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int lr = lane & 15, lg = lane >> 4;
+  const int nunits = (Nw / 16) / unit;
+  const int u0 = (int)((int64_t)g * nunits / G), u1 = (int)((int64_t)(g + 1) * nunits / G);
+  const int b0 = u0 * unit, nb = (u1 - u0) * unit;  // this workgroup's blocks (<= XB_MAXB)
+  const int nw = (wave < nb ? 1 : 0) + (wave + 4 < nb ? 1 : 0);
+  const int nchunks = Kd / XB_KC;
+  const int nsteps = nchunks * SC;
+  const T* Xg = X + (int64_t)gi * xbs;
+  const T* Wg = W + (int64_t)gi * Nw * Kd;
+
+  auto run = [&](auto nbwc) {
+    constexpr int NBW = decltype(nbwc)::value;  // blocks of this wave
+    constexpr int NBA = NBW > 0 ? NBW : 1;
+    const T* wrow[NBA];
+#pragma unroll
+    for (int j = 0; j < NBA; ++j) {
+      const int blk = min(b0 + wave + 4 * j, Nw / 16 - 1);
+      wrow[j] = Wg + (int64_t)(blk * 16 + lr) * Kd + lg * P16;
+    }
+    u32x4 xr[XB_XSETS][XV];
+    auto xload = [&](int set, int c) {
+      c = min(c, nchunks - 1);
+#pragma unroll
+      for (int i = 0; i < XV; ++i) {
+        const int idx = threadIdx.x + i * 256;
+        const int row = idx / (XB_KC / P16), col = idx % (XB_KC / P16);
+        const int rr = min(m0 + row, M - 1);
+        xr[set][i] = *reinterpret_cast<const u32x4*>(Xg + (int64_t)rr * Kd + c * XB_KC + col * P16);
+      }
+    };
+    auto xstore = [&](int set, bool live) {
+#pragma unroll
+      for (int i = 0; i < XV; ++i) {
+        const int idx = threadIdx.x + i * 256;
+        const int row = idx / (XB_KC / P16), col = idx % (XB_KC / P16);
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        *reinterpret_cast<u32x4*>(&xs[row * LDX + col * P16]) = live ? xr[set][i] : z;
+      }
+    };
+    u32x4 fb[PF][NBA];
+    auto wload = [&](int u, int st) {
+      if constexpr (NBW > 0) {
+        const int k = min(st, nsteps - 1) * KSTEP;
+#pragma unroll
+        for (int j = 0; j < NBW; ++j) fb[u][j] = *reinterpret_cast<const u32x4*>(wrow[j] + k);
+      }
+    };
+    f32x4 acc[MB][NBA];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int j = 0; j < NBA; ++j) acc[mb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // Prologue: the loads the loop would have issued during the GS steps
+    // before step 0, in the same order, so the loop head sees one
+    // pending-load pattern on entry and on every turn.
+#pragma unroll
+    for (int i = 0; i < GS; ++i) {
+      const int tau = i - GS;
+      if (tau % SC == 0 && tau >= -XB_XSETS * SC) {
+        const int q = tau / SC + XB_XSETS;
+        xload(q, q);
+      }
+      if (tau >= -PF) wload(tau + PF, tau + PF);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // Whole groups only; chunks past the end store zeros, adding nothing.
+    for (int s0 = 0; s0 < nsteps; s0 += GS) {
+#pragma unroll
+      for (int sl = 0; sl < GS; ++sl) {
+        if (sl % SC == 0) {
+          const int q = (s0 + sl) / SC;
+          const int set = (sl / SC) % XB_XSETS;
+          __syncthreads();  // everyone is done reading the previous chunk
+          xstore(set, q < nchunks);
+          __syncthreads();
+          xload(set, q + XB_XSETS);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        if constexpr (NBW > 0) {
+          const int u = sl % PF, kk = sl % SC;
+          u32x4 xa[MB];
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb)
+            xa[mb] = *reinterpret_cast<const u32x4*>(&xs[(mb * 16 + lr) * LDX + kk * KSTEP + lg * P16]);
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int j = 0; j < NBW; ++j) acc[mb][j] = TR::mma(xa[mb], fb[u][j], acc[mb][j]);
+          wload(u, s0 + sl + PF);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    }
+    // lane holds weight row lr of local block wave + 4j, activation rows
+    // mb*16 + 4*lg + r
+#pragma unroll
+    for (int j = 0; j < NBW; ++j)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          ep[((wave + 4 * j) * 16 + lr) * LDE + mb * 16 + lg * 4 + r] = acc[mb][j][r];
+  };
+  if (nw == 2) run(std::integral_constant<int, 2>());
+  else if (nw == 1) run(std::integral_constant<int, 1>());
+  else run(std::integral_constant<int, 0>());
+  __syncthreads();
+
+  if (EPI == MEDUSA_EPI_SWIGLU) {
+    // local blocks 2p (gate) and 2p+1 (up); b0 is even
+    const int F = Nw / 2, f0 = b0 / 2 * 16, nf = nb / 2 * 16;
+    T* Yg = reinterpret_cast<T*>(Y) + (int64_t)gi * M * F;
+    for (int e = threadIdx.x; e < nf * TM; e += 256) {
+      const int m = e / nf, fl = e % nf;
+      const int gr = (fl / 16) * 32 + fl % 16;  // gate row in the range; up is 16 further
+      if (m0 + m < M) st<T>(Yg, (int64_t)(m0 + m) * F + f0 + fl, silu_f(ep[gr * LDE + m]) * ep[(gr + 16) * LDE + m]);
+    }
+    return;
+  }
+  const int nn = nb * 16;
+  for (int e = threadIdx.x; e < nn * TM; e += 256) {
+    const int m = e / nn, nl = e % nn;
+    if (m0 + m < M) xb_store<T, EPI>(gi, M, Nw, xbs, bias, aux, Y, y_f32, m0 + m, b0 * 16 + nl, ep[nl * LDE + m]);
+  }
+}
+
 #ifndef MEDUSA_GEMM_NB
 #define MEDUSA_GEMM_NB 2
 #endif
@@ -412,6 +599,9 @@ __global__ __launch_bounds__(256) void gemm_split_reduce_kernel(const float* __r
 #ifndef MEDUSA_GEMM_XL_NB
 #define MEDUSA_GEMM_XL_NB 2
 #endif
+#ifndef MEDUSA_GEMM_XB_PF
+#define MEDUSA_GEMM_XB_PF 8
+#endif
 #ifndef MEDUSA_GEMM_XL_TARGET_WGS
 #define MEDUSA_GEMM_XL_TARGET_WGS 384
 #endif
@@ -427,11 +617,32 @@ namespace medusa_host {
 struct GemmPlan {
   bool xl;
   int ksplit;
+  bool xb;      // block-range variant
+  int xb_unit;  // blocks per unit (2: SwiGLU gate/up pairs)
+  int xb_G;     // workgroups per (batch element, row tile)
+  int MT;       // activation-row tiles
 };
-GemmPlan gemm_plan(int64_t M, int64_t Kd, int64_t Nw, int dt) {
+#ifndef MEDUSA_GEMM_XB_MIN_BLOCKS
+#define MEDUSA_GEMM_XB_MIN_BLOCKS 512
+#endif
+#ifndef MEDUSA_GEMM_XB_WGS
+#define MEDUSA_GEMM_XB_WGS 256
+#endif
+GemmPlan gemm_plan(int64_t M, int64_t Kd, int64_t Nw, int dt, int epi) {
   using namespace medusa;
   constexpr int XNB = MEDUSA_GEMM_XL_NB;
-  GemmPlan p{false, 1};
+  GemmPlan p{false, 1, false, 1, 0, 1};
+  const int unit = epi == MEDUSA_EPI_SWIGLU ? 2 : 1;
+  if (dt == MEDUSA_BF16 && M > 16 && Kd % XB_KC == 0 && Nw % (16 * unit) == 0 &&
+      Nw / 16 >= MEDUSA_GEMM_XB_MIN_BLOCKS && Nw / 16 <= (1 << 24)) {
+    const int nunits = (int)(Nw / 16 / unit);
+    p.xb = true;
+    p.xb_unit = unit;
+    // about one workgroup per compute unit, at most XB_MAXB blocks each
+    p.xb_G = std::max(std::min(MEDUSA_GEMM_XB_WGS, nunits), (nunits + XB_MAXB / unit - 1) / (XB_MAXB / unit));
+    p.MT = (int)((M + (M <= 32 ? 32 : 64) - 1) / (M <= 32 ? 32 : 64));
+    return p;
+  }
   p.xl = dt == MEDUSA_BF16 && M > 16 && Kd % XL_KC == 0 && Nw >= MEDUSA_GEMM_XL_MIN_N &&
          Nw % (64 * XNB) == 0;
   if (!p.xl) return p;
@@ -448,9 +659,15 @@ GemmPlan gemm_plan(int64_t M, int64_t Kd, int64_t Nw, int dt) {
   return p;
 }
 size_t gemm_ws_bytes(int64_t M, int64_t Kd, int64_t Nw, int batch, int dt) {
-  const GemmPlan p = gemm_plan(M, Kd, Nw, dt);
-  if (!p.xl || p.ksplit <= 1) return 0;
-  return align_up((size_t)batch * p.ksplit * M * Nw * sizeof(float), 256);
+  // the larger of the two plan families (SwiGLU plans in gate/up pairs);
+  // only the split-contraction path uses scratch
+  size_t need = 0;
+  for (int epi : {(int)MEDUSA_EPI_NONE, (int)MEDUSA_EPI_SWIGLU}) {
+    const GemmPlan p = gemm_plan(M, Kd, Nw, dt, epi);
+    if (!p.xb && p.xl && p.ksplit > 1)
+      need = std::max(need, align_up((size_t)batch * p.ksplit * M * Nw * sizeof(float), 256));
+  }
+  return need;
 }
 }  // namespace medusa_host
 
@@ -462,7 +679,23 @@ static void launch_gemm_t(const void* X, int64_t xbs, int64_t M, int64_t Kd, con
   constexpr int NB = MEDUSA_GEMM_NB, KS = MEDUSA_GEMM_KS;
   constexpr int TN = 16 * NB;
   constexpr int XNB = MEDUSA_GEMM_XL_NB;
-  const medusa_host::GemmPlan plan = medusa_host::gemm_plan(M, Kd, Nw, sizeof(T) == 2 ? MEDUSA_BF16 : MEDUSA_F32);
+  const medusa_host::GemmPlan plan = medusa_host::gemm_plan(M, Kd, Nw, sizeof(T) == 2 ? MEDUSA_BF16 : MEDUSA_F32, EPI);
+  if constexpr (sizeof(T) == 2) {  // planned for bf16 only
+    if (plan.xb) {
+      const dim3 grid((unsigned)plan.xb_G, (unsigned)(batch * plan.MT));
+      if (M <= 32)
+        hipLaunchKernelGGL((gemm_xlb_kernel<T, 2, MEDUSA_GEMM_XB_PF, EPI>), grid, dim3(256), 0, st,
+                           reinterpret_cast<const T*>(X), xbs, (int)M, (int)Kd,
+                           reinterpret_cast<const T*>(W), (int)Nw, reinterpret_cast<const T*>(bias),
+                           aux, Y, y_f32, plan.xb_G, plan.MT, plan.xb_unit);
+      else
+        hipLaunchKernelGGL((gemm_xlb_kernel<T, 4, MEDUSA_GEMM_XB_PF, EPI>), grid, dim3(256), 0, st,
+                           reinterpret_cast<const T*>(X), xbs, (int)M, (int)Kd,
+                           reinterpret_cast<const T*>(W), (int)Nw, reinterpret_cast<const T*>(bias),
+                           aux, Y, y_f32, plan.xb_G, plan.MT, plan.xb_unit);
+      return;
+    }
+  }
   auto go = [&](auto mbc) {
     constexpr int MB = decltype(mbc)::value;
     const unsigned gy = (unsigned)((M + 16 * MB - 1) / (16 * MB));
