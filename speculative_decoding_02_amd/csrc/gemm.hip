@@ -61,6 +61,7 @@ __global__ __launch_bounds__(64 * KS) void gemm_kernel(const T* __restrict__ X, 
   constexpr int LDR = TN + 1;  // padded LDS row (floats)
   constexpr int PF = GemmRing<MB, NB>::PF;
   constexpr int NT = 64 * KS;
+  static_assert(EPI != MEDUSA_EPI_SWIGLU || NB % 2 == 0, "SwiGLU needs gate/up block pairs in a tile");
   __shared__ float red[KS][TM * LDR];
 
   const int g = blockIdx.z;
@@ -549,8 +550,10 @@ __global__ __launch_bounds__(256) void gemm_xlb_kernel(const T* __restrict__ X, 
   }
 }
 
+// 16-row blocks per workgroup of the small-row kernel (SwiGLU needs its
+// gate/up pair of blocks in one tile, so it always takes at least 2)
 #ifndef MEDUSA_GEMM_NB
-#define MEDUSA_GEMM_NB 2
+#define MEDUSA_GEMM_NB 1
 #endif
 #ifndef MEDUSA_GEMM_KS
 #define MEDUSA_GEMM_KS 4
@@ -676,7 +679,8 @@ template <typename T, int EPI>
 static void launch_gemm_t(const void* X, int64_t xbs, int64_t M, int64_t Kd, const void* W,
                           int64_t Nw, int batch, const void* bias, const void* aux, void* Y,
                           int y_f32, void* ws, hipStream_t st) {
-  constexpr int NB = MEDUSA_GEMM_NB, KS = MEDUSA_GEMM_KS;
+  constexpr int NB = (EPI == MEDUSA_EPI_SWIGLU && MEDUSA_GEMM_NB < 2) ? 2 : MEDUSA_GEMM_NB;
+  constexpr int KS = MEDUSA_GEMM_KS;
   constexpr int TN = 16 * NB;
   constexpr int XNB = MEDUSA_GEMM_XL_NB;
   const medusa_host::GemmPlan plan = medusa_host::gemm_plan(M, Kd, Nw, sizeof(T) == 2 ? MEDUSA_BF16 : MEDUSA_F32, EPI);
