@@ -33,7 +33,12 @@ def _rnd(dt, a):
 @pytest.mark.parametrize("dt", DTS, ids=DTN.get)
 @pytest.mark.parametrize("Mr,Kd,N", [(1, 256, 1000), (5, 72, 37), (17, 688, 80), (64, 256, 96),
                                      (100, 128, 33), (33, 4096, 64), (64, 512, 8192),
-                                     (40, 768, 12288), (17, 256, 16384), (130, 256, 8320)])
+                                     (40, 768, 12288), (17, 256, 16384), (130, 256, 8320),
+                                     # 4096-wide outputs (contraction split across
+                                     # workgroups; 11 chunks: uneven split)
+                                     (64, 4096, 4096), (48, 2816, 4096),
+                                     # block ranges with two blocks per wave
+                                     (64, 256, 32000), (24, 512, 22016)])
 def test_linear(lib, dt, Mr, Kd, N):
     case(f"linear {DTN[dt]} M={Mr} Kd={Kd} N={N}")
     g = synth.rngs(Mr * 7 + Kd + N, 2)
@@ -67,7 +72,8 @@ def test_linear_epilogues(lib, dt):
     # SwiGLU on interleaved gate/up rows (small, and large enough for the
     # shared-activation kernel)
     from speculative_decoding_02_amd.decoder import interleave_gate_up
-    for FF, XX in ((F, X), (4096, _rnd(dt, g[0].standard_normal((Mr, 256), dtype=np.float32)))):
+    XW = _rnd(dt, g[0].standard_normal((Mr, 256), dtype=np.float32))
+    for FF, XX in ((F, X), (4096, XW), (11008, XW)):  # 11008: several gate/up pairs per workgroup
         HH = XX.shape[1]
         Wg = _rnd(dt, g[5].standard_normal((FF, HH), dtype=np.float32) * 0.1)
         Wu = _rnd(dt, g[5].standard_normal((FF, HH), dtype=np.float32) * 0.1)
