@@ -87,6 +87,31 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// One LDS-DMA instruction: every lane's 16 bytes at gptr land at LDS byte
+// address lds_addr + 16 * lane (lds_addr is wave-uniform, set in m0).  It is
+// issued from inline asm so that the compiler does not treat it as an LDS
+// store it must wait for before every LDS read (it would wait for all DMA in
+// flight); the kernel's own vmcnt waits and barriers order the accesses.
+// The instruction writes no register.  m0 cannot be declared as clobbered
+// (it is reserved); the kernels that use this helper contain no other m0
+// use (no indexed register moves, no m0-based LDS or message instructions),
+// which their compiled code shows.
+__device__ __forceinline__ void lds_dma16(const void* gptr, uint32_t lds_addr) {
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_addr);
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+               :
+               : "s"(m0v), "v"(gptr)
+               : "memory");
+}
+
+// s_waitcnt immediate that waits for at most n vector-memory operations in
+// flight and leaves the LDS/scalar and export counters alone (gfx9 encoding:
+// vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
+__host__ __device__ constexpr int waitcnt_vm(int n) {
+  return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8);
+}
+constexpr int WAITCNT_LGKM0 = 0xC07F;  // lgkmcnt(0) only
+
 }  // namespace medusa
 
 // ---------------------------------------------------------------------------

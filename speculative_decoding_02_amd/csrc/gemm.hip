@@ -365,25 +365,26 @@ __global__ __launch_bounds__(256) void gemm_xlds_kernel(const T* __restrict__ X,
 
 // ---------------------------------------------------------------------------
 // Variant for wide outputs (M > 16 rows, N/16 >= MEDUSA_GEMM_XB_MIN_BLOCKS):
-// G workgroups per (batch element, activation-row tile), about one per
-// compute unit, each owning a contiguous range of whole 16-row weight blocks
-// over the full contraction (pairs of blocks for SwiGLU, whose gate and up
-// rows interleave in 16-row blocks).  Every compute unit then streams nearly
-// the same number of weight bytes with no split-contraction partials.
-// Within a workgroup, wave w takes the range's blocks w and w+4 (0, 1 or 2
-// blocks: one code path per count, all with the same sequence of barriers);
-// the activation rows are shared through LDS one 256-wide chunk at a time
-// (two register sets give a two-chunk lead).  Weight loads run PF steps
-// ahead in registers, every load is unconditional (clamped) and scheduling
-// barriers fix the issue order, so the compiler's wait counts stay exact.
-// The epilogue goes through LDS, so a gate block and its up block may sit in
-// different waves and the output stores are coalesced.  Each output is one
-// wave's accumulation chain in step order: results depend on (Kd, N) only.
+// G workgroups of eight waves per (batch element, activation-row tile), about
+// one per compute unit, each owning a contiguous range of whole 16-row weight
+// blocks over the full contraction (pairs of blocks for SwiGLU, whose gate
+// and up rows interleave in 16-row blocks).  Wave w streams block w of the
+// range (waves past the range only help stage activations), so every wave
+// keeps one row block's loads in flight, PF steps ahead in registers.
+// Workgroup g starts its contraction at chunk g*nchunks/G and wraps round:
+// at any moment the compute units read different column offsets of their
+// rows (when all start at column 0 together the weight stream measured 20-35%
+// slower).  The activation rows are staged through two LDS buffers, one
+// 256-wide chunk at a time, with one barrier per chunk; every load is
+// unconditional (clamped) and scheduling barriers fix the issue order, so the
+// compiler's wait counts stay exact.  The epilogue goes through LDS, so a
+// gate block and its up block may sit in different waves and the output
+// stores are coalesced.  Each output is one wave's accumulation chain in
+// step order from the workgroup's start chunk: results depend on (Kd, N) and
+// the launch plan, itself a function of the shape.
 constexpr int XB_KC = 256;
-constexpr int XB_XSETS = 2;
-constexpr int XB_MAXB = 8;  // blocks per workgroup: 2 per wave
-constexpr int xb_gcd(int a, int b) { return b == 0 ? a : xb_gcd(b, a % b); }
-constexpr int xb_lcm(int a, int b) { return a / xb_gcd(a, b) * b; }
+constexpr int XB_WAVES = 8;
+constexpr int XB_MAXB = XB_WAVES;  // blocks per workgroup: one per wave
 
 template <typename T, int EPI>
 __device__ __forceinline__ void xb_store(int gi, int M, int Nw, int64_t xbs, const T* bias,
@@ -404,21 +405,26 @@ __device__ __forceinline__ void xb_store(int gi, int M, int Nw, int64_t xbs, con
 }
 
 template <typename T, int MB, int PF, int EPI>
-__global__ __launch_bounds__(256) void gemm_xlb_kernel(const T* __restrict__ X, int64_t xbs, int M,
-                                                       int Kd, const T* __restrict__ W, int Nw,
-                                                       const T* __restrict__ bias, const void* aux,
-                                                       void* Y, int y_f32, int G, int MT, int unit) {
+__global__ __launch_bounds__(64 * XB_WAVES) void gemm_xlb_kernel(
+    const T* __restrict__ X, int64_t xbs, int M, int Kd, const T* __restrict__ W, int Nw,
+    const T* __restrict__ bias, const void* aux, void* Y, int y_f32, int G, int MT, int unit) {
   using TR = GemmTraits<T>;
   constexpr int P16 = TR::per16;
   constexpr int KSTEP = 4 * P16;
-  constexpr int SC = XB_KC / KSTEP;            // steps per chunk
+  constexpr int SC = XB_KC / KSTEP;             // steps per chunk
+  constexpr int NT = 64 * XB_WAVES;
   constexpr int TM = 16 * MB;
-  constexpr int LDX = XB_KC + P16;             // padded LDS row (elements)
-  constexpr int XV = TM * XB_KC / P16 / 256;   // 16-byte vectors per thread per chunk
-  constexpr int GS = xb_lcm(PF, XB_XSETS * SC);  // unrolled group: whole ring and set turns
+  constexpr int LDX = XB_KC + P16;              // padded LDS row (elements)
+  constexpr int XS = TM * LDX;                  // elements per activation buffer
+  constexpr int XV = TM * XB_KC / P16 / NT;     // 16-byte vectors per thread per chunk
   constexpr int LDE = TM + 1;
-  __shared__ __attribute__((aligned(16))) T xs[TM * LDX];
-  __shared__ float ep[XB_MAXB * 16 * LDE];
+  constexpr int XSB = 2 * XS * (int)sizeof(T);
+  constexpr int EPB = XB_MAXB * 16 * LDE * 4;
+  static_assert(PF == SC, "the prologue mirrors one chunk of the loop");
+  static_assert(XV * NT * P16 == TM * XB_KC, "activation chunk must split evenly");
+  __shared__ __attribute__((aligned(16))) char smem[XSB > EPB ? XSB : EPB];
+  T* xs = reinterpret_cast<T*>(smem);
+  float* ep = reinterpret_cast<float*>(smem);  // after the contraction
 
   const int g = blockIdx.x, slice = blockIdx.y;
   const int gi = slice / MT, m0 = (slice % MT) * TM;
@@ -427,116 +433,95 @@ __global__ __launch_bounds__(256) void gemm_xlb_kernel(const T* __restrict__ X, 
   const int nunits = (Nw / 16) / unit;
   const int u0 = (int)((int64_t)g * nunits / G), u1 = (int)((int64_t)(g + 1) * nunits / G);
   const int b0 = u0 * unit, nb = (u1 - u0) * unit;  // this workgroup's blocks (<= XB_MAXB)
-  const int nw = (wave < nb ? 1 : 0) + (wave + 4 < nb ? 1 : 0);
   const int nchunks = Kd / XB_KC;
   const int nsteps = nchunks * SC;
+  const int c0 = (int)((int64_t)g * nchunks / G);  // start chunk (< nchunks)
   const T* Xg = X + (int64_t)gi * xbs;
   const T* Wg = W + (int64_t)gi * Nw * Kd;
 
-  auto run = [&](auto nbwc) {
-    constexpr int NBW = decltype(nbwc)::value;  // blocks of this wave
-    constexpr int NBA = NBW > 0 ? NBW : 1;
-    const T* wrow[NBA];
+  u32x4 xr[XV];
+  auto xload = [&](int q) {  // the q-th chunk of this workgroup's order
+    int c = c0 + min(q, nchunks - 1);
+    if (c >= nchunks) c -= nchunks;
 #pragma unroll
-    for (int j = 0; j < NBA; ++j) {
-      const int blk = min(b0 + wave + 4 * j, Nw / 16 - 1);
-      wrow[j] = Wg + (int64_t)(blk * 16 + lr) * Kd + lg * P16;
+    for (int i = 0; i < XV; ++i) {
+      const int idx = threadIdx.x + i * NT;
+      const int row = idx / (XB_KC / P16), col = idx % (XB_KC / P16);
+      const int rr = min(m0 + row, M - 1);
+      xr[i] = *reinterpret_cast<const u32x4*>(Xg + (int64_t)rr * Kd + c * XB_KC + col * P16);
     }
-    u32x4 xr[XB_XSETS][XV];
-    auto xload = [&](int set, int c) {
-      c = min(c, nchunks - 1);
+  };
+  auto xstore = [&](int buf) {
 #pragma unroll
-      for (int i = 0; i < XV; ++i) {
-        const int idx = threadIdx.x + i * 256;
-        const int row = idx / (XB_KC / P16), col = idx % (XB_KC / P16);
-        const int rr = min(m0 + row, M - 1);
-        xr[set][i] = *reinterpret_cast<const u32x4*>(Xg + (int64_t)rr * Kd + c * XB_KC + col * P16);
-      }
-    };
-    auto xstore = [&](int set, bool live) {
+    for (int i = 0; i < XV; ++i) {
+      const int idx = threadIdx.x + i * NT;
+      const int row = idx / (XB_KC / P16), col = idx % (XB_KC / P16);
+      *reinterpret_cast<u32x4*>(&xs[buf * XS + row * LDX + col * P16]) = xr[i];
+    }
+  };
+  f32x4 acc[MB];
 #pragma unroll
-      for (int i = 0; i < XV; ++i) {
-        const int idx = threadIdx.x + i * 256;
-        const int row = idx / (XB_KC / P16), col = idx % (XB_KC / P16);
-        const u32x4 z = {0u, 0u, 0u, 0u};
-        *reinterpret_cast<u32x4*>(&xs[row * LDX + col * P16]) = live ? xr[set][i] : z;
-      }
-    };
-    u32x4 fb[PF][NBA];
-    auto wload = [&](int u, int st) {
-      if constexpr (NBW > 0) {
-        const int k = min(st, nsteps - 1) * KSTEP;
-#pragma unroll
-        for (int j = 0; j < NBW; ++j) fb[u][j] = *reinterpret_cast<const u32x4*>(wrow[j] + k);
-      }
-    };
-    f32x4 acc[MB][NBA];
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-      for (int j = 0; j < NBA; ++j) acc[mb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // Prologue: the loads the loop would have issued during the GS steps
-    // before step 0, in the same order, so the loop head sees one
-    // pending-load pattern on entry and on every turn.
-#pragma unroll
-    for (int i = 0; i < GS; ++i) {
-      const int tau = i - GS;
-      if (tau % SC == 0 && tau >= -XB_XSETS * SC) {
-        const int q = tau / SC + XB_XSETS;
-        xload(q, q);
+  auto run = [&](auto activec) {
+    constexpr bool ACT = decltype(activec)::value;
+    const int blk = min(b0 + wave, Nw / 16 - 1);
+    const T* wrow = Wg + (int64_t)(blk * 16 + lr) * Kd + lg * P16;
+    u32x4 fb[PF];
+    auto wload = [&](int u, int s) {  // the s-th step of this workgroup's order
+      if constexpr (ACT) {
+        int ps = min(s, nsteps - 1) + c0 * SC;
+        if (ps >= nsteps) ps -= nsteps;
+        fb[u] = *reinterpret_cast<const u32x4*>(wrow + (int64_t)ps * KSTEP);
       }
-      if (tau >= -PF) wload(tau + PF, tau + PF);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    // Whole groups only; chunks past the end store zeros, adding nothing.
-    for (int s0 = 0; s0 < nsteps; s0 += GS) {
+    };
+    // Prologue: chunk 0 into buffer 0, then the loads one loop turn issues
+    // (next chunk's activations, then PF weight steps), so the loop head sees
+    // one pending-load pattern on entry and on every turn.
+    xload(0);
+    xstore(0);
+    xload(1);
 #pragma unroll
-      for (int sl = 0; sl < GS; ++sl) {
-        if (sl % SC == 0) {
-          const int q = (s0 + sl) / SC;
-          const int set = (sl / SC) % XB_XSETS;
-          __syncthreads();  // everyone is done reading the previous chunk
-          xstore(set, q < nchunks);
-          __syncthreads();
-          xload(set, q + XB_XSETS);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        if constexpr (NBW > 0) {
-          const int u = sl % PF, kk = sl % SC;
+    for (int u = 0; u < PF; ++u) wload(u, u);
+    __builtin_amdgcn_sched_barrier(0);
+    for (int q = 0; q < nchunks; ++q) {
+      __syncthreads();  // chunk q is in buffer q&1; no one still reads chunk q-1
+      xstore((q + 1) & 1);  // chunk q+1 (after the last chunk: a store nobody reads)
+      xload(q + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (ACT) {
+        const T* xb = xs + (q & 1) * XS;
+#pragma unroll
+        for (int sl = 0; sl < SC; ++sl) {
           u32x4 xa[MB];
 #pragma unroll
           for (int mb = 0; mb < MB; ++mb)
-            xa[mb] = *reinterpret_cast<const u32x4*>(&xs[(mb * 16 + lr) * LDX + kk * KSTEP + lg * P16]);
+            xa[mb] = *reinterpret_cast<const u32x4*>(&xb[(mb * 16 + lr) * LDX + sl * KSTEP + lg * P16]);
 #pragma unroll
-          for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-            for (int j = 0; j < NBW; ++j) acc[mb][j] = TR::mma(xa[mb], fb[u][j], acc[mb][j]);
-          wload(u, s0 + sl + PF);
+          for (int mb = 0; mb < MB; ++mb) acc[mb] = TR::mma(xa[mb], fb[sl], acc[mb]);
+          wload(sl, q * SC + sl + PF);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
     }
-    // lane holds weight row lr of local block wave + 4j, activation rows
-    // mb*16 + 4*lg + r
-#pragma unroll
-    for (int j = 0; j < NBW; ++j)
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          ep[((wave + 4 * j) * 16 + lr) * LDE + mb * 16 + lg * 4 + r] = acc[mb][j][r];
   };
-  if (nw == 2) run(std::integral_constant<int, 2>());
-  else if (nw == 1) run(std::integral_constant<int, 1>());
-  else run(std::integral_constant<int, 0>());
+  if (wave < nb) run(std::true_type());
+  else run(std::false_type());
+  __syncthreads();  // the activation buffers become the epilogue tile
+  // lane holds weight row lr of local block `wave`, activation rows mb*16 + 4*lg + r
+  if (wave < nb) {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) ep[(wave * 16 + lr) * LDE + mb * 16 + lg * 4 + r] = acc[mb][r];
+  }
   __syncthreads();
 
   if (EPI == MEDUSA_EPI_SWIGLU) {
     // local blocks 2p (gate) and 2p+1 (up); b0 is even
     const int F = Nw / 2, f0 = b0 / 2 * 16, nf = nb / 2 * 16;
     T* Yg = reinterpret_cast<T*>(Y) + (int64_t)gi * M * F;
-    for (int e = threadIdx.x; e < nf * TM; e += 256) {
+    for (int e = threadIdx.x; e < nf * TM; e += NT) {
       const int m = e / nf, fl = e % nf;
       const int gr = (fl / 16) * 32 + fl % 16;  // gate row in the range; up is 16 further
       if (m0 + m < M) st<T>(Yg, (int64_t)(m0 + m) * F + f0 + fl, silu_f(ep[gr * LDE + m]) * ep[(gr + 16) * LDE + m]);
@@ -544,7 +529,159 @@ __global__ __launch_bounds__(256) void gemm_xlb_kernel(const T* __restrict__ X, 
     return;
   }
   const int nn = nb * 16;
-  for (int e = threadIdx.x; e < nn * TM; e += 256) {
+  for (int e = threadIdx.x; e < nn * TM; e += NT) {
+    const int m = e / nn, nl = e % nn;
+    if (m0 + m < M) xb_store<T, EPI>(gi, M, Nw, xbs, bias, aux, Y, y_f32, m0 + m, b0 * 16 + nl, ep[nl * LDE + m]);
+  }
+}
+
+// The same block-range plan with every operand brought in by LDS DMA (bf16).
+// A register load of a weight step reads 64 bytes of each of 16 rows (the
+// MFMA operand layout); here one DMA instruction reads 256 contiguous bytes
+// of each of 4 rows (two whole 128-byte lines per row) into a per-wave LDS
+// ring, and the MFMA operands are read back from LDS.  The activation chunk
+// comes in by DMA too (no registers, no LDS store instructions), double
+// buffered with one barrier per chunk.  Nothing is loaded into registers from
+// global memory in the loop, so every wait is an explicit vmcnt immediate
+// counted from the fixed issue order:
+//   chunk head:  [wait: own DMA of chunk q landed] barrier, DMA chunk q+1
+//   group g (4 steps, 2 per chunk): [wait: group g landed] 4 steps of MFMA,
+//                lgkmcnt(0), DMA group g+2 into the slot just read
+// In LDS both operands are XOR-swizzled in 16-byte units (slot ^ row) so
+// that the 16 rows of one operand read fall in distinct banks; the swizzle is
+// applied on the global side, since a DMA lane's LDS address is fixed.
+constexpr int XD_WR = 2;  // weight groups in flight per wave (4 steps, 4 KB each)
+
+template <int MB, int EPI>
+__global__ __launch_bounds__(64 * XB_WAVES) void gemm_xdma_kernel(
+    const bf16_t* __restrict__ X, int64_t xbs, int M, int Kd, const bf16_t* __restrict__ W, int Nw,
+    const bf16_t* __restrict__ bias, const void* aux, void* Y, int y_f32, int G, int MT, int unit) {
+  using T = bf16_t;
+  constexpr int P16 = 8;                        // bf16 per 16 bytes
+  constexpr int TM = 16 * MB;
+  constexpr int XROWB = XB_KC * 2;              // bytes of one activation row per chunk
+  constexpr int XBUFB = TM * XROWB;
+  constexpr int XD = XBUFB / 1024 / XB_WAVES;   // activation DMAs per wave per chunk
+  constexpr int WGB = 16 * 256;                 // one weight group: 16 rows x 256 bytes
+  constexpr int WSLOTB = XD_WR * WGB;
+  constexpr int LDE = TM + 1;
+  constexpr int SMEM = 2 * XBUFB + XB_WAVES * WSLOTB;
+  static_assert(XD >= 1 && XD * XB_WAVES * 1024 == XBUFB, "activation chunk must split into whole DMAs");
+  static_assert(XB_MAXB * 16 * LDE * 4 <= SMEM, "epilogue tile must fit");
+  constexpr int WAIT_CHUNK = waitcnt_vm(2 * 4);   // two weight groups follow a chunk's DMA
+  constexpr int WAIT_GROUP = waitcnt_vm(4 + XD);  // a group, then a chunk, follow a group
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[SMEM];
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem;
+  float* ep = reinterpret_cast<float*>(smem);  // after the contraction
+
+  const int g = blockIdx.x, slice = blockIdx.y;
+  const int gi = slice / MT, m0 = (slice % MT) * TM;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int lr = lane & 15, lg = lane >> 4;
+  const int nunits = (Nw / 16) / unit;
+  const int u0 = (int)((int64_t)g * nunits / G), u1 = (int)((int64_t)(g + 1) * nunits / G);
+  const int b0 = u0 * unit, nb = (u1 - u0) * unit;  // this workgroup's blocks (<= XB_MAXB)
+  const int nchunks = Kd / XB_KC;
+  const int ngroups = 2 * nchunks;
+  const int c0 = (int)((int64_t)g * nchunks / G);  // start chunk (< nchunks)
+  const T* Xg = X + (int64_t)gi * xbs;
+  const T* Wg = W + (int64_t)gi * Nw * Kd;
+
+  // chunk q of this workgroup's order -> buffer q&1; DMA j covers rows 2j, 2j+1
+  auto xissue = [&](int q) {
+    int c = c0 + min(q, nchunks - 1);
+    if (c >= nchunks) c -= nchunks;
+    const uint32_t base = lds0 + (q & 1) * XBUFB;
+#pragma unroll
+    for (int i = 0; i < XD; ++i) {
+      const int j = wave * XD + i;
+      const int row = 2 * j + (lane >> 5), slot = lane & 31;
+      const int rr = min(m0 + row, M - 1);
+      lds_dma16(Xg + (int64_t)rr * Kd + c * XB_KC + (slot ^ (row & 15)) * P16, base + j * 1024);
+    }
+  };
+  f32x4 acc[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto run = [&](auto activec) {
+    constexpr bool ACT = decltype(activec)::value;
+    const T* wblk = Wg + (int64_t)min(b0 + wave, Nw / 16 - 1) * 16 * Kd;
+    const uint32_t wring = lds0 + 2 * XBUFB + wave * WSLOTB;
+    // weight group gq of this workgroup's order -> ring slot gq % XD_WR;
+    // DMA qq covers rows 4qq..4qq+3, 256 bytes each
+    auto wissue = [&](int gq) {
+      int pg = c0 * 2 + min(gq, ngroups - 1);
+      if (pg >= ngroups) pg -= ngroups;
+      const uint32_t base = wring + (gq % XD_WR) * WGB;
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) {
+        const int row = 4 * qq + (lane >> 4), slot = lane & 15;
+        lds_dma16(wblk + (int64_t)row * Kd + pg * 128 + (slot ^ row) * P16, base + qq * 1024);
+      }
+    };
+    xissue(0);
+    if constexpr (ACT) {
+      wissue(0);
+      wissue(1);
+    }
+    for (int q = 0; q < nchunks; ++q) {
+      __builtin_amdgcn_s_waitcnt(ACT ? WAIT_CHUNK : waitcnt_vm(0));  // own DMA of chunk q landed
+      __builtin_amdgcn_s_barrier();  // every wave's, and chunk q-1 is no longer read
+      asm volatile("" ::: "memory");
+      xissue(q + 1);  // after the last chunk: a clamped copy nobody reads
+      if constexpr (ACT) {
+        const unsigned char* xb = smem + (q & 1) * XBUFB;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int gq = 2 * q + h;
+          __builtin_amdgcn_s_waitcnt(WAIT_GROUP);  // group gq landed
+          asm volatile("" ::: "memory");
+          const unsigned char* wb = smem + 2 * XBUFB + wave * WSLOTB + (gq % XD_WR) * WGB;
+#pragma unroll
+          for (int sl = 0; sl < 4; ++sl) {
+            const u32x4 bw = *reinterpret_cast<const u32x4*>(wb + lr * 256 + (((sl * 4 + lg) ^ lr) * 16));
+            u32x4 xa[MB];
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+              xa[mb] = *reinterpret_cast<const u32x4*>(
+                  xb + (mb * 16 + lr) * XROWB + ((((h * 4 + sl) * 4 + lg) ^ lr) * 16));
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) acc[mb] = mfma_bf16_16x16x32(xa[mb], bw, acc[mb]);
+          }
+          asm volatile("" ::: "memory");
+          __builtin_amdgcn_s_waitcnt(WAITCNT_LGKM0);  // this slot's LDS reads are done
+          asm volatile("" ::: "memory");
+          wissue(gq + XD_WR);
+        }
+      }
+    }
+  };
+  if (wave < nb) run(std::true_type());
+  else run(std::false_type());
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // the clamped refills
+  __syncthreads();  // the operand buffers become the epilogue tile
+  if (wave < nb) {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) ep[(wave * 16 + lr) * LDE + mb * 16 + lg * 4 + r] = acc[mb][r];
+  }
+  __syncthreads();
+
+  constexpr int NT = 64 * XB_WAVES;
+  if (EPI == MEDUSA_EPI_SWIGLU) {
+    const int F = Nw / 2, f0 = b0 / 2 * 16, nf = nb / 2 * 16;
+    T* Yg = reinterpret_cast<T*>(Y) + (int64_t)gi * M * F;
+    for (int e = threadIdx.x; e < nf * TM; e += NT) {
+      const int m = e / nf, fl = e % nf;
+      const int gr = (fl / 16) * 32 + fl % 16;  // gate row in the range; up is 16 further
+      if (m0 + m < M) st<T>(Yg, (int64_t)(m0 + m) * F + f0 + fl, silu_f(ep[gr * LDE + m]) * ep[(gr + 16) * LDE + m]);
+    }
+    return;
+  }
+  const int nn = nb * 16;
+  for (int e = threadIdx.x; e < nn * TM; e += NT) {
     const int m = e / nn, nl = e % nn;
     if (m0 + m < M) xb_store<T, EPI>(gi, M, Nw, xbs, bias, aux, Y, y_f32, m0 + m, b0 * 16 + nl, ep[nl * LDE + m]);
   }
@@ -604,6 +741,10 @@ __global__ __launch_bounds__(256) void gemm_split_reduce_kernel(const float* __r
 #endif
 #ifndef MEDUSA_GEMM_XB_PF
 #define MEDUSA_GEMM_XB_PF 8
+#endif
+// block-range projections through LDS DMA (1) or register loads (0)
+#ifndef MEDUSA_GEMM_XB_DMA
+#define MEDUSA_GEMM_XB_DMA 1
 #endif
 #ifndef MEDUSA_GEMM_XL_TARGET_WGS
 #define MEDUSA_GEMM_XL_TARGET_WGS 384
@@ -687,16 +828,23 @@ static void launch_gemm_t(const void* X, int64_t xbs, int64_t M, int64_t Kd, con
   if constexpr (sizeof(T) == 2) {  // planned for bf16 only
     if (plan.xb) {
       const dim3 grid((unsigned)plan.xb_G, (unsigned)(batch * plan.MT));
-      if (M <= 32)
-        hipLaunchKernelGGL((gemm_xlb_kernel<T, 2, MEDUSA_GEMM_XB_PF, EPI>), grid, dim3(256), 0, st,
-                           reinterpret_cast<const T*>(X), xbs, (int)M, (int)Kd,
-                           reinterpret_cast<const T*>(W), (int)Nw, reinterpret_cast<const T*>(bias),
-                           aux, Y, y_f32, plan.xb_G, plan.MT, plan.xb_unit);
-      else
-        hipLaunchKernelGGL((gemm_xlb_kernel<T, 4, MEDUSA_GEMM_XB_PF, EPI>), grid, dim3(256), 0, st,
-                           reinterpret_cast<const T*>(X), xbs, (int)M, (int)Kd,
-                           reinterpret_cast<const T*>(W), (int)Nw, reinterpret_cast<const T*>(bias),
-                           aux, Y, y_f32, plan.xb_G, plan.MT, plan.xb_unit);
+      const T* Xt = reinterpret_cast<const T*>(X);
+      const T* Wt = reinterpret_cast<const T*>(W);
+      const T* Bt = reinterpret_cast<const T*>(bias);
+      if (MEDUSA_GEMM_XB_DMA) {
+        if (M <= 32)
+          hipLaunchKernelGGL((gemm_xdma_kernel<2, EPI>), grid, dim3(64 * XB_WAVES), 0, st, Xt, xbs,
+                             (int)M, (int)Kd, Wt, (int)Nw, Bt, aux, Y, y_f32, plan.xb_G, plan.MT, plan.xb_unit);
+        else
+          hipLaunchKernelGGL((gemm_xdma_kernel<4, EPI>), grid, dim3(64 * XB_WAVES), 0, st, Xt, xbs,
+                             (int)M, (int)Kd, Wt, (int)Nw, Bt, aux, Y, y_f32, plan.xb_G, plan.MT, plan.xb_unit);
+      } else if (M <= 32) {
+        hipLaunchKernelGGL((gemm_xlb_kernel<T, 2, MEDUSA_GEMM_XB_PF, EPI>), grid, dim3(64 * XB_WAVES), 0, st,
+                           Xt, xbs, (int)M, (int)Kd, Wt, (int)Nw, Bt, aux, Y, y_f32, plan.xb_G, plan.MT, plan.xb_unit);
+      } else {
+        hipLaunchKernelGGL((gemm_xlb_kernel<T, 4, MEDUSA_GEMM_XB_PF, EPI>), grid, dim3(64 * XB_WAVES), 0, st,
+                           Xt, xbs, (int)M, (int)Kd, Wt, (int)Nw, Bt, aux, Y, y_f32, plan.xb_G, plan.MT, plan.xb_unit);
+      }
       return;
     }
   }

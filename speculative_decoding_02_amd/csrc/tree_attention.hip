@@ -397,23 +397,6 @@ __global__ __launch_bounds__(ATT_THREADS) void tree_attention_kernel(AttnArgs a)
 //   * Waits are explicit: s_barrier without a fence (a fenced barrier would
 //     wait for every DMA in flight) after waiting until only the later
 //     tiles' (R-1) x OPS DMA loads are outstanding.
-// One LDS-DMA instruction: every lane's 16 bytes at gptr land at LDS byte
-// address lds_addr + 16 * lane (lds_addr is wave-uniform, set in m0).  It is
-// issued from inline asm so that the compiler does not treat it as an LDS
-// store it must wait for before every LDS read (it would wait for all DMA in
-// flight); the kernel's own vmcnt waits and barriers order the accesses.
-// The instruction writes no register.  m0 cannot be declared as clobbered
-// (it is reserved); the kernels that use this helper contain no other m0
-// use (no indexed register moves, no m0-based LDS or message instructions),
-// which the compiled code of this file shows.
-__device__ __forceinline__ void lds_dma16(const void* gptr, uint32_t lds_addr) {
-  const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_addr);
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
-               :
-               : "s"(m0v), "v"(gptr)
-               : "memory");
-}
-
 template <int D, int R>
 __global__ __launch_bounds__(ATT_THREADS) void tree_attention_dma_kernel(AttnArgs a) {
   using T = bf16_t;
@@ -430,7 +413,7 @@ __global__ __launch_bounds__(ATT_THREADS) void tree_attention_dma_kernel(AttnArg
   constexpr int DB = D / 16;
   constexpr int WAITN = (R - 1) * OPS;         // DMA ops allowed in flight at a tile start
   static_assert(WAITN < 64, "vmcnt range");
-  constexpr int WAIT_IMM = (WAITN & 15) | ((WAITN >> 4) << 14) | (7 << 4) | (15 << 8);
+  constexpr int WAIT_IMM = waitcnt_vm(WAITN);
   __shared__ __attribute__((aligned(1024))) unsigned char lds[R * SLOTB];
   __shared__ int spages[ATT_MAX_SPLIT_PAGES];
 
@@ -578,7 +561,7 @@ __global__ __launch_bounds__(ATT_THREADS) void tree_attention_dma_kernel(AttnArg
       }
     }
     asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt(0xC07F);    // lgkmcnt(0): this wave's LDS reads are done
+    __builtin_amdgcn_s_waitcnt(WAITCNT_LGKM0);  // this wave's LDS reads are done
     __builtin_amdgcn_s_barrier();          // ... so the slot can be refilled
     asm volatile("" ::: "memory");
     issue(t + R, slot);
