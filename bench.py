@@ -351,7 +351,7 @@ def main():
         "verified_tree_tokens_per_s": round(64 * args.steps / (t1 - t0), 1),
         "plain_decode_tokens_per_s": plain,
         "typical": typical,
-        "roofline": {"bound": "hbm", "kernel": "gemm_xlb_kernel (gate/up projection, SwiGLU epilogue)",
+        "roofline": {"bound": "hbm", "kernel": "gemm_xdma_kernel (gate/up projection, SwiGLU epilogue)",
                      "achieved": round(gu_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gu_gbs / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic("gate_up_projection", "gemm.hip"),

@@ -248,6 +248,19 @@ int32_t medusa_embed(const int32_t* tokens, int64_t M, const void* table, int64_
 int32_t medusa_rmsnorm(const float* x, int64_t M, int64_t H, const void* gain, float eps,
                        int32_t dt, void* out, void* stream);
 
+/* The residual projection of a pre-norm block followed by the next block's
+ * RMSNorm: x [M, N] float (16-byte aligned, updated in place) += X W^T with
+ * X [M, Kd] and W [N, Kd] (dt), then out [M, N] (dt) = RMSNorm(x) * gain
+ * (gain [N] dt or NULL for 1; N a multiple of 4, N <= 8192).  The results
+ * equal, bit for bit, medusa_linear(X, W, MEDUSA_EPI_RES_ADD_F32, aux = Y = x)
+ * followed by medusa_rmsnorm(x, gain, eps, out): where the projection splits
+ * its contraction, the split sum, the residual add and the norm run in one
+ * pass per row instead of two launches.  out must not alias x, X or W.
+ * ws: medusa_linear_ws(M, Kd, N, 1, dt) bytes (NULL when that is 0). */
+int32_t medusa_linear_rmsnorm(const void* X, int64_t M, int64_t Kd, const void* W, int64_t N,
+                              int32_t dt, float* x, const void* gain, float eps, void* out,
+                              void* ws, size_t ws_bytes, void* stream);
+
 /* Split qkv [M, (Hq + 2 Hkv) * D] (dt) into q [M, Hq, D], k [M, Hkv, D],
  * v [M, Hkv, D] and rotate q and k by position pos[m] (rotate-half pairs
  * (j, j + D/2), angle pos * base^(-2j/D)). */

@@ -20,7 +20,6 @@ __global__ __launch_bounds__(256) void embed_kernel(const int* __restrict__ toke
 // costs one memory round trip; the sum of squares is reduced in a fixed order
 // (per-thread, then a butterfly per wave, then the 4 waves in order) and the
 // normalised values are written from registers.
-constexpr int RMS_V4 = 8;
 template <typename T>
 __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ x, int64_t M,
                                                       int64_t H, const T* __restrict__ gain,
@@ -34,28 +33,8 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ 
     const int64_t e = threadIdx.x + (int64_t)i * 256;
     v[i] = reinterpret_cast<const f32x4*>(xr)[e < H4 ? e : 0];
   }
-  float ss = 0.f;
-#pragma unroll
-  for (int i = 0; i < RMS_V4; ++i)
-    if (threadIdx.x + (int64_t)i * 256 < H4)
-      ss += v[i].x * v[i].x + v[i].y * v[i].y + v[i].z * v[i].z + v[i].w * v[i].w;
-  ss = wave_sum(ss);
-  __shared__ float part[4];
-  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
-  __syncthreads();
-  const float tot = (part[0] + part[1]) + (part[2] + part[3]);
-  const float rs = 1.0f / sqrtf(tot / (float)H + eps);
-  T* orow = out + m * H;
-#pragma unroll
-  for (int i = 0; i < RMS_V4; ++i) {
-    const int64_t e = threadIdx.x + (int64_t)i * 256;
-    if (e < H4)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float g = gain ? ld<T>(gain, e * 4 + r) : 1.f;
-        st<T>(orow, e * 4 + r, v[i][r] * rs * g);
-      }
-  }
+  const float rs = rms_row_scale(v, H, eps);
+  rms_row_store<T>(v, H, rs, gain, out + m * H);
 }
 
 // Rotary positions, rotate-half pairs (j, j + D/2), angle pos * base^(-2j/D).

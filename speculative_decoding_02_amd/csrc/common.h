@@ -87,6 +87,43 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// One 256-thread workgroup normalises one row of H floats held as up to
+// RMS_V4 f32x4 per thread (vector e = threadIdx.x + 256 i, e < H/4): the
+// row's sum of squares in a fixed order (per thread, then per wave, then the
+// four waves in pairs) and the scale 1/sqrt(mean + eps).  Both the plain
+// RMSNorm and the one fused behind a split projection use it, so their
+// results agree bit for bit.
+constexpr int RMS_V4 = 8;  // H <= 4 * 256 * RMS_V4
+__device__ __forceinline__ float rms_row_scale(const f32x4 (&v)[RMS_V4], int64_t H, float eps) {
+  const int64_t H4 = H / 4;
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < RMS_V4; ++i)
+    if (threadIdx.x + (int64_t)i * 256 < H4)
+      ss += v[i].x * v[i].x + v[i].y * v[i].y + v[i].z * v[i].z + v[i].w * v[i].w;
+  ss = wave_sum(ss);
+  __shared__ float rms_part[4];
+  if ((threadIdx.x & 63) == 0) rms_part[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  const float tot = (rms_part[0] + rms_part[1]) + (rms_part[2] + rms_part[3]);
+  return 1.0f / sqrtf(tot / (float)H + eps);
+}
+template <typename T>
+__device__ __forceinline__ void rms_row_store(const f32x4 (&v)[RMS_V4], int64_t H, float rs,
+                                              const T* __restrict__ gain, T* __restrict__ orow) {
+  const int64_t H4 = H / 4;
+#pragma unroll
+  for (int i = 0; i < RMS_V4; ++i) {
+    const int64_t e = threadIdx.x + (int64_t)i * 256;
+    if (e < H4)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float g = gain ? ld<T>(gain, e * 4 + r) : 1.f;
+        st<T>(orow, e * 4 + r, v[i][r] * rs * g);
+      }
+  }
+}
+
 // One LDS-DMA instruction: every lane's 16 bytes at gptr land at LDS byte
 // address lds_addr + 16 * lane (lds_addr is wave-uniform, set in m0).  It is
 // issued from inline asm so that the compiler does not treat it as an LDS

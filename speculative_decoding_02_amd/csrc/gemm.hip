@@ -550,12 +550,15 @@ __global__ __launch_bounds__(64 * XB_WAVES) void gemm_xlb_kernel(
 // In LDS both operands are XOR-swizzled in 16-byte units (slot ^ row) so
 // that the 16 rows of one operand read fall in distinct banks; the swizzle is
 // applied on the global side, since a DMA lane's LDS address is fixed.
-constexpr int XD_WR = 2;  // weight groups in flight per wave (4 steps, 4 KB each)
+#ifndef MEDUSA_GEMM_XD_WR
+#define MEDUSA_GEMM_XD_WR 2  // weight groups in flight per wave (4 steps, 4 KB each)
+#endif
 
-template <int MB, int EPI>
+template <int MB, int WR, int EPI>
 __global__ __launch_bounds__(64 * XB_WAVES) void gemm_xdma_kernel(
     const bf16_t* __restrict__ X, int64_t xbs, int M, int Kd, const bf16_t* __restrict__ W, int Nw,
-    const bf16_t* __restrict__ bias, const void* aux, void* Y, int y_f32, int G, int MT, int unit) {
+    const bf16_t* __restrict__ bias, const void* aux, void* Y, int y_f32, int G, int MT, int unit,
+    float* __restrict__ part) {
   using T = bf16_t;
   constexpr int P16 = 8;                        // bf16 per 16 bytes
   constexpr int TM = 16 * MB;
@@ -563,13 +566,18 @@ __global__ __launch_bounds__(64 * XB_WAVES) void gemm_xdma_kernel(
   constexpr int XBUFB = TM * XROWB;
   constexpr int XD = XBUFB / 1024 / XB_WAVES;   // activation DMAs per wave per chunk
   constexpr int WGB = 16 * 256;                 // one weight group: 16 rows x 256 bytes
-  constexpr int WSLOTB = XD_WR * WGB;
+  constexpr int WSLOTB = WR * WGB;
   constexpr int LDE = TM + 1;
   constexpr int SMEM = 2 * XBUFB + XB_WAVES * WSLOTB;
   static_assert(XD >= 1 && XD * XB_WAVES * 1024 == XBUFB, "activation chunk must split into whole DMAs");
   static_assert(XB_MAXB * 16 * LDE * 4 <= SMEM, "epilogue tile must fit");
-  constexpr int WAIT_CHUNK = waitcnt_vm(2 * 4);   // two weight groups follow a chunk's DMA
-  constexpr int WAIT_GROUP = waitcnt_vm(4 + XD);  // a group, then a chunk, follow a group
+  static_assert(WR == 2 || WR == 3, "wait counts are worked out for rings of 2 and 3 groups");
+  // Issue order per wave: prologue W(0) [.. W(WR-3)], X(0), W(WR-2), W(WR-1);
+  // then per chunk q: X(q+1), group 2q, W(2q+WR), group 2q+1, W(2q+1+WR).
+  // DMAs issued after the one awaited (4 per weight group, XD per chunk):
+  constexpr int WAIT_CHUNK = waitcnt_vm(2 * 4);  // X(q): W(2q+WR-2), W(2q+WR-1)
+  constexpr int WAIT_G0 = waitcnt_vm(WR == 2 ? 4 + XD : 8 + 2 * XD);  // W(2q): ..., X(q+1)
+  constexpr int WAIT_G1 = waitcnt_vm(WR == 2 ? 4 + XD : 8 + XD);      // W(2q+1): ..., W(2q+WR)
   __shared__ __attribute__((aligned(1024))) unsigned char smem[SMEM];
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem;
   float* ep = reinterpret_cast<float*>(smem);  // after the contraction
@@ -581,9 +589,12 @@ __global__ __launch_bounds__(64 * XB_WAVES) void gemm_xdma_kernel(
   const int nunits = (Nw / 16) / unit;
   const int u0 = (int)((int64_t)g * nunits / G), u1 = (int)((int64_t)(g + 1) * nunits / G);
   const int b0 = u0 * unit, nb = (u1 - u0) * unit;  // this workgroup's blocks (<= XB_MAXB)
-  const int nchunks = Kd / XB_KC;
+  // contraction split sp of S: chunks [cb, cb + nchunks)
+  const int sp = blockIdx.z, S = gridDim.z;
+  const int cb = (int)((int64_t)sp * (Kd / XB_KC) / S);
+  const int nchunks = (int)((int64_t)(sp + 1) * (Kd / XB_KC) / S) - cb;
   const int ngroups = 2 * nchunks;
-  const int c0 = (int)((int64_t)g * nchunks / G);  // start chunk (< nchunks)
+  const int c0 = (int)((int64_t)g * nchunks / G);  // start chunk within the split (< nchunks)
   const T* Xg = X + (int64_t)gi * xbs;
   const T* Wg = W + (int64_t)gi * Nw * Kd;
 
@@ -591,6 +602,7 @@ __global__ __launch_bounds__(64 * XB_WAVES) void gemm_xdma_kernel(
   auto xissue = [&](int q) {
     int c = c0 + min(q, nchunks - 1);
     if (c >= nchunks) c -= nchunks;
+    c += cb;
     const uint32_t base = lds0 + (q & 1) * XBUFB;
 #pragma unroll
     for (int i = 0; i < XD; ++i) {
@@ -608,22 +620,24 @@ __global__ __launch_bounds__(64 * XB_WAVES) void gemm_xdma_kernel(
     constexpr bool ACT = decltype(activec)::value;
     const T* wblk = Wg + (int64_t)min(b0 + wave, Nw / 16 - 1) * 16 * Kd;
     const uint32_t wring = lds0 + 2 * XBUFB + wave * WSLOTB;
-    // weight group gq of this workgroup's order -> ring slot gq % XD_WR;
+    // weight group gq of this workgroup's order -> ring slot gq % WR;
     // DMA qq covers rows 4qq..4qq+3, 256 bytes each
     auto wissue = [&](int gq) {
       int pg = c0 * 2 + min(gq, ngroups - 1);
       if (pg >= ngroups) pg -= ngroups;
-      const uint32_t base = wring + (gq % XD_WR) * WGB;
+      pg += 2 * cb;
+      const uint32_t base = wring + (gq % WR) * WGB;
 #pragma unroll
       for (int qq = 0; qq < 4; ++qq) {
         const int row = 4 * qq + (lane >> 4), slot = lane & 15;
         lds_dma16(wblk + (int64_t)row * Kd + pg * 128 + (slot ^ row) * P16, base + qq * 1024);
       }
     };
+    if constexpr (ACT && WR == 3) wissue(0);
     xissue(0);
     if constexpr (ACT) {
-      wissue(0);
-      wissue(1);
+      wissue(WR - 2);
+      wissue(WR - 1);
     }
     for (int q = 0; q < nchunks; ++q) {
       __builtin_amdgcn_s_waitcnt(ACT ? WAIT_CHUNK : waitcnt_vm(0));  // own DMA of chunk q landed
@@ -632,12 +646,12 @@ __global__ __launch_bounds__(64 * XB_WAVES) void gemm_xdma_kernel(
       xissue(q + 1);  // after the last chunk: a clamped copy nobody reads
       if constexpr (ACT) {
         const unsigned char* xb = smem + (q & 1) * XBUFB;
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
+        auto group = [&](auto hc) {
+          constexpr int h = decltype(hc)::value;
           const int gq = 2 * q + h;
-          __builtin_amdgcn_s_waitcnt(WAIT_GROUP);  // group gq landed
+          __builtin_amdgcn_s_waitcnt(h == 0 ? WAIT_G0 : WAIT_G1);  // group gq landed
           asm volatile("" ::: "memory");
-          const unsigned char* wb = smem + 2 * XBUFB + wave * WSLOTB + (gq % XD_WR) * WGB;
+          const unsigned char* wb = smem + 2 * XBUFB + wave * WSLOTB + (gq % WR) * WGB;
 #pragma unroll
           for (int sl = 0; sl < 4; ++sl) {
             const u32x4 bw = *reinterpret_cast<const u32x4*>(wb + lr * 256 + (((sl * 4 + lg) ^ lr) * 16));
@@ -652,8 +666,10 @@ __global__ __launch_bounds__(64 * XB_WAVES) void gemm_xdma_kernel(
           asm volatile("" ::: "memory");
           __builtin_amdgcn_s_waitcnt(WAITCNT_LGKM0);  // this slot's LDS reads are done
           asm volatile("" ::: "memory");
-          wissue(gq + XD_WR);
-        }
+          wissue(gq + WR);
+        };
+        group(std::integral_constant<int, 0>());
+        group(std::integral_constant<int, 1>());
       }
     }
   };
@@ -670,6 +686,15 @@ __global__ __launch_bounds__(64 * XB_WAVES) void gemm_xdma_kernel(
   __syncthreads();
 
   constexpr int NT = 64 * XB_WAVES;
+  if (S > 1) {  // fp32 partials [batch][S][M][N]; the split reducer applies the epilogue
+    const int nn = nb * 16;
+    float* pp = part + ((int64_t)gi * S + sp) * M * Nw;
+    for (int e = threadIdx.x; e < nn * TM; e += NT) {
+      const int m = e / nn, nl = e % nn;
+      if (m0 + m < M) pp[(int64_t)(m0 + m) * Nw + b0 * 16 + nl] = ep[nl * LDE + m];
+    }
+    return;
+  }
   if (EPI == MEDUSA_EPI_SWIGLU) {
     const int F = Nw / 2, f0 = b0 / 2 * 16, nf = nb / 2 * 16;
     T* Yg = reinterpret_cast<T*>(Y) + (int64_t)gi * M * F;
@@ -736,6 +761,37 @@ __global__ __launch_bounds__(256) void gemm_split_reduce_kernel(const float* __r
   }
 }
 
+// Split sum + residual add + RMSNorm, one workgroup per row (N <= 8192):
+// x[m] += sum of the partials in split order (the same sums and the same
+// final add as gemm_split_reduce_kernel's residual epilogue), then
+// out[m] = RMSNorm(x[m]) * gain with the plain RMSNorm's own reduction.
+template <typename T>
+__global__ __launch_bounds__(256) void split_reduce_rmsnorm_kernel(const float* __restrict__ part,
+                                                                   int ksplit, int M, int N,
+                                                                   float* __restrict__ x,
+                                                                   const T* __restrict__ gain,
+                                                                   float eps, T* __restrict__ out) {
+  const int m = blockIdx.x;
+  const int N4 = N / 4;
+  f32x4* xr = reinterpret_cast<f32x4*>(x + (int64_t)m * N);
+  const f32x4* p0 = reinterpret_cast<const f32x4*>(part + (int64_t)m * N);
+  const int64_t pstride = (int64_t)M * N4;  // one split's partials, in f32x4
+  f32x4 v[RMS_V4];
+#pragma unroll
+  for (int i = 0; i < RMS_V4; ++i) {
+    const int e = threadIdx.x + i * 256;
+    v[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (e < N4) {
+      f32x4 acc = p0[e];
+      for (int q = 1; q < ksplit; ++q) acc += p0[q * pstride + e];
+      v[i] = xr[e] + acc;
+      xr[e] = v[i];
+    }
+  }
+  const float rs = rms_row_scale(v, N, eps);
+  rms_row_store<T>(v, N, rs, gain, out + (int64_t)m * N);
+}
+
 #ifndef MEDUSA_GEMM_XL_NB
 #define MEDUSA_GEMM_XL_NB 2
 #endif
@@ -763,8 +819,9 @@ struct GemmPlan {
   int ksplit;
   bool xb;      // block-range variant
   int xb_unit;  // blocks per unit (2: SwiGLU gate/up pairs)
-  int xb_G;     // workgroups per (batch element, row tile)
+  int xb_G;     // workgroups per (batch element, row tile, contraction split)
   int MT;       // activation-row tiles
+  int xb_S;     // contraction splits of the block-range variant (partials when > 1)
 };
 #ifndef MEDUSA_GEMM_XB_MIN_BLOCKS
 #define MEDUSA_GEMM_XB_MIN_BLOCKS 512
@@ -772,18 +829,29 @@ struct GemmPlan {
 #ifndef MEDUSA_GEMM_XB_WGS
 #define MEDUSA_GEMM_XB_WGS 256
 #endif
+// narrower outputs (MEDUSA_GEMM_XD_MIN_BLOCKS <= N/16 < MEDUSA_GEMM_XB_MIN_BLOCKS)
+// take the DMA block-range kernel with the contraction split this many ways
+#ifndef MEDUSA_GEMM_XD_MIN_BLOCKS
+#define MEDUSA_GEMM_XD_MIN_BLOCKS 128
+#endif
+#ifndef MEDUSA_GEMM_XD_SPLIT
+#define MEDUSA_GEMM_XD_SPLIT 4
+#endif
 GemmPlan gemm_plan(int64_t M, int64_t Kd, int64_t Nw, int dt, int epi) {
   using namespace medusa;
   constexpr int XNB = MEDUSA_GEMM_XL_NB;
-  GemmPlan p{false, 1, false, 1, 0, 1};
+  GemmPlan p{false, 1, false, 1, 0, 1, 1};
   const int unit = epi == MEDUSA_EPI_SWIGLU ? 2 : 1;
+  const bool narrow = MEDUSA_GEMM_XB_DMA && Nw / 16 >= MEDUSA_GEMM_XD_MIN_BLOCKS;
   if (dt == MEDUSA_BF16 && M > 16 && Kd % XB_KC == 0 && Nw % (16 * unit) == 0 &&
-      Nw / 16 >= MEDUSA_GEMM_XB_MIN_BLOCKS && Nw / 16 <= (1 << 24)) {
+      (Nw / 16 >= MEDUSA_GEMM_XB_MIN_BLOCKS || narrow) && Nw / 16 <= (1 << 24)) {
     const int nunits = (int)(Nw / 16 / unit);
     p.xb = true;
     p.xb_unit = unit;
+    // a split contraction gives every compute unit's workgroup several blocks
+    p.xb_S = Nw / 16 >= MEDUSA_GEMM_XB_MIN_BLOCKS ? 1 : (int)std::min<int64_t>(MEDUSA_GEMM_XD_SPLIT, Kd / XB_KC);
     // about one workgroup per compute unit, at most XB_MAXB blocks each
-    p.xb_G = std::max(std::min(MEDUSA_GEMM_XB_WGS, nunits), (nunits + XB_MAXB / unit - 1) / (XB_MAXB / unit));
+    p.xb_G = std::max(std::min(MEDUSA_GEMM_XB_WGS / p.xb_S, nunits), (nunits + XB_MAXB / unit - 1) / (XB_MAXB / unit));
     p.MT = (int)((M + (M <= 32 ? 32 : 64) - 1) / (M <= 32 ? 32 : 64));
     return p;
   }
@@ -810,16 +878,26 @@ size_t gemm_ws_bytes(int64_t M, int64_t Kd, int64_t Nw, int batch, int dt) {
     const GemmPlan p = gemm_plan(M, Kd, Nw, dt, epi);
     if (!p.xb && p.xl && p.ksplit > 1)
       need = std::max(need, align_up((size_t)batch * p.ksplit * M * Nw * sizeof(float), 256));
+    if (p.xb && p.xb_S > 1)
+      need = std::max(need, align_up((size_t)batch * p.xb_S * M * Nw * sizeof(float), 256));
   }
   return need;
 }
 }  // namespace medusa_host
 
 namespace medusa {
+// RMSNorm fused behind a residual projection whose contraction is split
+struct SplitNorm {
+  const void* gain;
+  float eps;
+  void* out;
+};
+// Launches the projection; returns whether `norm` (residual epilogue only)
+// was applied, fused into the reduction of a split contraction.
 template <typename T, int EPI>
-static void launch_gemm_t(const void* X, int64_t xbs, int64_t M, int64_t Kd, const void* W,
+static bool launch_gemm_t(const void* X, int64_t xbs, int64_t M, int64_t Kd, const void* W,
                           int64_t Nw, int batch, const void* bias, const void* aux, void* Y,
-                          int y_f32, void* ws, hipStream_t st) {
+                          int y_f32, void* ws, hipStream_t st, const SplitNorm* norm = nullptr) {
   constexpr int NB = (EPI == MEDUSA_EPI_SWIGLU && MEDUSA_GEMM_NB < 2) ? 2 : MEDUSA_GEMM_NB;
   constexpr int KS = MEDUSA_GEMM_KS;
   constexpr int TN = 16 * NB;
@@ -827,17 +905,30 @@ static void launch_gemm_t(const void* X, int64_t xbs, int64_t M, int64_t Kd, con
   const medusa_host::GemmPlan plan = medusa_host::gemm_plan(M, Kd, Nw, sizeof(T) == 2 ? MEDUSA_BF16 : MEDUSA_F32, EPI);
   if constexpr (sizeof(T) == 2) {  // planned for bf16 only
     if (plan.xb) {
-      const dim3 grid((unsigned)plan.xb_G, (unsigned)(batch * plan.MT));
+      const dim3 grid((unsigned)plan.xb_G, (unsigned)(batch * plan.MT), (unsigned)plan.xb_S);
       const T* Xt = reinterpret_cast<const T*>(X);
       const T* Wt = reinterpret_cast<const T*>(W);
       const T* Bt = reinterpret_cast<const T*>(bias);
+      float* part = reinterpret_cast<float*>(ws);
       if (MEDUSA_GEMM_XB_DMA) {
         if (M <= 32)
-          hipLaunchKernelGGL((gemm_xdma_kernel<2, EPI>), grid, dim3(64 * XB_WAVES), 0, st, Xt, xbs,
-                             (int)M, (int)Kd, Wt, (int)Nw, Bt, aux, Y, y_f32, plan.xb_G, plan.MT, plan.xb_unit);
+          hipLaunchKernelGGL((gemm_xdma_kernel<2, MEDUSA_GEMM_XD_WR, EPI>), grid, dim3(64 * XB_WAVES), 0, st, Xt, xbs,
+                             (int)M, (int)Kd, Wt, (int)Nw, Bt, aux, Y, y_f32, plan.xb_G, plan.MT, plan.xb_unit, part);
         else
-          hipLaunchKernelGGL((gemm_xdma_kernel<4, EPI>), grid, dim3(64 * XB_WAVES), 0, st, Xt, xbs,
-                             (int)M, (int)Kd, Wt, (int)Nw, Bt, aux, Y, y_f32, plan.xb_G, plan.MT, plan.xb_unit);
+          hipLaunchKernelGGL((gemm_xdma_kernel<4, MEDUSA_GEMM_XD_WR, EPI>), grid, dim3(64 * XB_WAVES), 0, st, Xt, xbs,
+                             (int)M, (int)Kd, Wt, (int)Nw, Bt, aux, Y, y_f32, plan.xb_G, plan.MT, plan.xb_unit, part);
+        if (plan.xb_S > 1) {
+          if (EPI == MEDUSA_EPI_RES_ADD_F32 && norm) {
+            hipLaunchKernelGGL(split_reduce_rmsnorm_kernel<T>, dim3((unsigned)M), dim3(256), 0, st, part,
+                               plan.xb_S, (int)M, (int)Nw, reinterpret_cast<float*>(Y),
+                               reinterpret_cast<const T*>(norm->gain), norm->eps, reinterpret_cast<T*>(norm->out));
+            return true;
+          }
+          const int64_t cols = EPI == MEDUSA_EPI_SWIGLU ? Nw / 2 : Nw;
+          dim3 rgrid((unsigned)((M * cols + 255) / 256), (unsigned)batch);
+          hipLaunchKernelGGL((gemm_split_reduce_kernel<T, EPI>), rgrid, dim3(256), 0, st, part, plan.xb_S,
+                             (int)M, (int)Nw, xbs, Bt, aux, Y, y_f32);
+        }
       } else if (M <= 32) {
         hipLaunchKernelGGL((gemm_xlb_kernel<T, 2, MEDUSA_GEMM_XB_PF, EPI>), grid, dim3(64 * XB_WAVES), 0, st,
                            Xt, xbs, (int)M, (int)Kd, Wt, (int)Nw, Bt, aux, Y, y_f32, plan.xb_G, plan.MT, plan.xb_unit);
@@ -845,9 +936,10 @@ static void launch_gemm_t(const void* X, int64_t xbs, int64_t M, int64_t Kd, con
         hipLaunchKernelGGL((gemm_xlb_kernel<T, 4, MEDUSA_GEMM_XB_PF, EPI>), grid, dim3(64 * XB_WAVES), 0, st,
                            Xt, xbs, (int)M, (int)Kd, Wt, (int)Nw, Bt, aux, Y, y_f32, plan.xb_G, plan.MT, plan.xb_unit);
       }
-      return;
+      return false;
     }
   }
+  bool normed = false;
   auto go = [&](auto mbc) {
     constexpr int MB = decltype(mbc)::value;
     const unsigned gy = (unsigned)((M + 16 * MB - 1) / (16 * MB));
@@ -857,7 +949,13 @@ static void launch_gemm_t(const void* X, int64_t xbs, int64_t M, int64_t Kd, con
                          reinterpret_cast<const T*>(X), xbs, (int)M, (int)Kd,
                          reinterpret_cast<const T*>(W), (int)Nw, reinterpret_cast<const T*>(bias),
                          aux, Y, y_f32, plan.ksplit, reinterpret_cast<float*>(ws));
-      if (plan.ksplit > 1) {
+      if (plan.ksplit > 1 && EPI == MEDUSA_EPI_RES_ADD_F32 && norm) {
+        hipLaunchKernelGGL(split_reduce_rmsnorm_kernel<T>, dim3((unsigned)M), dim3(256), 0, st,
+                           reinterpret_cast<const float*>(ws), plan.ksplit, (int)M, (int)Nw,
+                           reinterpret_cast<float*>(Y), reinterpret_cast<const T*>(norm->gain), norm->eps,
+                           reinterpret_cast<T*>(norm->out));
+        normed = true;
+      } else if (plan.ksplit > 1) {
         const int64_t cols = EPI == MEDUSA_EPI_SWIGLU ? Nw / 2 : Nw;
         dim3 rgrid((unsigned)((M * cols + 255) / 256), (unsigned)batch);
         hipLaunchKernelGGL((gemm_split_reduce_kernel<T, EPI>), rgrid, dim3(256), 0, st,
@@ -875,6 +973,7 @@ static void launch_gemm_t(const void* X, int64_t xbs, int64_t M, int64_t Kd, con
   if (M <= 16) go(std::integral_constant<int, 1>());
   else if (M <= 32) go(std::integral_constant<int, 2>());
   else go(std::integral_constant<int, 4>());
+  return normed;
 }
 
 }  // namespace medusa
@@ -940,4 +1039,44 @@ extern "C" int32_t medusa_linear(const void* X, int64_t x_bstride, int64_t M, in
   launch_gemm(X, x_bstride, M, Kd, W, N, batch, dt, epilogue, bias, aux, Y, y_f32, ws,
               (hipStream_t)stream);
   return check_launch("medusa_linear");
+}
+
+extern "C" int32_t medusa_linear_rmsnorm(const void* X, int64_t M, int64_t Kd, const void* W,
+                                         int64_t N, int32_t dt, float* x, const void* gain,
+                                         float eps, void* out, void* ws, size_t ws_bytes,
+                                         void* stream) {
+  using namespace medusa_host;
+  MEDUSA_REQUIRE(dt == MEDUSA_F32 || dt == MEDUSA_BF16, MEDUSA_ERR_UNSUPPORTED,
+                 "medusa_linear_rmsnorm: unknown dtype %d", dt);
+  MEDUSA_REQUIRE(M >= 0 && Kd > 0 && N > 0 && eps >= 0.f, MEDUSA_ERR_INVALID_ARG,
+                 "medusa_linear_rmsnorm: bad sizes M=%lld Kd=%lld N=%lld", (long long)M,
+                 (long long)Kd, (long long)N);
+  MEDUSA_REQUIRE(M <= INT32_MAX && Kd <= INT32_MAX, MEDUSA_ERR_UNSUPPORTED,
+                 "medusa_linear_rmsnorm: sizes above 2^31");
+  const int p16 = dt == MEDUSA_BF16 ? 8 : 4;
+  MEDUSA_REQUIRE(Kd % p16 == 0, MEDUSA_ERR_UNSUPPORTED,
+                 "medusa_linear_rmsnorm: Kd must be a multiple of %d", p16);
+  MEDUSA_REQUIRE(N % 4 == 0 && N <= 4 * 256 * medusa::RMS_V4, MEDUSA_ERR_UNSUPPORTED,
+                 "medusa_linear_rmsnorm: N must be a multiple of 4 and at most %d",
+                 4 * 256 * medusa::RMS_V4);
+  if (M == 0) return MEDUSA_OK;
+  MEDUSA_REQUIRE(X && W && x && out, MEDUSA_ERR_INVALID_ARG,
+                 "medusa_linear_rmsnorm: NULL X, W, x or out");
+  MEDUSA_REQUIRE(((uintptr_t)X | (uintptr_t)W | (uintptr_t)x) % 16 == 0, MEDUSA_ERR_INVALID_ARG,
+                 "medusa_linear_rmsnorm: X, W and x must be 16-byte aligned");
+  const size_t need = gemm_ws_bytes(M, Kd, N, 1, dt);
+  MEDUSA_REQUIRE(need == 0 || (ws != NULL && ws_bytes >= need), MEDUSA_ERR_WORKSPACE,
+                 "medusa_linear_rmsnorm: workspace %zu < %zu bytes", ws_bytes, need);
+  const medusa::SplitNorm norm{gain, eps, out};
+  hipStream_t st = (hipStream_t)stream;
+  const bool normed =
+      dt == MEDUSA_BF16
+          ? medusa::launch_gemm_t<medusa::bf16_t, MEDUSA_EPI_RES_ADD_F32>(X, 0, M, Kd, W, N, 1, nullptr, x, x, 0, ws, st, &norm)
+          : medusa::launch_gemm_t<float, MEDUSA_EPI_RES_ADD_F32>(X, 0, M, Kd, W, N, 1, nullptr, x, x, 0, ws, st, &norm);
+  if (!normed) {
+    const int32_t rc = check_launch("medusa_linear_rmsnorm");
+    if (rc != MEDUSA_OK) return rc;
+    return medusa_rmsnorm(x, M, N, gain, eps, dt, out, stream);
+  }
+  return check_launch("medusa_linear_rmsnorm");
 }

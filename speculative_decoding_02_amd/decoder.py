@@ -151,20 +151,22 @@ class MedusaDecoder:
         n = tokens.shape[-1]
         x = M.medusa_embed(tokens.reshape(-1), t["embed"])
         scale = 1.0 / float(np.sqrt(m.head_dim))
-        for li, L in enumerate(t["layers"]):
-            h = M.medusa_rmsnorm(x, L["g_attn"], m.eps, m.dtype)
+        layers = t["layers"]
+        h = M.medusa_rmsnorm(x, layers[0]["g_attn"], m.eps, m.dtype)
+        for li, L in enumerate(layers):
             qkv = M.medusa_linear(h, L["wqkv"], ws=self.lin_ws)
             q, k, v = M.medusa_qkv_rope(qkv, m.n_heads, m.n_kv_heads, m.head_dim, pos.reshape(-1),
                                         m.rope_base)
             o = M.medusa_tree_attention(q[None], k[None], v[None], self.Kc[li], self.Vc[li],
                                         self.page_table, self.ctx, self.max_ctx,
                                         mask, scale, ws=self.attn_ws)
-            M.medusa_linear(o.reshape(n, -1), L["wo"], M.EPI_RES_ADD_F32, aux=x, out=x,
-                            ws=self.lin_ws)
-            h = M.medusa_rmsnorm(x, L["g_mlp"], m.eps, m.dtype)
+            # residual projections carry the next RMSNorm (the last one: the final norm)
+            h = M.medusa_linear_rmsnorm(o.reshape(n, -1), L["wo"], x, L["g_mlp"], m.eps,
+                                        ws=self.lin_ws)
             f = M.medusa_linear(h, L["wgu"], M.EPI_SWIGLU, ws=self.lin_ws)
-            M.medusa_linear(f, L["wd"], M.EPI_RES_ADD_F32, aux=x, out=x, ws=self.lin_ws)
-        hN = M.medusa_rmsnorm(x, t["g_final"], m.eps, m.dtype)
+            g_next = layers[li + 1]["g_attn"] if li + 1 < len(layers) else t["g_final"]
+            h = M.medusa_linear_rmsnorm(f, L["wd"], x, g_next, m.eps, ws=self.lin_ws)
+        hN = h
         logits = M.medusa_linear(hN, t["lm_head"], y_f32=True, ws=self.lin_ws)
         return logits, hN
 

@@ -45,6 +45,7 @@ _SIGS = {
                          i32, i32, i32, vp, vp, vp, vp]),
     "medusa_embed": (i32, [vp, i64, vp, i64, i64, i32, vp, vp]),
     "medusa_rmsnorm": (i32, [vp, i64, i64, vp, f32, i32, vp, vp]),
+    "medusa_linear_rmsnorm": (i32, [vp, i64, i64, vp, i64, i32, vp, vp, f32, vp, vp, sz, vp]),
     "medusa_qkv_rope": (i32, [vp, i64, i32, i32, i32, vp, f32, i32, vp, vp, vp, vp]),
     "medusa_swiglu": (i32, [vp, i64, i64, i32, vp, vp]),
     "medusa_gather_rows": (i32, [vp, i32, i32, i64, vp, vp, i32, i32, vp, vp]),
@@ -275,6 +276,21 @@ def medusa_rmsnorm(x, gain, eps, dtype, out=None):
     out = out if out is not None else torch.empty((M, H), dtype=dtype, device=x.device)
     _check("medusa_rmsnorm", _lib.medusa_rmsnorm(_p(x), M, H, _p(gain), float(eps), _dt(out),
                                                  _p(out), _stream()))
+    return out
+
+
+def medusa_linear_rmsnorm(X, W, x, gain, eps, out=None, ws=None):
+    """x += X W^T (x float [M, N], in place); returns RMSNorm(x) * gain in W's dtype."""
+    dt = _dt(W)
+    N, Kd = W.shape
+    M = X.shape[0]
+    out = out if out is not None else torch.empty((M, N), dtype=W.dtype, device=W.device)
+    need = _lib.medusa_linear_ws(M, Kd, N, 1, dt)
+    if need and (ws is None or ws.numel() < need):
+        ws = _ws(need, W.device)
+    _check("medusa_linear_rmsnorm", _lib.medusa_linear_rmsnorm(
+        _p(X), M, Kd, _p(W), N, dt, _p(x), _p(gain), float(eps), _p(out),
+        _p(ws) if need else None, ws.numel() if need else 0, _stream()))
     return out
 
 

@@ -38,7 +38,10 @@ def _rnd(dt, a):
                                      # workgroups; 11 chunks: uneven split)
                                      (64, 4096, 4096), (48, 2816, 4096),
                                      # block ranges with two blocks per wave
-                                     (64, 256, 32000), (24, 512, 22016)])
+                                     (64, 256, 32000), (24, 512, 22016),
+                                     # narrower outputs: split block ranges
+                                     # (32-row tiles; one chunk per split)
+                                     (20, 1024, 2048), (64, 768, 2048)])
 def test_linear(lib, dt, Mr, Kd, N):
     case(f"linear {DTN[dt]} M={Mr} Kd={Kd} N={N}")
     g = synth.rngs(Mr * 7 + Kd + N, 2)
@@ -86,6 +89,48 @@ def test_linear_epilogues(lib, dt):
     x2 = dev(R2, torch.float32)
     lib.medusa_linear(dev(X, dt), dev(W8, dt), lib.EPI_RES_ADD_F32, aux=x2, out=x2)
     assert_close(host(x2), R2 + orc.linear(X, W8), 1e-4 if dt == torch.float32 else 1e-3, "res_add N=8192")
+    # residual add at N=4096 from a 1024-long contraction (split block ranges)
+    X4 = _rnd(dt, g[0].standard_normal((Mr, 1024), dtype=np.float32))
+    R4 = g[3].standard_normal((Mr, 4096)).astype(np.float32)
+    W4 = _rnd(dt, g[4].standard_normal((4096, 1024), dtype=np.float32) * 0.05)
+    x4 = dev(R4, torch.float32)
+    lib.medusa_linear(dev(X4, dt), dev(W4, dt), lib.EPI_RES_ADD_F32, aux=x4, out=x4)
+    assert_close(host(x4), R4 + orc.linear(X4, W4), 1e-4 if dt == torch.float32 else 2e-3, "res_add N=4096")
+    # batched residual SiLU heads at H=2048, 40 rows (split block ranges, batch 2)
+    X5 = _rnd(dt, g[0].standard_normal((40, 2048), dtype=np.float32))
+    W5 = _rnd(dt, g[1].standard_normal((2, 2048, 2048), dtype=np.float32) * 0.02)
+    b5 = _rnd(dt, g[2].standard_normal((2, 2048), dtype=np.float32) * 0.1)
+    U5 = lib.medusa_linear(dev(X5, dt), dev(W5, dt), lib.EPI_BIAS_SILU_RES, bias=dev(b5, dt),
+                           aux=dev(X5, dt))
+    for k in range(2):
+        assert_close_stored(host(U5[k]), orc.head_hidden(X5, W5[k], b5[k]), TOL[dt], f"bias_silu_res H=2048 head {k}")
+
+
+@pytest.mark.parametrize("dt,Mr,Kd,N", [(torch.bfloat16, 64, 4096, 4096), (torch.bfloat16, 48, 2816, 4096),
+                                         (torch.bfloat16, 20, 1024, 2048), (torch.bfloat16, 40, 512, 1024),
+                                         (torch.bfloat16, 1, 4096, 4096), (torch.bfloat16, 64, 256, 8192),
+                                         (torch.float32, 33, 256, 512)],
+                         ids=["split64", "split11chunks", "split32rows", "tiles_split", "onerow", "nosplit",
+                              "f32"])
+def test_linear_rmsnorm(lib, dt, Mr, Kd, N):
+    """Residual projection + next RMSNorm: bit for bit the unfused pair
+    (fused into the split reduction or not), and close to the oracle."""
+    case(f"linear+rmsnorm {DTN[dt]} M={Mr} Kd={Kd} N={N}")
+    g = synth.rngs(Mr + Kd + 3 * N, 4)
+    X = _rnd(dt, g[0].standard_normal((Mr, Kd), dtype=np.float32))
+    W = _rnd(dt, g[1].standard_normal((N, Kd), dtype=np.float32) * 0.03)
+    R = g[2].standard_normal((Mr, N)).astype(np.float32) * 2
+    gain = _rnd(dt, 1 + 0.1 * g[3].standard_normal(N).astype(np.float32))
+    x_f = dev(R, torch.float32)
+    out = lib.medusa_linear_rmsnorm(dev(X, dt), dev(W, dt), x_f, dev(gain, dt), 1e-5)
+    x_u = dev(R, torch.float32)
+    lib.medusa_linear(dev(X, dt), dev(W, dt), lib.EPI_RES_ADD_F32, aux=x_u, out=x_u)
+    ref_out = lib.medusa_rmsnorm(x_u, dev(gain, dt), 1e-5, dt)
+    assert torch.equal(x_f, x_u), "residual stream differs from the unfused projection"
+    assert torch.equal(out, ref_out), "norm differs from the unfused RMSNorm"
+    xr = R + orc.linear(X, W)
+    assert_close(host(x_f), xr, 1e-4 * max(1, np.sqrt(Kd / 256)) * 4, "residual stream vs oracle")
+    assert_close(host(out), orc.rmsnorm(xr, gain, 1e-5), TOL[dt], "norm vs oracle")
 
 
 # ------------------------------------------------------------------- heads ---
