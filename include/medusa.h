@@ -244,14 +244,16 @@ int32_t medusa_embed(const int32_t* tokens, int64_t M, const void* table, int64_
                      int32_t dt, float* out, void* stream);
 
 /* out [M, H] (dt) = x / sqrt(mean(x^2) + eps) * gain; x float [M, H] (16-byte
- * aligned, H a multiple of 4, H <= 8192); gain [H] (dt) or NULL for 1. */
+ * aligned, H a multiple of 4, H <= 8192); gain [H] (dt) or NULL for 1; gain
+ * and out aligned to four elements (8 bytes bf16, 16 bytes fp32). */
 int32_t medusa_rmsnorm(const float* x, int64_t M, int64_t H, const void* gain, float eps,
                        int32_t dt, void* out, void* stream);
 
 /* The residual projection of a pre-norm block followed by the next block's
  * RMSNorm: x [M, N] float (16-byte aligned, updated in place) += X W^T with
  * X [M, Kd] and W [N, Kd] (dt), then out [M, N] (dt) = RMSNorm(x) * gain
- * (gain [N] dt or NULL for 1; N a multiple of 4, N <= 8192).  The results
+ * (gain [N] dt or NULL for 1; N a multiple of 4, N <= 8192; gain and out
+ * aligned to four elements).  The results
  * equal, bit for bit, medusa_linear(X, W, MEDUSA_EPI_RES_ADD_F32, aux = Y = x)
  * followed by medusa_rmsnorm(x, gain, eps, out): where the projection splits
  * its contraction, the split sum, the residual add and the norm run in one

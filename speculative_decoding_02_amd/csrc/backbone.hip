@@ -27,14 +27,15 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ 
   const int64_t m = blockIdx.x;
   const float* xr = x + m * H;
   const int64_t H4 = H / 4;
-  f32x4 v[RMS_V4];
+  f32x4 g[RMS_V4], v[RMS_V4];
+  rms_row_gain<T>(gain, H, g);
 #pragma unroll
   for (int i = 0; i < RMS_V4; ++i) {
     const int64_t e = threadIdx.x + (int64_t)i * 256;
     v[i] = reinterpret_cast<const f32x4*>(xr)[e < H4 ? e : 0];
   }
   const float rs = rms_row_scale(v, H, eps);
-  rms_row_store<T>(v, H, rs, gain, out + m * H);
+  rms_row_store<T>(v, H, rs, g, out + m * H);
 }
 
 // Rotary positions, rotate-half pairs (j, j + D/2), angle pos * base^(-2j/D).
@@ -140,6 +141,9 @@ extern "C" int32_t medusa_rmsnorm(const float* x, int64_t M, int64_t H, const vo
                  MEDUSA_ERR_UNSUPPORTED,
                  "medusa_rmsnorm: needs 16-byte aligned x, H a multiple of 4 and H <= %d",
                  4 * 256 * medusa::RMS_V4);
+  const int a4 = dt == MEDUSA_BF16 ? 8 : 16;  // four elements of gain and out
+  MEDUSA_REQUIRE(((uintptr_t)gain | (uintptr_t)out) % a4 == 0, MEDUSA_ERR_INVALID_ARG,
+                 "medusa_rmsnorm: gain and out must be %d-byte aligned", a4);
   MEDUSA_DT_DISPATCH(dt, hipLaunchKernelGGL(medusa::rmsnorm_kernel<T>, dim3((unsigned)M), dim3(256),
                                             0, (hipStream_t)stream, x, M, H, (const T*)gain, eps,
                                             (T*)out));

@@ -41,11 +41,27 @@ template <typename T> struct Elem;
 template <> struct Elem<float> {
   static __device__ __forceinline__ float load(const float* p, size_t i) { return p[i]; }
   static __device__ __forceinline__ void store(float* p, size_t i, float v) { p[i] = v; }
+  // elements 4*i4 .. 4*i4+3 (16-byte aligned)
+  static __device__ __forceinline__ f32x4 load4(const float* p, size_t i4) {
+    return reinterpret_cast<const f32x4*>(p)[i4];
+  }
+  static __device__ __forceinline__ void store4(float* p, size_t i4, f32x4 v) {
+    reinterpret_cast<f32x4*>(p)[i4] = v;
+  }
   static constexpr int per16 = 4;  // elements per 16-byte vector
 };
 template <> struct Elem<bf16_t> {
   static __device__ __forceinline__ float load(const bf16_t* p, size_t i) { return bf2f(p[i]); }
   static __device__ __forceinline__ void store(bf16_t* p, size_t i, float v) { p[i] = f2bf(v); }
+  // elements 4*i4 .. 4*i4+3 (8-byte aligned)
+  static __device__ __forceinline__ f32x4 load4(const bf16_t* p, size_t i4) {
+    const u32x2 u = reinterpret_cast<const u32x2*>(p)[i4];
+    return f32x4{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xFFFF0000u),
+                 __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xFFFF0000u)};
+  }
+  static __device__ __forceinline__ void store4(bf16_t* p, size_t i4, f32x4 v) {
+    reinterpret_cast<u32x2*>(p)[i4] = u32x2{pack_bf2(v.x, v.y), pack_bf2(v.z, v.w)};
+  }
   static constexpr int per16 = 8;
 };
 
@@ -108,19 +124,29 @@ __device__ __forceinline__ float rms_row_scale(const f32x4 (&v)[RMS_V4], int64_t
   const float tot = (rms_part[0] + rms_part[1]) + (rms_part[2] + rms_part[3]);
   return 1.0f / sqrtf(tot / (float)H + eps);
 }
+// gain [H] (NULL: 1) for this thread's vectors, loaded ahead of the row
+template <typename T>
+__device__ __forceinline__ void rms_row_gain(const T* __restrict__ gain, int64_t H, f32x4 (&g)[RMS_V4]) {
+  const int64_t H4 = H / 4;
+  if (gain) {
+#pragma unroll
+    for (int i = 0; i < RMS_V4; ++i) {
+      const int64_t e = threadIdx.x + (int64_t)i * 256;
+      g[i] = Elem<T>::load4(gain, e < H4 ? e : 0);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < RMS_V4; ++i) g[i] = f32x4{1.f, 1.f, 1.f, 1.f};
+  }
+}
 template <typename T>
 __device__ __forceinline__ void rms_row_store(const f32x4 (&v)[RMS_V4], int64_t H, float rs,
-                                              const T* __restrict__ gain, T* __restrict__ orow) {
+                                              const f32x4 (&g)[RMS_V4], T* __restrict__ orow) {
   const int64_t H4 = H / 4;
 #pragma unroll
   for (int i = 0; i < RMS_V4; ++i) {
     const int64_t e = threadIdx.x + (int64_t)i * 256;
-    if (e < H4)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float g = gain ? ld<T>(gain, e * 4 + r) : 1.f;
-        st<T>(orow, e * 4 + r, v[i][r] * rs * g);
-      }
+    if (e < H4) Elem<T>::store4(orow, e, (v[i] * rs) * g[i]);
   }
 }
 

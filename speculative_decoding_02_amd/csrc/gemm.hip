@@ -776,20 +776,39 @@ __global__ __launch_bounds__(256) void split_reduce_rmsnorm_kernel(const float* 
   f32x4* xr = reinterpret_cast<f32x4*>(x + (int64_t)m * N);
   const f32x4* p0 = reinterpret_cast<const f32x4*>(part + (int64_t)m * N);
   const int64_t pstride = (int64_t)M * N4;  // one split's partials, in f32x4
-  f32x4 v[RMS_V4];
+  // Every load is unconditional (indices clamped; lanes past the row only
+  // carry unused copies), so a batch of splits costs one memory round trip;
+  // the adds keep split order.
+  constexpr int QB = 3;
+  f32x4 g[RMS_V4], v[RMS_V4], acc[RMS_V4];
+  int ec[RMS_V4];
+  rms_row_gain<T>(gain, N, g);
 #pragma unroll
   for (int i = 0; i < RMS_V4; ++i) {
     const int e = threadIdx.x + i * 256;
-    v[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (e < N4) {
-      f32x4 acc = p0[e];
-      for (int q = 1; q < ksplit; ++q) acc += p0[q * pstride + e];
-      v[i] = xr[e] + acc;
-      xr[e] = v[i];
-    }
+    ec[i] = e < N4 ? e : 0;
+    acc[i] = p0[ec[i]];
+    v[i] = xr[ec[i]];
+  }
+  for (int q0 = 1; q0 < ksplit; q0 += QB) {
+    f32x4 t[QB][RMS_V4];
+#pragma unroll
+    for (int j = 0; j < QB; ++j)
+#pragma unroll
+      for (int i = 0; i < RMS_V4; ++i) t[j][i] = p0[min(q0 + j, ksplit - 1) * pstride + ec[i]];
+#pragma unroll
+    for (int j = 0; j < QB; ++j)
+      if (q0 + j < ksplit)
+#pragma unroll
+        for (int i = 0; i < RMS_V4; ++i) acc[i] += t[j][i];
+  }
+#pragma unroll
+  for (int i = 0; i < RMS_V4; ++i) {
+    v[i] = v[i] + acc[i];
+    if (threadIdx.x + i * 256 < N4) xr[threadIdx.x + i * 256] = v[i];
   }
   const float rs = rms_row_scale(v, N, eps);
-  rms_row_store<T>(v, N, rs, gain, out + (int64_t)m * N);
+  rms_row_store<T>(v, N, rs, g, out + (int64_t)m * N);
 }
 
 #ifndef MEDUSA_GEMM_XL_NB
@@ -849,7 +868,11 @@ GemmPlan gemm_plan(int64_t M, int64_t Kd, int64_t Nw, int dt, int epi) {
     p.xb = true;
     p.xb_unit = unit;
     // a split contraction gives every compute unit's workgroup several blocks
-    p.xb_S = Nw / 16 >= MEDUSA_GEMM_XB_MIN_BLOCKS ? 1 : (int)std::min<int64_t>(MEDUSA_GEMM_XD_SPLIT, Kd / XB_KC);
+    // (one split per ~8 chunks, at most MEDUSA_GEMM_XD_SPLIT: measured at 64 rows,
+    // 4096 x 4096 is fastest split 2 ways and 4096 x 11008 4 ways)
+    p.xb_S = Nw / 16 >= MEDUSA_GEMM_XB_MIN_BLOCKS
+                 ? 1
+                 : (int)std::max<int64_t>(1, std::min<int64_t>(MEDUSA_GEMM_XD_SPLIT, Kd / XB_KC / 8));
     // about one workgroup per compute unit, at most XB_MAXB blocks each
     p.xb_G = std::max(std::min(MEDUSA_GEMM_XB_WGS / p.xb_S, nunits), (nunits + XB_MAXB / unit - 1) / (XB_MAXB / unit));
     p.MT = (int)((M + (M <= 32 ? 32 : 64) - 1) / (M <= 32 ? 32 : 64));
@@ -1064,6 +1087,9 @@ extern "C" int32_t medusa_linear_rmsnorm(const void* X, int64_t M, int64_t Kd, c
                  "medusa_linear_rmsnorm: NULL X, W, x or out");
   MEDUSA_REQUIRE(((uintptr_t)X | (uintptr_t)W | (uintptr_t)x) % 16 == 0, MEDUSA_ERR_INVALID_ARG,
                  "medusa_linear_rmsnorm: X, W and x must be 16-byte aligned");
+  const int a4 = dt == MEDUSA_BF16 ? 8 : 16;  // four elements of gain and out
+  MEDUSA_REQUIRE(((uintptr_t)gain | (uintptr_t)out) % a4 == 0, MEDUSA_ERR_INVALID_ARG,
+                 "medusa_linear_rmsnorm: gain and out must be %d-byte aligned", a4);
   const size_t need = gemm_ws_bytes(M, Kd, N, 1, dt);
   MEDUSA_REQUIRE(need == 0 || (ws != NULL && ws_bytes >= need), MEDUSA_ERR_WORKSPACE,
                  "medusa_linear_rmsnorm: workspace %zu < %zu bytes", ws_bytes, need);

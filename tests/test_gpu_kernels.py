@@ -34,14 +34,14 @@ def _rnd(dt, a):
 @pytest.mark.parametrize("Mr,Kd,N", [(1, 256, 1000), (5, 72, 37), (17, 688, 80), (64, 256, 96),
                                      (100, 128, 33), (33, 4096, 64), (64, 512, 8192),
                                      (40, 768, 12288), (17, 256, 16384), (130, 256, 8320),
-                                     # 4096-wide outputs (contraction split across
-                                     # workgroups; 11 chunks: uneven split)
-                                     (64, 4096, 4096), (48, 2816, 4096),
+                                     # 4096-wide outputs (contraction split 2 and,
+                                     # over 43 chunks, 4 uneven ways)
+                                     (64, 4096, 4096), (48, 11008, 4096),
                                      # block ranges with two blocks per wave
                                      (64, 256, 32000), (24, 512, 22016),
-                                     # narrower outputs: split block ranges
-                                     # (32-row tiles; one chunk per split)
-                                     (20, 1024, 2048), (64, 768, 2048)])
+                                     # narrower outputs: block ranges (32-row
+                                     # tiles split 2 ways; 3 splits; unsplit)
+                                     (20, 4096, 2048), (64, 6144, 2048), (64, 768, 2048)])
 def test_linear(lib, dt, Mr, Kd, N):
     case(f"linear {DTN[dt]} M={Mr} Kd={Kd} N={N}")
     g = synth.rngs(Mr * 7 + Kd + N, 2)
@@ -96,21 +96,21 @@ def test_linear_epilogues(lib, dt):
     x4 = dev(R4, torch.float32)
     lib.medusa_linear(dev(X4, dt), dev(W4, dt), lib.EPI_RES_ADD_F32, aux=x4, out=x4)
     assert_close(host(x4), R4 + orc.linear(X4, W4), 1e-4 if dt == torch.float32 else 2e-3, "res_add N=4096")
-    # batched residual SiLU heads at H=2048, 40 rows (split block ranges, batch 2)
-    X5 = _rnd(dt, g[0].standard_normal((40, 2048), dtype=np.float32))
-    W5 = _rnd(dt, g[1].standard_normal((2, 2048, 2048), dtype=np.float32) * 0.02)
-    b5 = _rnd(dt, g[2].standard_normal((2, 2048), dtype=np.float32) * 0.1)
+    # batched residual SiLU heads at H=4096, 24 rows (split block ranges, batch 2)
+    X5 = _rnd(dt, g[0].standard_normal((24, 4096), dtype=np.float32))
+    W5 = _rnd(dt, g[1].standard_normal((2, 4096, 4096), dtype=np.float32) * 0.02)
+    b5 = _rnd(dt, g[2].standard_normal((2, 4096), dtype=np.float32) * 0.1)
     U5 = lib.medusa_linear(dev(X5, dt), dev(W5, dt), lib.EPI_BIAS_SILU_RES, bias=dev(b5, dt),
                            aux=dev(X5, dt))
     for k in range(2):
-        assert_close_stored(host(U5[k]), orc.head_hidden(X5, W5[k], b5[k]), TOL[dt], f"bias_silu_res H=2048 head {k}")
+        assert_close_stored(host(U5[k]), orc.head_hidden(X5, W5[k], b5[k]), TOL[dt], f"bias_silu_res H=4096 head {k}")
 
 
-@pytest.mark.parametrize("dt,Mr,Kd,N", [(torch.bfloat16, 64, 4096, 4096), (torch.bfloat16, 48, 2816, 4096),
-                                         (torch.bfloat16, 20, 1024, 2048), (torch.bfloat16, 40, 512, 1024),
+@pytest.mark.parametrize("dt,Mr,Kd,N", [(torch.bfloat16, 64, 4096, 4096), (torch.bfloat16, 48, 11008, 4096),
+                                         (torch.bfloat16, 20, 4096, 2048), (torch.bfloat16, 40, 512, 1024),
                                          (torch.bfloat16, 1, 4096, 4096), (torch.bfloat16, 64, 256, 8192),
                                          (torch.float32, 33, 256, 512)],
-                         ids=["split64", "split11chunks", "split32rows", "tiles_split", "onerow", "nosplit",
+                         ids=["split2", "split4_uneven", "split32rows", "tiles_split", "onerow", "nosplit",
                               "f32"])
 def test_linear_rmsnorm(lib, dt, Mr, Kd, N):
     """Residual projection + next RMSNorm: bit for bit the unfused pair
