@@ -32,9 +32,12 @@ __device__ __forceinline__ bf16_t f2bf(float f) {
   return (bf16_t)(u >> 16);
 }
 
-// Pack two fp32 values into one dword of two bf16 (lo = a, hi = b), RNE.
+// Pack two fp32 values into one dword of two bf16 (lo = a, hi = b), RNE, with
+// gfx950's packed conversion (the same rounding as f2bf for every non-NaN).
 __device__ __forceinline__ uint32_t pack_bf2(float a, float b) {
-  return (uint32_t)f2bf(a) | ((uint32_t)f2bf(b) << 16);
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
 }
 
 template <typename T> struct Elem;

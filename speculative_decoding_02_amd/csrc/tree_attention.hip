@@ -88,6 +88,7 @@ struct AttnArgs {
   void* opart;       // [B*Hq*S*N*D] of PartT<T>: a split's output divided by its own sum
   int max_pages, P, B, N, Hq, Hkv, chunk;  // chunk = keys per split (multiple of 64)
   int max_ctx;
+  int lp;            // log2(P) when P is a power of two, else -1 (page math by division)
   float scale_log2;
 };
 
@@ -139,9 +140,13 @@ __global__ __launch_bounds__(ATT_THREADS) void tree_attention_kernel(AttnArgs a)
   const int my_page = threadIdx.x < npages ? pt[page0 + threadIdx.x] : 0;
 
   // element offset of key j's row for kv head kvh (cache slot or tree node)
+  // page of key j and its slot there (shifts when P is a power of two: the
+  // address math runs per lane for every tile)
   auto cache_off = [&](int j) -> int64_t {
-    const int page = spages[j / a.P - page0];
-    return (((int64_t)page * a.Hkv + kvh) * a.P + (j % a.P)) * D;
+    const int pj = a.lp >= 0 ? (j >> a.lp) : j / a.P;
+    const int sj = a.lp >= 0 ? (j & (a.P - 1)) : j - pj * a.P;
+    const int page = spages[pj - page0];
+    return (((int64_t)page * a.Hkv + kvh) * a.P + sj) * D;
   };
   auto tree_off = [&](int j) -> int64_t {
     return (((int64_t)b * N + max(j - ctxb, 0)) * a.Hkv + kvh) * D;
@@ -269,29 +274,51 @@ __global__ __launch_bounds__(ATT_THREADS) void tree_attention_kernel(AttnArgs a)
       }
       float x[4][4];
       float tmax = -INFINITY;
+      // a tile wholly inside the cached keys needs no mask (wave-uniform)
+      const bool plain = tile0 + ATT_TILE <= min(ctxb, k_end);
+      if (plain) {
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
+        for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int j = tile0 + kb * 16 + lg * 4 + r;
-          const uint32_t bit = (uint32_t)(mrow >> (uint32_t)min(max(j - ctxb, 0), 63)) & 1u;
-          const bool ok = (j < k_end) & ((j < ctxb) | (bit != 0u));
-          x[kb][r] = ok ? sacc[kb][r] * a.scale_log2 : -INFINITY;
-          tmax = fmaxf(tmax, x[kb][r]);
-        }
+          for (int r = 0; r < 4; ++r) {
+            x[kb][r] = sacc[kb][r] * a.scale_log2;
+            tmax = fmaxf(tmax, x[kb][r]);
+          }
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int j = tile0 + kb * 16 + lg * 4 + r;
+            const uint32_t bit = (uint32_t)(mrow >> (uint32_t)min(max(j - ctxb, 0), 63)) & 1u;
+            const bool ok = (j < k_end) & ((j < ctxb) | (bit != 0u));
+            x[kb][r] = ok ? sacc[kb][r] * a.scale_log2 : -INFINITY;
+            tmax = fmaxf(tmax, x[kb][r]);
+          }
+      }
       tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
       tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
       const float mnew = fmaxf(mrun, tmax);
       const float alpha = (mnew == -INFINITY) ? 1.f : exp2f(mrun - mnew);
       float psum = 0.f;
+      if (plain) {  // every score finite, so mnew is too
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
+        for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float p = (x[kb][r] == -INFINITY) ? 0.f : exp2f(x[kb][r] - mnew);
-          x[kb][r] = p;
-          psum += p;
-        }
+          for (int r = 0; r < 4; ++r) {
+            x[kb][r] = exp2f(x[kb][r] - mnew);
+            psum += x[kb][r];
+          }
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float p = (x[kb][r] == -INFINITY) ? 0.f : exp2f(x[kb][r] - mnew);
+            x[kb][r] = p;
+            psum += p;
+          }
+      }
       lrun = lrun * alpha + psum;
       mrun = mnew;
 #pragma unroll
@@ -394,10 +421,18 @@ __global__ __launch_bounds__(ATT_THREADS) void tree_attention_kernel(AttnArgs a)
 //     transposing LDS read: within a 16-lane block, lane i returns element
 //     i%4 of the 4 values at source lane (i/4)+4r's address, so pointing lane
 //     j of block g at V[key 4g + j/4][dim 4(j%4)] yields V[key 4g + r][dim i].
-//   * Waits are explicit: s_barrier without a fence (a fenced barrier would
-//     wait for every DMA in flight) after waiting until only the later
-//     tiles' (R-1) x OPS DMA loads are outstanding.
-template <int D, int R>
+//   * One barrier per tile: at the start of tile t every wave has its own
+//     DMA of tile t landed (an explicit vmcnt wait: only the later tiles'
+//     (R-2) x OPS loads may still be in flight) and its LDS reads of tile t-1
+//     done, so after the barrier tile t is readable everywhere and tile t-1's
+//     slot is free; tile t+R-1 is issued into that slot at once and streams
+//     in while tile t is computed.  s_barrier goes without a fence (a fenced
+//     barrier would wait for every DMA in flight).
+//   * The DMA source addresses are computed without branches: the page
+//     lookups of a wave's rows are read from LDS together, cached and tree
+//     rows are chosen by selects, and P2 (page size a power of two) turns the
+//     page/slot split into a shift and a mask.
+template <int D, int R, bool P2>
 __global__ __launch_bounds__(ATT_THREADS) void tree_attention_dma_kernel(AttnArgs a) {
   using T = bf16_t;
   constexpr int P16 = 8;                       // bf16 per 16 bytes
@@ -411,7 +446,8 @@ __global__ __launch_bounds__(ATT_THREADS) void tree_attention_dma_kernel(AttnArg
   constexpr int OPS = 2 * DPW;                 // vector-memory ops per wave per tile
   constexpr int QSTEPS = D / 32;
   constexpr int DB = D / 16;
-  constexpr int WAITN = (R - 1) * OPS;         // DMA ops allowed in flight at a tile start
+  static_assert(R >= 3, "a slot is refilled one tile after it was read");
+  constexpr int WAITN = (R - 2) * OPS;         // DMA ops allowed in flight at a tile start
   static_assert(WAITN < 64, "vmcnt range");
   constexpr int WAIT_IMM = waitcnt_vm(WAITN);
   __shared__ __attribute__((aligned(1024))) unsigned char lds[R * SLOTB];
@@ -425,7 +461,8 @@ __global__ __launch_bounds__(ATT_THREADS) void tree_attention_dma_kernel(AttnArg
   const int kvh = h / group;
   const bool appender = (h % group) == 0;
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+  // wave index made provably uniform, so per-wave branches stay scalar
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, lr = lane & 15, lg = lane >> 4;
   const int node = wave * 16 + lr;
   const bool wave_active = wave * 16 < N;
   const int nodec = min(node, N - 1);
@@ -460,28 +497,47 @@ __global__ __launch_bounds__(ATT_THREADS) void tree_attention_dma_kernel(AttnArg
   const int k_end = min(k_beg + a.chunk, total);
   const int ntiles = (k_end - k_beg + ATT_TILE - 1) / ATT_TILE;
 
+  // page of key j and its slot there (shifts when P is a power of two: the
+  // address math runs per lane for every tile)
+  const int64_t page_elems = (int64_t)a.Hkv * a.P * D;  // one page of the cache
+  const int head_elems = kvh * a.P * D;                  // this head's rows in a page
   auto cache_off = [&](int j) -> int64_t {
-    const int page = spages[j / a.P - page0];
-    return (((int64_t)page * a.Hkv + kvh) * a.P + (j % a.P)) * D;
+    const int pj = P2 ? (j >> a.lp) : j / a.P;
+    const int sj = P2 ? (j & (a.P - 1)) : j - pj * a.P;
+    const int page = spages[pj - page0];
+    return (int64_t)page * page_elems + (head_elems + sj * D);
   };
+  const int64_t tree_base = ((int64_t)b * N * a.Hkv + kvh) * D;
   auto tree_off = [&](int j) -> int64_t {
-    return (((int64_t)b * N + max(j - ctxb, 0)) * a.Hkv + kvh) * D;
+    return tree_base + max(j - ctxb, 0) * (a.Hkv * D);
   };
 
   const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)lds;
-  // DMA of tile t (clamped to the split's last tile) into ring slot `slot`
+  // DMA of tile t (clamped to the split's last tile) into ring slot `slot`.
+  // Every key of [k_beg, k_end) has its page in spages (the tree keys' too:
+  // they go to cache slots ctx..ctx+N-1), so the lookup runs for every row
+  // and the tree rows just ignore it.
   auto issue = [&](int t, int slot) {
     const int tile0 = k_beg + min(t, ntiles - 1) * ATT_TILE;
+    int jj[DPW], pg[DPW];
+#pragma unroll
+    for (int i = 0; i < DPW; ++i) {
+      const int r = (wave * DPW + i) * RPD + lane / CPR;  // tile row this lane fills
+      jj[i] = min(tile0 + r, k_end - 1);
+      pg[i] = spages[(P2 ? (jj[i] >> a.lp) : jj[i] / a.P) - page0];
+    }
 #pragma unroll
     for (int i = 0; i < DPW; ++i) {
       const int q = wave * DPW + i;          // 1 KB block of the tile
-      const int r = q * RPD + lane / CPR;    // tile row this lane fills
+      const int r = q * RPD + lane / CPR;
       const int c = (lane % CPR) ^ (r & SW); // chunk fetched for that position
-      const int jj = min(tile0 + r, k_end - 1);
-      const bool cached = jj < ctxb;
-      const int64_t off = cached ? cache_off(jj) : tree_off(jj);
-      const T* ksrc = (cached ? Kcp : Ktp) + off + c * P16;
-      const T* vsrc = (cached ? Vcp : Vtp) + off + c * P16;
+      const int j = jj[i];
+      const bool cached = j < ctxb;
+      const int sj = P2 ? (j & (a.P - 1)) : j - (j / a.P) * a.P;
+      const int64_t coff = (int64_t)(uint32_t)pg[i] * page_elems + (head_elems + sj * D);
+      const int64_t off = (cached ? coff : tree_off(j)) + c * P16;
+      const T* ksrc = (cached ? Kcp : Ktp) + off;
+      const T* vsrc = (cached ? Vcp : Vtp) + off;
       const uint32_t kd = lds_base + slot * SLOTB + q * 1024;
       lds_dma16(ksrc, kd);
       lds_dma16(vsrc, kd + TILEB);
@@ -493,13 +549,15 @@ __global__ __launch_bounds__(ATT_THREADS) void tree_attention_dma_kernel(AttnArg
   for (int db = 0; db < DB; ++db) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
   float mrun = -INFINITY, lrun = 0.f;
 
-  for (int t = 0; t < R; ++t) issue(t, t);
+  for (int t = 0; t < R - 1; ++t) issue(t, t);
   for (int t = 0; t < ntiles; ++t) {
     const int slot = t % R;
     const int tile0 = k_beg + t * ATT_TILE;
-    __builtin_amdgcn_s_waitcnt(WAIT_IMM);  // this wave's DMA of tile t is done
-    __builtin_amdgcn_s_barrier();          // ... and every other wave's
-    asm volatile("" ::: "memory");         // no LDS access moves across the barrier
+    __builtin_amdgcn_s_waitcnt(WAIT_IMM);       // this wave's DMA of tile t is done
+    __builtin_amdgcn_s_waitcnt(WAITCNT_LGKM0);  // ... and its LDS reads of tile t-1
+    __builtin_amdgcn_s_barrier();               // ... and every other wave's
+    asm volatile("" ::: "memory");              // no LDS access moves across the barrier
+    issue(t + R - 1, (t + R - 1) % R);          // into tile t-1's slot
     const unsigned char* ks = lds + slot * SLOTB;
     const unsigned char* vs = ks + TILEB;
     if (wave_active) {
@@ -517,29 +575,51 @@ __global__ __launch_bounds__(ATT_THREADS) void tree_attention_dma_kernel(AttnArg
       }
       float x[4][4];
       float tmax = -INFINITY;
+      // a tile wholly inside the cached keys needs no mask (wave-uniform)
+      const bool plain = tile0 + ATT_TILE <= min(ctxb, k_end);
+      if (plain) {
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
+        for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int j = tile0 + kb * 16 + lg * 4 + r;
-          const uint32_t bit = (uint32_t)(mrow >> (uint32_t)min(max(j - ctxb, 0), 63)) & 1u;
-          const bool ok = (j < k_end) & ((j < ctxb) | (bit != 0u));
-          x[kb][r] = ok ? sacc[kb][r] * a.scale_log2 : -INFINITY;
-          tmax = fmaxf(tmax, x[kb][r]);
-        }
+          for (int r = 0; r < 4; ++r) {
+            x[kb][r] = sacc[kb][r] * a.scale_log2;
+            tmax = fmaxf(tmax, x[kb][r]);
+          }
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int j = tile0 + kb * 16 + lg * 4 + r;
+            const uint32_t bit = (uint32_t)(mrow >> (uint32_t)min(max(j - ctxb, 0), 63)) & 1u;
+            const bool ok = (j < k_end) & ((j < ctxb) | (bit != 0u));
+            x[kb][r] = ok ? sacc[kb][r] * a.scale_log2 : -INFINITY;
+            tmax = fmaxf(tmax, x[kb][r]);
+          }
+      }
       tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
       tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
       const float mnew = fmaxf(mrun, tmax);
-      const float alpha = (mnew == -INFINITY) ? 1.f : exp2f(mrun - mnew);
+      const float alpha = (mnew == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(mrun - mnew);
       float psum = 0.f;
+      if (plain) {  // every score finite, so mnew is too
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
+        for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float p = (x[kb][r] == -INFINITY) ? 0.f : exp2f(x[kb][r] - mnew);
-          x[kb][r] = p;
-          psum += p;
-        }
+          for (int r = 0; r < 4; ++r) {
+            x[kb][r] = __builtin_amdgcn_exp2f(x[kb][r] - mnew);
+            psum += x[kb][r];
+          }
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float p = (x[kb][r] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(x[kb][r] - mnew);
+            x[kb][r] = p;
+            psum += p;
+          }
+      }
       lrun = lrun * alpha + psum;
       mrun = mnew;
 #pragma unroll
@@ -561,10 +641,6 @@ __global__ __launch_bounds__(ATT_THREADS) void tree_attention_dma_kernel(AttnArg
       }
     }
     asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt(WAITCNT_LGKM0);  // this wave's LDS reads are done
-    __builtin_amdgcn_s_barrier();          // ... so the slot can be refilled
-    asm volatile("" ::: "memory");
-    issue(t + R, slot);
   }
   __builtin_amdgcn_s_waitcnt(0);           // drain the clamped refills before leaving
 
@@ -695,7 +771,7 @@ struct SplitPlan {
 #define MEDUSA_ATTN_DMA_WGS 256
 #endif
 #ifndef MEDUSA_ATTN_DMA_R
-#define MEDUSA_ATTN_DMA_R 2
+#define MEDUSA_ATTN_DMA_R 3
 #endif
 SplitPlan plan_splits(int B, int Hq, int N, int max_ctx, int P, int target) {
   const int total = max_ctx + N;
@@ -778,6 +854,7 @@ extern "C" int32_t medusa_tree_attention(const void* Q, const void* Kt, const vo
   a.ml = (float2*)((char*)ws + L.ml);
   a.opart = (char*)ws + L.opart;
   a.max_pages = max_pages; a.P = P; a.B = B; a.N = N; a.Hq = Hq; a.Hkv = Hkv;
+  a.lp = (P & (P - 1)) == 0 ? __builtin_ctz((unsigned)P) : -1;
   a.chunk = p.chunk;
   a.max_ctx = max_ctx;
   a.scale_log2 = scale * 1.4426950408889634f;
@@ -795,8 +872,11 @@ extern "C" int32_t medusa_tree_attention(const void* Q, const void* Kt, const vo
   } while (0)
   constexpr int RD = MEDUSA_ATTN_DMA_R;
   if (dt == MEDUSA_BF16) {
-    if (D == 128) MEDUSA_ATT_LAUNCH((medusa::tree_attention_dma_kernel<128, RD>), medusa::bf16_t, 128);
-    else MEDUSA_ATT_LAUNCH((medusa::tree_attention_dma_kernel<64, 2 * RD>), medusa::bf16_t, 64);
+    const bool p2 = a.lp >= 0;
+    if (D == 128 && p2) MEDUSA_ATT_LAUNCH((medusa::tree_attention_dma_kernel<128, RD, true>), medusa::bf16_t, 128);
+    else if (D == 128) MEDUSA_ATT_LAUNCH((medusa::tree_attention_dma_kernel<128, RD, false>), medusa::bf16_t, 128);
+    else if (p2) MEDUSA_ATT_LAUNCH((medusa::tree_attention_dma_kernel<64, 2 * RD, true>), medusa::bf16_t, 64);
+    else MEDUSA_ATT_LAUNCH((medusa::tree_attention_dma_kernel<64, 2 * RD, false>), medusa::bf16_t, 64);
   } else {
     if (D == 128) MEDUSA_ATT_LAUNCH((medusa::tree_attention_kernel<float, 128, PF>), float, 128);
     else MEDUSA_ATT_LAUNCH((medusa::tree_attention_kernel<float, 64, PF>), float, 64);
