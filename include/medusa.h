@@ -263,6 +263,23 @@ int32_t medusa_linear_rmsnorm(const void* X, int64_t M, int64_t Kd, const void* 
                               int32_t dt, float* x, const void* gain, float eps, void* out,
                               void* ws, size_t ws_bytes, void* stream);
 
+/* The QKV projection with the rotary positions of medusa_qkv_rope fused in:
+ * q [M, Hq, D], k [M, Hkv, D], v [M, Hkv, D] (dt) from X [M, Kd] (dt) and
+ * W [(Hq + 2 Hkv) D, Kd] whose q and k head rows are pair-interleaved: row
+ * 2j of a head holds the weights of element j and row 2j + 1 those of
+ * element j + D/2 (the v rows keep their order).  Bit for bit equal to the
+ * projection with the plain row order (medusa_linear, stored in dt) followed
+ * by medusa_qkv_rope.  Where the projection takes the block-range kernel
+ * without a contraction split, the rotation runs in its epilogue; otherwise
+ * the projection goes to ws and the rotary pass reads it there.
+ * ws: medusa_linear_qkv_rope_ws(...) bytes, 256-byte aligned (NULL when 0).
+ * X, W, v 16-byte aligned; D a multiple of 8 up to 128; base > 1. */
+size_t medusa_linear_qkv_rope_ws(int64_t M, int64_t Kd, int32_t Hq, int32_t Hkv, int32_t D,
+                                 int32_t dt);
+int32_t medusa_linear_qkv_rope(const void* X, int64_t M, int64_t Kd, const void* W, int32_t Hq,
+                               int32_t Hkv, int32_t D, const int32_t* pos, float base, int32_t dt,
+                               void* q, void* k, void* v, void* ws, size_t ws_bytes, void* stream);
+
 /* Split qkv [M, (Hq + 2 Hkv) * D] (dt) into q [M, Hq, D], k [M, Hkv, D],
  * v [M, Hkv, D] and rotate q and k by position pos[m] (rotate-half pairs
  * (j, j + D/2), angle pos * base^(-2j/D)). */

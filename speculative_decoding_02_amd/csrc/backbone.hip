@@ -38,10 +38,12 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ 
   rms_row_store<T>(v, H, rs, g, out + m * H);
 }
 
-// Rotary positions, rotate-half pairs (j, j + D/2), angle pos * base^(-2j/D).
-// The angle is formed and reduced to [-pi, pi] in fp64, then its cosine and
-// sine are taken in fp32; one pass per row over 4 consecutive j per thread.
-template <typename T>
+// Rotary positions, rotate-half pairs (j, j + D/2), angle pos * base^(-2j/D)
+// (rope_inv_freq / rope_cs / rope_rot); one pass per row over 4 consecutive j
+// per thread.  PAIRS: the q and k heads of qkv hold each pair side by side
+// (columns 2j, 2j+1 of a head = elements j, j + D/2), the layout of a
+// projection whose weight rows were interleaved that way.
+template <typename T, bool PAIRS>
 __global__ __launch_bounds__(256) void qkv_rope_kernel(const T* __restrict__ qkv, int Hq, int Hkv,
                                                        int D, const int* __restrict__ pos,
                                                        double log2_base, T* __restrict__ q,
@@ -50,12 +52,8 @@ __global__ __launch_bounds__(256) void qkv_rope_kernel(const T* __restrict__ qkv
   __shared__ float cs[64], sn[64];
   const int half = D / 2;
   if (threadIdx.x < half) {
-    const double inv = exp2(-(2.0 * threadIdx.x / D) * log2_base);
-    double ang = (double)pos[m] * inv;
-    const double two_pi = 6.283185307179586476925286766559;
-    ang -= two_pi * rint(ang / two_pi);
     float c, sv;
-    sincosf((float)ang, &sv, &c);
+    rope_cs(pos[m], rope_inv_freq(threadIdx.x, D, log2_base), c, sv);
     cs[threadIdx.x] = c;
     sn[threadIdx.x] = sv;
   }
@@ -69,9 +67,12 @@ __global__ __launch_bounds__(256) void qkv_rope_kernel(const T* __restrict__ qkv
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int j = j0 + r;
-      const float x1 = ld<T>(in, (int64_t)hh * D + j), x2 = ld<T>(in, (int64_t)hh * D + j + half);
-      st<T>(dst, j, x1 * cs[j] - x2 * sn[j]);
-      st<T>(dst, j + half, x2 * cs[j] + x1 * sn[j]);
+      const int64_t i1 = PAIRS ? (int64_t)hh * D + 2 * j : (int64_t)hh * D + j;
+      const int64_t i2 = PAIRS ? i1 + 1 : i1 + half;
+      float y1, y2;
+      rope_rot(ld<T>(in, i1), ld<T>(in, i2), cs[j], sn[j], y1, y2);
+      st<T>(dst, j, y1);
+      st<T>(dst, j + half, y2);
     }
   }
   // v: straight copy in 16-byte pieces
@@ -164,7 +165,7 @@ extern "C" int32_t medusa_qkv_rope(const void* qkv, int64_t M, int32_t Hq, int32
   if (M == 0) return MEDUSA_OK;
   MEDUSA_REQUIRE(qkv && pos && q && k && v, MEDUSA_ERR_INVALID_ARG, "medusa_qkv_rope: NULL pointer");
   const double lb = log2((double)base);
-  MEDUSA_DT_DISPATCH(dt, hipLaunchKernelGGL(medusa::qkv_rope_kernel<T>, dim3((unsigned)M), dim3(256), 0,
+  MEDUSA_DT_DISPATCH(dt, hipLaunchKernelGGL((medusa::qkv_rope_kernel<T, false>), dim3((unsigned)M), dim3(256), 0,
                                             (hipStream_t)stream, (const T*)qkv, Hq, Hkv, D, pos, lb,
                                             (T*)q, (T*)k, (T*)v));
   return check_launch("medusa_qkv_rope");
@@ -198,3 +199,13 @@ extern "C" int32_t medusa_gather_rows(const void* h, int32_t B, int32_t N, int64
                                             K, (T*)out));
   return check_launch("medusa_gather_rows");
 }
+
+namespace medusa_host {
+// Rotary kernel on a pair-interleaved qkv (arguments validated by the caller).
+void launch_qkv_rope_pairs(const void* qkv, int64_t M, int Hq, int Hkv, int D, const int32_t* pos,
+                           double log2_base, int dt, void* q, void* k, void* v, hipStream_t st) {
+  MEDUSA_DT_DISPATCH(dt, hipLaunchKernelGGL((medusa::qkv_rope_kernel<T, true>), dim3((unsigned)M), dim3(256),
+                                            0, st, (const T*)qkv, Hq, Hkv, D, pos, log2_base, (T*)q,
+                                            (T*)k, (T*)v));
+}
+}  // namespace medusa_host

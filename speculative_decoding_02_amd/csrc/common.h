@@ -153,6 +153,26 @@ __device__ __forceinline__ void rms_row_store(const f32x4 (&v)[RMS_V4], int64_t 
   }
 }
 
+// Rotary positions, rotate-half pairs (j, j + D/2): the pair's frequency
+// base^(-2j/D) and, at position pos, the angle reduced to [-pi, pi] in fp64
+// with its cosine and sine in fp32; the rotation with explicit FMAs.  Shared
+// by the standalone rotary kernel and the projection epilogue that fuses it,
+// so the two agree bit for bit.
+__device__ __forceinline__ double rope_inv_freq(int j, int D, double log2_base) {
+  return exp2(-(2.0 * j / D) * log2_base);
+}
+__device__ __forceinline__ void rope_cs(int pos, double inv, float& c, float& s) {
+  double ang = (double)pos * inv;
+  const double two_pi = 6.283185307179586476925286766559;
+  ang -= two_pi * rint(ang / two_pi);
+  sincosf((float)ang, &s, &c);
+}
+// (x1, x2) = elements j and j + D/2 -> their rotated values
+__device__ __forceinline__ void rope_rot(float x1, float x2, float c, float s, float& y1, float& y2) {
+  y1 = __builtin_fmaf(x1, c, -(x2 * s));
+  y2 = __builtin_fmaf(x2, c, x1 * s);
+}
+
 // One LDS-DMA instruction: every lane's 16 bytes at gptr land at LDS byte
 // address lds_addr + 16 * lane (lds_addr is wave-uniform, set in m0).  It is
 // issued from inline asm so that the compiler does not treat it as an LDS

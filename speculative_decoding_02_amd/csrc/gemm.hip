@@ -550,6 +550,20 @@ __global__ __launch_bounds__(64 * XB_WAVES) void gemm_xlb_kernel(
 // In LDS both operands are XOR-swizzled in 16-byte units (slot ^ row) so
 // that the 16 rows of one operand read fall in distinct banks; the swizzle is
 // applied on the global side, since a DMA lane's LDS address is fixed.
+// Internal epilogue of the QKV projection with rotary positions fused: W's q
+// and k head rows are pair-interleaved (rows 2j, 2j+1 of a head = elements j,
+// j + D/2), the accumulators are rounded to the model dtype (as the unfused
+// projection stores them), rotated, and written to q, k, v [M, heads, D].
+constexpr int EPI_ROPE_QKV = 16;
+struct RopeArgs {
+  const int32_t* pos;
+  double log2_base;
+  int Hq, Hkv, D;
+  bf16_t* q;
+  bf16_t* k;
+  bf16_t* v;
+};
+
 #ifndef MEDUSA_GEMM_XD_WR
 #define MEDUSA_GEMM_XD_WR 2  // weight groups in flight per wave (4 steps, 4 KB each)
 #endif
@@ -558,7 +572,7 @@ template <int MB, int WR, int EPI>
 __global__ __launch_bounds__(64 * XB_WAVES) void gemm_xdma_kernel(
     const bf16_t* __restrict__ X, int64_t xbs, int M, int Kd, const bf16_t* __restrict__ W, int Nw,
     const bf16_t* __restrict__ bias, const void* aux, void* Y, int y_f32, int G, int MT, int unit,
-    float* __restrict__ part) {
+    float* __restrict__ part, RopeArgs ra) {
   using T = bf16_t;
   constexpr int P16 = 8;                        // bf16 per 16 bytes
   constexpr int TM = 16 * MB;
@@ -570,7 +584,7 @@ __global__ __launch_bounds__(64 * XB_WAVES) void gemm_xdma_kernel(
   constexpr int LDE = TM + 1;
   constexpr int SMEM = 2 * XBUFB + XB_WAVES * WSLOTB;
   static_assert(XD >= 1 && XD * XB_WAVES * 1024 == XBUFB, "activation chunk must split into whole DMAs");
-  static_assert(XB_MAXB * 16 * LDE * 4 <= SMEM, "epilogue tile must fit");
+  static_assert(XB_MAXB * 16 * LDE * 4 + XB_MAXB * 8 * 8 <= SMEM, "epilogue tile (and pair table) must fit");
   static_assert(WR == 2 || WR == 3, "wait counts are worked out for rings of 2 and 3 groups");
   // Issue order per wave: prologue W(0) [.. W(WR-3)], X(0), W(WR-2), W(WR-1);
   // then per chunk q: X(q+1), group 2q, W(2q+WR), group 2q+1, W(2q+1+WR).
@@ -686,6 +700,39 @@ __global__ __launch_bounds__(64 * XB_WAVES) void gemm_xdma_kernel(
   __syncthreads();
 
   constexpr int NT = 64 * XB_WAVES;
+  if constexpr (EPI == EPI_ROPE_QKV) {
+    // pairs of adjacent columns; the pair frequencies of this range first
+    const int np = nb * 8;
+    const int qw = ra.Hq * ra.D, kw = ra.Hkv * ra.D, half = ra.D / 2;
+    double* invt = reinterpret_cast<double*>(smem + XB_MAXB * 16 * LDE * 4);
+    if (threadIdx.x < np)
+      invt[threadIdx.x] = rope_inv_freq(((b0 * 16 + 2 * threadIdx.x) % ra.D) / 2, ra.D, ra.log2_base);
+    __syncthreads();
+    for (int e = threadIdx.x; e < np * TM; e += NT) {
+      const int m = e / np, pl = e % np;
+      if (m0 + m >= M) continue;
+      const int n = b0 * 16 + 2 * pl;  // even column of qkv
+      const float x1 = bf2f(f2bf(ep[(2 * pl) * LDE + m]));
+      const float x2 = bf2f(f2bf(ep[(2 * pl + 1) * LDE + m]));
+      const int64_t row = m0 + m;
+      if (n < qw + kw) {
+        const bool isq = n < qw;
+        const int nh = isq ? n : n - qw;
+        const int hh = nh / ra.D, j = (nh % ra.D) / 2;
+        T* dst = isq ? ra.q + (row * ra.Hq + hh) * ra.D : ra.k + (row * ra.Hkv + hh) * ra.D;
+        float c, sn, y1, y2;
+        rope_cs(ra.pos[row], invt[pl], c, sn);
+        rope_rot(x1, x2, c, sn, y1, y2);
+        dst[j] = f2bf(y1);
+        dst[j + half] = f2bf(y2);
+      } else {
+        T* dst = ra.v + row * kw + (n - qw - kw);
+        dst[0] = f2bf(x1);
+        dst[1] = f2bf(x2);
+      }
+    }
+    return;
+  }
   if (S > 1) {  // fp32 partials [batch][S][M][N]; the split reducer applies the epilogue
     const int nn = nb * 16;
     float* pp = part + ((int64_t)gi * S + sp) * M * Nw;
@@ -936,10 +983,10 @@ static bool launch_gemm_t(const void* X, int64_t xbs, int64_t M, int64_t Kd, con
       if (MEDUSA_GEMM_XB_DMA) {
         if (M <= 32)
           hipLaunchKernelGGL((gemm_xdma_kernel<2, MEDUSA_GEMM_XD_WR, EPI>), grid, dim3(64 * XB_WAVES), 0, st, Xt, xbs,
-                             (int)M, (int)Kd, Wt, (int)Nw, Bt, aux, Y, y_f32, plan.xb_G, plan.MT, plan.xb_unit, part);
+                             (int)M, (int)Kd, Wt, (int)Nw, Bt, aux, Y, y_f32, plan.xb_G, plan.MT, plan.xb_unit, part, RopeArgs{});
         else
           hipLaunchKernelGGL((gemm_xdma_kernel<4, MEDUSA_GEMM_XD_WR, EPI>), grid, dim3(64 * XB_WAVES), 0, st, Xt, xbs,
-                             (int)M, (int)Kd, Wt, (int)Nw, Bt, aux, Y, y_f32, plan.xb_G, plan.MT, plan.xb_unit, part);
+                             (int)M, (int)Kd, Wt, (int)Nw, Bt, aux, Y, y_f32, plan.xb_G, plan.MT, plan.xb_unit, part, RopeArgs{});
         if (plan.xb_S > 1) {
           if (EPI == MEDUSA_EPI_RES_ADD_F32 && norm) {
             hipLaunchKernelGGL(split_reduce_rmsnorm_kernel<T>, dim3((unsigned)M), dim3(256), 0, st, part,
@@ -1105,4 +1152,78 @@ extern "C" int32_t medusa_linear_rmsnorm(const void* X, int64_t M, int64_t Kd, c
     return medusa_rmsnorm(x, M, N, gain, eps, dt, out, stream);
   }
   return check_launch("medusa_linear_rmsnorm");
+}
+
+namespace medusa_host {
+void launch_qkv_rope_pairs(const void* qkv, int64_t M, int Hq, int Hkv, int D, const int32_t* pos,
+                           double log2_base, int dt, void* q, void* k, void* v, hipStream_t st);
+// the fused epilogue runs where the projection takes the unsplit DMA block-range kernel
+static bool qkv_rope_fused(int64_t M, int64_t Kd, int64_t N, int dt) {
+  const GemmPlan p = gemm_plan(M, Kd, N, dt, MEDUSA_EPI_NONE);
+  return MEDUSA_GEMM_XB_DMA && dt == MEDUSA_BF16 && p.xb && p.xb_S == 1;
+}
+}  // namespace medusa_host
+
+extern "C" size_t medusa_linear_qkv_rope_ws(int64_t M, int64_t Kd, int32_t Hq, int32_t Hkv,
+                                            int32_t D, int32_t dt) {
+  using namespace medusa_host;
+  if (M <= 0 || Kd <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0) return 0;
+  const int64_t N = (int64_t)(Hq + 2 * Hkv) * D;
+  if (qkv_rope_fused(M, Kd, N, dt)) return 0;
+  const size_t es = dt == MEDUSA_BF16 ? 2 : 4;
+  return align_up((size_t)M * N * es, 256) + gemm_ws_bytes(M, Kd, N, 1, dt);
+}
+
+extern "C" int32_t medusa_linear_qkv_rope(const void* X, int64_t M, int64_t Kd, const void* W,
+                                          int32_t Hq, int32_t Hkv, int32_t D, const int32_t* pos,
+                                          float base, int32_t dt, void* q, void* k, void* v,
+                                          void* ws, size_t ws_bytes, void* stream) {
+  using namespace medusa_host;
+  MEDUSA_REQUIRE(dt == MEDUSA_F32 || dt == MEDUSA_BF16, MEDUSA_ERR_UNSUPPORTED,
+                 "medusa_linear_qkv_rope: unknown dtype %d", dt);
+  MEDUSA_REQUIRE(M >= 0 && Kd > 0 && M <= INT32_MAX && Kd <= INT32_MAX && Hq >= 1 && Hkv >= 1 &&
+                     base > 1.f,
+                 MEDUSA_ERR_INVALID_ARG, "medusa_linear_qkv_rope: bad sizes or base");
+  MEDUSA_REQUIRE(D >= 8 && D <= 128 && D % 8 == 0, MEDUSA_ERR_UNSUPPORTED,
+                 "medusa_linear_qkv_rope: head dim %d (multiple of 8 up to 128)", D);
+  const int p16 = dt == MEDUSA_BF16 ? 8 : 4;
+  MEDUSA_REQUIRE(Kd % p16 == 0, MEDUSA_ERR_UNSUPPORTED,
+                 "medusa_linear_qkv_rope: Kd must be a multiple of %d", p16);
+  if (M == 0) return MEDUSA_OK;
+  MEDUSA_REQUIRE(X && W && pos && q && k && v, MEDUSA_ERR_INVALID_ARG,
+                 "medusa_linear_qkv_rope: NULL pointer");
+  MEDUSA_REQUIRE(((uintptr_t)X | (uintptr_t)W | (uintptr_t)v) % 16 == 0, MEDUSA_ERR_INVALID_ARG,
+                 "medusa_linear_qkv_rope: X, W and v must be 16-byte aligned");
+  const int64_t N = (int64_t)(Hq + 2 * Hkv) * D;
+  const size_t need = medusa_linear_qkv_rope_ws(M, Kd, Hq, Hkv, D, dt);
+  MEDUSA_REQUIRE(need == 0 || (ws != NULL && ws_bytes >= need), MEDUSA_ERR_WORKSPACE,
+                 "medusa_linear_qkv_rope: workspace %zu < %zu bytes", ws_bytes, need);
+  MEDUSA_REQUIRE(need == 0 || (uintptr_t)ws % 256 == 0, MEDUSA_ERR_INVALID_ARG,
+                 "medusa_linear_qkv_rope: ws must be 256-byte aligned");
+  hipStream_t st = (hipStream_t)stream;
+  const double lb = log2((double)base);
+  if (qkv_rope_fused(M, Kd, N, dt)) {
+    using namespace medusa;
+    const GemmPlan plan = gemm_plan(M, Kd, N, dt, MEDUSA_EPI_NONE);
+    const dim3 grid((unsigned)plan.xb_G, (unsigned)plan.MT, 1u);
+    const RopeArgs ra{pos, lb, Hq, Hkv, D, (bf16_t*)q, (bf16_t*)k, (bf16_t*)v};
+    const bf16_t* Xt = (const bf16_t*)X;
+    const bf16_t* Wt = (const bf16_t*)W;
+    if (M <= 32)
+      hipLaunchKernelGGL((gemm_xdma_kernel<2, MEDUSA_GEMM_XD_WR, EPI_ROPE_QKV>), grid, dim3(64 * XB_WAVES), 0, st,
+                         Xt, (int64_t)0, (int)M, (int)Kd, Wt, (int)N, (const bf16_t*)nullptr, nullptr, nullptr, 0,
+                         plan.xb_G, plan.MT, 1, (float*)nullptr, ra);
+    else
+      hipLaunchKernelGGL((gemm_xdma_kernel<4, MEDUSA_GEMM_XD_WR, EPI_ROPE_QKV>), grid, dim3(64 * XB_WAVES), 0, st,
+                         Xt, (int64_t)0, (int)M, (int)Kd, Wt, (int)N, (const bf16_t*)nullptr, nullptr, nullptr, 0,
+                         plan.xb_G, plan.MT, 1, (float*)nullptr, ra);
+    return check_launch("medusa_linear_qkv_rope");
+  }
+  // projection into scratch (pair layout), then the rotary pass over it
+  const size_t es = dt == MEDUSA_BF16 ? 2 : 4;
+  char* qkv = (char*)ws;
+  void* gws = qkv + align_up((size_t)M * N * es, 256);
+  launch_gemm(X, 0, M, Kd, W, N, 1, dt, MEDUSA_EPI_NONE, nullptr, nullptr, qkv, 0, gws, st);
+  launch_qkv_rope_pairs(qkv, M, Hq, Hkv, D, pos, lb, dt, q, k, v, st);
+  return check_launch("medusa_linear_qkv_rope");
 }

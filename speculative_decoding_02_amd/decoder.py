@@ -49,17 +49,21 @@ class DeviceModel:
                 device=self.device, dtype=dtype)
             t = dict(embed=up(src.embed), g_final=up(src.g_final), lm_head=up(src.lm_head),
                      w1=up(src.w1), b1=up(src.b1), w2=up(src.w2), layers=[])
+            Hq, Hkv, D = src.n_heads, src.n_kv_heads, src.head_dim
             for L in src.layers:
                 t["layers"].append(dict(
-                    wqkv=up(np.concatenate([L["wq"], L["wk"], L["wv"]], axis=0)), wo=up(L["wo"]),
+                    wqkv_rp=up(np.concatenate([M.interleave_rope_pairs(L["wq"], Hq, D),
+                                               M.interleave_rope_pairs(L["wk"], Hkv, D), L["wv"]],
+                                              axis=0)),
+                    wo=up(L["wo"]),
                     wgu=up(interleave_gate_up(L["wg"], L["wu"])), wd=up(L["wd"]),
                     g_attn=up(L["g_attn"]), g_mlp=up(L["g_mlp"])))
             tensors = t
         self.meta = meta
         self.t = tensors
-        if "wqkv" not in tensors["layers"][0]:  # Llama layout -> GPU layout (one-time copy)
+        if "wqkv_rp" not in tensors["layers"][0]:  # Llama layout -> GPU layout (one-time copy)
             self.t = dict(tensors)
-            self.t["layers"] = [self._gpu_layout(L) for L in tensors["layers"]]
+            self.t["layers"] = [self._gpu_layout(L, meta) for L in tensors["layers"]]
         for k, v in meta.items():
             if k != "seed":
                 setattr(self, k, v)
@@ -67,11 +71,17 @@ class DeviceModel:
 
 
     @staticmethod
-    def _gpu_layout(L):
+    def _gpu_layout(L, meta):
+        """QKV rows concatenated with the q and k heads pair-interleaved (for the
+        projection with rotary positions fused), gate/up interleaved in 16-row
+        blocks (for the SwiGLU epilogue)."""
         wg, wu = L["wg"], L["wu"]
         F, H = wg.shape
         wgu = torch.stack([wg.reshape(F // 16, 16, H), wu.reshape(F // 16, 16, H)], 1)
-        return dict(wqkv=torch.cat([L["wq"], L["wk"], L["wv"]], 0).contiguous(), wo=L["wo"],
+        D = meta["head_dim"]
+        wqkv = torch.cat([M.interleave_rope_pairs(L["wq"], meta["n_heads"], D),
+                          M.interleave_rope_pairs(L["wk"], meta["n_kv_heads"], D), L["wv"]], 0)
+        return dict(wqkv_rp=wqkv.contiguous(), wo=L["wo"],
                     wgu=wgu.reshape(2 * F, H).contiguous(), wd=L["wd"], g_attn=L["g_attn"],
                     g_mlp=L["g_mlp"])
 
@@ -136,6 +146,10 @@ class MedusaDecoder:
         shapes = [(H, qkv_n), (model.n_heads * model.head_dim, H), (H, 2 * F), (F, H), (H, V)]
         self.lin_ws = M._ws(max([M.linear_ws_bytes(n, kd, nn, 1, dt) for n in range(1, 65)
                                  for kd, nn in shapes] + [256]), dev)
+        self.qkv_ws = M._ws(max([M._lib.medusa_linear_qkv_rope_ws(n, H, model.n_heads,
+                                                                  model.n_kv_heads,
+                                                                  model.head_dim, dt)
+                                 for n in range(1, 65)] + [256]), dev)
         self.out = (torch.zeros(1, **i32), torch.zeros((1, self.K + 1), **i32), torch.zeros(1, **i32))
         self.new_ctx = torch.zeros(1, **i32)
         self.src = torch.zeros((1, self.K + 1), **i32)
@@ -154,9 +168,9 @@ class MedusaDecoder:
         layers = t["layers"]
         h = M.medusa_rmsnorm(x, layers[0]["g_attn"], m.eps, m.dtype)
         for li, L in enumerate(layers):
-            qkv = M.medusa_linear(h, L["wqkv"], ws=self.lin_ws)
-            q, k, v = M.medusa_qkv_rope(qkv, m.n_heads, m.n_kv_heads, m.head_dim, pos.reshape(-1),
-                                        m.rope_base)
+            q, k, v = M.medusa_linear_qkv_rope(h, L["wqkv_rp"], m.n_heads, m.n_kv_heads,
+                                               m.head_dim, pos.reshape(-1), m.rope_base,
+                                               ws=self.qkv_ws)
             o = M.medusa_tree_attention(q[None], k[None], v[None], self.Kc[li], self.Vc[li],
                                         self.page_table, self.ctx, self.max_ctx,
                                         mask, scale, ws=self.attn_ws)

@@ -12,6 +12,7 @@ from __future__ import annotations
 import ctypes as C
 import os
 
+import numpy as np
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -46,6 +47,9 @@ _SIGS = {
     "medusa_embed": (i32, [vp, i64, vp, i64, i64, i32, vp, vp]),
     "medusa_rmsnorm": (i32, [vp, i64, i64, vp, f32, i32, vp, vp]),
     "medusa_linear_rmsnorm": (i32, [vp, i64, i64, vp, i64, i32, vp, vp, f32, vp, vp, sz, vp]),
+    "medusa_linear_qkv_rope_ws": (sz, [i64, i64, i32, i32, i32, i32]),
+    "medusa_linear_qkv_rope": (i32, [vp, i64, i64, vp, i32, i32, i32, vp, f32, i32, vp, vp, vp, vp,
+                                     sz, vp]),
     "medusa_qkv_rope": (i32, [vp, i64, i32, i32, i32, vp, f32, i32, vp, vp, vp, vp]),
     "medusa_swiglu": (i32, [vp, i64, i64, i32, vp, vp]),
     "medusa_gather_rows": (i32, [vp, i32, i32, i64, vp, vp, i32, i32, vp, vp]),
@@ -292,6 +296,32 @@ def medusa_linear_rmsnorm(X, W, x, gain, eps, out=None, ws=None):
         _p(X), M, Kd, _p(W), N, dt, _p(x), _p(gain), float(eps), _p(out),
         _p(ws) if need else None, ws.numel() if need else 0, _stream()))
     return out
+
+
+def interleave_rope_pairs(w, heads, D):
+    """Rows of ``heads`` heads of D -> pair-interleaved: row 2j of a head takes
+    row j, row 2j+1 takes row j + D/2 (numpy or torch, [heads*D, ...])."""
+    lead = w.shape[1:]
+    x = w.reshape(heads, 2, D // 2, *lead)
+    if isinstance(w, np.ndarray):
+        return np.swapaxes(x, 1, 2).reshape(heads * D, *lead)
+    return x.transpose(1, 2).reshape(heads * D, *lead).contiguous()
+
+
+def medusa_linear_qkv_rope(X, W, Hq, Hkv, D, pos, base, q=None, k=None, v=None, ws=None):
+    """q, k, v of the pair-interleaved QKV weight W (see interleave_rope_pairs), rotated."""
+    M, Kd = X.shape
+    dev, dt = X.device, W.dtype
+    q = q if q is not None else torch.empty((M, Hq, D), dtype=dt, device=dev)
+    k = k if k is not None else torch.empty((M, Hkv, D), dtype=dt, device=dev)
+    v = v if v is not None else torch.empty((M, Hkv, D), dtype=dt, device=dev)
+    need = _lib.medusa_linear_qkv_rope_ws(M, Kd, Hq, Hkv, D, _dt(W))
+    if need and (ws is None or ws.numel() < need):
+        ws = _ws(need, dev)
+    _check("medusa_linear_qkv_rope", _lib.medusa_linear_qkv_rope(
+        _p(X), M, Kd, _p(W), Hq, Hkv, D, _p(pos), float(base), _dt(W), _p(q), _p(k), _p(v),
+        _p(ws) if need else None, ws.numel() if need else 0, _stream()))
+    return q, k, v
 
 
 def medusa_qkv_rope(qkv, Hq, Hkv, D, pos, base, q=None, k=None, v=None):

@@ -133,6 +133,49 @@ def test_linear_rmsnorm(lib, dt, Mr, Kd, N):
     assert_close(host(out), orc.rmsnorm(xr, gain, 1e-5), TOL[dt], "norm vs oracle")
 
 
+@pytest.mark.parametrize("dt,Mr,Kd,Hq,Hkv,D", [
+    (torch.bfloat16, 64, 512, 32, 32, 128),   # wide block ranges: rotation in the epilogue
+    (torch.bfloat16, 20, 256, 16, 8, 128),    # 32-row tiles, grouped kv heads: epilogue
+    (torch.bfloat16, 48, 512, 32, 32, 64),    # head dim 64: epilogue
+    (torch.bfloat16, 64, 4096, 8, 8, 128),    # split contraction: projection, then rotary pass
+    (torch.bfloat16, 1, 512, 32, 32, 128),    # one row: projection, then rotary pass
+    (torch.float32, 13, 256, 4, 2, 64)],
+    ids=["epi_wide", "epi_32rows", "epi_d64", "split", "onerow", "f32"])
+def test_linear_qkv_rope(lib, dt, Mr, Kd, Hq, Hkv, D):
+    """QKV projection with rotary positions fused, on the pair-interleaved
+    weight: bit for bit the plain projection + medusa_qkv_rope, and close to
+    the oracle's rotary embedding."""
+    case(f"linear+qkv_rope {DTN[dt]} M={Mr} Kd={Kd} Hq={Hq} Hkv={Hkv} D={D}")
+    g = synth.rngs(Mr + Kd + Hq * D, 3)
+    N = (Hq + 2 * Hkv) * D
+    X = _rnd(dt, g[0].standard_normal((Mr, Kd), dtype=np.float32))
+    W = _rnd(dt, g[1].standard_normal((N, Kd), dtype=np.float32) * 0.05)
+    pos = g[2].integers(0, 6000, Mr).astype(np.int32)
+    Wp = np.concatenate([lib.interleave_rope_pairs(W[:Hq * D], Hq, D),
+                         lib.interleave_rope_pairs(W[Hq * D:(Hq + Hkv) * D], Hkv, D),
+                         W[(Hq + Hkv) * D:]], 0)
+    q, k, v = lib.medusa_linear_qkv_rope(dev(X, dt), dev(Wp, dt), Hq, Hkv, D, dev(pos), 10000.0)
+    qkv = lib.medusa_linear(dev(X, dt), dev(W, dt))
+    q0, k0, v0 = lib.medusa_qkv_rope(qkv, Hq, Hkv, D, dev(pos), 10000.0)
+    assert torch.equal(q, q0) and torch.equal(k, k0) and torch.equal(v, v0), \
+        "fused projection + rotary differs from the unfused pair"
+    # the projection is stored in dt before the rotation (as in the unfused
+    # pair), so an output's error scales with its pair's inputs |x_j| + |x_j+D/2|
+    y = orc.linear(X, W)
+    tol = TOL[dt] if dt == torch.bfloat16 else 2e-4 * max(1, np.sqrt(Kd / 256))
+
+    def check(got, xh, what):
+        ref = orc.rope(xh, pos, 10000.0)
+        s = np.abs(xh[..., :D // 2]) + np.abs(xh[..., D // 2:])
+        bound = tol * np.maximum(1.0, np.concatenate([s, s], -1))
+        err = np.abs(np.asarray(got, np.float64) - ref)
+        assert np.all(err <= bound), f"{what}: worst err/bound {np.max(err / bound):.3f}"
+
+    check(host(q), y[:, :Hq * D].reshape(Mr, Hq, D), "q")
+    check(host(k), y[:, Hq * D:(Hq + Hkv) * D].reshape(Mr, Hkv, D), "k")
+    assert_close_stored(host(v), y[:, (Hq + Hkv) * D:].reshape(Mr, Hkv, D), tol, "v")
+
+
 # ------------------------------------------------------------------- heads ---
 @pytest.mark.parametrize("H,V,Mr", [(256, 1000, 4), (256, 8192, 64), (512, 16384, 24)])
 def test_heads_zero_init_reproduces_lm_head_bitwise(lib, H, V, Mr):
