@@ -33,6 +33,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "accepted tokens/s + tree-attn HBM GB/s (% peak), 7B-shape, 64-node tree"
 HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = 2500.0  # dense bf16
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_7b_counters.md")
 
 
@@ -133,6 +134,98 @@ def tree_attention_c2(torch, M, synth, reps=10, copies=17):
                 kv_copies_rotated=copies, rotated_mb=round(copies * 2 * c["kc_bytes"] / 1e6, 1))
 
 
+def heads_c3(torch, M, rows, reps=10):
+    """The five Medusa heads + per-head top-10 at the 7B shape (H 4096, V 32000)
+    on ``rows`` hidden rows: stage 1 (residual SiLU layer), stage 2 (vocabulary
+    projection, fp32 logits kept in the workspace), top-k."""
+    K, H, V, k = 5, 4096, 32000, 10
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(3)
+    bf = torch.bfloat16
+    X = torch.randn((rows, H), generator=gen, device="cuda").to(bf)
+    W1 = torch.randn((K, H, H), generator=gen, device="cuda").mul_(0.01).to(bf)
+    b1 = torch.randn((K, H), generator=gen, device="cuda").mul_(0.01).to(bf)
+    W2 = torch.randn((K, V, H), generator=gen, device="cuda").mul_(0.02).to(bf)
+    ids = torch.empty((K, rows, k), dtype=torch.int32, device="cuda")
+    vals = torch.empty((K, rows, k), dtype=torch.float32, device="cuda")
+    ws = M._ws(M._lib.medusa_heads_ws(rows, H, K, V, k, M.BF16), "cuda")
+    call = lambda: M.medusa_heads(X, W1, b1, W2, topk=k, ids=ids, vals=vals, ws=ws, want_logits=False)
+    us, us_med = graph_time_us(torch, [call], reps=reps, inner=2)
+    nbytes = K * (H * H * 2 + H * 2 + V * H * 2) + rows * H * 2 + K * rows * k * 8
+    flops = 2.0 * rows * K * (H * H + V * H)
+    gbs = nbytes / (us * 1e-6) / 1e9
+    tf = flops / (us * 1e-6) / 1e12
+    out = dict(workload=f"5 heads, H 4096, V 32000, {rows} rows, top-10, bf16",
+               us=round(us, 2), us_median=round(us_med, 2), bytes=nbytes, gbs=round(gbs, 1),
+               hbm_frac=round(gbs / HBM_PEAK_GBS, 4), tflops=round(tf, 1),
+               mfma_frac=round(tf / MFMA_PEAK_TFLOPS, 4), rows_per_s=round(rows / (us * 1e-6), 1),
+               timing="HIP events around graph replays")
+    del X, W1, b1, W2, ws
+    torch.cuda.empty_cache()
+    return out
+
+
+def batched_attention_c5(torch, M, synth, reps=5):
+    """Batched tree verification attention over a 13B-shaped stack: 16
+    sequences of U{256..4096} cached tokens (seeded), 40 heads x 128, 16-token
+    pages in a seeded permuted order, each sequence its own pruned 64-node
+    tree; 40 layer launches, alternating over two layer pools (each larger
+    than the 256 MB MALL, so every launch streams its KV from HBM)."""
+    import numpy as np
+    B, N, H, D, P, L = 16, 64, 40, 128, 16, 40
+    rng = np.random.default_rng(np.random.SeedSequence(5))
+    lens = rng.integers(256, 4097, B)
+    max_ctx = 4096
+    max_pages = (max_ctx + N + P - 1) // P
+    npg = [(int(l) + N + P - 1) // P for l in lens]
+    perm = rng.permutation(sum(npg))
+    pt = np.zeros((B, max_pages), np.int32)
+    o = 0
+    for b in range(B):
+        pt[b, :npg[b]] = perm[o:o + npg[b]]
+        o += npg[b]
+    parents, ranks = [], []
+    for b in range(B):
+        pa, ra = synth.prune_template(*synth.tree_template((4, 3, 2, 2, 1)), N, 100 + b)
+        parents.append(pa)
+        ranks.append(ra)
+    dev, bf = "cuda", torch.bfloat16
+    i32 = dict(dtype=torch.int32, device=dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(5)
+    pools = [(torch.randn((sum(npg), H, P, D), generator=gen, device=dev).to(bf),
+              torch.randn((sum(npg), H, P, D), generator=gen, device=dev).to(bf)) for _ in range(2)]
+    Q = torch.randn((B, N, H, D), generator=gen, device=dev).to(bf)
+    Kt = torch.randn((B, N, H, D), generator=gen, device=dev).to(bf)
+    Vt = torch.randn((B, N, H, D), generator=gen, device=dev).to(bf)
+    ctx = torch.tensor(lens.astype(np.int32), **i32)
+    _, _, mask = M.medusa_build_tree(torch.tensor(np.stack(parents), **i32), torch.tensor(np.stack(ranks), **i32),
+                                     torch.zeros(B, **i32), torch.zeros((5, B, 4), **i32), ctx)
+    ptab = torch.tensor(pt, **i32)
+    out = torch.empty_like(Q)
+    ws = M._ws(M.tree_attention_ws_bytes(B, N, H, H, D, max_ctx, P), dev)
+    scale = 1.0 / np.sqrt(D)
+    launches = [lambda li=li: M.medusa_tree_attention(Q, Kt, Vt, pools[li % 2][0], pools[li % 2][1], ptab, ctx,
+                                                      max_ctx, mask, scale, out=out, ws=ws)
+                for li in range(L)]
+    us, us_med = graph_time_us(torch, launches, reps=reps, inner=1)  # per launch
+    per_layer = int(sum(int(l) + N for l in lens)) * H * D * 2 * 2 + 2 * B * N * H * D * 2 + B * N * 8 \
+        + B * N * H * D * 2 * 2
+    gbs = per_layer / (us * 1e-6) / 1e9
+    stack_ms = us * L / 1000.0
+    res = dict(workload="16 sequences, cached U{256..4096} (seeded), 40 heads x 128, 40 layers, "
+                        "16-token pages in permuted order, 64-node tree each, bf16",
+               cached_tokens=[int(x) for x in lens], ms_per_stack=round(stack_ms, 3),
+               us_per_layer=round(us, 2), bytes_per_layer=per_layer, gbs=round(gbs, 1),
+               frac=round(gbs / HBM_PEAK_GBS, 4),
+               verified_tree_tokens_per_s=round(B * N / (stack_ms * 1e-3), 1),
+               timing="HIP events around graph replays of the 40 layer launches (two layer pools, "
+                      "alternating)")
+    del pools, Q, Kt, Vt, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(torch, dec, model_src, emitted_per_step, sample_layers):
     """The oracle, as is, on a bounded sample of one decode step (host cores)."""
     import numpy as np
@@ -229,6 +322,8 @@ def main():
     ap.add_argument("--cpu-sample-layers", type=int, default=4)
     ap.add_argument("--skip-c2", action="store_true")
     ap.add_argument("--skip-plain", action="store_true")
+    ap.add_argument("--skip-extra", action="store_true",
+                    help="skip the heads (64 and 1024 rows) and batched-attention measurements")
     ap.add_argument("--kernels-only", action="store_true",
                     help="run only the dominant projection kernel (32 launches over 7B-shaped "
                          "gate/up weights), the tree-attention launches and a 1 GiB copy, "
@@ -331,6 +426,13 @@ def main():
         del tdec
 
     c2 = None if args.skip_c2 else tree_attention_c2(torch, M, synth)
+    c3 = c3b = c5 = None
+    if not args.skip_extra:
+        log("[bench] heads at the 7B shape: 64 rows, then 1024 rows")
+        c3 = heads_c3(torch, M, 64)
+        c3b = heads_c3(torch, M, 1024, reps=3)
+        log("[bench] batched tree attention over a 13B-shaped stack")
+        c5 = batched_attention_c5(torch, M, synth)
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] CPU oracle baseline (bounded sample)")
@@ -359,6 +461,9 @@ def main():
                      "us_median": round(gu_med, 2),
                      "timing": "HIP events around graph replays of the 32 per-step launches"},
         "tree_attention": c2,
+        "heads_c3": c3,
+        "heads_c3b": c3b,
+        "batched_attention_c5": c5,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
