@@ -35,6 +35,7 @@ namespace medusa {
 
 constexpr int ATT_TILE = 64;
 constexpr int ATT_THREADS = 256;
+constexpr int ATT_THREADS2 = 512;  // two-group bf16 kernel
 constexpr int ATT_MAX_SPLIT_PAGES = 256;  // page-table window of one split (LDS)
 
 template <typename T, int D>
@@ -687,6 +688,302 @@ __global__ __launch_bounds__(ATT_THREADS) void tree_attention_dma_kernel(AttnArg
   }
 }
 
+// bf16 variant with two wave groups: eight waves, group g (waves 4g..4g+3,
+// 16 nodes each) takes the tiles t = g mod 2 of the split with its own
+// online-softmax state, so a workgroup runs half as many tile steps and every
+// SIMD holds two waves.  The K/V ring has two pair-slots (four tiles): at the
+// start of pair p each wave waits for its own DMA of pair p, a barrier makes
+// all of it visible and frees pair p-1's slot, pair p+1 is issued into that
+// slot and streams in while the groups compute tiles 2p and 2p+1.  After the
+// loop, group 1's (max, sum, output) go through LDS and group 0 merges them
+// (the same rescaling as the split merge), then writes the output or the
+// split's partials as the single-group kernel does.  Tile layout, swizzle,
+// operand reads, masking and the softmax are those of the single-group
+// kernel.
+template <int D, bool P2>
+__global__ __launch_bounds__(ATT_THREADS2) void tree_attention_dma2_kernel(AttnArgs a) {
+  using T = bf16_t;
+  constexpr int NWAVES = ATT_THREADS2 / 64;
+  constexpr int P16 = 8;                       // bf16 per 16 bytes
+  constexpr int ROWB = D * 2;                  // bytes per key row
+  constexpr int CPR = ROWB / 16;               // 16-byte chunks per row
+  constexpr int SW = CPR - 1;                  // swizzle mask
+  constexpr int TILEB = ATT_TILE * ROWB;       // bytes of one K (or V) tile
+  constexpr int SLOTB = 2 * TILEB;
+  constexpr int RING = 4;                      // tiles: two pair-slots
+  constexpr int RPD = 1024 / ROWB;             // rows per DMA instruction (64 lanes x 16 B)
+  constexpr int DPW = TILEB / 1024 / NWAVES;   // DMA instructions per wave per tensor
+  constexpr int QSTEPS = D / 32;
+  constexpr int DB = D / 16;
+  static_assert(DPW >= 1 && DPW * NWAVES * 1024 == TILEB, "tile must split into whole DMAs");
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[RING * SLOTB];
+  __shared__ int spages[ATT_MAX_SPLIT_PAGES];
+
+  const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int S = gridDim.x;
+  const int N = a.N;
+  const int k_beg = s * a.chunk;
+  const int group = a.Hq / a.Hkv;
+  const int kvh = h / group;
+  const bool appender = (h % group) == 0;
+  const int tid = threadIdx.x;
+  // wave index made provably uniform, so per-wave branches stay scalar
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+  const int grp = wave >> 2, wv = wave & 3;
+  const int node = wv * 16 + lr;
+  const bool wave_active = wv * 16 < N;
+  const int nodec = min(node, N - 1);
+
+  const T* Qp = reinterpret_cast<const T*>(a.Q);
+  const T* Ktp = reinterpret_cast<const T*>(a.Kt);
+  const T* Vtp = reinterpret_cast<const T*>(a.Vt);
+  T* Kcp = reinterpret_cast<T*>(a.Kc);
+  T* Vcp = reinterpret_cast<T*>(a.Vc);
+  const int* pt = a.page_table + (int64_t)b * a.max_pages;
+
+  // One round trip before the tile stream (length, page-table slice, queries, masks).
+  const int page0 = k_beg / a.P;
+  const int slice_end = min(k_beg + a.chunk, a.max_ctx + N);
+  const int npages = slice_end > k_beg ? (slice_end - 1) / a.P - page0 + 1 : 0;
+  const int ctxb = min(max(a.ctx[b], 0), a.max_ctx);
+  static_assert(ATT_MAX_SPLIT_PAGES <= ATT_THREADS2, "one page-table entry per thread");
+  const int my_page = threadIdx.x < npages ? pt[page0 + threadIdx.x] : 0;
+  u32x4 qf[QSTEPS];
+  {
+    const T* qrow = Qp + (((int64_t)b * N + nodec) * a.Hq + h) * D;
+#pragma unroll
+    for (int st = 0; st < QSTEPS; ++st)
+      qf[st] = *reinterpret_cast<const u32x4*>(qrow + st * 4 * P16 + lg * P16);
+  }
+  const uint64_t mrow = a.mask[(int64_t)b * N + nodec];
+  __builtin_amdgcn_s_waitcnt(0);
+  if (threadIdx.x < npages) spages[threadIdx.x] = my_page;
+  __syncthreads();
+  const int total = ctxb + N;
+  if (k_beg >= total) return;  // uniform over the workgroup
+  const int k_end = min(k_beg + a.chunk, total);
+  const int ntiles = (k_end - k_beg + ATT_TILE - 1) / ATT_TILE;
+  const int npairs = (ntiles + 1) / 2;
+
+  const int64_t page_elems = (int64_t)a.Hkv * a.P * D;  // one page of the cache
+  const int head_elems = kvh * a.P * D;                  // this head's rows in a page
+  auto cache_off = [&](int j) -> int64_t {
+    const int pj = P2 ? (j >> a.lp) : j / a.P;
+    const int sj = P2 ? (j & (a.P - 1)) : j - pj * a.P;
+    const int page = spages[pj - page0];
+    return (int64_t)page * page_elems + (head_elems + sj * D);
+  };
+  const int64_t tree_base = ((int64_t)b * N * a.Hkv + kvh) * D;
+  auto tree_off = [&](int j) -> int64_t {
+    return tree_base + max(j - ctxb, 0) * (a.Hkv * D);
+  };
+
+  const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)lds;
+  // DMA of tile t (clamped to the split's last tile) into ring slot `slot`;
+  // branch-free addressing as in the single-group kernel
+  auto issue = [&](int t, int slot) {
+    const int tile0 = k_beg + min(t, ntiles - 1) * ATT_TILE;
+    int jj[DPW], pg[DPW];
+#pragma unroll
+    for (int i = 0; i < DPW; ++i) {
+      const int r = (wave * DPW + i) * RPD + lane / CPR;  // tile row this lane fills
+      jj[i] = min(tile0 + r, k_end - 1);
+      pg[i] = spages[(P2 ? (jj[i] >> a.lp) : jj[i] / a.P) - page0];
+    }
+#pragma unroll
+    for (int i = 0; i < DPW; ++i) {
+      const int q = wave * DPW + i;          // 1 KB block of the tile
+      const int r = q * RPD + lane / CPR;
+      const int c = (lane % CPR) ^ (r & SW); // chunk fetched for that position
+      const int j = jj[i];
+      const bool cached = j < ctxb;
+      const int sj = P2 ? (j & (a.P - 1)) : j - (j / a.P) * a.P;
+      const int64_t coff = (int64_t)(uint32_t)pg[i] * page_elems + (head_elems + sj * D);
+      const int64_t off = (cached ? coff : tree_off(j)) + c * P16;
+      const T* ksrc = (cached ? Kcp : Ktp) + off;
+      const T* vsrc = (cached ? Vcp : Vtp) + off;
+      const uint32_t kd = lds_base + slot * SLOTB + q * 1024;
+      lds_dma16(ksrc, kd);
+      lds_dma16(vsrc, kd + TILEB);
+    }
+  };
+
+  f32x4 oacc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float mrun = -INFINITY, lrun = 0.f;
+
+  issue(0, 0);
+  issue(1, 1);
+  for (int p = 0; p < npairs; ++p) {
+    __builtin_amdgcn_s_waitcnt(0);              // this wave's DMA of pair p is done
+    __builtin_amdgcn_s_barrier();               // ... and every other wave's; pair p-1 is read
+    asm volatile("" ::: "memory");              // no LDS access moves across the barrier
+    const int nxt = ((p + 1) & 1) * 2;          // pair p+1 goes into pair p-1's slots
+    issue(2 * p + 2, nxt);
+    issue(2 * p + 3, nxt + 1);
+    const int t = 2 * p + grp;
+    const int slot = (p & 1) * 2 + grp;
+    const int tile0 = k_beg + t * ATT_TILE;
+    const unsigned char* ks = lds + slot * SLOTB;
+    const unsigned char* vs = ks + TILEB;
+    if (wave_active && t < ntiles) {
+      f32x4 sacc[4];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        sacc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const int r = kb * 16 + lr;
+#pragma unroll
+        for (int st = 0; st < QSTEPS; ++st) {
+          const int c = (st * 4 + lg) ^ (r & SW);
+          const u32x4 kf = *reinterpret_cast<const u32x4*>(ks + r * ROWB + c * 16);
+          sacc[kb] = mfma_bf16_16x16x32(kf, qf[st], sacc[kb]);
+        }
+      }
+      float x[4][4];
+      float tmax = -INFINITY;
+      // a tile wholly inside the cached keys needs no mask (wave-uniform)
+      const bool plain = tile0 + ATT_TILE <= min(ctxb, k_end);
+      if (plain) {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            x[kb][r] = sacc[kb][r] * a.scale_log2;
+            tmax = fmaxf(tmax, x[kb][r]);
+          }
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int j = tile0 + kb * 16 + lg * 4 + r;
+            const uint32_t bit = (uint32_t)(mrow >> (uint32_t)min(max(j - ctxb, 0), 63)) & 1u;
+            const bool ok = (j < k_end) & ((j < ctxb) | (bit != 0u));
+            x[kb][r] = ok ? sacc[kb][r] * a.scale_log2 : -INFINITY;
+            tmax = fmaxf(tmax, x[kb][r]);
+          }
+      }
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+      const float mnew = fmaxf(mrun, tmax);
+      const float alpha = (mnew == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(mrun - mnew);
+      float psum = 0.f;
+      if (plain) {  // every score finite, so mnew is too
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            x[kb][r] = __builtin_amdgcn_exp2f(x[kb][r] - mnew);
+            psum += x[kb][r];
+          }
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float p = (x[kb][r] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(x[kb][r] - mnew);
+            x[kb][r] = p;
+            psum += p;
+          }
+      }
+      lrun = lrun * alpha + psum;
+      mrun = mnew;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        u32x2 pb;
+        pb.x = pack_bf2(x[kb][0], x[kb][1]);
+        pb.y = pack_bf2(x[kb][2], x[kb][3]);
+        const int rr = kb * 16 + 4 * lg + (lr >> 2);  // source row of this lane's address
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const int c = db * 2 + ((lr & 3) >> 1);
+          const unsigned char* src = vs + rr * ROWB + ((c ^ (rr & SW)) * 16) + (lr & 1) * 8;
+          typedef short s4 __attribute__((ext_vector_type(4)));
+          const s4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4*)src);
+          oacc[db] = mfma_bf16_16x16x16(__builtin_bit_cast(u32x2, v), pb, oacc[db]);
+        }
+      }
+    }
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(WAITCNT_LGKM0);  // this wave's LDS reads of pair p are done
+  }
+  __builtin_amdgcn_s_waitcnt(0);               // drain the clamped refills before leaving
+
+  // Store the tree keys' K/V of this split into cache slots ctx..ctx+N-1.
+  if (appender && k_end > ctxb) {
+    constexpr int CPRT = D / P16;
+    const int j0 = max(k_beg, ctxb);
+    const int items = (k_end - j0) * CPRT * 2;
+    for (int e = tid; e < items; e += ATT_THREADS2) {
+      const int which = e / ((k_end - j0) * CPRT), rem = e % ((k_end - j0) * CPRT);
+      const int j = j0 + rem / CPRT, part = rem % CPRT;
+      const T* src = (which ? Vtp : Ktp) + tree_off(j) + part * P16;
+      T* dst = (which ? Vcp : Kcp) + cache_off(j) + part * P16;
+      *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src);
+    }
+  }
+
+  // merge group 1 into group 0 (per node: max and sum per lane; output dims
+  // db*16 + lg*4 + r of this lane)
+  float ltot = lrun + __shfl_xor(lrun, 16, 64);
+  ltot = ltot + __shfl_xor(ltot, 32, 64);
+  __syncthreads();                             // the ring is free now
+  float* xch = reinterpret_cast<float*>(lds);  // [4 waves][64 lanes][DB*4 + 2]
+  constexpr int XW = DB * 4 + 2;
+  if (grp == 1) {
+    float* d = xch + (wv * 64 + lane) * XW;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) d[db * 4 + r] = oacc[db][r];
+    d[DB * 4] = mrun;
+    d[DB * 4 + 1] = ltot;
+  }
+  __syncthreads();
+  if (grp == 1) return;
+  {
+    const float* d = xch + (wv * 64 + lane) * XW;
+    const float m1 = d[DB * 4], l1 = d[DB * 4 + 1];
+    const float mm = fmaxf(mrun, m1);
+    const float w0 = mrun == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mrun - mm);
+    const float w1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - mm);
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) oacc[db][r] = oacc[db][r] * w0 + d[db * 4 + r] * w1;
+    ltot = ltot * w0 + l1 * w1;
+    mrun = mm;
+  }
+  const bool node_ok = wave_active && node < N;
+  if (S == 1) {
+    if (node_ok) {
+      const float inv = 1.f / ltot;
+      T* orow = reinterpret_cast<T*>(a.O) + (((int64_t)b * N + node) * a.Hq + h) * D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) st<T>(orow, db * 16 + lg * 4 + r, oacc[db][r] * inv);
+    }
+    return;
+  }
+  const int64_t bh = (int64_t)b * a.Hq + h;
+  if (node_ok) {
+    _Float16* op = reinterpret_cast<_Float16*>(a.opart) + ((bh * S + s) * N + node) * D;
+    const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+    typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      h4 v = {(_Float16)(oacc[db][0] * inv), (_Float16)(oacc[db][1] * inv), (_Float16)(oacc[db][2] * inv),
+              (_Float16)(oacc[db][3] * inv)};
+      *reinterpret_cast<h4*>(op + db * 16 + lg * 4) = v;
+    }
+    if (lg == 0) a.ml[(bh * S + s) * N + node] = make_float2(mrun, ltot);
+  }
+}
+
 // Merge of the split partials of one (sequence, head): O = sum_s w_s l_s o_s
 // / sum_s w_s l_s with w_s = 2^(m_s - max m) and o_s the split's normalised
 // output, splits in index order.  One
@@ -769,6 +1066,10 @@ struct SplitPlan {
 };
 #ifndef MEDUSA_ATTN_DMA_WGS
 #define MEDUSA_ATTN_DMA_WGS 256
+#endif
+// bf16 attention with two wave groups on alternating tiles (1) or one group (0)
+#ifndef MEDUSA_ATTN_PAIRS
+#define MEDUSA_ATTN_PAIRS 1
 #endif
 #ifndef MEDUSA_ATTN_DMA_R
 #define MEDUSA_ATTN_DMA_R 3
@@ -873,6 +1174,22 @@ extern "C" int32_t medusa_tree_attention(const void* Q, const void* Kt, const vo
   constexpr int RD = MEDUSA_ATTN_DMA_R;
   if (dt == MEDUSA_BF16) {
     const bool p2 = a.lp >= 0;
+    if (MEDUSA_ATTN_PAIRS) {
+      const dim3 blk2(medusa::ATT_THREADS2);
+#define MEDUSA_ATT_LAUNCH2(KERNEL, DD)                                                       \
+  do {                                                                                       \
+    hipLaunchKernelGGL((KERNEL), grid, blk2, 0, st, a);                                      \
+    if (p.splits > 1)                                                                        \
+      hipLaunchKernelGGL((medusa::tree_attention_combine_kernel<medusa::bf16_t, DD>), cgrid, blk, 0, st, \
+                         a, p.splits);                                                       \
+  } while (0)
+      if (D == 128 && p2) MEDUSA_ATT_LAUNCH2((medusa::tree_attention_dma2_kernel<128, true>), 128);
+      else if (D == 128) MEDUSA_ATT_LAUNCH2((medusa::tree_attention_dma2_kernel<128, false>), 128);
+      else if (p2) MEDUSA_ATT_LAUNCH2((medusa::tree_attention_dma2_kernel<64, true>), 64);
+      else MEDUSA_ATT_LAUNCH2((medusa::tree_attention_dma2_kernel<64, false>), 64);
+#undef MEDUSA_ATT_LAUNCH2
+      return check_launch("medusa_tree_attention");
+    }
     if (D == 128 && p2) MEDUSA_ATT_LAUNCH((medusa::tree_attention_dma_kernel<128, RD, true>), medusa::bf16_t, 128);
     else if (D == 128) MEDUSA_ATT_LAUNCH((medusa::tree_attention_dma_kernel<128, RD, false>), medusa::bf16_t, 128);
     else if (p2) MEDUSA_ATT_LAUNCH((medusa::tree_attention_dma_kernel<64, 2 * RD, true>), medusa::bf16_t, 64);
