@@ -35,7 +35,6 @@ namespace medusa {
 
 constexpr int ATT_TILE = 64;
 constexpr int ATT_THREADS = 256;
-constexpr int ATT_THREADS2 = 512;  // two-group bf16 kernel
 constexpr int ATT_MAX_SPLIT_PAGES = 256;  // page-table window of one split (LDS)
 
 template <typename T, int D>
@@ -409,11 +408,19 @@ __global__ __launch_bounds__(ATT_THREADS) void tree_attention_kernel(AttnArgs a)
   }
 }
 
-// bf16 variant with the key/value tiles streamed straight into LDS.
+// bf16 kernel: the split's key/value tiles stream straight into LDS.
+//   * 4*KQ waves: wave w owns tree nodes 16*(w%4) .. +15 and, in every
+//     64-key tile, the 64/KQ keys of part w/4, with its own online-softmax
+//     state; the parts are merged through LDS after the tile loop.  KQ waves
+//     per SIMD keep the MFMA and vector pipes busy while the others wait on
+//     their dependency chains (LDS reads, MFMA results, exponentials).
 //   * Each wave issues LDS-DMA loads (16 bytes per lane, written at m0 +
-//     16*lane) for its quarter of a tile's K and V rows; tiles go to a ring of
-//     R LDS slots, so R tiles are in flight without holding registers, and
-//     the loop body is not unrolled (the slot is a runtime index).
+//     16*lane) for its share of a tile's K and V rows into a ring of R LDS
+//     slots.  The first R tiles are issued together right after the
+//     page-table round trip; afterwards a slot is refilled as soon as every
+//     wave is done reading it, so up to R-1 tiles stay in flight while one is
+//     computed.  Only tiles of the split are loaded, and the wait before tile
+//     t lets exactly the later tiles already issued remain in flight.
 //   * Row r of a tile keeps its 16-byte chunk c at position c ^ (r & SW):
 //     the lane that fills position p fetches chunk p ^ (r & SW).  The score
 //     MFMA's operand reads (16 rows, one chunk column) then hit 16 distinct
@@ -423,19 +430,29 @@ __global__ __launch_bounds__(ATT_THREADS) void tree_attention_kernel(AttnArgs a)
 //     i%4 of the 4 values at source lane (i/4)+4r's address, so pointing lane
 //     j of block g at V[key 4g + j/4][dim 4(j%4)] yields V[key 4g + r][dim i].
 //   * One barrier per tile: at the start of tile t every wave has its own
-//     DMA of tile t landed (an explicit vmcnt wait: only the later tiles'
-//     (R-2) x OPS loads may still be in flight) and its LDS reads of tile t-1
-//     done, so after the barrier tile t is readable everywhere and tile t-1's
-//     slot is free; tile t+R-1 is issued into that slot at once and streams
-//     in while tile t is computed.  s_barrier goes without a fence (a fenced
-//     barrier would wait for every DMA in flight).
+//     DMA of tile t landed and its LDS reads of tile t-1 done, so after the
+//     barrier tile t is readable everywhere and tile t-1's slot is free for
+//     tile t-1+R.  s_barrier goes without a fence (a fenced barrier would
+//     wait for every DMA in flight).
+//   * Online softmax with a lazy reference: the running maximum m (log2
+//     units) only moves, and the output and sum are only rescaled, when some
+//     node of the wave sees a score above m + ATT_LAZY; otherwise the tile's
+//     probabilities are taken against the old m (each at most 2^ATT_LAZY,
+//     far inside fp32 and bf16 range).  Output, sum and m always refer to the
+//     same m, so the normalised result is the same softmax.
 //   * The DMA source addresses are computed without branches: the page
 //     lookups of a wave's rows are read from LDS together, cached and tree
 //     rows are chosen by selects, and P2 (page size a power of two) turns the
 //     page/slot split into a shift and a mask.
-template <int D, int R, bool P2>
-__global__ __launch_bounds__(ATT_THREADS) void tree_attention_dma_kernel(AttnArgs a) {
+constexpr float ATT_LAZY = 8.f;
+template <int D, int R, int KQ, bool P2>
+__global__ __launch_bounds__(256 * KQ) void tree_attention_stream_kernel(AttnArgs a) {
   using T = bf16_t;
+  constexpr int NT = 256 * KQ;                 // threads
+  constexpr int NW = NT / 64;                  // waves
+  constexpr int KW = ATT_TILE / KQ;            // keys per wave and tile
+  constexpr int KB = KW / 16;                  // 16-key MFMA blocks per wave and tile
+  static_assert(KQ == 2 || KQ == 4, "two or four key parts");
   constexpr int P16 = 8;                       // bf16 per 16 bytes
   constexpr int ROWB = D * 2;                  // bytes per key row
   constexpr int CPR = ROWB / 16;               // 16-byte chunks per row
@@ -443,14 +460,13 @@ __global__ __launch_bounds__(ATT_THREADS) void tree_attention_dma_kernel(AttnArg
   constexpr int TILEB = ATT_TILE * ROWB;       // bytes of one K (or V) tile
   constexpr int SLOTB = 2 * TILEB;
   constexpr int RPD = 1024 / ROWB;             // rows per DMA instruction (64 lanes x 16 B)
-  constexpr int DPW = TILEB / 1024 / 4;        // DMA instructions per wave per tensor
+  constexpr int DPW = TILEB / 1024 / NW;       // DMA instructions per wave per tensor
   constexpr int OPS = 2 * DPW;                 // vector-memory ops per wave per tile
   constexpr int QSTEPS = D / 32;
   constexpr int DB = D / 16;
-  static_assert(R >= 3, "a slot is refilled one tile after it was read");
-  constexpr int WAITN = (R - 2) * OPS;         // DMA ops allowed in flight at a tile start
-  static_assert(WAITN < 64, "vmcnt range");
-  constexpr int WAIT_IMM = waitcnt_vm(WAITN);
+  static_assert(DPW >= 1 && DPW * NW * 1024 == TILEB, "tile must split into whole DMAs");
+  static_assert(R >= 2 && R <= 8, "ring of 2..8 tiles");
+  static_assert((R - 1) * OPS < 64, "vmcnt range");
   __shared__ __attribute__((aligned(1024))) unsigned char lds[R * SLOTB];
   __shared__ int spages[ATT_MAX_SPLIT_PAGES];
 
@@ -464,8 +480,9 @@ __global__ __launch_bounds__(ATT_THREADS) void tree_attention_dma_kernel(AttnArg
   const int tid = threadIdx.x;
   // wave index made provably uniform, so per-wave branches stay scalar
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, lr = lane & 15, lg = lane >> 4;
-  const int node = wave * 16 + lr;
-  const bool wave_active = wave * 16 < N;
+  const int nb = wave & 3, hf = wave >> 2;     // node block, key part
+  const int node = nb * 16 + lr;
+  const bool wave_active = nb * 16 < N;
   const int nodec = min(node, N - 1);
 
   const T* Qp = reinterpret_cast<const T*>(a.Q);
@@ -475,12 +492,19 @@ __global__ __launch_bounds__(ATT_THREADS) void tree_attention_dma_kernel(AttnArg
   T* Vcp = reinterpret_cast<T*>(a.Vc);
   const int* pt = a.page_table + (int64_t)b * a.max_pages;
 
-  // One round trip before the tile stream (as in tree_attention_kernel).
+  // One round trip before the tile stream: the sequence length, the split's
+  // slice of the page table (sized from max_ctx + N, so it does not wait for
+  // the length; it covers the cache slots and the tree slots the split may
+  // touch), this wave's queries and its nodes' ancestor masks.  The page
+  // slice goes to LDS, so that address computation never waits on a global
+  // load (a wait there would also wait for every tile load in flight).
   const int page0 = k_beg / a.P;
   const int slice_end = min(k_beg + a.chunk, a.max_ctx + N);
   const int npages = slice_end > k_beg ? (slice_end - 1) / a.P - page0 + 1 : 0;
+  // (a length outside [0, max_ctx] breaks the caller's contract; it is
+  // clamped so that every access stays inside the page slice)
   const int ctxb = min(max(a.ctx[b], 0), a.max_ctx);
-  static_assert(ATT_MAX_SPLIT_PAGES <= ATT_THREADS, "one page-table entry per thread");
+  static_assert(ATT_MAX_SPLIT_PAGES <= NT, "one page-table entry per thread");
   const int my_page = threadIdx.x < npages ? pt[page0 + threadIdx.x] : 0;
   u32x4 qf[QSTEPS];
   {
@@ -498,8 +522,7 @@ __global__ __launch_bounds__(ATT_THREADS) void tree_attention_dma_kernel(AttnArg
   const int k_end = min(k_beg + a.chunk, total);
   const int ntiles = (k_end - k_beg + ATT_TILE - 1) / ATT_TILE;
 
-  // page of key j and its slot there (shifts when P is a power of two: the
-  // address math runs per lane for every tile)
+  // page of key j and its slot there
   const int64_t page_elems = (int64_t)a.Hkv * a.P * D;  // one page of the cache
   const int head_elems = kvh * a.P * D;                  // this head's rows in a page
   auto cache_off = [&](int j) -> int64_t {
@@ -514,12 +537,13 @@ __global__ __launch_bounds__(ATT_THREADS) void tree_attention_dma_kernel(AttnArg
   };
 
   const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)lds;
-  // DMA of tile t (clamped to the split's last tile) into ring slot `slot`.
-  // Every key of [k_beg, k_end) has its page in spages (the tree keys' too:
-  // they go to cache slots ctx..ctx+N-1), so the lookup runs for every row
-  // and the tree rows just ignore it.
+  // DMA of tile t (< ntiles) into ring slot `slot`.  Rows past the split's
+  // end re-read its last key (their scores are masked).  Every key of
+  // [k_beg, k_end) has its page in spages (the tree keys' too: they go to
+  // cache slots ctx..ctx+N-1), so the lookup runs for every row and the
+  // tree rows just ignore it.
   auto issue = [&](int t, int slot) {
-    const int tile0 = k_beg + min(t, ntiles - 1) * ATT_TILE;
+    const int tile0 = k_beg + t * ATT_TILE;
     int jj[DPW], pg[DPW];
 #pragma unroll
     for (int i = 0; i < DPW; ++i) {
@@ -544,380 +568,165 @@ __global__ __launch_bounds__(ATT_THREADS) void tree_attention_dma_kernel(AttnArg
       lds_dma16(vsrc, kd + TILEB);
     }
   };
-
-  f32x4 oacc[DB];
-#pragma unroll
-  for (int db = 0; db < DB; ++db) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float mrun = -INFINITY, lrun = 0.f;
-
-  for (int t = 0; t < R - 1; ++t) issue(t, t);
-  for (int t = 0; t < ntiles; ++t) {
-    const int slot = t % R;
-    const int tile0 = k_beg + t * ATT_TILE;
-    __builtin_amdgcn_s_waitcnt(WAIT_IMM);       // this wave's DMA of tile t is done
-    __builtin_amdgcn_s_waitcnt(WAITCNT_LGKM0);  // ... and its LDS reads of tile t-1
-    __builtin_amdgcn_s_barrier();               // ... and every other wave's
-    asm volatile("" ::: "memory");              // no LDS access moves across the barrier
-    issue(t + R - 1, (t + R - 1) % R);          // into tile t-1's slot
-    const unsigned char* ks = lds + slot * SLOTB;
-    const unsigned char* vs = ks + TILEB;
-    if (wave_active) {
-      f32x4 sacc[4];
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        sacc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const int r = kb * 16 + lr;
-#pragma unroll
-        for (int st = 0; st < QSTEPS; ++st) {
-          const int c = (st * 4 + lg) ^ (r & SW);
-          const u32x4 kf = *reinterpret_cast<const u32x4*>(ks + r * ROWB + c * 16);
-          sacc[kb] = mfma_bf16_16x16x32(kf, qf[st], sacc[kb]);
-        }
-      }
-      float x[4][4];
-      float tmax = -INFINITY;
-      // a tile wholly inside the cached keys needs no mask (wave-uniform)
-      const bool plain = tile0 + ATT_TILE <= min(ctxb, k_end);
-      if (plain) {
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            x[kb][r] = sacc[kb][r] * a.scale_log2;
-            tmax = fmaxf(tmax, x[kb][r]);
-          }
-      } else {
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int j = tile0 + kb * 16 + lg * 4 + r;
-            const uint32_t bit = (uint32_t)(mrow >> (uint32_t)min(max(j - ctxb, 0), 63)) & 1u;
-            const bool ok = (j < k_end) & ((j < ctxb) | (bit != 0u));
-            x[kb][r] = ok ? sacc[kb][r] * a.scale_log2 : -INFINITY;
-            tmax = fmaxf(tmax, x[kb][r]);
-          }
-      }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-      const float mnew = fmaxf(mrun, tmax);
-      const float alpha = (mnew == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(mrun - mnew);
-      float psum = 0.f;
-      if (plain) {  // every score finite, so mnew is too
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            x[kb][r] = __builtin_amdgcn_exp2f(x[kb][r] - mnew);
-            psum += x[kb][r];
-          }
-      } else {
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float p = (x[kb][r] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(x[kb][r] - mnew);
-            x[kb][r] = p;
-            psum += p;
-          }
-      }
-      lrun = lrun * alpha + psum;
-      mrun = mnew;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        u32x2 pb;
-        pb.x = pack_bf2(x[kb][0], x[kb][1]);
-        pb.y = pack_bf2(x[kb][2], x[kb][3]);
-        const int rr = kb * 16 + 4 * lg + (lr >> 2);  // source row of this lane's address
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const int c = db * 2 + ((lr & 3) >> 1);
-          const unsigned char* src = vs + rr * ROWB + ((c ^ (rr & SW)) * 16) + (lr & 1) * 8;
-          typedef short s4 __attribute__((ext_vector_type(4)));
-          const s4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4*)src);
-          oacc[db] = mfma_bf16_16x16x16(__builtin_bit_cast(u32x2, v), pb, oacc[db]);
-        }
-      }
+  // wait until at most n tiles of this wave's DMA are in flight (n < R)
+  auto wait_tiles = [&](int n) {
+    switch (n) {
+      case 0: __builtin_amdgcn_s_waitcnt(waitcnt_vm(0)); break;
+      case 1: __builtin_amdgcn_s_waitcnt(waitcnt_vm(R > 1 ? 1 * OPS : 0)); break;
+      case 2: __builtin_amdgcn_s_waitcnt(waitcnt_vm(R > 2 ? 2 * OPS : 0)); break;
+      case 3: __builtin_amdgcn_s_waitcnt(waitcnt_vm(R > 3 ? 3 * OPS : 0)); break;
+      case 4: __builtin_amdgcn_s_waitcnt(waitcnt_vm(R > 4 ? 4 * OPS : 0)); break;
+      case 5: __builtin_amdgcn_s_waitcnt(waitcnt_vm(R > 5 ? 5 * OPS : 0)); break;
+      case 6: __builtin_amdgcn_s_waitcnt(waitcnt_vm(R > 6 ? 6 * OPS : 0)); break;
+      default: __builtin_amdgcn_s_waitcnt(waitcnt_vm(R > 7 ? 7 * OPS : 0)); break;
     }
-    asm volatile("" ::: "memory");
-  }
-  __builtin_amdgcn_s_waitcnt(0);           // drain the clamped refills before leaving
+  };
 
-  // Store the tree keys' K/V of this split into cache slots ctx..ctx+N-1.
-  if (appender && k_end > ctxb) {
-    constexpr int CPRT = D / P16;
-    const int j0 = max(k_beg, ctxb);
-    const int items = (k_end - j0) * CPRT * 2;
-    for (int e = tid; e < items; e += ATT_THREADS) {
-      const int which = e / ((k_end - j0) * CPRT), rem = e % ((k_end - j0) * CPRT);
-      const int j = j0 + rem / CPRT, part = rem % CPRT;
-      const T* src = (which ? Vtp : Ktp) + tree_off(j) + part * P16;
-      T* dst = (which ? Vcp : Kcp) + cache_off(j) + part * P16;
-      *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src);
-    }
-  }
-
-  float ltot = lrun + __shfl_xor(lrun, 16, 64);
-  ltot = ltot + __shfl_xor(ltot, 32, 64);
-  const bool node_ok = wave_active && node < N;
-  if (S == 1) {
-    if (node_ok) {
-      const float inv = 1.f / ltot;
-      T* orow = reinterpret_cast<T*>(a.O) + (((int64_t)b * N + node) * a.Hq + h) * D;
+  // This lane's LDS byte offsets inside a ring slot (first 16-key block; the
+  // next block is 16 rows further): K operand chunk of each contraction step,
+  // and the transposing-read address of each 16-dim block of V.
+  int kofs[QSTEPS], vofs[DB];
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) st<T>(orow, db * 16 + lg * 4 + r, oacc[db][r] * inv);
-    }
-    return;
-  }
-  const int64_t bh = (int64_t)b * a.Hq + h;
-  if (node_ok) {
-    _Float16* op = reinterpret_cast<_Float16*>(a.opart) + ((bh * S + s) * N + node) * D;
-    const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
-    typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+  for (int st = 0; st < QSTEPS; ++st)
+    kofs[st] = (hf * KW + lr) * ROWB + (((st * 4 + lg) ^ (lr & SW)) * 16);
+  {
+    const int rr = hf * KW + 4 * lg + (lr >> 2);  // source row of this lane's address
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
-      h4 v = {(_Float16)(oacc[db][0] * inv), (_Float16)(oacc[db][1] * inv), (_Float16)(oacc[db][2] * inv),
-              (_Float16)(oacc[db][3] * inv)};
-      *reinterpret_cast<h4*>(op + db * 16 + lg * 4) = v;
+      const int c = db * 2 + ((lr & 3) >> 1);
+      vofs[db] = rr * ROWB + ((c ^ (rr & SW)) * 16) + (lr & 1) * 8;
     }
-    if (lg == 0) a.ml[(bh * S + s) * N + node] = make_float2(mrun, ltot);
   }
-}
-
-// bf16 variant with two wave groups: eight waves, group g (waves 4g..4g+3,
-// 16 nodes each) takes the tiles t = g mod 2 of the split with its own
-// online-softmax state, so a workgroup runs half as many tile steps and every
-// SIMD holds two waves.  The K/V ring has two pair-slots (four tiles): at the
-// start of pair p each wave waits for its own DMA of pair p, a barrier makes
-// all of it visible and frees pair p-1's slot, pair p+1 is issued into that
-// slot and streams in while the groups compute tiles 2p and 2p+1.  After the
-// loop, group 1's (max, sum, output) go through LDS and group 0 merges them
-// (the same rescaling as the split merge), then writes the output or the
-// split's partials as the single-group kernel does.  Tile layout, swizzle,
-// operand reads, masking and the softmax are those of the single-group
-// kernel.
-template <int D, bool P2>
-__global__ __launch_bounds__(ATT_THREADS2) void tree_attention_dma2_kernel(AttnArgs a) {
-  using T = bf16_t;
-  constexpr int NWAVES = ATT_THREADS2 / 64;
-  constexpr int P16 = 8;                       // bf16 per 16 bytes
-  constexpr int ROWB = D * 2;                  // bytes per key row
-  constexpr int CPR = ROWB / 16;               // 16-byte chunks per row
-  constexpr int SW = CPR - 1;                  // swizzle mask
-  constexpr int TILEB = ATT_TILE * ROWB;       // bytes of one K (or V) tile
-  constexpr int SLOTB = 2 * TILEB;
-  constexpr int RING = 4;                      // tiles: two pair-slots
-  constexpr int RPD = 1024 / ROWB;             // rows per DMA instruction (64 lanes x 16 B)
-  constexpr int DPW = TILEB / 1024 / NWAVES;   // DMA instructions per wave per tensor
-  constexpr int QSTEPS = D / 32;
-  constexpr int DB = D / 16;
-  static_assert(DPW >= 1 && DPW * NWAVES * 1024 == TILEB, "tile must split into whole DMAs");
-  __shared__ __attribute__((aligned(1024))) unsigned char lds[RING * SLOTB];
-  __shared__ int spages[ATT_MAX_SPLIT_PAGES];
-
-  const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int S = gridDim.x;
-  const int N = a.N;
-  const int k_beg = s * a.chunk;
-  const int group = a.Hq / a.Hkv;
-  const int kvh = h / group;
-  const bool appender = (h % group) == 0;
-  const int tid = threadIdx.x;
-  // wave index made provably uniform, so per-wave branches stay scalar
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, lr = lane & 15, lg = lane >> 4;
-  const int grp = wave >> 2, wv = wave & 3;
-  const int node = wv * 16 + lr;
-  const bool wave_active = wv * 16 < N;
-  const int nodec = min(node, N - 1);
-
-  const T* Qp = reinterpret_cast<const T*>(a.Q);
-  const T* Ktp = reinterpret_cast<const T*>(a.Kt);
-  const T* Vtp = reinterpret_cast<const T*>(a.Vt);
-  T* Kcp = reinterpret_cast<T*>(a.Kc);
-  T* Vcp = reinterpret_cast<T*>(a.Vc);
-  const int* pt = a.page_table + (int64_t)b * a.max_pages;
-
-  // One round trip before the tile stream (length, page-table slice, queries, masks).
-  const int page0 = k_beg / a.P;
-  const int slice_end = min(k_beg + a.chunk, a.max_ctx + N);
-  const int npages = slice_end > k_beg ? (slice_end - 1) / a.P - page0 + 1 : 0;
-  const int ctxb = min(max(a.ctx[b], 0), a.max_ctx);
-  static_assert(ATT_MAX_SPLIT_PAGES <= ATT_THREADS2, "one page-table entry per thread");
-  const int my_page = threadIdx.x < npages ? pt[page0 + threadIdx.x] : 0;
-  u32x4 qf[QSTEPS];
-  {
-    const T* qrow = Qp + (((int64_t)b * N + nodec) * a.Hq + h) * D;
-#pragma unroll
-    for (int st = 0; st < QSTEPS; ++st)
-      qf[st] = *reinterpret_cast<const u32x4*>(qrow + st * 4 * P16 + lg * P16);
-  }
-  const uint64_t mrow = a.mask[(int64_t)b * N + nodec];
-  __builtin_amdgcn_s_waitcnt(0);
-  if (threadIdx.x < npages) spages[threadIdx.x] = my_page;
-  __syncthreads();
-  const int total = ctxb + N;
-  if (k_beg >= total) return;  // uniform over the workgroup
-  const int k_end = min(k_beg + a.chunk, total);
-  const int ntiles = (k_end - k_beg + ATT_TILE - 1) / ATT_TILE;
-  const int npairs = (ntiles + 1) / 2;
-
-  const int64_t page_elems = (int64_t)a.Hkv * a.P * D;  // one page of the cache
-  const int head_elems = kvh * a.P * D;                  // this head's rows in a page
-  auto cache_off = [&](int j) -> int64_t {
-    const int pj = P2 ? (j >> a.lp) : j / a.P;
-    const int sj = P2 ? (j & (a.P - 1)) : j - pj * a.P;
-    const int page = spages[pj - page0];
-    return (int64_t)page * page_elems + (head_elems + sj * D);
-  };
-  const int64_t tree_base = ((int64_t)b * N * a.Hkv + kvh) * D;
-  auto tree_off = [&](int j) -> int64_t {
-    return tree_base + max(j - ctxb, 0) * (a.Hkv * D);
-  };
-
-  const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)lds;
-  // DMA of tile t (clamped to the split's last tile) into ring slot `slot`;
-  // branch-free addressing as in the single-group kernel
-  auto issue = [&](int t, int slot) {
-    const int tile0 = k_beg + min(t, ntiles - 1) * ATT_TILE;
-    int jj[DPW], pg[DPW];
-#pragma unroll
-    for (int i = 0; i < DPW; ++i) {
-      const int r = (wave * DPW + i) * RPD + lane / CPR;  // tile row this lane fills
-      jj[i] = min(tile0 + r, k_end - 1);
-      pg[i] = spages[(P2 ? (jj[i] >> a.lp) : jj[i] / a.P) - page0];
-    }
-#pragma unroll
-    for (int i = 0; i < DPW; ++i) {
-      const int q = wave * DPW + i;          // 1 KB block of the tile
-      const int r = q * RPD + lane / CPR;
-      const int c = (lane % CPR) ^ (r & SW); // chunk fetched for that position
-      const int j = jj[i];
-      const bool cached = j < ctxb;
-      const int sj = P2 ? (j & (a.P - 1)) : j - (j / a.P) * a.P;
-      const int64_t coff = (int64_t)(uint32_t)pg[i] * page_elems + (head_elems + sj * D);
-      const int64_t off = (cached ? coff : tree_off(j)) + c * P16;
-      const T* ksrc = (cached ? Kcp : Ktp) + off;
-      const T* vsrc = (cached ? Vcp : Vtp) + off;
-      const uint32_t kd = lds_base + slot * SLOTB + q * 1024;
-      lds_dma16(ksrc, kd);
-      lds_dma16(vsrc, kd + TILEB);
-    }
-  };
 
   f32x4 oacc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
   float mrun = -INFINITY, lrun = 0.f;
 
-  issue(0, 0);
-  issue(1, 1);
-  for (int p = 0; p < npairs; ++p) {
-    __builtin_amdgcn_s_waitcnt(0);              // this wave's DMA of pair p is done
-    __builtin_amdgcn_s_barrier();               // ... and every other wave's; pair p-1 is read
+  const int first = min(ntiles, R);
+  for (int t = 0; t < first; ++t) issue(t, t);
+  for (int t = 0; t < ntiles; ++t) {
+    const int slot = t % R;
+    // tiles issued before this point: min(ntiles, R + max(t - 1, 0))
+    wait_tiles(t == 0 ? first - 1 : min(ntiles - 1 - t, R - 2));  // tile t has landed
+    __builtin_amdgcn_s_waitcnt(WAITCNT_LGKM0);  // ... and this wave's LDS reads of tile t-1
+    __builtin_amdgcn_s_barrier();               // ... and every other wave's
     asm volatile("" ::: "memory");              // no LDS access moves across the barrier
-    const int nxt = ((p + 1) & 1) * 2;          // pair p+1 goes into pair p-1's slots
-    issue(2 * p + 2, nxt);
-    issue(2 * p + 3, nxt + 1);
-    const int t = 2 * p + grp;
-    const int slot = (p & 1) * 2 + grp;
-    const int tile0 = k_beg + t * ATT_TILE;
+    if (t >= 1 && t - 1 + R < ntiles) issue(t - 1 + R, (t - 1) % R);  // into tile t-1's slot
+    const int key0 = k_beg + t * ATT_TILE + hf * KW;  // this wave's KW keys
     const unsigned char* ks = lds + slot * SLOTB;
     const unsigned char* vs = ks + TILEB;
-    if (wave_active && t < ntiles) {
-      f32x4 sacc[4];
+    if (wave_active && key0 < k_end) {
+      f32x4 sacc[KB];
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
+      for (int kb = 0; kb < KB; ++kb) {
         sacc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const int r = kb * 16 + lr;
 #pragma unroll
         for (int st = 0; st < QSTEPS; ++st) {
-          const int c = (st * 4 + lg) ^ (r & SW);
-          const u32x4 kf = *reinterpret_cast<const u32x4*>(ks + r * ROWB + c * 16);
+          const u32x4 kf = *reinterpret_cast<const u32x4*>(ks + kofs[st] + kb * 16 * ROWB);
           sacc[kb] = mfma_bf16_16x16x32(kf, qf[st], sacc[kb]);
         }
       }
-      float x[4][4];
+      // raw scores x (masked: -inf); the scale (> 0, in log2 units) is
+      // applied to the maximum and inside the exponent's FMA
+      float x[KB][4];
       float tmax = -INFINITY;
-      // a tile wholly inside the cached keys needs no mask (wave-uniform)
-      const bool plain = tile0 + ATT_TILE <= min(ctxb, k_end);
+      // keys wholly inside the cached range need no mask (wave-uniform)
+      const bool plain = key0 + KW <= min(ctxb, k_end);
       if (plain) {
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
+        for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            x[kb][r] = sacc[kb][r] * a.scale_log2;
+            x[kb][r] = sacc[kb][r];
             tmax = fmaxf(tmax, x[kb][r]);
           }
       } else {
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
+        for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const int j = tile0 + kb * 16 + lg * 4 + r;
+            const int j = key0 + kb * 16 + lg * 4 + r;
             const uint32_t bit = (uint32_t)(mrow >> (uint32_t)min(max(j - ctxb, 0), 63)) & 1u;
             const bool ok = (j < k_end) & ((j < ctxb) | (bit != 0u));
-            x[kb][r] = ok ? sacc[kb][r] * a.scale_log2 : -INFINITY;
+            x[kb][r] = ok ? sacc[kb][r] : -INFINITY;
             tmax = fmaxf(tmax, x[kb][r]);
           }
       }
       tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
       tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-      const float mnew = fmaxf(mrun, tmax);
-      const float alpha = (mnew == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(mrun - mnew);
-      float psum = 0.f;
-      if (plain) {  // every score finite, so mnew is too
+      tmax *= a.scale_log2;
+      // move the reference only when some node's scores outgrow it
+      if (__builtin_amdgcn_ballot_w64(tmax > mrun + ATT_LAZY) != 0) {
+        const float mnew = fmaxf(mrun, tmax);
+        const float alpha = (mnew == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(mrun - mnew);
+        lrun *= alpha;
+        mrun = mnew;
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
+        for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+      }
+      float psum = 0.f;
+      if (plain) {  // every score finite, and mrun finite once a score was seen
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            x[kb][r] = __builtin_amdgcn_exp2f(x[kb][r] - mnew);
+            x[kb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[kb][r], a.scale_log2, -mrun));
             psum += x[kb][r];
           }
       } else {
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
+        for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const float p = (x[kb][r] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(x[kb][r] - mnew);
+            const float p = (x[kb][r] == -INFINITY)
+                                ? 0.f
+                                : __builtin_amdgcn_exp2f(__builtin_fmaf(x[kb][r], a.scale_log2, -mrun));
             x[kb][r] = p;
             psum += p;
           }
       }
-      lrun = lrun * alpha + psum;
-      mrun = mnew;
+      lrun += psum;
+      // O^T += V^T P^T.  Lane l holds the probabilities of keys kb*16 +
+      // 4*(l/16) + r; two 16-key blocks form the 8-element contraction slice
+      // of one 16x16x32 step (element i = block i/4, r = i%4), and the two
+      // transposing reads of those blocks give V^T in the same key order.
+      typedef short s4 __attribute__((ext_vector_type(4)));
+      auto vread = [&](int kb, int db) -> u32x2 {
+        const unsigned char* src = vs + vofs[db] + kb * 16 * ROWB;
+        return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                             (__attribute__((address_space(3))) s4*)src));
+      };
+      if constexpr (KB % 2 == 0) {
 #pragma unroll
-      for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+        for (int kb = 0; kb < KB; kb += 2) {
+          const u32x4 pb = {pack_bf2(x[kb][0], x[kb][1]), pack_bf2(x[kb][2], x[kb][3]),
+                            pack_bf2(x[kb + 1][0], x[kb + 1][1]), pack_bf2(x[kb + 1][2], x[kb + 1][3])};
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        u32x2 pb;
-        pb.x = pack_bf2(x[kb][0], x[kb][1]);
-        pb.y = pack_bf2(x[kb][2], x[kb][3]);
-        const int rr = kb * 16 + 4 * lg + (lr >> 2);  // source row of this lane's address
+          for (int db = 0; db < DB; ++db) {
+            const u32x2 v0 = vread(kb, db), v1 = vread(kb + 1, db);
+            oacc[db] = mfma_bf16_16x16x32(u32x4{v0.x, v0.y, v1.x, v1.y}, pb, oacc[db]);
+          }
+        }
+      } else {
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const int c = db * 2 + ((lr & 3) >> 1);
-          const unsigned char* src = vs + rr * ROWB + ((c ^ (rr & SW)) * 16) + (lr & 1) * 8;
-          typedef short s4 __attribute__((ext_vector_type(4)));
-          const s4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4*)src);
-          oacc[db] = mfma_bf16_16x16x16(__builtin_bit_cast(u32x2, v), pb, oacc[db]);
+        for (int kb = 0; kb < KB; ++kb) {
+          const u32x2 pb = {pack_bf2(x[kb][0], x[kb][1]), pack_bf2(x[kb][2], x[kb][3])};
+#pragma unroll
+          for (int db = 0; db < DB; ++db) oacc[db] = mfma_bf16_16x16x16(vread(kb, db), pb, oacc[db]);
         }
       }
     }
     asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt(WAITCNT_LGKM0);  // this wave's LDS reads of pair p are done
   }
-  __builtin_amdgcn_s_waitcnt(0);               // drain the clamped refills before leaving
+  // (every tile issued was waited for above: no DMA is left in flight)
 
   // Store the tree keys' K/V of this split into cache slots ctx..ctx+N-1.
   if (appender && k_end > ctxb) {
     constexpr int CPRT = D / P16;
     const int j0 = max(k_beg, ctxb);
     const int items = (k_end - j0) * CPRT * 2;
-    for (int e = tid; e < items; e += ATT_THREADS2) {
+    for (int e = tid; e < items; e += NT) {
       const int which = e / ((k_end - j0) * CPRT), rem = e % ((k_end - j0) * CPRT);
       const int j = j0 + rem / CPRT, part = rem % CPRT;
       const T* src = (which ? Vtp : Ktp) + tree_off(j) + part * P16;
@@ -926,15 +735,16 @@ __global__ __launch_bounds__(ATT_THREADS2) void tree_attention_dma2_kernel(AttnA
     }
   }
 
-  // merge group 1 into group 0 (per node: max and sum per lane; output dims
-  // db*16 + lg*4 + r of this lane)
+  // merge key parts 1..KQ-1 into part 0, in part order (per node: max and
+  // sum per lane; output dims db*16 + lg*4 + r of this lane)
   float ltot = lrun + __shfl_xor(lrun, 16, 64);
   ltot = ltot + __shfl_xor(ltot, 32, 64);
-  __syncthreads();                             // the ring is free now
-  float* xch = reinterpret_cast<float*>(lds);  // [4 waves][64 lanes][DB*4 + 2]
+  __syncthreads();                             // every wave is done with the ring
+  float* xch = reinterpret_cast<float*>(lds);  // [KQ-1 parts][4 node blocks][64 lanes][DB*4 + 2]
   constexpr int XW = DB * 4 + 2;
-  if (grp == 1) {
-    float* d = xch + (wv * 64 + lane) * XW;
+  static_assert((KQ - 1) * 4 * 64 * XW * 4 <= R * SLOTB, "exchange fits in the ring");
+  if (hf >= 1) {
+    float* d = xch + (((hf - 1) * 4 + nb) * 64 + lane) * XW;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -943,9 +753,10 @@ __global__ __launch_bounds__(ATT_THREADS2) void tree_attention_dma2_kernel(AttnA
     d[DB * 4 + 1] = ltot;
   }
   __syncthreads();
-  if (grp == 1) return;
-  {
-    const float* d = xch + (wv * 64 + lane) * XW;
+  if (hf >= 1) return;
+#pragma unroll
+  for (int q = 1; q < KQ; ++q) {
+    const float* d = xch + (((q - 1) * 4 + nb) * 64 + lane) * XW;
     const float m1 = d[DB * 4], l1 = d[DB * 4 + 1];
     const float mm = fmaxf(mrun, m1);
     const float w0 = mrun == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mrun - mm);
@@ -1067,12 +878,8 @@ struct SplitPlan {
 #ifndef MEDUSA_ATTN_DMA_WGS
 #define MEDUSA_ATTN_DMA_WGS 256
 #endif
-// bf16 attention with two wave groups on alternating tiles (1) or one group (0)
-#ifndef MEDUSA_ATTN_PAIRS
-#define MEDUSA_ATTN_PAIRS 1
-#endif
 #ifndef MEDUSA_ATTN_DMA_R
-#define MEDUSA_ATTN_DMA_R 3
+#define MEDUSA_ATTN_DMA_R 4
 #endif
 SplitPlan plan_splits(int B, int Hq, int N, int max_ctx, int P, int target) {
   const int total = max_ctx + N;
@@ -1174,26 +981,21 @@ extern "C" int32_t medusa_tree_attention(const void* Q, const void* Kt, const vo
   constexpr int RD = MEDUSA_ATTN_DMA_R;
   if (dt == MEDUSA_BF16) {
     const bool p2 = a.lp >= 0;
-    if (MEDUSA_ATTN_PAIRS) {
-      const dim3 blk2(medusa::ATT_THREADS2);
-#define MEDUSA_ATT_LAUNCH2(KERNEL, DD)                                                       \
+    // two key parts per tile (8 waves); four parts (16 waves) measured slower
+    constexpr int KQ = 2;
+    const dim3 blk8(256 * KQ);
+#define MEDUSA_ATT_LAUNCH_S(KERNEL, DD)                                                      \
   do {                                                                                       \
-    hipLaunchKernelGGL((KERNEL), grid, blk2, 0, st, a);                                      \
+    hipLaunchKernelGGL((KERNEL), grid, blk8, 0, st, a);                                      \
     if (p.splits > 1)                                                                        \
       hipLaunchKernelGGL((medusa::tree_attention_combine_kernel<medusa::bf16_t, DD>), cgrid, blk, 0, st, \
                          a, p.splits);                                                       \
   } while (0)
-      if (D == 128 && p2) MEDUSA_ATT_LAUNCH2((medusa::tree_attention_dma2_kernel<128, true>), 128);
-      else if (D == 128) MEDUSA_ATT_LAUNCH2((medusa::tree_attention_dma2_kernel<128, false>), 128);
-      else if (p2) MEDUSA_ATT_LAUNCH2((medusa::tree_attention_dma2_kernel<64, true>), 64);
-      else MEDUSA_ATT_LAUNCH2((medusa::tree_attention_dma2_kernel<64, false>), 64);
-#undef MEDUSA_ATT_LAUNCH2
-      return check_launch("medusa_tree_attention");
-    }
-    if (D == 128 && p2) MEDUSA_ATT_LAUNCH((medusa::tree_attention_dma_kernel<128, RD, true>), medusa::bf16_t, 128);
-    else if (D == 128) MEDUSA_ATT_LAUNCH((medusa::tree_attention_dma_kernel<128, RD, false>), medusa::bf16_t, 128);
-    else if (p2) MEDUSA_ATT_LAUNCH((medusa::tree_attention_dma_kernel<64, 2 * RD, true>), medusa::bf16_t, 64);
-    else MEDUSA_ATT_LAUNCH((medusa::tree_attention_dma_kernel<64, 2 * RD, false>), medusa::bf16_t, 64);
+    if (D == 128 && p2) MEDUSA_ATT_LAUNCH_S((medusa::tree_attention_stream_kernel<128, RD, KQ, true>), 128);
+    else if (D == 128) MEDUSA_ATT_LAUNCH_S((medusa::tree_attention_stream_kernel<128, RD, KQ, false>), 128);
+    else if (p2) MEDUSA_ATT_LAUNCH_S((medusa::tree_attention_stream_kernel<64, 2 * RD, KQ, true>), 64);
+    else MEDUSA_ATT_LAUNCH_S((medusa::tree_attention_stream_kernel<64, 2 * RD, KQ, false>), 64);
+#undef MEDUSA_ATT_LAUNCH_S
   } else {
     if (D == 128) MEDUSA_ATT_LAUNCH((medusa::tree_attention_kernel<float, 128, PF>), float, 128);
     else MEDUSA_ATT_LAUNCH((medusa::tree_attention_kernel<float, 64, PF>), float, 64);
