@@ -45,6 +45,12 @@ accept_typical: special cases only (threshold 0 accepts everything; a
               epsilon and delta).  The threshold FORMULA ``min(eps,
               delta*exp(-H))`` is not printed on the pages, which only tie
               the threshold to the entropy: parity unpinned for it.
+accept_sample: the Philox4x64-10 generator equals numpy's Philox bit
+              generator (numpy advances the counter before each block);
+              Gumbel-max draws follow softmax(z/T) (chi-square); the first
+              and second emitted tokens of a sampled tree step follow the base
+              model's distributions (the lossless claim, chi-square); a tiny
+              temperature reproduces greedy acceptance.
 kv_compact:   compacted cache equals the cache of sequential decoding of the
               same tokens; hand example path (0, 2, 7).
 """
@@ -280,6 +286,111 @@ def accept_typical(logits, tokens, parent, n_heads, temperature, epsilon, delta,
 
 
 # ----------------------------------------------------------------------------
+# sampled verification: rejection sampling against the base model's own
+# distribution keeps Medusa-1 lossless ("Têtes de décodage Medusa", section
+# "Plongée profonde", and its "Questions fréquemment posées" entry on lossless
+# acceleration: exact rejection sampling checks the accepted candidates
+# against the base model's distribution)
+# ----------------------------------------------------------------------------
+_M64 = (1 << 64) - 1
+_PHILOX_M = (0xD2E7470EE14C6C93, 0xCA5A826395121157)   # round multipliers
+_PHILOX_W = (0x9E3779B97F4A7C15, 0xBB67AE8584CAA73B)   # key schedule (Weyl) increments
+
+
+def _mulhilo64(a, b):
+    """High and low 64-bit halves of the 128-bit product of uint64 arrays,
+    from 32-bit limbs (numpy has no 128-bit integers)."""
+    a = np.asarray(a, np.uint64)
+    b = np.asarray(b, np.uint64)
+    m32 = np.uint64(0xFFFFFFFF)
+    s32 = np.uint64(32)
+    a0, a1 = a & m32, a >> s32
+    b0, b1 = b & m32, b >> s32
+    p00, p01, p10, p11 = a0 * b0, a0 * b1, a1 * b0, a1 * b1
+    mid = (p00 >> s32) + (p01 & m32) + (p10 & m32)          # < 3 * 2^32: no overflow
+    hi = p11 + (p01 >> s32) + (p10 >> s32) + (mid >> s32)
+    lo = a * b                                                # wraps modulo 2^64
+    return hi, lo
+
+
+def philox4x64_10(counter, key):
+    """Philox4x64 with 10 rounds (Salmon, Moraes, Dror and Shaw, "Parallel
+    random numbers: as easy as 1, 2, 3", SC 2011): counter = 4 uint64 words
+    (each an array, broadcast together), key = 2 uint64 words.  Each round
+    multiplies words 0 and 2 by the two round constants, swaps halves and
+    XORs in the round key; the key advances by the Weyl constants.  Returns
+    the 4 output words."""
+    with np.errstate(over="ignore"):
+        c = [np.asarray(w, np.uint64) for w in counter]
+        k = [np.uint64(int(w) & _M64) for w in key]
+        for _ in range(10):
+            hi0, lo0 = _mulhilo64(np.uint64(_PHILOX_M[0]), c[0])
+            hi1, lo1 = _mulhilo64(np.uint64(_PHILOX_M[1]), c[2])
+            c = [hi1 ^ c[1] ^ k[0], lo1, hi0 ^ c[3] ^ k[1], lo0]
+            k = [k[0] + np.uint64(_PHILOX_W[0]), k[1] + np.uint64(_PHILOX_W[1])]
+    return c
+
+
+def sample_uniforms(V, seed, step, b, node):
+    """Uniforms in (0, 1) for vocabulary entries 0..V-1 of tree node ``node`` of
+    sequence ``b`` at decode step ``step``: key (seed, step), counter
+    (v // 4, node, b, 0), output word v % 4; u = (top 23 bits + 1/2) / 2^23,
+    exact in float32."""
+    v = np.arange(V, dtype=np.uint64)
+    words = philox4x64_10([v >> np.uint64(2), np.uint64(node), np.uint64(b), np.uint64(0)],
+                          [seed, step])
+    w = np.choose((v & np.uint64(3)).astype(np.int64), words)
+    return ((w >> np.uint64(41)).astype(F64) + 0.5) / float(1 << 23)
+
+
+def sample_scores(logits_row, temperature, seed, step, b, node):
+    """Gumbel-max scores z/T + G with G = -log(-log(u)): the index of their
+    maximum is a draw from softmax(z/T) (float64; z rounded to float32)."""
+    u = sample_uniforms(len(logits_row), seed, step, b, node)
+    return f32(logits_row).astype(F64) / float(temperature) - np.log(-np.log(u))
+
+
+def sample_token(logits_row, temperature, seed, step, b, node):
+    """One draw from softmax(z/T) (lowest index on a tie of scores)."""
+    sc = sample_scores(logits_row, temperature, seed, step, b, node)
+    return int(np.flatnonzero(sc == sc.max())[0])
+
+
+def accept_sample(logits, tokens, parent, n_heads, temperature, seed, step, b=0,
+                  return_margins=False):
+    """Sampled verification of the tree (rejection sampling against the base model).
+
+    Reading: the heads' candidates are fixed (top-k), so the rejection test of
+    a candidate x under the base distribution p accepts it with probability
+    p(x); probing the children of an accepted node in rank order, each with p
+    renormalised over the tokens not yet rejected, and drawing from the rest
+    when all are rejected, yields the same joint law as one draw z ~ p at
+    that node: the child whose token is z is accepted, and when no child
+    carries z, z itself is the next token and the branch ends.  That is how it
+    is computed here: z_u = one draw from softmax(logits[u] / T) per node
+    (Gumbel-max, counter-based noise keyed by (seed, step)); node i is
+    accepted iff its parent is and tokens[i] == z_parent; the next root token
+    is z at the deepest accepted node.  Every emitted token is thus a draw
+    from the base model given its prefix.  ``return_margins`` adds, per node,
+    the gap between its two best scores (near-ties decide in rounding).
+    """
+    n = len(parent)
+    z = []
+    gaps = np.full(n, np.inf)
+    for u in range(n):
+        sc = sample_scores(logits[u], temperature, seed, step, b, u)
+        top2 = np.partition(sc, -2)[-2:] if len(sc) > 1 else np.array([-np.inf, sc[0]])
+        gaps[u] = float(top2[1] - top2[0])
+        z.append(int(np.flatnonzero(sc == sc.max())[0]))
+    a, path, best = _accept_sweep(tokens, parent,
+                                  lambda i: int(tokens[i]) == z[int(parent[i])], n_heads)
+    out = dict(accept_len=a, path=path, next_token=z[best], best=best, samples=z)
+    if return_margins:
+        out["margins"] = gaps
+    return out
+
+
+# ----------------------------------------------------------------------------
 # KV compaction (only the kept branch stays in the cache: "Medusa Heads",
 # tree attention section, the longest accepted branch is kept)
 # ----------------------------------------------------------------------------
@@ -395,16 +506,20 @@ def sequential_greedy(model, prompt, n_new, capacity=None):
 
 
 def medusa_generate(model, prompt, n_new, parent, rank, mode="greedy", temperature=1.0,
-                    epsilon=0.3, delta=0.09, heads=None, capacity=None, record=None):
+                    epsilon=0.3, delta=0.09, heads=None, capacity=None, record=None, seed=0):
     """Medusa decoding loop, steps in the order the pages give them.
 
     1. Prefill; root = argmax of the last row; heads on the last hidden state
        give per-head top-k (k = max rank + 1 of the template).
     2. Build the tree from the template; verify all nodes in one forward pass
        with the ancestor mask.
-    3. Accept the longest branch (greedy or typical); emit its a+1 tokens.
+    3. Accept the longest branch (greedy, typical or sampled); emit its a+1
+       tokens.
     4. Keep only that branch in the cache; feed its last hidden state to the
-       heads for the next round; next root = argmax of its last row.
+       heads for the next round; next root = argmax of its last row (a draw
+       from it in sampled mode).
+    Sampled mode draws the prefill root at step 0 (node 0) and verifies decode
+    step s = 1, 2, ... with key (seed, s).
     ``heads`` (optional) replaces the learned heads by a function
     hidden_row -> [K, V] logits (used by pins).  ``record`` collects per-step
     dicts.  Returns (tokens int32[n_new], cache, ctx).
@@ -426,15 +541,22 @@ def medusa_generate(model, prompt, n_new, parent, rank, mode="greedy", temperatu
         lg = heads(hrow) if heads is not None else head_logits(hrow[None], model.w1, model.b1, model.w2)[:, 0]
         return [topk(lg[k], width)[0] for k in range(n_heads)]
 
-    root = argmax(logits[-1])
+    if mode == "sample":
+        root = sample_token(logits[-1], temperature, seed, 0, 0, 0)
+    else:
+        root = argmax(logits[-1])
     ids = head_topk(hf[-1])
     out = []
+    step = 0
     while len(out) < n_new:
+        step += 1
         tree = build_tree(parent, rank, root, ids, ctx)
         logits, hf = forward_rows(model, tree["tokens"], tree["pos"], tree["mask"], cache, ctx)
         lf = f32(logits)
         if mode == "greedy":
             res = accept_greedy(lf, tree["tokens"], parent, n_heads)
+        elif mode == "sample":
+            res = accept_sample(lf, tree["tokens"], parent, n_heads, temperature, seed, step)
         else:
             res = accept_typical(lf, tree["tokens"], parent, n_heads, temperature, epsilon, delta)
         a, path = res["accept_len"], res["path"]
