@@ -280,6 +280,30 @@ def cpu_baseline(torch, dec, model_src, emitted_per_step, sample_layers):
                 step_seconds_extrapolated=round(step_s, 3), _ids=len(ids))
 
 
+def sampled_accept_us(torch, M):
+    """Sampled verification alone on one step's verification logits (64 nodes,
+    vocab 32000): one Philox4x64-10 block per 4 entries, Gumbel-max per node,
+    the tree sweep.  Graph-timed; the step counter advances every call."""
+    import numpy as np
+    import synth
+    N, V, K = 64, 32000, 5
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(9)
+    logits = torch.randn((1, N, V), generator=gen, device="cuda")
+    parent, _ = synth.prune_template(*synth.tree_template((4, 3, 2, 2, 1)), N, 2)
+    par = torch.tensor(parent[None], dtype=torch.int32, device="cuda")
+    tok = torch.zeros((1, N), dtype=torch.int32, device="cuda")
+    rng = M.rng_state(1, 0)
+    out = (torch.empty(1, dtype=torch.int32, device="cuda"),
+           torch.empty((1, K + 1), dtype=torch.int32, device="cuda"),
+           torch.empty(1, dtype=torch.int32, device="cuda"))
+    ws = M._ws(M._lib.medusa_accept_ws(1, N), "cuda")
+    us, med = graph_time_us(torch, [lambda: M.medusa_accept_sample(logits, tok, par, K, 1.0, rng,
+                                                                    out=out, ws=ws)], reps=10, inner=20)
+    return dict(us=round(us, 2), us_median=round(med, 2), nodes=N, vocab=V,
+                logits_gbs=round(N * V * 4 / (us * 1e-6) / 1e9, 1))
+
+
 def kernels_only(torch, M, synth, log):
     """Counter-pass workload: 32 gate/up projection launches (64 rows, 7B
     shapes, one weight copy per layer as in the step), 17 tree-attention
@@ -402,28 +426,34 @@ def main():
         plain = round(args.steps / (time.perf_counter() - p0), 2)
         del pdec
 
-    typical = None
-    if args.mode == "greedy" and not args.skip_plain:
-        log("[bench] typical acceptance (epsilon 0.3, delta 0.09) on the same model")
-        tdec = MedusaDecoder(model, parent, rank, capacity=capacity, mode="typical",
-                             epsilon=0.3, delta=0.09)
-        tdec.prefill(prompt)
-        tdec.capture()
+    def other_mode(mode, **kw):
+        """Emitted tokens/s of the same step with another acceptance rule."""
+        odec = MedusaDecoder(model, parent, rank, capacity=capacity, mode=mode, **kw)
+        odec.prefill(prompt)
+        odec.capture()
         for _ in range(args.warmup):
-            int(tdec.step_graph()[0].item())
-        tdec.prefill(prompt)
+            int(odec.step_graph()[0].item())
+        odec.prefill(prompt)
         torch.cuda.synchronize()
-        t_emit, t_acc = 0, []
+        o_emit, o_acc = 0, []
         q0 = time.perf_counter()
         for _ in range(args.steps):
-            a = int(tdec.step_graph()[0].item())
-            t_acc.append(a)
-            t_emit += a + 1
+            a = int(odec.step_graph()[0].item())
+            o_acc.append(a)
+            o_emit += a + 1
         torch.cuda.synchronize()
         dt_ = time.perf_counter() - q0
-        typical = dict(tokens_per_s=round(t_emit / dt_, 2), mean_accept_len=round(float(np.mean(t_acc)), 3),
-                       ms_per_step=round(1000 * dt_ / args.steps, 3), epsilon=0.3, delta=0.09)
-        del tdec
+        del odec
+        return dict(tokens_per_s=round(o_emit / dt_, 2), mean_accept_len=round(float(np.mean(o_acc)), 3),
+                    ms_per_step=round(1000 * dt_ / args.steps, 3), **kw)
+
+    typical = sampled = None
+    if args.mode == "greedy" and not args.skip_plain:
+        log("[bench] typical acceptance (epsilon 0.3, delta 0.09) on the same model")
+        typical = other_mode("typical", epsilon=0.3, delta=0.09)
+        log("[bench] sampled verification (temperature 1, seed 0) on the same model")
+        sampled = other_mode("sample", temperature=1.0, seed=0)
+        sampled["accept_kernel"] = sampled_accept_us(torch, M)
 
     c2 = None if args.skip_c2 else tree_attention_c2(torch, M, synth)
     c3 = c3b = c5 = None
@@ -453,6 +483,7 @@ def main():
         "verified_tree_tokens_per_s": round(64 * args.steps / (t1 - t0), 1),
         "plain_decode_tokens_per_s": plain,
         "typical": typical,
+        "sampled": sampled,
         "roofline": {"bound": "hbm", "kernel": "gemm_xdma_kernel (gate/up projection, SwiGLU epilogue)",
                      "achieved": round(gu_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gu_gbs / HBM_PEAK_GBS, 4),

@@ -217,6 +217,35 @@ int32_t medusa_accept(const float* logits, int64_t V, const int32_t* tokens,
                       void* stream);
 
 /* ------------------------------------------------------------------------
+ * medusa_accept_sample: sampled verification, the rejection sampling against
+ * the base model that keeps Medusa-1's output distribution that of the base
+ * model ("Têtes de décodage Medusa", section "Plongée profonde" and its
+ * "Questions fréquemment posées" entry on lossless acceleration).
+ * The candidates are fixed top-k tokens, so testing them one by one against
+ * p = softmax(logits[node] / temperature), renormalised over the tokens not
+ * yet rejected, takes child c with probability p(token c) and otherwise ends
+ * the branch with a draw from the rest: the law of one draw z ~ p at every
+ * visited node.  That is what is computed: for every node u one draw z_u by
+ * Gumbel-max, argmax over v of fl(fl(logits[u, v] * fl(1 / temperature)) +
+ * G), G = -log(-log(u_v)) in float, u_v = ((w >> 41) + 1/2) / 2^23 where w
+ * is word v % 4 of Philox4x64-10 (Salmon et al., SC 2011) with key (seed,
+ * step) and counter (v / 4, u, b, 0); lowest v on a tie.  Node i is accepted
+ * iff its parent is and tokens[i] == z_parent; accept_len, path as for
+ * medusa_accept; next_token [B] = z at the deepest accepted node.
+ *   rng [2] uint64 (device): (seed, step).  The call draws with that key and
+ *     then adds 1 to step on the device, so a captured decode step replays
+ *     with fresh noise.  Calls sharing one rng buffer are ordered by their
+ *     stream.  A one-node tree (N = 1, parent [-1]) samples a plain next
+ *     token.
+ *   temperature > 0.  ws: medusa_accept_ws(B, N) bytes.
+ * ---------------------------------------------------------------------- */
+int32_t medusa_accept_sample(const float* logits, int64_t V, const int32_t* tokens,
+                             const int32_t* parent, int32_t B, int32_t N, int32_t K,
+                             float temperature, uint64_t* rng, int32_t* accept_len,
+                             int32_t* path, int32_t* next_token, void* ws, size_t ws_bytes,
+                             void* stream);
+
+/* ------------------------------------------------------------------------
  * kv_compact: keep only the accepted branch in every layer's cache (the
  * branch the model accepted is kept: "Medusa Heads", tree section).
  * For d = 0..accept_len[b]: slot ctx[b]+d <- slot ctx[b]+path[b, d], K and V,

@@ -6,7 +6,8 @@ successivi" and "Attenzione sull'albero e accettazione"):
   build_tree  (root token + per-head top-k -> N tree tokens, positions, masks)
   verification forward of the N tree rows in ONE pass (Llama-style layers;
       tree-masked attention over the paged KV cache + the tree's own keys)
-  accept      (greedy or typical; longest accepted branch, next root token)
+  accept      (greedy, typical or sampled; longest accepted branch, next root
+              token)
   kv_compact  (keep only the accepted branch in every layer's cache)
   gather_rows + heads (the kept branch's last hidden state -> next top-k)
 
@@ -98,10 +99,13 @@ class MedusaDecoder:
 
     ``parent``, ``rank``: the tree template (node 0 = root); a single-node
     template turns the loop into plain greedy decoding (no heads).
+    ``mode``: "greedy", "typical" or "sample" (sampled verification with the
+    counter-based stream keyed by ``seed``: the prefill's next token draws at
+    step 0, decode step s at step s).
     """
 
     def __init__(self, model: DeviceModel, parent, rank, capacity, page_size=16, mode="greedy",
-                 temperature=1.0, epsilon=0.3, delta=0.09):
+                 temperature=1.0, epsilon=0.3, delta=0.09, seed=0):
         self.m = model
         dev = model.device
         parent = np.asarray(parent, np.int32)
@@ -114,6 +118,9 @@ class MedusaDecoder:
         self.width = int(rank.max()) + 1
         if self.K > 0:
             M.medusa_tree_validate(parent, rank, self.K, self.width)
+        if mode not in ("greedy", "typical", "sample"):
+            raise ValueError(f"mode {mode!r}")
+        self.sampled = mode == "sample"
         self.mode = 0 if mode == "greedy" else 1
         self.T, self.eps, self.delta = temperature, epsilon, delta
         self.P = page_size
@@ -151,6 +158,13 @@ class MedusaDecoder:
                                                                   model.head_dim, dt)
                                  for n in range(1, 65)] + [256]), dev)
         self.out = (torch.zeros(1, **i32), torch.zeros((1, self.K + 1), **i32), torch.zeros(1, **i32))
+        # sampled mode: (seed, step) on the device, advanced by every draw; a
+        # one-node tree draws the prefill's next token
+        self.seed = seed
+        self.rng = M.rng_state(seed, 0, dev)
+        self.one_tok = torch.zeros((1, 1), **i32)
+        self.one_parent = torch.full((1, 1), -1, **i32)
+        self.one_out = (torch.zeros(1, **i32), torch.zeros((1, 1), **i32), torch.zeros(1, **i32))
         self.new_ctx = torch.zeros(1, **i32)
         self.src = torch.zeros((1, self.K + 1), **i32)
         self.dst = torch.zeros((1, self.K + 1), **i32)
@@ -201,6 +215,7 @@ class MedusaDecoder:
         prompt = np.asarray(prompt, np.int32)
         dev = self.m.device
         self._set_ctx(0)
+        self.rng.copy_(M.rng_state(self.seed, 0, dev))  # a generation's draws start at step 0
         c = 0
         while c < len(prompt):
             n = min(64, len(prompt) - c)
@@ -211,8 +226,14 @@ class MedusaDecoder:
             logits, hN = self.forward(tok, pos, mask)
             c += n
             self._set_ctx(c)
-        ids, _ = M.medusa_topk(logits[n - 1:n].contiguous(), 1)
-        self.root.copy_(ids.reshape(1))
+        if self.sampled:
+            _, _, nxt = M.medusa_accept_sample(logits[None, n - 1:n], self.one_tok, self.one_parent,
+                                               0, self.T, self.rng, out=self.one_out,
+                                               ws=self.acc_ws)
+            self.root.copy_(nxt)
+        else:
+            ids, _ = M.medusa_topk(logits[n - 1:n].contiguous(), 1)
+            self.root.copy_(ids.reshape(1))
         self._heads(hN[n - 1:n].contiguous())
 
     def step(self):
@@ -220,8 +241,13 @@ class MedusaDecoder:
         tokens, pos, mask = M.medusa_build_tree(self.parent, self.rank, self.root, self.topk_ids,
                                                 self.ctx)
         logits, hN = self.forward(tokens, pos, mask)
-        acc, path, nxt = M.medusa_accept(logits[None], tokens, self.parent, self.K, self.mode,
-                                         self.T, self.eps, self.delta, out=self.out, ws=self.acc_ws)
+        if self.sampled:
+            acc, path, nxt = M.medusa_accept_sample(logits[None], tokens, self.parent, self.K,
+                                                    self.T, self.rng, out=self.out, ws=self.acc_ws)
+        else:
+            acc, path, nxt = M.medusa_accept(logits[None], tokens, self.parent, self.K, self.mode,
+                                             self.T, self.eps, self.delta, out=self.out,
+                                             ws=self.acc_ws)
         M.kv_compact(self.Kc, self.Vc, self.page_table, self.ctx, path, acc, new_ctx=self.new_ctx,
                      src=self.src, dst=self.dst)
         if self.K > 0:

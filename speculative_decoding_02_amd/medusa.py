@@ -42,6 +42,8 @@ _SIGS = {
     "medusa_accept_ws": (sz, [i32, i32]),
     "medusa_accept": (i32, [vp, i64, vp, vp, i32, i32, i32, i32, f32, f32, f32, vp, vp, vp, vp,
                             sz, vp]),
+    "medusa_accept_sample": (i32, [vp, i64, vp, vp, i32, i32, i32, f32, vp, vp, vp, vp, vp, sz,
+                                   vp]),
     "kv_compact": (i32, [C.POINTER(vp), C.POINTER(vp), i32, vp, i32, i32, vp, vp, vp, i32, i32,
                          i32, i32, i32, vp, vp, vp, vp]),
     "medusa_embed": (i32, [vp, i64, vp, i64, i64, i32, vp, vp]),
@@ -247,6 +249,34 @@ def medusa_accept(logits, tokens, parent, K, mode=0, temperature=1.0, epsilon=0.
     _check("medusa_accept", _lib.medusa_accept(
         _p(logits), V, _p(tokens), _p(parent), B, N, K, int(mode), float(temperature),
         float(epsilon), float(delta), _p(acc), _p(path), _p(nxt), _p(ws), ws.numel(), _stream()))
+    return acc, path, nxt
+
+
+def rng_state(seed, step=0, device="cuda"):
+    """Device (seed, step) pair for medusa_accept_sample (uint64 bit patterns)."""
+    import numpy as np
+    return torch.from_numpy(np.array([seed, step], dtype=np.uint64).view(np.int64)).to(device)
+
+
+def medusa_accept_sample(logits, tokens, parent, K, temperature, rng, out=None, ws=None):
+    """Sampled verification.  logits [B,N,V] float; tokens, parent [B,N] int32;
+    rng: 2-element int64 device tensor (seed, step) holding uint64 bit patterns,
+    advanced by one on the device -> (accept_len [B], path [B,K+1], next [B])."""
+    B, N, V = logits.shape
+    dev = logits.device
+    if rng.numel() != 2 or rng.dtype != torch.int64:
+        raise ValueError("rng must be a 2-element int64 tensor (seed, step)")
+    if out is None:
+        out = (torch.empty(B, dtype=torch.int32, device=dev),
+               torch.empty((B, K + 1), dtype=torch.int32, device=dev),
+               torch.empty(B, dtype=torch.int32, device=dev))
+    need = _lib.medusa_accept_ws(B, N)
+    if ws is None or ws.numel() < need:
+        ws = _ws(need, dev)
+    acc, path, nxt = out
+    _check("medusa_accept_sample", _lib.medusa_accept_sample(
+        _p(logits), V, _p(tokens), _p(parent), B, N, K, float(temperature), _p(rng), _p(acc),
+        _p(path), _p(nxt), _p(ws), ws.numel(), _stream()))
     return acc, path, nxt
 
 

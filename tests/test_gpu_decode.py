@@ -1,7 +1,8 @@
 """GPU end to end on the tiny fp32 decoder: Medusa greedy decoding through
 libmedusa emits exactly the tokens of the oracle's sequential greedy decoding
 (the lossless claim of greedy acceptance), and so does plain one-token greedy
-decoding through the same library."""
+decoding through the same library.  Sampled verification emits the oracle's
+sampled Medusa decoding token for token (same counter-based stream)."""
 import numpy as np
 import pytest
 import torch
@@ -83,3 +84,28 @@ def test_c1_graph_replays_match_eager_and_oracle(c1):
     got2 = dec.generate(prompt, 64, graph=True)
     assert got2.tolist() == seq.tolist()
     assert torch.isfinite(scratch)
+
+
+@pytest.mark.parametrize("T", [1.0, 0.6])
+def test_c1_medusa_sampled_equals_oracle_sampled(c1, T):
+    """Sampled verification (rejection sampling against the base model, draws
+    from the shared Philox stream keyed by the seed) emits the oracle's tokens;
+    the graph-replayed step emits the same."""
+    from speculative_decoding_02_amd.decoder import DeviceModel, MedusaDecoder
+    m, prompt, _ = c1
+    case(f"c1 medusa sampled T={T}")
+    parent, rank = synth.tree_template((2, 3))
+    ref, _, _ = orc.medusa_generate(m, prompt, 48, parent, rank, mode="sample", temperature=T,
+                                    seed=5)
+    dm = DeviceModel(m, dtype=torch.float32)
+    dec = MedusaDecoder(dm, parent, rank, capacity=32 + 48 + 16, mode="sample", temperature=T,
+                        seed=5)
+    got = dec.generate(prompt, 48)
+    assert got.tolist() == ref.tolist(), _report(ref, got)
+    assert got2_equal(dec, prompt, ref)
+
+
+def got2_equal(dec, prompt, ref):
+    got = dec.generate(prompt, len(ref), graph=True)
+    assert got.tolist() == ref.tolist(), _report(ref, got)
+    return True

@@ -365,6 +365,78 @@ def test_accept_typical(lib, seed, eps, delta):
     assert near < B
 
 
+# --------------------------------------------------------- sampled accept ---
+def _plant_draws(seed, T, rng_seed, step, parent, tokens, logits, frac=0.7):
+    """Make many candidates equal to their parent's oracle draw (so that the
+    sampled walks go deep), at most one child per parent."""
+    tokens = tokens.copy()
+    rng = np.random.default_rng(seed + 100)
+    for b in range(tokens.shape[0]):
+        z = orc.accept_sample(logits[b], tokens[b], parent[b], 5, T, rng_seed, step, b=b)["samples"]
+        taken = set()
+        for i in range(1, tokens.shape[1]):
+            p = int(parent[b, i])
+            if p not in taken and rng.random() < frac:
+                tokens[b, i] = z[p]
+                taken.add(p)
+    return tokens
+
+
+@pytest.mark.parametrize("seed", range(3))
+@pytest.mark.parametrize("V,T,B", [(1000, 1.0, 3), (1001, 0.6, 3), (32000, 1.0, 1)])
+def test_accept_sample(lib, seed, V, T, B):
+    """Draws (Philox4x64-10 + Gumbel-max), walk and next token equal the
+    oracle's on the same logits and (seed, step); decisions within float32
+    rounding of a tie (oracle score gap < 1e-4 at a node the walk reads) are
+    counted and skipped.  The step counter advances by one per call."""
+    case(f"accept sample seed={seed} V={V} T={T} B={B}")
+    N, K = 64, 5
+    rng_seed, step = 1000 + seed, 7 + seed
+    parent, tokens, logits = _accept_inputs(seed, B, N, V)
+    tokens = _plant_draws(seed, T, rng_seed, step, parent, tokens, logits)
+    rng = lib.rng_state(rng_seed, step)
+    acc, path, nxt = lib.medusa_accept_sample(dev(logits), dev(tokens), dev(parent), K, T, rng)
+    assert host(rng).view(np.uint64).tolist() == [rng_seed, step + 1]
+    near, deep = 0, 0
+    for b in range(B):
+        r = orc.accept_sample(logits[b], tokens[b], parent[b], K, T, rng_seed, step, b=b,
+                              return_margins=True)
+        walk = [int(x) for x in r["path"] if x >= 0]
+        if np.min(r["margins"][walk]) < 1e-4:
+            near += 1
+            continue
+        assert int(host(acc)[b]) == r["accept_len"]
+        assert host(path[b]).tolist() == r["path"].tolist()
+        assert int(host(nxt)[b]) == r["next_token"]
+        deep += r["accept_len"] >= 2
+    assert near < B and (deep >= 1 or B == 1)
+
+
+def test_accept_sample_single_node_and_repeat(lib):
+    """A one-node tree draws a plain next token (per sequence); the same
+    (seed, step) draws the same tokens, the next step other ones."""
+    case("accept sample single node")
+    B, V, T = 4, 5003, 0.8
+    logits = (np.random.default_rng(3).standard_normal((B, 1, V)) * 1.5).astype(np.float32)
+    tokens = np.zeros((B, 1), np.int32)
+    parent = -np.ones((B, 1), np.int32)
+    rng = lib.rng_state(77, 0)
+    outs = []
+    for _ in range(2):
+        rng.copy_(lib.rng_state(77, 0))
+        acc, path, nxt = lib.medusa_accept_sample(dev(logits), dev(tokens), dev(parent), 0, T, rng)
+        outs.append(host(nxt).tolist())
+        assert host(acc).tolist() == [0] * B
+    assert outs[0] == outs[1]
+    _, _, nxt2 = lib.medusa_accept_sample(dev(logits), dev(tokens), dev(parent), 0, T, rng)
+    for b in range(B):
+        sc = orc.sample_scores(logits[b, 0], T, 77, 0, b, 0)
+        top2 = np.sort(sc)[-2:]
+        if top2[1] - top2[0] >= 1e-4:
+            assert outs[0][b] == orc.sample_token(logits[b, 0], T, 77, 0, b, 0)
+    assert host(nxt2).tolist() != outs[0]
+
+
 # -------------------------------------------------------------- kv_compact ---
 @pytest.mark.parametrize("dt", DTS, ids=DTN.get)
 def test_kv_compact(lib, dt):

@@ -63,6 +63,13 @@ def test_bad_arguments_are_rejected_on_the_host(M):
     assert lib.medusa_linear_rmsnorm(None, 4, 64, None, 10, 1, None, None, 1e-5, None, None, 0,
                                      None) == 2  # N not a multiple of 4
     assert lib.medusa_rmsnorm(None, 2, 64, None, -1.0, 1, None, None) == 1  # eps < 0
+    # sampled acceptance: temperature must be positive; N outside [1, 64]
+    assert lib.medusa_accept_sample(None, 100, None, None, 1, 9, 2, 0.0, None, None, None, None,
+                                    None, 0, None) == 1
+    assert lib.medusa_accept_sample(None, 100, None, None, 1, 65, 2, 1.0, None, None, None, None,
+                                    None, 0, None) == 2
+    assert lib.medusa_accept_sample(None, 100, None, None, 0, 9, 2, 1.0, None, None, None, None,
+                                    None, 0, None) == 0  # empty batch
     # zero rows: nothing to do, success without pointers
     assert lib.medusa_linear(None, 0, 0, 8, None, 4, 1, 1, 0, None, None, None, 0, None, 0,
                              None) == 0
