@@ -345,9 +345,13 @@ def sample_uniforms(V, seed, step, b, node):
 
 def sample_scores(logits_row, temperature, seed, step, b, node):
     """Gumbel-max scores z/T + G with G = -log(-log(u)): the index of their
-    maximum is a draw from softmax(z/T) (float64; z rounded to float32)."""
+    maximum is a draw from softmax(z/T).  The decision is taken in float32,
+    the precision of the logits: G is computed in float64 and rounded, and
+    the score is float32(float32(z * float32(1/T)) + G)."""
     u = sample_uniforms(len(logits_row), seed, step, b, node)
-    return f32(logits_row).astype(F64) / float(temperature) - np.log(-np.log(u))
+    g = f32(-np.log(-np.log(u)))
+    inv_t = np.float32(1.0) / np.float32(temperature)
+    return (f32(logits_row) * inv_t) + g
 
 
 def sample_token(logits_row, temperature, seed, step, b, node):
