@@ -106,6 +106,24 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// Reductions over the four lanes {l, l^16, l^32, l^48} (the 16-lane rows of a
+// wave that hold the same MFMA output column), with gfx950's row-swap
+// permutes instead of LDS round trips: after a 16-row swap of x with itself
+// each lane holds {x_l, x_(l^16)}, after a 32-row swap {x_l, x_(l^32)}.  The
+// operations are commutative, so all four lanes get bitwise the same result.
+__device__ __forceinline__ float rows4_max(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float rows4_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // One 256-thread workgroup normalises one row of H floats held as up to
 // RMS_V4 f32x4 per thread (vector e = threadIdx.x + 256 i, e < H/4): the
 // row's sum of squares in a fixed order (per thread, then per wave, then the
