@@ -759,6 +759,178 @@ __global__ __launch_bounds__(64 * XB_WAVES) void gemm_xdma_kernel(
   }
 }
 
+// Large-row projection (M >= 256 rows: batched serving, heads over many
+// rows), where the product is MFMA-bound rather than weight-stream bound.
+//   * A workgroup computes a TN x TM tile of Y^T (TN weight rows by TM
+//     activation rows) with WGN x WGM waves, each a WN x WM sub-tile of FN x FM
+//     16x16 MFMA blocks.  The weight rows are the A operand and the
+//     activation rows the B operand, so a lane's four results are four
+//     consecutive output columns of one output row (vector stores).
+//   * The contraction advances in stages of BK elements: a stage holds the
+//     TN + TM rows' 2*BK-byte pieces, brought in by LDS-DMA (each lane's
+//     source row and chunk are fixed, only the contraction offset moves) into
+//     a ring of R stages: the first R stages are issued together, a slot is
+//     refilled as soon as every wave has read it, and the wait before stage
+//     t counts exactly the later stages already issued (one barrier per
+//     stage, no fence).
+//   * Inside a stage, row r keeps its 16-byte chunk c at position
+//     c ^ ((r / L) % C), with L = 256 / (2*BK) rows per 64-bank line and C
+//     chunks per row: the 16 rows of one operand read then fall in 16
+//     distinct bank groups.
+//   * Workgroup ids are remapped so that the ids one XCD receives (the
+//     dispatcher deals them out round robin) walk the activation tiles of one
+//     weight tile: the weight tile is read from memory once per XCD.
+//   * Accumulation runs over the contraction in stage order, the same for
+//     every shape of this plan: results depend on (M, Kd, N) only.
+constexpr int GB_KALIGN = 64;  // contraction multiple the plan requires
+template <int TN, int TM, int WGN, int WGM, int BK, int R, int EPI>
+__global__ __launch_bounds__(64 * WGN * WGM) void gemm_big_kernel(
+    const bf16_t* __restrict__ X, int64_t xbs, int M, int Kd, const bf16_t* __restrict__ W, int Nw,
+    const bf16_t* __restrict__ bias, const void* aux, void* Y, int y_f32, int tilesN, int tilesM) {
+  using T = bf16_t;
+  constexpr int NW = WGN * WGM;
+  constexpr int WN = TN / WGN, WM = TM / WGM;
+  constexpr int FN = WN / 16, FM = WM / 16;
+  constexpr int ROWB = BK * 2;               // bytes of one row in a stage
+  constexpr int CPR = ROWB / 16;             // 16-byte chunks per row
+  constexpr int LPR = 256 / ROWB;            // rows sharing one 64-bank line
+  constexpr int KSTEPS = BK / 32;            // MFMA contraction steps per stage
+  constexpr int STAGEB = (TN + TM) * ROWB;
+  constexpr int RPD = 1024 / ROWB;           // rows per DMA instruction
+  constexpr int DPW = (TN + TM) / RPD / NW;  // DMA instructions per wave per stage
+  static_assert(BK == 32 || BK == 64, "stage of 32 or 64 contraction elements");
+  static_assert(GB_KALIGN % BK == 0, "the plan's contraction multiple covers a stage");
+  static_assert(DPW >= 1 && DPW * NW * RPD == TN + TM, "a stage splits into whole DMAs per wave");
+  static_assert(R >= 2 && R <= 4 && (R - 1) * DPW < 64, "ring of 2..4 stages, vmcnt range");
+  static_assert(EPI != MEDUSA_EPI_SWIGLU || WN % 32 == 0, "gate/up block pairs inside a wave");
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[R * STAGEB];
+
+  const int tiles = tilesN * tilesM;
+  const int g = blockIdx.y;  // batch element
+  int id = blockIdx.x;
+  const int q8 = tiles / 8;
+  if (id < 8 * q8) id = (id % 8) * q8 + id / 8;  // XCD-aware: a bijection of [0, 8*q8)
+  const int nt = id / tilesM, mt = id % tilesM;
+  const int n0 = nt * TN, m0 = mt * TM;
+  const T* Wg = W + (int64_t)g * Nw * Kd;
+  const T* Xg = X + (int64_t)g * xbs;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+  const int wn = wave % WGN, wm = wave / WGN;
+
+  // DMA sources of this lane (rows past the matrix edge re-read its last row;
+  // their results are not stored)
+  const T* src[DPW];
+#pragma unroll
+  for (int i = 0; i < DPW; ++i) {
+    const int r = (wave * DPW + i) * RPD + lane / CPR;      // stage row this lane fills
+    const int c = (lane % CPR) ^ ((r / LPR) % CPR);          // chunk fetched for its position
+    src[i] = r < TN ? Wg + (int64_t)min(n0 + r, Nw - 1) * Kd + c * 8
+                    : Xg + (int64_t)min(m0 + r - TN, M - 1) * Kd + c * 8;
+  }
+  const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)lds;
+  auto issue = [&](int t, int slot) {
+#pragma unroll
+    for (int i = 0; i < DPW; ++i)
+      lds_dma16(src[i] + t * BK, lds_base + slot * STAGEB + (wave * DPW + i) * 1024);
+  };
+  auto wait_stages = [&](int n) {  // at most n stages of this wave's DMA in flight
+    switch (n) {
+      case 0: __builtin_amdgcn_s_waitcnt(waitcnt_vm(0)); break;
+      case 1: __builtin_amdgcn_s_waitcnt(waitcnt_vm(1 * DPW)); break;
+      case 2: __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * DPW)); break;
+      default: __builtin_amdgcn_s_waitcnt(waitcnt_vm(3 * DPW)); break;
+    }
+  };
+
+  // operand offsets inside a stage (A: weight rows first, B: activation
+  // rows), per contraction step ks (chunk 4*ks + lg)
+  int aofs[KSTEPS][FN], bofs[KSTEPS][FM];
+#pragma unroll
+  for (int ks = 0; ks < KSTEPS; ++ks) {
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) {
+      const int r = wn * WN + fn * 16 + lr;
+      aofs[ks][fn] = r * ROWB + (((4 * ks + lg) ^ ((r / LPR) % CPR)) * 16);
+    }
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+      const int r = TN + wm * WM + fm * 16 + lr;
+      bofs[ks][fm] = r * ROWB + (((4 * ks + lg) ^ ((r / LPR) % CPR)) * 16);
+    }
+  }
+
+  f32x4 acc[FN][FM];
+#pragma unroll
+  for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) acc[fn][fm] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nk = Kd / BK;
+  const int first = min(nk, R);
+  for (int t = 0; t < first; ++t) issue(t, t);
+  for (int t = 0; t < nk; ++t) {
+    // stages issued before this point: min(nk, R + max(t - 1, 0))
+    wait_stages(t == 0 ? first - 1 : min(nk - 1 - t, R - 2));  // stage t has landed
+    __builtin_amdgcn_s_waitcnt(WAITCNT_LGKM0);  // ... and this wave's reads of stage t-1
+    __builtin_amdgcn_s_barrier();               // ... and every other wave's
+    asm volatile("" ::: "memory");
+    if (t >= 1 && t - 1 + R < nk) issue(t - 1 + R, (t - 1) % R);
+    const unsigned char* sb = lds + (t % R) * STAGEB;
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      u32x4 af[FN], bfr[FM];
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn) af[fn] = *reinterpret_cast<const u32x4*>(sb + aofs[ks][fn]);
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm) bfr[fm] = *reinterpret_cast<const u32x4*>(sb + bofs[ks][fm]);
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm) acc[fn][fm] = mfma_bf16_16x16x32(af[fn], bfr[fm], acc[fn][fm]);
+    }
+    asm volatile("" ::: "memory");
+  }
+
+  // epilogue: lane holds Y[m][n .. n+3], m = m0 + wm*WM + fm*16 + lr,
+  // n = n0 + wn*WN + fn*16 + 4*lg
+#pragma unroll
+  for (int fm = 0; fm < FM; ++fm) {
+    const int m = m0 + wm * WM + fm * 16 + lr;
+    if (m >= M) continue;
+    if constexpr (EPI == MEDUSA_EPI_SWIGLU) {
+      const int F = Nw / 2;
+      T* Yg = reinterpret_cast<T*>(Y) + (int64_t)g * M * F;
+#pragma unroll
+      for (int fp = 0; fp < FN; fp += 2) {  // gate block fp, up block fp + 1
+        const int nb = n0 + wn * WN + fp * 16;
+        if (nb >= Nw) continue;
+        const int f = nb / 2 + 4 * lg;
+        const f32x4 gt = acc[fp][fm], up = acc[fp + 1][fm];
+        *reinterpret_cast<u32x2*>(Yg + (int64_t)m * F + f) =
+            u32x2{pack_bf2(silu_f(gt[0]) * up[0], silu_f(gt[1]) * up[1]),
+                  pack_bf2(silu_f(gt[2]) * up[2], silu_f(gt[3]) * up[3])};
+      }
+    } else {
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn) {
+        const int n = n0 + wn * WN + fn * 16 + 4 * lg;
+        if (n >= Nw) continue;
+        const f32x4 v = acc[fn][fm];
+        if (EPI == MEDUSA_EPI_NONE) {
+          const int64_t o = (int64_t)g * M * Nw + (int64_t)m * Nw + n;
+          if (y_f32) *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(Y) + o) = v;
+          else *reinterpret_cast<u32x2*>(reinterpret_cast<T*>(Y) + o) = u32x2{pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3])};
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) xb_store<T, EPI>(g, M, Nw, xbs, bias, aux, Y, y_f32, m, n + r, v[r]);
+        }
+      }
+    }
+  }
+}
+
 // 16-row blocks per workgroup of the small-row kernel (SwiGLU needs its
 // gate/up pair of blocks in one tile, so it always takes at least 2)
 #ifndef MEDUSA_GEMM_NB
@@ -888,6 +1060,7 @@ struct GemmPlan {
   int xb_G;     // workgroups per (batch element, row tile, contraction split)
   int MT;       // activation-row tiles
   int xb_S;     // contraction splits of the block-range variant (partials when > 1)
+  int big;      // large-row MFMA tiling: 0 off, 1 = 256 x 256 tiles, 2 = 128 x 128 tiles
 };
 #ifndef MEDUSA_GEMM_XB_MIN_BLOCKS
 #define MEDUSA_GEMM_XB_MIN_BLOCKS 512
@@ -903,11 +1076,37 @@ struct GemmPlan {
 #ifndef MEDUSA_GEMM_XD_SPLIT
 #define MEDUSA_GEMM_XD_SPLIT 4
 #endif
+#ifndef MEDUSA_GEMM_BIG_MIN_M
+#define MEDUSA_GEMM_BIG_MIN_M 256
+#endif
+// stage depth and ring of the 256- and 128-wide large-row tilings (measured
+// at 1024 rows x 4096: 64-deep stages beat 32-deep ones by 6-12%; the ring
+// depth beyond two stages changed little)
+#ifndef MEDUSA_GEMM_BIG_BK1
+#define MEDUSA_GEMM_BIG_BK1 64
+#endif
+#ifndef MEDUSA_GEMM_BIG_R1
+#define MEDUSA_GEMM_BIG_R1 2
+#endif
+#ifndef MEDUSA_GEMM_BIG_BK2
+#define MEDUSA_GEMM_BIG_BK2 64
+#endif
+#ifndef MEDUSA_GEMM_BIG_R2
+#define MEDUSA_GEMM_BIG_R2 3
+#endif
 GemmPlan gemm_plan(int64_t M, int64_t Kd, int64_t Nw, int dt, int epi) {
   using namespace medusa;
   constexpr int XNB = MEDUSA_GEMM_XL_NB;
-  GemmPlan p{false, 1, false, 1, 0, 1, 1};
+  GemmPlan p{false, 1, false, 1, 0, 1, 1, 0};
   const int unit = epi == MEDUSA_EPI_SWIGLU ? 2 : 1;
+  // enough rows for the product to be MFMA-bound: square tiles, 256 wide when
+  // they alone give about one workgroup per compute unit
+  if (dt == MEDUSA_BF16 && M >= MEDUSA_GEMM_BIG_MIN_M && Kd % GB_KALIGN == 0 && Nw % (16 * unit) == 0 &&
+      Nw <= INT32_MAX / 2) {
+    const int64_t t256 = ((Nw + 255) / 256) * ((M + 255) / 256);
+    p.big = t256 >= 200 ? 1 : 2;
+    return p;
+  }
   const bool narrow = MEDUSA_GEMM_XB_DMA && Nw / 16 >= MEDUSA_GEMM_XD_MIN_BLOCKS;
   if (dt == MEDUSA_BF16 && M > 16 && Kd % XB_KC == 0 && Nw % (16 * unit) == 0 &&
       (Nw / 16 >= MEDUSA_GEMM_XB_MIN_BLOCKS || narrow) && Nw / 16 <= (1 << 24)) {
@@ -974,6 +1173,23 @@ static bool launch_gemm_t(const void* X, int64_t xbs, int64_t M, int64_t Kd, con
   constexpr int XNB = MEDUSA_GEMM_XL_NB;
   const medusa_host::GemmPlan plan = medusa_host::gemm_plan(M, Kd, Nw, sizeof(T) == 2 ? MEDUSA_BF16 : MEDUSA_F32, EPI);
   if constexpr (sizeof(T) == 2) {  // planned for bf16 only
+    if (plan.big) {
+      const T* Xt = reinterpret_cast<const T*>(X);
+      const T* Wt = reinterpret_cast<const T*>(W);
+      const T* Bt = reinterpret_cast<const T*>(bias);
+      if (plan.big == 1) {
+        const int tN = (int)((Nw + 255) / 256), tM = (int)((M + 255) / 256);
+        hipLaunchKernelGGL((gemm_big_kernel<256, 256, 2, 4, MEDUSA_GEMM_BIG_BK1, MEDUSA_GEMM_BIG_R1, EPI>),
+                           dim3((unsigned)(tN * tM), (unsigned)batch),
+                           dim3(512), 0, st, Xt, xbs, (int)M, (int)Kd, Wt, (int)Nw, Bt, aux, Y, y_f32, tN, tM);
+      } else {
+        const int tN = (int)((Nw + 127) / 128), tM = (int)((M + 127) / 128);
+        hipLaunchKernelGGL((gemm_big_kernel<128, 128, 2, 2, MEDUSA_GEMM_BIG_BK2, MEDUSA_GEMM_BIG_R2, EPI>),
+                           dim3((unsigned)(tN * tM), (unsigned)batch),
+                           dim3(256), 0, st, Xt, xbs, (int)M, (int)Kd, Wt, (int)Nw, Bt, aux, Y, y_f32, tN, tM);
+      }
+      return false;
+    }
     if (plan.xb) {
       const dim3 grid((unsigned)plan.xb_G, (unsigned)(batch * plan.MT), (unsigned)plan.xb_S);
       const T* Xt = reinterpret_cast<const T*>(X);

@@ -35,41 +35,101 @@ __device__ __forceinline__ void list_insert(float (&lv)[KMAX], int (&li)[KMAX], 
   }
 }
 
-// k rounds: the block-wide best of the threads' list heads is emitted and its
-// owner pops it (ids are unique, so exactly one owner).
+// Best (value, index) over a wave without LDS traffic: quad permutes (xor 1,
+// xor 2), the 8- and 16-lane mirrors, then gfx950's 16- and 32-row swaps.
+// The selection is a total order (ties: lower index), so every lane ends with
+// the same winner.
+__device__ __forceinline__ void pick(float& bv, int& bi, float ov, int oi) {
+  if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+}
+template <int CTRL>
+__device__ __forceinline__ void dpp_pick(float& bv, int& bi) {
+  const float ov = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(bv), CTRL, 0xF, 0xF, false));
+  const int oi = __builtin_amdgcn_mov_dpp(bi, CTRL, 0xF, 0xF, false);
+  pick(bv, bi, ov, oi);
+}
+__device__ __forceinline__ void wave_argmax(float& bv, int& bi) {
+  dpp_pick<0xB1>(bv, bi);   // quad_perm [1,0,3,2]
+  dpp_pick<0x4E>(bv, bi);   // quad_perm [2,3,0,1]
+  dpp_pick<0x141>(bv, bi);  // row_half_mirror: lane i <-> 7-i
+  dpp_pick<0x140>(bv, bi);  // row_mirror: lane i <-> 15-i
+  {
+    const auto sv = __builtin_amdgcn_permlane16_swap(__float_as_uint(bv), __float_as_uint(bv), false, false);
+    const auto si = __builtin_amdgcn_permlane16_swap((unsigned)bi, (unsigned)bi, false, false);
+    bv = __uint_as_float(sv[0]); bi = (int)si[0];
+    pick(bv, bi, __uint_as_float(sv[1]), (int)si[1]);
+  }
+  {
+    const auto sv = __builtin_amdgcn_permlane32_swap(__float_as_uint(bv), __float_as_uint(bv), false, false);
+    const auto si = __builtin_amdgcn_permlane32_swap((unsigned)bi, (unsigned)bi, false, false);
+    bv = __uint_as_float(sv[0]); bi = (int)si[0];
+    pick(bv, bi, __uint_as_float(sv[1]), (int)si[1]);
+  }
+}
+
+// k best of the threads' sorted lists.  k <= 16: every wave emits its own k
+// best (k rounds of a wave argmax over the list heads; the owner pops, ids
+// being unique), the four lists meet in LDS, and wave 0 selects k of those
+// 4k (one candidate per lane).  k > 16: k rounds of a block-wide argmax.
 template <int KMAX>
 __device__ __forceinline__ void block_select(float (&lv)[KMAX], int (&li)[KMAX], int k,
                                              int* __restrict__ ids, float* __restrict__ vals) {
-  __shared__ float sv[TOPK_THREADS / 64];
-  __shared__ int si[TOPK_THREADS / 64];
-  __shared__ int winner_i;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int r = 0; r < k; ++r) {
-    float bv = lv[0];
-    int bi = li[0];
+  if constexpr (KMAX <= 16) {
+    __shared__ float cv[TOPK_THREADS / 64][KMAX];
+    __shared__ int ci[TOPK_THREADS / 64][KMAX];
+    for (int r = 0; r < k; ++r) {
+      float bv = lv[0];
+      int bi = li[0];
+      wave_argmax(bv, bi);
+      if (lane == 0) { cv[wave][r] = bv; ci[wave][r] = bi; }
+      if (li[0] == bi) {
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const float ov = __shfl_xor(bv, o, 64);
-      const int oi = __shfl_xor(bi, o, 64);
-      if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
-    }
-    if (lane == 0) { sv[wave] = bv; si[wave] = bi; }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      float wv = sv[0];
-      int wi = si[0];
-      for (int w = 1; w < TOPK_THREADS / 64; ++w)
-        if (better(sv[w], si[w], wv, wi)) { wv = sv[w]; wi = si[w]; }
-      winner_i = wi;
-      ids[r] = wi;
-      vals[r] = wv;
+        for (int j = 0; j + 1 < KMAX; ++j) { lv[j] = lv[j + 1]; li[j] = li[j + 1]; }
+        lv[KMAX - 1] = -INFINITY;
+        li[KMAX - 1] = 0x7fffffff;
+      }
     }
     __syncthreads();
-    if (li[0] == winner_i) {
+    if (wave != 0) return;
+    static_assert(TOPK_THREADS / 64 * KMAX <= 64, "one candidate per lane");
+    const int w = lane / KMAX, j = lane % KMAX;
+    float v = -INFINITY;
+    int i = 0x7fffffff;
+    if (w < TOPK_THREADS / 64 && j < k) { v = cv[w][j]; i = ci[w][j]; }
+    for (int r = 0; r < k; ++r) {
+      float bv = v;
+      int bi = i;
+      wave_argmax(bv, bi);
+      if (lane == 0) { ids[r] = bi; vals[r] = bv; }
+      if (i == bi) { v = -INFINITY; i = 0x7fffffff; }
+    }
+  } else {
+    __shared__ float sv[TOPK_THREADS / 64];
+    __shared__ int si[TOPK_THREADS / 64];
+    __shared__ int winner_i;
+    for (int r = 0; r < k; ++r) {
+      float bv = lv[0];
+      int bi = li[0];
+      wave_argmax(bv, bi);
+      if (lane == 0) { sv[wave] = bv; si[wave] = bi; }
+      __syncthreads();
+      if (threadIdx.x == 0) {
+        float wv = sv[0];
+        int wi = si[0];
+        for (int w = 1; w < TOPK_THREADS / 64; ++w)
+          if (better(sv[w], si[w], wv, wi)) { wv = sv[w]; wi = si[w]; }
+        winner_i = wi;
+        ids[r] = wi;
+        vals[r] = wv;
+      }
+      __syncthreads();
+      if (li[0] == winner_i) {
 #pragma unroll
-      for (int j = 0; j + 1 < KMAX; ++j) { lv[j] = lv[j + 1]; li[j] = li[j + 1]; }
-      lv[KMAX - 1] = -INFINITY;
-      li[KMAX - 1] = 0x7fffffff;
+        for (int j = 0; j + 1 < KMAX; ++j) { lv[j] = lv[j + 1]; li[j] = li[j + 1]; }
+        lv[KMAX - 1] = -INFINITY;
+        li[KMAX - 1] = 0x7fffffff;
+      }
     }
   }
 }
@@ -161,6 +221,7 @@ void launch_topk(const float* logits, int64_t R, int64_t V, int k, int* ids, flo
                          S * k, k, ids, vals);                                                \
   } while (0)
   if (k <= 4) MEDUSA_TOPK(4);
+  else if (k <= 10) MEDUSA_TOPK(10);
   else if (k <= 16) MEDUSA_TOPK(16);
   else MEDUSA_TOPK(64);
 #undef MEDUSA_TOPK

@@ -106,6 +106,55 @@ def test_linear_epilogues(lib, dt):
         assert_close_stored(host(U5[k]), orc.head_hidden(X5, W5[k], b5[k]), TOL[dt], f"bias_silu_res H=4096 head {k}")
 
 
+# Large-row projections (M >= 256, bf16): MFMA-bound tiling, 128-wide tiles
+# when 256-wide ones would leave the chip under-filled; ragged rows/columns.
+@pytest.mark.parametrize("Mr,Kd,N", [(256, 256, 4096), (300, 512, 1040), (1024, 256, 12800),
+                                     (520, 256, 25600), (768, 1024, 2048), (260, 4096, 512)])
+def test_linear_large_rows(lib, Mr, Kd, N):
+    dt = torch.bfloat16
+    case(f"linear large rows M={Mr} Kd={Kd} N={N}")
+    g = synth.rngs(Mr * 5 + Kd + N, 2)
+    X = _rnd(dt, g[0].standard_normal((Mr, Kd), dtype=np.float32))
+    W = _rnd(dt, g[1].standard_normal((N, Kd), dtype=np.float32) * 0.05)
+    ref = orc.linear(X, W)
+    y32 = lib.medusa_linear(dev(X, dt), dev(W, dt), y_f32=True)
+    assert_close(host(y32), ref, 1e-4 * max(1, np.sqrt(Kd / 256)), "linear f32 out")
+    y = lib.medusa_linear(dev(X, dt), dev(W, dt))
+    assert_close_stored(host(y), ref, TOL[dt], "linear (stored in bf16)")
+    # the plan is a function of the shape: a second call is bitwise equal
+    assert torch.equal(lib.medusa_linear(dev(X, dt), dev(W, dt), y_f32=True), y32)
+
+
+def test_linear_large_rows_epilogues(lib):
+    dt = torch.bfloat16
+    case("linear large rows epilogues")
+    g = synth.rngs(77, 6)
+    Mr, H = 300, 256
+    X = _rnd(dt, g[0].standard_normal((Mr, H), dtype=np.float32))
+    W1 = _rnd(dt, g[1].standard_normal((2, H, H), dtype=np.float32) * 0.1)
+    b1 = _rnd(dt, g[2].standard_normal((2, H), dtype=np.float32) * 0.1)
+    U = lib.medusa_linear(dev(X, dt), dev(W1, dt), lib.EPI_BIAS_SILU_RES, bias=dev(b1, dt),
+                          aux=dev(X, dt))
+    for k in range(2):
+        assert_close_stored(host(U[k]), orc.head_hidden(X, W1[k], b1[k]), TOL[dt], f"bias_silu_res head {k}")
+    R = g[3].standard_normal((Mr, 1024)).astype(np.float32)
+    Wo = _rnd(dt, g[4].standard_normal((1024, H), dtype=np.float32) * 0.1)
+    x = dev(R, torch.float32)
+    lib.medusa_linear(dev(X, dt), dev(Wo, dt), lib.EPI_RES_ADD_F32, aux=x, out=x)
+    assert_close(host(x), R + orc.linear(X, Wo), 1e-3, "res_add")
+    from speculative_decoding_02_amd.decoder import interleave_gate_up
+    Wg = _rnd(dt, g[5].standard_normal((1024, H), dtype=np.float32) * 0.1)
+    Wu = _rnd(dt, g[5].standard_normal((1024, H), dtype=np.float32) * 0.1)
+    f = lib.medusa_linear(dev(X, dt), dev(interleave_gate_up(Wg, Wu), dt), lib.EPI_SWIGLU)
+    assert_close_stored(host(f), orc.silu(orc.linear(X, Wg)) * orc.linear(X, Wu), TOL[dt], "swiglu")
+    # residual projection + RMSNorm (the norm runs as its own pass here)
+    gain = _rnd(dt, 1 + 0.1 * g[3].standard_normal(1024).astype(np.float32))
+    x_f = dev(R, torch.float32)
+    out = lib.medusa_linear_rmsnorm(dev(X, dt), dev(Wo, dt), x_f, dev(gain, dt), 1e-5)
+    xr = R + orc.linear(X, Wo)
+    assert_close(host(out), orc.rmsnorm(xr, gain, 1e-5), TOL[dt], "norm vs oracle")
+
+
 @pytest.mark.parametrize("dt,Mr,Kd,N", [(torch.bfloat16, 64, 4096, 4096), (torch.bfloat16, 48, 11008, 4096),
                                          (torch.bfloat16, 20, 4096, 2048), (torch.bfloat16, 40, 512, 1024),
                                          (torch.bfloat16, 1, 4096, 4096), (torch.bfloat16, 64, 256, 8192),
@@ -177,7 +226,7 @@ def test_linear_qkv_rope(lib, dt, Mr, Kd, Hq, Hkv, D):
 
 
 # ------------------------------------------------------------------- heads ---
-@pytest.mark.parametrize("H,V,Mr", [(256, 1000, 4), (256, 8192, 64), (512, 16384, 24)])
+@pytest.mark.parametrize("H,V,Mr", [(256, 1000, 4), (256, 8192, 64), (512, 16384, 24), (256, 8192, 300)])
 def test_heads_zero_init_reproduces_lm_head_bitwise(lib, H, V, Mr):
     """The page's snippet on the GPU: W1 = 0, b1 = 0, W2 = lm_head copies
     (also at shapes that take the shared-activation projection kernel)."""
@@ -197,7 +246,7 @@ def test_heads_zero_init_reproduces_lm_head_bitwise(lib, H, V, Mr):
 @pytest.mark.parametrize("dt", DTS, ids=DTN.get)
 @pytest.mark.parametrize("Mr,H,V,K,k", [(1, 256, 1000, 3, 3), (7, 128, 515, 5, 10),
                                         (64, 256, 2000, 2, 4), (64, 256, 8192, 3, 10),
-                                        (20, 512, 12288, 2, 64)])
+                                        (20, 512, 12288, 2, 64), (260, 256, 4096, 2, 10)])
 def test_heads_vs_oracle(lib, dt, Mr, H, V, K, k):
     case(f"heads {DTN[dt]} M={Mr} H={H} V={V} K={K} k={k}")
     d = synth.heads_inputs(Mr + V, Mr, H, V, K, w1_std=0.05, w2_std=0.05,
