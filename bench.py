@@ -280,6 +280,36 @@ def cpu_baseline(torch, dec, model_src, emitted_per_step, sample_layers):
                 step_seconds_extrapolated=round(step_s, 3), _ids=len(ids))
 
 
+def batched_projections_f4(torch, M, rows=1024, reps=5):
+    """One 7B layer's projections for batched tree verification (16 sequences
+    x 64 nodes = 1024 rows, bf16): QKV 4096 -> 12288, O 4096 -> 4096 + residual,
+    gate/up 4096 -> 2 x 11008 + SwiGLU, down 11008 -> 4096 + residual; the
+    MFMA-bound tiling.  Graph-timed; FLOPs = 2 * rows * (sum of K x N)."""
+    H, F, Q = 4096, 11008, 12288
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(11)
+    bf = torch.bfloat16
+    w = lambda n, k: torch.randn((n, k), generator=gen, device="cuda").mul_(0.02).to(bf)
+    Wqkv, Wo, Wgu, Wd = w(Q, H), w(H, H), w(2 * F, H), w(H, F)
+    h = torch.randn((rows, H), generator=gen, device="cuda").to(bf)
+    o = torch.randn((rows, H), generator=gen, device="cuda").to(bf)
+    x = torch.randn((rows, H), generator=gen, device="cuda")
+    qkv = torch.empty((rows, Q), device="cuda", dtype=bf)
+    f = torch.empty((rows, F), device="cuda", dtype=bf)
+    ws = M._ws(max(M.linear_ws_bytes(rows, k, n, 1, M.BF16) for k, n in ((H, Q), (H, H), (H, 2 * F), (F, H))), "cuda")
+    launches = [lambda: M.medusa_linear(h, Wqkv, out=qkv, ws=ws),
+                lambda: M.medusa_linear(o, Wo, M.EPI_RES_ADD_F32, aux=x, out=x, ws=ws),
+                lambda: M.medusa_linear(h, Wgu, M.EPI_SWIGLU, out=f, ws=ws),
+                lambda: M.medusa_linear(f, Wd, M.EPI_RES_ADD_F32, aux=x, out=x, ws=ws)]
+    us, med = graph_time_us(torch, launches, reps=reps, inner=2)
+    us_layer = us * len(launches)
+    flops = 2.0 * rows * (H * Q + H * H + H * 2 * F + F * H)
+    tf = flops / (us_layer * 1e-6) / 1e12
+    return dict(workload=f"one 7B layer's projections at {rows} rows (16 sequences x 64 tree nodes), bf16",
+                us_per_layer=round(us_layer, 1), tflops=round(tf, 1), mfma_frac=round(tf / MFMA_PEAK_TFLOPS, 4),
+                timing="HIP events around graph replays of the four launches")
+
+
 def sampled_accept_us(torch, M):
     """Sampled verification alone on one step's verification logits (64 nodes,
     vocab 32000): one Philox4x64-10 block per 4 entries, Gumbel-max per node,
@@ -456,13 +486,15 @@ def main():
         sampled["accept_kernel"] = sampled_accept_us(torch, M)
 
     c2 = None if args.skip_c2 else tree_attention_c2(torch, M, synth)
-    c3 = c3b = c5 = None
+    c3 = c3b = c5 = f4 = None
     if not args.skip_extra:
         log("[bench] heads at the 7B shape: 64 rows, then 1024 rows")
         c3 = heads_c3(torch, M, 64)
         c3b = heads_c3(torch, M, 1024, reps=3)
         log("[bench] batched tree attention over a 13B-shaped stack")
         c5 = batched_attention_c5(torch, M, synth)
+        log("[bench] one layer's projections at 1024 rows")
+        f4 = batched_projections_f4(torch, M)
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] CPU oracle baseline (bounded sample)")
@@ -495,6 +527,7 @@ def main():
         "heads_c3": c3,
         "heads_c3b": c3b,
         "batched_attention_c5": c5,
+        "batched_projections_f4": f4,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

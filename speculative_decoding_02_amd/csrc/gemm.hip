@@ -998,7 +998,9 @@ __global__ __launch_bounds__(256) void split_reduce_rmsnorm_kernel(const float* 
   // Every load is unconditional (indices clamped; lanes past the row only
   // carry unused copies), so a batch of splits costs one memory round trip;
   // the adds keep split order.
-  constexpr int QB = 3;
+  // (the first batch of up to QB splits is loaded together with the
+  // residual row and the gain: one round trip for splits <= QB)
+  constexpr int QB = 4;
   f32x4 g[RMS_V4], v[RMS_V4], acc[RMS_V4];
   int ec[RMS_V4];
   rms_row_gain<T>(gain, N, g);
@@ -1006,10 +1008,9 @@ __global__ __launch_bounds__(256) void split_reduce_rmsnorm_kernel(const float* 
   for (int i = 0; i < RMS_V4; ++i) {
     const int e = threadIdx.x + i * 256;
     ec[i] = e < N4 ? e : 0;
-    acc[i] = p0[ec[i]];
     v[i] = xr[ec[i]];
   }
-  for (int q0 = 1; q0 < ksplit; q0 += QB) {
+  for (int q0 = 0; q0 < ksplit; q0 += QB) {
     f32x4 t[QB][RMS_V4];
 #pragma unroll
     for (int j = 0; j < QB; ++j)
@@ -1019,7 +1020,7 @@ __global__ __launch_bounds__(256) void split_reduce_rmsnorm_kernel(const float* 
     for (int j = 0; j < QB; ++j)
       if (q0 + j < ksplit)
 #pragma unroll
-        for (int i = 0; i < RMS_V4; ++i) acc[i] += t[j][i];
+        for (int i = 0; i < RMS_V4; ++i) acc[i] = (q0 + j == 0) ? t[j][i] : acc[i] + t[j][i];
   }
 #pragma unroll
   for (int i = 0; i < RMS_V4; ++i) {
@@ -1084,6 +1085,9 @@ struct GemmPlan {
 // depth beyond two stages changed little)
 #ifndef MEDUSA_GEMM_BIG_BK1
 #define MEDUSA_GEMM_BIG_BK1 64
+#endif
+#ifndef MEDUSA_GEMM_BIG_WM1
+#define MEDUSA_GEMM_BIG_WM1 4  // waves along the activation rows of a 256-wide tile (x 2 along the weight rows)
 #endif
 #ifndef MEDUSA_GEMM_BIG_R1
 #define MEDUSA_GEMM_BIG_R1 2
@@ -1179,9 +1183,9 @@ static bool launch_gemm_t(const void* X, int64_t xbs, int64_t M, int64_t Kd, con
       const T* Bt = reinterpret_cast<const T*>(bias);
       if (plan.big == 1) {
         const int tN = (int)((Nw + 255) / 256), tM = (int)((M + 255) / 256);
-        hipLaunchKernelGGL((gemm_big_kernel<256, 256, 2, 4, MEDUSA_GEMM_BIG_BK1, MEDUSA_GEMM_BIG_R1, EPI>),
+        hipLaunchKernelGGL((gemm_big_kernel<256, 256, 2, MEDUSA_GEMM_BIG_WM1, MEDUSA_GEMM_BIG_BK1, MEDUSA_GEMM_BIG_R1, EPI>),
                            dim3((unsigned)(tN * tM), (unsigned)batch),
-                           dim3(512), 0, st, Xt, xbs, (int)M, (int)Kd, Wt, (int)Nw, Bt, aux, Y, y_f32, tN, tM);
+                           dim3(128 * MEDUSA_GEMM_BIG_WM1), 0, st, Xt, xbs, (int)M, (int)Kd, Wt, (int)Nw, Bt, aux, Y, y_f32, tN, tM);
       } else {
         const int tN = (int)((Nw + 127) / 128), tM = (int)((M + 127) / 128);
         hipLaunchKernelGGL((gemm_big_kernel<128, 128, 2, 2, MEDUSA_GEMM_BIG_BK2, MEDUSA_GEMM_BIG_R2, EPI>),
