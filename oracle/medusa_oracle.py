@@ -53,6 +53,10 @@ accept_sample: the Philox4x64-10 generator equals numpy's Philox bit
               temperature reproduces greedy acceptance.
 kv_compact:   compacted cache equals the cache of sequential decoding of the
               same tokens; hand example path (0, 2, 7).
+sparse_tree:  hand-derived 5-node example (tests/golden/sparse_tree.json);
+              brute force over every prefix-closed tree of n nodes: the kept
+              set has the largest expected acceptance; kept sets are
+              prefix-closed and pass the template checks.
 """
 from __future__ import annotations
 
@@ -153,6 +157,42 @@ def build_tree(parent, rank, root_tok, topk_ids, ctx):
         tokens[i] = int(topk_ids[depth[i] - 1][int(rank[i])])
         mask[i] = mask[p] | (np.uint64(1) << np.uint64(i))
     return dict(tokens=tokens, depth=depth, pos=(ctx + depth).astype(np.int32), mask=mask)
+
+
+def sparse_tree(accuracy, n_nodes):
+    """Sparse tree of the most accurate head combinations ("Medusa Heads",
+    section "Attenzione sull'albero e accettazione": a sparse 64-node tree
+    built from the most accurate combinations beat a dense 256-node one).
+
+    ``accuracy[k][r]`` (in [0, 1]) is the chance that head k+1's rank-r
+    candidate is the right token.  Reading: a combination is a rank tuple
+    (r1..rd), d <= K, and its accuracy is the product of its heads'
+    accuracies (the chance that the whole branch is accepted, heads taken as
+    independent); the tree keeps the root and the n_nodes - 1 most accurate
+    combinations, ties to the shallower and then the lexicographically
+    smaller tuple.  (With accuracies <= 1 a combination is never more
+    accurate than its prefix, so the kept set is prefix-closed.)  The sum of
+    the kept accuracies is the expected number of accepted candidates.
+    Returns (parent int32[n], rank int32[n]) in canonical order (by depth,
+    then lexicographic by rank tuple) and the expected acceptance length.
+    Enumerates every combination: small K and top-k only."""
+    acc = np.asarray(accuracy, dtype=F64)
+    K, width = acc.shape
+    combos = []
+    for d in range(1, K + 1):
+        for t in itertools.product(range(width), repeat=d):
+            v = 1.0
+            for j, r in enumerate(t):
+                v = v * float(acc[j, r])
+            combos.append((-v, d, t))
+    combos.sort()
+    kept = [()] + [t for _, _, t in combos[:n_nodes - 1]]
+    kept.sort(key=lambda t: (len(t), t))
+    index = {t: i for i, t in enumerate(kept)}
+    parent = np.array([-1] + [index[t[:-1]] for t in kept[1:]], dtype=np.int32)
+    rank = np.array([0] + [t[-1] for t in kept[1:]], dtype=np.int32)
+    expected = float(sum(-v for v, _, _ in combos[:n_nodes - 1]))
+    return parent, rank, expected
 
 
 def visible(mask_i, n):
