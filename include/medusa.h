@@ -79,6 +79,23 @@ int32_t medusa_tree_validate(const int32_t* parent, const int32_t* rank, int32_t
                              int32_t K, int32_t topk);
 
 /* ------------------------------------------------------------------------
+ * medusa_tree_from_accuracy (host): the sparse tree of the most accurate
+ * head combinations ("Medusa Heads", tree section: a sparse 64-node tree
+ * built from the most accurate combinations beat a dense 256-node tree).
+ *   accuracy [K, topk] float (host), in [0, 1]: the chance that head k+1's
+ *     rank-r candidate is the right token (measured on the caller's data).
+ * A combination (r1..rd), d <= K, has accuracy prod_j accuracy[j][r_j]; the
+ * tree keeps the root and the N-1 most accurate combinations (ties: the
+ * shallower, then the lexicographically smaller rank tuple), a prefix-closed
+ * set.  Outputs (host): parent [N], rank [N] in canonical order (by depth,
+ * then rank tuple; the form medusa_tree_validate accepts) and, if expected is
+ * not NULL, the sum of the kept accuracies (expected accepted candidates per
+ * step when the heads are independent).
+ * ---------------------------------------------------------------------- */
+int32_t medusa_tree_from_accuracy(const float* accuracy, int32_t K, int32_t topk, int32_t N,
+                                  int32_t* parent, int32_t* rank, double* expected);
+
+/* ------------------------------------------------------------------------
  * Generic projection  Y = epilogue(X W^T)   (nn.Linear orientation).
  * The backbone's projections and the heads' two layers ("Medusa Heads",
  * section "Come le teste prevedono i token successivi": a feed-forward layer

@@ -44,6 +44,7 @@ _SIGS = {
                             sz, vp]),
     "medusa_accept_sample": (i32, [vp, i64, vp, vp, i32, i32, i32, f32, vp, vp, vp, vp, vp, sz,
                                    vp]),
+    "medusa_tree_from_accuracy": (i32, [vp, i32, i32, i32, vp, vp, vp]),
     "kv_compact": (i32, [C.POINTER(vp), C.POINTER(vp), i32, vp, i32, i32, vp, vp, vp, i32, i32,
                          i32, i32, i32, vp, vp, vp, vp]),
     "medusa_embed": (i32, [vp, i64, vp, i64, i64, i32, vp, vp]),
@@ -121,6 +122,20 @@ def _ws(nbytes, device):
 
 
 # ---------------------------------------------------------------------------
+def medusa_tree_from_accuracy(accuracy, N):
+    """Sparse tree of the N most accurate combinations (host): accuracy [K, topk]
+    -> (parent int32[N], rank int32[N], expected accepted candidates)."""
+    import numpy as np
+    acc = np.ascontiguousarray(np.asarray(accuracy, dtype=np.float32))
+    K, topk = acc.shape
+    parent = np.zeros(N, np.int32)
+    rank = np.zeros(N, np.int32)
+    expected = C.c_double(0.0)
+    _check("medusa_tree_from_accuracy", _lib.medusa_tree_from_accuracy(
+        acc.ctypes.data, K, topk, N, parent.ctypes.data, rank.ctypes.data, C.byref(expected)))
+    return parent, rank, expected.value
+
+
 def medusa_tree_validate(parent, rank, K, topk):
     """Host-side check of a tree template (numpy/int32 or torch CPU arrays)."""
     import numpy as np
