@@ -456,9 +456,10 @@ def main():
         plain = round(args.steps / (time.perf_counter() - p0), 2)
         del pdec
 
-    def other_mode(mode, **kw):
-        """Emitted tokens/s of the same step with another acceptance rule."""
-        odec = MedusaDecoder(model, parent, rank, capacity=capacity, mode=mode, **kw)
+    def other_mode(mode, tree=None, **kw):
+        """Emitted tokens/s of the same step with another acceptance rule (and tree)."""
+        tp, tr = tree if tree is not None else (parent, rank)
+        odec = MedusaDecoder(model, tp, tr, capacity=capacity, mode=mode, **kw)
         odec.prefill(prompt)
         odec.capture()
         for _ in range(args.warmup):
@@ -477,13 +478,19 @@ def main():
         return dict(tokens_per_s=round(o_emit / dt_, 2), mean_accept_len=round(float(np.mean(o_acc)), 3),
                     ms_per_step=round(1000 * dt_ / args.steps, 3), **kw)
 
-    typical = sampled = None
+    typical = sampled = sparse = None
     if args.mode == "greedy" and not args.skip_plain:
         log("[bench] typical acceptance (epsilon 0.3, delta 0.09) on the same model")
         typical = other_mode("typical", epsilon=0.3, delta=0.09)
         log("[bench] sampled verification (temperature 1, seed 0) on the same model")
         sampled = other_mode("sample", temperature=1.0, seed=0)
         sampled["accept_kernel"] = sampled_accept_us(torch, M)
+        log("[bench] typical acceptance on a 64-node tree of the most accurate combinations")
+        acc_table = np.array([[0.7 * 0.5 ** r for r in range(4)] for _ in range(5)], np.float32)
+        sp, sr, exp_acc = M.medusa_tree_from_accuracy(acc_table, 64)
+        sparse = other_mode("typical", tree=(sp, sr), epsilon=0.3, delta=0.09)
+        sparse["tree"] = "64 nodes from a synthetic accuracy table a[d][r] = 0.7 * 0.5^r (5 heads x top-4)"
+        sparse["table_expected_accept"] = round(exp_acc, 4)
 
     c2 = None if args.skip_c2 else tree_attention_c2(torch, M, synth)
     c3 = c3b = c5 = f4 = None
@@ -516,6 +523,7 @@ def main():
         "plain_decode_tokens_per_s": plain,
         "typical": typical,
         "sampled": sampled,
+        "sparse_tree_typical": sparse,
         "roofline": {"bound": "hbm", "kernel": "gemm_xdma_kernel (gate/up projection, SwiGLU epilogue)",
                      "achieved": round(gu_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gu_gbs / HBM_PEAK_GBS, 4),
