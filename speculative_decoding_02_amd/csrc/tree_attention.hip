@@ -551,6 +551,21 @@ __global__ __launch_bounds__(256 * KQ) void tree_attention_stream_kernel(AttnArg
       jj[i] = min(tile0 + r, k_end - 1);
       pg[i] = spages[(P2 ? (jj[i] >> a.lp) : jj[i] / a.P) - page0];
     }
+    if (tile0 + ATT_TILE <= ctxb) {  // (wave-uniform) every row of the tile is a cache row
+#pragma unroll
+      for (int i = 0; i < DPW; ++i) {
+        const int q = wave * DPW + i;          // 1 KB block of the tile
+        const int r = q * RPD + lane / CPR;
+        const int c = (lane % CPR) ^ (r & SW); // chunk fetched for that position
+        const int j = jj[i];
+        const int sj = P2 ? (j & (a.P - 1)) : j - (j / a.P) * a.P;
+        const int64_t off = (int64_t)(uint32_t)pg[i] * page_elems + (head_elems + sj * D + c * P16);
+        const uint32_t kd = lds_base + slot * SLOTB + q * 1024;
+        lds_dma16(Kcp + off, kd);
+        lds_dma16(Vcp + off, kd + TILEB);
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < DPW; ++i) {
       const int q = wave * DPW + i;          // 1 KB block of the tile
@@ -627,6 +642,16 @@ __global__ __launch_bounds__(256 * KQ) void tree_attention_stream_kernel(AttnArg
           sacc[kb] = mfma_bf16_16x16x32(kf, qf[st], sacc[kb]);
         }
       }
+      // the V^T operands do not depend on the softmax: read them now, so the
+      // LDS latency overlaps the score MFMAs and the exponentials
+      typedef short s4 __attribute__((ext_vector_type(4)));
+      u32x2 vf[KB][DB];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+          vf[kb][db] = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                           (__attribute__((address_space(3))) s4*)(vs + vofs[db] + kb * 16 * ROWB)));
       // raw scores x (masked: -inf); the scale (> 0, in log2 units) is
       // applied to the maximum and inside the exponent's FMA
       float x[KB][4];
@@ -653,9 +678,7 @@ __global__ __launch_bounds__(256 * KQ) void tree_attention_stream_kernel(AttnArg
             tmax = fmaxf(tmax, x[kb][r]);
           }
       }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-      tmax *= a.scale_log2;
+      tmax = rows4_max(tmax) * a.scale_log2;
       // move the reference only when some node's scores outgrow it
       if (__builtin_amdgcn_ballot_w64(tmax > mrun + ATT_LAZY) != 0) {
         const float mnew = fmaxf(mrun, tmax);
@@ -691,12 +714,7 @@ __global__ __launch_bounds__(256 * KQ) void tree_attention_stream_kernel(AttnArg
       // 4*(l/16) + r; two 16-key blocks form the 8-element contraction slice
       // of one 16x16x32 step (element i = block i/4, r = i%4), and the two
       // transposing reads of those blocks give V^T in the same key order.
-      typedef short s4 __attribute__((ext_vector_type(4)));
-      auto vread = [&](int kb, int db) -> u32x2 {
-        const unsigned char* src = vs + vofs[db] + kb * 16 * ROWB;
-        return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                                             (__attribute__((address_space(3))) s4*)src));
-      };
+      auto vread = [&](int kb, int db) -> u32x2 { return vf[kb][db]; };
       if constexpr (KB % 2 == 0) {
 #pragma unroll
         for (int kb = 0; kb < KB; kb += 2) {
@@ -737,8 +755,7 @@ __global__ __launch_bounds__(256 * KQ) void tree_attention_stream_kernel(AttnArg
 
   // merge key parts 1..KQ-1 into part 0, in part order (per node: max and
   // sum per lane; output dims db*16 + lg*4 + r of this lane)
-  float ltot = lrun + __shfl_xor(lrun, 16, 64);
-  ltot = ltot + __shfl_xor(ltot, 32, 64);
+  float ltot = rows4_sum(lrun);
   __syncthreads();                             // every wave is done with the ring
   float* xch = reinterpret_cast<float*>(lds);  // [KQ-1 parts][4 node blocks][64 lanes][DB*4 + 2]
   constexpr int XW = DB * 4 + 2;
@@ -881,6 +898,9 @@ struct SplitPlan {
 #ifndef MEDUSA_ATTN_DMA_R
 #define MEDUSA_ATTN_DMA_R 4
 #endif
+#ifndef MEDUSA_ATTN_KQ
+#define MEDUSA_ATTN_KQ 2
+#endif
 SplitPlan plan_splits(int B, int Hq, int N, int max_ctx, int P, int target) {
   const int total = max_ctx + N;
   const int bh = B * Hq;
@@ -982,8 +1002,9 @@ extern "C" int32_t medusa_tree_attention(const void* Q, const void* Kt, const vo
   if (dt == MEDUSA_BF16) {
     const bool p2 = a.lp >= 0;
     // two key parts per tile (8 waves); four parts (16 waves) measured slower
-    constexpr int KQ = 2;
-    const dim3 blk8(256 * KQ);
+    constexpr int KQ = MEDUSA_ATTN_KQ;
+    constexpr int KQ64 = KQ < 2 ? KQ : 2;  // a 64-wide tile is 8 DMA blocks: at most 8 waves
+    const dim3 blk8(256 * (D == 128 ? KQ : KQ64));
 #define MEDUSA_ATT_LAUNCH_S(KERNEL, DD)                                                      \
   do {                                                                                       \
     hipLaunchKernelGGL((KERNEL), grid, blk8, 0, st, a);                                      \
@@ -993,8 +1014,8 @@ extern "C" int32_t medusa_tree_attention(const void* Q, const void* Kt, const vo
   } while (0)
     if (D == 128 && p2) MEDUSA_ATT_LAUNCH_S((medusa::tree_attention_stream_kernel<128, RD, KQ, true>), 128);
     else if (D == 128) MEDUSA_ATT_LAUNCH_S((medusa::tree_attention_stream_kernel<128, RD, KQ, false>), 128);
-    else if (p2) MEDUSA_ATT_LAUNCH_S((medusa::tree_attention_stream_kernel<64, 2 * RD, KQ, true>), 64);
-    else MEDUSA_ATT_LAUNCH_S((medusa::tree_attention_stream_kernel<64, 2 * RD, KQ, false>), 64);
+    else if (p2) MEDUSA_ATT_LAUNCH_S((medusa::tree_attention_stream_kernel<64, 2 * RD, KQ64, true>), 64);
+    else MEDUSA_ATT_LAUNCH_S((medusa::tree_attention_stream_kernel<64, 2 * RD, KQ64, false>), 64);
 #undef MEDUSA_ATT_LAUNCH_S
   } else {
     if (D == 128) MEDUSA_ATT_LAUNCH((medusa::tree_attention_kernel<float, 128, PF>), float, 128);
