@@ -405,28 +405,48 @@ def main():
     parent, rank = synth.prune_template(*synth.tree_template((4, 3, 2, 2, 1)), 64, 2)
     prompt = synth.prompt_tokens(4, 512, 32000)
     capacity = 512 + 6 * (args.warmup + args.steps) + 128
+    def timed_steps(d, steps, warmup):
+        """Warm up, restart from the prompt, then time `steps` graph replays.
+        The fused tail logs the emitted tokens on the device, so the timed
+        replays run back to back and the log is read once afterwards; the
+        separate tail reads accept_len after every step.  Returns (emitted,
+        accept lengths, seconds)."""
+        d.prefill(prompt)
+        d.capture()
+        for _ in range(warmup):
+            d.step_graph()
+        d.prefill(prompt)  # timed steps start from the prompt again
+        torch.cuda.synchronize()
+        accs = []
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            acc, _, _ = d.step_graph()
+            if not d.fused:
+                accs.append(int(acc.item()))
+        torch.cuda.synchronize()
+        sec = time.perf_counter() - t0
+        if d.fused:
+            lg = d.log[0].cpu().numpy()
+            cap = (len(lg) - 2) // 2
+            assert int(lg[1]) == steps
+            accs = [int(a) for a in lg[2 + cap:2 + cap + steps]]
+        return sum(a + 1 for a in accs), accs, sec
+
     dec = MedusaDecoder(model, parent, rank, capacity=capacity, mode=args.mode)
-    log("[bench] prefill 512 + record the step graph + warmup")
-    dec.prefill(prompt)
-    dec.capture()
-    for _ in range(args.warmup):
-        acc, _, _ = dec.step_graph()
-        int(acc.item())
-    dec.prefill(prompt)  # timed steps start from the 512-token prompt again
-    torch.cuda.synchronize()
-    log(f"[bench] timing {args.steps} steps (graph replay, one host read of accept_len per step)")
-    emitted, accepts = 0, []
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        acc, _, _ = dec.step_graph()
-        a = int(acc.item())
-        accepts.append(a)
-        emitted += a + 1
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
+    log(f"[bench] prefill 512 + record the step graph + {args.warmup} warmup + {args.steps} timed "
+        "steps (graph replays back to back; the decode log is read once at the end)")
+    emitted, accepts, secs = timed_steps(dec, args.steps, args.warmup)
     dec.ctx_sample = 512 + emitted - (accepts[-1] + 1)  # ctx of the last timed step
-    step_ms = 1000.0 * (t1 - t0) / args.steps
-    tok_s = emitted / (t1 - t0)
+    step_ms = 1000.0 * secs / args.steps
+    tok_s = emitted / secs
+    sep = None
+    if not args.skip_plain:
+        log("[bench] the same step with the tail as separate launches and a host read per step")
+        sdec = MedusaDecoder(model, parent, rank, capacity=capacity, mode=args.mode, tail="separate")
+        s_emit, s_acc, s_sec = timed_steps(sdec, args.steps, args.warmup)
+        sep = dict(tokens_per_s=round(s_emit / s_sec, 2), ms_per_step=round(1000 * s_sec / args.steps, 3),
+                   mean_accept_len=round(float(np.mean(s_acc)), 3))
+        del sdec
 
     # dominant kernel: the gate/up projection (SwiGLU epilogue), weight
     # streaming; one step's 32 launches over the model's own weights
@@ -444,36 +464,15 @@ def main():
     if not args.skip_plain:
         log("[bench] plain one-token greedy decoding on the same path")
         pdec = MedusaDecoder(model, np.array([-1]), np.array([0]), capacity=capacity)
-        pdec.prefill(prompt)
-        pdec.capture()
-        for _ in range(3):
-            int(pdec.step_graph()[0].item())
-        torch.cuda.synchronize()
-        p0 = time.perf_counter()
-        for _ in range(args.steps):
-            int(pdec.step_graph()[0].item())
-        torch.cuda.synchronize()
-        plain = round(args.steps / (time.perf_counter() - p0), 2)
+        p_emit, _, p_sec = timed_steps(pdec, args.steps, 3)
+        plain = round(p_emit / p_sec, 2)
         del pdec
 
     def other_mode(mode, tree=None, **kw):
         """Emitted tokens/s of the same step with another acceptance rule (and tree)."""
         tp, tr = tree if tree is not None else (parent, rank)
         odec = MedusaDecoder(model, tp, tr, capacity=capacity, mode=mode, **kw)
-        odec.prefill(prompt)
-        odec.capture()
-        for _ in range(args.warmup):
-            int(odec.step_graph()[0].item())
-        odec.prefill(prompt)
-        torch.cuda.synchronize()
-        o_emit, o_acc = 0, []
-        q0 = time.perf_counter()
-        for _ in range(args.steps):
-            a = int(odec.step_graph()[0].item())
-            o_acc.append(a)
-            o_emit += a + 1
-        torch.cuda.synchronize()
-        dt_ = time.perf_counter() - q0
+        o_emit, o_acc, dt_ = timed_steps(odec, args.steps, args.warmup)
         del odec
         return dict(tokens_per_s=round(o_emit / dt_, 2), mean_accept_len=round(float(np.mean(o_acc)), 3),
                     ms_per_step=round(1000 * dt_ / args.steps, 3), **kw)
@@ -519,8 +518,9 @@ def main():
                    "mode": args.mode, "tree_nodes": 64, "prompt": 512, "batch": 1},
         "mean_accept_len": round(float(np.mean(accepts)), 3),
         "tokens_per_step": round(emitted / args.steps, 3),
-        "verified_tree_tokens_per_s": round(64 * args.steps / (t1 - t0), 1),
+        "verified_tree_tokens_per_s": round(64 * args.steps / secs, 1),
         "plain_decode_tokens_per_s": plain,
+        "tail_separate": sep,
         "typical": typical,
         "sampled": sampled,
         "sparse_tree_typical": sparse,

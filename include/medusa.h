@@ -14,7 +14,8 @@
  *   4. The longest branch the model agrees with is kept, greedy or typical
  *      (medusa_accept), and only that branch stays in the KV cache
  *      (kv_compact); its last hidden state feeds the heads next round
- *      (medusa_gather_rows).
+ *      (medusa_gather_rows).  medusa_decode_tail does all of step 4 and
+ *      the step's bookkeeping in two launches.
  *
  * Conventions for every call
  * --------------------------
@@ -341,6 +342,45 @@ int32_t medusa_swiglu(const void* gu, int64_t M, int64_t F, int32_t dt, void* ou
 int32_t medusa_gather_rows(const void* h, int32_t B, int32_t N, int64_t H, const int32_t* path,
                            const int32_t* accept_len, int32_t K, int32_t dt, void* out,
                            void* stream);
+
+/* ------------------------------------------------------------------------
+ * medusa_decode_tail: the end of one decode step in two launches, with no
+ * host involvement: acceptance (greedy, typical or sampled, as medusa_accept
+ * and medusa_accept_sample), the cache compaction of kv_compact, the kept
+ * branch's last hidden state (medusa_gather_rows), and the commit of the
+ * step.  The longest accepted branch is kept and its tokens plus one are
+ * emitted ("Medusa Heads", section "Attenzione sull'albero e accettazione";
+ * sampled verification: "Têtes de décodage Medusa", section "Plongée
+ * profonde").  The outputs equal those of the separate calls bit for bit.
+ *   logits [B, N, V] float; tokens, parent [B, N]; mode 0 greedy, 1 typical
+ *     (temperature, epsilon, delta), 2 sampled (temperature, rng [2] as for
+ *     medusa_accept_sample; step advanced by one).  K <= 8.
+ *   Kc, Vc: HOST arrays of L device pools [pages, Hkv, P, D] (dt), page_table
+ *     [B, max_pages].
+ *   hidden [B, N, H] (dt) -> h_best [B, H] = hidden[b, kept node]; H * element
+ *     size a multiple of 16 bytes, both 16-byte aligned.
+ *   ctx [B] (in/out): advanced by accept_len + 1.  root [B] (out): the next
+ *     root token (= next_token).  accept_len [B], path [B, K+1], next_token [B]
+ *     as medusa_accept.
+ *   log [B, 2 + 2*cap] int32 (in/out), per sequence: [0] tokens emitted so
+ *     far, [1] steps so far, [2, 2+cap) the emitted tokens (path order,
+ *     accept_len + 1 per step), [2+cap, 2+2cap) each step's accept_len.
+ *     Entries past cap are dropped; the counts keep counting.  Zero it before
+ *     a generation.
+ *   ws: medusa_decode_tail_ws(B, N) bytes.  Its last part holds per-sequence
+ *     counters that must be zero before the first call (zero-fill the
+ *     workspace once); every call leaves them zero.  Calls sharing a
+ *     workspace must be ordered by their stream.
+ * ---------------------------------------------------------------------- */
+size_t medusa_decode_tail_ws(int32_t B, int32_t N);
+int32_t medusa_decode_tail(const float* logits, int64_t V, const int32_t* tokens,
+                           const int32_t* parent, int32_t B, int32_t N, int32_t K, int32_t mode,
+                           float temperature, float epsilon, float delta, uint64_t* rng,
+                           void* const* Kc, void* const* Vc, int32_t L, const int32_t* page_table,
+                           int32_t max_pages, int32_t P, int32_t Hkv, int32_t D, int32_t dt,
+                           const void* hidden, int64_t H, void* h_best, int32_t* ctx,
+                           int32_t* root, int32_t* accept_len, int32_t* path, int32_t* next_token,
+                           int32_t* log, int32_t cap, void* ws, size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

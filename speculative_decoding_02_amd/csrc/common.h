@@ -216,6 +216,13 @@ __host__ __device__ constexpr int waitcnt_vm(int n) {
 }
 constexpr int WAITCNT_LGKM0 = 0xC07F;  // lgkmcnt(0) only
 
+// One KV pool per layer (K and V), passed by value to the kernels that touch
+// every layer's cache.
+struct LayerPtrs {
+  void* k[MEDUSA_MAX_LAYERS];
+  void* v[MEDUSA_MAX_LAYERS];
+};
+
 }  // namespace medusa
 
 // ---------------------------------------------------------------------------

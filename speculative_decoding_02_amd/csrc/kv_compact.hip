@@ -11,11 +11,6 @@
 
 namespace medusa {
 
-struct LayerPtrs {
-  void* k[MEDUSA_MAX_LAYERS];
-  void* v[MEDUSA_MAX_LAYERS];
-};
-
 template <int D, int ES>
 __global__ __launch_bounds__(256) void kv_compact_kernel(LayerPtrs lp, int Hkv, int P,
                                                          const int* __restrict__ page_table,

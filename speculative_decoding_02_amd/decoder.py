@@ -105,7 +105,7 @@ class MedusaDecoder:
     """
 
     def __init__(self, model: DeviceModel, parent, rank, capacity, page_size=16, mode="greedy",
-                 temperature=1.0, epsilon=0.3, delta=0.09, seed=0):
+                 temperature=1.0, epsilon=0.3, delta=0.09, seed=0, tail="fused"):
         self.m = model
         dev = model.device
         parent = np.asarray(parent, np.int32)
@@ -120,6 +120,9 @@ class MedusaDecoder:
             M.medusa_tree_validate(parent, rank, self.K, self.width)
         if mode not in ("greedy", "typical", "sample"):
             raise ValueError(f"mode {mode!r}")
+        if tail not in ("fused", "separate"):
+            raise ValueError(f"tail {tail!r}")
+        self.fused = tail == "fused"
         self.sampled = mode == "sample"
         self.mode = 0 if mode == "greedy" else 1
         self.T, self.eps, self.delta = temperature, epsilon, delta
@@ -165,6 +168,11 @@ class MedusaDecoder:
         self.one_tok = torch.zeros((1, 1), **i32)
         self.one_parent = torch.full((1, 1), -1, **i32)
         self.one_out = (torch.zeros(1, **i32), torch.zeros((1, 1), **i32), torch.zeros(1, **i32))
+        # the fused tail: per-sequence arrival counters (zero-filled here, left
+        # zero by every call), the kept hidden row, and the decode log
+        self.tail_ws = M._ws(M._lib.medusa_decode_tail_ws(1, 64), dev)
+        self.h_best = torch.zeros((1, model.hidden), dtype=model.dtype, device=dev)
+        self.log = M.decode_log(1, self.capacity, dev)
         self.new_ctx = torch.zeros(1, **i32)
         self.src = torch.zeros((1, self.K + 1), **i32)
         self.dst = torch.zeros((1, self.K + 1), **i32)
@@ -216,6 +224,7 @@ class MedusaDecoder:
         dev = self.m.device
         self._set_ctx(0)
         self.rng.copy_(M.rng_state(self.seed, 0, dev))  # a generation's draws start at step 0
+        self.log.zero_()
         c = 0
         while c < len(prompt):
             n = min(64, len(prompt) - c)
@@ -241,6 +250,16 @@ class MedusaDecoder:
         tokens, pos, mask = M.medusa_build_tree(self.parent, self.rank, self.root, self.topk_ids,
                                                 self.ctx)
         logits, hN = self.forward(tokens, pos, mask)
+        if self.fused:
+            acc, path, nxt, hbest = M.medusa_decode_tail(
+                logits[None], tokens, self.parent, self.K, 2 if self.sampled else self.mode,
+                self.Kc, self.Vc, self.page_table, hN[None], self.ctx, self.root, self.log,
+                temperature=self.T, epsilon=self.eps, delta=self.delta, rng=self.rng,
+                h_best=self.h_best, out=self.out, ws=self.tail_ws)
+            if self.K > 0:
+                self._heads(hbest)
+            self.last = dict(tokens=tokens, logits=logits, hN=hN, pos=pos, mask=mask)
+            return acc, path, tokens
         if self.sampled:
             acc, path, nxt = M.medusa_accept_sample(logits[None], tokens, self.parent, self.K,
                                                     self.T, self.rng, out=self.out, ws=self.acc_ws)
@@ -283,10 +302,29 @@ class MedusaDecoder:
         return self.g_out
 
     def generate(self, prompt, n_new, record=None, graph=False):
-        """Prefill, then Medusa steps until n_new tokens are emitted.  Returns int32[n_new]."""
+        """Prefill, then Medusa steps until n_new tokens are emitted.  Returns int32[n_new].
+
+        With the fused tail the emitted tokens collect in the device log and
+        the host reads only the count, after batches of steps: at least
+        ceil(remaining / (K + 1)) more steps are needed, so that many run
+        back to back before the next read."""
         self.prefill(prompt)
         if graph and getattr(self, "graph", None) is None:
             self.capture()
+        if self.fused:
+            cap = (self.log.shape[1] - 2) // 2
+            if n_new + self.K + 1 > cap:
+                raise ValueError(f"n_new={n_new} exceeds the decode log ({cap} tokens)")
+            done = 0
+            while done < n_new:
+                for _ in range(max(1, -(-(n_new - done) // (self.K + 1)))):
+                    self.step_graph() if graph else self.step()
+                done = int(self.log[0, 0].item())
+            lg = self.log[0].cpu().numpy()
+            if record is not None:
+                record.extend(int(a) for a in lg[2 + cap:2 + cap + int(lg[1])])
+            self.ctx_host += done
+            return lg[2:2 + n_new].astype(np.int32)
         out = []
         while len(out) < n_new:
             acc, path, tokens = self.step_graph() if graph else self.step()

@@ -56,6 +56,10 @@ _SIGS = {
     "medusa_qkv_rope": (i32, [vp, i64, i32, i32, i32, vp, f32, i32, vp, vp, vp, vp]),
     "medusa_swiglu": (i32, [vp, i64, i64, i32, vp, vp]),
     "medusa_gather_rows": (i32, [vp, i32, i32, i64, vp, vp, i32, i32, vp, vp]),
+    "medusa_decode_tail_ws": (sz, [i32, i32]),
+    "medusa_decode_tail": (i32, [vp, i64, vp, vp, i32, i32, i32, i32, f32, f32, f32, vp,
+                                 C.POINTER(vp), C.POINTER(vp), i32, vp, i32, i32, i32, i32, i32,
+                                 vp, i64, vp, vp, vp, vp, vp, vp, vp, i32, vp, sz, vp]),
 }
 EXPORTS = tuple(_SIGS)
 
@@ -394,3 +398,45 @@ def medusa_gather_rows(h, path, accept_len, out=None):
     _check("medusa_gather_rows", _lib.medusa_gather_rows(
         _p(h), B, N, H, _p(path), _p(accept_len), path.shape[1] - 1, _dt(h), _p(out), _stream()))
     return out
+
+
+def decode_log(B, cap, device="cuda"):
+    """A zeroed decode log for medusa_decode_tail: [B, 2 + 2*cap] int32."""
+    return torch.zeros((B, 2 + 2 * cap), dtype=torch.int32, device=device)
+
+
+def medusa_decode_tail(logits, tokens, parent, K, mode, Kc_list, Vc_list, page_table, hidden,
+                       ctx, root, log, temperature=1.0, epsilon=0.3, delta=0.09, rng=None,
+                       h_best=None, out=None, ws=None):
+    """The decode step's tail: accept (mode 0 greedy, 1 typical, 2 sampled),
+    compact every layer's cache, gather the kept hidden row, set root, advance
+    ctx and append to the decode log.  Returns (accept_len, path, next, h_best).
+
+    ws must be zero-filled when first allocated (the call leaves its counters
+    zero); the default allocates one per call."""
+    B, N, V = logits.shape
+    H = hidden.shape[-1]
+    dev = logits.device
+    L = len(Kc_list)
+    Hkv, P, D = Kc_list[0].shape[1], Kc_list[0].shape[2], Kc_list[0].shape[3]
+    if mode == 2 and (rng is None or rng.numel() != 2 or rng.dtype != torch.int64):
+        raise ValueError("sampled mode needs rng: a 2-element int64 tensor (seed, step)")
+    if out is None:
+        out = (torch.empty(B, dtype=torch.int32, device=dev),
+               torch.empty((B, K + 1), dtype=torch.int32, device=dev),
+               torch.empty(B, dtype=torch.int32, device=dev))
+    h_best = h_best if h_best is not None else torch.empty((B, H), dtype=hidden.dtype, device=dev)
+    need = _lib.medusa_decode_tail_ws(B, N)
+    if ws is None or ws.numel() < need:
+        ws = _ws(need, dev)
+    acc, path, nxt = out
+    karr = (vp * L)(*[_p(t) for t in Kc_list])
+    varr = (vp * L)(*[_p(t) for t in Vc_list])
+    cap = (log.shape[1] - 2) // 2
+    _check("medusa_decode_tail", _lib.medusa_decode_tail(
+        _p(logits), V, _p(tokens), _p(parent), B, N, K, int(mode), float(temperature),
+        float(epsilon), float(delta), _p(rng) if mode == 2 else None, karr, varr, L,
+        _p(page_table), page_table.shape[1], P, Hkv, D, _dt(Kc_list[0]), _p(hidden), H,
+        _p(h_best), _p(ctx), _p(root), _p(acc), _p(path), _p(nxt), _p(log), cap, _p(ws),
+        ws.numel(), _stream()))
+    return acc, path, nxt, h_best

@@ -109,3 +109,28 @@ def got2_equal(dec, prompt, ref):
     got = dec.generate(prompt, len(ref), graph=True)
     assert got.tolist() == ref.tolist(), _report(ref, got)
     return True
+
+
+@pytest.mark.parametrize("mode", ["greedy", "sample"])
+def test_c1_separate_tail_equals_oracle(c1, mode):
+    """The decode step with its tail as separate launches (accept, kv_compact,
+    gather_rows, host read per step) emits the same tokens as the oracle, as
+    the fused tail does; the fused tail's accept lengths (from its device log)
+    equal the separate path's."""
+    from speculative_decoding_02_amd.decoder import DeviceModel, MedusaDecoder
+    m, prompt, seq = c1
+    case(f"c1 separate tail {mode}")
+    parent, rank = synth.tree_template((2, 3))
+    kw = dict(mode="sample", temperature=0.8, seed=9) if mode == "sample" else {}
+    ref = seq[:48] if mode == "greedy" else orc.medusa_generate(m, prompt, 48, parent, rank,
+                                                                 mode="sample", temperature=0.8,
+                                                                 seed=9)[0]
+    dm = DeviceModel(m, dtype=torch.float32)
+    recs = {}
+    for tail in ("separate", "fused"):
+        dec = MedusaDecoder(dm, parent, rank, capacity=32 + 48 + 16, tail=tail, **kw)
+        rec = []
+        got = dec.generate(prompt, 48, record=rec, graph=True)
+        assert got.tolist() == ref.tolist(), _report(ref, got)
+        recs[tail] = rec
+    assert recs["fused"] == recs["separate"]

@@ -516,6 +516,127 @@ def test_kv_compact(lib, dt):
         assert int(host(new_ctx)[b]) == nc
 
 
+# ------------------------------------------------------------ decode tail ---
+def _oracle_accept(mode, logits, tokens, parent, K, T, eps, delta, seed, step, b):
+    """The oracle's decision and whether it lies within fp32 rounding of a tie."""
+    if mode == 0:
+        return orc.accept_greedy(logits, tokens, parent, K), False
+    if mode == 1:
+        r = orc.accept_typical(logits, tokens, parent, K, T, eps, delta, return_margins=True)
+        return r, bool(np.min(np.abs(r["margins"][1:])) < 1e-4)
+    r = orc.accept_sample(logits, tokens, parent, K, T, seed, step, b=b, return_margins=True)
+    walk = [int(x) for x in r["path"] if x >= 0]
+    return r, bool(np.min(r["margins"][walk]) < 1e-4)
+
+
+@pytest.mark.parametrize("dt", DTS, ids=DTN.get)
+@pytest.mark.parametrize("mode", [0, 1, 2], ids=["greedy", "typical", "sample"])
+@pytest.mark.parametrize("L,Hkv,D", [(3, 2, 128), (32, 8, 64)])
+def test_decode_tail(lib, dt, mode, L, Hkv, D):
+    """The fused tail (accept + compaction + kept hidden row + commit + log)
+    over three calls in a row on one workspace: every output equals the
+    separate calls' bit for bit (accept / accept_sample, kv_compact,
+    gather_rows), the decision equals the oracle's (calls within fp32
+    rounding of a tie are counted), the compacted caches equal the oracle's
+    compaction, ctx advances by accept_len + 1, the log appends the emitted
+    tokens (dropping those past its capacity) and the arrival counters are
+    left at zero."""
+    case(f"decode tail {DTN[dt]} mode={mode} L={L} Hkv={Hkv} D={D}")
+    B, N, V, K, P, H, cap = 2, 64, 1000, 5, 16, 256, 12
+    T, eps, delta, seed, step0 = (0.7 if mode == 2 else 1.0), 0.3, 0.09, 321, 4
+    rng = np.random.default_rng(L + D + mode)
+    ctx0 = np.array([37, 200], np.int32)
+    max_pages = (int(ctx0.max()) + 4 * 64) // P + 1
+    pages = B * max_pages
+    pt = rng.permutation(pages).reshape(B, max_pages).astype(np.int32)
+    pk = [_rnd(dt, rng.standard_normal((pages, Hkv, P, D)).astype(np.float32)) for _ in range(L)]
+    pv = [_rnd(dt, rng.standard_normal((pages, Hkv, P, D)).astype(np.float32)) for _ in range(L)]
+    Kd, Vd = [dev(a, dt) for a in pk], [dev(a, dt) for a in pv]
+    Ks, Vs = [t.clone() for t in Kd], [t.clone() for t in Vd]      # the separate calls' copy
+    ctx, root = dev(ctx0), dev(np.zeros(B, np.int32))
+    ctx_s = dev(ctx0)
+    log = lib.decode_log(B, cap)
+    log[1, 0] = cap - 3          # sequence 1's log is nearly full: later tokens are dropped
+    log[1, 1] = 2
+    rng_t, rng_s = lib.rng_state(seed, step0), lib.rng_state(seed, step0)
+    ws = lib._ws(lib._lib.medusa_decode_tail_ws(B, N), "cuda")
+    cnt_off = lib._lib.medusa_accept_ws(B, N)
+    near, deep = 0, 0
+    emitted = [[], []]
+    for call in range(3):
+        parent, tokens, logits = _accept_inputs(10 * call + mode, B, N, V)
+        if mode == 2:
+            tokens = _plant_draws(call, T, seed, step0 + call, parent, tokens, logits)
+        hid = _rnd(dt, rng.standard_normal((B, N, H)).astype(np.float32))
+        dl, dtok, dpar, dh = dev(logits), dev(tokens), dev(parent), dev(hid, dt)
+        c_before = host(ctx).copy()
+        logs_before = host(log).copy()
+        acc, path, nxt, hb = lib.medusa_decode_tail(dl, dtok, dpar, K, mode, Kd, Vd, dev(pt), dh, ctx,
+                                                     root, log, temperature=T, epsilon=eps,
+                                                     delta=delta, rng=rng_t, ws=ws)
+        # the separate calls on the copy
+        if mode == 2:
+            acc2, path2, nxt2 = lib.medusa_accept_sample(dl, dtok, dpar, K, T, rng_s)
+        else:
+            acc2, path2, nxt2 = lib.medusa_accept(dl, dtok, dpar, K, mode=mode, temperature=T,
+                                                  epsilon=eps, delta=delta)
+        nc2, _, _ = lib.kv_compact(Ks, Vs, dev(pt), ctx_s, path2, acc2)
+        hb2 = lib.medusa_gather_rows(dh, path2, acc2)
+        ctx_s = nc2.clone()
+        assert host(acc).tolist() == host(acc2).tolist()
+        assert host(path).tolist() == host(path2).tolist()
+        assert host(nxt).tolist() == host(nxt2).tolist()
+        assert host(root).tolist() == host(nxt).tolist()
+        np.testing.assert_array_equal(host(hb), host(hb2))
+        for l in range(L):
+            np.testing.assert_array_equal(host(Kd[l]), host(Ks[l]))
+            np.testing.assert_array_equal(host(Vd[l]), host(Vs[l]))
+        assert host(ws[cnt_off:cnt_off + 4 * B].view(torch.int32)).tolist() == [0] * B
+        if mode == 2:
+            assert host(rng_t).view(np.uint64).tolist() == [seed, step0 + call + 1]
+        a_g, p_g = host(acc), host(path)
+        for b in range(B):
+            r, is_near = _oracle_accept(mode, logits[b], tokens[b], parent[b], K, T, eps, delta,
+                                        seed, step0 + call, b)
+            if is_near:
+                near += 1
+            else:
+                assert int(a_g[b]) == r["accept_len"]
+                assert p_g[b].tolist() == r["path"].tolist()
+                assert int(host(nxt)[b]) == r["next_token"]
+            a = int(a_g[b])
+            deep += a >= 2
+            assert int(host(ctx)[b]) == c_before[b] + a + 1
+            np.testing.assert_array_equal(host(hb)[b], hid[b, p_g[b][a]])
+            # compaction against the oracle's (on the caches before the call)
+            c = int(c_before[b])
+            for pools, dpool in ((pk, Kd), (pv, Vd)):
+                for l in range(L):
+                    lg = orc.cache_rows(pools[l], pt[b], max_pages * P, P)
+                    want, _, _, _ = orc.kv_compact(lg, c, p_g[b], a)
+                    got = orc.cache_rows(host(dpool[l]), pt[b], max_pages * P, P)
+                    np.testing.assert_array_equal(got, want)
+            # the decode log
+            lb, la = logs_before[b], host(log)[b]
+            n0, s0 = int(lb[0]), int(lb[1])
+            assert int(la[0]) == n0 + a + 1 and int(la[1]) == s0 + 1
+            toks = [int(tokens[b, p_g[b][d]]) for d in range(a + 1)]
+            emitted[b] += toks
+            want_log = lb.copy()
+            for d, tk in enumerate(toks):
+                if n0 + d < cap:
+                    want_log[2 + n0 + d] = tk
+            if s0 < cap:
+                want_log[2 + cap + s0] = a
+            want_log[0], want_log[1] = n0 + a + 1, s0 + 1
+            assert la.tolist() == want_log.tolist()
+        pk = [host(t) for t in Kd]
+        pv = [host(t) for t in Vd]
+    n_log = min(len(emitted[0]), cap)
+    assert host(log)[0, 2:2 + n_log].tolist() == emitted[0][:n_log]
+    assert near < 3 * B and deep >= 1
+
+
 # ---------------------------------------------------------------- backbone ---
 @pytest.mark.parametrize("dt", DTS, ids=DTN.get)
 def test_backbone_ops(lib, dt):

@@ -73,6 +73,28 @@ def test_bad_arguments_are_rejected_on_the_host(M):
     # zero rows: nothing to do, success without pointers
     assert lib.medusa_linear(None, 0, 0, 8, None, 4, 1, 1, 0, None, None, None, 0, None, 0,
                              None) == 0
+    # the fused decode tail: K above 8, unknown mode, sampled without a
+    # positive temperature, head dim, hidden rows not whole 16-byte chunks,
+    # an empty batch, and (with stand-in addresses that are never read) a
+    # missing workspace
+    vp = M.vp
+    pools = (vp * 1)(256)
+
+    def tail(K=5, mode=0, T=1.0, D=128, H=256, B=1, ws=None, nbytes=0, dt=1):
+        a = 256
+        return lib.medusa_decode_tail(a, 1000, a, a, B, 64, K, mode, T, 0.3, 0.09, a, pools, pools,
+                                      1, a, 8, 16, 2, D, dt, a, H, a, a, a, a, a, a, a, 16, ws,
+                                      nbytes, None)
+    assert tail(K=9) == 2
+    assert tail(mode=3) == 1
+    assert tail(mode=2, T=0.0) == 1
+    assert tail(D=96) == 2
+    assert tail(H=4) == 1          # 8 bytes of bf16
+    assert tail(B=0) == 0
+    assert tail() == 3
+    need = lib.medusa_decode_tail_ws(1, 64)
+    assert need == lib.medusa_accept_ws(1, 64) + 256
+    assert tail(ws=4096, nbytes=need - 1) == 3
 
 
 def test_workspace_queries_follow_the_plan(M):
