@@ -296,6 +296,19 @@ int32_t medusa_embed(const int32_t* tokens, int64_t M, const void* table, int64_
 int32_t medusa_rmsnorm(const float* x, int64_t M, int64_t H, const void* gain, float eps,
                        int32_t dt, void* out, void* stream);
 
+/* medusa_tree_embed: medusa_build_tree, then medusa_embed of the B*N tree
+ * tokens and medusa_rmsnorm of those rows with gain (the first block's norm),
+ * in one launch; the outputs equal the three calls' bit for bit.  Arguments
+ * as there: tokens, pos [B, N], mask [B, N]; x [B*N, H] float (16-byte
+ * aligned) = the embedding rows; h [B*N, H] (dt) = RMSNorm(x) * gain (gain
+ * NULL for 1).  H a multiple of 4, H <= 8192; table, gain and h aligned to
+ * four elements. */
+int32_t medusa_tree_embed(int32_t B, int32_t N, const int32_t* parent, const int32_t* rank,
+                          const int32_t* root_tok, const int32_t* topk_ids, int32_t K,
+                          int32_t topk, const int32_t* ctx, int32_t* tokens, int32_t* pos,
+                          uint64_t* mask, const void* table, int64_t V, int64_t H, int32_t dt,
+                          const void* gain, float eps, float* x, void* h, void* stream);
+
 /* The residual projection of a pre-norm block followed by the next block's
  * RMSNorm: x [M, N] float (16-byte aligned, updated in place) += X W^T with
  * X [M, Kd] and W [N, Kd] (dt), then out [M, N] (dt) = RMSNorm(x) * gain

@@ -6,12 +6,30 @@
 
 namespace medusa {
 
+// One workgroup per row.  Rows of whole 4-element vectors (H a multiple of 4,
+// aligned table and output) are copied with every thread's loads issued
+// before its stores; other rows element by element.
 template <typename T>
 __global__ __launch_bounds__(256) void embed_kernel(const int* __restrict__ tokens,
                                                     const T* __restrict__ table, int64_t H,
-                                                    float* __restrict__ out) {
+                                                    float* __restrict__ out, int vec) {
   const int64_t m = blockIdx.x;
   const T* row = table + (int64_t)tokens[m] * H;
+  if (vec) {
+    const int64_t H4 = H / 4;
+    for (int64_t e0 = threadIdx.x; e0 < H4; e0 += 256 * RMS_V4) {
+      f32x4 v[RMS_V4];
+#pragma unroll
+      for (int i = 0; i < RMS_V4; ++i) {
+        const int64_t e = e0 + i * 256;
+        v[i] = Elem<T>::load4(row, e < H4 ? e : 0);
+      }
+#pragma unroll
+      for (int i = 0; i < RMS_V4; ++i)
+        if (e0 + i * 256 < H4) Elem<float>::store4(out + m * H, e0 + i * 256, v[i]);
+    }
+    return;
+  }
   for (int64_t e = threadIdx.x; e < H; e += 256) out[m * H + e] = ld<T>(row, e);
 }
 
@@ -125,8 +143,10 @@ extern "C" int32_t medusa_embed(const int32_t* tokens, int64_t M, const void* ta
                  "medusa_embed: bad sizes");
   if (M == 0) return MEDUSA_OK;
   MEDUSA_REQUIRE(tokens && table && out, MEDUSA_ERR_INVALID_ARG, "medusa_embed: NULL pointer");
+  const int vec = H % 4 == 0 && ((uintptr_t)out) % 16 == 0 &&
+                  ((uintptr_t)table) % (dt == MEDUSA_BF16 ? 8 : 16) == 0;
   MEDUSA_DT_DISPATCH(dt, hipLaunchKernelGGL(medusa::embed_kernel<T>, dim3((unsigned)M), dim3(256), 0,
-                                            (hipStream_t)stream, tokens, (const T*)table, H, out));
+                                            (hipStream_t)stream, tokens, (const T*)table, H, out, vec));
   return check_launch("medusa_embed");
 }
 

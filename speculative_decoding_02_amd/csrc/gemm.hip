@@ -1077,6 +1077,9 @@ struct GemmPlan {
 #ifndef MEDUSA_GEMM_XD_SPLIT
 #define MEDUSA_GEMM_XD_SPLIT 4
 #endif
+#ifndef MEDUSA_GEMM_XD_CPS
+#define MEDUSA_GEMM_XD_CPS 8  // contraction chunks per split, at least
+#endif
 #ifndef MEDUSA_GEMM_BIG_MIN_M
 #define MEDUSA_GEMM_BIG_MIN_M 256
 #endif
@@ -1122,7 +1125,7 @@ GemmPlan gemm_plan(int64_t M, int64_t Kd, int64_t Nw, int dt, int epi) {
     // 4096 x 4096 is fastest split 2 ways and 4096 x 11008 4 ways)
     p.xb_S = Nw / 16 >= MEDUSA_GEMM_XB_MIN_BLOCKS
                  ? 1
-                 : (int)std::max<int64_t>(1, std::min<int64_t>(MEDUSA_GEMM_XD_SPLIT, Kd / XB_KC / 8));
+                 : (int)std::max<int64_t>(1, std::min<int64_t>(MEDUSA_GEMM_XD_SPLIT, Kd / XB_KC / MEDUSA_GEMM_XD_CPS));
     // about one workgroup per compute unit, at most XB_MAXB blocks each
     p.xb_G = std::max(std::min(MEDUSA_GEMM_XB_WGS / p.xb_S, nunits), (nunits + XB_MAXB / unit - 1) / (XB_MAXB / unit));
     p.MT = (int)((M + (M <= 32 ? 32 : 64) - 1) / (M <= 32 ? 32 : 64));

@@ -184,11 +184,17 @@ class MedusaDecoder:
         Stores the rows' K/V at cache slots ctx..ctx+n-1.  Returns (logits
         [n,V] float32, final hidden [n,H] model dtype)."""
         m, t = self.m, self.m.t
-        n = tokens.shape[-1]
         x = M.medusa_embed(tokens.reshape(-1), t["embed"])
+        h = M.medusa_rmsnorm(x, t["layers"][0]["g_attn"], m.eps, m.dtype)
+        return self._layers(x, h, pos, mask)
+
+    def _layers(self, x, h, pos, mask):
+        """The layers, final norm and lm_head over n rows: x [n, H] float (the
+        residual stream, updated in place), h = the first block's RMSNorm of x."""
+        m, t = self.m, self.m.t
+        n = x.shape[0]
         scale = 1.0 / float(np.sqrt(m.head_dim))
         layers = t["layers"]
-        h = M.medusa_rmsnorm(x, layers[0]["g_attn"], m.eps, m.dtype)
         for li, L in enumerate(layers):
             q, k, v = M.medusa_linear_qkv_rope(h, L["wqkv_rp"], m.n_heads, m.n_kv_heads,
                                                m.head_dim, pos.reshape(-1), m.rope_base,
@@ -247,9 +253,15 @@ class MedusaDecoder:
 
     def step(self):
         """One Medusa decode step (all on the GPU); returns (accept_len, path, tokens) tensors."""
-        tokens, pos, mask = M.medusa_build_tree(self.parent, self.rank, self.root, self.topk_ids,
-                                                self.ctx)
-        logits, hN = self.forward(tokens, pos, mask)
+        if self.fused:
+            tokens, pos, mask, x, h = M.medusa_tree_embed(
+                self.parent, self.rank, self.root, self.topk_ids, self.ctx, self.m.t["embed"],
+                self.m.t["layers"][0]["g_attn"], self.m.eps)
+            logits, hN = self._layers(x, h, pos, mask)
+        else:
+            tokens, pos, mask = M.medusa_build_tree(self.parent, self.rank, self.root,
+                                                    self.topk_ids, self.ctx)
+            logits, hN = self.forward(tokens, pos, mask)
         if self.fused:
             acc, path, nxt, hbest = M.medusa_decode_tail(
                 logits[None], tokens, self.parent, self.K, 2 if self.sampled else self.mode,

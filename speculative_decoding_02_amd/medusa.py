@@ -56,6 +56,8 @@ _SIGS = {
     "medusa_qkv_rope": (i32, [vp, i64, i32, i32, i32, vp, f32, i32, vp, vp, vp, vp]),
     "medusa_swiglu": (i32, [vp, i64, i64, i32, vp, vp]),
     "medusa_gather_rows": (i32, [vp, i32, i32, i64, vp, vp, i32, i32, vp, vp]),
+    "medusa_tree_embed": (i32, [i32, i32, vp, vp, vp, vp, i32, i32, vp, vp, vp, vp, vp, i64, i64,
+                                i32, vp, f32, vp, vp, vp]),
     "medusa_decode_tail_ws": (sz, [i32, i32]),
     "medusa_decode_tail": (i32, [vp, i64, vp, vp, i32, i32, i32, i32, f32, f32, f32, vp,
                                  C.POINTER(vp), C.POINTER(vp), i32, vp, i32, i32, i32, i32, i32,
@@ -440,3 +442,24 @@ def medusa_decode_tail(logits, tokens, parent, K, mode, Kc_list, Vc_list, page_t
         _p(h_best), _p(ctx), _p(root), _p(acc), _p(path), _p(nxt), _p(log), cap, _p(ws),
         ws.numel(), _stream()))
     return acc, path, nxt, h_best
+
+
+def medusa_tree_embed(parent, rank, root_tok, topk_ids, ctx, table, gain, eps, out=None):
+    """medusa_build_tree + medusa_embed + medusa_rmsnorm in one launch.
+    Returns (tokens [B,N], pos [B,N], mask [B,N] int64, x [B*N,H] float, h [B*N,H])."""
+    B, N = parent.shape
+    K, _, topk = topk_ids.shape
+    V, H = table.shape
+    dev = parent.device
+    if out is None:
+        out = (torch.empty((B, N), dtype=torch.int32, device=dev),
+               torch.empty((B, N), dtype=torch.int32, device=dev),
+               torch.empty((B, N), dtype=torch.int64, device=dev),
+               torch.empty((B * N, H), dtype=torch.float32, device=dev),
+               torch.empty((B * N, H), dtype=table.dtype, device=dev))
+    tokens, pos, mask, x, h = out
+    _check("medusa_tree_embed", _lib.medusa_tree_embed(
+        B, N, _p(parent), _p(rank), _p(root_tok), _p(topk_ids), K, topk, _p(ctx), _p(tokens),
+        _p(pos), _p(mask), _p(table), V, H, _dt(table), _p(gain), float(eps), _p(x), _p(h),
+        _stream()))
+    return out

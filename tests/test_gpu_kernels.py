@@ -301,6 +301,38 @@ def test_build_tree(lib):
     assert host(tok[0]).tolist() == [5, 11, 12, 21, 22, 23, 21, 22, 23]
 
 
+@pytest.mark.parametrize("dt", DTS, ids=DTN.get)
+@pytest.mark.parametrize("H", [256, 4096, 8192])
+def test_tree_embed(lib, dt, H):
+    """The fused tree build + embedding + first RMSNorm equals the three
+    separate calls bit for bit, and the oracle's tree (tokens, positions,
+    masks), embedding rows and RMSNorm (within the dtype's tolerance)."""
+    case(f"tree_embed {DTN[dt]} H={H}")
+    B, N, K, width, V = 3, 64, 5, 4, 1000
+    parent, rank = synth.random_template_batch((4, 3, 2, 2, 1), N, seeds=[4, 5, 6])
+    rng = np.random.default_rng(H)
+    ids = rng.integers(0, V, size=(K, B, width)).astype(np.int32)
+    root = rng.integers(0, V, size=B).astype(np.int32)
+    ctx = np.array([0, 17, 2048], np.int32)
+    table = _rnd(dt, rng.standard_normal((V, H)).astype(np.float32))
+    gain = _rnd(dt, 1 + 0.1 * rng.standard_normal(H).astype(np.float32))
+    args = (dev(parent), dev(rank), dev(root), dev(ids), dev(ctx))
+    tok, pos, mask, x, h = lib.medusa_tree_embed(*args, dev(table, dt), dev(gain, dt), 1e-5)
+    tok2, pos2, mask2 = lib.medusa_build_tree(*args)
+    x2 = lib.medusa_embed(tok2.reshape(-1), dev(table, dt))
+    h2 = lib.medusa_rmsnorm(x2, dev(gain, dt), 1e-5, dt)
+    for a, b2 in ((tok, tok2), (pos, pos2), (mask, mask2), (x, x2), (h, h2)):
+        np.testing.assert_array_equal(host(a), host(b2))
+    for b in range(B):
+        t = orc.build_tree(parent[b], rank[b], root[b], ids[:, b, :], int(ctx[b]))
+        assert host(tok[b]).tolist() == t["tokens"].tolist()
+        assert host(pos[b]).tolist() == t["pos"].tolist()
+        assert host(mask[b]).view(np.uint64).tolist() == t["mask"].tolist()
+        rows = table[t["tokens"]]
+        np.testing.assert_array_equal(host(x)[b * N:(b + 1) * N], rows)
+        assert_close(host(h)[b * N:(b + 1) * N], orc.rmsnorm(rows, gain, 1e-5), TOL[dt], "tree rows' norm")
+
+
 # ---------------------------------------------------------- tree attention ---
 ATT_CASES = [
     # B, N, Hq, Hkv, D, ctx, P, permute, dtype

@@ -95,6 +95,15 @@ def test_bad_arguments_are_rejected_on_the_host(M):
     need = lib.medusa_decode_tail_ws(1, 64)
     assert need == lib.medusa_accept_ws(1, 64) + 256
     assert tail(ws=4096, nbytes=need - 1) == 3
+    # the fused tree + embedding + norm: H not a multiple of 4, H above 8192,
+    # N above 64, an empty batch
+    emb = lambda B=1, N=9, H=256: lib.medusa_tree_embed(B, N, None, None, None, None, 2, 3, None,
+                                                        None, None, None, None, 100, H, 1, None,
+                                                        1e-5, None, None, None)
+    assert emb(H=250) == 2
+    assert emb(H=8196) == 2
+    assert emb(N=65) == 1
+    assert emb(B=0) == 0
 
 
 def test_workspace_queries_follow_the_plan(M):
