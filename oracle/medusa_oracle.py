@@ -550,7 +550,8 @@ def sequential_greedy(model, prompt, n_new, capacity=None):
 
 
 def medusa_generate(model, prompt, n_new, parent, rank, mode="greedy", temperature=1.0,
-                    epsilon=0.3, delta=0.09, heads=None, capacity=None, record=None, seed=0):
+                    epsilon=0.3, delta=0.09, heads=None, capacity=None, record=None, seed=0,
+                    b=0):
     """Medusa decoding loop, steps in the order the pages give them.
 
     1. Prefill; root = argmax of the last row; heads on the last hidden state
@@ -563,7 +564,9 @@ def medusa_generate(model, prompt, n_new, parent, rank, mode="greedy", temperatu
        heads for the next round; next root = argmax of its last row (a draw
        from it in sampled mode).
     Sampled mode draws the prefill root at step 0 (node 0) and verifies decode
-    step s = 1, 2, ... with key (seed, s).
+    step s = 1, 2, ... with key (seed, s); ``b`` is the sequence's index in a
+    batch, the third word of every draw's counter (a batch of sequences
+    decoded together draws sequence b's noise from its own counters).
     ``heads`` (optional) replaces the learned heads by a function
     hidden_row -> [K, V] logits (used by pins).  ``record`` collects per-step
     dicts.  Returns (tokens int32[n_new], cache, ctx).
@@ -586,7 +589,7 @@ def medusa_generate(model, prompt, n_new, parent, rank, mode="greedy", temperatu
         return [topk(lg[k], width)[0] for k in range(n_heads)]
 
     if mode == "sample":
-        root = sample_token(logits[-1], temperature, seed, 0, 0, 0)
+        root = sample_token(logits[-1], temperature, seed, 0, b, 0)
     else:
         root = argmax(logits[-1])
     ids = head_topk(hf[-1])
@@ -600,7 +603,7 @@ def medusa_generate(model, prompt, n_new, parent, rank, mode="greedy", temperatu
         if mode == "greedy":
             res = accept_greedy(lf, tree["tokens"], parent, n_heads)
         elif mode == "sample":
-            res = accept_sample(lf, tree["tokens"], parent, n_heads, temperature, seed, step)
+            res = accept_sample(lf, tree["tokens"], parent, n_heads, temperature, seed, step, b=b)
         else:
             res = accept_typical(lf, tree["tokens"], parent, n_heads, temperature, epsilon, delta)
         a, path = res["accept_len"], res["path"]

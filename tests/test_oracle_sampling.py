@@ -150,3 +150,23 @@ def test_tiny_temperature_is_greedy(seed):
     assert s["accept_len"] == g["accept_len"]
     np.testing.assert_array_equal(s["path"], g["path"])
     assert s["next_token"] == g["next_token"]
+
+
+def test_generate_sequence_index_selects_its_counters():
+    """A batch's sequence b draws with counter word b: on the same prompt,
+    sequence 0 reproduces the default run and sequence 1 draws other noise
+    (its prefill draw equals a direct draw with b = 1)."""
+    m = synth.tiny_decoder(seed=1)
+    prompt = synth.prompt_tokens(7, 12, m.vocab)
+    parent, rank = synth.tree_template((2, 2))
+    a0, _, _ = orc.medusa_generate(m, prompt, 12, parent, rank, mode="sample", temperature=1.0,
+                                   seed=4)
+    b0, _, _ = orc.medusa_generate(m, prompt, 12, parent, rank, mode="sample", temperature=1.0,
+                                   seed=4, b=0)
+    b1, _, _ = orc.medusa_generate(m, prompt, 12, parent, rank, mode="sample", temperature=1.0,
+                                   seed=4, b=1)
+    assert a0.tolist() == b0.tolist()
+    assert a0.tolist() != b1.tolist()
+    cache = orc.KVCache(m, 64)
+    logits, _ = orc.prefill(m, prompt, cache)
+    assert b1[0] == orc.sample_token(logits[-1], 1.0, 4, 0, 1, 0)
