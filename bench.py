@@ -405,17 +405,19 @@ def main():
     parent, rank = synth.prune_template(*synth.tree_template((4, 3, 2, 2, 1)), 64, 2)
     prompt = synth.prompt_tokens(4, 512, 32000)
     capacity = 512 + 6 * (args.warmup + args.steps) + 128
-    def timed_steps(d, steps, warmup):
+    def timed_steps(d, steps, warmup, prompts=None):
         """Warm up, restart from the prompt, then time `steps` graph replays.
         The fused tail logs the emitted tokens on the device, so the timed
         replays run back to back and the log is read once afterwards; the
         separate tail reads accept_len after every step.  Returns (emitted,
-        accept lengths, seconds)."""
-        d.prefill(prompt)
+        accept lengths, seconds) of the first sequence; with a batch, also
+        the batch's total emitted tokens as d.batch_emitted."""
+        pr = prompt if prompts is None else prompts
+        d.prefill(pr)
         d.capture()
         for _ in range(warmup):
             d.step_graph()
-        d.prefill(prompt)  # timed steps start from the prompt again
+        d.prefill(pr)  # timed steps start from the prompt again
         torch.cuda.synchronize()
         accs = []
         t0 = time.perf_counter()
@@ -426,10 +428,12 @@ def main():
         torch.cuda.synchronize()
         sec = time.perf_counter() - t0
         if d.fused:
-            lg = d.log[0].cpu().numpy()
+            lga = d.log.cpu().numpy()
+            lg = lga[0]
             cap = (len(lg) - 2) // 2
             assert int(lg[1]) == steps
             accs = [int(a) for a in lg[2 + cap:2 + cap + steps]]
+            d.batch_emitted = int(lga[:, 0].sum())
         return sum(a + 1 for a in accs), accs, sec
 
     dec = MedusaDecoder(model, parent, rank, capacity=capacity, mode=args.mode)
@@ -491,6 +495,24 @@ def main():
         sparse["tree"] = "64 nodes from a synthetic accuracy table a[d][r] = 0.7 * 0.5^r (5 heads x top-4)"
         sparse["table_expected_accept"] = round(exp_acc, 4)
 
+    batched = None
+    if not args.skip_extra:
+        log("[bench] batched decoding: 16 sequences x 64-node trees (1024 verification rows)")
+        Bb, bsteps = 16, 10
+        bprompts = np.stack([synth.prompt_tokens(40 + b, 512, 32000) for b in range(Bb)])
+        bdec = MedusaDecoder(model, parent, rank, capacity=512 + 6 * (2 + bsteps) + 128,
+                             mode=args.mode, batch=Bb)
+        _, b_acc, b_sec = timed_steps(bdec, bsteps, 2, prompts=bprompts)
+        batched = dict(workload="16 sequences (prompts of 512, own pages and contexts), 64-node tree "
+                                "each: 1024 rows through every projection, batched attention, "
+                                "fused tail; greedy",
+                       sequences=Bb, steps=bsteps, tokens_per_s=round(bdec.batch_emitted / b_sec, 1),
+                       ms_per_step=round(1000 * b_sec / bsteps, 3),
+                       verified_tree_tokens_per_s=round(Bb * 64 * bsteps / b_sec, 1),
+                       mean_accept_len_seq0=round(float(np.mean(b_acc)), 3))
+        del bdec
+        torch.cuda.empty_cache()
+
     c2 = None if args.skip_c2 else tree_attention_c2(torch, M, synth)
     c3 = c3b = c5 = f4 = None
     if not args.skip_extra:
@@ -521,6 +543,7 @@ def main():
         "verified_tree_tokens_per_s": round(64 * args.steps / secs, 1),
         "plain_decode_tokens_per_s": plain,
         "tail_separate": sep,
+        "batched_decode_f4": batched,
         "typical": typical,
         "sampled": sampled,
         "sparse_tree_typical": sparse,

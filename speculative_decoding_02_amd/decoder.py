@@ -95,21 +95,27 @@ class DeviceModel:
 
 
 class MedusaDecoder:
-    """Paged-KV Medusa decoding for one sequence (B = 1).
+    """Paged-KV Medusa decoding of B sequences at once (B = ``batch``, default 1).
 
-    ``parent``, ``rank``: the tree template (node 0 = root); a single-node
-    template turns the loop into plain greedy decoding (no heads).
-    ``mode``: "greedy", "typical" or "sample" (sampled verification with the
-    counter-based stream keyed by ``seed``: the prefill's next token draws at
-    step 0, decode step s at step s).
+    ``parent``, ``rank``: the tree template (node 0 = root), shared by the
+    batch; a single-node template turns the loop into plain greedy decoding
+    (no heads).  ``mode``: "greedy", "typical" or "sample" (sampled
+    verification with the counter-based stream keyed by ``seed``: the
+    prefill's next token draws at step 0, decode step s at step s; sequence b
+    draws with counter word b).  Each sequence owns ``capacity`` cache slots
+    (its own pages); the verification forward runs the B trees' B*N rows
+    through every projection at once.
     """
 
     def __init__(self, model: DeviceModel, parent, rank, capacity, page_size=16, mode="greedy",
-                 temperature=1.0, epsilon=0.3, delta=0.09, seed=0, tail="fused"):
+                 temperature=1.0, epsilon=0.3, delta=0.09, seed=0, tail="fused", batch=1):
         self.m = model
         dev = model.device
         parent = np.asarray(parent, np.int32)
         rank = np.asarray(rank, np.int32)
+        self.B = B = int(batch)
+        if B < 1:
+            raise ValueError(f"batch {batch}")
         self.N = len(parent)
         depth = np.zeros(self.N, np.int32)
         for i in range(1, self.N):
@@ -130,80 +136,86 @@ class MedusaDecoder:
         self.max_pages = (capacity + self.N + 64 + page_size - 1) // page_size
         self.capacity = self.max_pages * page_size
         i32 = dict(dtype=torch.int32, device=dev)
-        self.parent = torch.tensor(parent[None], **i32)
-        self.rank = torch.tensor(rank[None], **i32)
-        self.page_table = torch.arange(self.max_pages, **i32)[None].contiguous()
-        shape = (self.max_pages, model.n_kv_heads, page_size, model.head_dim)
+        self.parent = torch.tensor(np.tile(parent, (B, 1)), **i32)
+        self.rank = torch.tensor(np.tile(rank, (B, 1)), **i32)
+        # sequence b owns pages b*max_pages .. (b+1)*max_pages-1 of every pool
+        self.page_table = torch.arange(B * self.max_pages, **i32).reshape(B, self.max_pages).contiguous()
+        shape = (B * self.max_pages, model.n_kv_heads, page_size, model.head_dim)
         self.Kc = [torch.zeros(shape, dtype=model.dtype, device=dev) for _ in range(model.n_layers)]
         self.Vc = [torch.zeros(shape, dtype=model.dtype, device=dev) for _ in range(model.n_layers)]
-        self.ctx = torch.zeros(1, **i32)
+        self.ctx = torch.zeros(B, **i32)
         self.ctx_host = 0
-        self.root = torch.zeros(1, **i32)
+        self.root = torch.zeros(B, **i32)
         Kh = max(self.K, 1)
-        self.topk_ids = torch.zeros((Kh, 1, self.width), **i32)
-        self.topk_vals = torch.zeros((Kh, 1, self.width), dtype=torch.float32, device=dev)
+        self.topk_ids = torch.zeros((Kh, B, self.width), **i32)
+        self.topk_vals = torch.zeros((Kh, B, self.width), dtype=torch.float32, device=dev)
         self.max_ctx = self.capacity - 64          # every call has ctx + n <= capacity
-        self.attn_ws = M._ws(max(M.tree_attention_ws_bytes(1, n, model.n_heads, model.n_kv_heads,
+        self.attn_ws = M._ws(max(M.tree_attention_ws_bytes(B, n, model.n_heads, model.n_kv_heads,
                                                            model.head_dim, self.max_ctx, page_size)
                                  for n in range(1, 65)), dev)
-        self.acc_ws = M._ws(M._lib.medusa_accept_ws(1, 64), dev)
+        self.acc_ws = M._ws(M._lib.medusa_accept_ws(B, 64), dev)
         dt = M._dt(model.t["embed"])
-        self.heads_ws = M._ws(M._lib.medusa_heads_ws(1, model.hidden, model.n_medusa, model.vocab,
+        self.heads_ws = M._ws(M._lib.medusa_heads_ws(B, model.hidden, model.n_medusa, model.vocab,
                                                      self.width, dt), dev)
-        # split-contraction scratch of the verification projections (rows <= 64)
+        # split-contraction scratch of the verification projections (rows <= 64 per sequence)
         H, F, V = model.hidden, model.ffn, model.vocab
         qkv_n = (model.n_heads + 2 * model.n_kv_heads) * model.head_dim
         shapes = [(H, qkv_n), (model.n_heads * model.head_dim, H), (H, 2 * F), (F, H), (H, V)]
-        self.lin_ws = M._ws(max([M.linear_ws_bytes(n, kd, nn, 1, dt) for n in range(1, 65)
+        self.lin_ws = M._ws(max([M.linear_ws_bytes(B * n, kd, nn, 1, dt) for n in range(1, 65)
                                  for kd, nn in shapes] + [256]), dev)
-        self.qkv_ws = M._ws(max([M._lib.medusa_linear_qkv_rope_ws(n, H, model.n_heads,
+        self.qkv_ws = M._ws(max([M._lib.medusa_linear_qkv_rope_ws(B * n, H, model.n_heads,
                                                                   model.n_kv_heads,
                                                                   model.head_dim, dt)
                                  for n in range(1, 65)] + [256]), dev)
-        self.out = (torch.zeros(1, **i32), torch.zeros((1, self.K + 1), **i32), torch.zeros(1, **i32))
+        self.out = (torch.zeros(B, **i32), torch.zeros((B, self.K + 1), **i32), torch.zeros(B, **i32))
         # sampled mode: (seed, step) on the device, advanced by every draw; a
         # one-node tree draws the prefill's next token
         self.seed = seed
         self.rng = M.rng_state(seed, 0, dev)
-        self.one_tok = torch.zeros((1, 1), **i32)
-        self.one_parent = torch.full((1, 1), -1, **i32)
-        self.one_out = (torch.zeros(1, **i32), torch.zeros((1, 1), **i32), torch.zeros(1, **i32))
+        self.one_tok = torch.zeros((B, 1), **i32)
+        self.one_parent = torch.full((B, 1), -1, **i32)
+        self.one_out = (torch.zeros(B, **i32), torch.zeros((B, 1), **i32), torch.zeros(B, **i32))
         # the fused tail: per-sequence arrival counters (zero-filled here, left
-        # zero by every call), the kept hidden row, and the decode log
-        self.tail_ws = M._ws(M._lib.medusa_decode_tail_ws(1, 64), dev)
-        self.h_best = torch.zeros((1, model.hidden), dtype=model.dtype, device=dev)
-        self.log = M.decode_log(1, self.capacity, dev)
-        self.new_ctx = torch.zeros(1, **i32)
-        self.src = torch.zeros((1, self.K + 1), **i32)
-        self.dst = torch.zeros((1, self.K + 1), **i32)
+        # zero by every call), the kept hidden rows, and the decode log
+        self.tail_ws = M._ws(M._lib.medusa_decode_tail_ws(B, 64), dev)
+        self.h_best = torch.zeros((B, model.hidden), dtype=model.dtype, device=dev)
+        self.log = M.decode_log(B, self.capacity, dev)
+        self.new_ctx = torch.zeros(B, **i32)
+        self.src = torch.zeros((B, self.K + 1), **i32)
+        self.dst = torch.zeros((B, self.K + 1), **i32)
 
     # ------------------------------------------------------------------
     def forward(self, tokens, pos, mask):
-        """Verification forward of n rows (tokens/pos [1,n] int32, mask [1,n] int64).
+        """Verification forward of n rows per sequence (tokens/pos [B,n] int32,
+        mask [B,n] int64).
 
         Stores the rows' K/V at cache slots ctx..ctx+n-1.  Returns (logits
-        [n,V] float32, final hidden [n,H] model dtype)."""
+        [B*n,V] float32, final hidden [B*n,H] model dtype), rows sequence-major."""
         m, t = self.m, self.m.t
         x = M.medusa_embed(tokens.reshape(-1), t["embed"])
         h = M.medusa_rmsnorm(x, t["layers"][0]["g_attn"], m.eps, m.dtype)
         return self._layers(x, h, pos, mask)
 
     def _layers(self, x, h, pos, mask):
-        """The layers, final norm and lm_head over n rows: x [n, H] float (the
-        residual stream, updated in place), h = the first block's RMSNorm of x."""
+        """The layers, final norm and lm_head over B*n rows: x [B*n, H] float
+        (the residual stream, updated in place), h = the first block's RMSNorm
+        of x."""
         m, t = self.m, self.m.t
-        n = x.shape[0]
+        rows = x.shape[0]
+        n = rows // self.B
         scale = 1.0 / float(np.sqrt(m.head_dim))
         layers = t["layers"]
         for li, L in enumerate(layers):
             q, k, v = M.medusa_linear_qkv_rope(h, L["wqkv_rp"], m.n_heads, m.n_kv_heads,
                                                m.head_dim, pos.reshape(-1), m.rope_base,
                                                ws=self.qkv_ws)
-            o = M.medusa_tree_attention(q[None], k[None], v[None], self.Kc[li], self.Vc[li],
-                                        self.page_table, self.ctx, self.max_ctx,
-                                        mask, scale, ws=self.attn_ws)
+            o = M.medusa_tree_attention(q.view(self.B, n, m.n_heads, m.head_dim),
+                                        k.view(self.B, n, m.n_kv_heads, m.head_dim),
+                                        v.view(self.B, n, m.n_kv_heads, m.head_dim),
+                                        self.Kc[li], self.Vc[li], self.page_table, self.ctx,
+                                        self.max_ctx, mask, scale, ws=self.attn_ws)
             # residual projections carry the next RMSNorm (the last one: the final norm)
-            h = M.medusa_linear_rmsnorm(o.reshape(n, -1), L["wo"], x, L["g_mlp"], m.eps,
+            h = M.medusa_linear_rmsnorm(o.reshape(rows, -1), L["wo"], x, L["g_mlp"], m.eps,
                                         ws=self.lin_ws)
             f = M.medusa_linear(h, L["wgu"], M.EPI_SWIGLU, ws=self.lin_ws)
             g_next = layers[li + 1]["g_attn"] if li + 1 < len(layers) else t["g_final"]
@@ -212,77 +224,80 @@ class MedusaDecoder:
         logits = M.medusa_linear(hN, t["lm_head"], y_f32=True, ws=self.lin_ws)
         return logits, hN
 
-    def _heads(self, h_row):
+    def _heads(self, h_rows):
         if self.K == 0:
             return
         t = self.m.t
-        M.medusa_heads(h_row, t["w1"], t["b1"], t["w2"], self.width, logits=None,
+        M.medusa_heads(h_rows, t["w1"], t["b1"], t["w2"], self.width, logits=None,
                        ids=self.topk_ids, vals=self.topk_vals, ws=self.heads_ws,
                        want_logits=False)
 
     def _set_ctx(self, c):
-        self.ctx.copy_(torch.tensor([c], dtype=torch.int32))
+        self.ctx.fill_(int(c))
         self.ctx_host = c
 
     def prefill(self, prompt):
-        """Causal forward over the prompt in chunks of <= 64 chain-masked rows."""
-        prompt = np.asarray(prompt, np.int32)
+        """Causal forward over the prompts ([P] for one sequence, or [B, P]) in
+        chunks of <= 64 chain-masked rows per sequence."""
+        prompt = np.asarray(prompt, np.int32).reshape(self.B, -1)
         dev = self.m.device
+        B = self.B
         self._set_ctx(0)
         self.rng.copy_(M.rng_state(self.seed, 0, dev))  # a generation's draws start at step 0
         self.log.zero_()
-        c = 0
-        while c < len(prompt):
-            n = min(64, len(prompt) - c)
-            tok = torch.tensor(prompt[None, c:c + n], dtype=torch.int32, device=dev)
-            pos = torch.arange(c, c + n, dtype=torch.int32, device=dev)[None].contiguous()
-            mask = torch.tensor([[(1 << (i + 1)) - 1 if i < 63 else -1 for i in range(n)]],
+        c, plen = 0, prompt.shape[1]
+        while c < plen:
+            n = min(64, plen - c)
+            tok = torch.tensor(prompt[:, c:c + n], dtype=torch.int32, device=dev).contiguous()
+            pos = torch.arange(c, c + n, dtype=torch.int32, device=dev).repeat(B, 1).contiguous()
+            mask = torch.tensor([[(1 << (i + 1)) - 1 if i < 63 else -1 for i in range(n)]] * B,
                                 dtype=torch.int64, device=dev)
             logits, hN = self.forward(tok, pos, mask)
             c += n
             self._set_ctx(c)
+        last = logits.view(B, n, -1)[:, n - 1].contiguous()
         if self.sampled:
-            _, _, nxt = M.medusa_accept_sample(logits[None, n - 1:n], self.one_tok, self.one_parent,
-                                               0, self.T, self.rng, out=self.one_out,
-                                               ws=self.acc_ws)
+            _, _, nxt = M.medusa_accept_sample(last[:, None], self.one_tok, self.one_parent, 0,
+                                               self.T, self.rng, out=self.one_out, ws=self.acc_ws)
             self.root.copy_(nxt)
         else:
-            ids, _ = M.medusa_topk(logits[n - 1:n].contiguous(), 1)
-            self.root.copy_(ids.reshape(1))
-        self._heads(hN[n - 1:n].contiguous())
+            ids, _ = M.medusa_topk(last, 1)
+            self.root.copy_(ids.reshape(B))
+        self._heads(hN.view(B, n, -1)[:, n - 1].contiguous())
 
     def step(self):
-        """One Medusa decode step (all on the GPU); returns (accept_len, path, tokens) tensors."""
+        """One Medusa decode step of the batch (all on the GPU); returns
+        (accept_len [B], path [B,K+1], tokens [B,N]) tensors."""
         if self.fused:
             tokens, pos, mask, x, h = M.medusa_tree_embed(
                 self.parent, self.rank, self.root, self.topk_ids, self.ctx, self.m.t["embed"],
                 self.m.t["layers"][0]["g_attn"], self.m.eps)
             logits, hN = self._layers(x, h, pos, mask)
-        else:
-            tokens, pos, mask = M.medusa_build_tree(self.parent, self.rank, self.root,
-                                                    self.topk_ids, self.ctx)
-            logits, hN = self.forward(tokens, pos, mask)
-        if self.fused:
             acc, path, nxt, hbest = M.medusa_decode_tail(
-                logits[None], tokens, self.parent, self.K, 2 if self.sampled else self.mode,
-                self.Kc, self.Vc, self.page_table, hN[None], self.ctx, self.root, self.log,
+                logits.view(self.B, self.N, -1), tokens, self.parent, self.K,
+                2 if self.sampled else self.mode, self.Kc, self.Vc, self.page_table,
+                hN.view(self.B, self.N, -1), self.ctx, self.root, self.log,
                 temperature=self.T, epsilon=self.eps, delta=self.delta, rng=self.rng,
                 h_best=self.h_best, out=self.out, ws=self.tail_ws)
             if self.K > 0:
                 self._heads(hbest)
             self.last = dict(tokens=tokens, logits=logits, hN=hN, pos=pos, mask=mask)
             return acc, path, tokens
+        tokens, pos, mask = M.medusa_build_tree(self.parent, self.rank, self.root,
+                                                self.topk_ids, self.ctx)
+        logits, hN = self.forward(tokens, pos, mask)
+        lv = logits.view(self.B, self.N, -1)
         if self.sampled:
-            acc, path, nxt = M.medusa_accept_sample(logits[None], tokens, self.parent, self.K,
-                                                    self.T, self.rng, out=self.out, ws=self.acc_ws)
+            acc, path, nxt = M.medusa_accept_sample(lv, tokens, self.parent, self.K, self.T,
+                                                    self.rng, out=self.out, ws=self.acc_ws)
         else:
-            acc, path, nxt = M.medusa_accept(logits[None], tokens, self.parent, self.K, self.mode,
+            acc, path, nxt = M.medusa_accept(lv, tokens, self.parent, self.K, self.mode,
                                              self.T, self.eps, self.delta, out=self.out,
                                              ws=self.acc_ws)
         M.kv_compact(self.Kc, self.Vc, self.page_table, self.ctx, path, acc, new_ctx=self.new_ctx,
                      src=self.src, dst=self.dst)
         if self.K > 0:
-            hbest = M.medusa_gather_rows(hN[None], path, acc)
+            hbest = M.medusa_gather_rows(hN.view(self.B, self.N, -1), path, acc)
             self._heads(hbest)
         self.root.copy_(nxt)
         self.ctx.copy_(self.new_ctx)
@@ -314,12 +329,22 @@ class MedusaDecoder:
         return self.g_out
 
     def generate(self, prompt, n_new, record=None, graph=False):
-        """Prefill, then Medusa steps until n_new tokens are emitted.  Returns int32[n_new].
+        """Prefill, then Medusa steps until every sequence has emitted n_new
+        tokens.  Returns int32 [n_new] (one sequence) or [B, n_new].
 
         With the fused tail the emitted tokens collect in the device log and
-        the host reads only the count, after batches of steps: at least
-        ceil(remaining / (K + 1)) more steps are needed, so that many run
-        back to back before the next read."""
+        the host reads only the counts, after batches of steps: at least
+        ceil(remaining / (K + 1)) more steps are needed (remaining counted for
+        the sequence that is furthest behind), so that many run back to back
+        before the next read.  ``record`` receives each step's accept length
+        (a list per sequence when B > 1)."""
+        B = self.B
+        plen = np.asarray(prompt).reshape(B, -1).shape[1]
+        # every step emits 1..K+1 tokens per sequence and runs until the
+        # slowest sequence is done: the fastest may emit (K+1) per step
+        worst = plen + (n_new if B == 1 else n_new * (self.K + 1)) + self.K + self.N
+        if worst > self.capacity:
+            raise ValueError(f"capacity {self.capacity} < {worst} slots that {n_new} tokens may need")
         self.prefill(prompt)
         if graph and getattr(self, "graph", None) is None:
             self.capture()
@@ -331,20 +356,27 @@ class MedusaDecoder:
             while done < n_new:
                 for _ in range(max(1, -(-(n_new - done) // (self.K + 1)))):
                     self.step_graph() if graph else self.step()
-                done = int(self.log[0, 0].item())
-            lg = self.log[0].cpu().numpy()
+                done = int(self.log[:, 0].min().item())
+            lg = self.log.cpu().numpy()
             if record is not None:
-                record.extend(int(a) for a in lg[2 + cap:2 + cap + int(lg[1])])
+                recs = [[int(a) for a in lg[b, 2 + cap:2 + cap + int(lg[b, 1])]] for b in range(B)]
+                record.extend(recs[0] if B == 1 else recs)
             self.ctx_host += done
-            return lg[2:2 + n_new].astype(np.int32)
-        out = []
-        while len(out) < n_new:
+            out = lg[:, 2:2 + n_new].astype(np.int32)
+            return out[0] if B == 1 else out
+        outs = [[] for _ in range(B)]
+        recs = [[] for _ in range(B)]
+        while min(len(o) for o in outs) < n_new:
             acc, path, tokens = self.step_graph() if graph else self.step()
-            a = int(acc.item())
-            p = path[0, :a + 1].cpu().numpy()
-            tk = tokens[0].cpu().numpy()
-            out.extend(int(tk[j]) for j in p)
-            self.ctx_host += a + 1
-            if record is not None:
-                record.append(a)
-        return np.array(out[:n_new], np.int32)
+            a_h = acc.cpu().numpy()
+            p_h = path.cpu().numpy()
+            t_h = tokens.cpu().numpy()
+            for b in range(B):
+                a = int(a_h[b])
+                outs[b].extend(int(t_h[b, j]) for j in p_h[b, :a + 1])
+                recs[b].append(a)
+            self.ctx_host += int(a_h[0]) + 1
+        if record is not None:
+            record.extend(recs[0] if B == 1 else recs)
+        out = np.array([o[:n_new] for o in outs], np.int32)
+        return out[0] if B == 1 else out

@@ -134,3 +134,49 @@ def test_c1_separate_tail_equals_oracle(c1, mode):
         assert got.tolist() == ref.tolist(), _report(ref, got)
         recs[tail] = rec
     assert recs["fused"] == recs["separate"]
+
+
+def _prompts(B, n, V, seed0=300):
+    return np.stack([synth.prompt_tokens(seed0 + b, n, V) for b in range(B)])
+
+
+@pytest.mark.parametrize("tail", ["fused", "separate"])
+def test_c1_batched_greedy_equals_oracle_per_sequence(c1, tail):
+    """Three sequences decoded together (their trees' rows through every
+    projection at once, each with its own pages and context) emit exactly
+    each prompt's sequential greedy tokens, eagerly and from a replayed graph."""
+    from speculative_decoding_02_amd.decoder import DeviceModel, MedusaDecoder
+    m, _, _ = c1
+    case(f"c1 batched greedy B=3 tail={tail}")
+    B, n_new = 3, 40
+    prompts = _prompts(B, 32, m.vocab)
+    refs = [orc.sequential_greedy(m, prompts[b], n_new)[0] for b in range(B)]
+    dm = DeviceModel(m, dtype=torch.float32)
+    parent, rank = synth.tree_template((2, 3))
+    dec = MedusaDecoder(dm, parent, rank, capacity=32 + 3 * n_new + 16, batch=B, tail=tail)
+    for graph in (False, True):
+        rec = []
+        got = dec.generate(prompts, n_new, record=rec, graph=graph)
+        assert got.shape == (B, n_new)
+        for b in range(B):
+            assert got[b].tolist() == refs[b].tolist(), f"sequence {b}: " + _report(refs[b], got[b])
+        assert len(rec) == B and all(len(r) == len(rec[0]) for r in rec)
+
+
+def test_c1_batched_sampled_equals_oracle_per_sequence(c1):
+    """Sampled verification of a batch: sequence b emits the oracle's sampled
+    decoding of its prompt with counter word b."""
+    from speculative_decoding_02_amd.decoder import DeviceModel, MedusaDecoder
+    m, _, _ = c1
+    case("c1 batched sampled B=2")
+    B, n_new, T, seed = 2, 32, 0.8, 11
+    prompts = _prompts(B, 24, m.vocab, seed0=500)
+    parent, rank = synth.tree_template((2, 3))
+    refs = [orc.medusa_generate(m, prompts[b], n_new, parent, rank, mode="sample", temperature=T,
+                                seed=seed, b=b)[0] for b in range(B)]
+    dm = DeviceModel(m, dtype=torch.float32)
+    dec = MedusaDecoder(dm, parent, rank, capacity=24 + 3 * n_new + 16, batch=B, mode="sample",
+                        temperature=T, seed=seed)
+    got = dec.generate(prompts, n_new, graph=True)
+    for b in range(B):
+        assert got[b].tolist() == refs[b].tolist(), f"sequence {b}: " + _report(refs[b], got[b])

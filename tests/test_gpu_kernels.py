@@ -158,9 +158,9 @@ def test_linear_large_rows_epilogues(lib):
 @pytest.mark.parametrize("dt,Mr,Kd,N", [(torch.bfloat16, 64, 4096, 4096), (torch.bfloat16, 48, 11008, 4096),
                                          (torch.bfloat16, 20, 4096, 2048), (torch.bfloat16, 40, 512, 1024),
                                          (torch.bfloat16, 1, 4096, 4096), (torch.bfloat16, 64, 256, 8192),
-                                         (torch.float32, 33, 256, 512)],
+                                         (torch.float32, 33, 256, 512), (torch.bfloat16, 300, 512, 4096)],
                          ids=["split2", "split4_uneven", "split32rows", "tiles_split", "onerow", "nosplit",
-                              "f32"])
+                              "f32", "large_rows"])
 def test_linear_rmsnorm(lib, dt, Mr, Kd, N):
     """Residual projection + next RMSNorm: bit for bit the unfused pair
     (fused into the split reduction or not), and close to the oracle."""
@@ -188,8 +188,9 @@ def test_linear_rmsnorm(lib, dt, Mr, Kd, N):
     (torch.bfloat16, 48, 512, 32, 32, 64),    # head dim 64: epilogue
     (torch.bfloat16, 64, 4096, 8, 8, 128),    # split contraction: projection, then rotary pass
     (torch.bfloat16, 1, 512, 32, 32, 128),    # one row: projection, then rotary pass
-    (torch.float32, 13, 256, 4, 2, 64)],
-    ids=["epi_wide", "epi_32rows", "epi_d64", "split", "onerow", "f32"])
+    (torch.float32, 13, 256, 4, 2, 64),
+    (torch.bfloat16, 300, 512, 8, 8, 128)],   # large-row tiling: projection, then rotary pass
+    ids=["epi_wide", "epi_32rows", "epi_d64", "split", "onerow", "f32", "large_rows"])
 def test_linear_qkv_rope(lib, dt, Mr, Kd, Hq, Hkv, D):
     """QKV projection with rotary positions fused, on the pair-interleaved
     weight: bit for bit the plain projection + medusa_qkv_rope, and close to
