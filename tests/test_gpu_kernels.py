@@ -264,6 +264,32 @@ def test_heads_vs_oracle(lib, dt, Mr, H, V, K, k):
             assert np.array_equal(host(vals[kk, m]), ov)
 
 
+@pytest.mark.parametrize("Mr,H,V,K,k", [(17, 256, 8192, 2, 4), (32, 512, 12288, 3, 10),
+                                        (64, 256, 8192, 5, 16), (100, 256, 16384, 2, 1),
+                                        (255, 512, 8192, 2, 10), (64, 256, 8192, 2, 17),
+                                        (5, 256, 8192, 2, 4)])
+def test_heads_topk_without_logits_buffer(lib, Mr, H, V, K, k):
+    """Without a logits buffer (the decode loop's call) the heads' top-k ids
+    and values equal those of the run that stores the logits, which equal the
+    oracle's top-k of those logits."""
+    case(f"heads top-k without logits M={Mr} H={H} V={V} K={K} k={k}")
+    d = synth.heads_inputs(Mr * 3 + V, Mr, H, V, K, w1_std=0.05, w2_std=0.05, bf16=True)
+    bf = torch.bfloat16
+    args = (dev(d["X"], bf), dev(d["W1"], bf), dev(d["b1"], bf), dev(d["W2"], bf))
+    ws = lib._ws(lib._lib.medusa_heads_ws(Mr, H, K, V, k, lib.BF16), "cuda")
+    ids = torch.empty((K, Mr, k), dtype=torch.int32, device="cuda")
+    vals = torch.empty((K, Mr, k), dtype=torch.float32, device="cuda")
+    lib.medusa_heads(*args, topk=k, ids=ids, vals=vals, ws=ws, want_logits=False)
+    logits, ids2, vals2 = lib.medusa_heads(*args, topk=k)
+    assert torch.equal(ids, ids2) and torch.equal(vals, vals2)
+    lg = host(logits)
+    for kk in range(K):
+        for m in range(0, Mr, max(1, Mr // 9)):
+            oi, ov = orc.topk(lg[kk, m], k)
+            assert host(ids[kk, m]).tolist() == oi.tolist()
+            assert np.array_equal(host(vals[kk, m]), ov)
+
+
 # -------------------------------------------------------------------- topk ---
 @pytest.mark.parametrize("R,V,k", [(3, 1000, 1), (4, 1000, 3), (5, 32000, 10), (2, 70, 64),
                                    (6, 4097, 16), (1, 256, 17)])
