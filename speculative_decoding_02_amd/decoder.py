@@ -3,17 +3,20 @@
 One decode step ("Medusa Heads", sections "Come le teste prevedono i token
 successivi" and "Attenzione sull'albero e accettazione"):
 
-  build_tree  (root token + per-head top-k -> N tree tokens, positions, masks)
+  tree build  (root token + per-head top-k -> N tree tokens, positions, masks;
+              with the embedding rows and the first RMSNorm: medusa_tree_embed)
   verification forward of the N tree rows in ONE pass (Llama-style layers;
       tree-masked attention over the paged KV cache + the tree's own keys)
-  accept      (greedy, typical or sampled; longest accepted branch, next root
-              token)
-  kv_compact  (keep only the accepted branch in every layer's cache)
-  gather_rows + heads (the kept branch's last hidden state -> next top-k)
+  tail        (medusa_decode_tail: accept, greedy / typical / sampled, keep only
+              the accepted branch in every layer's cache, the kept branch's
+              last hidden state, next root token, context length, decode log)
+  heads       (that hidden state -> the next round's top-k)
 
-Python only allocates device buffers, uploads static inputs (weights, tree
-template, prompt) and reads back the accepted tokens; every computation is a
-library kernel.  Weight layout chosen for the GPU: Wq|Wk|Wv stacked into one
+``tail="separate"`` runs the same step with the individual calls
+(medusa_build_tree, medusa_embed, medusa_rmsnorm, medusa_accept, kv_compact,
+medusa_gather_rows) and host copies.  Python only allocates device buffers,
+uploads static inputs (weights, tree template, prompts) and reads back the
+emitted tokens; every computation is a library kernel.  Weight layout chosen for the GPU: Wq|Wk|Wv stacked into one
 [(Hq+2Hkv)*D, H] matrix, and gate/up interleaved in 16-row blocks so the
 down-projection input comes straight out of the SwiGLU epilogue.
 """
