@@ -364,24 +364,21 @@ __global__ __launch_bounds__(256) void gemm_xlds_kernel(const T* __restrict__ X,
 }
 
 // ---------------------------------------------------------------------------
-// Variant for wide outputs (M > 16 rows, N/16 >= MEDUSA_GEMM_XB_MIN_BLOCKS):
-// G workgroups of eight waves per (batch element, activation-row tile), about
-// one per compute unit, each owning a contiguous range of whole 16-row weight
-// blocks over the full contraction (pairs of blocks for SwiGLU, whose gate
-// and up rows interleave in 16-row blocks).  Wave w streams block w of the
-// range (waves past the range only help stage activations), so every wave
-// keeps one row block's loads in flight, PF steps ahead in registers.
-// Workgroup g starts its contraction at chunk g*nchunks/G and wraps round:
-// at any moment the compute units read different column offsets of their
-// rows (when all start at column 0 together the weight stream measured 20-35%
-// slower).  The activation rows are staged through two LDS buffers, one
-// 256-wide chunk at a time, with one barrier per chunk; every load is
-// unconditional (clamped) and scheduling barriers fix the issue order, so the
-// compiler's wait counts stay exact.  The epilogue goes through LDS, so a
-// gate block and its up block may sit in different waves and the output
-// stores are coalesced.  Each output is one wave's accumulation chain in
-// step order from the workgroup's start chunk: results depend on (Kd, N) and
-// the launch plan, itself a function of the shape.
+// Block-range plan for M > 16 rows (bf16): G workgroups of eight waves per
+// (batch element, activation-row tile, contraction split), about one per
+// compute unit, each owning a contiguous range of whole 16-row weight blocks
+// (pairs of blocks for SwiGLU, whose gate and up rows interleave in 16-row
+// blocks).  Wave w streams block w of the range (waves past the range only
+// help stage activations).  Workgroup g starts its contraction at chunk
+// g*nchunks/G and wraps round: at any moment the compute units read different
+// column offsets of their rows (when all start at column 0 together the weight
+// stream measured 20-35% slower).  The activation rows are staged through two
+// LDS buffers, one 256-wide chunk at a time, with one barrier per chunk.  The
+// epilogue goes through LDS, so a gate block and its up block may sit in
+// different waves and the output stores are coalesced.  Each output is one
+// wave's accumulation chain in step order from the workgroup's start chunk:
+// results depend on (Kd, N) and the launch plan, itself a function of the
+// shape.
 constexpr int XB_KC = 256;
 constexpr int XB_WAVES = 8;
 constexpr int XB_MAXB = XB_WAVES;  // blocks per workgroup: one per wave
@@ -404,142 +401,12 @@ __device__ __forceinline__ void xb_store(int gi, int M, int Nw, int64_t xbs, con
   }
 }
 
-template <typename T, int MB, int PF, int EPI>
-__global__ __launch_bounds__(64 * XB_WAVES) void gemm_xlb_kernel(
-    const T* __restrict__ X, int64_t xbs, int M, int Kd, const T* __restrict__ W, int Nw,
-    const T* __restrict__ bias, const void* aux, void* Y, int y_f32, int G, int MT, int unit) {
-  using TR = GemmTraits<T>;
-  constexpr int P16 = TR::per16;
-  constexpr int KSTEP = 4 * P16;
-  constexpr int SC = XB_KC / KSTEP;             // steps per chunk
-  constexpr int NT = 64 * XB_WAVES;
-  constexpr int TM = 16 * MB;
-  constexpr int LDX = XB_KC + P16;              // padded LDS row (elements)
-  constexpr int XS = TM * LDX;                  // elements per activation buffer
-  constexpr int XV = TM * XB_KC / P16 / NT;     // 16-byte vectors per thread per chunk
-  constexpr int LDE = TM + 1;
-  constexpr int XSB = 2 * XS * (int)sizeof(T);
-  constexpr int EPB = XB_MAXB * 16 * LDE * 4;
-  static_assert(PF == SC, "the prologue mirrors one chunk of the loop");
-  static_assert(XV * NT * P16 == TM * XB_KC, "activation chunk must split evenly");
-  __shared__ __attribute__((aligned(16))) char smem[XSB > EPB ? XSB : EPB];
-  T* xs = reinterpret_cast<T*>(smem);
-  float* ep = reinterpret_cast<float*>(smem);  // after the contraction
 
-  const int g = blockIdx.x, slice = blockIdx.y;
-  const int gi = slice / MT, m0 = (slice % MT) * TM;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int lr = lane & 15, lg = lane >> 4;
-  const int nunits = (Nw / 16) / unit;
-  const int u0 = (int)((int64_t)g * nunits / G), u1 = (int)((int64_t)(g + 1) * nunits / G);
-  const int b0 = u0 * unit, nb = (u1 - u0) * unit;  // this workgroup's blocks (<= XB_MAXB)
-  const int nchunks = Kd / XB_KC;
-  const int nsteps = nchunks * SC;
-  const int c0 = (int)((int64_t)g * nchunks / G);  // start chunk (< nchunks)
-  const T* Xg = X + (int64_t)gi * xbs;
-  const T* Wg = W + (int64_t)gi * Nw * Kd;
-
-  u32x4 xr[XV];
-  auto xload = [&](int q) {  // the q-th chunk of this workgroup's order
-    int c = c0 + min(q, nchunks - 1);
-    if (c >= nchunks) c -= nchunks;
-#pragma unroll
-    for (int i = 0; i < XV; ++i) {
-      const int idx = threadIdx.x + i * NT;
-      const int row = idx / (XB_KC / P16), col = idx % (XB_KC / P16);
-      const int rr = min(m0 + row, M - 1);
-      xr[i] = *reinterpret_cast<const u32x4*>(Xg + (int64_t)rr * Kd + c * XB_KC + col * P16);
-    }
-  };
-  auto xstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < XV; ++i) {
-      const int idx = threadIdx.x + i * NT;
-      const int row = idx / (XB_KC / P16), col = idx % (XB_KC / P16);
-      *reinterpret_cast<u32x4*>(&xs[buf * XS + row * LDX + col * P16]) = xr[i];
-    }
-  };
-  f32x4 acc[MB];
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  auto run = [&](auto activec) {
-    constexpr bool ACT = decltype(activec)::value;
-    const int blk = min(b0 + wave, Nw / 16 - 1);
-    const T* wrow = Wg + (int64_t)(blk * 16 + lr) * Kd + lg * P16;
-    u32x4 fb[PF];
-    auto wload = [&](int u, int s) {  // the s-th step of this workgroup's order
-      if constexpr (ACT) {
-        int ps = min(s, nsteps - 1) + c0 * SC;
-        if (ps >= nsteps) ps -= nsteps;
-        fb[u] = *reinterpret_cast<const u32x4*>(wrow + (int64_t)ps * KSTEP);
-      }
-    };
-    // Prologue: chunk 0 into buffer 0, then the loads one loop turn issues
-    // (next chunk's activations, then PF weight steps), so the loop head sees
-    // one pending-load pattern on entry and on every turn.
-    xload(0);
-    xstore(0);
-    xload(1);
-#pragma unroll
-    for (int u = 0; u < PF; ++u) wload(u, u);
-    __builtin_amdgcn_sched_barrier(0);
-    for (int q = 0; q < nchunks; ++q) {
-      __syncthreads();  // chunk q is in buffer q&1; no one still reads chunk q-1
-      xstore((q + 1) & 1);  // chunk q+1 (after the last chunk: a store nobody reads)
-      xload(q + 2);
-      __builtin_amdgcn_sched_barrier(0);
-      if constexpr (ACT) {
-        const T* xb = xs + (q & 1) * XS;
-#pragma unroll
-        for (int sl = 0; sl < SC; ++sl) {
-          u32x4 xa[MB];
-#pragma unroll
-          for (int mb = 0; mb < MB; ++mb)
-            xa[mb] = *reinterpret_cast<const u32x4*>(&xb[(mb * 16 + lr) * LDX + sl * KSTEP + lg * P16]);
-#pragma unroll
-          for (int mb = 0; mb < MB; ++mb) acc[mb] = TR::mma(xa[mb], fb[sl], acc[mb]);
-          wload(sl, q * SC + sl + PF);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
-    }
-  };
-  if (wave < nb) run(std::true_type());
-  else run(std::false_type());
-  __syncthreads();  // the activation buffers become the epilogue tile
-  // lane holds weight row lr of local block `wave`, activation rows mb*16 + 4*lg + r
-  if (wave < nb) {
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) ep[(wave * 16 + lr) * LDE + mb * 16 + lg * 4 + r] = acc[mb][r];
-  }
-  __syncthreads();
-
-  if (EPI == MEDUSA_EPI_SWIGLU) {
-    // local blocks 2p (gate) and 2p+1 (up); b0 is even
-    const int F = Nw / 2, f0 = b0 / 2 * 16, nf = nb / 2 * 16;
-    T* Yg = reinterpret_cast<T*>(Y) + (int64_t)gi * M * F;
-    for (int e = threadIdx.x; e < nf * TM; e += NT) {
-      const int m = e / nf, fl = e % nf;
-      const int gr = (fl / 16) * 32 + fl % 16;  // gate row in the range; up is 16 further
-      if (m0 + m < M) st<T>(Yg, (int64_t)(m0 + m) * F + f0 + fl, silu_f(ep[gr * LDE + m]) * ep[(gr + 16) * LDE + m]);
-    }
-    return;
-  }
-  const int nn = nb * 16;
-  for (int e = threadIdx.x; e < nn * TM; e += NT) {
-    const int m = e / nn, nl = e % nn;
-    if (m0 + m < M) xb_store<T, EPI>(gi, M, Nw, xbs, bias, aux, Y, y_f32, m0 + m, b0 * 16 + nl, ep[nl * LDE + m]);
-  }
-}
-
-// The same block-range plan with every operand brought in by LDS DMA (bf16).
-// A register load of a weight step reads 64 bytes of each of 16 rows (the
-// MFMA operand layout); here one DMA instruction reads 256 contiguous bytes
-// of each of 4 rows (two whole 128-byte lines per row) into a per-wave LDS
-// ring, and the MFMA operands are read back from LDS.  The activation chunk
+// The block-range kernel, with every operand brought in by LDS DMA (bf16).
+// A register load of a weight step would read 64 bytes of each of 16 rows
+// (the MFMA operand layout); here one DMA instruction reads 256 contiguous
+// bytes of each of 4 rows (two whole 128-byte lines per row) into a per-wave
+// LDS ring, and the MFMA operands are read back from LDS.  The activation chunk
 // comes in by DMA too (no registers, no LDS store instructions), double
 // buffered with one barrier per chunk.  Nothing is loaded into registers from
 // global memory in the loop, so every wait is an explicit vmcnt immediate
@@ -1034,13 +901,6 @@ __global__ __launch_bounds__(256) void split_reduce_rmsnorm_kernel(const float* 
 #ifndef MEDUSA_GEMM_XL_NB
 #define MEDUSA_GEMM_XL_NB 2
 #endif
-#ifndef MEDUSA_GEMM_XB_PF
-#define MEDUSA_GEMM_XB_PF 8
-#endif
-// block-range projections through LDS DMA (1) or register loads (0)
-#ifndef MEDUSA_GEMM_XB_DMA
-#define MEDUSA_GEMM_XB_DMA 1
-#endif
 #ifndef MEDUSA_GEMM_XL_TARGET_WGS
 #define MEDUSA_GEMM_XL_TARGET_WGS 384
 #endif
@@ -1114,7 +974,7 @@ GemmPlan gemm_plan(int64_t M, int64_t Kd, int64_t Nw, int dt, int epi) {
     p.big = t256 >= 200 ? 1 : 2;
     return p;
   }
-  const bool narrow = MEDUSA_GEMM_XB_DMA && Nw / 16 >= MEDUSA_GEMM_XD_MIN_BLOCKS;
+  const bool narrow = Nw / 16 >= MEDUSA_GEMM_XD_MIN_BLOCKS;
   if (dt == MEDUSA_BF16 && M > 16 && Kd % XB_KC == 0 && Nw % (16 * unit) == 0 &&
       (Nw / 16 >= MEDUSA_GEMM_XB_MIN_BLOCKS || narrow) && Nw / 16 <= (1 << 24)) {
     const int nunits = (int)(Nw / 16 / unit);
@@ -1203,31 +1063,23 @@ static bool launch_gemm_t(const void* X, int64_t xbs, int64_t M, int64_t Kd, con
       const T* Wt = reinterpret_cast<const T*>(W);
       const T* Bt = reinterpret_cast<const T*>(bias);
       float* part = reinterpret_cast<float*>(ws);
-      if (MEDUSA_GEMM_XB_DMA) {
-        if (M <= 32)
-          hipLaunchKernelGGL((gemm_xdma_kernel<2, MEDUSA_GEMM_XD_WR, EPI>), grid, dim3(64 * XB_WAVES), 0, st, Xt, xbs,
-                             (int)M, (int)Kd, Wt, (int)Nw, Bt, aux, Y, y_f32, plan.xb_G, plan.MT, plan.xb_unit, part, RopeArgs{});
-        else
-          hipLaunchKernelGGL((gemm_xdma_kernel<4, MEDUSA_GEMM_XD_WR, EPI>), grid, dim3(64 * XB_WAVES), 0, st, Xt, xbs,
-                             (int)M, (int)Kd, Wt, (int)Nw, Bt, aux, Y, y_f32, plan.xb_G, plan.MT, plan.xb_unit, part, RopeArgs{});
-        if (plan.xb_S > 1) {
-          if (EPI == MEDUSA_EPI_RES_ADD_F32 && norm) {
-            hipLaunchKernelGGL(split_reduce_rmsnorm_kernel<T>, dim3((unsigned)M), dim3(256), 0, st, part,
-                               plan.xb_S, (int)M, (int)Nw, reinterpret_cast<float*>(Y),
-                               reinterpret_cast<const T*>(norm->gain), norm->eps, reinterpret_cast<T*>(norm->out));
-            return true;
-          }
-          const int64_t cols = EPI == MEDUSA_EPI_SWIGLU ? Nw / 2 : Nw;
-          dim3 rgrid((unsigned)((M * cols + 255) / 256), (unsigned)batch);
-          hipLaunchKernelGGL((gemm_split_reduce_kernel<T, EPI>), rgrid, dim3(256), 0, st, part, plan.xb_S,
-                             (int)M, (int)Nw, xbs, Bt, aux, Y, y_f32);
+      if (M <= 32)
+        hipLaunchKernelGGL((gemm_xdma_kernel<2, MEDUSA_GEMM_XD_WR, EPI>), grid, dim3(64 * XB_WAVES), 0, st, Xt, xbs,
+                           (int)M, (int)Kd, Wt, (int)Nw, Bt, aux, Y, y_f32, plan.xb_G, plan.MT, plan.xb_unit, part, RopeArgs{});
+      else
+        hipLaunchKernelGGL((gemm_xdma_kernel<4, MEDUSA_GEMM_XD_WR, EPI>), grid, dim3(64 * XB_WAVES), 0, st, Xt, xbs,
+                           (int)M, (int)Kd, Wt, (int)Nw, Bt, aux, Y, y_f32, plan.xb_G, plan.MT, plan.xb_unit, part, RopeArgs{});
+      if (plan.xb_S > 1) {
+        if (EPI == MEDUSA_EPI_RES_ADD_F32 && norm) {
+          hipLaunchKernelGGL(split_reduce_rmsnorm_kernel<T>, dim3((unsigned)M), dim3(256), 0, st, part,
+                             plan.xb_S, (int)M, (int)Nw, reinterpret_cast<float*>(Y),
+                             reinterpret_cast<const T*>(norm->gain), norm->eps, reinterpret_cast<T*>(norm->out));
+          return true;
         }
-      } else if (M <= 32) {
-        hipLaunchKernelGGL((gemm_xlb_kernel<T, 2, MEDUSA_GEMM_XB_PF, EPI>), grid, dim3(64 * XB_WAVES), 0, st,
-                           Xt, xbs, (int)M, (int)Kd, Wt, (int)Nw, Bt, aux, Y, y_f32, plan.xb_G, plan.MT, plan.xb_unit);
-      } else {
-        hipLaunchKernelGGL((gemm_xlb_kernel<T, 4, MEDUSA_GEMM_XB_PF, EPI>), grid, dim3(64 * XB_WAVES), 0, st,
-                           Xt, xbs, (int)M, (int)Kd, Wt, (int)Nw, Bt, aux, Y, y_f32, plan.xb_G, plan.MT, plan.xb_unit);
+        const int64_t cols = EPI == MEDUSA_EPI_SWIGLU ? Nw / 2 : Nw;
+        dim3 rgrid((unsigned)((M * cols + 255) / 256), (unsigned)batch);
+        hipLaunchKernelGGL((gemm_split_reduce_kernel<T, EPI>), rgrid, dim3(256), 0, st, part, plan.xb_S,
+                           (int)M, (int)Nw, xbs, Bt, aux, Y, y_f32);
       }
       return false;
     }
@@ -1383,7 +1235,7 @@ void launch_qkv_rope_pairs(const void* qkv, int64_t M, int Hq, int Hkv, int D, c
 // the fused epilogue runs where the projection takes the unsplit DMA block-range kernel
 static bool qkv_rope_fused(int64_t M, int64_t Kd, int64_t N, int dt) {
   const GemmPlan p = gemm_plan(M, Kd, N, dt, MEDUSA_EPI_NONE);
-  return MEDUSA_GEMM_XB_DMA && dt == MEDUSA_BF16 && p.xb && p.xb_S == 1;
+  return dt == MEDUSA_BF16 && p.xb && p.xb_S == 1;
 }
 }  // namespace medusa_host
 
