@@ -390,7 +390,9 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures the one-GPU Medusa step; runs on more than one GPU are not "
-              "part of this build (see DESIGN.md for how the path would shard).", file=sys.stderr)
+              "part of this implementation: it would shard tree attention by head or sequence "
+              "and the heads' vocabulary projection by vocabulary slice, one GPU's share being "
+              "what this measures.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
