@@ -696,6 +696,42 @@ def test_decode_tail(lib, dt, mode, L, Hkv, D):
     assert near < 3 * B and deep >= 1
 
 
+@pytest.mark.parametrize("shape", ["chain9", "root_only"])
+def test_decode_tail_edges(lib, shape):
+    """The tail's degenerate trees: a 9-node chain whose every candidate is
+    its parent's argmax (the longest accept, K = 8, every row already in
+    place), and a root-only tree (K = 0: plain decoding)."""
+    case(f"decode tail edge {shape}")
+    V, P, D, Hkv, L = 500, 16, 64, 2, 2
+    rng = np.random.default_rng(31)
+    N = 9 if shape == "chain9" else 1
+    K = N - 1
+    parent = np.arange(-1, N - 1, dtype=np.int32)
+    logits = (rng.standard_normal((N, V)) * 2).astype(np.float32)
+    tok = np.zeros(N, np.int32)
+    tok[0] = 7
+    for i in range(1, N):
+        tok[i] = orc.argmax(logits[i - 1])
+    ctx = 21
+    max_pages = (ctx + N + P) // P + 1
+    pools = [dev(rng.standard_normal((max_pages, Hkv, P, D)).astype(np.float32)) for _ in range(2 * L)]
+    ref_pools = [t.clone() for t in pools]
+    hid = dev(rng.standard_normal((1, N, 64)).astype(np.float32))
+    pt = dev(np.arange(max_pages, dtype=np.int32)[None])
+    ctx_t, root, log = dev(np.array([ctx], np.int32)), dev(np.zeros(1, np.int32)), lib.decode_log(1, 16)
+    acc, path, nxt, hb = lib.medusa_decode_tail(dev(logits[None]), dev(tok[None]), dev(parent[None]), K,
+                                                0, pools[:L], pools[L:], pt, hid, ctx_t, root, log)
+    r = orc.accept_greedy(logits, tok, parent, K)
+    assert r["accept_len"] == K
+    assert int(host(acc)[0]) == K and host(path)[0].tolist() == list(range(N))
+    assert int(host(nxt)[0]) == r["next_token"] == int(host(root)[0])
+    assert int(host(ctx_t)[0]) == ctx + N
+    np.testing.assert_array_equal(host(hb)[0], host(hid)[0, N - 1])
+    assert all(torch.equal(a, b) for a, b in zip(pools, ref_pools))   # path[d] == d: nothing moves
+    lg = host(log)[0]
+    assert lg[0] == N and lg[1] == 1 and lg[2:2 + N].tolist() == tok.tolist() and lg[2 + 16] == K
+
+
 # ---------------------------------------------------------------- backbone ---
 @pytest.mark.parametrize("dt", DTS, ids=DTN.get)
 def test_backbone_ops(lib, dt):
