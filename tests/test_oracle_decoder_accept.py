@@ -174,6 +174,44 @@ def test_typical_monotone_in_epsilon_and_delta():
             prev = a
 
 
+def _one_child(row, tok):
+    """Root + one child carrying ``tok``; the root's logits row decides."""
+    logits = np.stack([np.asarray(row, np.float32), np.zeros(len(row), np.float32)])
+    return logits, np.array([0, tok], np.int32), np.array([-1, 0], np.int32)
+
+
+@pytest.mark.parametrize("V", [2, 7, 1000])
+def test_typical_uniform_row_entropy_is_log_v(V):
+    """Uniform logits: p(x) = 1/V and H = ln V, so the threshold is
+    min(eps, delta / V): delta < 1 accepts, delta > 1 rejects (an entropy in
+    another base, or with a sign error, fails one of the two)."""
+    logits, tok, par = _one_child(np.full(V, 0.37), 1)
+    assert orc.accept_typical(logits, tok, par, 1, 1.0, 1.0, 0.5)["accept_len"] == 1
+    assert orc.accept_typical(logits, tok, par, 1, 1.0, 1.0, 2.0)["accept_len"] == 0
+    r = orc.accept_typical(logits, tok, par, 1, 1.0, 1.0, 0.5, return_margins=True)
+    # margin = ln p - ln thr = ln(1/V) - ln(0.5/V) = ln 2
+    assert r["margins"][1] == pytest.approx(np.log(2.0), abs=1e-6)
+
+
+def test_typical_two_point_distribution_closed_form():
+    """p = (1/4, 3/4) (logits 0 and ln 3, the rest -60): H = ln 4 - (3/4) ln 3.
+    Token 0 (p = 1/4) is accepted iff delta e^-H < 1/4; the decision flips
+    where the closed form says, and the temperature divides the logits
+    (T = 2 on doubled logits gives the same law)."""
+    V = 6
+    row = np.full(V, -60.0)
+    row[0], row[1] = 0.0, np.log(3.0)
+    H = np.log(4.0) - 0.75 * np.log(3.0)
+    d_star = 0.25 * np.exp(H)
+    for T, r_ in ((1.0, row), (2.0, 2 * row)):
+        logits, tok, par = _one_child(r_, 0)
+        assert orc.accept_typical(logits, tok, par, 1, T, 1.0, d_star * (1 - 1e-4))["accept_len"] == 1
+        assert orc.accept_typical(logits, tok, par, 1, T, 1.0, d_star * (1 + 1e-4))["accept_len"] == 0
+        # the hard threshold epsilon binds when it is the smaller one
+        assert orc.accept_typical(logits, tok, par, 1, T, 0.2499, 10.0)["accept_len"] == 1
+        assert orc.accept_typical(logits, tok, par, 1, T, 0.2501, 10.0)["accept_len"] == 0
+
+
 def test_greedy_accept_hand_example():
     """Top-2 x top-3 tree; the model's choices make the branch (1, 0) win."""
     parent, rank = synth.tree_template((2, 3))
