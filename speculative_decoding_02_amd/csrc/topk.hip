@@ -3,11 +3,20 @@
 // Order: value descending, equal values by lower index.
 //
 // Two launches.  Stage 1, grid (chunks, rows): a workgroup takes a 4096-wide
-// slice of a row; each thread reads its 16 values with 16-byte loads issued
-// together (no load waits on a comparison), keeps a sorted register list,
-// and the workgroup merges the lists by k rounds of a block-wide selection
-// into k candidates.  Stage 2, one workgroup per row: the same selection over
-// the chunks' candidates.  With one chunk, stage 1 writes the result.
+// slice of a row, each thread 16 values read with 16-byte loads issued
+// together.  For k <= 16 each wave then filters its 1024 values by a
+// threshold T, the k-th largest of its 64 lane maxima: at least k values
+// reach T, so no value below it can be among the k best, and on ordinary
+// data only a few more than k do.  The survivors are packed into LDS by
+// ballot and sorted across the wave by a bitonic network on 64-bit keys
+// (order-preserving value bits, then the complemented index); lanes 0..k-1
+// hold the wave's k best.  A wave whose survivors do not fit one per lane
+// (long runs of equal values) takes the sorted per-lane lists and k rounds
+// of a wave argmax instead.  Wave 0 sorts the four waves' lists the same
+// way.  Stage 2 merges a row's chunk candidates, one wave per row: 64 at a
+// time sorted, each batch folded into the running best by the bitonic
+// merge step.  For k > 16 both stages keep a block-wide selection.  With one
+// chunk, stage 1 writes the result.
 #include "common.h"
 
 namespace medusa {
@@ -67,69 +76,157 @@ __device__ __forceinline__ void wave_argmax(float& bv, int& bi) {
   }
 }
 
-// k best of the threads' sorted lists.  k <= 16: every wave emits its own k
-// best (k rounds of a wave argmax over the list heads; the owner pops, ids
-// being unique), the four lists meet in LDS, and wave 0 selects k of those
-// 4k (one candidate per lane).  k > 16: k rounds of a block-wide argmax.
+// Sort keys: the float's bits made order-preserving as unsigned (-0 taken
+// as +0, so signed zeros tie as they compare), then the index complemented,
+// so a larger key is the better (value, index) pair.  NaN never becomes a
+// key: it fails every comparison that admits a value.
+__device__ __forceinline__ uint64_t topk_key(float v, int i) {
+  uint32_t u = __float_as_uint(v);
+  if (u == 0x80000000u) u = 0u;
+  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((uint64_t)u << 32) | (uint32_t)~(uint32_t)i;
+}
+__device__ __forceinline__ int key_index(uint64_t key) { return (int)~(uint32_t)key; }
+__device__ __forceinline__ float key_value(uint64_t key) {
+  const uint32_t u = (uint32_t)(key >> 32);
+  return __uint_as_float((u & 0x80000000u) ? (u & 0x7fffffffu) : ~u);
+}
+// The list padding (-inf, 0x7fffffff): below every real entry.
+constexpr uint64_t TOPK_PAD_KEY = (uint64_t)0x007fffffu << 32 | 0x80000000u;
+
+// Lane l's copy of lane l ^ J's register.
+template <int J>
+__device__ __forceinline__ uint32_t lane_xor(uint32_t v) {
+  if constexpr (J == 1) return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);
+  else if constexpr (J == 2) return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);
+  else return (uint32_t)__shfl_xor((int)v, J, 64);
+}
+template <int J>
+__device__ __forceinline__ uint64_t lane_xor(uint64_t v) {
+  return ((uint64_t)lane_xor<J>((uint32_t)(v >> 32)) << 32) | lane_xor<J>((uint32_t)v);
+}
+template <int J>
+__device__ __forceinline__ float lane_xor(float v) {
+  return __uint_as_float(lane_xor<J>(__float_as_uint(v)));
+}
+
+// Bitonic network over the 64 lanes of a wave (one key per lane).  Stage
+// (KK, J) compares lanes l and l ^ J; the pair belongs to a block of KK lanes
+// ordered descending when (l & KK) == 0 matches `desc`, and the lower lane
+// of the pair keeps the larger key in a descending block.
+template <int KK, int J, typename Key>
+__device__ __forceinline__ Key bitonic_pass(Key x, int lane, bool desc) {
+  const Key y = lane_xor<J>(x);
+  const bool block_desc = ((lane & KK) == 0) == desc;
+  const bool keep_larger = ((lane & J) == 0) == block_desc;
+  x = ((x > y) == keep_larger) ? x : y;
+  if constexpr (J > 1) return bitonic_pass<KK, J / 2>(x, lane, desc);
+  else return x;
+}
+template <int KK, typename Key>
+__device__ __forceinline__ Key bitonic_sort_from(Key x, int lane, bool desc) {
+  x = bitonic_pass<KK, KK / 2>(x, lane, desc);
+  if constexpr (KK < 64) return bitonic_sort_from<KK * 2>(x, lane, desc);
+  else return x;
+}
+// The wave's 64 keys sorted: lane 0 holds the largest when desc.
+template <typename Key>
+__device__ __forceinline__ Key wave_sort(Key x, int lane, bool desc) {
+  return bitonic_sort_from<2>(x, lane, desc);
+}
+// A bitonic sequence over the wave, sorted.
+template <typename Key>
+__device__ __forceinline__ Key wave_bitonic_merge(Key x, int lane, bool desc) {
+  return bitonic_pass<64, 32>(x, lane, desc);
+}
+
+// One wave's k best (k <= KMAX <= 16) of its lanes' 16 values each, written
+// as keys to out[0..k-1].  v[j] is element e(j) = base + (g*256 + t)*4 + r for
+// j = 4g + r; elements past V hold -inf and are never taken.
+template <int KMAX>
+__device__ __forceinline__ void wave_topk16(const float (&v)[TOPK_PER_THREAD], int64_t base,
+                                            int64_t V, int k, uint64_t* __restrict__ stage,
+                                            uint64_t* __restrict__ out) {
+  const int lane = threadIdx.x & 63;
+  float m = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < TOPK_PER_THREAD; ++j) m = fmaxf(m, v[j]);
+  const float sorted = wave_sort(m, lane, true);
+  const float T = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sorted), k - 1));
+  // survivors v >= T packed into stage[] by ballot; count C is wave-uniform
+  int C = 0;
+#pragma unroll
+  for (int j = 0; j < TOPK_PER_THREAD; ++j) {
+    const int64_t e = base + (int64_t)((j / 4) * TOPK_THREADS + threadIdx.x) * 4 + (j % 4);
+    const bool pred = e < V && v[j] >= T;
+    const uint64_t bal = __ballot(pred);
+    const int pos = C + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                                       __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+    if (pred && pos < 64) stage[pos] = topk_key(v[j], (int)e);
+    C += __popcll(bal);
+  }
+  if (C >= k && C <= 64) {
+    __builtin_amdgcn_wave_barrier();
+    uint64_t x = lane < C ? stage[lane] : TOPK_PAD_KEY;
+    x = wave_sort(x, lane, true);
+    if (lane < k) out[lane] = x;
+    return;
+  }
+  // too many equal values at the threshold (or fewer than k real ones):
+  // sorted per-lane lists, then k rounds of the wave argmax
+  float lv[KMAX];
+  int li[KMAX];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) { lv[j] = -INFINITY; li[j] = 0x7fffffff; }
+#pragma unroll
+  for (int j = 0; j < TOPK_PER_THREAD; ++j) {
+    const int64_t e = base + (int64_t)((j / 4) * TOPK_THREADS + threadIdx.x) * 4 + (j % 4);
+    if (e < V) list_insert<KMAX>(lv, li, v[j], (int)e);
+  }
+  for (int r = 0; r < k; ++r) {
+    float bv = lv[0];
+    int bi = li[0];
+    wave_argmax(bv, bi);
+    if (lane == 0) out[r] = topk_key(bv, bi);
+    if (li[0] == bi) {
+#pragma unroll
+      for (int j = 0; j + 1 < KMAX; ++j) { lv[j] = lv[j + 1]; li[j] = li[j + 1]; }
+      lv[KMAX - 1] = -INFINITY;
+      li[KMAX - 1] = 0x7fffffff;
+    }
+  }
+}
+
+// k best of the threads' sorted lists (k > 16): k rounds of a block-wide
+// argmax over the list heads; the owner pops (ids are unique).
 template <int KMAX>
 __device__ __forceinline__ void block_select(float (&lv)[KMAX], int (&li)[KMAX], int k,
                                              int* __restrict__ ids, float* __restrict__ vals) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  if constexpr (KMAX <= 16) {
-    __shared__ float cv[TOPK_THREADS / 64][KMAX];
-    __shared__ int ci[TOPK_THREADS / 64][KMAX];
-    for (int r = 0; r < k; ++r) {
-      float bv = lv[0];
-      int bi = li[0];
-      wave_argmax(bv, bi);
-      if (lane == 0) { cv[wave][r] = bv; ci[wave][r] = bi; }
-      if (li[0] == bi) {
-#pragma unroll
-        for (int j = 0; j + 1 < KMAX; ++j) { lv[j] = lv[j + 1]; li[j] = li[j + 1]; }
-        lv[KMAX - 1] = -INFINITY;
-        li[KMAX - 1] = 0x7fffffff;
-      }
+  __shared__ float sv[TOPK_THREADS / 64];
+  __shared__ int si[TOPK_THREADS / 64];
+  __shared__ int winner_i;
+  for (int r = 0; r < k; ++r) {
+    float bv = lv[0];
+    int bi = li[0];
+    wave_argmax(bv, bi);
+    if (lane == 0) { sv[wave] = bv; si[wave] = bi; }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      float wv = sv[0];
+      int wi = si[0];
+      for (int w = 1; w < TOPK_THREADS / 64; ++w)
+        if (better(sv[w], si[w], wv, wi)) { wv = sv[w]; wi = si[w]; }
+      winner_i = wi;
+      ids[r] = wi;
+      vals[r] = wv;
     }
     __syncthreads();
-    if (wave != 0) return;
-    static_assert(TOPK_THREADS / 64 * KMAX <= 64, "one candidate per lane");
-    const int w = lane / KMAX, j = lane % KMAX;
-    float v = -INFINITY;
-    int i = 0x7fffffff;
-    if (w < TOPK_THREADS / 64 && j < k) { v = cv[w][j]; i = ci[w][j]; }
-    for (int r = 0; r < k; ++r) {
-      float bv = v;
-      int bi = i;
-      wave_argmax(bv, bi);
-      if (lane == 0) { ids[r] = bi; vals[r] = bv; }
-      if (i == bi) { v = -INFINITY; i = 0x7fffffff; }
-    }
-  } else {
-    __shared__ float sv[TOPK_THREADS / 64];
-    __shared__ int si[TOPK_THREADS / 64];
-    __shared__ int winner_i;
-    for (int r = 0; r < k; ++r) {
-      float bv = lv[0];
-      int bi = li[0];
-      wave_argmax(bv, bi);
-      if (lane == 0) { sv[wave] = bv; si[wave] = bi; }
-      __syncthreads();
-      if (threadIdx.x == 0) {
-        float wv = sv[0];
-        int wi = si[0];
-        for (int w = 1; w < TOPK_THREADS / 64; ++w)
-          if (better(sv[w], si[w], wv, wi)) { wv = sv[w]; wi = si[w]; }
-        winner_i = wi;
-        ids[r] = wi;
-        vals[r] = wv;
-      }
-      __syncthreads();
-      if (li[0] == winner_i) {
+    if (li[0] == winner_i) {
 #pragma unroll
-        for (int j = 0; j + 1 < KMAX; ++j) { lv[j] = lv[j + 1]; li[j] = li[j + 1]; }
-        lv[KMAX - 1] = -INFINITY;
-        li[KMAX - 1] = 0x7fffffff;
-      }
+      for (int j = 0; j + 1 < KMAX; ++j) { lv[j] = lv[j + 1]; li[j] = li[j + 1]; }
+      lv[KMAX - 1] = -INFINITY;
+      li[KMAX - 1] = 0x7fffffff;
     }
   }
 }
@@ -143,10 +240,6 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_chunk_kernel(const float* _
   const int s = blockIdx.x;
   const int64_t row = blockIdx.y;
   const float* x = logits + row * V;
-  float lv[KMAX];
-  int li[KMAX];
-#pragma unroll
-  for (int j = 0; j < KMAX; ++j) { lv[j] = -INFINITY; li[j] = 0x7fffffff; }
   const int64_t base = (int64_t)s * TOPK_CHUNK;
   // 16 values per thread: four 16-byte groups, strided by the block width
   float v[TOPK_PER_THREAD];
@@ -163,15 +256,68 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_chunk_kernel(const float* _
       for (int r = 0; r < 4; ++r) v[g * 4 + r] = (e0 + r < V) ? x[e0 + r] : -INFINITY;
     }
   }
-#pragma unroll
-  for (int g = 0; g < TOPK_PER_THREAD / 4; ++g)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int64_t e = base + (int64_t)(g * TOPK_THREADS + threadIdx.x) * 4 + r;
-      if (e < V) list_insert<KMAX>(lv, li, v[g * 4 + r], (int)e);
-    }
   const int64_t o = (row * gridDim.x + s) * (int64_t)out_stride;
-  block_select<KMAX>(lv, li, k, ids + o, vals + o);
+  if constexpr (KMAX <= 16) {
+    constexpr int NW = TOPK_THREADS / 64;
+    __shared__ uint64_t stage[NW][64];
+    __shared__ uint64_t best[NW][16];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    wave_topk16<KMAX>(v, base, V, k, stage[wave], best[wave]);
+    __syncthreads();
+    if (wave != 0) return;
+    uint64_t key = (lane % 16) < k ? best[lane / 16][lane % 16] : TOPK_PAD_KEY;
+    key = wave_sort(key, lane, true);
+    if (lane < k) {
+      ids[o + lane] = key_index(key);
+      vals[o + lane] = key_value(key);
+    }
+  } else {
+    float lv[KMAX];
+    int li[KMAX];
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) { lv[j] = -INFINITY; li[j] = 0x7fffffff; }
+#pragma unroll
+    for (int g = 0; g < TOPK_PER_THREAD / 4; ++g)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t e = base + (int64_t)(g * TOPK_THREADS + threadIdx.x) * 4 + r;
+        if (e < V) list_insert<KMAX>(lv, li, v[g * 4 + r], (int)e);
+      }
+    block_select<KMAX>(lv, li, k, ids + o, vals + o);
+  }
+}
+
+// Stage 2 for k <= 16: one wave per row.  The row's candidates are taken 64
+// at a time; the first batch is sorted descending, every later one ascending
+// and folded in by the lane-wise maximum (which leaves the 64 best of both
+// as a bitonic sequence) and one bitonic merge.
+__global__ __launch_bounds__(TOPK_THREADS) void topk_merge_wave_kernel(
+    const int* __restrict__ cids, const float* __restrict__ cvals, int64_t R, int ncand, int k,
+    int* __restrict__ ids, float* __restrict__ vals) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * (TOPK_THREADS / 64) + (threadIdx.x >> 6);
+  if (row >= R) return;
+  const int* ci = cids + row * ncand;
+  const float* cv = cvals + row * ncand;
+  int nid = lane < ncand ? ci[lane] : 0;
+  float nv = lane < ncand ? cv[lane] : 0.f;
+  uint64_t top = TOPK_PAD_KEY;
+  for (int c0 = 0; c0 < ncand; c0 += 64) {
+    uint64_t x = c0 + lane < ncand ? topk_key(nv, nid) : TOPK_PAD_KEY;
+    const int c1 = c0 + 64 + lane;  // next batch in flight during this one's sort
+    if (c1 < ncand) { nid = ci[c1]; nv = cv[c1]; }
+    if (c0 == 0) {
+      top = wave_sort(x, lane, true);
+    } else {
+      x = wave_sort(x, lane, false);
+      top = top > x ? top : x;
+      top = wave_bitonic_merge(top, lane, true);
+    }
+  }
+  if (lane < k) {
+    ids[row * k + lane] = key_index(top);
+    vals[row * k + lane] = key_value(top);
+  }
 }
 
 template <int KMAX>
@@ -216,8 +362,11 @@ void launch_topk(const float* logits, int64_t R, int64_t V, int k, int* ids, flo
 #define MEDUSA_TOPK(KM)                                                                       \
   do {                                                                                        \
     hipLaunchKernelGGL(topk_chunk_kernel<KM>, g1, blk, 0, st, logits, V, k, cid, cval, k);    \
-    if (S > 1)                                                                                \
-      hipLaunchKernelGGL(topk_merge_kernel<KM>, dim3((unsigned)R), blk, 0, st, cid, cval,     \
+    if (S > 1 && KM <= 16)                                                                    \
+      hipLaunchKernelGGL(topk_merge_wave_kernel, dim3((unsigned)((R + 3) / 4)), blk, 0, st,   \
+                         cid, cval, R, S * k, k, ids, vals);                                  \
+    else if (S > 1)                                                                           \
+      hipLaunchKernelGGL(topk_merge_kernel<64>, dim3((unsigned)R), blk, 0, st, cid, cval,     \
                          S * k, k, ids, vals);                                                \
   } while (0)
   if (k <= 4) MEDUSA_TOPK(4);

@@ -304,6 +304,40 @@ def test_topk_ties(lib, R, V, k):
         assert np.array_equal(host(vals[r]), ov)
 
 
+@pytest.mark.parametrize("kind,R,V,k", [
+    ("normal", 321, 32000, 10), ("normal", 7, 128000, 16), ("normal", 5, 32000, 4),
+    ("increasing", 3, 5000, 16), ("decreasing", 3, 4097, 16), ("signed_zeros", 4, 8192, 1),
+    ("constant", 2, 12000, 16), ("mixed", 6, 20000, 10), ("normal", 9, 4096, 13),
+    ("normal", 3, 33, 16), ("normal", 2, 4099, 5)])
+def test_topk_structured(lib, kind, R, V, k):
+    """Rows shaped to take every branch of the top-k: the threshold filter
+    (ordinary rows), its fallback (equal values at the threshold, chunks with
+    fewer than k elements), survivor counts near one per lane (monotone rows,
+    k = 16), signed zeros, and several merge batches (128000 wide)."""
+    case(f"topk {kind} R={R} V={V} k={k}")
+    rng = np.random.default_rng(R * 7 + V + k)
+    if kind == "normal":
+        x = rng.standard_normal((R, V)).astype(np.float32)
+    elif kind == "increasing":
+        x = np.tile(np.arange(V, dtype=np.float32), (R, 1)) + np.arange(R, dtype=np.float32)[:, None]
+    elif kind == "decreasing":
+        x = -np.tile(np.arange(V, dtype=np.float32), (R, 1))
+    elif kind == "signed_zeros":
+        x = np.where(rng.random((R, V)) < 0.5, -0.0, 0.0).astype(np.float32)
+        x[:, ::7] = -1.0
+    elif kind == "constant":
+        x = np.full((R, V), 3.0, np.float32)
+    else:  # ordinary rows with a run of equal maxima in some chunks only
+        x = rng.standard_normal((R, V)).astype(np.float32)
+        x[:, 4096:4096 + 300] = 9.0
+        x[1::2, 12000:12050] = 9.0
+    ids, vals = lib.medusa_topk(dev(x), k)
+    for r in range(R):
+        oi, ov = orc.topk(x[r], k)
+        assert host(ids[r]).tolist() == oi.tolist()
+        assert np.array_equal(host(vals[r]), ov)
+
+
 # -------------------------------------------------------------- build tree ---
 def test_build_tree(lib):
     case("build_tree")
