@@ -1044,7 +1044,11 @@ static bool launch_gemm_t(const void* X, int64_t xbs, int64_t M, int64_t Kd, con
       const T* Xt = reinterpret_cast<const T*>(X);
       const T* Wt = reinterpret_cast<const T*>(W);
       const T* Bt = reinterpret_cast<const T*>(bias);
-      if (plan.big == 1) {
+      // Both tilings run the contraction in the same order (64-deep stages,
+      // two 32-deep MFMA steps each), so their results are bit-identical and
+      // the choice may count the tiles of every batch element.
+      const int64_t t256 = ((Nw + 255) / 256) * ((M + 255) / 256) * batch;
+      if (plan.big == 1 || t256 >= 200) {
         const int tN = (int)((Nw + 255) / 256), tM = (int)((M + 255) / 256);
         hipLaunchKernelGGL((gemm_big_kernel<256, 256, 2, MEDUSA_GEMM_BIG_WM1, MEDUSA_GEMM_BIG_BK1, MEDUSA_GEMM_BIG_R1, EPI>),
                            dim3((unsigned)(tN * tM), (unsigned)batch),

@@ -123,16 +123,17 @@ __device__ __forceinline__ Key bitonic_pass(Key x, int lane, bool desc) {
   if constexpr (J > 1) return bitonic_pass<KK, J / 2>(x, lane, desc);
   else return x;
 }
-template <int KK, typename Key>
+template <int KK, int WIDTH, typename Key>
 __device__ __forceinline__ Key bitonic_sort_from(Key x, int lane, bool desc) {
   x = bitonic_pass<KK, KK / 2>(x, lane, desc);
-  if constexpr (KK < 64) return bitonic_sort_from<KK * 2>(x, lane, desc);
+  if constexpr (KK < WIDTH) return bitonic_sort_from<KK * 2, WIDTH>(x, lane, desc);
   else return x;
 }
-// The wave's 64 keys sorted: lane 0 holds the largest when desc.
-template <typename Key>
+// Each block of WIDTH lanes sorted; lanes 0..WIDTH-1 in the order asked
+// (lane 0 holds the largest when desc).  WIDTH = 64 sorts the whole wave.
+template <int WIDTH = 64, typename Key>
 __device__ __forceinline__ Key wave_sort(Key x, int lane, bool desc) {
-  return bitonic_sort_from<2>(x, lane, desc);
+  return bitonic_sort_from<2, WIDTH>(x, lane, desc);
 }
 // A bitonic sequence over the wave, sorted.
 template <typename Key>
@@ -145,15 +146,15 @@ __device__ __forceinline__ Key wave_bitonic_merge(Key x, int lane, bool desc) {
 // j = 4g + r; elements past V hold -inf and are never taken.
 template <int KMAX>
 __device__ __forceinline__ void wave_topk16(const float (&v)[TOPK_PER_THREAD], int64_t base,
-                                            int64_t V, int k, uint64_t* __restrict__ stage,
-                                            uint64_t* __restrict__ out) {
+                                            int64_t V, int k, float* __restrict__ stage_v,
+                                            int* __restrict__ stage_i, uint64_t* __restrict__ out) {
   const int lane = threadIdx.x & 63;
   float m = -INFINITY;
 #pragma unroll
   for (int j = 0; j < TOPK_PER_THREAD; ++j) m = fmaxf(m, v[j]);
   const float sorted = wave_sort(m, lane, true);
   const float T = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sorted), k - 1));
-  // survivors v >= T packed into stage[] by ballot; count C is wave-uniform
+  // survivors v >= T packed into the stage by ballot; count C is wave-uniform
   int C = 0;
 #pragma unroll
   for (int j = 0; j < TOPK_PER_THREAD; ++j) {
@@ -162,13 +163,16 @@ __device__ __forceinline__ void wave_topk16(const float (&v)[TOPK_PER_THREAD], i
     const uint64_t bal = __ballot(pred);
     const int pos = C + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
                                                        __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
-    if (pred && pos < 64) stage[pos] = topk_key(v[j], (int)e);
+    if (pred && pos < 64) { stage_v[pos] = v[j]; stage_i[pos] = (int)e; }
     C += __popcll(bal);
   }
   if (C >= k && C <= 64) {
     __builtin_amdgcn_wave_barrier();
-    uint64_t x = lane < C ? stage[lane] : TOPK_PAD_KEY;
-    x = wave_sort(x, lane, true);
+    uint64_t x = lane < C ? topk_key(stage_v[lane], stage_i[lane]) : TOPK_PAD_KEY;
+    // sort only as many lanes as hold survivors
+    if (C <= 16) x = wave_sort<16>(x, lane, true);
+    else if (C <= 32) x = wave_sort<32>(x, lane, true);
+    else x = wave_sort<64>(x, lane, true);
     if (lane < k) out[lane] = x;
     return;
   }
@@ -259,14 +263,20 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_chunk_kernel(const float* _
   const int64_t o = (row * gridDim.x + s) * (int64_t)out_stride;
   if constexpr (KMAX <= 16) {
     constexpr int NW = TOPK_THREADS / 64;
-    __shared__ uint64_t stage[NW][64];
+    __shared__ float stage_v[NW][64];
+    __shared__ int stage_i[NW][64];
     __shared__ uint64_t best[NW][16];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    wave_topk16<KMAX>(v, base, V, k, stage[wave], best[wave]);
+    wave_topk16<KMAX>(v, base, V, k, stage_v[wave], stage_i[wave], best[wave]);
     __syncthreads();
     if (wave != 0) return;
-    uint64_t key = (lane % 16) < k ? best[lane / 16][lane % 16] : TOPK_PAD_KEY;
-    key = wave_sort(key, lane, true);
+    // four descending runs of 16 (padded past k); odd runs read reversed, so
+    // lanes 0-31 and 32-63 are bitonic: two merge levels sort the wave
+    static_assert(NW == 4, "four runs of 16 fill the wave");
+    const int run = lane / 16, r = (run & 1) ? 15 - lane % 16 : lane % 16;
+    uint64_t key = r < k ? best[run][r] : TOPK_PAD_KEY;
+    key = bitonic_pass<32, 16>(key, lane, true);
+    key = bitonic_pass<64, 32>(key, lane, true);
     if (lane < k) {
       ids[o + lane] = key_index(key);
       vals[o + lane] = key_value(key);

@@ -264,6 +264,26 @@ def test_heads_vs_oracle(lib, dt, Mr, H, V, K, k):
             assert np.array_equal(host(vals[kk, m]), ov)
 
 
+def test_heads_bits_independent_of_batch(lib):
+    """Seven heads over 1024 rows take the 256-wide large-row tiles (their
+    tiles together fill the chip) while one head alone takes the 128-wide
+    ones; the contraction order is the same, so every head's logits are the
+    same bits either way, and they match the oracle on sampled rows."""
+    Mr, H, V, K = 1024, 2048, 2048, 7
+    case(f"heads batch-independent bits M={Mr} H={H} V={V} K={K}")
+    d = synth.heads_inputs(11, Mr, H, V, K, w1_std=0.02, w2_std=0.02, bf16=True)
+    bf = torch.bfloat16
+    X, W1, b1, W2 = (dev(d[n], bf) for n in ("X", "W1", "b1", "W2"))
+    logits, _, _ = lib.medusa_heads(X, W1, b1, W2, topk=4)
+    rows = np.array([0, 1, 255, 256, 511, 700, 1023])
+    ref = orc.head_logits(d["X"][rows], d["W1"], d["b1"], d["W2"])
+    assert_close(host(logits)[:, rows], ref, TOL[bf], "head logits")
+    for kk in (0, 3, 6):
+        one, _, _ = lib.medusa_heads(X, W1[kk:kk + 1].contiguous(), b1[kk:kk + 1].contiguous(),
+                                     W2[kk:kk + 1].contiguous(), topk=4)
+        assert torch.equal(one[0], logits[kk]), kk
+
+
 @pytest.mark.parametrize("Mr,H,V,K,k", [(17, 256, 8192, 2, 4), (32, 512, 12288, 3, 10),
                                         (64, 256, 8192, 5, 16), (100, 256, 16384, 2, 1),
                                         (255, 512, 8192, 2, 10), (64, 256, 8192, 2, 17),
