@@ -383,6 +383,8 @@ def main():
     ap.add_argument("--skip-plain", action="store_true")
     ap.add_argument("--skip-extra", action="store_true",
                     help="skip the heads (64 and 1024 rows) and batched-attention measurements")
+    ap.add_argument("--heads-only", action="store_true",
+                    help="run only the five heads + top-10 at 64 and 1024 rows (for kernel traces)")
     ap.add_argument("--kernels-only", action="store_true",
                     help="run only the dominant projection kernel (32 launches over 7B-shaped "
                          "gate/up weights), the tree-attention launches and a 1 GiB copy, "
@@ -405,6 +407,9 @@ def main():
     log = lambda *a: print(*a, file=sys.stderr, flush=True)
     if args.kernels_only:
         kernels_only(torch, M, synth, log)
+        return
+    if args.heads_only:
+        print(json.dumps({"heads_c3": heads_c3(torch, M, 64), "heads_c3b": heads_c3(torch, M, 1024)}))
         return
     log("[bench] drawing the random 7B-shaped decoder on the GPU")
     src = synth.device_llama(seed=4)
