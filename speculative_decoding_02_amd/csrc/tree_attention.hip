@@ -817,12 +817,13 @@ __global__ __launch_bounds__(256 * KQ) void tree_attention_stream_kernel(AttnArg
 // output, splits in index order.  One
 // workgroup per (group of 8 nodes, head, sequence); 32 lanes per node (4
 // head dims each), so the grid covers the chip even at batch 1.  Up to
-// CMB_BATCH splits are loaded in one go together with the sequence length
-// (splits past the sequence's last one are read but weighted out), so a
-// decode-time merge costs one round trip.
+// CMB_BATCH splits (the smallest of 4, 8, 16 that covers the plan's split
+// count) are loaded in one go together with the sequence length (splits past
+// the sequence's last one are read but weighted out), so a decode-time merge
+// costs one round trip.  The batch size changes no arithmetic: the splits
+// are added in index order either way.
 constexpr int CMB_NODES = 8;
-constexpr int CMB_BATCH = 16;
-template <typename T, int D>
+template <typename T, int D, int CMB_BATCH>
 __global__ __launch_bounds__(ATT_THREADS) void tree_attention_combine_kernel(AttnArgs a, int S) {
   const int h = blockIdx.y, b = blockIdx.z;
   const int N = a.N;
@@ -991,12 +992,21 @@ extern "C" int32_t medusa_tree_attention(const void* Q, const void* Kt, const vo
   hipStream_t st = (hipStream_t)stream;
   const dim3 blk(medusa::ATT_THREADS);
   constexpr int PF = MEDUSA_ATTN_PF;
+  // split batch of the merge: 4, 8 or 16 (at 7 splits a batch of 8 measured
+  // faster than 16: fewer registers and no clamped re-reads)
+#define MEDUSA_ATT_COMBINE(T, DD)                                                            \
+  do {                                                                                       \
+    if (p.splits <= 4)                                                                       \
+      hipLaunchKernelGGL((medusa::tree_attention_combine_kernel<T, DD, 4>), cgrid, blk, 0, st, a, p.splits); \
+    else if (p.splits <= 8)                                                                  \
+      hipLaunchKernelGGL((medusa::tree_attention_combine_kernel<T, DD, 8>), cgrid, blk, 0, st, a, p.splits); \
+    else                                                                                     \
+      hipLaunchKernelGGL((medusa::tree_attention_combine_kernel<T, DD, 16>), cgrid, blk, 0, st, a, p.splits); \
+  } while (0)
 #define MEDUSA_ATT_LAUNCH(KERNEL, T, DD)                                                     \
   do {                                                                                       \
     hipLaunchKernelGGL((KERNEL), grid, blk, 0, st, a);                                       \
-    if (p.splits > 1)                                                                        \
-      hipLaunchKernelGGL((medusa::tree_attention_combine_kernel<T, DD>), cgrid, blk, 0, st,  \
-                         a, p.splits);                                                       \
+    if (p.splits > 1) MEDUSA_ATT_COMBINE(T, DD);                                             \
   } while (0)
   constexpr int RD = MEDUSA_ATTN_DMA_R;
   if (dt == MEDUSA_BF16) {
@@ -1008,9 +1018,7 @@ extern "C" int32_t medusa_tree_attention(const void* Q, const void* Kt, const vo
 #define MEDUSA_ATT_LAUNCH_S(KERNEL, DD)                                                      \
   do {                                                                                       \
     hipLaunchKernelGGL((KERNEL), grid, blk8, 0, st, a);                                      \
-    if (p.splits > 1)                                                                        \
-      hipLaunchKernelGGL((medusa::tree_attention_combine_kernel<medusa::bf16_t, DD>), cgrid, blk, 0, st, \
-                         a, p.splits);                                                       \
+    if (p.splits > 1) MEDUSA_ATT_COMBINE(medusa::bf16_t, DD);                                \
   } while (0)
     if (D == 128 && p2) MEDUSA_ATT_LAUNCH_S((medusa::tree_attention_stream_kernel<128, RD, KQ, true>), 128);
     else if (D == 128) MEDUSA_ATT_LAUNCH_S((medusa::tree_attention_stream_kernel<128, RD, KQ, false>), 128);
@@ -1022,5 +1030,6 @@ extern "C" int32_t medusa_tree_attention(const void* Q, const void* Kt, const vo
     else MEDUSA_ATT_LAUNCH((medusa::tree_attention_kernel<float, 64, PF>), float, 64);
   }
 #undef MEDUSA_ATT_LAUNCH
+#undef MEDUSA_ATT_COMBINE
   return check_launch("medusa_tree_attention");
 }
