@@ -851,7 +851,7 @@ __global__ __launch_bounds__(256) void gemm_split_reduce_kernel(const float* __r
 // x[m] += sum of the partials in split order (the same sums and the same
 // final add as gemm_split_reduce_kernel's residual epilogue), then
 // out[m] = RMSNorm(x[m]) * gain with the plain RMSNorm's own reduction.
-template <typename T>
+template <typename T, int QB>
 __global__ __launch_bounds__(256) void split_reduce_rmsnorm_kernel(const float* __restrict__ part,
                                                                    int ksplit, int M, int N,
                                                                    float* __restrict__ x,
@@ -866,8 +866,8 @@ __global__ __launch_bounds__(256) void split_reduce_rmsnorm_kernel(const float* 
   // carry unused copies), so a batch of splits costs one memory round trip;
   // the adds keep split order.
   // (the first batch of up to QB splits is loaded together with the
-  // residual row and the gain: one round trip for splits <= QB)
-  constexpr int QB = 4;
+  // residual row and the gain: one round trip for splits <= QB; the launch
+  // takes QB = 2 for two splits, else 4, which changes no sum)
   f32x4 g[RMS_V4], v[RMS_V4], acc[RMS_V4];
   int ec[RMS_V4];
   rms_row_gain<T>(gain, N, g);
@@ -1028,6 +1028,17 @@ struct SplitNorm {
   float eps;
   void* out;
 };
+template <typename T>
+static void launch_split_reduce_rmsnorm(const float* part, int ksplit, int64_t M, int64_t Nw, void* Y,
+                                        const SplitNorm* norm, hipStream_t st) {
+  auto go = [&](auto qb) {
+    hipLaunchKernelGGL((split_reduce_rmsnorm_kernel<T, decltype(qb)::value>), dim3((unsigned)M), dim3(256), 0, st,
+                       part, ksplit, (int)M, (int)Nw, reinterpret_cast<float*>(Y),
+                       reinterpret_cast<const T*>(norm->gain), norm->eps, reinterpret_cast<T*>(norm->out));
+  };
+  if (ksplit <= 2) go(std::integral_constant<int, 2>{});
+  else go(std::integral_constant<int, 4>{});
+}
 // Launches the projection; returns whether `norm` (residual epilogue only)
 // was applied, fused into the reduction of a split contraction.
 template <typename T, int EPI>
@@ -1075,9 +1086,7 @@ static bool launch_gemm_t(const void* X, int64_t xbs, int64_t M, int64_t Kd, con
                            (int)M, (int)Kd, Wt, (int)Nw, Bt, aux, Y, y_f32, plan.xb_G, plan.MT, plan.xb_unit, part, RopeArgs{});
       if (plan.xb_S > 1) {
         if (EPI == MEDUSA_EPI_RES_ADD_F32 && norm) {
-          hipLaunchKernelGGL(split_reduce_rmsnorm_kernel<T>, dim3((unsigned)M), dim3(256), 0, st, part,
-                             plan.xb_S, (int)M, (int)Nw, reinterpret_cast<float*>(Y),
-                             reinterpret_cast<const T*>(norm->gain), norm->eps, reinterpret_cast<T*>(norm->out));
+          launch_split_reduce_rmsnorm<T>(part, plan.xb_S, M, Nw, Y, norm, st);
           return true;
         }
         const int64_t cols = EPI == MEDUSA_EPI_SWIGLU ? Nw / 2 : Nw;
@@ -1099,10 +1108,7 @@ static bool launch_gemm_t(const void* X, int64_t xbs, int64_t M, int64_t Kd, con
                          reinterpret_cast<const T*>(W), (int)Nw, reinterpret_cast<const T*>(bias),
                          aux, Y, y_f32, plan.ksplit, reinterpret_cast<float*>(ws));
       if (plan.ksplit > 1 && EPI == MEDUSA_EPI_RES_ADD_F32 && norm) {
-        hipLaunchKernelGGL(split_reduce_rmsnorm_kernel<T>, dim3((unsigned)M), dim3(256), 0, st,
-                           reinterpret_cast<const float*>(ws), plan.ksplit, (int)M, (int)Nw,
-                           reinterpret_cast<float*>(Y), reinterpret_cast<const T*>(norm->gain), norm->eps,
-                           reinterpret_cast<T*>(norm->out));
+        launch_split_reduce_rmsnorm<T>(reinterpret_cast<const float*>(ws), plan.ksplit, M, Nw, Y, norm, st);
         normed = true;
       } else if (plan.ksplit > 1) {
         const int64_t cols = EPI == MEDUSA_EPI_SWIGLU ? Nw / 2 : Nw;
