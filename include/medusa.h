@@ -382,8 +382,10 @@ int32_t medusa_gather_rows(const void* h, int32_t B, int32_t N, int64_t H, const
  *     a generation.
  *   ws: medusa_decode_tail_ws(B, N) bytes.  Its last part holds per-sequence
  *     counters that must be zero before the first call (zero-fill the
- *     workspace once); every call leaves them zero.  Calls sharing a
- *     workspace must be ordered by their stream.
+ *     workspace once); every call leaves them zero.  The counters sit at an
+ *     offset that depends on B only (after the statistics of a 64-node
+ *     tree), so one workspace may serve calls with the same B and any N.
+ *     Calls sharing a workspace must be ordered by their stream.
  * ---------------------------------------------------------------------- */
 size_t medusa_decode_tail_ws(int32_t B, int32_t N);
 int32_t medusa_decode_tail(const float* logits, int64_t V, const int32_t* tokens,

@@ -605,7 +605,8 @@ def medusa_generate(model, prompt, n_new, parent, rank, mode="greedy", temperatu
         elif mode == "sample":
             res = accept_sample(lf, tree["tokens"], parent, n_heads, temperature, seed, step, b=b)
         else:
-            res = accept_typical(lf, tree["tokens"], parent, n_heads, temperature, epsilon, delta)
+            res = accept_typical(lf, tree["tokens"], parent, n_heads, temperature, epsilon, delta,
+                                 return_margins=True)
         a, path = res["accept_len"], res["path"]
         out.extend(int(tree["tokens"][path[d]]) for d in range(a + 1))
         for li in range(model.n_layers):

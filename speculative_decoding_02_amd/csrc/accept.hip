@@ -514,10 +514,15 @@ extern "C" int32_t medusa_accept_sample(const float* logits, int64_t V, const in
   return check_launch("medusa_accept_sample");
 }
 
+// The arrival counters sit after the statistics of the largest tree (N = 64),
+// at an offset that depends on B only, so one workspace serves calls of any
+// N (the counters of one call are never another call's statistics).
+static size_t tail_counter_offset(int32_t B) { return medusa_accept_ws(B, MEDUSA_MAX_NODES); }
+
 extern "C" size_t medusa_decode_tail_ws(int32_t B, int32_t N) {
   if (B < 0 || N < 0) return 0;
   // the accept statistics or draws, then one arrival counter per sequence
-  return medusa_accept_ws(B, N) + medusa_host::align_up((size_t)B * sizeof(unsigned), 256);
+  return tail_counter_offset(B) + medusa_host::align_up((size_t)B * sizeof(unsigned), 256);
 }
 
 extern "C" int32_t medusa_decode_tail(
@@ -593,7 +598,7 @@ extern "C" int32_t medusa_decode_tail(
   t.next_token = next_token;
   t.log = log;
   t.cap = cap;
-  t.arrive = (unsigned*)((char*)ws + medusa_accept_ws(B, N));
+  t.arrive = (unsigned*)((char*)ws + tail_counter_offset(B));
   if (mode == 2) {
     t.draws = (medusa::Draw*)ws;
     t.S = medusa::row_splits(B, N, V);

@@ -50,11 +50,29 @@ struct AttnCfg {
   static_assert(KCHUNKS % ATT_THREADS == 0, "K tile chunks");
 };
 
-// Element type of the split partials: fp16 for bf16 attention (the partial
-// is the split's normalised output, |O_s| <= max |v|, so fp16's 2^-11
-// relative rounding sits far inside bf16's 2^-8), fp32 for fp32 attention.
+// Element type of the split partials: fp16 for bf16 attention, fp32 for fp32
+// attention.  A split's partial is its normalised output, a convex
+// combination of V rows.  In fp16 it is stored block-scaled: each (split,
+// node) row is multiplied by 2^-s, with s chosen from the row's largest
+// magnitude so that it lands in [2^14, 2^15), and s is kept with the row's
+// (max, sum).  fp16's 11-bit significand then covers the row's large
+// entries (relative rounding 2^-11, far inside bf16's 2^-8) whatever the
+// magnitude of V, which bf16 allows up to 3.4e38, while fp16 alone would
+// overflow above 65504.  The scaling by a power of two is exact.
 template <typename T> struct PartT { using type = float; };
 template <> struct PartT<bf16_t> { using type = _Float16; };
+
+// (running max in log2 units, sum, scale exponent s of the stored row, pad)
+struct PartStat {
+  float m, l;
+  int s, pad;
+};
+// the exponent s with mx * 2^-s in [2^14, 2^15) (0 for an all-zero row)
+__device__ __forceinline__ int part_scale_exp(float mx) {
+  int e = 0;
+  (void)frexpf(mx, &e);  // mx = f * 2^e, f in [1/2, 1)
+  return mx > 0.f ? e - 15 : 0;
+}
 
 // component i (compile-time after unrolling) of a 16-byte register vector
 __device__ __forceinline__ uint32_t u4c(u32x4 v, int i) { return v[i]; }
@@ -84,7 +102,7 @@ struct AttnArgs {
   const int* ctx;
   const uint64_t* mask;
   void* O;
-  float2* ml;        // [B*Hq*S*N]  (running max in log2 units, sum)
+  PartStat* ml;      // [B*Hq*S*N]
   void* opart;       // [B*Hq*S*N*D] of PartT<T>: a split's output divided by its own sum
   int max_pages, P, B, N, Hq, Hkv, chunk;  // chunk = keys per split (multiple of 64)
   int max_ctx;
@@ -404,7 +422,7 @@ __global__ __launch_bounds__(ATT_THREADS) void tree_attention_kernel(AttnArgs a)
         *reinterpret_cast<f32x4*>(op + db * 16 + lg * 4) = oacc[db] * inv;
       }
     }
-    if (lg == 0) a.ml[(bh * S + s) * N + node] = make_float2(mrun, ltot);
+    if (lg == 0) a.ml[(bh * S + s) * N + node] = PartStat{mrun, ltot, 0, 0};
   }
 }
 
@@ -798,17 +816,25 @@ __global__ __launch_bounds__(256 * KQ) void tree_attention_stream_kernel(AttnArg
     return;
   }
   const int64_t bh = (int64_t)b * a.Hq + h;
+  // the row's block exponent: its largest magnitude over the four lanes that
+  // hold node `node` (every lane of a wave takes part in the row swaps)
+  const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+  float amax = 0.f;
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) amax = fmaxf(amax, fabsf(oacc[db][r] * inv));
+  const int sexp = part_scale_exp(rows4_max(amax));
   if (node_ok) {
     _Float16* op = reinterpret_cast<_Float16*>(a.opart) + ((bh * S + s) * N + node) * D;
-    const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
     typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
-      h4 v = {(_Float16)(oacc[db][0] * inv), (_Float16)(oacc[db][1] * inv), (_Float16)(oacc[db][2] * inv),
-              (_Float16)(oacc[db][3] * inv)};
+      h4 v = {(_Float16)ldexpf(oacc[db][0] * inv, -sexp), (_Float16)ldexpf(oacc[db][1] * inv, -sexp),
+              (_Float16)ldexpf(oacc[db][2] * inv, -sexp), (_Float16)ldexpf(oacc[db][3] * inv, -sexp)};
       *reinterpret_cast<h4*>(op + db * 16 + lg * 4) = v;
     }
-    if (lg == 0) a.ml[(bh * S + s) * N + node] = make_float2(mrun, ltot);
+    if (lg == 0) a.ml[(bh * S + s) * N + node] = PartStat{mrun, ltot, sexp, 0};
   }
 }
 
@@ -836,7 +862,7 @@ __global__ __launch_bounds__(ATT_THREADS) void tree_attention_combine_kernel(Att
   float M = -INFINITY, L = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   for (int q0 = 0; q0 < S; q0 += CMB_BATCH) {
-    float2 ml[CMB_BATCH];
+    PartStat ml[CMB_BATCH];
     f32x4 op[CMB_BATCH];
 #pragma unroll
     for (int j = 0; j < CMB_BATCH; ++j) {
@@ -847,7 +873,9 @@ __global__ __launch_bounds__(ATT_THREADS) void tree_attention_combine_kernel(Att
       if constexpr (sizeof(PT) == 2) {
         typedef _Float16 h4 __attribute__((ext_vector_type(4)));
         const h4 v = *reinterpret_cast<const h4*>(src);
-        op[j] = f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+        const int sx = ml[j].s;  // undo the row's block scaling (exact)
+        op[j] = f32x4{ldexpf((float)v[0], sx), ldexpf((float)v[1], sx), ldexpf((float)v[2], sx),
+                      ldexpf((float)v[3], sx)};
       } else {
         op[j] = *reinterpret_cast<const f32x4*>(src);
       }
@@ -857,14 +885,14 @@ __global__ __launch_bounds__(ATT_THREADS) void tree_attention_combine_kernel(Att
     float Mb = M;
 #pragma unroll
     for (int j = 0; j < CMB_BATCH; ++j)
-      if (q0 + j < nsplit) Mb = fmaxf(Mb, ml[j].x);
+      if (q0 + j < nsplit) Mb = fmaxf(Mb, ml[j].m);
     const float r = (M == -INFINITY) ? 0.f : exp2f(M - Mb);
     L *= r;
     acc *= r;
 #pragma unroll
     for (int j = 0; j < CMB_BATCH; ++j) {
-      if (q0 + j < nsplit && ml[j].x != -INFINITY) {
-        const float wl = exp2f(ml[j].x - Mb) * ml[j].y;
+      if (q0 + j < nsplit && ml[j].m != -INFINITY) {
+        const float wl = exp2f(ml[j].m - Mb) * ml[j].l;
         L += wl;
         acc += wl * op[j];
       }
@@ -921,7 +949,7 @@ WsLayout ws_layout(int B, int Hq, int N, int D, int S, size_t part_elem) {
   using medusa_host::align_up;
   WsLayout w;
   w.ml = 0;
-  w.opart = w.ml + align_up((size_t)B * Hq * S * N * sizeof(float2), 256);
+  w.opart = w.ml + align_up((size_t)B * Hq * S * N * sizeof(medusa::PartStat), 256);
   w.total = w.opart + align_up((size_t)B * Hq * S * N * D * part_elem, 256);
   return w;
 }
@@ -980,7 +1008,7 @@ extern "C" int32_t medusa_tree_attention(const void* Q, const void* Kt, const vo
   medusa::AttnArgs a;
   a.Q = Q; a.Kt = Kt; a.Vt = Vt; a.Kc = Kc; a.Vc = Vc;
   a.page_table = page_table; a.ctx = ctx; a.mask = mask; a.O = O;
-  a.ml = (float2*)((char*)ws + L.ml);
+  a.ml = (medusa::PartStat*)((char*)ws + L.ml);
   a.opart = (char*)ws + L.opart;
   a.max_pages = max_pages; a.P = P; a.B = B; a.N = N; a.Hq = Hq; a.Hkv = Hkv;
   a.lp = (P & (P - 1)) == 0 ? __builtin_ctz((unsigned)P) : -1;

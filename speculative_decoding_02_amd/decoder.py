@@ -35,6 +35,46 @@ def interleave_gate_up(wg: np.ndarray, wu: np.ndarray) -> np.ndarray:
     return np.stack([wg.reshape(F // 16, 16, H), wu.reshape(F // 16, 16, H)], axis=1).reshape(2 * F, H)
 
 
+def max_step_context(plen: int, n_new: int, K: int, B: int) -> int:
+    """The largest context length a decode step of ``generate`` can start
+    from, for prompts of ``plen`` tokens and ``n_new`` new ones per sequence.
+
+    Every step emits 1..K+1 tokens per sequence.  One sequence: a step starts
+    only while fewer than n_new tokens are out, and the batches of steps run
+    back to back before a read never start one past that (a batch of r =
+    ceil(remaining / (K+1)) steps starts its last step after at most
+    (r-1)(K+1) < remaining more tokens), so the bound is plen + n_new - 1.
+    B sequences: the loop runs until the slowest one is done, at most n_new
+    steps, while the fastest may emit K+1 tokens in each, so the bound is
+    plen + (n_new - 1)(K+1)."""
+    if n_new <= 0:
+        return plen
+    return plen + (n_new - 1) * (1 if B == 1 else K + 1)
+
+
+def plan_cache(capacity: int, N: int, page_size: int):
+    """Pages per sequence, slots per sequence and the attention calls'
+    max_ctx for a requested ``capacity`` of cached tokens and N-node trees.
+
+    Every attention call (a prefill chunk of up to 64 rows, or a tree of N)
+    needs ctx + rows <= slots, so max_ctx = slots - 64; the slots cover the
+    requested capacity plus one tree and one chunk."""
+    max_pages = (capacity + N + 64 + page_size - 1) // page_size
+    slots = max_pages * page_size
+    return max_pages, slots, slots - 64
+
+
+def check_generation(plen: int, n_new: int, K: int, B: int, max_ctx: int) -> None:
+    """Raise ValueError unless every attention call of a generation of n_new
+    tokens from prompts of plen starts at a context <= max_ctx (a longer one
+    would be clamped by the kernels, dropping keys): the prefill's chunks
+    start below plen, the decode steps at most at max_step_context."""
+    worst = max(max_step_context(plen, n_new, K, B), plen)
+    if worst > max_ctx:
+        raise ValueError(f"a step may start at context {worst} > max_ctx {max_ctx}: "
+                         "raise the capacity")
+
+
 class DeviceModel:
     """Device copy of a Llama-style decoder with Medusa heads.
 
@@ -136,8 +176,7 @@ class MedusaDecoder:
         self.mode = 0 if mode == "greedy" else 1
         self.T, self.eps, self.delta = temperature, epsilon, delta
         self.P = page_size
-        self.max_pages = (capacity + self.N + 64 + page_size - 1) // page_size
-        self.capacity = self.max_pages * page_size
+        self.max_pages, self.capacity, self.max_ctx = plan_cache(capacity, self.N, page_size)
         i32 = dict(dtype=torch.int32, device=dev)
         self.parent = torch.tensor(np.tile(parent, (B, 1)), **i32)
         self.rank = torch.tensor(np.tile(rank, (B, 1)), **i32)
@@ -152,7 +191,6 @@ class MedusaDecoder:
         Kh = max(self.K, 1)
         self.topk_ids = torch.zeros((Kh, B, self.width), **i32)
         self.topk_vals = torch.zeros((Kh, B, self.width), dtype=torch.float32, device=dev)
-        self.max_ctx = self.capacity - 64          # every call has ctx + n <= capacity
         self.attn_ws = M._ws(max(M.tree_attention_ws_bytes(B, n, model.n_heads, model.n_kv_heads,
                                                            model.head_dim, self.max_ctx, page_size)
                                  for n in range(1, 65)), dev)
@@ -343,11 +381,7 @@ class MedusaDecoder:
         (a list per sequence when B > 1)."""
         B = self.B
         plen = np.asarray(prompt).reshape(B, -1).shape[1]
-        # every step emits 1..K+1 tokens per sequence and runs until the
-        # slowest sequence is done: the fastest may emit (K+1) per step
-        worst = plen + (n_new if B == 1 else n_new * (self.K + 1)) + self.K + self.N
-        if worst > self.capacity:
-            raise ValueError(f"capacity {self.capacity} < {worst} slots that {n_new} tokens may need")
+        check_generation(plen, n_new, self.K, B, self.max_ctx)
         self.prefill(prompt)
         if graph and getattr(self, "graph", None) is None:
             self.capture()

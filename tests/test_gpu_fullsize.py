@@ -3,10 +3,10 @@ bench.py times (same shapes, so the same launch plans), against the oracle on
 outputs it can compute one at a time:
 
 * tree attention at the 7B layer (1 x 64 nodes, 32 heads x 128, 2048 cached
-  tokens, 16-token pages): three whole heads, plus the appended tree K/V;
+  tokens, 16-token pages): every head, plus the appended tree K/V;
 * batched tree attention, one 13B-shaped layer (16 sequences of
-  U{256..4096} cached tokens, 40 heads, permuted pages): six
-  (sequence, head) pairs, including the longest and the shortest sequence;
+  U{256..4096} cached tokens, 40 heads, permuted pages): every head of the
+  longest and the shortest sequence and three heads of every other one;
 * the five heads + top-10 at 64 rows x 4096 -> 32000: sampled logits of
   three (head, row) pairs and every top-k list against the oracle's top-k of
   the GPU's own logits;
@@ -63,8 +63,11 @@ def test_c2_tree_attention_7b_layer(lib):
                                     dev(d["page_table"]), dev(d["ctx"]), ctx, dev(masks),
                                     float(d["scale"]), ws=ws)
     o = host(out)[0]
-    for h in (0, 17, 31):
-        assert_close(o[:, h], _one_head(d, 0, h, ctx, masks), TOL[bf], f"head {h}")
+    ref = orc.tree_attention(d["Q"][0], orc.cache_rows(d["Kc"], d["page_table"][0], ctx, 16),
+                             orc.cache_rows(d["Vc"], d["page_table"][0], ctx, 16), d["Kt"][0],
+                             d["Vt"][0], masks[0], d["scale"])
+    for h in range(H):
+        assert_close(o[:, h], ref[:, h], TOL[bf], f"head {h}")
     kt = orc.cache_rows(host(Kc), d["page_table"][0], ctx + N, 16)
     vt = orc.cache_rows(host(Vc), d["page_table"][0], ctx + N, 16)
     np.testing.assert_array_equal(kt[ctx:], d["Kt"][0])
@@ -87,7 +90,11 @@ def test_c5_batched_attention_13b_layer(lib):
                                     max_ctx, dev(masks), float(d["scale"]))
     o = host(out)
     lo, hi = int(np.argmin(lens)), int(np.argmax(lens))
-    for b, h in ((lo, 0), (hi, 39), (hi, 7), (3, 21), (9, 33), (lo, 12)):
+    # every head of the longest and the shortest sequence, three heads of
+    # every other sequence (a different three each)
+    pairs = [(b, h) for b in (hi, lo) for h in range(H)]
+    pairs += [(b, (7 * b + 13 * j) % H) for b in range(B) if b not in (lo, hi) for j in range(3)]
+    for b, h in pairs:
         assert_close(o[b][:, h], _one_head(d, b, h, int(lens[b]), masks), TOL[bf],
                      f"sequence {b} (ctx {lens[b]}) head {h}")
 
