@@ -208,6 +208,29 @@ int32_t medusa_tree_attention(const void* Q, const void* Kt, const void* Vt, voi
                               void* stream);
 
 /* ------------------------------------------------------------------------
+ * medusa_tree_attention_noalloc: medusa_tree_attention for callers that
+ * cannot allocate (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments and results, minus the
+ * workspace: the split partials live in a fixed device array inside the
+ * library, MEDUSA_ATTN_NOALLOC_MAX_BYTES bytes on each GPU it runs on, held
+ * until the process ends.  The call allocates and frees nothing.
+ *   Sizes whose medusa_tree_attention_ws(...) exceeds the array return
+ *   MEDUSA_ERR_UNSUPPORTED (nothing is enqueued).  The first call on a
+ *   device looks up the array's device address (hipGetSymbolAddress); a
+ *   failure there returns MEDUSA_ERR_HIP.
+ *   Every call on one GPU shares that GPU's array (it keeps the last call's
+ *   partials; no call needs it cleared): calls that overlap in time on one
+ *   GPU, from any stream or thread, race and give undefined results.
+ * ---------------------------------------------------------------------- */
+#define MEDUSA_ATTN_NOALLOC_MAX_BYTES ((size_t)32 << 20)
+int32_t medusa_tree_attention_noalloc(const void* Q, const void* Kt, const void* Vt, void* Kc,
+                                      void* Vc, const int32_t* page_table, int32_t max_pages,
+                                      int32_t P, const int32_t* ctx, int32_t max_ctx,
+                                      const uint64_t* mask, int32_t B, int32_t N, int32_t Hq,
+                                      int32_t Hkv, int32_t D, float scale, int32_t dt, void* O,
+                                      void* stream);
+
+/* ------------------------------------------------------------------------
  * medusa_accept: longest accepted branch per sequence ("Medusa Heads", tree
  * section: the longest branch the model accepts is kept; greedy keeps a
  * candidate equal to the model's top choice; typical acceptance keeps a

@@ -28,6 +28,7 @@
 //     (unrolled, so every stage index is static), keeping a workgroup's whole
 //     key range in flight for the short ranges of decode-time splits.
 #include <algorithm>
+#include <mutex>
 
 #include "common.h"
 
@@ -966,44 +967,121 @@ extern "C" size_t medusa_tree_attention_ws(int32_t B, int32_t N, int32_t Hq, int
   return ws_layout(B, Hq, N, D, std::max(p1.splits, p2.splits), sizeof(float)).total;
 }
 
+static int32_t tree_attention_impl(const char* fn, const void* Q, const void* Kt, const void* Vt,
+                                   void* Kc, void* Vc, const int32_t* page_table, int32_t max_pages,
+                                   int32_t P, const int32_t* ctx, int32_t max_ctx,
+                                   const uint64_t* mask, int32_t B, int32_t N, int32_t Hq,
+                                   int32_t Hkv, int32_t D, float scale, int32_t dt, void* O,
+                                   void* ws, size_t ws_bytes, void* stream);
+
 extern "C" int32_t medusa_tree_attention(const void* Q, const void* Kt, const void* Vt, void* Kc,
                                          void* Vc, const int32_t* page_table, int32_t max_pages,
                                          int32_t P, const int32_t* ctx, int32_t max_ctx,
                                          const uint64_t* mask, int32_t B, int32_t N, int32_t Hq,
                                          int32_t Hkv, int32_t D, float scale, int32_t dt,
                                          void* O, void* ws, size_t ws_bytes, void* stream) {
+  return tree_attention_impl("medusa_tree_attention", Q, Kt, Vt, Kc, Vc, page_table, max_pages, P,
+                             ctx, max_ctx, mask, B, N, Hq, Hkv, D, scale, dt, O, ws, ws_bytes,
+                             stream);
+}
+
+// ---------------------------------------------------------------------------
+// The variant that allocates nothing, for callers that cannot allocate (code
+// under graph capture, tight serving loops): the split partials live in a
+// file-scope device array of fixed size, one copy per GPU, held until the
+// process ends.  Host code never passes the array's name to a kernel (on the
+// host it is a stand-in, not a device address): the device address comes
+// from hipGetSymbolAddress, taken once per device with that device current.
+// ---------------------------------------------------------------------------
+static constexpr size_t kAttnScratchBytes = MEDUSA_ATTN_NOALLOC_MAX_BYTES;
+static __device__ __align__(256) unsigned char scratch[kAttnScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch` on each device, or null
+
+// the current device's address of `scratch` (taken on first use), or null
+// with the error recorded
+void* scratch_ptr(const char* fn) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    medusa_host::fail(MEDUSA_ERR_HIP, "%s: no current device (or device id %d >= %d)", fn, dev,
+                      kMaxDevices);
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr) {
+      medusa_host::fail(MEDUSA_ERR_HIP, "%s: hipGetSymbolAddress(scratch) on device %d: %s", fn,
+                        dev, hipGetErrorString(e));
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
+}  // namespace
+
+extern "C" int32_t medusa_tree_attention_noalloc(const void* Q, const void* Kt, const void* Vt,
+                                                 void* Kc, void* Vc, const int32_t* page_table,
+                                                 int32_t max_pages, int32_t P, const int32_t* ctx,
+                                                 int32_t max_ctx, const uint64_t* mask, int32_t B,
+                                                 int32_t N, int32_t Hq, int32_t Hkv, int32_t D,
+                                                 float scale, int32_t dt, void* O, void* stream) {
+  using namespace medusa_host;
+  const char* fn = "medusa_tree_attention_noalloc";
+  const size_t need = medusa_tree_attention_ws(B, N, Hq, Hkv, D, max_ctx, P);
+  MEDUSA_REQUIRE(need <= kAttnScratchBytes, MEDUSA_ERR_UNSUPPORTED,
+                 "%s: B=%d N=%d Hq=%d D=%d max_ctx=%d need %zu bytes of split partials, more "
+                 "than the fixed %zu (use medusa_tree_attention with a workspace)",
+                 fn, B, N, Hq, D, max_ctx, need, kAttnScratchBytes);
+  void* ws = scratch_ptr(fn);
+  if (ws == nullptr) return MEDUSA_ERR_HIP;
+  return tree_attention_impl(fn, Q, Kt, Vt, Kc, Vc, page_table, max_pages, P, ctx, max_ctx, mask,
+                             B, N, Hq, Hkv, D, scale, dt, O, ws, kAttnScratchBytes, stream);
+}
+
+static int32_t tree_attention_impl(const char* fn, const void* Q, const void* Kt, const void* Vt,
+                                   void* Kc, void* Vc, const int32_t* page_table, int32_t max_pages,
+                                   int32_t P, const int32_t* ctx, int32_t max_ctx,
+                                   const uint64_t* mask, int32_t B, int32_t N, int32_t Hq,
+                                   int32_t Hkv, int32_t D, float scale, int32_t dt, void* O,
+                                   void* ws, size_t ws_bytes, void* stream) {
   using namespace medusa_host;
   MEDUSA_REQUIRE(dt == MEDUSA_F32 || dt == MEDUSA_BF16, MEDUSA_ERR_UNSUPPORTED,
-                 "medusa_tree_attention: unknown dtype %d", dt);
+                 "%s: unknown dtype %d", fn, dt);
   MEDUSA_REQUIRE(D == 64 || D == 128, MEDUSA_ERR_UNSUPPORTED,
-                 "medusa_tree_attention: head dim %d not in {64, 128}", D);
+                 "%s: head dim %d not in {64, 128}", fn, D);
   MEDUSA_REQUIRE(N >= 1 && N <= MEDUSA_MAX_NODES, MEDUSA_ERR_UNSUPPORTED,
-                 "medusa_tree_attention: N=%d outside [1, 64]", N);
+                 "%s: N=%d outside [1, 64]", fn, N);
   MEDUSA_REQUIRE(B >= 0 && Hq >= 1 && Hkv >= 1 && Hq % Hkv == 0, MEDUSA_ERR_INVALID_ARG,
-                 "medusa_tree_attention: B=%d Hq=%d Hkv=%d (Hq must be a multiple of Hkv)", B, Hq,
+                 "%s: B=%d Hq=%d Hkv=%d (Hq must be a multiple of Hkv)", fn, B, Hq,
                  Hkv);
   MEDUSA_REQUIRE(P >= 1 && max_pages >= 1 && max_ctx >= 0, MEDUSA_ERR_INVALID_ARG,
-                 "medusa_tree_attention: P=%d max_pages=%d max_ctx=%d", P, max_pages, max_ctx);
+                 "%s: P=%d max_pages=%d max_ctx=%d", fn, P, max_pages, max_ctx);
   MEDUSA_REQUIRE(P >= 4 && P <= 4096, MEDUSA_ERR_UNSUPPORTED,
-                 "medusa_tree_attention: page size %d outside [4, 4096]", P);
+                 "%s: page size %d outside [4, 4096]", fn, P);
   MEDUSA_REQUIRE((int64_t)max_ctx + N <= (int64_t)max_pages * P, MEDUSA_ERR_INVALID_ARG,
-                 "medusa_tree_attention: max_ctx + N = %d exceeds max_pages * P = %lld",
+                 "%s: max_ctx + N = %d exceeds max_pages * P = %lld", fn,
                  max_ctx + N, (long long)max_pages * P);
   MEDUSA_REQUIRE(scale > 0.f && scale < 1e30f, MEDUSA_ERR_INVALID_ARG,
-                 "medusa_tree_attention: scale must be positive and finite");
+                 "%s: scale must be positive and finite", fn);
   if (B == 0) return MEDUSA_OK;
   MEDUSA_REQUIRE(Q && Kt && Vt && Kc && Vc && page_table && ctx && mask && O,
-                 MEDUSA_ERR_INVALID_ARG, "medusa_tree_attention: NULL pointer");
+                 MEDUSA_ERR_INVALID_ARG, "%s: NULL pointer", fn);
   MEDUSA_REQUIRE(((uintptr_t)Q | (uintptr_t)Kt | (uintptr_t)Vt | (uintptr_t)Kc | (uintptr_t)Vc) %
                          16 == 0,
-                 MEDUSA_ERR_INVALID_ARG, "medusa_tree_attention: tensors must be 16-byte aligned");
+                 MEDUSA_ERR_INVALID_ARG, "%s: tensors must be 16-byte aligned", fn);
   const SplitPlan p = plan_splits(B, Hq, N, max_ctx, P,
                                   dt == MEDUSA_BF16 ? MEDUSA_ATTN_DMA_WGS : MEDUSA_ATTN_TARGET_WGS);
   const WsLayout L = ws_layout(B, Hq, N, D, p.splits, sizeof(float));
   MEDUSA_REQUIRE(ws != NULL && ws_bytes >= L.total, MEDUSA_ERR_WORKSPACE,
-                 "medusa_tree_attention: workspace %zu < %zu bytes", ws_bytes, L.total);
+                 "%s: workspace %zu < %zu bytes", fn, ws_bytes, L.total);
   MEDUSA_REQUIRE((uintptr_t)ws % 256 == 0, MEDUSA_ERR_INVALID_ARG,
-                 "medusa_tree_attention: ws must be 256-byte aligned");
+                 "%s: ws must be 256-byte aligned", fn);
 
   medusa::AttnArgs a;
   a.Q = Q; a.Kt = Kt; a.Vt = Vt; a.Kc = Kc; a.Vc = Vc;
@@ -1059,5 +1137,5 @@ extern "C" int32_t medusa_tree_attention(const void* Q, const void* Kt, const vo
   }
 #undef MEDUSA_ATT_LAUNCH
 #undef MEDUSA_ATT_COMBINE
-  return check_launch("medusa_tree_attention");
+  return check_launch(fn);
 }

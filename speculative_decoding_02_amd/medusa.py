@@ -39,6 +39,8 @@ _SIGS = {
     "medusa_tree_attention_ws": (sz, [i32, i32, i32, i32, i32, i32, i32]),
     "medusa_tree_attention": (i32, [vp, vp, vp, vp, vp, vp, i32, i32, vp, i32, vp, i32, i32, i32,
                                     i32, i32, f32, i32, vp, vp, sz, vp]),
+    "medusa_tree_attention_noalloc": (i32, [vp, vp, vp, vp, vp, vp, i32, i32, vp, i32, vp, i32,
+                                            i32, i32, i32, i32, f32, i32, vp, vp]),
     "medusa_accept_ws": (sz, [i32, i32]),
     "medusa_accept": (i32, [vp, i64, vp, vp, i32, i32, i32, i32, f32, f32, f32, vp, vp, vp, vp,
                             sz, vp]),
@@ -251,6 +253,23 @@ def medusa_tree_attention(Q, Kt, Vt, Kc, Vc, page_table, ctx, max_ctx, mask, sca
         _p(Q), _p(Kt), _p(Vt), _p(Kc), _p(Vc), _p(page_table), page_table.shape[1], P, _p(ctx),
         int(max_ctx), _p(mask), B, N, Hq, Hkv, D, float(scale), dt, _p(out), _p(ws), ws.numel(),
         _stream()))
+    return out
+
+
+NOALLOC_MAX_BYTES = 32 << 20  # MEDUSA_ATTN_NOALLOC_MAX_BYTES
+
+
+def medusa_tree_attention_noalloc(Q, Kt, Vt, Kc, Vc, page_table, ctx, max_ctx, mask, scale,
+                                  out):
+    """medusa_tree_attention without a workspace: the library's fixed per-GPU
+    array holds the split partials (calls on one GPU must not overlap).  The
+    caller passes the output buffer; nothing is allocated."""
+    dt = _dt(Q)
+    B, N, Hq, D = Q.shape
+    Hkv, P = Kc.shape[1], Kc.shape[2]
+    _check("medusa_tree_attention_noalloc", _lib.medusa_tree_attention_noalloc(
+        _p(Q), _p(Kt), _p(Vt), _p(Kc), _p(Vc), _p(page_table), page_table.shape[1], P, _p(ctx),
+        int(max_ctx), _p(mask), B, N, Hq, Hkv, D, float(scale), dt, _p(out), _stream()))
     return out
 
 

@@ -1,0 +1,73 @@
+"""The attention entry point that allocates nothing (for callers that cannot
+allocate) against the workspace entry point, through the C ABI: two calls in
+a row on the library's per-GPU array, the second smaller, each bit for bit
+equal to medusa_tree_attention on the same inputs (the same kernels and
+launch plan), and the first also against the oracle; a size whose split
+partials exceed the array is refused before any launch."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import medusa_oracle as orc
+from gpu_util import TOL, assert_close, case, dev, host
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from speculative_decoding_02_amd import medusa
+    return medusa
+
+
+def _inputs(seed, B, N, H, Hkv, D, ctx, P, dt):
+    d = synth.attention_inputs(seed, B, N, H, Hkv, D, ctx, page_size=P, permute_pages=True,
+                               bf16=dt == torch.bfloat16)
+    masks = np.stack([orc.build_tree(d["parent"][b], d["rank"][b], 0, np.zeros((8, 8), np.int32),
+                                     0)["mask"] for b in range(B)])
+    return d, masks
+
+
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+def test_noalloc_attention_equals_workspace_call(lib, dt):
+    shapes = [(1, 64, 32, 32, 128, 2048, 16),   # the 7B layer
+              (2, 20, 4, 2, 64, [300, 41], 12)]  # smaller, grouped kv heads, other page size
+    for i, (B, N, H, Hkv, D, ctx, P) in enumerate(shapes):
+        case(f"no-alloc attention call {i}: B={B} N={N} H={H} Hkv={Hkv} D={D} ctx={ctx} P={P}")
+        d, masks = _inputs(31 + i, B, N, H, Hkv, D, ctx, P, dt)
+        max_ctx = int(np.max(d["ctx"]))
+        args = lambda Kc, Vc: (dev(d["Q"], dt), dev(d["Kt"], dt), dev(d["Vt"], dt), Kc, Vc,
+                               dev(d["page_table"]), dev(d["ctx"]), max_ctx, dev(masks),
+                               float(d["scale"]))
+        Kc1, Vc1 = dev(d["Kc"], dt), dev(d["Vc"], dt)
+        Kc2, Vc2 = dev(d["Kc"], dt), dev(d["Vc"], dt)
+        o_ws = lib.medusa_tree_attention(*args(Kc1, Vc1))
+        o_na = torch.full_like(o_ws, float("nan"))
+        lib.medusa_tree_attention_noalloc(*args(Kc2, Vc2), out=o_na)
+        torch.cuda.synchronize()
+        assert torch.equal(o_na, o_ws), "no-alloc output differs from the workspace call"
+        assert torch.equal(Kc1, Kc2) and torch.equal(Vc1, Vc2), "appended tree K/V differ"
+        if i == 0:
+            c = int(d["ctx"][0])
+            ref = orc.tree_attention(d["Q"][0][:, :4], orc.cache_rows(d["Kc"], d["page_table"][0], c, P)[:, :4],
+                                     orc.cache_rows(d["Vc"], d["page_table"][0], c, P)[:, :4],
+                                     d["Kt"][0][:, :4], d["Vt"][0][:, :4], masks[0], d["scale"])
+            assert_close(host(o_na)[0][:, :4], ref, TOL[dt], "no-alloc vs oracle (heads 0-3)")
+
+
+def test_noalloc_attention_refuses_oversize(lib):
+    case("no-alloc attention: oversize refused")
+    B, N, H, D, max_ctx = 64, 64, 64, 128, 8192
+    need = lib._lib.medusa_tree_attention_ws(B, N, H, H, D, max_ctx, 16)
+    assert need > lib.NOALLOC_MAX_BYTES
+    t = torch.zeros((B, N, H, D), dtype=torch.bfloat16, device="cuda")
+    kc = torch.zeros((1, H, 16, D), dtype=torch.bfloat16, device="cuda")
+    pt = torch.zeros((B, (max_ctx + N) // 16 + 1), dtype=torch.int32, device="cuda")
+    ctx = torch.zeros(B, dtype=torch.int32, device="cuda")
+    mask = torch.zeros((B, N), dtype=torch.int64, device="cuda")
+    with pytest.raises(lib.MedusaError) as e:
+        lib.medusa_tree_attention_noalloc(t, t, t, kc, kc, pt, ctx, max_ctx, mask, 0.1, out=t)
+    assert e.value.status == 2 and "more than the fixed" in str(e.value)
