@@ -134,6 +134,118 @@ def tree_attention_c2(torch, M, synth, reps=10, copies=17):
                 kv_copies_rotated=copies, rotated_mb=round(copies * 2 * c["kc_bytes"] / 1e6, 1))
 
 
+def tree_attention_step_shape(torch, M, synth, ctx, max_ctx, reps=10, copies=17):
+    """Tree attention alone at the decode step's shape: the 7B layer (32
+    heads x 128, 64-node tree) at ``ctx`` cached tokens, planned for
+    ``max_ctx`` as the decoder plans it; KV rotated over > 256 MB."""
+    import numpy as np
+    B, N, H, D, P = 1, 64, 32, 128, 16
+    dev = "cuda"
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(5)
+    bf = torch.bfloat16
+    pages = (max_ctx + N + P - 1) // P
+    Q = torch.randn((B, N, H, D), generator=gen, device=dev).to(bf)
+    Kt = torch.randn((B, N, H, D), generator=gen, device=dev).to(bf)
+    Vt = torch.randn((B, N, H, D), generator=gen, device=dev).to(bf)
+    Kc = [torch.randn((pages, H, P, D), generator=gen, device=dev).to(bf) for _ in range(copies)]
+    Vc = [torch.randn((pages, H, P, D), generator=gen, device=dev).to(bf) for _ in range(copies)]
+    parent, rank = synth.prune_template(*synth.tree_template((4, 3, 2, 2, 1)), N, 2)
+    i32 = dict(dtype=torch.int32, device=dev)
+    pt = torch.arange(pages, **i32)[None].contiguous()
+    ctx_t = torch.tensor([ctx], **i32)
+    _, _, mask = M.medusa_build_tree(torch.tensor(parent[None], **i32), torch.tensor(rank[None], **i32),
+                                     torch.zeros(1, **i32), torch.zeros((5, 1, 4), **i32), ctx_t)
+    out = torch.empty_like(Q)
+    ws = M._ws(M.tree_attention_ws_bytes(B, N, H, H, D, max_ctx), dev)
+    scale = 1.0 / np.sqrt(D)
+    launches = [lambda i=i: M.medusa_tree_attention(Q, Kt, Vt, Kc[i], Vc[i], pt, ctx_t, max_ctx, mask, scale,
+                                                    out=out, ws=ws) for i in range(copies)]
+    us, us_med = graph_time_us(torch, launches, reps=reps)
+    nbytes = (ctx + N) * H * D * 2 * 2 + 2 * B * N * H * D * 2 + N * 8 + N * H * D * 2 * 2
+    gbs = nbytes / (us * 1e-6) / 1e9
+    return dict(workload=f"7B layer: 32 heads x 128, ctx {ctx} + 64-node tree (planned for max_ctx "
+                         f"{max_ctx}), bf16, 16-token pages",
+                us=round(us, 3), us_median=round(us_med, 3), bytes=nbytes, gbs=round(gbs, 1),
+                frac=round(gbs / HBM_PEAK_GBS, 4))
+
+
+def hbm_copy_rate(torch, nbytes=1 << 30, reps=5):
+    """Device-to-device copy of ``nbytes`` (HIP events): GB/s counting the
+    bytes read and written, the plain-copy rate the kernels' fractions are
+    also reported against."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    best = None
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        dst.copy_(src)
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b)
+        best = ms if best is None else min(best, ms)
+    del src, dst
+    torch.cuda.empty_cache()
+    return round(2 * nbytes / (best * 1e-3) / 1e9, 1)
+
+
+def c1_generation(torch, synth):
+    """The tiny fp32 decoder (2 layers, hidden 256, 4x64 heads, vocab 1000, 3
+    heads, top-2 x top-3 tree): 64 tokens of Medusa greedy decoding from a
+    32-token prompt, the step graph-replayed; prefill and decode timed apart."""
+    from speculative_decoding_02_amd.decoder import DeviceModel, MedusaDecoder
+    m = synth.tiny_decoder(seed=1)
+    prompt = synth.prompt_tokens(101, 32, m.vocab)
+    parent, rank = synth.tree_template((2, 3))
+    dec = MedusaDecoder(DeviceModel(m, dtype=torch.float32), parent, rank, capacity=32 + 64 + 16)
+    dec.generate(prompt, 64, graph=True)  # records the step graph
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    dec.prefill(prompt)
+    torch.cuda.synchronize()
+    t_pre = time.perf_counter() - t0
+    rec = []
+    t0 = time.perf_counter()
+    toks = dec.generate(prompt, 64, record=rec, graph=True)
+    torch.cuda.synchronize()
+    t_all = time.perf_counter() - t0
+    t_dec = max(t_all - t_pre, 1e-9)
+    return dict(workload="tiny fp32 decoder (2 layers, hidden 256, vocab 1000) + 3 heads, top-2 x top-3 "
+                         "tree (9 nodes), prompt 32, 64 greedy tokens",
+                tokens=len(toks), steps=len(rec), mean_accept_len=round(float(sum(rec)) / len(rec), 3),
+                tokens_per_s=round(64 / t_dec, 1), prefill_ms=round(1000 * t_pre, 3),
+                decode_ms=round(1000 * t_dec, 3))
+
+
+def c4_generation(torch, model, parent, rank, prompt, mode, n_new=256, **kw):
+    """The configuration as stated: 256 tokens generated from the 512-token
+    prompt with the step graph-replayed (the device log read once per batch
+    of steps); prefill timed apart and excluded from tokens/s."""
+    from speculative_decoding_02_amd.decoder import MedusaDecoder
+    import numpy as np
+    dec = MedusaDecoder(model, parent, rank, capacity=len(prompt) + n_new + 64, mode=mode, **kw)
+    dec.generate(prompt, n_new, graph=True)  # records the step graph, warms up
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    dec.prefill(prompt)
+    torch.cuda.synchronize()
+    t_pre = time.perf_counter() - t0
+    rec = []
+    t0 = time.perf_counter()
+    dec.generate(prompt, n_new, record=rec, graph=True)
+    torch.cuda.synchronize()
+    t_all = time.perf_counter() - t0
+    t_dec = max(t_all - t_pre, 1e-9)
+    del dec
+    torch.cuda.empty_cache()
+    return dict(tokens=n_new, steps=len(rec), mean_accept_len=round(float(np.mean(rec)), 3),
+                tokens_per_s=round(n_new / t_dec, 2), ms_per_step=round(1000 * t_dec / len(rec), 3),
+                prefill_ms=round(1000 * t_pre, 2), decode_s=round(t_dec, 4), **kw)
+
+
 def heads_c3(torch, M, rows, reps=10):
     """The five Medusa heads + per-head top-10 at the 7B shape (H 4096, V 32000)
     on ``rows`` hidden rows: stage 1 (residual SiLU layer), stage 2 (vocabulary
@@ -226,8 +338,26 @@ def batched_attention_c5(torch, M, synth, reps=5):
     return res
 
 
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), or None."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(torch, dec, model_src, emitted_per_step, sample_layers, reps=3):
-    """The oracle, as is, on a bounded sample of one decode step (host cores)."""
+    """The oracle, as is, on a bounded sample of one decode step (host cores):
+    its BLAS pool runs one thread per CPU this process may use."""
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(limits=len(os.sched_getaffinity(0))):
+        return _cpu_baseline(torch, dec, model_src, emitted_per_step, sample_layers, reps)
+
+
+def _cpu_baseline(torch, dec, model_src, emitted_per_step, sample_layers, reps):
     import numpy as np
     from threadpoolctl import threadpool_info
     import synth
@@ -276,7 +406,8 @@ def cpu_baseline(torch, dec, model_src, emitted_per_step, sample_layers, reps=3)
     step_s = t_layers * meta["n_layers"] / sample_layers + t_head
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     return dict(value=round(emitted_per_step / step_s, 4), unit="tokens/s", cores=int(threads),
-                kind="oracle",
+                kind="oracle", affinity_cpus=len(os.sched_getaffinity(0)), nproc=os.cpu_count(),
+                cpu_model=cpu_model(),
                 sample=(f"one 64-node verification step at ctx={ctx}, run {reps} times (median): "
                         f"{sample_layers} of {meta['n_layers']} layers timed ({t_layers:.2f} s, "
                         f"scaled x{meta['n_layers'] / sample_layers:g}) plus lm_head, greedy accept "
@@ -385,6 +516,11 @@ def main():
                     help="skip the heads (64 and 1024 rows) and batched-attention measurements")
     ap.add_argument("--heads-only", action="store_true",
                     help="run only the five heads + top-10 at 64 and 1024 rows (for kernel traces)")
+    ap.add_argument("--attn-only", action="store_true",
+                    help="run only tree attention at the 7B layer shape (2048 cached tokens) and at "
+                         "the decode step's shape, for per-shape kernel traces")
+    ap.add_argument("--skip-generation", action="store_true",
+                    help="skip the 256-token generations (greedy, typical) and the tiny fp32 model")
     ap.add_argument("--kernels-only", action="store_true",
                     help="run only the dominant projection kernel (32 launches over 7B-shaped "
                          "gate/up weights), the tree-attention launches and a 1 GiB copy, "
@@ -410,6 +546,13 @@ def main():
         return
     if args.heads_only:
         print(json.dumps({"heads_c3": heads_c3(torch, M, 64), "heads_c3b": heads_c3(torch, M, 1024)}))
+        return
+    if args.attn_only:
+        from speculative_decoding_02_amd.decoder import plan_cache
+        cap = 512 + 6 * (args.warmup + args.steps) + 128
+        print(json.dumps({"tree_attention": tree_attention_c2(torch, M, synth),
+                          "tree_attention_step": tree_attention_step_shape(
+                              torch, M, synth, 531, plan_cache(cap, 64, 16)[2])}))
         return
     log("[bench] drawing the random 7B-shaped decoder on the GPU")
     src = synth.device_llama(seed=4)
@@ -525,7 +668,21 @@ def main():
         del bdec
         torch.cuda.empty_cache()
 
-    c2 = None if args.skip_c2 else tree_attention_c2(torch, M, synth)
+    gen = c1 = None
+    if not args.skip_generation:
+        log("[bench] the configuration as stated: 256 tokens from the 512-token prompt, greedy then typical")
+        gen = {"greedy": c4_generation(torch, model, parent, rank, prompt, "greedy"),
+               "typical": c4_generation(torch, model, parent, rank, prompt, "typical", epsilon=0.3,
+                                        delta=0.09)}
+        log("[bench] the tiny fp32 decoder: 64 greedy tokens")
+        c1 = c1_generation(torch, synth)
+    c2 = step_attn = None
+    if not args.skip_c2:
+        from speculative_decoding_02_amd.decoder import plan_cache
+        c2 = tree_attention_c2(torch, M, synth)
+        step_attn = tree_attention_step_shape(torch, M, synth, dec.ctx_sample, dec.max_ctx)
+    log("[bench] plain device-to-device copy (the measured streaming rate)")
+    copy_gbs = hbm_copy_rate(torch)
     c3 = c3b = c5 = f4 = None
     if not args.skip_extra:
         log("[bench] heads at the 7B shape: 64 rows, then 1024 rows")
@@ -559,14 +716,20 @@ def main():
         "typical": typical,
         "sampled": sampled,
         "sparse_tree_typical": sparse,
+        "c4_generation": gen,
+        "c1_tiny_fp32": c1,
+        "hbm_copy_gbs": copy_gbs,
         "roofline": {"bound": "hbm", "kernel": "gemm_xdma_kernel (gate/up projection, SwiGLU epilogue)",
                      "achieved": round(gu_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gu_gbs / HBM_PEAK_GBS, 4),
+                     "frac_of_copy": round(gu_gbs / copy_gbs, 4),
                      "traffic": measured_traffic("gate_up_projection", "gemm.hip"),
                      "bytes_per_launch": gu_bytes, "us_per_launch": round(gu_us, 2),
                      "us_median": round(gu_med, 2),
                      "timing": "HIP events around graph replays of the 32 per-step launches"},
-        "tree_attention": c2,
+        "tree_attention": dict(c2, frac_of_copy=round(c2["gbs"] / copy_gbs, 4)) if c2 else None,
+        "tree_attention_step": dict(step_attn, frac_of_copy=round(step_attn["gbs"] / copy_gbs, 4))
+        if step_attn else None,
         "heads_c3": c3,
         "heads_c3b": c3b,
         "batched_attention_c5": c5,

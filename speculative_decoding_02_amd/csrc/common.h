@@ -89,6 +89,15 @@ __device__ __forceinline__ f32x4 mfma_bf16_16x16x16(u32x2 a, u32x2 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, a),
                                                    __builtin_bit_cast(i16x4, b), c, 0, 0, 0);
 }
+// bf16, 32x32x16 (twice the issue rate of the 16x16 shapes on gfx950): lane
+// l supplies row l%32 of A and column l%32 of B with contraction indices
+// 8(l/32) .. +7; element e of the result holds row 8(e/4) + 4(l/32) + e%4,
+// column l%32.
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+__device__ __forceinline__ f32x16 mfma_bf16_32x32x16(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
 // fp32: one contraction element per lane (16x16x4), index l/16.
 __device__ __forceinline__ f32x4 mfma_f32_16x16x4(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
@@ -196,14 +205,15 @@ __device__ __forceinline__ void rope_rot(float x1, float x2, float c, float s, f
 // issued from inline asm so that the compiler does not treat it as an LDS
 // store it must wait for before every LDS read (it would wait for all DMA in
 // flight); the kernel's own vmcnt waits and barriers order the accesses.
-// The instruction writes no register.  m0 cannot be declared as clobbered
-// (it is reserved); the kernels that use this helper contain no other m0
-// use (no indexed register moves, no m0-based LDS or message instructions),
-// which their compiled code shows.
+// The instruction writes no register.  m0 is reserved (it cannot be named
+// as clobbered), so the block saves it in a scratch SGPR and restores it
+// after the instruction has issued: whatever value the compiler keeps in m0
+// around the call survives it.
 __device__ __forceinline__ void lds_dma16(const void* gptr, uint32_t lds_addr) {
   const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_addr);
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
-               :
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %2, off\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved)
                : "s"(m0v), "v"(gptr)
                : "memory");
 }
