@@ -931,12 +931,22 @@ struct SplitPlan {
 #ifndef MEDUSA_ATTN_KQ
 #define MEDUSA_ATTN_KQ 2
 #endif
+// A split holds at most MEDUSA_ATTN_MAX_CHUNK keys: with many (sequence,
+// head) pairs one split each would do, but in a ragged batch a pair's
+// workgroup then streams its whole context, and the longest ones finish far
+// behind the rest.  Capped splits keep every workgroup's work within one
+// chunk; the splits past a sequence's own length exit at once, so each
+// sequence takes as many as its actual context needs.
+#ifndef MEDUSA_ATTN_MAX_CHUNK
+#define MEDUSA_ATTN_MAX_CHUNK 1536
+#endif
 SplitPlan plan_splits(int B, int Hq, int N, int max_ctx, int P, int target) {
   const int total = max_ctx + N;
   const int bh = B * Hq;
   const int want = (target + bh - 1) / bh;
   int chunk = (total + want - 1) / want;
   chunk = (chunk + medusa::ATT_TILE - 1) / medusa::ATT_TILE * medusa::ATT_TILE;
+  if (chunk > MEDUSA_ATTN_MAX_CHUNK) chunk = MEDUSA_ATTN_MAX_CHUNK / medusa::ATT_TILE * medusa::ATT_TILE;
   // a split's keys must span at most ATT_MAX_SPLIT_PAGES pages
   const int cap = ((medusa::ATT_MAX_SPLIT_PAGES - 1) * P) / medusa::ATT_TILE * medusa::ATT_TILE;
   if (cap >= medusa::ATT_TILE && chunk > cap) chunk = cap;
