@@ -142,11 +142,7 @@ int32_t medusa_linear(const void* X, int64_t x_bstride, int64_t M, int64_t Kd, c
  *   topk (0..64): if > 0, topk_ids [K, M, topk] int32 and topk_vals
  *   [K, M, topk] float receive each row's largest logits, value descending,
  *   equal values ordered by lower token id.
- *   ws: device workspace of at least medusa_heads_ws(...) bytes, 256-byte
- *     aligned.  Its first 16 KiB hold top-k arrival counters that must be
- *     zero before the first call (zero-fill the workspace once); every call
- *     leaves them zero, whatever its M, K, V or topk.  Calls sharing one ws
- *     must not overlap in time.
+ *   ws: device workspace of at least medusa_heads_ws(...) bytes.
  * With W1 = 0, b1 = 0 and W2_k = lm_head the logits equal
  * medusa_linear(X, lm_head) bit for bit.
  * ---------------------------------------------------------------------- */
@@ -159,12 +155,7 @@ int32_t medusa_heads(const void* X, int64_t M, int64_t H, int32_t K, const void*
 /* medusa_topk: top-k of each float row ("Medusa Heads", tree section: the
  * heads' best guesses).  logits [R, V] float -> ids [R, k] int32, vals [R, k]
  * float; order value descending, ties by lower index; 1 <= k <= 64, k <= V.
- * ws: medusa_topk_ws(R, V, k) bytes, 256-byte aligned (0 when V <= 4096;
- * then ws may be NULL).  With several 4096-wide chunks per row and k <= 16,
- * R <= 4096, the row's last chunk merges the row in the same launch; its
- * arrival counters take the first 16 KiB of ws, which must be zero before
- * the first call (zero-fill once; every call leaves them zero).  Calls
- * sharing one ws must not overlap in time. */
+ * ws: medusa_topk_ws(R, V, k) bytes (0 when V <= 4096; then ws may be NULL). */
 size_t medusa_topk_ws(int64_t R, int64_t V, int32_t k);
 int32_t medusa_topk(const float* logits, int64_t R, int64_t V, int32_t k, int32_t* ids,
                     float* vals, void* ws, size_t ws_bytes, void* stream);

@@ -133,13 +133,6 @@ __device__ __forceinline__ float rows4_sum(float x) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-// Top-k's per-row arrival counters (the row's last chunk merges it) sit at
-// the start of a top-k workspace, one per row for up to TOPK_ARRIVE_ROWS
-// rows, in a slot of fixed size so that every call on one workspace finds
-// them at the same place.
-constexpr int TOPK_ARRIVE_ROWS = 4096;
-constexpr size_t TOPK_ARRIVE_BYTES = (size_t)TOPK_ARRIVE_ROWS * sizeof(unsigned);
-
 // One 256-thread workgroup normalises one row of H floats held as up to
 // RMS_V4 f32x4 per thread (vector e = threadIdx.x + 256 i, e < H/4): the
 // row's sum of squares in a fixed order (per thread, then per wave, then the

@@ -15,12 +15,8 @@
 // of a wave argmax instead.  Wave 0 sorts the four waves' lists the same
 // way.  Stage 2 merges a row's chunk candidates, one wave per row: 64 at a
 // time sorted, each batch folded into the running best by the bitonic
-// merge step.  For k <= 16 and at most TOPK_ARRIVE_ROWS rows, stage 2 runs
-// inside the stage-1 launch: the workgroup that finishes a row's last chunk
-// (a per-row arrival counter, counted after a device-scope fence behind each
-// chunk's candidates) merges the row and zeroes the counter again.  For
-// k > 16 both stages keep a block-wide selection.  With one chunk, stage 1
-// writes the result.
+// merge step.  For k > 16 both stages keep a block-wide selection.  With one
+// chunk, stage 1 writes the result.
 #include "common.h"
 
 namespace medusa {
@@ -239,54 +235,12 @@ __device__ __forceinline__ void block_select(float (&lv)[KMAX], int (&li)[KMAX],
   }
 }
 
-// Stage 2 for k <= 16 on one wave: a row's ncand candidates taken 64 at a
-// time; the first batch is sorted descending, every later one ascending and
-// folded in by the lane-wise maximum (which leaves the 64 best of both as a
-// bitonic sequence) and one bitonic merge.  Lanes 0..k-1 write the result.
-__device__ __forceinline__ void merge_row_wave(const int* ci, const float* cv, int ncand, int k,
-                                               int* __restrict__ ids, float* __restrict__ vals) {
-  const int lane = threadIdx.x & 63;
-  int nid = lane < ncand ? ci[lane] : 0;
-  float nv = lane < ncand ? cv[lane] : 0.f;
-  uint64_t top = TOPK_PAD_KEY;
-  for (int c0 = 0; c0 < ncand; c0 += 64) {
-    uint64_t x = c0 + lane < ncand ? topk_key(nv, nid) : TOPK_PAD_KEY;
-    const int c1 = c0 + 64 + lane;  // next batch in flight during this one's sort
-    if (c1 < ncand) { nid = ci[c1]; nv = cv[c1]; }
-    if (c0 == 0) {
-      top = wave_sort(x, lane, true);
-    } else {
-      x = wave_sort(x, lane, false);
-      top = top > x ? top : x;
-      top = wave_bitonic_merge(top, lane, true);
-    }
-  }
-  if (lane < k) {
-    ids[lane] = key_index(top);
-    vals[lane] = key_value(top);
-  }
-}
-
-__global__ __launch_bounds__(TOPK_THREADS) void topk_merge_wave_kernel(
-    const int* __restrict__ cids, const float* __restrict__ cvals, int64_t R, int ncand, int k,
-    int* __restrict__ ids, float* __restrict__ vals) {
-  const int64_t row = (int64_t)blockIdx.x * (TOPK_THREADS / 64) + (threadIdx.x >> 6);
-  if (row >= R) return;
-  merge_row_wave(cids + row * ncand, cvals + row * ncand, ncand, k, ids + row * k, vals + row * k);
-}
-
-// Stage 1 writes chunk s of row r to ids/vals at (r * gridDim.x + s) *
-// out_stride.  fids/fvals/arrive (k <= 16, several chunks, stage 2 in this
-// launch; arrive NULL otherwise): the rows' final top-k and their arrival
-// counters (zero before the launch, zero again after it).  ids/vals carry no
-// __restrict__: the merging workgroup reads what the others wrote there.
 template <int KMAX>
 __global__ __launch_bounds__(TOPK_THREADS) void topk_chunk_kernel(const float* __restrict__ logits,
-                                                                  int64_t V, int k, int* ids,
-                                                                  float* vals, int out_stride,
-                                                                  int* __restrict__ fids,
-                                                                  float* __restrict__ fvals,
-                                                                  unsigned* __restrict__ arrive) {
+                                                                  int64_t V, int k,
+                                                                  int* __restrict__ ids,
+                                                                  float* __restrict__ vals,
+                                                                  int out_stride) {
   const int s = blockIdx.x;
   const int64_t row = blockIdx.y;
   const float* x = logits + row * V;
@@ -327,19 +281,6 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_chunk_kernel(const float* _
       ids[o + lane] = key_index(key);
       vals[o + lane] = key_value(key);
     }
-    if (arrive == nullptr) return;
-    // the row's last chunk to finish merges the row: every chunk's
-    // candidates are made visible device-wide before its arrival is counted,
-    // and read after the last arrival
-    __threadfence();
-    unsigned prev = 0;
-    if (lane == 0) prev = atomicAdd(arrive + row, 1u);
-    prev = __shfl(prev, 0, 64);
-    if (prev != gridDim.x - 1) return;
-    __threadfence();
-    const int ncand = gridDim.x * out_stride;
-    merge_row_wave(ids + row * ncand, vals + row * ncand, ncand, k, fids + row * k, fvals + row * k);
-    if (lane == 0) arrive[row] = 0u;  // ready for the next call (kernel boundary orders it)
   } else {
     float lv[KMAX];
     int li[KMAX];
@@ -353,6 +294,39 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_chunk_kernel(const float* _
         if (e < V) list_insert<KMAX>(lv, li, v[g * 4 + r], (int)e);
       }
     block_select<KMAX>(lv, li, k, ids + o, vals + o);
+  }
+}
+
+// Stage 2 for k <= 16: one wave per row.  The row's candidates are taken 64
+// at a time; the first batch is sorted descending, every later one ascending
+// and folded in by the lane-wise maximum (which leaves the 64 best of both
+// as a bitonic sequence) and one bitonic merge.
+__global__ __launch_bounds__(TOPK_THREADS) void topk_merge_wave_kernel(
+    const int* __restrict__ cids, const float* __restrict__ cvals, int64_t R, int ncand, int k,
+    int* __restrict__ ids, float* __restrict__ vals) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * (TOPK_THREADS / 64) + (threadIdx.x >> 6);
+  if (row >= R) return;
+  const int* ci = cids + row * ncand;
+  const float* cv = cvals + row * ncand;
+  int nid = lane < ncand ? ci[lane] : 0;
+  float nv = lane < ncand ? cv[lane] : 0.f;
+  uint64_t top = TOPK_PAD_KEY;
+  for (int c0 = 0; c0 < ncand; c0 += 64) {
+    uint64_t x = c0 + lane < ncand ? topk_key(nv, nid) : TOPK_PAD_KEY;
+    const int c1 = c0 + 64 + lane;  // next batch in flight during this one's sort
+    if (c1 < ncand) { nid = ci[c1]; nv = cv[c1]; }
+    if (c0 == 0) {
+      top = wave_sort(x, lane, true);
+    } else {
+      x = wave_sort(x, lane, false);
+      top = top > x ? top : x;
+      top = wave_bitonic_merge(top, lane, true);
+    }
+  }
+  if (lane < k) {
+    ids[row * k + lane] = key_index(top);
+    vals[row * k + lane] = key_value(top);
   }
 }
 
@@ -377,42 +351,33 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_merge_kernel(const int* __r
 namespace medusa_host {
 static int topk_chunks(int64_t V) { return (int)((V + medusa::TOPK_CHUNK - 1) / medusa::TOPK_CHUNK); }
 
-// every chunk's candidates (ids, then values); 0 when one chunk holds a row
-size_t topk_cand_bytes(int64_t R, int64_t V, int k) {
+size_t topk_ws_bytes(int64_t R, int64_t V, int k) {
   const int S = topk_chunks(V);
   if (S <= 1 || R <= 0 || k <= 0) return 0;
   return align_up((size_t)R * S * k * sizeof(int), 256) + align_up((size_t)R * S * k * sizeof(float), 256);
 }
-// the arrival counters come first, at a size fixed for every call, so that
-// calls of any R on one workspace keep them at the same place
-size_t topk_ws_bytes(int64_t R, int64_t V, int k) {
-  const size_t c = topk_cand_bytes(R, V, k);
-  return c ? medusa::TOPK_ARRIVE_BYTES + c : 0;
-}
 
-void launch_topk(const float* logits, int64_t R, int64_t V, int k, int* ids, float* vals,
-                 void* cand, unsigned* arrive, hipStream_t st) {
+void launch_topk(const float* logits, int64_t R, int64_t V, int k, int* ids, float* vals, void* ws,
+                 hipStream_t st) {
   using namespace medusa;
   if (R <= 0) return;
   const int S = topk_chunks(V);
   int* cid = ids;
   float* cval = vals;
   if (S > 1) {
-    cid = (int*)cand;
-    cval = (float*)((char*)cand + align_up((size_t)R * S * k * sizeof(int), 256));
+    cid = (int*)ws;
+    cval = (float*)((char*)ws + align_up((size_t)R * S * k * sizeof(int), 256));
   }
-  const bool fused = S > 1 && k <= 16 && R <= TOPK_ARRIVE_ROWS;
   const dim3 g1((unsigned)S, (unsigned)R), blk(TOPK_THREADS);
-#define MEDUSA_TOPK(KM)                                                                        \
-  do {                                                                                         \
-    hipLaunchKernelGGL(topk_chunk_kernel<KM>, g1, blk, 0, st, logits, V, k, cid, cval, k, ids,  \
-                       vals, fused ? arrive : nullptr);                                        \
-    if (S > 1 && KM <= 16 && !fused)                                                           \
-      hipLaunchKernelGGL(topk_merge_wave_kernel, dim3((unsigned)((R + 3) / 4)), blk, 0, st,    \
-                         cid, cval, R, S * k, k, ids, vals);                                   \
-    else if (S > 1 && KM > 16)                                                                 \
-      hipLaunchKernelGGL(topk_merge_kernel<64>, dim3((unsigned)R), blk, 0, st, cid, cval,      \
-                         S * k, k, ids, vals);                                                 \
+#define MEDUSA_TOPK(KM)                                                                       \
+  do {                                                                                        \
+    hipLaunchKernelGGL(topk_chunk_kernel<KM>, g1, blk, 0, st, logits, V, k, cid, cval, k);    \
+    if (S > 1 && KM <= 16)                                                                    \
+      hipLaunchKernelGGL(topk_merge_wave_kernel, dim3((unsigned)((R + 3) / 4)), blk, 0, st,   \
+                         cid, cval, R, S * k, k, ids, vals);                                  \
+    else if (S > 1)                                                                           \
+      hipLaunchKernelGGL(topk_merge_kernel<64>, dim3((unsigned)R), blk, 0, st, cid, cval,     \
+                         S * k, k, ids, vals);                                                \
   } while (0)
   if (k <= 4) MEDUSA_TOPK(4);
   else if (k <= 10) MEDUSA_TOPK(10);
@@ -438,9 +403,6 @@ extern "C" int32_t medusa_topk(const float* logits, int64_t R, int64_t V, int32_
   const size_t need = topk_ws_bytes(R, V, k);
   MEDUSA_REQUIRE(need == 0 || (ws != NULL && ws_bytes >= need), MEDUSA_ERR_WORKSPACE,
                  "medusa_topk: workspace %zu < %zu bytes", ws_bytes, need);
-  MEDUSA_REQUIRE(need == 0 || (uintptr_t)ws % 256 == 0, MEDUSA_ERR_INVALID_ARG,
-                 "medusa_topk: ws must be 256-byte aligned");
-  launch_topk(logits, R, V, k, ids, vals, (char*)ws + medusa::TOPK_ARRIVE_BYTES, (unsigned*)ws,
-              (hipStream_t)stream);
+  launch_topk(logits, R, V, k, ids, vals, ws, (hipStream_t)stream);
   return check_launch("medusa_topk");
 }

@@ -312,26 +312,6 @@ def test_heads_topk_without_logits_buffer(lib, Mr, H, V, K, k):
             assert np.array_equal(host(vals[kk, m]), ov)
 
 
-def test_heads_workspace_reused(lib):
-    """One heads workspace through calls of different M and top-k: after each
-    call the top-k arrival counters (the first 16 KiB) are zero again, and the
-    top-k equals that of a call on a fresh workspace."""
-    H, V, K = 256, 8192, 3
-    calls = [(64, 10), (5, 4), (33, 16), (64, 17), (17, 1)]
-    ws = lib._ws(max(lib._lib.medusa_heads_ws(m, H, K, V, k, lib.BF16) for m, k in calls), "cuda")
-    bf = torch.bfloat16
-    for i, (Mr, k) in enumerate(calls):
-        case(f"heads reused ws M={Mr} k={k}")
-        d = synth.heads_inputs(50 + i, Mr, H, V, K, w1_std=0.05, w2_std=0.05, bf16=True)
-        args = (dev(d["X"], bf), dev(d["W1"], bf), dev(d["b1"], bf), dev(d["W2"], bf))
-        ids = torch.empty((K, Mr, k), dtype=torch.int32, device="cuda")
-        vals = torch.empty((K, Mr, k), dtype=torch.float32, device="cuda")
-        lib.medusa_heads(*args, topk=k, ids=ids, vals=vals, ws=ws, want_logits=False)
-        assert not host(ws[:16384]).any()
-        _, ids2, vals2 = lib.medusa_heads(*args, topk=k)
-        assert torch.equal(ids, ids2) and torch.equal(vals, vals2)
-
-
 # -------------------------------------------------------------------- topk ---
 @pytest.mark.parametrize("R,V,k", [(3, 1000, 1), (4, 1000, 3), (5, 32000, 10), (2, 70, 64),
                                    (6, 4097, 16), (1, 256, 17)])
@@ -378,26 +358,6 @@ def test_topk_structured(lib, kind, R, V, k):
         oi, ov = orc.topk(x[r], k)
         assert host(ids[r]).tolist() == oi.tolist()
         assert np.array_equal(host(vals[r]), ov)
-
-
-def test_topk_workspace_reused(lib):
-    """One workspace through calls of different R, V and k: the rows' arrival
-    counters (the first 16 KiB) are zero after every call, whether the chunk
-    merge ran in the chunk launch (k <= 16, R <= 4096) or in its own (R = 4100,
-    k = 20), and every call's result equals the oracle's."""
-    calls = [(5, 32000, 10), (2, 9000, 16), (4100, 4097, 3), (3, 20000, 20), (33, 12288, 4),
-             (1, 5000, 1)]
-    ws = lib._ws(max(lib._lib.medusa_topk_ws(R, V, k) for R, V, k in calls), "cuda")
-    for i, (R, V, k) in enumerate(calls):
-        case(f"topk reused ws R={R} V={V} k={k}")
-        rng = np.random.default_rng(100 + i)
-        x = (rng.integers(-200, 200, size=(R, V)) / 8).astype(np.float32)
-        ids, vals = lib.medusa_topk(dev(x), k, ws=ws)
-        assert not host(ws[:16384]).any()
-        for r in sorted({0, R // 3, R - 1}):
-            oi, ov = orc.topk(x[r], k)
-            assert host(ids[r]).tolist() == oi.tolist()
-            assert np.array_equal(host(vals[r]), ov)
 
 
 # -------------------------------------------------------------- build tree ---
