@@ -519,6 +519,9 @@ def main():
     ap.add_argument("--attn-only", action="store_true",
                     help="run only tree attention at the 7B layer shape (2048 cached tokens) and at "
                          "the decode step's shape, for per-shape kernel traces")
+    ap.add_argument("--f4-only", action="store_true",
+                    help="run only one 7B layer's four projections at 1024 rows (the large-row "
+                         "tiling), for kernel traces and counter passes")
     ap.add_argument("--skip-generation", action="store_true",
                     help="skip the 256-token generations (greedy, typical) and the tiny fp32 model")
     ap.add_argument("--kernels-only", action="store_true",
@@ -546,6 +549,9 @@ def main():
         return
     if args.heads_only:
         print(json.dumps({"heads_c3": heads_c3(torch, M, 64), "heads_c3b": heads_c3(torch, M, 1024)}))
+        return
+    if args.f4_only:
+        print(json.dumps({"batched_projections_f4": batched_projections_f4(torch, M)}))
         return
     if args.attn_only:
         from speculative_decoding_02_amd.decoder import plan_cache

@@ -62,5 +62,33 @@ def build(verbose: bool = True, out: str = LIB, defines=(), build_dir: str = BUI
     return out
 
 
+# Host-only build with AddressSanitizer and UndefinedBehaviorSanitizer on the
+# host code (the argument checks, workspace queries and host-side tree
+# code), for CPU checks of those paths; its kernels are built as usual.
+SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+            "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def build_host_sanitized(build_dir: str, out: str) -> str:
+    """Compile every source host-only with the sanitizers into ``out``."""
+    os.makedirs(build_dir, exist_ok=True)
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    flags = ["-O1", "-g", f"--offload-arch={ARCH}", "-std=c++17", "-fPIC", *SANITIZE,
+             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+
+    def one(src):
+        obj = os.path.join(build_dir, os.path.basename(src) + ".o")
+        r = subprocess.run([HIPCC, *flags, "-c", src, "-o", obj], capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc (sanitized host build) failed for {src}:\n{r.stderr}")
+        return obj
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        objs = list(ex.map(one, srcs))
+    r = subprocess.run([HIPCC, *flags, "-shared", *objs, "-o", out], capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link (sanitized host build) failed:\n{r.stderr}")
+    return out
+
+
 if __name__ == "__main__":
     build()

@@ -1000,7 +1000,7 @@ GemmPlan gemm_plan(int64_t M, int64_t Kd, int64_t Nw, int dt, int epi) {
   // share (measured: splitting 172+ tiles is a loss, 32-96 tiles a large win).
   const int64_t tiles = (Nw / (64 * XNB)) * ((M + 63) / 64);
   int64_t ks = 1;
-  if (tiles < 160) ks = (MEDUSA_GEMM_XL_TARGET_WGS + tiles - 1) / tiles;
+  if (tiles > 0 && tiles < 160) ks = (MEDUSA_GEMM_XL_TARGET_WGS + tiles - 1) / tiles;
   ks = std::min<int64_t>(ks, Kd / XL_KC);
   ks = std::min<int64_t>(ks, 8);
   p.ksplit = (int)std::max<int64_t>(ks, 1);
@@ -1155,7 +1155,10 @@ void launch_gemm(const void* X, int64_t xbs, int64_t M, int64_t Kd, const void* 
 }  // namespace medusa_host
 
 extern "C" size_t medusa_linear_ws(int64_t M, int64_t Kd, int64_t N, int32_t batch, int32_t dt) {
+  // shapes medusa_linear rejects need nothing (and stay out of the planner's arithmetic)
   if (M <= 0 || Kd <= 0 || N <= 0 || batch <= 0) return 0;
+  if (M > INT32_MAX || Kd > INT32_MAX || N > INT32_MAX || (dt != MEDUSA_F32 && dt != MEDUSA_BF16))
+    return 0;
   return medusa_host::gemm_ws_bytes(M, Kd, N, batch, dt);
 }
 
@@ -1252,8 +1255,12 @@ static bool qkv_rope_fused(int64_t M, int64_t Kd, int64_t N, int dt) {
 extern "C" size_t medusa_linear_qkv_rope_ws(int64_t M, int64_t Kd, int32_t Hq, int32_t Hkv,
                                             int32_t D, int32_t dt) {
   using namespace medusa_host;
-  if (M <= 0 || Kd <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0) return 0;
-  const int64_t N = (int64_t)(Hq + 2 * Hkv) * D;
+  // shapes medusa_linear_qkv_rope rejects need nothing
+  if (M <= 0 || Kd <= 0 || Hq <= 0 || Hkv <= 0 || D < 8 || D > 128 || M > INT32_MAX ||
+      Kd > INT32_MAX || (dt != MEDUSA_F32 && dt != MEDUSA_BF16))
+    return 0;
+  const int64_t N = ((int64_t)Hq + 2 * (int64_t)Hkv) * D;
+  if (N > INT32_MAX) return 0;
   if (qkv_rope_fused(M, Kd, N, dt)) return 0;
   const size_t es = dt == MEDUSA_BF16 ? 2 : 4;
   return align_up((size_t)M * N * es, 256) + gemm_ws_bytes(M, Kd, N, 1, dt);
@@ -1279,7 +1286,9 @@ extern "C" int32_t medusa_linear_qkv_rope(const void* X, int64_t M, int64_t Kd, 
                  "medusa_linear_qkv_rope: NULL pointer");
   MEDUSA_REQUIRE(((uintptr_t)X | (uintptr_t)W | (uintptr_t)v) % 16 == 0, MEDUSA_ERR_INVALID_ARG,
                  "medusa_linear_qkv_rope: X, W and v must be 16-byte aligned");
-  const int64_t N = (int64_t)(Hq + 2 * Hkv) * D;
+  const int64_t N = ((int64_t)Hq + 2 * (int64_t)Hkv) * D;
+  MEDUSA_REQUIRE(N <= INT32_MAX, MEDUSA_ERR_UNSUPPORTED,
+                 "medusa_linear_qkv_rope: (Hq + 2 Hkv) D = %lld above 2^31 - 1", (long long)N);
   const size_t need = medusa_linear_qkv_rope_ws(M, Kd, Hq, Hkv, D, dt);
   MEDUSA_REQUIRE(need == 0 || (ws != NULL && ws_bytes >= need), MEDUSA_ERR_WORKSPACE,
                  "medusa_linear_qkv_rope: workspace %zu < %zu bytes", ws_bytes, need);

@@ -25,7 +25,11 @@ size_t topk_ws_bytes(int64_t R, int64_t V, int k);
 
 extern "C" size_t medusa_heads_ws(int64_t M, int64_t H, int32_t K, int64_t V, int32_t topk,
                                   int32_t dt) {
-  if (M < 0 || H < 0 || K < 0 || V < 0) return 0;
+  // shapes medusa_heads rejects (or M = 0) need nothing
+  if (M <= 0 || H <= 0 || V <= 0 || K < 1 || K > MEDUSA_MAX_HEADS || topk < 0 ||
+      topk > MEDUSA_MAX_TOPK || M > INT32_MAX || H > INT32_MAX || V > INT32_MAX ||
+      (dt != MEDUSA_F32 && dt != MEDUSA_BF16))
+    return 0;
   const size_t es = dt == MEDUSA_BF16 ? 2 : 4;
   using namespace medusa_host;
   const size_t gws = std::max(gemm_ws_bytes(M, H, H, K, dt), gemm_ws_bytes(M, H, V, K, dt));

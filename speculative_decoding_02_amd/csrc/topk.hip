@@ -352,8 +352,10 @@ namespace medusa_host {
 static int topk_chunks(int64_t V) { return (int)((V + medusa::TOPK_CHUNK - 1) / medusa::TOPK_CHUNK); }
 
 size_t topk_ws_bytes(int64_t R, int64_t V, int k) {
+  // sizes the entry points reject need nothing (and keep the products below in range)
+  if (R <= 0 || k <= 0 || k > MEDUSA_MAX_TOPK || V <= 0 || R > INT32_MAX || V > INT32_MAX) return 0;
   const int S = topk_chunks(V);
-  if (S <= 1 || R <= 0 || k <= 0) return 0;
+  if (S <= 1) return 0;
   return align_up((size_t)R * S * k * sizeof(int), 256) + align_up((size_t)R * S * k * sizeof(float), 256);
 }
 

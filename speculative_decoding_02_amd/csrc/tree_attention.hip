@@ -941,18 +941,20 @@ struct SplitPlan {
 #define MEDUSA_ATTN_MAX_CHUNK 1536
 #endif
 SplitPlan plan_splits(int B, int Hq, int N, int max_ctx, int P, int target) {
-  const int total = max_ctx + N;
-  const int bh = B * Hq;
-  const int want = (target + bh - 1) / bh;
-  int chunk = (total + want - 1) / want;
+  const int64_t total = (int64_t)max_ctx + N;
+  const int64_t bh = (int64_t)B * Hq;
+  const int64_t want = (target + bh - 1) / bh;
+  int64_t chunk = (total + want - 1) / want;
   chunk = (chunk + medusa::ATT_TILE - 1) / medusa::ATT_TILE * medusa::ATT_TILE;
   if (chunk > MEDUSA_ATTN_MAX_CHUNK) chunk = MEDUSA_ATTN_MAX_CHUNK / medusa::ATT_TILE * medusa::ATT_TILE;
   // a split's keys must span at most ATT_MAX_SPLIT_PAGES pages
-  const int cap = ((medusa::ATT_MAX_SPLIT_PAGES - 1) * P) / medusa::ATT_TILE * medusa::ATT_TILE;
+  const int64_t cap = ((medusa::ATT_MAX_SPLIT_PAGES - 1) * (int64_t)P) / medusa::ATT_TILE * medusa::ATT_TILE;
   if (cap >= medusa::ATT_TILE && chunk > cap) chunk = cap;
-  return {chunk, (total + chunk - 1) / chunk};
+  return {(int)chunk, (int)((total + chunk - 1) / chunk)};
 }
 
+// largest B and Hq (grid dimensions of the attention launches)
+#define MEDUSA_ATTN_MAX_GRID 65535
 struct WsLayout {
   size_t ml, opart, total;
 };
@@ -969,8 +971,11 @@ WsLayout ws_layout(int B, int Hq, int N, int D, int S, size_t part_elem) {
 
 extern "C" size_t medusa_tree_attention_ws(int32_t B, int32_t N, int32_t Hq, int32_t Hkv,
                                            int32_t D, int32_t max_ctx, int32_t P) {
-  (void)Hkv;
-  if (B <= 0 || N <= 0 || Hq <= 0 || D <= 0 || max_ctx < 0 || P < 1) return 0;
+  // shapes medusa_tree_attention rejects need nothing
+  if (B <= 0 || N < 1 || N > MEDUSA_MAX_NODES || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 ||
+      (D != 64 && D != 128) || max_ctx < 0 || P < 4 || P > 4096 || max_ctx > INT32_MAX - N ||
+      B > MEDUSA_ATTN_MAX_GRID || Hq > MEDUSA_ATTN_MAX_GRID)
+    return 0;
   // either dtype's plan (fp32 partials are the larger element)
   const SplitPlan p1 = plan_splits(B, Hq, N, max_ctx, P, MEDUSA_ATTN_TARGET_WGS);
   const SplitPlan p2 = plan_splits(B, Hq, N, max_ctx, P, MEDUSA_ATTN_DMA_WGS);
@@ -1070,6 +1075,9 @@ static int32_t tree_attention_impl(const char* fn, const void* Q, const void* Kt
   MEDUSA_REQUIRE(B >= 0 && Hq >= 1 && Hkv >= 1 && Hq % Hkv == 0, MEDUSA_ERR_INVALID_ARG,
                  "%s: B=%d Hq=%d Hkv=%d (Hq must be a multiple of Hkv)", fn, B, Hq,
                  Hkv);
+  MEDUSA_REQUIRE(B <= MEDUSA_ATTN_MAX_GRID && Hq <= MEDUSA_ATTN_MAX_GRID && max_ctx <= INT32_MAX - N,
+                 MEDUSA_ERR_UNSUPPORTED, "%s: B=%d or Hq=%d above %d, or max_ctx=%d too large", fn,
+                 B, Hq, MEDUSA_ATTN_MAX_GRID, max_ctx);
   MEDUSA_REQUIRE(P >= 1 && max_pages >= 1 && max_ctx >= 0, MEDUSA_ERR_INVALID_ARG,
                  "%s: P=%d max_pages=%d max_ctx=%d", fn, P, max_pages, max_ctx);
   MEDUSA_REQUIRE(P >= 4 && P <= 4096, MEDUSA_ERR_UNSUPPORTED,

@@ -433,6 +433,11 @@ ATT_CASES = [
     (2, 64, 8, 2, 128, [700, 130], 24, True, torch.bfloat16),
     (1, 64, 2, 2, 128, 700, 12, True, torch.float32),
     (2, 20, 4, 2, 64, [130, 0], 24, False, torch.float32),
+    # longer bf16 ranges (more splits per head, the merge's larger batches)
+    (1, 64, 2, 2, 128, 3000, 16, True, torch.bfloat16),
+    (2, 37, 3, 3, 64, [2500, 7], 8, True, torch.bfloat16),
+    (2, 64, 8, 2, 128, [2300, 130], 24, True, torch.bfloat16),
+    (1, 20, 4, 4, 64, 2200, 12, False, torch.bfloat16),
 ]
 
 
@@ -465,14 +470,15 @@ def test_tree_attention(lib, B, N, Hq, Hkv, D, ctx, P, perm, dt):
         np.testing.assert_array_equal(kt[:c], kc)
 
 
-@pytest.mark.parametrize("D,P", [(128, 16), (64, 12)])
-def test_tree_attention_large_values(lib, D, P):
-    """|V| near 1e5 (legal bf16, past fp16's largest finite 65504) through a
-    call with many key splits: every split's partial output is about 1e5 in
-    magnitude, so its block-scaled fp16 store must keep it finite.  Outputs
-    are stored in bf16: the bar is 2e-2 relative above |y| = 1."""
-    case(f"tree_attention large values D={D} P={P}")
-    B, N, H, c = 1, 64, 4, 1500
+@pytest.mark.parametrize("D,P,c", [(128, 16, 3000), (64, 12, 3000), (128, 16, 1500)])
+def test_tree_attention_large_values(lib, D, P, c):
+    """|V| near 1e5 (legal bf16, past fp16's largest finite 65504) through
+    calls with many key splits (1500 and 3000 cached keys): every split's
+    partial output is about 1e5 in magnitude, so its block-scaled fp16 store
+    must keep it finite.  Outputs are stored in bf16: the bar is 2e-2
+    relative above |y| = 1."""
+    case(f"tree_attention large values D={D} P={P} ctx={c}")
+    B, N, H = 1, 64, 4
     d = synth.attention_inputs(21 + D, B, N, H, H, D, c, page_size=P, permute_pages=True, bf16=True)
     sgn = np.where(np.arange(D) % 3 == 0, -1.0, 1.0).astype(np.float32)
     big = lambda v: synth.round_bf16(1e5 * sgn + 300.0 * v)
