@@ -60,6 +60,7 @@ typedef enum {
 #define MEDUSA_MAX_NODES 64
 #define MEDUSA_MAX_HEADS 8
 #define MEDUSA_MAX_TOPK 64
+#define MEDUSA_MAX_TOPK_LISTS 64   /* per-chunk top-k lists per row (vocabulary <= 64 x 4096) */
 #define MEDUSA_MAX_LAYERS 128
 
 const char* medusa_status_string(int32_t status);
@@ -147,6 +148,17 @@ int32_t medusa_linear(const void* X, int64_t x_bstride, int64_t M, int64_t Kd, c
  * medusa_linear(X, lm_head) bit for bit.
  * ---------------------------------------------------------------------- */
 size_t medusa_heads_ws(int64_t M, int64_t H, int32_t K, int64_t V, int32_t topk, int32_t dt);
+/* medusa_heads_lists: medusa_heads with the top-k's first stage only, for a
+ * consumer that merges the lists itself (medusa_tree_embed with lists > 1):
+ * list_ids [K, M, S, topk] int32 and list_vals [K, M, S, topk] float, S =
+ * medusa_topk_lists(V), hold each 4096-wide vocabulary chunk's top-k of each
+ * row (value descending, ties by lower token id); the row's top-k is the
+ * top-k of its S lists.  1 <= topk <= min(64, V); the rest as medusa_heads
+ * (its workspace query included). */
+int32_t medusa_heads_lists(const void* X, int64_t M, int64_t H, int32_t K, const void* W1,
+                           const void* b1, const void* W2, int64_t V, int32_t dt, int32_t topk,
+                           int32_t* list_ids, float* list_vals, void* ws, size_t ws_bytes,
+                           void* stream);
 int32_t medusa_heads(const void* X, int64_t M, int64_t H, int32_t K, const void* W1,
                      const void* b1, const void* W2, int64_t V, int32_t dt, float* logits,
                      int32_t topk, int32_t* topk_ids, float* topk_vals, void* ws,
@@ -157,6 +169,10 @@ int32_t medusa_heads(const void* X, int64_t M, int64_t H, int32_t K, const void*
  * float; order value descending, ties by lower index; 1 <= k <= 64, k <= V.
  * ws: medusa_topk_ws(R, V, k) bytes (0 when V <= 4096; then ws may be NULL). */
 size_t medusa_topk_ws(int64_t R, int64_t V, int32_t k);
+/* The top-k runs in two stages: each 4096-wide chunk of a row keeps its own
+ * top-k list (the same order), then the row's lists are merged.  The number
+ * of chunk lists per row: ceil(V / 4096) (0 for V outside [1, 2^31 - 1]). */
+int32_t medusa_topk_lists(int64_t V);
 int32_t medusa_topk(const float* logits, int64_t R, int64_t V, int32_t k, int32_t* ids,
                     float* vals, void* ws, size_t ws_bytes, void* stream);
 
@@ -325,9 +341,14 @@ int32_t medusa_rmsnorm(const float* x, int64_t M, int64_t H, const void* gain, f
  * as there: tokens, pos [B, N], mask [B, N]; x [B*N, H] float (16-byte
  * aligned) = the embedding rows; h [B*N, H] (dt) = RMSNorm(x) * gain (gain
  * NULL for 1).  H a multiple of 4, H <= 8192; table, gain and h aligned to
- * four elements. */
+ * four elements.  lists = 1: topk_ids [K, B, topk] are the heads' top-k lists
+ * (topk_vals unused, may be NULL).  lists = S > 1 (<= 64): topk_ids and
+ * topk_vals [K, B, S, topk] are per-chunk lists as medusa_heads_lists writes
+ * them, and each node's token is found by merging its row's lists in the
+ * launch; the outputs equal those from the merged lists bit for bit. */
 int32_t medusa_tree_embed(int32_t B, int32_t N, const int32_t* parent, const int32_t* rank,
-                          const int32_t* root_tok, const int32_t* topk_ids, int32_t K,
+                          const int32_t* root_tok, const int32_t* topk_ids,
+                          const float* topk_vals, int32_t lists, int32_t K,
                           int32_t topk, const int32_t* ctx, int32_t* tokens, int32_t* pos,
                           uint64_t* mask, const void* table, int64_t V, int64_t H, int32_t dt,
                           const void* gain, float eps, float* x, void* h, void* stream);

@@ -18,6 +18,7 @@
 // merge step.  For k > 16 both stages keep a block-wide selection.  With one
 // chunk, stage 1 writes the result.
 #include "common.h"
+#include "topk_wave.h"
 
 namespace medusa {
 
@@ -74,71 +75,6 @@ __device__ __forceinline__ void wave_argmax(float& bv, int& bi) {
     bv = __uint_as_float(sv[0]); bi = (int)si[0];
     pick(bv, bi, __uint_as_float(sv[1]), (int)si[1]);
   }
-}
-
-// Sort keys: the float's bits made order-preserving as unsigned (-0 taken
-// as +0, so signed zeros tie as they compare), then the index complemented,
-// so a larger key is the better (value, index) pair.  NaN never becomes a
-// key: it fails every comparison that admits a value.
-__device__ __forceinline__ uint64_t topk_key(float v, int i) {
-  uint32_t u = __float_as_uint(v);
-  if (u == 0x80000000u) u = 0u;
-  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-  return ((uint64_t)u << 32) | (uint32_t)~(uint32_t)i;
-}
-__device__ __forceinline__ int key_index(uint64_t key) { return (int)~(uint32_t)key; }
-__device__ __forceinline__ float key_value(uint64_t key) {
-  const uint32_t u = (uint32_t)(key >> 32);
-  return __uint_as_float((u & 0x80000000u) ? (u & 0x7fffffffu) : ~u);
-}
-// The list padding (-inf, 0x7fffffff): below every real entry.
-constexpr uint64_t TOPK_PAD_KEY = (uint64_t)0x007fffffu << 32 | 0x80000000u;
-
-// Lane l's copy of lane l ^ J's register.
-template <int J>
-__device__ __forceinline__ uint32_t lane_xor(uint32_t v) {
-  if constexpr (J == 1) return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);
-  else if constexpr (J == 2) return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);
-  else return (uint32_t)__shfl_xor((int)v, J, 64);
-}
-template <int J>
-__device__ __forceinline__ uint64_t lane_xor(uint64_t v) {
-  return ((uint64_t)lane_xor<J>((uint32_t)(v >> 32)) << 32) | lane_xor<J>((uint32_t)v);
-}
-template <int J>
-__device__ __forceinline__ float lane_xor(float v) {
-  return __uint_as_float(lane_xor<J>(__float_as_uint(v)));
-}
-
-// Bitonic network over the 64 lanes of a wave (one key per lane).  Stage
-// (KK, J) compares lanes l and l ^ J; the pair belongs to a block of KK lanes
-// ordered descending when (l & KK) == 0 matches `desc`, and the lower lane
-// of the pair keeps the larger key in a descending block.
-template <int KK, int J, typename Key>
-__device__ __forceinline__ Key bitonic_pass(Key x, int lane, bool desc) {
-  const Key y = lane_xor<J>(x);
-  const bool block_desc = ((lane & KK) == 0) == desc;
-  const bool keep_larger = ((lane & J) == 0) == block_desc;
-  x = ((x > y) == keep_larger) ? x : y;
-  if constexpr (J > 1) return bitonic_pass<KK, J / 2>(x, lane, desc);
-  else return x;
-}
-template <int KK, int WIDTH, typename Key>
-__device__ __forceinline__ Key bitonic_sort_from(Key x, int lane, bool desc) {
-  x = bitonic_pass<KK, KK / 2>(x, lane, desc);
-  if constexpr (KK < WIDTH) return bitonic_sort_from<KK * 2, WIDTH>(x, lane, desc);
-  else return x;
-}
-// Each block of WIDTH lanes sorted; lanes 0..WIDTH-1 in the order asked
-// (lane 0 holds the largest when desc).  WIDTH = 64 sorts the whole wave.
-template <int WIDTH = 64, typename Key>
-__device__ __forceinline__ Key wave_sort(Key x, int lane, bool desc) {
-  return bitonic_sort_from<2, WIDTH>(x, lane, desc);
-}
-// A bitonic sequence over the wave, sorted.
-template <typename Key>
-__device__ __forceinline__ Key wave_bitonic_merge(Key x, int lane, bool desc) {
-  return bitonic_pass<64, 32>(x, lane, desc);
 }
 
 // One wave's k best (k <= KMAX <= 16) of its lanes' 16 values each, written
@@ -297,33 +233,14 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_chunk_kernel(const float* _
   }
 }
 
-// Stage 2 for k <= 16: one wave per row.  The row's candidates are taken 64
-// at a time; the first batch is sorted descending, every later one ascending
-// and folded in by the lane-wise maximum (which leaves the 64 best of both
-// as a bitonic sequence) and one bitonic merge.
+// Stage 2 for k <= 16: one wave per row merges the row's chunk lists.
 __global__ __launch_bounds__(TOPK_THREADS) void topk_merge_wave_kernel(
     const int* __restrict__ cids, const float* __restrict__ cvals, int64_t R, int ncand, int k,
     int* __restrict__ ids, float* __restrict__ vals) {
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * (TOPK_THREADS / 64) + (threadIdx.x >> 6);
   if (row >= R) return;
-  const int* ci = cids + row * ncand;
-  const float* cv = cvals + row * ncand;
-  int nid = lane < ncand ? ci[lane] : 0;
-  float nv = lane < ncand ? cv[lane] : 0.f;
-  uint64_t top = TOPK_PAD_KEY;
-  for (int c0 = 0; c0 < ncand; c0 += 64) {
-    uint64_t x = c0 + lane < ncand ? topk_key(nv, nid) : TOPK_PAD_KEY;
-    const int c1 = c0 + 64 + lane;  // next batch in flight during this one's sort
-    if (c1 < ncand) { nid = ci[c1]; nv = cv[c1]; }
-    if (c0 == 0) {
-      top = wave_sort(x, lane, true);
-    } else {
-      x = wave_sort(x, lane, false);
-      top = top > x ? top : x;
-      top = wave_bitonic_merge(top, lane, true);
-    }
-  }
+  const uint64_t top = merge_lists_wave(cids + row * ncand, cvals + row * ncand, ncand);
   if (lane < k) {
     ids[row * k + lane] = key_index(top);
     vals[row * k + lane] = key_value(top);
@@ -387,7 +304,23 @@ void launch_topk(const float* logits, int64_t R, int64_t V, int k, int* ids, flo
   else MEDUSA_TOPK(64);
 #undef MEDUSA_TOPK
 }
+// Stage 1 only: each row's per-chunk lists straight into ids/vals [R][S][k]
+// (with one chunk, the row's top-k).
+void launch_topk_lists(const float* logits, int64_t R, int64_t V, int k, int* ids, float* vals,
+                       hipStream_t st) {
+  using namespace medusa;
+  if (R <= 0) return;
+  const dim3 g1((unsigned)topk_chunks(V), (unsigned)R), blk(TOPK_THREADS);
+  if (k <= 4) hipLaunchKernelGGL(topk_chunk_kernel<4>, g1, blk, 0, st, logits, V, k, ids, vals, k);
+  else if (k <= 10) hipLaunchKernelGGL(topk_chunk_kernel<10>, g1, blk, 0, st, logits, V, k, ids, vals, k);
+  else if (k <= 16) hipLaunchKernelGGL(topk_chunk_kernel<16>, g1, blk, 0, st, logits, V, k, ids, vals, k);
+  else hipLaunchKernelGGL(topk_chunk_kernel<64>, g1, blk, 0, st, logits, V, k, ids, vals, k);
+}
 }  // namespace medusa_host
+
+extern "C" int32_t medusa_topk_lists(int64_t V) {
+  return V >= 1 && V <= INT32_MAX ? medusa_host::topk_chunks(V) : 0;
+}
 
 extern "C" size_t medusa_topk_ws(int64_t R, int64_t V, int32_t k) {
   return medusa_host::topk_ws_bytes(R, V, k);

@@ -6,6 +6,7 @@
 // One thread per node.  A node walks its parent links (at most 64 steps) to
 // find its depth and to OR its ancestors' bits into its mask.
 #include "common.h"
+#include "topk_wave.h"
 
 namespace medusa {
 
@@ -41,11 +42,16 @@ __global__ __launch_bounds__(64) void build_tree_kernel(int N, const int* __rest
 // holds parent[j]; one step per tree level), picks the node's token and
 // writes the tree outputs; then the workgroup copies the token's embedding
 // row into the fp32 residual stream and normalises it (the RMSNorm kernel's
-// helpers, so the results equal the separate calls' bit for bit).
+// helpers, so the results equal the separate calls' bit for bit).  With
+// lists > 1 the heads' rows come as per-chunk candidate lists (ids and
+// values, lists x topk per row) and wave 0 merges its row's lists to find the
+// token of the node's rank: the same total order (value descending, lower id
+// first) as the top-k's own merge, so the same token.
 template <typename T>
 __global__ __launch_bounds__(256) void tree_embed_kernel(
     int N, const int* __restrict__ parent, const int* __restrict__ rank,
-    const int* __restrict__ root_tok, const int* __restrict__ topk_ids, int B, int topk,
+    const int* __restrict__ root_tok, const int* __restrict__ topk_ids,
+    const float* __restrict__ topk_vals, int lists, int B, int topk,
     const int* __restrict__ ctx, int* __restrict__ tokens, int* __restrict__ pos,
     uint64_t* __restrict__ mask, const T* __restrict__ table, int64_t H,
     const T* __restrict__ gain, float eps, float* __restrict__ x, T* __restrict__ h) {
@@ -67,10 +73,18 @@ __global__ __launch_bounds__(256) void tree_embed_kernel(
     }
     const uint32_t lo = __shfl((uint32_t)anc, n, 64), hi = __shfl((uint32_t)(anc >> 32), n, 64);
     const uint64_t an = ((uint64_t)hi << 32) | lo;
+    const int depth = __popcll(an) - 1;  // the same in every lane
+    const int64_t row = (int64_t)max(depth - 1, 0) * B + b;
+    int tok = 0;
+    if (depth > 0 && lists > 1) {
+      const int64_t c0 = row * lists * topk;
+      const uint64_t top = merge_lists_wave(topk_ids + c0, topk_vals + c0, lists * topk);
+      tok = key_index(((uint64_t)__shfl((uint32_t)(top >> 32), rank[o], 64) << 32) |
+                      __shfl((uint32_t)top, rank[o], 64));
+    }
     if (tid == 0) {
-      const int depth = __popcll(an) - 1;
-      const int tok = depth == 0 ? root_tok[b]
-                                 : topk_ids[((int64_t)(depth - 1) * B + b) * topk + rank[o]];
+      if (depth == 0) tok = root_tok[b];
+      else if (lists == 1) tok = topk_ids[row * topk + rank[o]];
       tokens[o] = tok;
       pos[o] = ctx[b] + depth;
       mask[o] = an;
@@ -99,7 +113,8 @@ __global__ __launch_bounds__(256) void tree_embed_kernel(
 
 extern "C" int32_t medusa_tree_embed(int32_t B, int32_t N, const int32_t* parent,
                                      const int32_t* rank, const int32_t* root_tok,
-                                     const int32_t* topk_ids, int32_t K, int32_t topk,
+                                     const int32_t* topk_ids, const float* topk_vals,
+                                     int32_t lists, int32_t K, int32_t topk,
                                      const int32_t* ctx, int32_t* tokens, int32_t* pos,
                                      uint64_t* mask, const void* table, int64_t V, int64_t H,
                                      int32_t dt, const void* gain, float eps, float* x, void* h,
@@ -110,13 +125,15 @@ extern "C" int32_t medusa_tree_embed(int32_t B, int32_t N, const int32_t* parent
                  "%s: B=%d N=%d (N must be in [1, 64])", fn, B, N);
   MEDUSA_REQUIRE(K >= 0 && K <= MEDUSA_MAX_HEADS && topk >= 1 && topk <= MEDUSA_MAX_TOPK,
                  MEDUSA_ERR_INVALID_ARG, "%s: K=%d topk=%d", fn, K, topk);
+  MEDUSA_REQUIRE(lists >= 1 && lists <= MEDUSA_MAX_TOPK_LISTS, MEDUSA_ERR_INVALID_ARG,
+                 "%s: lists=%d outside [1, %d]", fn, lists, MEDUSA_MAX_TOPK_LISTS);
   MEDUSA_REQUIRE(dt == MEDUSA_F32 || dt == MEDUSA_BF16, MEDUSA_ERR_UNSUPPORTED, "%s: dtype", fn);
   MEDUSA_REQUIRE(V >= 1 && eps >= 0.f && H % 4 == 0 && H >= 4 && H <= 4 * 256 * medusa::RMS_V4,
                  MEDUSA_ERR_UNSUPPORTED, "%s: needs V >= 1, eps >= 0, H a multiple of 4 and H <= %d",
                  fn, 4 * 256 * medusa::RMS_V4);
   if (B == 0) return MEDUSA_OK;
   MEDUSA_REQUIRE(parent && rank && root_tok && ctx && tokens && pos && mask && table && x && h &&
-                     (topk_ids || N == 1),
+                     (topk_ids || N == 1) && (topk_vals || lists == 1 || N == 1),
                  MEDUSA_ERR_INVALID_ARG, "%s: NULL pointer", fn);
   const int a4 = dt == MEDUSA_BF16 ? 8 : 16;  // four elements of table, gain and h
   MEDUSA_REQUIRE(((uintptr_t)x) % 16 == 0 && ((uintptr_t)table | (uintptr_t)gain | (uintptr_t)h) % a4 == 0,
@@ -124,12 +141,13 @@ extern "C" int32_t medusa_tree_embed(int32_t B, int32_t N, const int32_t* parent
   hipStream_t st = (hipStream_t)stream;
   if (dt == MEDUSA_BF16)
     hipLaunchKernelGGL(medusa::tree_embed_kernel<medusa::bf16_t>, dim3(N, B), dim3(256), 0, st, N,
-                       parent, rank, root_tok, topk_ids, B, topk, ctx, tokens, pos, mask,
+                       parent, rank, root_tok, topk_ids, topk_vals, lists, B, topk, ctx, tokens,
+                       pos, mask,
                        (const medusa::bf16_t*)table, H, (const medusa::bf16_t*)gain, eps, x,
                        (medusa::bf16_t*)h);
   else
     hipLaunchKernelGGL(medusa::tree_embed_kernel<float>, dim3(N, B), dim3(256), 0, st, N, parent,
-                       rank, root_tok, topk_ids, B, topk, ctx, tokens, pos, mask,
+                       rank, root_tok, topk_ids, topk_vals, lists, B, topk, ctx, tokens, pos, mask,
                        (const float*)table, H, (const float*)gain, eps, x, (float*)h);
   return check_launch(fn);
 }

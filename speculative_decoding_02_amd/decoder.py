@@ -189,8 +189,15 @@ class MedusaDecoder:
         self.ctx_host = 0
         self.root = torch.zeros(B, **i32)
         Kh = max(self.K, 1)
+        if self.K > model.n_medusa:
+            raise ValueError(f"the tree is {self.K} deep; the model has {model.n_medusa} heads")
         self.topk_ids = torch.zeros((Kh, B, self.width), **i32)
         self.topk_vals = torch.zeros((Kh, B, self.width), dtype=torch.float32, device=dev)
+        # the fused step takes the heads' per-chunk top-k lists and merges them
+        # inside the tree build (one launch fewer than a separate merge)
+        S = M._lib.medusa_topk_lists(model.vocab)
+        self.list_ids = torch.zeros((Kh, B, S, self.width), **i32)
+        self.list_vals = torch.zeros((Kh, B, S, self.width), dtype=torch.float32, device=dev)
         self.attn_ws = M._ws(max(M.tree_attention_ws_bytes(B, n, model.n_heads, model.n_kv_heads,
                                                            model.head_dim, self.max_ctx, page_size)
                                  for n in range(1, 65)), dev)
@@ -266,12 +273,18 @@ class MedusaDecoder:
         return logits, hN
 
     def _heads(self, h_rows):
+        """The first K heads (K = the tree's depth) on the rows: per-chunk
+        top-k lists for the fused step, merged top-k lists otherwise."""
         if self.K == 0:
             return
         t = self.m.t
-        M.medusa_heads(h_rows, t["w1"], t["b1"], t["w2"], self.width, logits=None,
-                       ids=self.topk_ids, vals=self.topk_vals, ws=self.heads_ws,
-                       want_logits=False)
+        w1, b1, w2 = t["w1"][:self.K], t["b1"][:self.K], t["w2"][:self.K]
+        if self.fused:
+            M.medusa_heads_lists(h_rows, w1, b1, w2, self.width, ids=self.list_ids,
+                                 vals=self.list_vals, ws=self.heads_ws)
+        else:
+            M.medusa_heads(h_rows, w1, b1, w2, self.width, logits=None, ids=self.topk_ids,
+                           vals=self.topk_vals, ws=self.heads_ws, want_logits=False)
 
     def _set_ctx(self, c):
         self.ctx.fill_(int(c))
@@ -311,8 +324,8 @@ class MedusaDecoder:
         (accept_len [B], path [B,K+1], tokens [B,N]) tensors."""
         if self.fused:
             tokens, pos, mask, x, h = M.medusa_tree_embed(
-                self.parent, self.rank, self.root, self.topk_ids, self.ctx, self.m.t["embed"],
-                self.m.t["layers"][0]["g_attn"], self.m.eps)
+                self.parent, self.rank, self.root, self.list_ids, self.ctx, self.m.t["embed"],
+                self.m.t["layers"][0]["g_attn"], self.m.eps, topk_vals=self.list_vals)
             logits, hN = self._layers(x, h, pos, mask)
             acc, path, nxt, hbest = M.medusa_decode_tail(
                 logits.view(self.B, self.N, -1), tokens, self.parent, self.K,

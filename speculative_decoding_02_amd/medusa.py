@@ -34,6 +34,8 @@ _SIGS = {
     "medusa_heads_ws": (sz, [i64, i64, i32, i64, i32, i32]),
     "medusa_heads": (i32, [vp, i64, i64, i32, vp, vp, vp, i64, i32, vp, i32, vp, vp, vp, sz, vp]),
     "medusa_topk_ws": (sz, [i64, i64, i32]),
+    "medusa_topk_lists": (i32, [i64]),
+    "medusa_heads_lists": (i32, [vp, i64, i64, i32, vp, vp, vp, i64, i32, i32, vp, vp, vp, sz, vp]),
     "medusa_topk": (i32, [vp, i64, i64, i32, vp, vp, vp, sz, vp]),
     "medusa_build_tree": (i32, [i32, i32, vp, vp, vp, vp, i32, i32, vp, vp, vp, vp, vp]),
     "medusa_tree_attention_ws": (sz, [i32, i32, i32, i32, i32, i32, i32]),
@@ -58,8 +60,8 @@ _SIGS = {
     "medusa_qkv_rope": (i32, [vp, i64, i32, i32, i32, vp, f32, i32, vp, vp, vp, vp]),
     "medusa_swiglu": (i32, [vp, i64, i64, i32, vp, vp]),
     "medusa_gather_rows": (i32, [vp, i32, i32, i64, vp, vp, i32, i32, vp, vp]),
-    "medusa_tree_embed": (i32, [i32, i32, vp, vp, vp, vp, i32, i32, vp, vp, vp, vp, vp, i64, i64,
-                                i32, vp, f32, vp, vp, vp]),
+    "medusa_tree_embed": (i32, [i32, i32, vp, vp, vp, vp, vp, i32, i32, i32, vp, vp, vp, vp, vp,
+                                i64, i64, i32, vp, f32, vp, vp, vp]),
     "medusa_decode_tail_ws": (sz, [i32, i32]),
     "medusa_decode_tail": (i32, [vp, i64, vp, vp, i32, i32, i32, i32, f32, f32, f32, vp,
                                  C.POINTER(vp), C.POINTER(vp), i32, vp, i32, i32, i32, i32, i32,
@@ -204,6 +206,30 @@ def medusa_heads(X, W1, b1, W2, topk=0, logits=None, ids=None, vals=None, ws=Non
         _p(X), M, H, K, _p(W1), _p(b1), _p(W2), V, dt, _p(logits), topk,
         _p(ids) if topk else None, _p(vals) if topk else None, _p(ws), ws.numel(), _stream()))
     return logits, ids[..., :topk], vals[..., :topk]
+
+
+def medusa_heads_lists(X, W1, b1, W2, topk, ids=None, vals=None, ws=None):
+    """Per-chunk top-k lists of the K heads' logits on X [M, H]: ids [K, M, S,
+    topk] int32 and vals [K, M, S, topk] float, S = medusa_topk_lists(V)."""
+    dt = _dt(X)
+    K, H = W1.shape[0], W1.shape[1]
+    V = W2.shape[1]
+    M = X.shape[0]
+    S = _lib.medusa_topk_lists(V)
+    dev = X.device
+    if ids is None:
+        ids = torch.empty((K, M, S, topk), dtype=torch.int32, device=dev)
+    if vals is None:
+        vals = torch.empty((K, M, S, topk), dtype=torch.float32, device=dev)
+    if tuple(ids.shape) != (K, M, S, topk) or tuple(vals.shape) != (K, M, S, topk):
+        raise ValueError(f"lists must be [K, M, S, topk] = {(K, M, S, topk)}")
+    need = _lib.medusa_heads_ws(M, H, K, V, topk, dt)
+    if ws is None or ws.numel() < need:
+        ws = _ws(need, dev)
+    _check("medusa_heads_lists", _lib.medusa_heads_lists(
+        _p(X), M, H, K, _p(W1), _p(b1), _p(W2), V, dt, topk, _p(ids), _p(vals), _p(ws),
+        ws.numel(), _stream()))
+    return ids, vals
 
 
 def medusa_topk(logits, k, ids=None, vals=None, ws=None):
@@ -463,11 +489,18 @@ def medusa_decode_tail(logits, tokens, parent, K, mode, Kc_list, Vc_list, page_t
     return acc, path, nxt, h_best
 
 
-def medusa_tree_embed(parent, rank, root_tok, topk_ids, ctx, table, gain, eps, out=None):
+def medusa_tree_embed(parent, rank, root_tok, topk_ids, ctx, table, gain, eps, out=None,
+                      topk_vals=None):
     """medusa_build_tree + medusa_embed + medusa_rmsnorm in one launch.
+    ``topk_ids`` [K, B, topk] (the heads' top-k), or per-chunk lists
+    [K, B, S, topk] with their ``topk_vals`` (medusa_heads_lists), merged in
+    the launch.
     Returns (tokens [B,N], pos [B,N], mask [B,N] int64, x [B*N,H] float, h [B*N,H])."""
     B, N = parent.shape
-    K, _, topk = topk_ids.shape
+    if topk_ids.dim() == 4:
+        K, _, lists, topk = topk_ids.shape
+    else:
+        (K, _, topk), lists = topk_ids.shape, 1
     V, H = table.shape
     dev = parent.device
     if out is None:
@@ -478,7 +511,8 @@ def medusa_tree_embed(parent, rank, root_tok, topk_ids, ctx, table, gain, eps, o
                torch.empty((B * N, H), dtype=table.dtype, device=dev))
     tokens, pos, mask, x, h = out
     _check("medusa_tree_embed", _lib.medusa_tree_embed(
-        B, N, _p(parent), _p(rank), _p(root_tok), _p(topk_ids), K, topk, _p(ctx), _p(tokens),
+        B, N, _p(parent), _p(rank), _p(root_tok), _p(topk_ids), _p(topk_vals), lists, K, topk,
+        _p(ctx), _p(tokens),
         _p(pos), _p(mask), _p(table), V, H, _dt(table), _p(gain), float(eps), _p(x), _p(h),
         _stream()))
     return out

@@ -197,6 +197,13 @@ static void check_rejections(void) {
          "heads topk = 65");
   EXPECT(medusa_heads(NULL, 4, 256, 2, NULL, NULL, NULL, 1000, 1, NULL, 4, NULL, NULL, NULL, 0, NULL) ==
              MEDUSA_ERR_INVALID_ARG, "heads NULL operands");
+  EXPECT(medusa_heads_lists(NULL, 4, 256, 2, NULL, NULL, NULL, 1000, 1, 0, NULL, NULL, NULL, 0, NULL) ==
+             MEDUSA_ERR_UNSUPPORTED, "heads lists topk = 0");
+  EXPECT(medusa_heads_lists(NULL, 4, 256, 2, NULL, NULL, NULL, 1000, 1, 4, NULL, NULL, NULL, 0, NULL) ==
+             MEDUSA_ERR_INVALID_ARG, "heads lists NULL operands");
+  for (int64_t v = -2; v <= 3 * 4096 + 2; v += 2047)
+    EXPECT(medusa_topk_lists(v) == (v >= 1 ? (int32_t)((v + 4095) / 4096) : 0), "topk lists V=%lld", (long long)v);
+  EXPECT(medusa_topk_lists(INT64_MAX) == 0, "topk lists huge V");
   /* top-k: k outside [1, min(64, V)], NULL pointers, too small a workspace */
   EXPECT(medusa_topk(NULL, 2, 100, 0, NULL, NULL, NULL, 0, NULL) != MEDUSA_OK, "topk k = 0");
   EXPECT(medusa_topk(NULL, 2, 10, 11, NULL, NULL, NULL, 0, NULL) != MEDUSA_OK, "topk k > V");
@@ -266,12 +273,16 @@ static void check_rejections(void) {
     EXPECT(TAIL(5, 0, 1.f, 128, 256, 0, NULL, 0) == MEDUSA_OK, "tail empty batch");
     EXPECT(TAIL(5, 0, 1.f, 128, 256, 1, NULL, 0) == MEDUSA_ERR_WORKSPACE, "tail workspace");
 #undef TAIL
-    EXPECT(medusa_tree_embed(1, 9, NULL, NULL, NULL, NULL, 2, 3, NULL, NULL, NULL, NULL, NULL, 100, 250, 1, NULL,
-                             1e-5f, NULL, NULL, NULL) == MEDUSA_ERR_UNSUPPORTED, "embed H");
-    EXPECT(medusa_tree_embed(1, 65, NULL, NULL, NULL, NULL, 2, 3, NULL, NULL, NULL, NULL, NULL, 100, 256, 1, NULL,
-                             1e-5f, NULL, NULL, NULL) == MEDUSA_ERR_INVALID_ARG, "embed N");
-    EXPECT(medusa_tree_embed(0, 9, NULL, NULL, NULL, NULL, 2, 3, NULL, NULL, NULL, NULL, NULL, 100, 256, 1, NULL,
-                             1e-5f, NULL, NULL, NULL) == MEDUSA_OK, "embed empty batch");
+    EXPECT(medusa_tree_embed(1, 9, NULL, NULL, NULL, NULL, NULL, 1, 2, 3, NULL, NULL, NULL, NULL, NULL, 100, 250,
+                             1, NULL, 1e-5f, NULL, NULL, NULL) == MEDUSA_ERR_UNSUPPORTED, "embed H");
+    EXPECT(medusa_tree_embed(1, 65, NULL, NULL, NULL, NULL, NULL, 1, 2, 3, NULL, NULL, NULL, NULL, NULL, 100, 256,
+                             1, NULL, 1e-5f, NULL, NULL, NULL) == MEDUSA_ERR_INVALID_ARG, "embed N");
+    EXPECT(medusa_tree_embed(1, 9, NULL, NULL, NULL, NULL, NULL, 0, 2, 3, NULL, NULL, NULL, NULL, NULL, 100, 256,
+                             1, NULL, 1e-5f, NULL, NULL, NULL) == MEDUSA_ERR_INVALID_ARG, "embed lists = 0");
+    EXPECT(medusa_tree_embed(1, 9, NULL, NULL, NULL, NULL, NULL, 65, 2, 3, NULL, NULL, NULL, NULL, NULL, 100, 256,
+                             1, NULL, 1e-5f, NULL, NULL, NULL) == MEDUSA_ERR_INVALID_ARG, "embed lists = 65");
+    EXPECT(medusa_tree_embed(0, 9, NULL, NULL, NULL, NULL, NULL, 1, 2, 3, NULL, NULL, NULL, NULL, NULL, 100, 256,
+                             1, NULL, 1e-5f, NULL, NULL, NULL) == MEDUSA_OK, "embed empty batch");
   }
   EXPECT(strlen(medusa_last_error()) > 0, "a rejection leaves a message");
 }

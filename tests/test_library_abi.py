@@ -97,13 +97,19 @@ def test_bad_arguments_are_rejected_on_the_host(M):
     assert tail(ws=4096, nbytes=need - 1) == 3
     # the fused tree + embedding + norm: H not a multiple of 4, H above 8192,
     # N above 64, an empty batch
-    emb = lambda B=1, N=9, H=256: lib.medusa_tree_embed(B, N, None, None, None, None, 2, 3, None,
-                                                        None, None, None, None, 100, H, 1, None,
-                                                        1e-5, None, None, None)
+    emb = lambda B=1, N=9, H=256, lists=1: lib.medusa_tree_embed(
+        B, N, None, None, None, None, None, lists, 2, 3, None, None, None, None, None, 100, H, 1,
+        None, 1e-5, None, None, None)
     assert emb(H=250) == 2
     assert emb(H=8196) == 2
     assert emb(N=65) == 1
+    assert emb(lists=0) == 1
+    assert emb(lists=65) == 1
     assert emb(B=0) == 0
+    # the per-chunk top-k list count: ceil(V / 4096)
+    assert [lib.medusa_topk_lists(v) for v in (1, 4096, 4097, 32000, 0)] == [1, 1, 2, 8, 0]
+    assert lib.medusa_heads_lists(None, 4, 256, 2, None, None, None, 1000, 1, 0, None, None, None,
+                                  0, None) == 2  # topk below 1
 
 
 def test_workspace_queries_follow_the_plan(M):
