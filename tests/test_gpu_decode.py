@@ -101,6 +101,37 @@ def test_c1_medusa_typical_equals_oracle_typical(c1, T, eps, delta):
         assert pos > 0
 
 
+def test_typical_decoding_with_several_topk_lists_per_head():
+    """A 9000-token vocabulary: each head row's top-k comes as three 4096-wide
+    chunk lists, merged inside the fused step's tree build.  Typical decoding
+    (T 1, epsilon 0.3, delta 0.09) equals the oracle's step by step: the
+    accept lengths depend on every candidate token the merge picks.  Steps
+    after a near-threshold decision are not compared (as above)."""
+    from speculative_decoding_02_amd.decoder import DeviceModel, MedusaDecoder
+    case("typical decoding, vocabulary 9000 (three top-k lists per head row)")
+    m = synth.tiny_decoder(seed=3, vocab=9000)
+    prompt = synth.prompt_tokens(7, 32, m.vocab)
+    parent, rank = synth.tree_template((3, 2, 2))
+    n_new = 40
+    orec = []
+    ref, _, _ = orc.medusa_generate(m, prompt, n_new, parent, rank, mode="typical", record=orec)
+    dec = MedusaDecoder(DeviceModel(m, dtype=torch.float32), parent, rank,
+                        capacity=32 + n_new + 32, mode="typical")
+    assert dec.list_ids.shape[2] == 3
+    rec = []
+    got = dec.generate(prompt, n_new, record=rec)
+    pos, compared = 0, 0
+    for s, r in enumerate(orec):
+        if np.min(np.abs(r["accept"]["margins"][1:])) < 1e-4:
+            break
+        a = r["accept"]["accept_len"]
+        assert rec[s] == a, f"step {s}: accept length {rec[s]} != oracle {a}"
+        end = min(pos + a + 1, n_new)
+        assert got[pos:end].tolist() == ref[pos:end].tolist(), f"step {s}: " + _report(ref, got)
+        pos, compared = end, compared + (a > 0)
+    assert pos >= n_new // 2 and compared > 0
+
+
 def test_c1_graph_replays_match_eager_and_oracle(c1):
     """The decode step recorded once as a HIP graph and replayed step after
     step (with eager host reads and other GPU work in between) emits the same

@@ -416,16 +416,17 @@ def test_tree_embed(lib, dt, H):
         assert_close(host(h)[b * N:(b + 1) * N], orc.rmsnorm(rows, gain, 1e-5), TOL[dt], "tree rows' norm")
 
 
-@pytest.mark.parametrize("dt,V,width", [(torch.bfloat16, 20000, 4), (torch.float32, 9000, 3),
-                                         (torch.bfloat16, 4096, 4), (torch.bfloat16, 12300, 17)])
-def test_tree_embed_from_chunk_lists(lib, dt, V, width):
+@pytest.mark.parametrize("dt,V,width,B", [(torch.bfloat16, 20000, 4, 3), (torch.float32, 9000, 3, 3),
+                                           (torch.bfloat16, 4096, 4, 3), (torch.bfloat16, 12300, 17, 3),
+                                           (torch.bfloat16, 32000, 4, 1)])
+def test_tree_embed_from_chunk_lists(lib, dt, V, width, B):
     """The heads' per-chunk top-k lists (medusa_heads_lists) are each 4096-wide
     chunk's top-k of the heads' logits (the oracle's top-k of that chunk), and
     the fused tree build that merges them in its launch gives the same tokens,
     positions, masks, rows and norms, bit for bit, as the build from the
     merged top-k (medusa_heads + medusa_tree_embed)."""
-    case(f"tree_embed from chunk lists {DTN[dt]} V={V} width={width}")
-    B, N, K, H = 3, 64, 5, 256
+    case(f"tree_embed from chunk lists {DTN[dt]} V={V} width={width} B={B}")
+    N, K, H = 64, 5, 256
     d = synth.heads_inputs(V + width, B, H, V, K, w1_std=0.05, w2_std=0.05, bf16=dt == torch.bfloat16)
     args = tuple(dev(d[k], dt) for k in ("X", "W1", "b1", "W2"))
     S = lib._lib.medusa_topk_lists(V)
@@ -445,10 +446,10 @@ def test_tree_embed_from_chunk_lists(lib, dt, V, width):
     if width > 16:
         return  # trees use lists of at most 16 here; the merge is the same for any width
     tree = (4, 3, 2, 2, 1) if width == 4 else (3, 3, 2, 2, 1)
-    parent, rank = synth.random_template_batch(tree, N, seeds=[7, 8, 9])
+    parent, rank = synth.random_template_batch(tree, N, seeds=[7, 8, 9][:B])
     rng = np.random.default_rng(V)
     root = dev(rng.integers(0, V, size=B).astype(np.int32))
-    ctx = dev(np.array([5, 0, 900], np.int32))
+    ctx = dev(np.array([5, 0, 900][:B], np.int32))
     table = dev(_rnd(dt, rng.standard_normal((V, H)).astype(np.float32)), dt)
     gain = dev(_rnd(dt, 1 + 0.1 * rng.standard_normal(H).astype(np.float32)), dt)
     one = lib.medusa_tree_embed(dev(parent), dev(rank), root, ids, ctx, table, gain, 1e-5)
