@@ -74,17 +74,17 @@ __global__ __launch_bounds__(256) void tree_embed_kernel(
     const uint32_t lo = __shfl((uint32_t)anc, n, 64), hi = __shfl((uint32_t)(anc >> 32), n, 64);
     const uint64_t an = ((uint64_t)hi << 32) | lo;
     const int depth = __popcll(an) - 1;  // the same in every lane
-    const int64_t row = (int64_t)max(depth - 1, 0) * B + b;
+    const int64_t hrow = (int64_t)max(depth - 1, 0) * B + b;  // the heads' row of this node
     int tok = 0;
     if (depth > 0 && lists > 1) {
-      const int64_t c0 = row * lists * topk;
+      const int64_t c0 = hrow * lists * topk;
       const uint64_t top = merge_lists_wave(topk_ids + c0, topk_vals + c0, lists * topk);
       tok = key_index(((uint64_t)__shfl((uint32_t)(top >> 32), rank[o], 64) << 32) |
                       __shfl((uint32_t)top, rank[o], 64));
     }
     if (tid == 0) {
       if (depth == 0) tok = root_tok[b];
-      else if (lists == 1) tok = topk_ids[row * topk + rank[o]];
+      else if (lists == 1) tok = topk_ids[hrow * topk + rank[o]];
       tokens[o] = tok;
       pos[o] = ctx[b] + depth;
       mask[o] = an;
