@@ -519,6 +519,12 @@ def main():
     ap.add_argument("--attn-only", action="store_true",
                     help="run only tree attention at the 7B layer shape (2048 cached tokens) and at "
                          "the decode step's shape, for per-shape kernel traces")
+    ap.add_argument("--config", choices=["c1", "c2", "c3", "c5"],
+                    help="run one configuration's measurement alone and print its JSON object: "
+                         "c1 the tiny fp32 model's 64 greedy tokens, c2 tree attention at the 7B "
+                         "layer (and at the decode step's shape), c3 the five heads + top-10 at 64 "
+                         "and 1024 rows, c5 the ragged 16-sequence 13B attention stack (c4 is the "
+                         "default run)")
     ap.add_argument("--f4-only", action="store_true",
                     help="run only one 7B layer's four projections at 1024 rows (the large-row "
                          "tiling), for kernel traces and counter passes")
@@ -547,6 +553,16 @@ def main():
     if args.kernels_only:
         kernels_only(torch, M, synth, log)
         return
+    if args.config == "c1":
+        print(json.dumps({"c1_tiny_fp32": c1_generation(torch, synth)}))
+        return
+    if args.config == "c5":
+        print(json.dumps({"batched_attention_c5": batched_attention_c5(torch, M, synth)}))
+        return
+    if args.config == "c3":
+        args.heads_only = True
+    if args.config == "c2":
+        args.attn_only = True
     if args.heads_only:
         print(json.dumps({"heads_c3": heads_c3(torch, M, 64), "heads_c3b": heads_c3(torch, M, 1024)}))
         return
