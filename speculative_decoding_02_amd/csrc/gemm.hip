@@ -921,7 +921,7 @@ struct GemmPlan {
   int xb_G;     // workgroups per (batch element, row tile, contraction split)
   int MT;       // activation-row tiles
   int xb_S;     // contraction splits of the block-range variant (partials when > 1)
-  int big;      // large-row MFMA tiling: 0 off, 1 = 256 x 256 tiles, 2 = 128 x 128 tiles
+  int big;      // large-row MFMA tiling (1; 0 off)
 };
 #ifndef MEDUSA_GEMM_XB_MIN_BLOCKS
 #define MEDUSA_GEMM_XB_MIN_BLOCKS 512
@@ -961,17 +961,18 @@ struct GemmPlan {
 #ifndef MEDUSA_GEMM_BIG_R2
 #define MEDUSA_GEMM_BIG_R2 3
 #endif
+#ifndef MEDUSA_GEMM_BIG_R3
+#define MEDUSA_GEMM_BIG_R3 2
+#endif
 GemmPlan gemm_plan(int64_t M, int64_t Kd, int64_t Nw, int dt, int epi) {
   using namespace medusa;
   constexpr int XNB = MEDUSA_GEMM_XL_NB;
   GemmPlan p{false, 1, false, 1, 0, 1, 1, 0};
   const int unit = epi == MEDUSA_EPI_SWIGLU ? 2 : 1;
-  // enough rows for the product to be MFMA-bound: square tiles, 256 wide when
-  // they alone give about one workgroup per compute unit
+  // enough rows for the product to be MFMA-bound: the large-row tilings
   if (dt == MEDUSA_BF16 && M >= MEDUSA_GEMM_BIG_MIN_M && Kd % GB_KALIGN == 0 && Nw % (16 * unit) == 0 &&
       Nw <= INT32_MAX / 2) {
-    const int64_t t256 = ((Nw + 255) / 256) * ((M + 255) / 256);
-    p.big = t256 >= 200 ? 1 : 2;
+    p.big = 1;  // the launch picks the tiling, the batch counted (big_tiling)
     return p;
   }
   const bool narrow = Nw / 16 >= MEDUSA_GEMM_XD_MIN_BLOCKS;
@@ -1005,6 +1006,28 @@ GemmPlan gemm_plan(int64_t M, int64_t Kd, int64_t Nw, int dt, int epi) {
   ks = std::min<int64_t>(ks, 8);
   p.ksplit = (int)std::max<int64_t>(ks, 1);
   return p;
+}
+
+// Tiling of the large-row plan for M rows x Nw outputs x batch: 1 = 256 x 256
+// tiles (8 waves of 128 x 64), 3 = 128 weight rows x 256 activation rows (8
+// waves of 64 x 64), 2 = 128 x 128 (4 waves of 64 x 64).  Per unit of work the
+// 256-wide tiles are the fastest (measured at 1024 rows: ≈ 1.4x the 128 x 256
+// tiles and ≈ 1.6x the 128 x 128 ones), so they are taken when their last
+// round over the 256 compute units is at least three quarters full or there
+// are many rounds; otherwise the 128 x 256 tiles when they fill at least one
+// round, else 128 x 128.  At 1024 rows: QKV (-> 12288) 136 -> 112 us with the
+// 256-wide tiles, gate/up (-> 2 x 11008) 221 -> 212 us and the five heads' W1
+// stage 283 -> 239 us with the 128 x 256 tiles; O and down keep 128 x 128.  All
+// three run the contraction in the same order, so the choice changes no bit
+// of the result and may count the tiles of every batch element.
+int big_tiling(int64_t M, int64_t Nw, int batch) {
+  constexpr int64_t CUS = 256;
+  const int64_t t1 = ((Nw + 255) / 256) * ((M + 255) / 256) * batch;
+  const int64_t t3 = ((Nw + 127) / 128) * ((M + 255) / 256) * batch;
+  const int64_t last1 = t1 - (t1 - 1) / CUS * CUS;  // tiles in the last round
+  if (4 * last1 >= 3 * CUS || t1 >= 8 * CUS) return 1;
+  if (t3 >= CUS) return 3;
+  return 2;
 }
 size_t gemm_ws_bytes(int64_t M, int64_t Kd, int64_t Nw, int batch, int dt) {
   // the larger of the two plan families (SwiGLU plans in gate/up pairs);
@@ -1058,12 +1081,17 @@ static bool launch_gemm_t(const void* X, int64_t xbs, int64_t M, int64_t Kd, con
       // Both tilings run the contraction in the same order (64-deep stages,
       // two 32-deep MFMA steps each), so their results are bit-identical and
       // the choice may count the tiles of every batch element.
-      const int64_t t256 = ((Nw + 255) / 256) * ((M + 255) / 256) * batch;
-      if (plan.big == 1 || t256 >= 200) {
+      const int tiling = medusa_host::big_tiling(M, Nw, batch);
+      if (tiling == 1) {
         const int tN = (int)((Nw + 255) / 256), tM = (int)((M + 255) / 256);
         hipLaunchKernelGGL((gemm_big_kernel<256, 256, 2, MEDUSA_GEMM_BIG_WM1, MEDUSA_GEMM_BIG_BK1, MEDUSA_GEMM_BIG_R1, EPI>),
                            dim3((unsigned)(tN * tM), (unsigned)batch),
                            dim3(128 * MEDUSA_GEMM_BIG_WM1), 0, st, Xt, xbs, (int)M, (int)Kd, Wt, (int)Nw, Bt, aux, Y, y_f32, tN, tM);
+      } else if (tiling == 3) {
+        const int tN = (int)((Nw + 127) / 128), tM = (int)((M + 255) / 256);
+        hipLaunchKernelGGL((gemm_big_kernel<128, 256, 2, 4, 64, MEDUSA_GEMM_BIG_R3, EPI>),
+                           dim3((unsigned)(tN * tM), (unsigned)batch),
+                           dim3(512), 0, st, Xt, xbs, (int)M, (int)Kd, Wt, (int)Nw, Bt, aux, Y, y_f32, tN, tM);
       } else {
         const int tN = (int)((Nw + 127) / 128), tM = (int)((M + 127) / 128);
         hipLaunchKernelGGL((gemm_big_kernel<128, 128, 2, 2, MEDUSA_GEMM_BIG_BK2, MEDUSA_GEMM_BIG_R2, EPI>),
