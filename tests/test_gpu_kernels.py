@@ -418,7 +418,7 @@ def test_tree_embed(lib, dt, H):
 
 @pytest.mark.parametrize("dt,V,width,B", [(torch.bfloat16, 20000, 4, 3), (torch.float32, 9000, 3, 3),
                                            (torch.bfloat16, 4096, 4, 3), (torch.bfloat16, 12300, 17, 3),
-                                           (torch.bfloat16, 32000, 4, 1)])
+                                           (torch.bfloat16, 32000, 4, 1), (torch.bfloat16, 9000, 1, 2)])
 def test_tree_embed_from_chunk_lists(lib, dt, V, width, B):
     """The heads' per-chunk top-k lists (medusa_heads_lists) are each 4096-wide
     chunk's top-k of the heads' logits (the oracle's top-k of that chunk), and
@@ -445,8 +445,9 @@ def test_tree_embed_from_chunk_lists(lib, dt, V, width, B):
                 assert np.array_equal(lv[kk, m, c, :n], ov)
     if width > 16:
         return  # trees use lists of at most 16 here; the merge is the same for any width
-    tree = (4, 3, 2, 2, 1) if width == 4 else (3, 3, 2, 2, 1)
+    tree = {4: (4, 3, 2, 2, 1), 3: (3, 3, 2, 2, 1), 1: (1, 1, 1, 1, 1)}[width]
     parent, rank = synth.random_template_batch(tree, N, seeds=[7, 8, 9][:B])
+    N = parent.shape[1]
     rng = np.random.default_rng(V)
     root = dev(rng.integers(0, V, size=B).astype(np.int32))
     ctx = dev(np.array([5, 0, 900][:B], np.int32))
@@ -481,6 +482,9 @@ ATT_CASES = [
     (2, 37, 3, 3, 64, [2500, 7], 8, True, torch.bfloat16),
     (2, 64, 8, 2, 128, [2300, 130], 24, True, torch.bfloat16),
     (1, 20, 4, 4, 64, 2200, 12, False, torch.bfloat16),
+    # bf16 with an empty cache (only the tree's keys) and a single-node tree
+    (1, 64, 8, 8, 64, 0, 16, False, torch.bfloat16),
+    (2, 1, 4, 4, 128, [0, 77], 16, True, torch.bfloat16),
 ]
 
 
