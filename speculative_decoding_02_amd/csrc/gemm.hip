@@ -964,6 +964,7 @@ struct GemmPlan {
 #ifndef MEDUSA_GEMM_BIG_R3
 #define MEDUSA_GEMM_BIG_R3 2
 #endif
+
 GemmPlan gemm_plan(int64_t M, int64_t Kd, int64_t Nw, int dt, int epi) {
   using namespace medusa;
   constexpr int XNB = MEDUSA_GEMM_XL_NB;
@@ -1010,7 +1011,8 @@ GemmPlan gemm_plan(int64_t M, int64_t Kd, int64_t Nw, int dt, int epi) {
 
 // Tiling of the large-row plan for M rows x Nw outputs x batch: 1 = 256 x 256
 // tiles (8 waves of 128 x 64), 3 = 128 weight rows x 256 activation rows (8
-// waves of 64 x 64), 2 = 128 x 128 (4 waves of 64 x 64).  Per unit of work the
+// waves of 64 x 64), 2 = 128 x 128 (8 waves of 64 x 32; with 4 waves of
+// 64 x 64 the O and down projections at 1024 rows measured 4-5% slower).  Per unit of work the
 // 256-wide tiles are the fastest (measured at 1024 rows: ≈ 1.4x the 128 x 256
 // tiles and ≈ 1.6x the 128 x 128 ones), so they are taken when their last
 // round over the 256 compute units is at least three quarters full or there
@@ -1094,9 +1096,9 @@ static bool launch_gemm_t(const void* X, int64_t xbs, int64_t M, int64_t Kd, con
                            dim3(512), 0, st, Xt, xbs, (int)M, (int)Kd, Wt, (int)Nw, Bt, aux, Y, y_f32, tN, tM);
       } else {
         const int tN = (int)((Nw + 127) / 128), tM = (int)((M + 127) / 128);
-        hipLaunchKernelGGL((gemm_big_kernel<128, 128, 2, 2, MEDUSA_GEMM_BIG_BK2, MEDUSA_GEMM_BIG_R2, EPI>),
+        hipLaunchKernelGGL((gemm_big_kernel<128, 128, 2, 4, MEDUSA_GEMM_BIG_BK2, MEDUSA_GEMM_BIG_R2, EPI>),
                            dim3((unsigned)(tN * tM), (unsigned)batch),
-                           dim3(256), 0, st, Xt, xbs, (int)M, (int)Kd, Wt, (int)Nw, Bt, aux, Y, y_f32, tN, tM);
+                           dim3(512), 0, st, Xt, xbs, (int)M, (int)Kd, Wt, (int)Nw, Bt, aux, Y, y_f32, tN, tM);
       }
       return false;
     }
