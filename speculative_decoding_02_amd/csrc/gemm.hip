@@ -950,7 +950,7 @@ struct GemmPlan {
 #define MEDUSA_GEMM_BIG_BK1 64
 #endif
 #ifndef MEDUSA_GEMM_BIG_WM1
-#define MEDUSA_GEMM_BIG_WM1 4  // waves along the activation rows of a 256-wide tile (x 2 along the weight rows)
+#define MEDUSA_GEMM_BIG_WM1 8  // waves along the activation rows of a 256-wide tile (x 2 along the weight rows)
 #endif
 #ifndef MEDUSA_GEMM_BIG_R1
 #define MEDUSA_GEMM_BIG_R1 2
@@ -963,6 +963,12 @@ struct GemmPlan {
 #endif
 #ifndef MEDUSA_GEMM_BIG_R3
 #define MEDUSA_GEMM_BIG_R3 2
+#endif
+#ifndef MEDUSA_GEMM_BIG_WM2
+#define MEDUSA_GEMM_BIG_WM2 4  // waves along the activation rows of a 128 x 128 tile (x 2 along the weight rows)
+#endif
+#ifndef MEDUSA_GEMM_BIG_WM3
+#define MEDUSA_GEMM_BIG_WM3 8  // the same for 128 weight rows x 256 activation rows
 #endif
 
 GemmPlan gemm_plan(int64_t M, int64_t Kd, int64_t Nw, int dt, int epi) {
@@ -1010,9 +1016,12 @@ GemmPlan gemm_plan(int64_t M, int64_t Kd, int64_t Nw, int dt, int epi) {
 }
 
 // Tiling of the large-row plan for M rows x Nw outputs x batch: 1 = 256 x 256
-// tiles (8 waves of 128 x 64), 3 = 128 weight rows x 256 activation rows (8
-// waves of 64 x 64), 2 = 128 x 128 (8 waves of 64 x 32; with 4 waves of
-// 64 x 64 the O and down projections at 1024 rows measured 4-5% slower).  Per unit of work the
+// tiles (16 waves of 128 x 32), 3 = 128 weight rows x 256 activation rows (16
+// waves of 64 x 32), 2 = 128 x 128 (8 waves of 64 x 32).  Four waves per SIMD
+// hide the operand reads' latency better than two (at 1024 rows: QKV 114.5
+// -> 108 us, gate/up 212 -> 204 us, the heads' W2 stage -2.5%); the 128 x 128
+// tiles gain nothing from 16 waves, and with 4 waves the O and down
+// projections measured 4-5% slower.  Per unit of work the
 // 256-wide tiles are the fastest (measured at 1024 rows: ≈ 1.4x the 128 x 256
 // tiles and ≈ 1.6x the 128 x 128 ones), so they are taken when their last
 // round over the 256 compute units is at least three quarters full or there
@@ -1091,14 +1100,14 @@ static bool launch_gemm_t(const void* X, int64_t xbs, int64_t M, int64_t Kd, con
                            dim3(128 * MEDUSA_GEMM_BIG_WM1), 0, st, Xt, xbs, (int)M, (int)Kd, Wt, (int)Nw, Bt, aux, Y, y_f32, tN, tM);
       } else if (tiling == 3) {
         const int tN = (int)((Nw + 127) / 128), tM = (int)((M + 255) / 256);
-        hipLaunchKernelGGL((gemm_big_kernel<128, 256, 2, 4, 64, MEDUSA_GEMM_BIG_R3, EPI>),
+        hipLaunchKernelGGL((gemm_big_kernel<128, 256, 2, MEDUSA_GEMM_BIG_WM3, 64, MEDUSA_GEMM_BIG_R3, EPI>),
                            dim3((unsigned)(tN * tM), (unsigned)batch),
-                           dim3(512), 0, st, Xt, xbs, (int)M, (int)Kd, Wt, (int)Nw, Bt, aux, Y, y_f32, tN, tM);
+                           dim3(128 * MEDUSA_GEMM_BIG_WM3), 0, st, Xt, xbs, (int)M, (int)Kd, Wt, (int)Nw, Bt, aux, Y, y_f32, tN, tM);
       } else {
         const int tN = (int)((Nw + 127) / 128), tM = (int)((M + 127) / 128);
-        hipLaunchKernelGGL((gemm_big_kernel<128, 128, 2, 4, MEDUSA_GEMM_BIG_BK2, MEDUSA_GEMM_BIG_R2, EPI>),
+        hipLaunchKernelGGL((gemm_big_kernel<128, 128, 2, MEDUSA_GEMM_BIG_WM2, MEDUSA_GEMM_BIG_BK2, MEDUSA_GEMM_BIG_R2, EPI>),
                            dim3((unsigned)(tN * tM), (unsigned)batch),
-                           dim3(512), 0, st, Xt, xbs, (int)M, (int)Kd, Wt, (int)Nw, Bt, aux, Y, y_f32, tN, tM);
+                           dim3(128 * MEDUSA_GEMM_BIG_WM2), 0, st, Xt, xbs, (int)M, (int)Kd, Wt, (int)Nw, Bt, aux, Y, y_f32, tN, tM);
       }
       return false;
     }
