@@ -439,7 +439,7 @@ template <int MB, int WR, int EPI>
 __global__ __launch_bounds__(64 * XB_WAVES) void gemm_xdma_kernel(
     const bf16_t* __restrict__ X, int64_t xbs, int M, int Kd, const bf16_t* __restrict__ W, int Nw,
     const bf16_t* __restrict__ bias, const void* aux, void* Y, int y_f32, int G, int MT, int unit,
-    float* __restrict__ part, RopeArgs ra) {
+    float* __restrict__ part, int nsub, RopeArgs ra) {
   using T = bf16_t;
   constexpr int P16 = 8;                        // bf16 per 16 bytes
   constexpr int TM = 16 * MB;
@@ -619,10 +619,19 @@ __global__ __launch_bounds__(64 * XB_WAVES) void gemm_xdma_kernel(
     }
     return;
   }
+  // nsub < Nw: a batch sharing its activation rows planned as one projection
+  // onto its stacked weights; output column n is column n % nsub of element n / nsub
   const int nn = nb * 16;
-  for (int e = threadIdx.x; e < nn * TM; e += NT) {
-    const int m = e / nn, nl = e % nn;
-    if (m0 + m < M) xb_store<T, EPI>(gi, M, Nw, xbs, bias, aux, Y, y_f32, m0 + m, b0 * 16 + nl, ep[nl * LDE + m]);
+  if (nsub == Nw) {
+    for (int e = threadIdx.x; e < nn * TM; e += NT) {
+      const int m = e / nn, nl = e % nn;
+      if (m0 + m < M) xb_store<T, EPI>(gi, M, Nw, xbs, bias, aux, Y, y_f32, m0 + m, b0 * 16 + nl, ep[nl * LDE + m]);
+    }
+  } else {
+    for (int e = threadIdx.x; e < nn * TM; e += NT) {
+      const int m = e / nn, nl = e % nn, n = b0 * 16 + nl;
+      if (m0 + m < M) xb_store<T, EPI>(n / nsub, M, nsub, xbs, bias, aux, Y, y_f32, m0 + m, n % nsub, ep[nl * LDE + m]);
+    }
   }
 }
 
@@ -1083,7 +1092,24 @@ static bool launch_gemm_t(const void* X, int64_t xbs, int64_t M, int64_t Kd, con
   constexpr int KS = MEDUSA_GEMM_KS;
   constexpr int TN = 16 * NB;
   constexpr int XNB = MEDUSA_GEMM_XL_NB;
-  const medusa_host::GemmPlan plan = medusa_host::gemm_plan(M, Kd, Nw, sizeof(T) == 2 ? MEDUSA_BF16 : MEDUSA_F32, EPI);
+  constexpr int DT = sizeof(T) == 2 ? MEDUSA_BF16 : MEDUSA_F32;
+  medusa_host::GemmPlan plan = medusa_host::gemm_plan(M, Kd, Nw, DT, EPI);
+  // A batch that shares its activation rows (xbs == 0) is one projection onto
+  // its stacked weights [batch * Nw, Kd].  It is planned that way when each
+  // element alone would split the contraction (the heads' first layer at
+  // 64 rows: five 4096-wide outputs), so that every compute unit streams
+  // whole blocks over the full contraction and no reduce launch follows.
+  int64_t Nf = Nw;  // output columns of the launch
+  int bf = batch;   // batch elements of the launch
+  if ((EPI == MEDUSA_EPI_NONE || EPI == MEDUSA_EPI_BIAS_SILU_RES) && batch > 1 && xbs == 0 && !norm &&
+      plan.xb && plan.xb_S > 1 && Nw * batch <= INT32_MAX / 2) {
+    const medusa_host::GemmPlan pf = medusa_host::gemm_plan(M, Kd, Nw * batch, DT, EPI);
+    if (pf.xb && pf.xb_S == 1) {
+      plan = pf;
+      Nf = Nw * batch;
+      bf = 1;
+    }
+  }
   if constexpr (sizeof(T) == 2) {  // planned for bf16 only
     if (plan.big) {
       const T* Xt = reinterpret_cast<const T*>(X);
@@ -1112,17 +1138,19 @@ static bool launch_gemm_t(const void* X, int64_t xbs, int64_t M, int64_t Kd, con
       return false;
     }
     if (plan.xb) {
-      const dim3 grid((unsigned)plan.xb_G, (unsigned)(batch * plan.MT), (unsigned)plan.xb_S);
+      const dim3 grid((unsigned)plan.xb_G, (unsigned)(bf * plan.MT), (unsigned)plan.xb_S);
       const T* Xt = reinterpret_cast<const T*>(X);
       const T* Wt = reinterpret_cast<const T*>(W);
       const T* Bt = reinterpret_cast<const T*>(bias);
       float* part = reinterpret_cast<float*>(ws);
       if (M <= 32)
         hipLaunchKernelGGL((gemm_xdma_kernel<2, MEDUSA_GEMM_XD_WR, EPI>), grid, dim3(64 * XB_WAVES), 0, st, Xt, xbs,
-                           (int)M, (int)Kd, Wt, (int)Nw, Bt, aux, Y, y_f32, plan.xb_G, plan.MT, plan.xb_unit, part, RopeArgs{});
+                           (int)M, (int)Kd, Wt, (int)Nf, Bt, aux, Y, y_f32, plan.xb_G, plan.MT, plan.xb_unit, part,
+                           (int)Nw, RopeArgs{});
       else
         hipLaunchKernelGGL((gemm_xdma_kernel<4, MEDUSA_GEMM_XD_WR, EPI>), grid, dim3(64 * XB_WAVES), 0, st, Xt, xbs,
-                           (int)M, (int)Kd, Wt, (int)Nw, Bt, aux, Y, y_f32, plan.xb_G, plan.MT, plan.xb_unit, part, RopeArgs{});
+                           (int)M, (int)Kd, Wt, (int)Nf, Bt, aux, Y, y_f32, plan.xb_G, plan.MT, plan.xb_unit, part,
+                           (int)Nw, RopeArgs{});
       if (plan.xb_S > 1) {
         if (EPI == MEDUSA_EPI_RES_ADD_F32 && norm) {
           launch_split_reduce_rmsnorm<T>(part, plan.xb_S, M, Nw, Y, norm, st);
@@ -1345,11 +1373,11 @@ extern "C" int32_t medusa_linear_qkv_rope(const void* X, int64_t M, int64_t Kd, 
     if (M <= 32)
       hipLaunchKernelGGL((gemm_xdma_kernel<2, MEDUSA_GEMM_XD_WR, EPI_ROPE_QKV>), grid, dim3(64 * XB_WAVES), 0, st,
                          Xt, (int64_t)0, (int)M, (int)Kd, Wt, (int)N, (const bf16_t*)nullptr, nullptr, nullptr, 0,
-                         plan.xb_G, plan.MT, 1, (float*)nullptr, ra);
+                         plan.xb_G, plan.MT, 1, (float*)nullptr, (int)N, ra);
     else
       hipLaunchKernelGGL((gemm_xdma_kernel<4, MEDUSA_GEMM_XD_WR, EPI_ROPE_QKV>), grid, dim3(64 * XB_WAVES), 0, st,
                          Xt, (int64_t)0, (int)M, (int)Kd, Wt, (int)N, (const bf16_t*)nullptr, nullptr, nullptr, 0,
-                         plan.xb_G, plan.MT, 1, (float*)nullptr, ra);
+                         plan.xb_G, plan.MT, 1, (float*)nullptr, (int)N, ra);
     return check_launch("medusa_linear_qkv_rope");
   }
   // projection into scratch (pair layout), then the rotary pass over it

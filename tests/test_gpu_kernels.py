@@ -106,6 +106,34 @@ def test_linear_epilogues(lib, dt):
         assert_close_stored(host(U5[k]), orc.head_hidden(X5, W5[k], b5[k]), TOL[dt], f"bias_silu_res H=4096 head {k}", dt)
 
 
+# A batch sharing its activation rows, whose elements alone would each split
+# the contraction, is planned as one projection onto the stacked weights
+# (whole blocks over the full contraction); its output columns are mapped
+# back to [batch, M, N].  Block ranges cross element boundaries when N/16 is
+# not a multiple of the per-workgroup share (N = 2064: 129 blocks each).
+@pytest.mark.parametrize("Mr,Kd,N,batch,epi", [(64, 4096, 2064, 4, "none"), (40, 4096, 4096, 3, "bias_silu_res"),
+                                               (64, 6144, 2048, 4, "none"), (17, 4096, 4096, 5, "bias_silu_res"),
+                                               (64, 4096, 4096, 5, "bias_silu_res")])
+def test_linear_shared_rows_batch(lib, Mr, Kd, N, batch, epi):
+    case(f"linear shared rows M={Mr} Kd={Kd} N={N} batch={batch} {epi}")
+    bf = torch.bfloat16
+    g = synth.rngs(Mr + Kd + N + batch, 3)
+    X = _rnd(bf, g[0].standard_normal((Mr, Kd), dtype=np.float32))
+    W = _rnd(bf, g[1].standard_normal((batch, N, Kd), dtype=np.float32) * 0.02)
+    if epi == "none":
+        y = lib.medusa_linear(dev(X, bf), dev(W, bf), lib.EPI_NONE, y_f32=True)
+        yb = lib.medusa_linear(dev(X, bf), dev(W, bf), lib.EPI_NONE)
+        for k in range(batch):
+            ref = orc.linear(X, W[k])
+            assert_close(host(y[k]), ref, TOL[torch.float32], f"element {k} (fp32 out)")
+            assert_close_stored(host(yb[k]), ref, TOL[bf], f"element {k} (bf16 out)", bf)
+    else:
+        b = _rnd(bf, g[2].standard_normal((batch, N), dtype=np.float32) * 0.1)
+        U = lib.medusa_linear(dev(X, bf), dev(W, bf), lib.EPI_BIAS_SILU_RES, bias=dev(b, bf), aux=dev(X, bf))
+        for k in range(batch):
+            assert_close_stored(host(U[k]), orc.head_hidden(X, W[k], b[k]), TOL[bf], f"head {k}", bf)
+
+
 # Large-row projections (M >= 256, bf16): MFMA-bound tiling, 128-wide tiles
 # when 256-wide ones would leave the chip under-filled; ragged rows/columns.
 @pytest.mark.parametrize("Mr,Kd,N", [(256, 256, 4096), (300, 512, 1040), (1024, 256, 12800),
