@@ -979,6 +979,15 @@ struct GemmPlan {
 #ifndef MEDUSA_GEMM_BIG_WM3
 #define MEDUSA_GEMM_BIG_WM3 8  // the same for 128 weight rows x 256 activation rows
 #endif
+#ifndef MEDUSA_GEMM_BIG_WM4
+#define MEDUSA_GEMM_BIG_WM4 4  // the same for 192 weight rows x 256 activation rows
+#endif
+#ifndef MEDUSA_GEMM_BIG_R4
+#define MEDUSA_GEMM_BIG_R4 2
+#endif
+#ifndef MEDUSA_GEMM_BIG_WN4
+#define MEDUSA_GEMM_BIG_WN4 2  // waves along the weight rows of a 192-row tile
+#endif
 
 GemmPlan gemm_plan(int64_t M, int64_t Kd, int64_t Nw, int dt, int epi) {
   using namespace medusa;
@@ -1041,13 +1050,30 @@ GemmPlan gemm_plan(int64_t M, int64_t Kd, int64_t Nw, int dt, int epi) {
 // three run the contraction in the same order, so the choice changes no bit
 // of the result and may count the tiles of every batch element.
 int big_tiling(int64_t M, int64_t Nw, int batch) {
+#ifdef MEDUSA_GEMM_BIG_FORCE
+  return MEDUSA_GEMM_BIG_FORCE;  // one tiling for every shape (to time the tilings against each other)
+#endif
+  // Estimated time = rounds of tiles over the compute units x the time of
+  // one round of that tile shape (a round of partly idle units costs about
+  // as much as a full one).  Round costs relative to the 256 x 256 tiles,
+  // measured at 1024 rows x 4096 (gate/up, QKV, the heads): 192 x 256: 0.92,
+  // 128 x 256: 0.667, 128 x 128: 0.40.  Ties go to the larger tiles.
   constexpr int64_t CUS = 256;
-  const int64_t t1 = ((Nw + 255) / 256) * ((M + 255) / 256) * batch;
-  const int64_t t3 = ((Nw + 127) / 128) * ((M + 255) / 256) * batch;
-  const int64_t last1 = t1 - (t1 - 1) / CUS * CUS;  // tiles in the last round
-  if (4 * last1 >= 3 * CUS || t1 >= 8 * CUS) return 1;
-  if (t3 >= CUS) return 3;
-  return 2;
+  struct Tiling {
+    int id, tn, tm, cost;
+  };
+  constexpr Tiling cand[4] = {{1, 256, 256, 1000}, {4, 192, 256, 920}, {3, 128, 256, 667}, {2, 128, 128, 400}};
+  int best = 1;
+  int64_t best_t = -1;
+  for (const Tiling& c : cand) {
+    const int64_t tiles = ((Nw + c.tn - 1) / c.tn) * ((M + c.tm - 1) / c.tm) * batch;
+    const int64_t t = (tiles + CUS - 1) / CUS * c.cost;
+    if (best_t < 0 || t < best_t) {
+      best = c.id;
+      best_t = t;
+    }
+  }
+  return best;
 }
 size_t gemm_ws_bytes(int64_t M, int64_t Kd, int64_t Nw, int batch, int dt) {
   // the larger of the two plan families (SwiGLU plans in gate/up pairs);
@@ -1124,6 +1150,11 @@ static bool launch_gemm_t(const void* X, int64_t xbs, int64_t M, int64_t Kd, con
         hipLaunchKernelGGL((gemm_big_kernel<256, 256, 2, MEDUSA_GEMM_BIG_WM1, MEDUSA_GEMM_BIG_BK1, MEDUSA_GEMM_BIG_R1, EPI>),
                            dim3((unsigned)(tN * tM), (unsigned)batch),
                            dim3(128 * MEDUSA_GEMM_BIG_WM1), 0, st, Xt, xbs, (int)M, (int)Kd, Wt, (int)Nw, Bt, aux, Y, y_f32, tN, tM);
+      } else if (tiling == 4) {
+        const int tN = (int)((Nw + 191) / 192), tM = (int)((M + 255) / 256);
+        hipLaunchKernelGGL((gemm_big_kernel<192, 256, MEDUSA_GEMM_BIG_WN4, MEDUSA_GEMM_BIG_WM4, 64, MEDUSA_GEMM_BIG_R4, EPI>),
+                           dim3((unsigned)(tN * tM), (unsigned)batch),
+                           dim3(64 * MEDUSA_GEMM_BIG_WN4 * MEDUSA_GEMM_BIG_WM4), 0, st, Xt, xbs, (int)M, (int)Kd, Wt, (int)Nw, Bt, aux, Y, y_f32, tN, tM);
       } else if (tiling == 3) {
         const int tN = (int)((Nw + 127) / 128), tM = (int)((M + 255) / 256);
         hipLaunchKernelGGL((gemm_big_kernel<128, 256, 2, MEDUSA_GEMM_BIG_WM3, 64, MEDUSA_GEMM_BIG_R3, EPI>),
