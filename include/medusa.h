@@ -112,10 +112,14 @@ int32_t medusa_tree_from_accuracy(const float* accuracy, int32_t K, int32_t topk
  *     MEDUSA_EPI_SWIGLU      W holds gate and up rows interleaved in blocks of
  *                            16 (block j: gate rows 16j..16j+15 then up rows);
  *                            Y [M, N/2] = SiLU(gate) * up   (dt)
- *   The launch plan (tiling, contraction split) is a function of (M, Kd, N,
- *   dt) only, never of the batch, and every reduction runs in a fixed order:
- *   equal inputs and shapes give bitwise equal outputs.
- * Kd must be a multiple of 8 (bf16) or 4 (f32).
+ *   Every reduction runs in a fixed order: equal inputs, shapes and batch
+ *   give bitwise equal outputs.  The launch plan is a function of (M, Kd, N,
+ *   dt), and of the batch only where a batch that shares its activation rows
+ *   (x_bstride 0) is planned as one projection onto its stacked weights; the
+ *   large-row tilings (bf16, M >= 256) all accumulate in the same order, so
+ *   there a batch element's outputs do not depend on the batch.
+ * Kd must be a multiple of 8 (bf16) or 4 (f32); X, W, Y, aux and bias
+ * 16-byte aligned (MEDUSA_ERR_INVALID_ARG otherwise).
  * ws: medusa_linear_ws(M, Kd, N, batch, dt) bytes of scratch for contraction
  * split partials (0 for shapes that do not split; then ws may be NULL).
  * ---------------------------------------------------------------------- */

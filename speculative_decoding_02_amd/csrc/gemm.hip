@@ -794,13 +794,30 @@ __global__ __launch_bounds__(64 * WGN * WGM) void gemm_big_kernel(
         const int n = n0 + wn * WN + fn * 16 + 4 * lg;
         if (n >= Nw) continue;
         const f32x4 v = acc[fn][fm];
+        // four consecutive outputs per lane: one vector access each (the
+        // entry point requires Y, aux and bias 16-byte aligned, Nw % 16 == 0)
+        const int64_t o = (int64_t)g * M * Nw + (int64_t)m * Nw + n;
         if (EPI == MEDUSA_EPI_NONE) {
-          const int64_t o = (int64_t)g * M * Nw + (int64_t)m * Nw + n;
           if (y_f32) *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(Y) + o) = v;
           else *reinterpret_cast<u32x2*>(reinterpret_cast<T*>(Y) + o) = u32x2{pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3])};
-        } else {
+        } else if (EPI == MEDUSA_EPI_RES_ADD_F32) {  // batch 1: Y, aux [M][Nw] float
+          const int64_t r = (int64_t)m * Nw + n;
+          const f32x4 res = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(aux) + r);
+          *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(Y) + r) =
+              f32x4{res[0] + v[0], res[1] + v[1], res[2] + v[2], res[3] + v[3]};
+        } else {  // MEDUSA_EPI_BIAS_SILU_RES
+          const u32x2 rr = *reinterpret_cast<const u32x2*>(reinterpret_cast<const T*>(aux) + (int64_t)g * xbs +
+                                                           (int64_t)m * Nw + n);
+          float bb[4] = {0.f, 0.f, 0.f, 0.f};
+          if (bias) {
+            const u32x2 bv = *reinterpret_cast<const u32x2*>(bias + (int64_t)g * Nw + n);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) xb_store<T, EPI>(g, M, Nw, xbs, bias, aux, Y, y_f32, m, n + r, v[r]);
+            for (int q = 0; q < 4; ++q) bb[q] = bf2f((bf16_t)(bv[q / 2] >> (16 * (q % 2))));
+          }
+          float y[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) y[q] = bf2f((bf16_t)(rr[q / 2] >> (16 * (q % 2)))) + silu_f(v[q] + bb[q]);
+          *reinterpret_cast<u32x2*>(reinterpret_cast<T*>(Y) + o) = u32x2{pack_bf2(y[0], y[1]), pack_bf2(y[2], y[3])};
         }
       }
     }
@@ -1279,8 +1296,8 @@ extern "C" int32_t medusa_linear(const void* X, int64_t x_bstride, int64_t M, in
                  "medusa_linear: Kd and x_bstride must be multiples of %d", p16);
   if (M == 0) return MEDUSA_OK;
   MEDUSA_REQUIRE(X && W && Y, MEDUSA_ERR_INVALID_ARG, "medusa_linear: NULL X, W or Y");
-  MEDUSA_REQUIRE(((uintptr_t)X | (uintptr_t)W) % 16 == 0, MEDUSA_ERR_INVALID_ARG,
-                 "medusa_linear: X and W must be 16-byte aligned");
+  MEDUSA_REQUIRE(((uintptr_t)X | (uintptr_t)W | (uintptr_t)Y | (uintptr_t)aux | (uintptr_t)bias) % 16 == 0,
+                 MEDUSA_ERR_INVALID_ARG, "medusa_linear: X, W, Y, aux and bias must be 16-byte aligned");
   if (epilogue == MEDUSA_EPI_BIAS_SILU_RES)
     MEDUSA_REQUIRE(aux != NULL, MEDUSA_ERR_INVALID_ARG, "medusa_linear: residual (aux) is NULL");
   if (epilogue == MEDUSA_EPI_RES_ADD_F32)
