@@ -418,7 +418,8 @@ def _cpu_baseline(torch, dec, model_src, emitted_per_step, sample_layers, reps):
 
 def batched_projections_f4(torch, M, rows=1024, reps=5):
     """One 7B layer's projections for batched tree verification (16 sequences
-    x 64 nodes = 1024 rows, bf16): QKV 4096 -> 12288, O 4096 -> 4096 + residual,
+    x 64 nodes = 1024 rows, bf16): QKV 4096 -> 12288 with rotary positions (as
+    the decoder calls it), O 4096 -> 4096 + residual,
     gate/up 4096 -> 2 x 11008 + SwiGLU, down 11008 -> 4096 + residual; the
     MFMA-bound tiling.  Graph-timed; FLOPs = 2 * rows * (sum of K x N)."""
     H, F, Q = 4096, 11008, 12288
@@ -430,10 +431,12 @@ def batched_projections_f4(torch, M, rows=1024, reps=5):
     h = torch.randn((rows, H), generator=gen, device="cuda").to(bf)
     o = torch.randn((rows, H), generator=gen, device="cuda").to(bf)
     x = torch.randn((rows, H), generator=gen, device="cuda")
-    qkv = torch.empty((rows, Q), device="cuda", dtype=bf)
+    pos = torch.arange(600, 600 + rows, dtype=torch.int32, device="cuda")
+    q, k, v = (torch.empty((rows, 32, 128), device="cuda", dtype=bf) for _ in range(3))
     f = torch.empty((rows, F), device="cuda", dtype=bf)
-    ws = M._ws(max(M.linear_ws_bytes(rows, k, n, 1, M.BF16) for k, n in ((H, Q), (H, H), (H, 2 * F), (F, H))), "cuda")
-    launches = [lambda: M.medusa_linear(h, Wqkv, out=qkv, ws=ws),
+    ws = M._ws(max([M.linear_ws_bytes(rows, kk, n, 1, M.BF16) for kk, n in ((H, H), (H, 2 * F), (F, H))] +
+                   [M.qkv_rope_ws_bytes(rows, H, 32, 32, 128, M.BF16)]), "cuda")
+    launches = [lambda: M.medusa_linear_qkv_rope(h, Wqkv, 32, 32, 128, pos, 10000.0, q=q, k=k, v=v, ws=ws),
                 lambda: M.medusa_linear(o, Wo, M.EPI_RES_ADD_F32, aux=x, out=x, ws=ws),
                 lambda: M.medusa_linear(h, Wgu, M.EPI_SWIGLU, out=f, ws=ws),
                 lambda: M.medusa_linear(f, Wd, M.EPI_RES_ADD_F32, aux=x, out=x, ws=ws)]

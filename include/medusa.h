@@ -381,7 +381,7 @@ int32_t medusa_linear_rmsnorm(const void* X, int64_t M, int64_t Kd, const void* 
  * without a contraction split, the rotation runs in its epilogue; otherwise
  * the projection goes to ws and the rotary pass reads it there.
  * ws: medusa_linear_qkv_rope_ws(...) bytes, 256-byte aligned (NULL when 0).
- * X, W, v 16-byte aligned; D a multiple of 8 up to 128; base > 1. */
+ * X, W, q, k, v 16-byte aligned; D a multiple of 8 up to 128; base > 1. */
 size_t medusa_linear_qkv_rope_ws(int64_t M, int64_t Kd, int32_t Hq, int32_t Hkv, int32_t D,
                                  int32_t dt);
 int32_t medusa_linear_qkv_rope(const void* X, int64_t M, int64_t Kd, const void* W, int32_t Hq,
@@ -390,7 +390,8 @@ int32_t medusa_linear_qkv_rope(const void* X, int64_t M, int64_t Kd, const void*
 
 /* Split qkv [M, (Hq + 2 Hkv) * D] (dt) into q [M, Hq, D], k [M, Hkv, D],
  * v [M, Hkv, D] and rotate q and k by position pos[m] (rotate-half pairs
- * (j, j + D/2), angle pos * base^(-2j/D)). */
+ * (j, j + D/2), angle pos * base^(-2j/D)).  qkv, q, k, v 16-byte aligned;
+ * D a multiple of 8 up to 128; base > 1. */
 int32_t medusa_qkv_rope(const void* qkv, int64_t M, int32_t Hq, int32_t Hkv, int32_t D,
                         const int32_t* pos, float base, int32_t dt, void* q, void* k, void* v,
                         void* stream);

@@ -79,19 +79,28 @@ __global__ __launch_bounds__(256) void qkv_rope_kernel(const T* __restrict__ qkv
   const int W = (Hq + 2 * Hkv) * D;
   const T* in = qkv + m * W;
   const int quads = (Hq + Hkv) * (half / 4);   // 4 consecutive j per item
+  // each item: four pairs j0 .. j0+3 read and written with vector accesses
+  // (every offset is a multiple of four elements: D % 8 == 0)
   for (int e = threadIdx.x; e < quads; e += 256) {
     const int hh = e / (half / 4), j0 = (e % (half / 4)) * 4;
     T* dst = hh < Hq ? q + (m * Hq + hh) * D : k + (m * Hkv + (hh - Hq)) * D;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int j = j0 + r;
-      const int64_t i1 = PAIRS ? (int64_t)hh * D + 2 * j : (int64_t)hh * D + j;
-      const int64_t i2 = PAIRS ? i1 + 1 : i1 + half;
-      float y1, y2;
-      rope_rot(ld<T>(in, i1), ld<T>(in, i2), cs[j], sn[j], y1, y2);
-      st<T>(dst, j, y1);
-      st<T>(dst, j + half, y2);
+    float x1[4], x2[4];
+    if (PAIRS) {  // elements (j, j + D/2) side by side: 8 consecutive values
+      const int64_t i4 = ((int64_t)hh * D + 2 * j0) / 4;
+      const f32x4 a = Elem<T>::load4(in, i4), b = Elem<T>::load4(in, i4 + 1);
+      x1[0] = a.x; x2[0] = a.y; x1[1] = a.z; x2[1] = a.w;
+      x1[2] = b.x; x2[2] = b.y; x1[3] = b.z; x2[3] = b.w;
+    } else {
+      const f32x4 a = Elem<T>::load4(in, ((int64_t)hh * D + j0) / 4);
+      const f32x4 b = Elem<T>::load4(in, ((int64_t)hh * D + j0 + half) / 4);
+      x1[0] = a.x; x1[1] = a.y; x1[2] = a.z; x1[3] = a.w;
+      x2[0] = b.x; x2[1] = b.y; x2[2] = b.z; x2[3] = b.w;
     }
+    float y1[4], y2[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) rope_rot(x1[r], x2[r], cs[j0 + r], sn[j0 + r], y1[r], y2[r]);
+    Elem<T>::store4(dst, j0 / 4, f32x4{y1[0], y1[1], y1[2], y1[3]});
+    Elem<T>::store4(dst, (j0 + half) / 4, f32x4{y2[0], y2[1], y2[2], y2[3]});
   }
   // v: straight copy in 16-byte pieces
   const int vb = Hkv * D * (int)sizeof(T) / 16;
@@ -178,8 +187,8 @@ extern "C" int32_t medusa_qkv_rope(const void* qkv, int64_t M, int32_t Hq, int32
   MEDUSA_REQUIRE(dt == MEDUSA_F32 || dt == MEDUSA_BF16, MEDUSA_ERR_UNSUPPORTED, "medusa_qkv_rope: dtype");
   MEDUSA_REQUIRE(D >= 8 && D <= 128 && D % 8 == 0, MEDUSA_ERR_UNSUPPORTED,
                  "medusa_qkv_rope: head dim %d (multiple of 8 up to 128)", D);
-  MEDUSA_REQUIRE(((uintptr_t)qkv | (uintptr_t)v) % 16 == 0, MEDUSA_ERR_INVALID_ARG,
-                 "medusa_qkv_rope: qkv and v must be 16-byte aligned");
+  MEDUSA_REQUIRE(((uintptr_t)qkv | (uintptr_t)q | (uintptr_t)k | (uintptr_t)v) % 16 == 0,
+                 MEDUSA_ERR_INVALID_ARG, "medusa_qkv_rope: qkv, q, k and v must be 16-byte aligned");
   MEDUSA_REQUIRE(M >= 0 && M <= INT32_MAX && Hq >= 1 && Hkv >= 1 && base > 1.f,
                  MEDUSA_ERR_INVALID_ARG, "medusa_qkv_rope: bad sizes or base");
   if (M == 0) return MEDUSA_OK;

@@ -1399,8 +1399,8 @@ extern "C" int32_t medusa_linear_qkv_rope(const void* X, int64_t M, int64_t Kd, 
   if (M == 0) return MEDUSA_OK;
   MEDUSA_REQUIRE(X && W && pos && q && k && v, MEDUSA_ERR_INVALID_ARG,
                  "medusa_linear_qkv_rope: NULL pointer");
-  MEDUSA_REQUIRE(((uintptr_t)X | (uintptr_t)W | (uintptr_t)v) % 16 == 0, MEDUSA_ERR_INVALID_ARG,
-                 "medusa_linear_qkv_rope: X, W and v must be 16-byte aligned");
+  MEDUSA_REQUIRE(((uintptr_t)X | (uintptr_t)W | (uintptr_t)q | (uintptr_t)k | (uintptr_t)v) % 16 == 0,
+                 MEDUSA_ERR_INVALID_ARG, "medusa_linear_qkv_rope: X, W, q, k and v must be 16-byte aligned");
   const int64_t N = ((int64_t)Hq + 2 * (int64_t)Hkv) * D;
   MEDUSA_REQUIRE(N <= INT32_MAX, MEDUSA_ERR_UNSUPPORTED,
                  "medusa_linear_qkv_rope: (Hq + 2 Hkv) D = %lld above 2^31 - 1", (long long)N);

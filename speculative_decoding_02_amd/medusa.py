@@ -159,6 +159,10 @@ def linear_ws_bytes(M, Kd, N, batch, dt):
     return _lib.medusa_linear_ws(M, Kd, N, batch, dt)
 
 
+def qkv_rope_ws_bytes(M, Kd, Hq, Hkv, D, dt):
+    return _lib.medusa_linear_qkv_rope_ws(M, Kd, Hq, Hkv, D, dt)
+
+
 def medusa_linear(X, W, epilogue=EPI_NONE, bias=None, aux=None, out=None, y_f32=False,
                   x_bstride=0, ws=None):
     """Y = epilogue(X W^T).  W [batch, N, Kd] or [N, Kd]; X [M, Kd] or [batch, M, Kd]."""

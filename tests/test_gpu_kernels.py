@@ -217,8 +217,11 @@ def test_linear_rmsnorm(lib, dt, Mr, Kd, N):
     (torch.bfloat16, 64, 4096, 8, 8, 128),    # split contraction: projection, then rotary pass
     (torch.bfloat16, 1, 512, 32, 32, 128),    # one row: projection, then rotary pass
     (torch.float32, 13, 256, 4, 2, 64),
-    (torch.bfloat16, 300, 512, 8, 8, 128)],   # large-row tiling: projection, then rotary pass
-    ids=["epi_wide", "epi_32rows", "epi_d64", "split", "onerow", "f32", "large_rows"])
+    (torch.bfloat16, 300, 512, 8, 8, 128),    # large-row tiling: rotation in its epilogue
+    (torch.bfloat16, 260, 512, 16, 4, 64),    # large rows, grouped kv heads, head dim 64
+    (torch.bfloat16, 1024, 4096, 32, 32, 128)],  # the 16-sequence batch's 7B QKV (192-row tiles)
+    ids=["epi_wide", "epi_32rows", "epi_d64", "split", "onerow", "f32", "large_rows", "large_rows_gqa",
+         "large_rows_7b"])
 def test_linear_qkv_rope(lib, dt, Mr, Kd, Hq, Hkv, D):
     """QKV projection with rotary positions fused, on the pair-interleaved
     weight: bit for bit the plain projection + medusa_qkv_rope, and close to
