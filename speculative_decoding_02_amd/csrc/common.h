@@ -191,7 +191,8 @@ __device__ __forceinline__ double rope_inv_freq(int j, int D, double log2_base) 
 __device__ __forceinline__ void rope_cs(int pos, double inv, float& c, float& s) {
   double ang = (double)pos * inv;
   const double two_pi = 6.283185307179586476925286766559;
-  ang -= two_pi * rint(ang / two_pi);
+  const double inv_two_pi = 0.15915494309189533576888376337251;  // the quotient is only rounded to an integer
+  ang -= two_pi * rint(ang * inv_two_pi);
   sincosf((float)ang, &s, &c);
 }
 // (x1, x2) = elements j and j + D/2 -> their rotated values
