@@ -256,6 +256,24 @@ static void check_rejections(void) {
              MEDUSA_ERR_UNSUPPORTED, "linear_rmsnorm N");
   EXPECT(medusa_linear_qkv_rope(NULL, 4, 64, NULL, 2, 2, 6, NULL, 10000.f, 1, NULL, NULL, NULL, NULL, 0, NULL) ==
              MEDUSA_ERR_UNSUPPORTED, "qkv_rope D");
+  /* 16-byte alignment of every tensor the projections and the rotary pass
+     touch with vector accesses (addresses never read: rejected before any
+     launch) */
+  {
+    void* const al = (void*)(uintptr_t)256;
+    void* const mis8 = (void*)(uintptr_t)(256 + 8);
+    void* const mis4 = (void*)(uintptr_t)(256 + 4);
+    EXPECT(medusa_linear(al, 0, 4, 8, al, 4, 1, MEDUSA_BF16, MEDUSA_EPI_NONE, NULL, NULL, mis8, 0, NULL, 0,
+                         NULL) == MEDUSA_ERR_INVALID_ARG, "linear Y alignment");
+    EXPECT(medusa_linear(al, 0, 4, 8, al, 4, 1, MEDUSA_BF16, MEDUSA_EPI_RES_ADD_F32, NULL, mis4, al, 0, NULL, 0,
+                         NULL) == MEDUSA_ERR_INVALID_ARG, "linear aux alignment");
+    EXPECT(medusa_linear(al, 0, 4, 8, al, 8, 1, MEDUSA_BF16, MEDUSA_EPI_BIAS_SILU_RES, mis8, al, al, 0, NULL, 0,
+                         NULL) == MEDUSA_ERR_INVALID_ARG, "linear bias alignment");
+    EXPECT(medusa_linear_qkv_rope(al, 4, 64, al, 2, 2, 8, (const int32_t*)al, 10000.f, MEDUSA_BF16, mis8, al, al,
+                                  NULL, 0, NULL) == MEDUSA_ERR_INVALID_ARG, "linear_qkv_rope q alignment");
+    EXPECT(medusa_qkv_rope(al, 4, 2, 2, 8, (const int32_t*)al, 10000.f, MEDUSA_BF16, al, mis8, al, NULL) ==
+               MEDUSA_ERR_INVALID_ARG, "qkv_rope k alignment");
+  }
   /* fused decode tail and fused tree embedding (addresses never read) */
   {
     const uintptr_t a = 256;
