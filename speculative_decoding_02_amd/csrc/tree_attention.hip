@@ -476,6 +476,11 @@ __global__ __launch_bounds__(256 * KQ) void tree_attention_stream_kernel(AttnArg
   constexpr int ROWB = D * 2;                  // bytes per key row
   constexpr int CPR = ROWB / 16;               // 16-byte chunks per row
   constexpr int SW = CPR - 1;                  // swizzle mask
+  // V rows are read 8 rows x 2 adjacent chunks per 32-lane pass of the
+  // transposing read: with 16 chunks a row (D = 128) the chunk is XORed with
+  // twice the row so that those 16 pieces land on 16 distinct bank groups
+  // (XOR with the row would map chunks 2d, 2d+1 of rows r, r^1 together)
+  auto vsw = [](int r) { return CPR == 16 ? ((2 * r) & SW) : (r & SW); };
   constexpr int TILEB = ATT_TILE * ROWB;       // bytes of one K (or V) tile
   constexpr int SLOTB = 2 * TILEB;
   constexpr int RPD = 1024 / ROWB;             // rows per DMA instruction (64 lanes x 16 B)
@@ -576,12 +581,13 @@ __global__ __launch_bounds__(256 * KQ) void tree_attention_stream_kernel(AttnArg
         const int q = wave * DPW + i;          // 1 KB block of the tile
         const int r = q * RPD + lane / CPR;
         const int c = (lane % CPR) ^ (r & SW); // chunk fetched for that position
+        const int cv = (lane % CPR) ^ vsw(r);
         const int j = jj[i];
         const int sj = P2 ? (j & (a.P - 1)) : j - (j / a.P) * a.P;
-        const int64_t off = (int64_t)(uint32_t)pg[i] * page_elems + (head_elems + sj * D + c * P16);
+        const int64_t row = (int64_t)(uint32_t)pg[i] * page_elems + (head_elems + sj * D);
         const uint32_t kd = lds_base + slot * SLOTB + q * 1024;
-        lds_dma16(Kcp + off, kd);
-        lds_dma16(Vcp + off, kd + TILEB);
+        lds_dma16(Kcp + row + c * P16, kd);
+        lds_dma16(Vcp + row + cv * P16, kd + TILEB);
       }
       return;
     }
@@ -590,13 +596,14 @@ __global__ __launch_bounds__(256 * KQ) void tree_attention_stream_kernel(AttnArg
       const int q = wave * DPW + i;          // 1 KB block of the tile
       const int r = q * RPD + lane / CPR;
       const int c = (lane % CPR) ^ (r & SW); // chunk fetched for that position
+      const int cv = (lane % CPR) ^ vsw(r);
       const int j = jj[i];
       const bool cached = j < ctxb;
       const int sj = P2 ? (j & (a.P - 1)) : j - (j / a.P) * a.P;
       const int64_t coff = (int64_t)(uint32_t)pg[i] * page_elems + (head_elems + sj * D);
-      const int64_t off = (cached ? coff : tree_off(j)) + c * P16;
-      const T* ksrc = (cached ? Kcp : Ktp) + off;
-      const T* vsrc = (cached ? Vcp : Vtp) + off;
+      const int64_t off = cached ? coff : tree_off(j);
+      const T* ksrc = (cached ? Kcp : Ktp) + off + c * P16;
+      const T* vsrc = (cached ? Vcp : Vtp) + off + cv * P16;
       const uint32_t kd = lds_base + slot * SLOTB + q * 1024;
       lds_dma16(ksrc, kd);
       lds_dma16(vsrc, kd + TILEB);
@@ -628,7 +635,7 @@ __global__ __launch_bounds__(256 * KQ) void tree_attention_stream_kernel(AttnArg
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
       const int c = db * 2 + ((lr & 3) >> 1);
-      vofs[db] = rr * ROWB + ((c ^ (rr & SW)) * 16) + (lr & 1) * 8;
+      vofs[db] = rr * ROWB + ((c ^ vsw(rr)) * 16) + (lr & 1) * 8;
     }
   }
 
