@@ -364,7 +364,7 @@ __global__ __launch_bounds__(256) void gemm_xlds_kernel(const T* __restrict__ X,
 }
 
 // ---------------------------------------------------------------------------
-// Block-range plan for M > 16 rows (bf16): G workgroups of eight waves per
+// Block-range plan for M >= 2 rows (bf16): G workgroups of eight waves per
 // (batch element, activation-row tile, contraction split), about one per
 // compute unit, each owning a contiguous range of whole 16-row weight blocks
 // (pairs of blocks for SwiGLU, whose gate and up rows interleave in 16-row
@@ -973,6 +973,13 @@ struct GemmPlan {
 #ifndef MEDUSA_GEMM_XD_SPLIT
 #define MEDUSA_GEMM_XD_SPLIT 4
 #endif
+#ifndef MEDUSA_GEMM_XD_MIN_M
+// fewest rows the block-range plan takes (one row keeps the one-block-per-
+// workgroup kernel, which streams its weights at 6.2 TB/s there); at 16 rows
+// (the heads of a 16-sequence batch) the block ranges took 275 us against
+// 434 us for the five heads
+#define MEDUSA_GEMM_XD_MIN_M 2
+#endif
 #ifndef MEDUSA_GEMM_XD_CPS
 #define MEDUSA_GEMM_XD_CPS 8  // contraction chunks per split, at least
 #endif
@@ -1028,7 +1035,7 @@ GemmPlan gemm_plan(int64_t M, int64_t Kd, int64_t Nw, int dt, int epi) {
     return p;
   }
   const bool narrow = Nw / 16 >= MEDUSA_GEMM_XD_MIN_BLOCKS;
-  if (dt == MEDUSA_BF16 && M > 16 && Kd % XB_KC == 0 && Nw % (16 * unit) == 0 &&
+  if (dt == MEDUSA_BF16 && M >= MEDUSA_GEMM_XD_MIN_M && Kd % XB_KC == 0 && Nw % (16 * unit) == 0 &&
       (Nw / 16 >= MEDUSA_GEMM_XB_MIN_BLOCKS || narrow) && Nw / 16 <= (1 << 24)) {
     const int nunits = (int)(Nw / 16 / unit);
     p.xb = true;

@@ -41,7 +41,9 @@ def _rnd(dt, a):
                                      (64, 256, 32000), (24, 512, 22016),
                                      # narrower outputs: block ranges (32-row
                                      # tiles split 2 ways; 3 splits; unsplit)
-                                     (20, 4096, 2048), (64, 6144, 2048), (64, 768, 2048)])
+                                     (20, 4096, 2048), (64, 6144, 2048), (64, 768, 2048),
+                                     # 2-16 rows: block ranges on 32-row tiles, mostly empty
+                                     (2, 256, 8192), (16, 4096, 4096), (9, 512, 12288), (16, 256, 32000)])
 def test_linear(lib, dt, Mr, Kd, N):
     case(f"linear {DTN[dt]} M={Mr} Kd={Kd} N={N}")
     g = synth.rngs(Mr * 7 + Kd + N, 2)
@@ -113,7 +115,8 @@ def test_linear_epilogues(lib, dt):
 # not a multiple of the per-workgroup share (N = 2064: 129 blocks each).
 @pytest.mark.parametrize("Mr,Kd,N,batch,epi", [(64, 4096, 2064, 4, "none"), (40, 4096, 4096, 3, "bias_silu_res"),
                                                (64, 6144, 2048, 4, "none"), (17, 4096, 4096, 5, "bias_silu_res"),
-                                               (64, 4096, 4096, 5, "bias_silu_res")])
+                                               (64, 4096, 4096, 5, "bias_silu_res"),
+                                               (16, 4096, 4096, 5, "bias_silu_res"), (2, 4096, 2064, 4, "none")])
 def test_linear_shared_rows_batch(lib, Mr, Kd, N, batch, epi):
     case(f"linear shared rows M={Mr} Kd={Kd} N={N} batch={batch} {epi}")
     bf = torch.bfloat16
@@ -313,7 +316,8 @@ def test_heads_zero_init_reproduces_lm_head_bitwise(lib, H, V, Mr):
 @pytest.mark.parametrize("dt", DTS, ids=DTN.get)
 @pytest.mark.parametrize("Mr,H,V,K,k", [(1, 256, 1000, 3, 3), (7, 128, 515, 5, 10),
                                         (64, 256, 2000, 2, 4), (64, 256, 8192, 3, 10),
-                                        (20, 512, 12288, 2, 64), (260, 256, 4096, 2, 10)])
+                                        (20, 512, 12288, 2, 64), (260, 256, 4096, 2, 10),
+                                        (16, 512, 8192, 5, 4)])
 def test_heads_vs_oracle(lib, dt, Mr, H, V, K, k):
     case(f"heads {DTN[dt]} M={Mr} H={H} V={V} K={K} k={k}")
     d = synth.heads_inputs(Mr + V, Mr, H, V, K, w1_std=0.05, w2_std=0.05,
