@@ -222,9 +222,10 @@ def test_linear_large_rows_192_row_tiles(lib):
 @pytest.mark.parametrize("dt,Mr,Kd,N", [(torch.bfloat16, 64, 4096, 4096), (torch.bfloat16, 48, 11008, 4096),
                                          (torch.bfloat16, 20, 4096, 2048), (torch.bfloat16, 40, 512, 1024),
                                          (torch.bfloat16, 1, 4096, 4096), (torch.bfloat16, 64, 256, 8192),
-                                         (torch.float32, 33, 256, 512), (torch.bfloat16, 300, 512, 4096)],
+                                         (torch.float32, 33, 256, 512), (torch.bfloat16, 300, 512, 4096),
+                                         (torch.bfloat16, 8, 4096, 4096), (torch.bfloat16, 16, 11008, 4096)],
                          ids=["split2", "split4_uneven", "split32rows", "tiles_split", "onerow", "nosplit",
-                              "f32", "large_rows"])
+                              "f32", "large_rows", "split2_8rows", "split4_16rows"])
 def test_linear_rmsnorm(lib, dt, Mr, Kd, N):
     """Residual projection + next RMSNorm: bit for bit the unfused pair
     (fused into the split reduction or not), and close to the oracle."""
@@ -255,9 +256,11 @@ def test_linear_rmsnorm(lib, dt, Mr, Kd, N):
     (torch.float32, 13, 256, 4, 2, 64),
     (torch.bfloat16, 300, 512, 8, 8, 128),    # large-row tiling: rotation in its epilogue
     (torch.bfloat16, 260, 512, 16, 4, 64),    # large rows, grouped kv heads, head dim 64
-    (torch.bfloat16, 1024, 4096, 32, 32, 128)],  # the 16-sequence batch's 7B QKV (192-row tiles)
+    (torch.bfloat16, 1024, 4096, 32, 32, 128),  # the 16-sequence batch's 7B QKV (192-row tiles)
+    (torch.bfloat16, 2, 4096, 32, 32, 128),    # two rows, 7B QKV: rotation in the epilogue
+    (torch.bfloat16, 16, 4096, 8, 8, 128)],    # 16 rows, split contraction: projection, then rotary pass
     ids=["epi_wide", "epi_32rows", "epi_d64", "split", "onerow", "f32", "large_rows", "large_rows_gqa",
-         "large_rows_7b"])
+         "large_rows_7b", "epi_2rows_7b", "split_16rows"])
 def test_linear_qkv_rope(lib, dt, Mr, Kd, Hq, Hkv, D):
     """QKV projection with rotary positions fused, on the pair-interleaved
     weight: bit for bit the plain projection + medusa_qkv_rope, and close to
