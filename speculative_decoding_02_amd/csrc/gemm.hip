@@ -729,20 +729,18 @@ __global__ __launch_bounds__(64 * WGN * WGM) void gemm_big_kernel(
   };
 
   // operand offsets inside a stage (A: weight rows first, B: activation
-  // rows), per contraction step ks (chunk 4*ks + lg)
-  int aofs[KSTEPS][FN], bofs[KSTEPS][FM];
+  // rows), per contraction step ks (chunk 4*ks + lg).  Every fragment's first
+  // row is a multiple of 16, so a row's chunk position depends on lr only
+  // ((r / LPR) % CPR = (lr / LPR) % CPR): fragment fn sits a constant
+  // fn * 16 rows after fragment 0, and one base register per step serves all
+  // fragments of an operand.
+  static_assert(TN % 16 == 0 && WN % 16 == 0 && WM % 16 == 0 && 16 % LPR == 0, "fragment rows start at multiples of 16");
+  int abase[KSTEPS], bbase[KSTEPS];
 #pragma unroll
   for (int ks = 0; ks < KSTEPS; ++ks) {
-#pragma unroll
-    for (int fn = 0; fn < FN; ++fn) {
-      const int r = wn * WN + fn * 16 + lr;
-      aofs[ks][fn] = r * ROWB + (((4 * ks + lg) ^ ((r / LPR) % CPR)) * 16);
-    }
-#pragma unroll
-    for (int fm = 0; fm < FM; ++fm) {
-      const int r = TN + wm * WM + fm * 16 + lr;
-      bofs[ks][fm] = r * ROWB + (((4 * ks + lg) ^ ((r / LPR) % CPR)) * 16);
-    }
+    const int c = ((4 * ks + lg) ^ ((lr / LPR) % CPR)) * 16;
+    abase[ks] = (wn * WN + lr) * ROWB + c;
+    bbase[ks] = (TN + wm * WM + lr) * ROWB + c;
   }
 
   f32x4 acc[FN][FM];
@@ -766,9 +764,9 @@ __global__ __launch_bounds__(64 * WGN * WGM) void gemm_big_kernel(
     for (int ks = 0; ks < KSTEPS; ++ks) {
       u32x4 af[FN], bfr[FM];
 #pragma unroll
-      for (int fn = 0; fn < FN; ++fn) af[fn] = *reinterpret_cast<const u32x4*>(sb + aofs[ks][fn]);
+      for (int fn = 0; fn < FN; ++fn) af[fn] = *reinterpret_cast<const u32x4*>(sb + abase[ks] + fn * 16 * ROWB);
 #pragma unroll
-      for (int fm = 0; fm < FM; ++fm) bfr[fm] = *reinterpret_cast<const u32x4*>(sb + bofs[ks][fm]);
+      for (int fm = 0; fm < FM; ++fm) bfr[fm] = *reinterpret_cast<const u32x4*>(sb + bbase[ks] + fm * 16 * ROWB);
       if constexpr (PRIO > 0) __builtin_amdgcn_s_setprio(PRIO);
 #pragma unroll
       for (int fn = 0; fn < FN; ++fn)
@@ -992,8 +990,15 @@ struct GemmPlan {
 #ifndef MEDUSA_GEMM_BIG_BK1
 #define MEDUSA_GEMM_BIG_BK1 64
 #endif
+// 256 x 256 tiles: 4 x 4 waves of 64 x 64 (each stage's operand reads from
+// LDS: 16 KB per wave against 20 KB for 2 x 8 waves of 128 x 32, which
+// measured 2% slower: the heads' vocabulary projection at 1024 rows 1157-1163
+// against 1184-1189 us)
 #ifndef MEDUSA_GEMM_BIG_WM1
-#define MEDUSA_GEMM_BIG_WM1 8  // waves along the activation rows of a 256-wide tile (x 2 along the weight rows)
+#define MEDUSA_GEMM_BIG_WM1 4  // waves along the activation rows of a 256-wide tile
+#endif
+#ifndef MEDUSA_GEMM_BIG_WN1
+#define MEDUSA_GEMM_BIG_WN1 4  // waves along the weight rows of a 256-wide tile
 #endif
 #ifndef MEDUSA_GEMM_BIG_R1
 #define MEDUSA_GEMM_BIG_R1 2
@@ -1068,7 +1073,7 @@ GemmPlan gemm_plan(int64_t M, int64_t Kd, int64_t Nw, int dt, int epi) {
 }
 
 // Tiling of the large-row plan for M rows x Nw outputs x batch: 1 = 256 x 256
-// tiles (16 waves of 128 x 32), 3 = 128 weight rows x 256 activation rows (16
+// tiles (16 waves of 64 x 64), 3 = 128 weight rows x 256 activation rows (16
 // waves of 64 x 32), 2 = 128 x 128 (8 waves of 64 x 32).  Four waves per SIMD
 // hide the operand reads' latency better than two (at 1024 rows: QKV 114.5
 // -> 108 us, gate/up 212 -> 204 us, the heads' W2 stage -2.5%); the 128 x 128
@@ -1181,9 +1186,9 @@ static bool launch_gemm_t(const void* X, int64_t xbs, int64_t M, int64_t Kd, con
       const int tiling = medusa_host::big_tiling(M, Nw, batch);
       if (tiling == 1) {
         const int tN = (int)((Nw + 255) / 256), tM = (int)((M + 255) / 256);
-        hipLaunchKernelGGL((gemm_big_kernel<256, 256, 2, MEDUSA_GEMM_BIG_WM1, MEDUSA_GEMM_BIG_BK1, MEDUSA_GEMM_BIG_R1, EPI, MEDUSA_GEMM_BIG_PRIO>),
+        hipLaunchKernelGGL((gemm_big_kernel<256, 256, MEDUSA_GEMM_BIG_WN1, MEDUSA_GEMM_BIG_WM1, MEDUSA_GEMM_BIG_BK1, MEDUSA_GEMM_BIG_R1, EPI, MEDUSA_GEMM_BIG_PRIO>),
                            dim3((unsigned)(tN * tM), (unsigned)batch),
-                           dim3(128 * MEDUSA_GEMM_BIG_WM1), 0, st, Xt, xbs, (int)M, (int)Kd, Wt, (int)Nw, Bt, aux, Y, y_f32, tN, tM);
+                           dim3(64 * MEDUSA_GEMM_BIG_WN1 * MEDUSA_GEMM_BIG_WM1), 0, st, Xt, xbs, (int)M, (int)Kd, Wt, (int)Nw, Bt, aux, Y, y_f32, tN, tM);
       } else if (tiling == 4) {
         const int tN = (int)((Nw + 191) / 192), tM = (int)((M + 255) / 256);
         hipLaunchKernelGGL((gemm_big_kernel<192, 256, MEDUSA_GEMM_BIG_WN4, MEDUSA_GEMM_BIG_WM4, 64, MEDUSA_GEMM_BIG_R4, EPI, MEDUSA_GEMM_BIG_PRIO>),
