@@ -680,12 +680,14 @@ def main():
         log("[bench] batched decoding: 16 sequences x 64-node trees (1024 verification rows)")
         Bb, bsteps = 16, 10
         bprompts = np.stack([synth.prompt_tokens(40 + b, 512, 32000) for b in range(Bb)])
-        bdec = MedusaDecoder(model, parent, rank, capacity=512 + 6 * (2 + bsteps) + 128,
+        # each sequence verifies its own pruned 64-node template
+        bparent, brank = synth.random_template_batch((4, 3, 2, 2, 1), 64, [100 + b for b in range(Bb)])
+        bdec = MedusaDecoder(model, bparent, brank, capacity=512 + 6 * (2 + bsteps) + 128,
                              mode=args.mode, batch=Bb)
         _, b_acc, b_sec = timed_steps(bdec, bsteps, 2, prompts=bprompts)
-        batched = dict(workload="16 sequences (prompts of 512, own pages and contexts), 64-node tree "
-                                "each: 1024 rows through every projection, batched attention, "
-                                "fused tail; greedy",
+        batched = dict(workload="16 sequences (prompts of 512, own pages and contexts), each with its "
+                                "own pruned 64-node tree: 1024 rows through every projection, batched "
+                                "attention, fused tail; greedy",
                        sequences=Bb, steps=bsteps, tokens_per_s=round(bdec.batch_emitted / b_sec, 1),
                        ms_per_step=round(1000 * b_sec / bsteps, 3),
                        verified_tree_tokens_per_s=round(Bb * 64 * bsteps / b_sec, 1),

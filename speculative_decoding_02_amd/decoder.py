@@ -140,9 +140,11 @@ class DeviceModel:
 class MedusaDecoder:
     """Paged-KV Medusa decoding of B sequences at once (B = ``batch``, default 1).
 
-    ``parent``, ``rank``: the tree template (node 0 = root), shared by the
-    batch; a single-node template turns the loop into plain greedy decoding
-    (no heads).  ``mode``: "greedy", "typical" or "sample" (sampled
+    ``parent``, ``rank``: the tree template (node 0 = root): ``[N]``, shared
+    by the batch, or ``[batch, N]``, one template per sequence (the same node
+    count; the heads run to the deepest template and give each head's top-k
+    for the widest, of which a narrower template uses a prefix).  A
+    single-node template turns the loop into plain greedy decoding (no heads).  ``mode``: "greedy", "typical" or "sample" (sampled
     verification with the counter-based stream keyed by ``seed``: the
     prefill's next token draws at step 0, decode step s at step s; sequence b
     draws with counter word b).  Each sequence owns ``capacity`` cache slots
@@ -153,20 +155,27 @@ class MedusaDecoder:
     def __init__(self, model: DeviceModel, parent, rank, capacity, page_size=16, mode="greedy",
                  temperature=1.0, epsilon=0.3, delta=0.09, seed=0, tail="fused", batch=1):
         self.m = model
-        dev = model.device
         parent = np.asarray(parent, np.int32)
         rank = np.asarray(rank, np.int32)
         self.B = B = int(batch)
         if B < 1:
             raise ValueError(f"batch {batch}")
-        self.N = len(parent)
-        depth = np.zeros(self.N, np.int32)
+        if parent.ndim == 1:
+            parent = np.tile(parent, (B, 1))
+        if rank.ndim == 1:
+            rank = np.tile(rank, (B, 1))
+        if parent.ndim != 2 or parent.shape[0] != B or rank.shape != parent.shape:
+            raise ValueError(f"templates {parent.shape} / {rank.shape} for a batch of {B}")
+        self.N = parent.shape[1]
+        depth = np.zeros(parent.shape, np.int32)
         for i in range(1, self.N):
-            depth[i] = depth[parent[i]] + 1
+            depth[:, i] = depth[np.arange(B), np.clip(parent[:, i], 0, i - 1)] + 1
         self.K = int(depth.max())
         self.width = int(rank.max()) + 1
         if self.K > 0:
-            M.medusa_tree_validate(parent, rank, self.K, self.width)
+            for b in range(B):
+                M.medusa_tree_validate(parent[b], rank[b], self.K, self.width)
+        dev = model.device
         if mode not in ("greedy", "typical", "sample"):
             raise ValueError(f"mode {mode!r}")
         if tail not in ("fused", "separate"):
@@ -178,8 +187,8 @@ class MedusaDecoder:
         self.P = page_size
         self.max_pages, self.capacity, self.max_ctx = plan_cache(capacity, self.N, page_size)
         i32 = dict(dtype=torch.int32, device=dev)
-        self.parent = torch.tensor(np.tile(parent, (B, 1)), **i32)
-        self.rank = torch.tensor(np.tile(rank, (B, 1)), **i32)
+        self.parent = torch.tensor(parent, **i32)
+        self.rank = torch.tensor(rank, **i32)
         # sequence b owns pages b*max_pages .. (b+1)*max_pages-1 of every pool
         self.page_table = torch.arange(B * self.max_pages, **i32).reshape(B, self.max_pages).contiguous()
         shape = (B * self.max_pages, model.n_kv_heads, page_size, model.head_dim)
