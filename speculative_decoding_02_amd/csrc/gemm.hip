@@ -451,7 +451,7 @@ __global__ __launch_bounds__(64 * XB_WAVES) void gemm_xdma_kernel(
   constexpr int LDE = TM + 1;
   constexpr int SMEM = 2 * XBUFB + XB_WAVES * WSLOTB;
   static_assert(XD >= 1 && XD * XB_WAVES * 1024 == XBUFB, "activation chunk must split into whole DMAs");
-  static_assert(XB_MAXB * 16 * LDE * 4 + XB_MAXB * 8 * 8 <= SMEM, "epilogue tile (and pair table) must fit");
+  static_assert(XB_MAXB * 16 * LDE * 4 + XB_MAXB * 8 * 12 <= SMEM, "epilogue tile (and pair tables) must fit");
   static_assert(WR == 2 || WR == 3, "wait counts are worked out for rings of 2 and 3 groups");
   // Issue order per wave: prologue W(0) [.. W(WR-3)], X(0), W(WR-2), W(WR-1);
   // then per chunk q: X(q+1), group 2q, W(2q+WR), group 2q+1, W(2q+1+WR).
@@ -568,32 +568,38 @@ __global__ __launch_bounds__(64 * XB_WAVES) void gemm_xdma_kernel(
 
   constexpr int NT = 64 * XB_WAVES;
   if constexpr (EPI == EPI_ROPE_QKV) {
-    // pairs of adjacent columns; the pair frequencies of this range first
+    // pairs of adjacent columns: per pair of this range its frequency and
+    // its output (q, k or v, and the column in that row) first
     const int np = nb * 8;
     const int qw = ra.Hq * ra.D, kw = ra.Hkv * ra.D, half = ra.D / 2;
     double* invt = reinterpret_cast<double*>(smem + XB_MAXB * 16 * LDE * 4);
-    if (threadIdx.x < np)
-      invt[threadIdx.x] = rope_inv_freq(((b0 * 16 + 2 * threadIdx.x) % ra.D) / 2, ra.D, ra.log2_base);
+    int* ptab = reinterpret_cast<int*>(invt + XB_MAXB * 8);
+    if (threadIdx.x < np) {
+      const int n = b0 * 16 + 2 * threadIdx.x;  // even column of qkv
+      const int kind = n < qw ? 0 : n < qw + kw ? 1 : 2;
+      const int nh = kind == 0 ? n : n - qw;
+      // q and k rows 2j, 2j + 1 of a head are its elements j, j + D/2
+      const int col = kind == 2 ? n - qw - kw : (nh / ra.D) * ra.D + (nh % ra.D) / 2;
+      invt[threadIdx.x] = rope_inv_freq((n % ra.D) / 2, ra.D, ra.log2_base);
+      ptab[threadIdx.x] = col * 4 + kind;
+    }
     __syncthreads();
     for (int e = threadIdx.x; e < np * TM; e += NT) {
       const int m = e / np, pl = e % np;
       if (m0 + m >= M) continue;
-      const int n = b0 * 16 + 2 * pl;  // even column of qkv
       const float x1 = bf2f(f2bf(ep[(2 * pl) * LDE + m]));
       const float x2 = bf2f(f2bf(ep[(2 * pl + 1) * LDE + m]));
       const int64_t row = m0 + m;
-      if (n < qw + kw) {
-        const bool isq = n < qw;
-        const int nh = isq ? n : n - qw;
-        const int hh = nh / ra.D, j = (nh % ra.D) / 2;
-        T* dst = isq ? ra.q + (row * ra.Hq + hh) * ra.D : ra.k + (row * ra.Hkv + hh) * ra.D;
+      const int info = ptab[pl], kind = info & 3, col = info >> 2;
+      if (kind < 2) {
+        T* dst = (kind == 0 ? ra.q + row * qw : ra.k + row * kw) + col;
         float c, sn, y1, y2;
         rope_cs(ra.pos[row], invt[pl], c, sn);
         rope_rot(x1, x2, c, sn, y1, y2);
-        dst[j] = f2bf(y1);
-        dst[j + half] = f2bf(y2);
+        dst[0] = f2bf(y1);
+        dst[half] = f2bf(y2);
       } else {
-        T* dst = ra.v + row * kw + (n - qw - kw);
+        T* dst = ra.v + row * kw + col;
         dst[0] = f2bf(x1);
         dst[1] = f2bf(x2);
       }
