@@ -374,8 +374,10 @@ __global__ __launch_bounds__(256) void gemm_xlds_kernel(const T* __restrict__ X,
 // column offsets of their rows (when all start at column 0 together the weight
 // stream measured 20-35% slower).  The activation rows are staged through two
 // LDS buffers, one 256-wide chunk at a time, with one barrier per chunk.  The
-// epilogue goes through LDS, so a gate block and its up block may sit in
-// different waves and the output stores are coalesced.  Each output is one
+// epilogues with arithmetic go through LDS, so a gate block and its up block
+// may sit in different waves and the output stores are coalesced; plain fp32
+// results (split partials, fp32 outputs) are stored by each wave from its
+// accumulators.  Each output is one
 // wave's accumulation chain in step order from the workgroup's start chunk:
 // results depend on (Kd, N) and the launch plan, itself a function of the
 // shape.
@@ -557,6 +559,27 @@ __global__ __launch_bounds__(64 * XB_WAVES) void gemm_xdma_kernel(
   if (wave < nb) run(std::true_type());
   else run(std::false_type());
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // the clamped refills
+  // fp32 results with no epilogue arithmetic (split partials [batch][S][M][N],
+  // plain fp32 outputs): each wave stores its own accumulators, lane (lr, lg)
+  // holding column lr of its block for rows 4 lg .. 4 lg + 3 of each 16-row
+  // block (64-byte row pieces), without the LDS round trip and its barriers
+  if constexpr (EPI != EPI_ROPE_QKV) {
+    if (S > 1 || (EPI == MEDUSA_EPI_NONE && y_f32 && nsub == Nw)) {
+      if (wave < nb) {
+        float* dst = S > 1 ? part + ((int64_t)gi * S + sp) * M * Nw
+                           : reinterpret_cast<float*>(Y) + (int64_t)gi * M * Nw;
+        dst += (b0 + wave) * 16 + lr;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int m = m0 + mb * 16 + lg * 4 + r;
+            if (m < M) dst[(int64_t)m * Nw] = acc[mb][r];
+          }
+      }
+      return;
+    }
+  }
   __syncthreads();  // the operand buffers become the epilogue tile
   if (wave < nb) {
 #pragma unroll
@@ -603,15 +626,6 @@ __global__ __launch_bounds__(64 * XB_WAVES) void gemm_xdma_kernel(
         dst[0] = f2bf(x1);
         dst[1] = f2bf(x2);
       }
-    }
-    return;
-  }
-  if (S > 1) {  // fp32 partials [batch][S][M][N]; the split reducer applies the epilogue
-    const int nn = nb * 16;
-    float* pp = part + ((int64_t)gi * S + sp) * M * Nw;
-    for (int e = threadIdx.x; e < nn * TM; e += NT) {
-      const int m = e / nn, nl = e % nn;
-      if (m0 + m < M) pp[(int64_t)(m0 + m) * Nw + b0 * 16 + nl] = ep[nl * LDE + m];
     }
     return;
   }
