@@ -228,6 +228,21 @@ int32_t medusa_tree_attention(const void* Q, const void* Kt, const void* Vt, voi
                               void* stream);
 
 /* ------------------------------------------------------------------------
+ * medusa_tree_attention_splits: how medusa_tree_attention would run a call
+ * of these shapes (the plan depends on them only, so equal shapes always
+ * take the same arithmetic path).
+ *   0: one launch, no key splits: one workgroup per (sequence, query head,
+ *      16-node block) over its head's whole key range (bf16 calls with at
+ *      most 256 such workgroups whose page table of max_ctx + N slots spans
+ *      at most 4096 pages);
+ *   S >= 1: S key splits per (sequence, head), plus a merge launch when
+ *      S > 1;
+ *   -1: shapes or dtype medusa_tree_attention rejects.
+ * ---------------------------------------------------------------------- */
+int32_t medusa_tree_attention_splits(int32_t B, int32_t N, int32_t Hq, int32_t Hkv, int32_t D,
+                                     int32_t max_ctx, int32_t P, int32_t dt);
+
+/* ------------------------------------------------------------------------
  * medusa_tree_attention_noalloc: medusa_tree_attention for callers that
  * cannot allocate (code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc).  Same arguments and results, minus the

@@ -846,6 +846,323 @@ __global__ __launch_bounds__(256 * KQ) void tree_attention_stream_kernel(AttnArg
   }
 }
 
+// bf16 kernel without key splits, for launches with few (sequence, head)
+// pairs, such as one sequence's decode step: one workgroup per (sequence,
+// query head, block of 16 tree nodes) covers its head's whole key range, so
+// no split partials are written and no merge launch follows.
+//   * The 8 waves take the range's 16-key chunks in turn (chunk c goes to
+//     wave c % 8), each with its own online softmax over its chunks; the
+//     eight states of a node are merged through LDS in wave order after the
+//     loop (a fixed order: the result does not depend on timing).
+//   * Each wave streams its chunks' K and V rows by LDS-DMA into a ring of R
+//     slots of its own, so inside the loop a wave waits only on its own
+//     loads: eight independent chains per CU and no barrier per tile.  The
+//     chunks' rows use the split kernel's 16-byte-chunk swizzles, so the
+//     score operand reads and the transposing V reads are conflict-free.
+//   * The workgroups that read the same kv head (its node blocks and the
+//     query heads of its group) run on one XCD: workgroup i goes to XCD
+//     i % 8, and the grid is ordered so that every workgroup of one
+//     (sequence, kv head) shares i % 8.  Their K/V rows then come from HBM
+//     once and from that XCD's L2 for the other readers.
+//   * The workgroups of the first query head of a kv group store their
+//     nodes' K/V rows into cache slots ctx + node.  The other workgroups
+//     read tree keys from Kt/Vt and cached keys from slots below ctx only,
+//     so those stores race with no read.
+constexpr int NBK_WAVES = 8;
+constexpr int NBK_CHUNK = 16;
+constexpr int NBK_MAX_PAGES = 4096;  // page-table window (LDS), all of max_ctx + N
+template <int D, int R, bool P2>
+__global__ __launch_bounds__(64 * NBK_WAVES) void tree_attention_nodes_kernel(AttnArgs a, int runs,
+                                                                            int per_run) {
+  using T = bf16_t;
+  constexpr int NT = 64 * NBK_WAVES;
+  constexpr int P16 = 8;                       // bf16 per 16 bytes
+  constexpr int ROWB = D * 2;                  // bytes per key row
+  constexpr int CPR = ROWB / 16;               // 16-byte chunks per row
+  constexpr int SW = CPR - 1;                  // swizzle mask
+  auto vsw = [](int r) { return CPR == 16 ? ((2 * r) & SW) : (r & SW); };
+  constexpr int CHB = NBK_CHUNK * ROWB;        // bytes of one chunk's K (or V)
+  constexpr int SLOTB = 2 * CHB;               // K then V
+  constexpr int WAVEB = R * SLOTB;             // one wave's ring
+  constexpr int RPD = 1024 / ROWB;             // rows per DMA instruction (64 lanes x 16 B)
+  constexpr int DPC = CHB / 1024;              // DMA instructions per chunk and tensor
+  constexpr int OPS = 2 * DPC;                 // vector-memory ops per chunk
+  constexpr int QSTEPS = D / 32;
+  constexpr int DB = D / 16;
+  constexpr int XW = DB * 4 + 2;               // exchange words per lane
+  static_assert(DPC >= 1 && DPC * 1024 == CHB, "a chunk must split into whole DMAs");
+  static_assert(R >= 2 && R <= 8 && (R - 1) * OPS < 64, "ring depth / vmcnt range");
+  static_assert(NBK_WAVES * 64 * XW * 4 <= NBK_WAVES * WAVEB, "exchange fits in the rings");
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[NBK_WAVES * WAVEB];
+  __shared__ int spages[NBK_MAX_PAGES];
+
+  // workgroup -> (sequence, kv head) run, then (query head in group, node block)
+  const int wg = blockIdx.x;
+  const int run = (wg >> 3) / per_run * 8 + (wg & 7);
+  if (run >= runs) return;  // padding of the XCD-ordered grid (uniform)
+  const int k = (wg >> 3) % per_run;
+  const int N = a.N;
+  const int NB = (N + 15) >> 4;
+  const int group = a.Hq / a.Hkv;
+  const int b = run / a.Hkv, kvh = run % a.Hkv;
+  const int h = kvh * group + k / NB;
+  const int nb = k % NB;
+  const bool appender = (h % group) == 0;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+  const int node = nb * 16 + lr;
+  const int nodec = min(node, N - 1);
+  const int ntree = min(N, nb * 16 + 16);      // tree keys this block's nodes may see
+
+  const T* Qp = reinterpret_cast<const T*>(a.Q);
+  const T* Ktp = reinterpret_cast<const T*>(a.Kt);
+  const T* Vtp = reinterpret_cast<const T*>(a.Vt);
+  T* Kcp = reinterpret_cast<T*>(a.Kc);
+  T* Vcp = reinterpret_cast<T*>(a.Vc);
+  const int* pt = a.page_table + (int64_t)b * a.max_pages;
+
+  // One round trip before the stream: the length, the page table of slots
+  // 0 .. max_ctx + N - 1 (into LDS), this lane's query row and its node's
+  // ancestor mask.  (The host checks npages <= NBK_MAX_PAGES and
+  // max_ctx + N <= max_pages * P.)
+  const int npages = (a.max_ctx + N + a.P - 1) / a.P;
+  const int ctxb = min(max(a.ctx[b], 0), a.max_ctx);
+  u32x4 qf[QSTEPS];
+  {
+    const T* qrow = Qp + (((int64_t)b * N + nodec) * a.Hq + h) * D;
+#pragma unroll
+    for (int st = 0; st < QSTEPS; ++st)
+      qf[st] = *reinterpret_cast<const u32x4*>(qrow + st * 4 * P16 + lg * P16);
+  }
+  const uint64_t mrow = a.mask[(int64_t)b * N + nodec];
+  for (int e = tid; e < npages; e += NT) spages[e] = pt[e];
+  // every prologue load has landed: the loop's waits then count chunk DMA only
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  const int tot = ctxb + ntree;
+  const int nchunks = (tot + NBK_CHUNK - 1) / NBK_CHUNK;
+  const int nw = nchunks > wave ? (nchunks - wave + NBK_WAVES - 1) / NBK_WAVES : 0;
+
+  const int64_t page_elems = (int64_t)a.Hkv * a.P * D;  // one page of the cache
+  const int head_elems = kvh * a.P * D;                  // this head's rows in a page
+  auto cache_off = [&](int j) -> int64_t {
+    const int pj = P2 ? (j >> a.lp) : j / a.P;
+    const int sj = P2 ? (j & (a.P - 1)) : j - pj * a.P;
+    return (int64_t)(uint32_t)spages[pj] * page_elems + (head_elems + sj * D);
+  };
+  const int64_t tree_base = ((int64_t)b * N * a.Hkv + kvh) * D;
+  auto tree_off = [&](int j) -> int64_t {
+    return tree_base + max(j - ctxb, 0) * (a.Hkv * D);
+  };
+
+  const uint32_t wave_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)lds +
+                            wave * WAVEB;
+  const uintptr_t kc_u = reinterpret_cast<uintptr_t>(Kcp), kt_u = reinterpret_cast<uintptr_t>(Ktp);
+  const uintptr_t vc_u = reinterpret_cast<uintptr_t>(Vcp), vt_u = reinterpret_cast<uintptr_t>(Vtp);
+  // DMA of this wave's chunk ci into ring slot `slot`.  Rows past the range
+  // re-read its last key (their scores are masked).  Every key below
+  // max_ctx + N has its page in spages, so the lookup runs for every row and
+  // tree rows ignore it.
+  auto issue = [&](int ci, int slot) {
+    const int key0 = (wave + NBK_WAVES * ci) * NBK_CHUNK;
+    const uint32_t kd = wave_lds + slot * SLOTB;
+    // the rows' page lookups first, all together (a DMA's memory clobber
+    // would otherwise keep each lookup behind the previous DMA); every key
+    // below max_ctx + N has its page in spages, tree rows ignore theirs
+    int jj[DPC], pg[DPC];
+#pragma unroll
+    for (int q = 0; q < DPC; ++q) {
+      jj[q] = min(key0 + q * RPD + lane / CPR, tot - 1);
+      pg[q] = spages[P2 ? (jj[q] >> a.lp) : jj[q] / a.P];
+    }
+#pragma unroll
+    for (int q = 0; q < DPC; ++q) {
+      const int r = q * RPD + lane / CPR;      // chunk row this lane fills
+      const int c = (lane % CPR) ^ (r & SW);   // K chunk fetched for that position
+      const int cv = (lane % CPR) ^ vsw(r);    // V chunk
+      const int j = jj[q];
+      const bool cached = j < ctxb;
+      // both offsets, then selects on values (no branch, no pointer select
+      // through memory)
+      const int sj = P2 ? (j & (a.P - 1)) : j - (j / a.P) * a.P;
+      const int64_t coff = (int64_t)(uint32_t)pg[q] * page_elems + (head_elems + sj * D);
+      const int64_t toff = tree_off(j);
+      const int64_t off = cached ? coff : toff;
+      const uintptr_t kbase = cached ? kc_u : kt_u, vbase = cached ? vc_u : vt_u;
+      lds_dma16(reinterpret_cast<const T*>(kbase) + off + c * P16, kd + q * 1024);
+      lds_dma16(reinterpret_cast<const T*>(vbase) + off + cv * P16, kd + CHB + q * 1024);
+    }
+  };
+  // wait until at most n chunks of this wave's DMA are in flight (n < R)
+  auto wait_chunks = [&](int n) {
+    switch (n) {
+      case 0: __builtin_amdgcn_s_waitcnt(waitcnt_vm(0)); break;
+      case 1: __builtin_amdgcn_s_waitcnt(waitcnt_vm(R > 1 ? 1 * OPS : 0)); break;
+      case 2: __builtin_amdgcn_s_waitcnt(waitcnt_vm(R > 2 ? 2 * OPS : 0)); break;
+      case 3: __builtin_amdgcn_s_waitcnt(waitcnt_vm(R > 3 ? 3 * OPS : 0)); break;
+      case 4: __builtin_amdgcn_s_waitcnt(waitcnt_vm(R > 4 ? 4 * OPS : 0)); break;
+      case 5: __builtin_amdgcn_s_waitcnt(waitcnt_vm(R > 5 ? 5 * OPS : 0)); break;
+      case 6: __builtin_amdgcn_s_waitcnt(waitcnt_vm(R > 6 ? 6 * OPS : 0)); break;
+      default: __builtin_amdgcn_s_waitcnt(waitcnt_vm(R > 7 ? 7 * OPS : 0)); break;
+    }
+  };
+
+  // this lane's LDS byte offsets inside a slot: the K operand chunk of each
+  // contraction step (key row lr) and the transposing-read address of each
+  // 16-dim block of V (key row 4*lg + lr/4)
+  int kofs[QSTEPS], vofs[DB];
+#pragma unroll
+  for (int st = 0; st < QSTEPS; ++st) kofs[st] = lr * ROWB + (((st * 4 + lg) ^ (lr & SW)) * 16);
+  {
+    const int rr = 4 * lg + (lr >> 2);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const int c = db * 2 + ((lr & 3) >> 1);
+      vofs[db] = rr * ROWB + ((c ^ vsw(rr)) * 16) + (lr & 1) * 8;
+    }
+  }
+
+  f32x4 oacc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float mrun = -INFINITY, lrun = 0.f;
+
+  const int first = min(nw, R);
+  for (int ci = 0; ci < first; ++ci) issue(ci, ci);
+  for (int ci = 0; ci < nw; ++ci) {
+    const int slot = ci % R;
+    // chunks issued so far: min(nw, R + ci); the ones after ci stay in flight
+    wait_chunks(min(nw, R + ci) - ci - 1);
+    asm volatile("" ::: "memory");
+    const unsigned char* ks = lds + wave * WAVEB + slot * SLOTB;
+    const unsigned char* vs = ks + CHB;
+    u32x4 kf[QSTEPS];
+#pragma unroll
+    for (int st = 0; st < QSTEPS; ++st) kf[st] = *reinterpret_cast<const u32x4*>(ks + kofs[st]);
+    typedef short s4 __attribute__((ext_vector_type(4)));
+    u32x2 vf[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+      vf[db] = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                   (__attribute__((address_space(3))) s4*)(vs + vofs[db])));
+    // the slot's operands are in registers: refill it
+    __builtin_amdgcn_s_waitcnt(WAITCNT_LGKM0);
+    asm volatile("" ::: "memory");
+    if (ci + R < nw) issue(ci + R, slot);
+
+    const int key0 = (wave + NBK_WAVES * ci) * NBK_CHUNK;
+    f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int st = 0; st < QSTEPS; ++st) sacc = mfma_bf16_16x16x32(kf[st], qf[st], sacc);
+    // raw scores (masked: -inf); lane l holds keys key0 + 4*lg + r of node lr
+    float x[4];
+    float tmax = -INFINITY;
+    const bool plain = key0 + NBK_CHUNK <= ctxb;  // (wave-uniform) cached keys only: no mask
+    if (plain) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        x[r] = sacc[r];
+        tmax = fmaxf(tmax, x[r]);
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int j = key0 + lg * 4 + r;
+        const uint32_t bit = (uint32_t)(mrow >> (uint32_t)min(max(j - ctxb, 0), 63)) & 1u;
+        const bool ok = (j < tot) & ((j < ctxb) | (bit != 0u));
+        x[r] = ok ? sacc[r] : -INFINITY;
+        tmax = fmaxf(tmax, x[r]);
+      }
+    }
+    tmax = rows4_max(tmax) * a.scale_log2;
+    // lazy reference, as in the split kernel
+    if (__builtin_amdgcn_ballot_w64(tmax > mrun + ATT_LAZY) != 0) {
+      const float mnew = fmaxf(mrun, tmax);
+      const float alpha = (mnew == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(mrun - mnew);
+      lrun *= alpha;
+      mrun = mnew;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+    }
+    float psum = 0.f;
+    if (plain) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        x[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[r], a.scale_log2, -mrun));
+        psum += x[r];
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float p = (x[r] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(__builtin_fmaf(x[r], a.scale_log2, -mrun));
+        x[r] = p;
+        psum += p;
+      }
+    }
+    lrun += psum;
+    // O^T += V^T P^T over the chunk's 16 keys (contraction index 4*lg + r)
+    const u32x2 pb = {pack_bf2(x[0], x[1]), pack_bf2(x[2], x[3])};
+#pragma unroll
+    for (int db = 0; db < DB; ++db) oacc[db] = mfma_bf16_16x16x16(vf[db], pb, oacc[db]);
+    asm volatile("" ::: "memory");
+  }
+  // (every chunk issued was waited for above: no DMA is left in flight)
+
+  // this block's tree rows into cache slots ctx + t
+  if (appender) {
+    constexpr int CPRT = D / P16;
+    const int t0 = nb * 16;
+    const int rows = ntree - t0;
+    const int items = rows * CPRT * 2;
+    for (int e = tid; e < items; e += NT) {
+      const int which = e / (rows * CPRT), rem = e % (rows * CPRT);
+      const int j = ctxb + t0 + rem / CPRT, part = rem % CPRT;
+      const T* src = reinterpret_cast<const T*>(which ? vt_u : kt_u) + tree_off(j) + part * P16;
+      T* dst = reinterpret_cast<T*>(which ? vc_u : kc_u) + cache_off(j) + part * P16;
+      *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src);
+    }
+  }
+
+  // merge the waves' states per node, in wave order; wave w finishes the
+  // 16-dim blocks db = w, w + 8, ...
+  const float ltot = rows4_sum(lrun);
+  __syncthreads();                             // every wave is done with its ring
+  float* xch = reinterpret_cast<float*>(lds);  // [waves][64 lanes][XW]
+  {
+    float* d = xch + (wave * 64 + lane) * XW;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) d[db * 4 + r] = oacc[db][r];
+    d[DB * 4] = mrun;
+    d[DB * 4 + 1] = ltot;
+  }
+  __syncthreads();
+  if (node >= N) return;
+  T* orow = reinterpret_cast<T*>(a.O) + (((int64_t)b * N + node) * a.Hq + h) * D;
+  for (int db = wave; db < DB; db += NBK_WAVES) {
+    float mm = -INFINITY;
+#pragma unroll
+    for (int q = 0; q < NBK_WAVES; ++q) mm = fmaxf(mm, xch[(q * 64 + lane) * XW + DB * 4]);
+    float l = 0.f;
+    f32x4 o = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int q = 0; q < NBK_WAVES; ++q) {
+      const float* d = xch + (q * 64 + lane) * XW;
+      const float mq = d[DB * 4];
+      const float w = mq == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mq - mm);
+      l += w * d[DB * 4 + 1];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) o[r] += w * d[db * 4 + r];
+    }
+    const float inv = 1.f / l;
+    const u32x2 v = {pack_bf2(o[0] * inv, o[1] * inv), pack_bf2(o[2] * inv, o[3] * inv)};
+    *reinterpret_cast<u32x2*>(orow + db * 16 + lg * 4) = v;
+  }
+}
+
 // Merge of the split partials of one (sequence, head): O = sum_s w_s l_s o_s
 // / sum_s w_s l_s with w_s = 2^(m_s - max m) and o_s the split's normalised
 // output, splits in index order.  One
@@ -960,6 +1277,32 @@ SplitPlan plan_splits(int B, int Hq, int N, int max_ctx, int P, int target) {
   return {(int)chunk, (int)((total + chunk - 1) / chunk)};
 }
 
+// bf16 calls whose (sequence, query head, 16-node block) workgroups fit in
+// one round of one workgroup per CU, and whose page table (slots 0 ..
+// max_ctx + N - 1) fits the LDS window, take the kernel without key splits;
+// with more workgroups than that the split kernel's balance over the CUs
+// wins (and its one workgroup per key range needs no L2 sharing).
+// Every workgroup of that kernel streams its head's whole key range, so its
+// time grows with the range about 2.7 times as fast as the split kernel's
+// (measured at the 7B layer: 10.9 us at 595 keys, 24.1 us at 2112, against
+// 13.5 and 18.3 us for the split kernel and its merge); it takes ranges of
+// up to MEDUSA_ATTN_NODES_MAX_KEYS planned keys (max_ctx + N), near the
+// crossing point.
+#ifndef MEDUSA_ATTN_NODES_MAX_WGS
+#define MEDUSA_ATTN_NODES_MAX_WGS 256
+#endif
+#ifndef MEDUSA_ATTN_NODES_MAX_KEYS
+#define MEDUSA_ATTN_NODES_MAX_KEYS 1024
+#endif
+bool nodes_path(int B, int N, int Hq, int max_ctx, int P, int dt) {
+  if (dt != MEDUSA_BF16) return false;
+  const int64_t wgs = (int64_t)B * Hq * ((N + 15) / 16);
+  const int64_t keys = (int64_t)max_ctx + N;
+  const int64_t pages = (keys + P - 1) / P;
+  return wgs <= MEDUSA_ATTN_NODES_MAX_WGS && keys <= MEDUSA_ATTN_NODES_MAX_KEYS &&
+         pages <= medusa::NBK_MAX_PAGES;
+}
+
 // largest B and Hq (grid dimensions of the attention launches)
 #define MEDUSA_ATTN_MAX_GRID 65535
 struct WsLayout {
@@ -995,6 +1338,18 @@ static int32_t tree_attention_impl(const char* fn, const void* Q, const void* Kt
                                    const uint64_t* mask, int32_t B, int32_t N, int32_t Hq,
                                    int32_t Hkv, int32_t D, float scale, int32_t dt, void* O,
                                    void* ws, size_t ws_bytes, void* stream);
+
+extern "C" int32_t medusa_tree_attention_splits(int32_t B, int32_t N, int32_t Hq, int32_t Hkv,
+                                                int32_t D, int32_t max_ctx, int32_t P,
+                                                int32_t dt) {
+  if (medusa_tree_attention_ws(B, N, Hq, Hkv, D, max_ctx, P) == 0 ||
+      (dt != MEDUSA_F32 && dt != MEDUSA_BF16))
+    return -1;
+  if (nodes_path(B, N, Hq, max_ctx, P, dt)) return 0;
+  return plan_splits(B, Hq, N, max_ctx, P,
+                     dt == MEDUSA_BF16 ? MEDUSA_ATTN_DMA_WGS : MEDUSA_ATTN_TARGET_WGS)
+      .splits;
+}
 
 extern "C" int32_t medusa_tree_attention(const void* Q, const void* Kt, const void* Vt, void* Kc,
                                          void* Vc, const int32_t* page_table, int32_t max_pages,
@@ -1140,6 +1495,24 @@ static int32_t tree_attention_impl(const char* fn, const void* Q, const void* Kt
     if (p.splits > 1) MEDUSA_ATT_COMBINE(T, DD);                                             \
   } while (0)
   constexpr int RD = MEDUSA_ATTN_DMA_R;
+  if (nodes_path(B, N, Hq, max_ctx, P, dt)) {
+    // XCD-ordered grid: runs of (sequence, kv head), each of group * NB
+    // workgroups, dealt to the 8 XCDs in turn (padding exits at once)
+    const int NB = (N + 15) / 16;
+    const int runs = B * Hkv, per_run = (Hq / Hkv) * NB;
+    const dim3 ngrid((unsigned)(((runs + 7) / 8) * 8 * per_run));
+    const dim3 nblk(64 * medusa::NBK_WAVES);
+    const bool p2 = a.lp >= 0;
+    if (D == 128 && p2)
+      hipLaunchKernelGGL((medusa::tree_attention_nodes_kernel<128, 2, true>), ngrid, nblk, 0, st, a, runs, per_run);
+    else if (D == 128)
+      hipLaunchKernelGGL((medusa::tree_attention_nodes_kernel<128, 2, false>), ngrid, nblk, 0, st, a, runs, per_run);
+    else if (p2)
+      hipLaunchKernelGGL((medusa::tree_attention_nodes_kernel<64, 4, true>), ngrid, nblk, 0, st, a, runs, per_run);
+    else
+      hipLaunchKernelGGL((medusa::tree_attention_nodes_kernel<64, 4, false>), ngrid, nblk, 0, st, a, runs, per_run);
+    return check_launch(fn);
+  }
   if (dt == MEDUSA_BF16) {
     const bool p2 = a.lp >= 0;
     // two key parts per tile (8 waves); four parts (16 waves) measured slower

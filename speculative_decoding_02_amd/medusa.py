@@ -39,6 +39,7 @@ _SIGS = {
     "medusa_topk": (i32, [vp, i64, i64, i32, vp, vp, vp, sz, vp]),
     "medusa_build_tree": (i32, [i32, i32, vp, vp, vp, vp, i32, i32, vp, vp, vp, vp, vp]),
     "medusa_tree_attention_ws": (sz, [i32, i32, i32, i32, i32, i32, i32]),
+    "medusa_tree_attention_splits": (i32, [i32, i32, i32, i32, i32, i32, i32, i32]),
     "medusa_tree_attention": (i32, [vp, vp, vp, vp, vp, vp, i32, i32, vp, i32, vp, i32, i32, i32,
                                     i32, i32, f32, i32, vp, vp, sz, vp]),
     "medusa_tree_attention_noalloc": (i32, [vp, vp, vp, vp, vp, vp, i32, i32, vp, i32, vp, i32,
@@ -266,6 +267,13 @@ def medusa_build_tree(parent, rank, root_tok, topk_ids, ctx, tokens=None, pos=No
 
 def tree_attention_ws_bytes(B, N, Hq, Hkv, D, max_ctx, P=16):
     return _lib.medusa_tree_attention_ws(B, N, Hq, Hkv, D, max_ctx, P)
+
+
+def tree_attention_splits(B, N, Hq, Hkv, D, max_ctx, P=16, bf16=True):
+    """The plan medusa_tree_attention takes for these shapes: 0 = one launch
+    without key splits, S >= 1 = S key splits (+ a merge launch if S > 1)."""
+    return _lib.medusa_tree_attention_splits(B, N, Hq, Hkv, D, int(max_ctx), P,
+                                             BF16 if bf16 else F32)
 
 
 def medusa_tree_attention(Q, Kt, Vt, Kc, Vc, page_table, ctx, max_ctx, mask, scale, out=None,

@@ -51,16 +51,25 @@ def _one_head(d, b, h, c, masks):
                               d["Vt"][b][:, h:h + 1], masks[b], d["scale"])[:, 0]
 
 
-def test_c2_tree_attention_7b_layer(lib):
-    case("full size: tree attention, 7B layer, ctx 2048")
-    B, N, H, D, ctx = 1, 64, 32, 128, 2048
+@pytest.mark.parametrize("ctx,max_ctx", [(2048, 2048), (531, 928)], ids=["ctx2048", "step"])
+def test_c2_tree_attention_7b_layer(lib, ctx, max_ctx):
+    """The 7B layer at 2048 cached tokens (key splits and their merge) and at
+    the decode step's shape, 531 cached tokens planned for 928 (the
+    one-launch kernel): every head against the oracle."""
+    B, N, H, D = 1, 64, 32, 128
+    plan = lib.tree_attention_splits(B, N, H, H, D, max_ctx, 16)
+    assert (plan == 0) == (max_ctx == 928)
+    case(f"full size: tree attention, 7B layer, ctx {ctx} (max_ctx {max_ctx}, plan {plan})")
     d = synth.attention_inputs(2, B, N, H, H, D, ctx, bf16=True)
     masks = _mask(d, B)
     bf = torch.bfloat16
+    width = (max_ctx + N + 15) // 16
+    pt = np.zeros((B, width), np.int32)          # the launch plan of max_ctx
+    pt[:, :d["page_table"].shape[1]] = d["page_table"]
     Kc, Vc = dev(d["Kc"], bf), dev(d["Vc"], bf)
-    ws = lib._ws(lib.tree_attention_ws_bytes(B, N, H, H, D, ctx), "cuda")
+    ws = lib._ws(lib.tree_attention_ws_bytes(B, N, H, H, D, max_ctx), "cuda")
     out = lib.medusa_tree_attention(dev(d["Q"], bf), dev(d["Kt"], bf), dev(d["Vt"], bf), Kc, Vc,
-                                    dev(d["page_table"]), dev(d["ctx"]), ctx, dev(masks),
+                                    dev(pt), dev(d["ctx"]), max_ctx, dev(masks),
                                     float(d["scale"]), ws=ws)
     o = host(out)[0]
     ref = orc.tree_attention(d["Q"][0], orc.cache_rows(d["Kc"], d["page_table"][0], ctx, 16),

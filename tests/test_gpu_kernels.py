@@ -556,13 +556,25 @@ ATT_CASES = [
     # bf16 with an empty cache (only the tree's keys) and a single-node tree
     (1, 64, 8, 8, 64, 0, 16, False, torch.bfloat16),
     (2, 1, 4, 4, 128, [0, 77], 16, True, torch.bfloat16),
+    # bf16 calls with more than 256 (sequence, head, 16-node block)
+    # workgroups: the key-split kernel and its merge launch (the calls above
+    # take the one-launch kernel without splits)
+    (5, 64, 16, 4, 128, [300, 1000, 0, 77, 513], 16, True, torch.bfloat16),
+    (3, 37, 32, 8, 64, [2500, 7, 130], 24, True, torch.bfloat16),
+    (1, 64, 80, 80, 128, 1500, 24, True, torch.bfloat16),
+    (2, 20, 160, 160, 64, [40, 900], 8, False, torch.bfloat16),
+    # the one-launch kernel at its limits: 256 workgroups, a GQA group of 8
+    # on one kv head, and a ragged batch
+    (1, 64, 64, 8, 128, 900, 16, True, torch.bfloat16),
+    (4, 50, 16, 2, 64, [900, 0, 333, 64], 12, True, torch.bfloat16),
 ]
 
 
 @pytest.mark.parametrize("B,N,Hq,Hkv,D,ctx,P,perm,dt", ATT_CASES)
 def test_tree_attention(lib, B, N, Hq, Hkv, D, ctx, P, perm, dt):
-    case(f"tree_attention B={B} N={N} Hq={Hq} Hkv={Hkv} D={D} ctx={ctx} P={P} {DTN[dt]}")
     bf = dt == torch.bfloat16
+    plan = lib.tree_attention_splits(B, N, Hq, Hkv, D, int(np.max(ctx)), P, bf16=bf)
+    case(f"tree_attention B={B} N={N} Hq={Hq} Hkv={Hkv} D={D} ctx={ctx} P={P} {DTN[dt]} plan={plan}")
     d = synth.attention_inputs(B * 100 + N + D, B, N, Hq, Hkv, D, ctx, page_size=P,
                                permute_pages=perm, bf16=bf)
     masks = np.stack([orc.build_tree(d["parent"][b], d["rank"][b], 0,
@@ -588,15 +600,19 @@ def test_tree_attention(lib, B, N, Hq, Hkv, D, ctx, P, perm, dt):
         np.testing.assert_array_equal(kt[:c], kc)
 
 
-@pytest.mark.parametrize("D,P,c", [(128, 16, 3000), (64, 12, 3000), (128, 16, 1500)])
-def test_tree_attention_large_values(lib, D, P, c):
-    """|V| near 1e5 (legal bf16, past fp16's largest finite 65504) through
-    calls with many key splits (1500 and 3000 cached keys): every split's
-    partial output is about 1e5 in magnitude, so its block-scaled fp16 store
-    must keep it finite.  Outputs are stored in bf16: the bar is 2e-2
-    relative above |y| = 1."""
-    case(f"tree_attention large values D={D} P={P} ctx={c}")
-    B, N, H = 1, 64, 4
+@pytest.mark.parametrize("D,P,c,H", [(128, 16, 3000, 4), (64, 12, 3000, 4), (128, 16, 1500, 80),
+                                     (128, 16, 900, 4), (64, 12, 700, 4)])
+def test_tree_attention_large_values(lib, D, P, c, H):
+    """|V| near 1e5 (legal bf16, past fp16's largest finite 65504).  With
+    1500 and 3000 cached keys the call takes the key-split kernel: every
+    split's partial output is about 1e5 in magnitude, so its block-scaled
+    fp16 store must keep it finite; with 700 and 900 it takes the one-launch
+    kernel, whose fp32 wave states must too.  Outputs are stored in bf16:
+    the bar is 2e-2 relative above |y| = 1."""
+    plan = lib.tree_attention_splits(1, 64, H, H, D, c, P)
+    assert (plan == 0) == (c < 1000)
+    case(f"tree_attention large values D={D} P={P} ctx={c} H={H} plan={plan}")
+    B, N = 1, 64
     d = synth.attention_inputs(21 + D, B, N, H, H, D, c, page_size=P, permute_pages=True, bf16=True)
     sgn = np.where(np.arange(D) % 3 == 0, -1.0, 1.0).astype(np.float32)
     big = lambda v: synth.round_bf16(1e5 * sgn + 300.0 * v)

@@ -137,3 +137,35 @@ def test_interleave_rope_pairs_definition(M):
             np.testing.assert_array_equal(p[h * D + 2 * j + 1], w[h * D + j + D // 2])
     import torch
     np.testing.assert_array_equal(M.interleave_rope_pairs(torch.tensor(w), heads, D).numpy(), p)
+
+
+def test_attention_plans_reach_both_bf16_kernels(M):
+    """The attention plan is a function of the shapes only: the one-launch
+    kernel (plan 0) for bf16 calls of at most 256 (sequence, head, 16-node
+    block) workgroups over at most 1024 planned keys (max_ctx + N), key
+    splits otherwise and for fp32.  The parity cases
+    of the GPU tests reach both bf16 kernels at both head dims and with
+    power-of-two and other page sizes."""
+    sp = M.tree_attention_splits
+    assert sp(1, 64, 32, 32, 128, 928, 16) == 0               # one 7B sequence's decode step
+    assert sp(1, 64, 32, 32, 128, 960, 16) == 0               # 1024 planned keys
+    assert sp(1, 64, 32, 32, 128, 961, 16) > 0                # 1025
+    assert sp(1, 64, 32, 32, 128, 2048, 16) > 0               # the 7B layer at 2048 cached keys
+    assert sp(1, 64, 64, 8, 128, 900, 16) == 0                # exactly 256 workgroups
+    assert sp(1, 64, 65, 65, 128, 900, 16) > 0                # 260
+    assert sp(1, 65, 32, 32, 128, 100, 16) == -1              # N > 64: rejected
+    assert sp(16, 64, 32, 32, 128, 1024, 16) > 0              # a 16-sequence batch
+    assert sp(1, 64, 80, 80, 128, 1500, 16) > 0               # 320 workgroups
+    assert sp(1, 64, 32, 32, 128, 2048, 16, bf16=False) > 0   # fp32
+    assert sp(1, 64, 4, 4, 128, 4096 * 16, 16) > 0            # page table past the LDS window
+    from tests.test_gpu_kernels import ATT_CASES
+    import torch
+    seen = set()
+    for B, N, Hq, Hkv, D, ctx, P, _, dt in ATT_CASES:
+        if dt != torch.bfloat16:
+            continue
+        plan = sp(B, N, Hq, Hkv, D, int(np.max(ctx)), P)
+        assert plan >= 0
+        seen.add((plan == 0, D, P & (P - 1) == 0))
+    assert seen == {(z, D, p2) for z in (True, False) for D in (64, 128) for p2 in (True, False)}
+

@@ -33,10 +33,18 @@ def _inputs(seed, B, N, H, Hkv, D, ctx, P, dt):
 
 @pytest.mark.parametrize("dt", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
 def test_noalloc_attention_equals_workspace_call(lib, dt):
-    shapes = [(1, 64, 32, 32, 128, 2048, 16),   # the 7B layer
-              (2, 20, 4, 2, 64, [300, 41], 12)]  # smaller, grouped kv heads, other page size
+    # shapes whose bf16 plan splits the keys, so that both calls keep their
+    # split partials in the array (bf16 calls of at most 256 (sequence,
+    # head, node block) workgroups take the one-launch kernel, which uses
+    # none); the second call is smaller
+    shapes = [(4, 64, 32, 32, 128, [2048, 300, 1000, 7], 16),  # four 7B-layer sequences
+              (3, 20, 48, 16, 64, [300, 41, 900], 12)]          # grouped kv heads, other page size
     for i, (B, N, H, Hkv, D, ctx, P) in enumerate(shapes):
-        case(f"no-alloc attention call {i}: B={B} N={N} H={H} Hkv={Hkv} D={D} ctx={ctx} P={P}")
+        plan = lib.tree_attention_splits(B, N, H, Hkv, D, int(np.max(ctx)), P,
+                                         bf16=dt == torch.bfloat16)
+        assert plan >= 1
+        case(f"no-alloc attention call {i}: B={B} N={N} H={H} Hkv={Hkv} D={D} ctx={ctx} P={P} "
+             f"plan={plan}")
         d, masks = _inputs(31 + i, B, N, H, Hkv, D, ctx, P, dt)
         max_ctx = int(np.max(d["ctx"]))
         args = lambda Kc, Vc: (dev(d["Q"], dt), dev(d["Kt"], dt), dev(d["Vt"], dt), Kc, Vc,
