@@ -865,7 +865,9 @@ __global__ __launch_bounds__(256 * KQ) void tree_attention_stream_kernel(AttnArg
 //     (sequence, kv head) shares i % 8.  Their K/V rows then come from HBM
 //     once and from that XCD's L2 for the other readers.
 //   * The workgroups of the first query head of a kv group store their
-//     nodes' K/V rows into cache slots ctx + node.  The other workgroups
+//     nodes' K/V rows into cache slots ctx + node (the rows are loaded in
+//     the first round trip and stored after the loop, so the store adds no
+//     dependent load at the end).  The other workgroups
 //     read tree keys from Kt/Vt and cached keys from slots below ctx only,
 //     so those stores race with no read.
 constexpr int NBK_WAVES = 8;
@@ -936,6 +938,18 @@ __global__ __launch_bounds__(64 * NBK_WAVES) void tree_attention_nodes_kernel(At
       qf[st] = *reinterpret_cast<const u32x4*>(qrow + st * 4 * P16 + lg * P16);
   }
   const uint64_t mrow = a.mask[(int64_t)b * N + nodec];
+  // appending workgroups: this block's tree rows, stored at the end
+  const int t0 = nb * 16;
+  const int app_items = appender ? (ntree - t0) * (D / P16) * 2 : 0;
+  constexpr int APP = (16 * (D / P16) * 2 + NT - 1) / NT;  // 16-byte pieces per thread
+  u32x4 app[APP];
+#pragma unroll
+  for (int i = 0; i < APP; ++i) {
+    const int e = min(tid + i * NT, max(app_items - 1, 0));
+    const int which = e / ((ntree - t0) * (D / P16)), rem = e % ((ntree - t0) * (D / P16));
+    const int64_t off = (((int64_t)b * N + t0 + rem / (D / P16)) * a.Hkv + kvh) * D + (rem % (D / P16)) * P16;
+    app[i] = *reinterpret_cast<const u32x4*>((which ? Vtp : Ktp) + off);
+  }
   for (int e = tid; e < npages; e += NT) spages[e] = pt[e];
   // every prologue load has landed: the loop's waits then count chunk DMA only
   __builtin_amdgcn_s_waitcnt(0);
@@ -1110,18 +1124,16 @@ __global__ __launch_bounds__(64 * NBK_WAVES) void tree_attention_nodes_kernel(At
   }
   // (every chunk issued was waited for above: no DMA is left in flight)
 
-  // this block's tree rows into cache slots ctx + t
-  if (appender) {
-    constexpr int CPRT = D / P16;
-    const int t0 = nb * 16;
-    const int rows = ntree - t0;
-    const int items = rows * CPRT * 2;
-    for (int e = tid; e < items; e += NT) {
-      const int which = e / (rows * CPRT), rem = e % (rows * CPRT);
-      const int j = ctxb + t0 + rem / CPRT, part = rem % CPRT;
-      const T* src = reinterpret_cast<const T*>(which ? vt_u : kt_u) + tree_off(j) + part * P16;
-      T* dst = reinterpret_cast<T*>(which ? vc_u : kc_u) + cache_off(j) + part * P16;
-      *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src);
+  // this block's tree rows (loaded in the first round trip) into cache
+  // slots ctx + t
+#pragma unroll
+  for (int i = 0; i < APP; ++i) {
+    const int e = tid + i * NT;
+    if (e < app_items) {
+      const int which = e / ((ntree - t0) * (D / P16)), rem = e % ((ntree - t0) * (D / P16));
+      const int j = ctxb + t0 + rem / (D / P16);
+      T* dst = reinterpret_cast<T*>(which ? vc_u : kc_u) + cache_off(j) + (rem % (D / P16)) * P16;
+      *reinterpret_cast<u32x4*>(dst) = app[i];
     }
   }
 
