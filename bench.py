@@ -125,6 +125,7 @@ def tree_attention_c2(torch, M, synth, reps=10, copies=17):
     flops = 4.0 * N * H * D * (ctx + N)     # QK^T and PV, upper bound (all keys)
     gbs = nbytes / (us * 1e-6) / 1e9
     return dict(workload="7B layer: 32 heads x 128, ctx 2048 + 64-node tree, bf16, 16-token pages",
+                plan=M.tree_attention_splits(B, N, H, H, D, ctx, c["P"]),
                 us=round(us, 3), us_median=round(us_med, 3),
                 bytes=nbytes, gbs=round(gbs, 1), frac=round(gbs / HBM_PEAK_GBS, 4),
                 tflops=round(flops / (us * 1e-6) / 1e12, 2),
@@ -166,8 +167,10 @@ def tree_attention_step_shape(torch, M, synth, ctx, max_ctx, reps=10, copies=17)
     gbs = nbytes / (us * 1e-6) / 1e9
     return dict(workload=f"7B layer: 32 heads x 128, ctx {ctx} + 64-node tree (planned for max_ctx "
                          f"{max_ctx}), bf16, 16-token pages",
+                plan=M.tree_attention_splits(B, N, H, H, D, max_ctx, P),
                 us=round(us, 3), us_median=round(us_med, 3), bytes=nbytes, gbs=round(gbs, 1),
-                frac=round(gbs / HBM_PEAK_GBS, 4))
+                frac=round(gbs / HBM_PEAK_GBS, 4),
+                traffic=measured_traffic("tree_attention_step", "tree_attention.hip"))
 
 
 def hbm_copy_rate(torch, nbytes=1 << 30, reps=5):
