@@ -564,9 +564,12 @@ ATT_CASES = [
     (1, 64, 80, 80, 128, 1500, 24, True, torch.bfloat16),
     (2, 20, 160, 160, 64, [40, 900], 8, False, torch.bfloat16),
     # the one-launch kernel at its limits: 256 workgroups, a GQA group of 8
-    # on one kv head, and a ragged batch
+    # on one kv head, a ragged batch, and exactly 1024 planned keys (every
+    # wave streams 8 chunks, its ring turning over four times)
     (1, 64, 64, 8, 128, 900, 16, True, torch.bfloat16),
     (4, 50, 16, 2, 64, [900, 0, 333, 64], 12, True, torch.bfloat16),
+    (1, 64, 4, 4, 128, 960, 16, True, torch.bfloat16),
+    (2, 64, 6, 2, 64, [960, 17], 12, True, torch.bfloat16),
 ]
 
 
@@ -630,11 +633,15 @@ def test_tree_attention_large_values(lib, D, P, c, H):
     assert_close_stored(host(out[0]), ref, TOL[bf], "attention with |V| ~ 1e5")
 
 
-def test_tree_attention_chain_is_causal_and_repeatable(lib):
+@pytest.mark.parametrize("c", [1500, 700], ids=["splits", "one_launch"])
+def test_tree_attention_chain_is_causal_and_repeatable(lib, c):
     """Chain tree = causal attention; a second call on the same workspace gives
-    bitwise equal output (fixed merge order, no atomics)."""
-    case("tree_attention chain + repeat")
-    B, N, H, D, c = 1, 64, 4, 128, 1500
+    bitwise equal output (fixed merge orders, no atomics), for the key-split
+    plan (1500 cached keys) and the one-launch plan (700)."""
+    B, N, H, D = 1, 64, 4, 128
+    plan = lib.tree_attention_splits(B, N, H, H, D, c, 16)
+    assert (plan == 0) == (c == 700)
+    case(f"tree_attention chain + repeat, ctx {c}, plan {plan}")
     d = synth.attention_inputs(9, B, N, H, H, D, c, bf16=True)
     mask = orc.chain_mask(N)[None]
     args = [dev(d["Q"], torch.bfloat16), dev(d["Kt"], torch.bfloat16), dev(d["Vt"], torch.bfloat16),
