@@ -237,7 +237,8 @@ int32_t medusa_tree_attention(const void* Q, const void* Kt, const void* Vt, voi
  *      at most 4096 pages);
  *   S >= 1: S key splits per (sequence, head), plus a merge launch when
  *      S > 1;
- *   -1: shapes or dtype medusa_tree_attention rejects.
+ *   -1: shapes or dtype medusa_tree_attention rejects, or B = 0 (a call
+ *       that enqueues nothing).
  * ---------------------------------------------------------------------- */
 int32_t medusa_tree_attention_splits(int32_t B, int32_t N, int32_t Hq, int32_t Hkv, int32_t D,
                                      int32_t max_ctx, int32_t P, int32_t dt);
@@ -255,7 +256,10 @@ int32_t medusa_tree_attention_splits(int32_t B, int32_t N, int32_t Hq, int32_t H
  *   failure there returns MEDUSA_ERR_HIP.
  *   Every call on one GPU shares that GPU's array (it keeps the last call's
  *   partials; no call needs it cleared): calls that overlap in time on one
- *   GPU, from any stream or thread, race and give undefined results.
+ *   GPU, from any stream or thread, race and give undefined results.  Calls
+ *   whose plan is the one launch without key splits
+ *   (medusa_tree_attention_splits(...) == 0) write no partials and leave
+ *   the array untouched.
  * ---------------------------------------------------------------------- */
 #define MEDUSA_ATTN_NOALLOC_MAX_BYTES ((size_t)32 << 20)
 int32_t medusa_tree_attention_noalloc(const void* Q, const void* Kt, const void* Vt, void* Kc,
