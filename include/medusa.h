@@ -233,8 +233,7 @@ int32_t medusa_tree_attention(const void* Q, const void* Kt, const void* Vt, voi
  * take the same arithmetic path).
  *   0: one launch, no key splits: one workgroup per (sequence, query head,
  *      16-node block) over its head's whole key range (bf16 calls with at
- *      most 256 such workgroups whose page table of max_ctx + N slots spans
- *      at most 4096 pages);
+ *      most 256 such workgroups and at most 1024 planned keys max_ctx + N);
  *   S >= 1: S key splits per (sequence, head), plus a merge launch when
  *      S > 1;
  *   -1: shapes or dtype medusa_tree_attention rejects, or B = 0 (a call

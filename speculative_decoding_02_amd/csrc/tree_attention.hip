@@ -867,12 +867,16 @@ __global__ __launch_bounds__(256 * KQ) void tree_attention_stream_kernel(AttnArg
 //   * The workgroups of the first query head of a kv group store their
 //     nodes' K/V rows into cache slots ctx + node (the rows are loaded in
 //     the first round trip and stored after the loop, so the store adds no
-//     dependent load at the end).  The other workgroups
-//     read tree keys from Kt/Vt and cached keys from slots below ctx only,
-//     so those stores race with no read.
+//     dependent load at the end).  The other workgroups read tree keys from
+//     Kt/Vt and cached keys from slots below ctx only, so those stores race
+//     with no read.
+//   * A workgroup's range is at most NBK_MAX_KEYS planned keys (max_ctx + N;
+//     the host plans longer ranges on the split kernel), so its page table
+//     fits a small LDS window.
 constexpr int NBK_WAVES = 8;
 constexpr int NBK_CHUNK = 16;
-constexpr int NBK_MAX_PAGES = 4096;  // page-table window (LDS), all of max_ctx + N
+constexpr int NBK_MAX_KEYS = 1024;                  // planned keys per workgroup
+constexpr int NBK_MAX_PAGES = NBK_MAX_KEYS / 4 + 1;  // page-table window (LDS): pages of >= 4 slots
 template <int D, int R, bool P2>
 __global__ __launch_bounds__(64 * NBK_WAVES) void tree_attention_nodes_kernel(AttnArgs a, int runs,
                                                                             int per_run) {
@@ -925,9 +929,9 @@ __global__ __launch_bounds__(64 * NBK_WAVES) void tree_attention_nodes_kernel(At
   const int* pt = a.page_table + (int64_t)b * a.max_pages;
 
   // One round trip before the stream: the length, the page table of slots
-  // 0 .. max_ctx + N - 1 (into LDS), this lane's query row and its node's
-  // ancestor mask.  (The host checks npages <= NBK_MAX_PAGES and
-  // max_ctx + N <= max_pages * P.)
+  // 0 .. max_ctx + N - 1 (into LDS), this lane's query row, its node's
+  // ancestor mask and, in appending workgroups, the block's tree rows.  (The
+  // host checks max_ctx + N <= NBK_MAX_KEYS and <= max_pages * P.)
   const int npages = (a.max_ctx + N + a.P - 1) / a.P;
   const int ctxb = min(max(a.ctx[b], 0), a.max_ctx);
   u32x4 qf[QSTEPS];
@@ -976,9 +980,7 @@ __global__ __launch_bounds__(64 * NBK_WAVES) void tree_attention_nodes_kernel(At
   const uintptr_t kc_u = reinterpret_cast<uintptr_t>(Kcp), kt_u = reinterpret_cast<uintptr_t>(Ktp);
   const uintptr_t vc_u = reinterpret_cast<uintptr_t>(Vcp), vt_u = reinterpret_cast<uintptr_t>(Vtp);
   // DMA of this wave's chunk ci into ring slot `slot`.  Rows past the range
-  // re-read its last key (their scores are masked).  Every key below
-  // max_ctx + N has its page in spages, so the lookup runs for every row and
-  // tree rows ignore it.
+  // re-read its last key (their scores are masked).
   auto issue = [&](int ci, int slot) {
     const int key0 = (wave + NBK_WAVES * ci) * NBK_CHUNK;
     const uint32_t kd = wave_lds + slot * SLOTB;
@@ -1310,9 +1312,9 @@ bool nodes_path(int B, int N, int Hq, int max_ctx, int P, int dt) {
   if (dt != MEDUSA_BF16) return false;
   const int64_t wgs = (int64_t)B * Hq * ((N + 15) / 16);
   const int64_t keys = (int64_t)max_ctx + N;
-  const int64_t pages = (keys + P - 1) / P;
+  // (keys <= NBK_MAX_KEYS and P >= 4 keep the page table inside the kernel's window)
   return wgs <= MEDUSA_ATTN_NODES_MAX_WGS && keys <= MEDUSA_ATTN_NODES_MAX_KEYS &&
-         pages <= medusa::NBK_MAX_PAGES;
+         keys <= medusa::NBK_MAX_KEYS && (keys + P - 1) / P <= medusa::NBK_MAX_PAGES;
 }
 
 // largest B and Hq (grid dimensions of the attention launches)
