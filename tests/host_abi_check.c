@@ -164,10 +164,24 @@ static void check_workspace_queries(void) {
       for (int h = 0; h < 7; ++h)
         for (int d = 0; d < 7; ++d)
           for (int c = 0; c < 6; ++c)
-            for (int p = 0; p < 9; ++p)
+            for (int p = 0; p < 9; ++p) {
               sink += medusa_tree_attention_ws(small[b], small[n], heads[h], heads[h], dims[d], ctxs[c], pages[p]);
+              for (int dt = -1; dt <= 2; ++dt)
+                sink += (size_t)(medusa_tree_attention_splits(small[b], small[n], heads[h], heads[h],
+                                                              dims[d], ctxs[c], pages[p], dt) + 1);
+            }
     }
   (void)sink;
+  /* the attention plan: one launch for a single 7B sequence's decode step,
+     key splits for long ranges, large batches and fp32; -1 where the call
+     rejects the shapes */
+  EXPECT(medusa_tree_attention_splits(1, 64, 32, 32, 128, 928, 16, MEDUSA_BF16) == 0, "one launch");
+  EXPECT(medusa_tree_attention_splits(1, 64, 32, 32, 128, 2048, 16, MEDUSA_BF16) > 0, "long range splits");
+  EXPECT(medusa_tree_attention_splits(16, 64, 32, 32, 128, 928, 16, MEDUSA_BF16) > 0, "batch splits");
+  EXPECT(medusa_tree_attention_splits(1, 64, 32, 32, 128, 928, 16, MEDUSA_F32) > 0, "fp32 splits");
+  EXPECT(medusa_tree_attention_splits(1, 64, 32, 32, 96, 928, 16, MEDUSA_BF16) == -1, "D = 96");
+  EXPECT(medusa_tree_attention_splits(1, 64, 32, 32, 128, 928, 16, 7) == -1, "unknown dtype");
+  EXPECT(medusa_tree_attention_splits(0, 64, 32, 32, 128, 928, 16, MEDUSA_BF16) == -1, "B = 0");
   /* ordinary sizes stay exact */
   EXPECT(medusa_topk_ws(5, 4096, 10) == 0, "one chunk needs no workspace");
   EXPECT(medusa_topk_ws(5, 32000, 10) >= (size_t)5 * 8 * 10 * 8, "several chunks keep their candidates");
