@@ -64,8 +64,8 @@ def test_c2_tree_attention_7b_layer(lib, ctx, max_ctx):
     masks = _mask(d, B)
     bf = torch.bfloat16
     width = (max_ctx + N + 15) // 16
-    pt = np.zeros((B, width), np.int32)          # the launch plan of max_ctx
-    pt[:, :d["page_table"].shape[1]] = d["page_table"]
+    pt = -np.ones((B, width), np.int32)          # the launch plan of max_ctx; the entries
+    pt[:, :d["page_table"].shape[1]] = d["page_table"]  # past ctx + N are never dereferenced
     Kc, Vc = dev(d["Kc"], bf), dev(d["Vc"], bf)
     ws = lib._ws(lib.tree_attention_ws_bytes(B, N, H, H, D, max_ctx), "cuda")
     out = lib.medusa_tree_attention(dev(d["Q"], bf), dev(d["Kt"], bf), dev(d["Vt"], bf), Kc, Vc,
